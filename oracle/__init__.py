@@ -1,0 +1,200 @@
+"""CPU oracle for multi-scale deformable attention and spatial cross-attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares
+no code with the HIP library and imports nothing from it.
+
+The arithmetic lives in ``oracle.c`` (plain loops, IEEE double); this module
+only marshals numpy arrays into it.  Every function returns float64 arrays.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+def use_library(path):
+    """Load the oracle from another build of oracle.c (the mutation tests
+    compile copies with planted mistakes).  None restores the default."""
+    global _lib
+    _lib = None
+    if path is not None:
+        _load(path)
+
+
+def _load(path=None):
+    global _lib
+    if _lib is not None:
+        return _lib
+    if path is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+    lib = ctypes.CDLL(path)
+    lib.oracle_msda.argtypes = [_p, _int, _p, _p, _p, _p, _int, _i64, _i64, _i64, _int, _int, _int, _int,
+                                _p, _i64, _p]
+    lib.oracle_msda_frames.argtypes = [_p, _int, _p, _p, _p, _p, _int, _i64, _i64, _i64, _i64, _int, _int,
+                                       _int, _int, _p, _i64, _p]
+    lib.oracle_sca.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
+                               _int, _int, _p, _i64, _p, _p, _p, _p]
+    lib.oracle_linear_bf16.argtypes = [_p, _int, _p, _p, _i64, _i64, _i64, _p]
+    lib.oracle_round_to_bf16.argtypes = [_p, _i64, _p]
+    lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_double.restype = ctypes.c_double
+    for f in (lib.oracle_msda, lib.oracle_msda_frames, lib.oracle_sca, lib.oracle_linear_bf16):
+        f.restype = _int
+    _lib = lib
+    return lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(_p)
+
+
+def _value(value):
+    """float32 array, or uint16 array holding bfloat16 bit patterns."""
+    if value.dtype == np.uint16:
+        v, p = _c(value, np.uint16)
+        return v, p, 1
+    v, p = _c(value, np.float32)
+    return v, p, 0
+
+
+def _rows(rows, total):
+    if rows is None:
+        return None, None, total
+    r, p = _c(rows, np.int64)
+    return r, p, len(r)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: oracle rejected its arguments (code {rc})")
+
+
+def msda(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+         weights_are_logits=False, rows=None):
+    """MSDA operator.  value [B,Nv,nH,Dh]; locations [B,Nq,nH,L,P,2];
+    weights [B,Nq,nH,L*P].  Returns [len(rows) or B*Nq, nH*Dh] float64."""
+    lib = _load()
+    B, Nv, nH, Dh = value.shape
+    _, Nq, _, L, P, _ = sampling_locations.shape
+    v, vp, vb = _value(value)
+    ss, ssp = _c(spatial_shapes, np.int64)
+    ls, lsp = _c(level_start_index, np.int64)
+    loc, locp = _c(sampling_locations, np.float32)
+    w, wp = _c(attention_weights, np.float32)
+    r, rp, n = _rows(rows, B * Nq)
+    out = np.zeros((n, nH * Dh), np.float64)
+    rc = lib.oracle_msda(vp, vb, ssp, lsp, locp, wp, int(bool(weights_are_logits)), B, Nv, Nq, nH, Dh, L, P,
+                         rp, n, out.ctypes.data_as(_p))
+    _check(rc, "oracle_msda")
+    del v, ss, ls, loc, w, r
+    return out
+
+
+def msda_frames(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+                weights_are_logits=True, rows=None):
+    """Mean over F frames of per-frame MSDA.  value [B,F,Nv,nH,Dh];
+    locations [B,F,Nq,nH,L,P,2]; weights [B,F,Nq,nH,L*P].  Returns
+    [len(rows) or B*Nq, nH*Dh] float64."""
+    lib = _load()
+    B, F, Nv, nH, Dh = value.shape
+    _, _, Nq, _, L, P, _ = sampling_locations.shape
+    v, vp, vb = _value(value)
+    ss, ssp = _c(spatial_shapes, np.int64)
+    ls, lsp = _c(level_start_index, np.int64)
+    loc, locp = _c(sampling_locations, np.float32)
+    w, wp = _c(attention_weights, np.float32)
+    r, rp, n = _rows(rows, B * Nq)
+    out = np.zeros((n, nH * Dh), np.float64)
+    rc = lib.oracle_msda_frames(vp, vb, ssp, lsp, locp, wp, int(bool(weights_are_logits)), B, F, Nv, Nq, nH,
+                                Dh, L, P, rp, n, out.ctypes.data_as(_p))
+    _check(rc, "oracle_msda_frames")
+    del v, ss, ls, loc, w, r
+    return out
+
+
+def sca(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
+        attention_logits, rows=None, want_slots=True):
+    """Spatial cross-attention.  value [B,Ncam,Nv,nH,Dh]; reference_points_cam
+    [Ncam,B,Nq,D,2]; bev_mask [Ncam,B,Nq,D]; sampling_offsets [B,Nq,nH,L,P,2];
+    attention_logits [B,Nq,nH,L*P].
+
+    Returns dict with slots [n,nH*Dh] float64 (None unless want_slots),
+    hit_count [B,Nq] int32, pair_offsets [B*Ncam+1] int32, pair_q [Npairs] int32.
+    """
+    lib = _load()
+    B, Ncam, Nv, nH, Dh = value.shape
+    _, _, Nq, D, _ = reference_points_cam.shape
+    _, _, _, L, P, _ = sampling_offsets.shape
+    v, vp, vb = _value(value)
+    ss, ssp = _c(spatial_shapes, np.int64)
+    ls, lsp = _c(level_start_index, np.int64)
+    rpc, rpcp = _c(reference_points_cam, np.float32)
+    bm, bmp = _c(bev_mask, np.uint8)
+    off, offp = _c(sampling_offsets, np.float32)
+    lg, lgp = _c(attention_logits, np.float32)
+    r, rp, n = _rows(rows, B * Nq)
+    slots = np.zeros((n, nH * Dh), np.float64) if want_slots else None
+    hit = np.zeros((B, Nq), np.int32)
+    offs = np.zeros(B * Ncam + 1, np.int32)
+    pq = np.zeros(max(1, B * Ncam * Nq), np.int32)
+    rc = lib.oracle_sca(vp, vb, ssp, lsp, rpcp, bmp, offp, lgp, B, Ncam, Nv, Nq, nH, Dh, L, P, D, rp, n,
+                        slots.ctypes.data_as(_p) if want_slots else None, hit.ctypes.data_as(_p),
+                        offs.ctypes.data_as(_p), pq.ctypes.data_as(_p))
+    _check(rc, "oracle_sca")
+    del v, ss, ls, rpc, bm, off, lg, r
+    return {"slots": slots, "hit_count": hit, "pair_offsets": offs, "pair_q": pq[: int(offs[-1])].copy()}
+
+
+def linear_bf16(X, W, bias=None):
+    """Y = X W^T + bias in float64 from bf16 operands.  X: uint16 bf16 bits
+    [M,K], or float32 [M,K] (rounded to the nearest bf16 first).  W: uint16
+    [N,K].  bias: float32 [N] or None."""
+    lib = _load()
+    M, K = X.shape
+    N = W.shape[0]
+    if X.dtype == np.uint16:
+        x, xp = _c(X, np.uint16)
+        xf = 0
+    else:
+        x, xp = _c(X, np.float32)
+        xf = 1
+    w, wp = _c(W, np.uint16)
+    if bias is not None:
+        b, bp = _c(bias, np.float32)
+    else:
+        b, bp = None, None
+    Y = np.zeros((M, N), np.float64)
+    rc = lib.oracle_linear_bf16(xp, xf, wp, bp, M, N, K, Y.ctypes.data_as(_p))
+    _check(rc, "oracle_linear_bf16")
+    del x, w, b
+    return Y
+
+
+def round_to_bf16(x):
+    """Nearest bf16 (ties to even) of each element, as uint16 bit patterns."""
+    lib = _load()
+    a, ap = _c(x, np.float64)
+    out = np.zeros(a.shape, np.uint16)
+    lib.oracle_round_to_bf16(ap, a.size, out.ctypes.data_as(_p))
+    return out
+
+
+def bf16_to_float64(bits):
+    """Exact widening of bf16 bit patterns."""
+    lib = _load()
+    flat = np.ascontiguousarray(bits, np.uint16).ravel()
+    return np.array([lib.oracle_bf16_to_double(int(b)) for b in flat], np.float64).reshape(np.shape(bits))
