@@ -1,0 +1,284 @@
+#!/usr/bin/env python
+"""Benchmark of the BEVFormer-base spatial cross-attention (SCA) forward pass
+on one MI355X, through libmsda.so's C ABI.
+
+Workload (default): BEVFormer-base SCA, fp32 value, batch 1, 6 cameras,
+200x200 BEV queries, 4 levels per camera (116x200, 58x100, 29x50, 15x25),
+8 heads x 32 channels, 8 points per level over 4 pillar anchors; seeded
+synthetic inputs from workloads.bevformer_sca().  One step is the whole hot
+path: visibility + compaction of the (camera, query) pairs (sca_compact) and
+the fused softmax / bilinear gather / weighted sum / camera mean
+(sca_gather).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  value = bilinear samples per second (one sample = one
+(camera, query, head, level, point) bilinear read of 4 corners x 32
+channels); roofline = the gather kernel's effective bytes (all 4 nominal
+corners of every sample, plus offsets, logits, anchors and output) per
+launch over its average launch time, measured with HIP events recorded on
+the stream the kernel runs on; cpu_baseline = the CPU oracle on the same
+workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --calibrate-copy   (a plain device copy of known size, for
+                                      scaling the HBM byte counters)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+GATHER_SOURCES = ["scale_deformable_attention_forward_amd/csrc/gather.hip",
+                  "scale_deformable_attention_forward_amd/csrc/common.hpp",
+                  "scale_deformable_attention_forward_amd/csrc/internal.hpp"]
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when the kernel's sources changed since they were taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if c.get("source_digest") != source_digest(GATHER_SOURCES):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 28  # 256 Mi floats = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4}))
+
+
+class Workload:
+    """A bench workload: inputs on the device and a step() that runs the hot path."""
+
+
+def sca_workload(bf16=False):
+    import numpy as np
+    import torch
+    import workloads as W
+    import scale_deformable_attention_forward_amd as m
+
+    w = W.bevformer_sca(value_bf16=bf16) if bf16 else W.bevformer_sca()
+    d = {}
+    for k in ("spatial_shapes", "level_start_index", "reference_points_cam", "bev_mask", "sampling_offsets",
+              "attention_logits"):
+        d[k] = torch.from_numpy(np.ascontiguousarray(w[k])).cuda()
+    if bf16:
+        d["value"] = torch.from_numpy(w["value"].view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        d["value"] = torch.from_numpy(w["value"]).cuda()
+    B, Ncam, Nq, nH, L, P, D = w["B"], w["Ncam"], w["Nq"], w["nH"], w["L"], w["P"], w["D"]
+    ws = torch.empty(m.sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device="cuda")
+    slots = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
+    offs = torch.empty(B * Ncam + 1, dtype=torch.int32, device="cuda")
+    pq = torch.empty(B * Ncam * Nq, dtype=torch.int32, device="cuda")
+    hit = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
+
+    wl = Workload()
+    wl.name = "sca_bf16" if bf16 else "sca"
+    wl.w = w
+
+    def compact():
+        m.sca_compact(d["bev_mask"], ws, hit_count=hit, pair_offsets=offs, pair_q=pq)
+
+    def gather():
+        m.sca_gather(d["value"], d["spatial_shapes"], d["level_start_index"], d["reference_points_cam"],
+                     d["sampling_offsets"], d["attention_logits"], ws, slots=slots, pair_offsets=offs, pair_q=pq)
+
+    wl.pre, wl.kernel = compact, gather
+
+    def finish():
+        torch.cuda.synchronize()
+        n_pairs = int(offs[-1].item())
+        elem = 2 if bf16 else 4
+        samples = n_pairs * nH * L * P
+        wl.samples = samples
+        # effective bytes of one gather launch: 4 nominal corners x 32 channels
+        # per sample, the per-query offsets and logits, the anchors of each
+        # pair, the camera masks and pair list, and the output rows
+        wl.eff_bytes = (samples * 4 * 32 * elem + B * Nq * nH * L * P * (8 + 4) + n_pairs * D * 8
+                        + B * Nq * 4 + n_pairs * 4 + B * Nq * nH * 32 * 4)
+        wl.gathered_bytes = samples * 4 * 32 * elem
+    wl.finish = finish
+    wl.config = {"workload": "BEVFormer-base spatial cross-attention layer, 6 cameras",
+                 "batch": B, "cameras": Ncam, "bev_queries": "200x200", "levels": "116x200/58x100/29x50/15x25",
+                 "heads": nH, "head_dim": 32, "points_per_level": P, "pillar_anchors": D,
+                 "value_dtype": "bf16" if bf16 else "fp32", "mask": "azimuth sectors, 1-2 cameras per query"}
+    wl.dtype = "fp32 accumulate, bf16 value" if bf16 else "fp32"
+    wl.kernel_key = "sca_gather_kernel_bf16" if bf16 else "sca_gather_kernel_fp32"
+
+    def cpu_baseline():
+        import oracle
+        t0 = time.perf_counter()
+        oracle.sca(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
+                   w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
+        t = time.perf_counter() - t0
+        return {"value": wl.samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole workload (all {B * Nq} queries, {wl.samples} samples), "
+                          f"single-threaded C, {t:.1f} s"}
+    wl.cpu_baseline = cpu_baseline
+    return wl
+
+
+def msda_workload(which):
+    import numpy as np
+    import torch
+    import workloads as W
+    import scale_deformable_attention_forward_amd as m
+
+    if which == "detr":
+        w = W.detr_encoder_msda()
+        F = 1
+    elif which == "tiny":
+        w = W.tiny_msda()
+        F = 1
+    else:
+        w = W.temporal_frames()
+        F = w["F"]
+    d = {k: torch.from_numpy(np.ascontiguousarray(w[k])).cuda()
+         for k in ("value", "spatial_shapes", "level_start_index", "sampling_locations", "attention_weights")}
+    B, Nq, nH, L, P = w["B"], w["Nq"], w["nH"], w["L"], w["P"]
+    out = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
+    wl = Workload()
+    wl.name = which
+    wl.w = w
+
+    def kernel():
+        if F == 1:
+            m.msda_forward(d["value"], d["spatial_shapes"], d["level_start_index"], d["sampling_locations"],
+                           d["attention_weights"], out=out)
+        else:
+            m.msda_forward_frames(d["value"], d["spatial_shapes"], d["level_start_index"], d["sampling_locations"],
+                                  d["attention_weights"], out=out)
+    wl.pre, wl.kernel = (lambda: None), kernel
+
+    def finish():
+        torch.cuda.synchronize()
+        wl.samples = B * F * Nq * nH * L * P
+        wl.gathered_bytes = wl.samples * 4 * 32 * 4
+        wl.eff_bytes = wl.gathered_bytes + wl.samples * (8 + 4) + B * Nq * nH * 32 * 4
+    wl.finish = finish
+    names = {"detr": "Deformable-DETR encoder MSDA, 4 levels 100x150/50x75/25x38/13x19, Nq=Nv=19947",
+             "tiny": "tiny MSDA, 256 queries, one 32x32 level",
+             "tsa": "temporal self-attention, 2 stacked 200x200 BEV maps, mean over frames"}
+    wl.config = {"workload": names[which], "batch": B, "queries": Nq, "heads": nH, "head_dim": 32,
+                 "levels": L, "points_per_level": P, "frames": F, "value_dtype": "fp32"}
+    wl.dtype = "fp32"
+    wl.kernel_key = "msda_gather_kernel_fp32"
+
+    def cpu_baseline():
+        import oracle
+        t0 = time.perf_counter()
+        if F == 1:
+            oracle.msda(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
+                        w["attention_weights"], True)
+        else:
+            oracle.msda_frames(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
+                               w["attention_weights"], True)
+        t = time.perf_counter() - t0
+        return {"value": wl.samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole workload ({wl.samples} samples), single-threaded C, {t:.1f} s"}
+    wl.cpu_baseline = cpu_baseline
+    return wl
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sca", choices=["sca", "sca_bf16", "detr", "tsa", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    import scale_deformable_attention_forward_amd as m
+    m.load_library()
+
+    if args.workload.startswith("sca"):
+        wl = sca_workload(bf16=args.workload == "sca_bf16")
+    else:
+        wl = msda_workload(args.workload)
+
+    for _ in range(args.warmup):
+        wl.pre()
+        wl.kernel()
+    wl.finish()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        wl.pre()
+        starts[k].record()  # torch's current stream = the stream the binding launches on
+        wl.kernel()
+        ends[k].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / K
+
+    achieved = wl.eff_bytes / (kernel_ms * 1e-3) / 1e9
+    traffic = measured_traffic(wl.kernel_key)
+    line = {
+        "metric": "MSDA samples/sec + effective HBM GB/s, BEVFormer-base SCA layer (6 cams)",
+        "value": wl.samples / (ms_per_step * 1e-3),
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded, BEVFormer-shaped; no dataset or trained weights)",
+        "config": wl.config,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": wl.kernel_key.rsplit("_", 1)[0], "kernel_ms": kernel_ms,
+                     "effective_bytes_per_launch": wl.eff_bytes, "gathered_bytes_per_launch": wl.gathered_bytes},
+        "effective_GBps_per_step": wl.eff_bytes / (ms_per_step * 1e-3) / 1e9,
+        "samples_per_step": wl.samples,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = wl.cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+/*
+ * msda.h -- C ABI of libmsda.so: multi-scale deformable attention (MSDA) and
+ * BEVFormer spatial cross-attention (SCA), forward pass, on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [8-heads]  "BEV(三) BEVFormer：Query 参数如何与 Feature 的 8 个 Head 交互"
+ *              (leheavengame.com, reprint of a CSDN post).
+ *   [SCA-note] Tencent Cloud developer article 2321140 on BEVFormer's Spatial
+ *              Cross-Attention (bev_mask rebatch code; scatter / count /
+ *              divide code).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers marked "device" point to GPU memory of the current HIP device;
+ *    "host" pointers to ordinary CPU memory.  Every buffer is owned by the
+ *    caller, dense and row-major in the shape given.  The library never
+ *    allocates or frees memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it asynchronously; no entry point synchronises the
+ *    host.  Buffers must stay valid until the stream has finished the work.
+ *  - Arguments are checked on the host before anything is enqueued.  A
+ *    non-zero return means nothing was enqueued, except MSDA_ERR_HIP, which
+ *    reports a failed launch (the stream may then hold part of the work).
+ *    msda_status_string() names a code; msda_last_error() gives the message
+ *    of the calling thread's last failure.
+ *  - With Nq = 0 nothing is enqueued and the per-query buffers (locations,
+ *    weights, offsets, logits, masks, anchors, outputs) may be NULL.
+ *  - Floating-point inputs must be finite.  Sample locations may lie
+ *    anywhere (outside the map they read zeros).
+ *  - Shared limits: head width Dh = 32; L*P <= 64 sampling points per head;
+ *    1 <= nH <= 64; one value image (Nv * nH * Dh elements of one batch
+ *    item, camera or frame) under 2^31 bytes; Nq, Nv < 2^31.
+ *  - Level table: spatial_shapes[l] = (H_l, W_l) and level_start_index[l] =
+ *    first pixel of level l in the flattened value axis; pixel (x, y) of
+ *    level l is value row level_start_index[l] + y*W_l + x.  Corners that
+ *    fall outside the level, or whose row falls outside [0, Nv), read zero.
+ *  - Channel layout: channel d of head h is element h*Dh + d of a pixel's
+ *    value row and of an output row ([8-heads] 18.2 and 9).
+ */
+#ifndef MSDA_H
+#define MSDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MSDA_OK 0
+#define MSDA_ERR_INVALID_ARG 1 /* null pointer, bad size or enum, misaligned buffer */
+#define MSDA_ERR_UNSUPPORTED 2 /* outside the shared limits above */
+#define MSDA_ERR_SHAPE 3       /* inconsistent shapes (e.g. P not a multiple of D) */
+#define MSDA_ERR_WORKSPACE 4   /* workspace missing, too small or misaligned */
+#define MSDA_ERR_HIP 5         /* the HIP runtime reported an error */
+
+/* element types */
+#define MSDA_F32 0  /* IEEE binary32 */
+#define MSDA_BF16 1 /* bfloat16 (upper half of a binary32), stored as uint16 */
+
+/* meaning of attention_weights */
+#define MSDA_WEIGHTS_PROB 0   /* already softmaxed over the L*P points of each head */
+#define MSDA_WEIGHTS_LOGITS 1 /* logits: softmax over each head's L*P points is fused */
+
+/*
+ * MSDA operator ([8-heads] 18.5: the operator receives value, spatial_shapes,
+ * level_start_index, sampling_locations and attention_weights; 4.2 softmax,
+ * 6 bilinear sampling at x = W_l*s_x - 1/2, y = H_l*s_y - 1/2, 8 weighted sum
+ * over levels and points, 9 concatenation of heads).
+ *
+ *   value               device [B][Nv][nH][Dh], MSDA_F32 or MSDA_BF16, 16-byte aligned
+ *   spatial_shapes      device int64 [L][2], (H_l, W_l)
+ *   level_start_index   device int64 [L]
+ *   sampling_locations  device float [B][Nq][nH][L][P][2], normalised (x, y), 8-byte aligned
+ *   attention_weights   device float [B][Nq][nH][L*P], per weight_mode
+ *   out                 device float [B][Nq][nH*Dh], 16-byte aligned; fully overwritten
+ *
+ * out[b][q][h*Dh + d] = sum over l, p of alpha[b][q][h][l*P + p] *
+ *                       bilinear(value[b][level l][.][h][d], sampling_locations[b][q][h][l][p])
+ * Accumulation is in float32; bf16 values are widened exactly.
+ */
+int msda_forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                 const int64_t* level_start_index, const float* sampling_locations,
+                 const float* attention_weights, int weight_mode, int64_t B, int64_t Nv, int64_t Nq,
+                 int nH, int Dh, int L, int P, float* out, void* stream);
+
+/*
+ * MSDA over F stacked value maps (the temporal workload: a BEV query attends
+ * to the previous, aligned BEV map and the current one), with the frame as
+ * an inner batch axis; each frame has its own locations and its own softmax,
+ * and the output is the arithmetic mean over frames.  The pages only give
+ * the operator ([8-heads] 18.5); the frame mean is this library's reading of
+ * the two-map workload.
+ *
+ *   value               device [B][F][Nv][nH][Dh]
+ *   sampling_locations  device float [B][F][Nq][nH][L][P][2]
+ *   attention_weights   device float [B][F][Nq][nH][L*P]
+ *   out                 device float [B][Nq][nH*Dh] = (1/F) * sum over f of MSDA(frame f)
+ * Other arguments as msda_forward.  F >= 1.
+ */
+int msda_forward_frames(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                        const int64_t* level_start_index, const float* sampling_locations,
+                        const float* attention_weights, int weight_mode, int64_t B, int64_t F,
+                        int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, float* out, void* stream);
+
+/*
+ * Workspace bytes sca_forward needs for (B, Ncam, Nq).  Host only; touches no
+ * device.  Returns MSDA_OK and writes *bytes, or MSDA_ERR_INVALID_ARG.
+ */
+int sca_workspace_size(int64_t B, int64_t Ncam, int64_t Nq, size_t* bytes);
+
+/*
+ * Spatial cross-attention forward, from the camera masks to the camera mean
+ * (before the output projection).
+ *
+ * Steps:
+ *  1. Visibility and compaction ([SCA-note] rebatch): camera c sees query q
+ *     of batch item b when any of its D anchors is marked in bev_mask.  For
+ *     each (b, c) in b-major order the ascending list of the queries c sees;
+ *     pair_offsets[b*Ncam + c] is the start of that list in pair_q and
+ *     pair_offsets[B*Ncam] the number of pairs.  hit_count[b][q] is the number
+ *     of cameras that see the query ([SCA-note] count).  These are exact
+ *     integers.
+ *  2. For each seen (b, c, q): one softmax per head over the query's L*P
+ *     logits ([8-heads] 4.2; the same for every camera, [8-heads] 10),
+ *     sampling location of point p of level l at anchor p mod D:
+ *     s = reference_points_cam[c][b][q][p mod D] + (dx / W_l, dy / H_l)
+ *     ([8-heads] 5), bilinear sampling and the weighted sum ([8-heads] 6-9).
+ *  3. slots[b][q] = (sum over the seeing cameras, in ascending order, of
+ *     step 2) / max(1, hit_count[b][q]) ([8-heads] 10; [SCA-note] clamp and
+ *     divide).  A query no camera sees gets zeros.
+ *
+ *   value                 device [B][Ncam][Nv][nH][Dh], MSDA_F32 or MSDA_BF16, 16-byte aligned
+ *   spatial_shapes        device int64 [L][2]; level_start_index device int64 [L]
+ *   reference_points_cam  device float [Ncam][B][Nq][D][2], normalised (x, y), 8-byte aligned
+ *   bev_mask              device uint8 [Ncam][B][Nq][D], nonzero = anchor marked
+ *   sampling_offsets      device float [B][Nq][nH][L][P][2], in cells of level l, 8-byte aligned
+ *   attention_logits      device float [B][Nq][nH][L*P]
+ *   slots                 device float [B][Nq][nH*Dh], 16-byte aligned; fully overwritten
+ *   hit_count             device int32 [B][Nq], or NULL
+ *   pair_offsets          device int32 [B*Ncam + 1], or NULL (then kept in the workspace)
+ *   pair_q                device int32 [B*Ncam*Nq] (only the first pair_offsets[B*Ncam]
+ *                         entries are written), or NULL (then kept in the workspace)
+ *   workspace             device, >= sca_workspace_size() bytes, 256-byte aligned; its
+ *                         contents on entry do not matter and are clobbered
+ * Limits: 1 <= Ncam <= 32; 1 <= D; P % D == 0 (else MSDA_ERR_SHAPE);
+ * B*Ncam*Nq < 2^31; the shared limits above.
+ * Equivalent to sca_compact followed by sca_gather (all arguments of both
+ * are checked before either is enqueued).
+ */
+int sca_forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                const int64_t* level_start_index, const float* reference_points_cam,
+                const uint8_t* bev_mask, const float* sampling_offsets, const float* attention_logits,
+                int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, int D,
+                float* slots, int32_t* hit_count, int32_t* pair_offsets, int32_t* pair_q,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 1 of sca_forward on its own: visibility, hit counts and the pair
+ * lists ([SCA-note] rebatch and count), written to hit_count / pair_offsets /
+ * pair_q when given and always to the workspace.  Since the camera masks do
+ * not change between the encoder layers of one frame, one sca_compact can
+ * serve several sca_gather calls.
+ *   bev_mask, hit_count, pair_offsets, pair_q, workspace: as sca_forward.
+ * Limits: 1 <= Ncam <= 32, D >= 1, B*Ncam*Nq < 2^31.
+ */
+int sca_compact(const uint8_t* bev_mask, int64_t B, int64_t Ncam, int64_t Nq, int D, int32_t* hit_count,
+                int32_t* pair_offsets, int32_t* pair_q, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 2 of sca_forward on its own: steps 2 and 3 for every pair that
+ * sca_compact listed.  The workspace must hold what sca_compact wrote for the
+ * same (B, Ncam, Nq), enqueued before on the same stream (or otherwise
+ * ordered before this call), and pair_offsets / pair_q must be the buffers
+ * given to that sca_compact (NULL if it was given NULL).  slots is fully
+ * overwritten.  Other arguments as sca_forward.  One kernel launch.
+ */
+int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes, const int64_t* level_start_index,
+               const float* reference_points_cam, const float* sampling_offsets, const float* attention_logits,
+               int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, int D, float* slots,
+               const int32_t* pair_offsets, const int32_t* pair_q, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * Dense projection on matrix cores, bf16 operands and float32 accumulation:
+ *   Y[M][N] = X[M][K] * W[N][K]^T + bias[N]
+ * The value projection V = W_v F + b_v ([8-heads] 3) and the output
+ * projection o = W_o g + b_o ([8-heads] 11) of the bf16 configuration.
+ *
+ *   X     device [M][K]; MSDA_BF16, or MSDA_F32 (each element rounded to the
+ *         nearest bf16, ties to even, as it is read); 16-byte aligned
+ *   W     device bf16 [N][K], 16-byte aligned
+ *   bias  device float [N], or NULL for zero
+ *   Y     device [M][N]; MSDA_BF16 (rounded to nearest, ties to even) or MSDA_F32
+ * Limits: K % 32 == 0 and 32 <= K <= 256; N % 16 == 0 and N <= 65536; M < 2^31.
+ */
+int msda_gemm_bf16(const void* X, int x_dtype, const uint16_t* W, const float* bias, void* Y,
+                   int y_dtype, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Name of a status code (host; static string). */
+const char* msda_status_string(int status);
+
+/* Message of the calling thread's last non-OK return (host; valid until the
+ * thread's next call into the library). */
+const char* msda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSDA_H */

@@ -184,6 +184,19 @@ def linear_bf16(X, W, bias=None):
     return Y
 
 
+def linear_bf16_blas(X, W, bias=None):
+    """Same as linear_bf16 for bf16-bit X, with the library float64 matmul as
+    the contraction step (for the full-size value projection, which plain
+    loops would take minutes for).  Decoding bf16 is exact, so only the
+    summation order differs from the loop version."""
+    assert X.dtype == np.uint16 and W.dtype == np.uint16
+    dec = lambda bits: (np.ascontiguousarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    Y = dec(X) @ dec(W).T
+    if bias is not None:
+        Y += np.asarray(bias, np.float64)
+    return Y
+
+
 def round_to_bf16(x):
     """Nearest bf16 (ties to even) of each element, as uint16 bit patterns."""
     lib = _load()

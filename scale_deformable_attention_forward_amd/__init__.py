@@ -1,0 +1,257 @@
+"""Multi-scale deformable attention and BEVFormer spatial cross-attention,
+forward pass, on AMD Instinct MI355X (gfx950).
+
+This module is the thin Python binding of libmsda.so (C ABI in
+include/msda.h).  It only marshals torch tensors into pointers and sizes:
+every step of the computation runs in the library's HIP kernels.  PyTorch
+provides device memory and the current stream.  If the library is missing,
+importing works but every call raises: there is no fallback path.
+
+Functions (same names as the C entry points):
+  msda_forward, msda_forward_frames, sca_workspace_size, sca_forward,
+  sca_compact, sca_gather, msda_gemm_bf16, msda_status_string, msda_last_error
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MsdaError", "MSDA_F32", "MSDA_BF16", "MSDA_WEIGHTS_PROB", "MSDA_WEIGHTS_LOGITS",
+    "library_path", "load_library", "msda_forward", "msda_forward_frames", "sca_workspace_size",
+    "sca_forward", "sca_compact", "sca_gather", "msda_gemm_bf16", "msda_status_string", "msda_last_error",
+]
+
+MSDA_F32, MSDA_BF16 = 0, 1
+MSDA_WEIGHTS_PROB, MSDA_WEIGHTS_LOGITS = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+_p, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+
+class MsdaError(RuntimeError):
+    """A non-zero status from libmsda.so."""
+
+    def __init__(self, fn, code, message):
+        super().__init__(f"{fn}: {msda_status_string(code)}: {message}")
+        self.code = code
+
+
+def library_path():
+    return os.path.join(_HERE, "libmsda.so")
+
+
+def load_library():
+    """Load the in-tree libmsda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m scale_deformable_attention_forward_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.msda_forward.argtypes = [_p, _int, _p, _p, _p, _p, _int, _i64, _i64, _i64, _int, _int, _int, _int, _p, _p]
+    lib.msda_forward_frames.argtypes = [_p, _int, _p, _p, _p, _p, _int, _i64, _i64, _i64, _i64, _int, _int, _int,
+                                        _int, _p, _p]
+    lib.sca_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
+    lib.sca_forward.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int,
+                                _int, _p, _p, _p, _p, _p, _sz, _p]
+    lib.sca_compact.argtypes = [_p, _i64, _i64, _i64, _int, _p, _p, _p, _p, _sz, _p]
+    lib.sca_gather.argtypes = [_p, _int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _int,
+                               _p, _p, _p, _p, _sz, _p]
+    lib.msda_gemm_bf16.argtypes = [_p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p]
+    for f in (lib.msda_forward, lib.msda_forward_frames, lib.sca_workspace_size, lib.sca_forward,
+              lib.sca_compact, lib.sca_gather, lib.msda_gemm_bf16):
+        f.restype = _int
+    lib.msda_status_string.argtypes = [_int]
+    lib.msda_status_string.restype = ctypes.c_char_p
+    lib.msda_last_error.argtypes = []
+    lib.msda_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def msda_status_string(code):
+    return load_library().msda_status_string(int(code)).decode()
+
+
+def msda_last_error():
+    return load_library().msda_last_error().decode()
+
+
+def _check(fn, code):
+    if code != 0:
+        raise MsdaError(fn, code, msda_last_error())
+
+
+def _ptr(t, name, dtypes=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    return t.data_ptr()
+
+
+def _value_dtype(value):
+    if value.dtype == torch.float32:
+        return MSDA_F32
+    if value.dtype == torch.bfloat16:
+        return MSDA_BF16
+    raise TypeError(f"value must be float32 or bfloat16, got {value.dtype}")
+
+
+def _stream(stream, device):
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+_I64 = (torch.int64,)
+_F32 = (torch.float32,)
+
+
+def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+                 weight_mode=MSDA_WEIGHTS_LOGITS, out=None, stream=None):
+    """value [B,Nv,nH,Dh] (float32|bfloat16); spatial_shapes int64 [L,2] (H,W);
+    level_start_index int64 [L]; sampling_locations float32 [B,Nq,nH,L,P,2];
+    attention_weights float32 [B,Nq,nH,L*P].  Returns out float32 [B,Nq,nH*Dh]."""
+    lib = load_library()
+    B, Nv, nH, Dh = value.shape
+    _, Nq, _, L, P, _ = sampling_locations.shape
+    if out is None:
+        out = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=value.device)
+    rc = lib.msda_forward(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
+                          _ptr(level_start_index, "level_start_index", _I64),
+                          _ptr(sampling_locations, "sampling_locations", _F32),
+                          _ptr(attention_weights, "attention_weights", _F32), int(weight_mode), B, Nv, Nq, nH, Dh,
+                          L, P, _ptr(out, "out", _F32), _stream(stream, value.device))
+    _check("msda_forward", rc)
+    return out
+
+
+def msda_forward_frames(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+                        weight_mode=MSDA_WEIGHTS_LOGITS, out=None, stream=None):
+    """value [B,F,Nv,nH,Dh]; sampling_locations [B,F,Nq,nH,L,P,2];
+    attention_weights [B,F,Nq,nH,L*P].  Returns the frame mean, float32
+    [B,Nq,nH*Dh]."""
+    lib = load_library()
+    B, F, Nv, nH, Dh = value.shape
+    _, _, Nq, _, L, P, _ = sampling_locations.shape
+    if out is None:
+        out = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=value.device)
+    rc = lib.msda_forward_frames(_ptr(value, "value"), _value_dtype(value),
+                                 _ptr(spatial_shapes, "spatial_shapes", _I64),
+                                 _ptr(level_start_index, "level_start_index", _I64),
+                                 _ptr(sampling_locations, "sampling_locations", _F32),
+                                 _ptr(attention_weights, "attention_weights", _F32), int(weight_mode), B, F, Nv, Nq,
+                                 nH, Dh, L, P, _ptr(out, "out", _F32), _stream(stream, value.device))
+    _check("msda_forward_frames", rc)
+    return out
+
+
+def sca_workspace_size(B, Ncam, Nq):
+    lib = load_library()
+    n = _sz(0)
+    _check("sca_workspace_size", lib.sca_workspace_size(int(B), int(Ncam), int(Nq), ctypes.byref(n)))
+    return n.value
+
+
+def sca_forward(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
+                attention_logits, slots=None, hit_count=None, pair_offsets=None, pair_q=None, workspace=None,
+                stream=None):
+    """value [B,Ncam,Nv,nH,Dh]; reference_points_cam float32 [Ncam,B,Nq,D,2];
+    bev_mask uint8|bool [Ncam,B,Nq,D]; sampling_offsets float32
+    [B,Nq,nH,L,P,2]; attention_logits float32 [B,Nq,nH,L*P].
+
+    Returns slots float32 [B,Nq,nH*Dh].  hit_count (int32 [B,Nq]),
+    pair_offsets (int32 [B*Ncam+1]) and pair_q (int32 [B*Ncam*Nq]) are
+    filled when given.  workspace: uint8 tensor of >= sca_workspace_size()
+    bytes, allocated here when None."""
+    lib = load_library()
+    B, Ncam, Nv, nH, Dh = value.shape
+    _, _, Nq, D, _ = reference_points_cam.shape
+    _, _, _, L, P, _ = sampling_offsets.shape
+    dev = value.device
+    if slots is None:
+        slots = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=dev)
+    need = sca_workspace_size(B, Ncam, Nq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    i32 = (torch.int32,)
+    rc = lib.sca_forward(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
+                         _ptr(level_start_index, "level_start_index", _I64),
+                         _ptr(reference_points_cam, "reference_points_cam", _F32),
+                         _ptr(bev_mask, "bev_mask", (torch.uint8, torch.bool)),
+                         _ptr(sampling_offsets, "sampling_offsets", _F32),
+                         _ptr(attention_logits, "attention_logits", _F32), B, Ncam, Nv, Nq, nH, Dh, L, P, D,
+                         _ptr(slots, "slots", _F32), _ptr(hit_count, "hit_count", i32),
+                         _ptr(pair_offsets, "pair_offsets", i32), _ptr(pair_q, "pair_q", i32),
+                         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                         _stream(stream, dev))
+    _check("sca_forward", rc)
+    return slots
+
+
+def sca_compact(bev_mask, workspace, hit_count=None, pair_offsets=None, pair_q=None, stream=None):
+    """Stage 1 of sca_forward: bev_mask uint8|bool [Ncam,B,Nq,D] -> camera
+    masks and pair lists in `workspace` (and hit_count / pair_offsets /
+    pair_q when given)."""
+    lib = load_library()
+    Ncam, B, Nq, D = bev_mask.shape
+    i32 = (torch.int32,)
+    rc = lib.sca_compact(_ptr(bev_mask, "bev_mask", (torch.uint8, torch.bool)), B, Ncam, Nq, D,
+                         _ptr(hit_count, "hit_count", i32), _ptr(pair_offsets, "pair_offsets", i32),
+                         _ptr(pair_q, "pair_q", i32), _ptr(workspace, "workspace"),
+                         workspace.numel() * workspace.element_size(), _stream(stream, bev_mask.device))
+    _check("sca_compact", rc)
+
+
+def sca_gather(value, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets, attention_logits,
+               workspace, slots=None, pair_offsets=None, pair_q=None, stream=None):
+    """Stage 2 of sca_forward: gather, weighted sums and camera mean for the
+    pairs the preceding sca_compact on `workspace` listed."""
+    lib = load_library()
+    B, Ncam, Nv, nH, Dh = value.shape
+    _, _, Nq, D, _ = reference_points_cam.shape
+    _, _, _, L, P, _ = sampling_offsets.shape
+    dev = value.device
+    if slots is None:
+        slots = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=dev)
+    i32 = (torch.int32,)
+    rc = lib.sca_gather(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
+                        _ptr(level_start_index, "level_start_index", _I64),
+                        _ptr(reference_points_cam, "reference_points_cam", _F32),
+                        _ptr(sampling_offsets, "sampling_offsets", _F32),
+                        _ptr(attention_logits, "attention_logits", _F32), B, Ncam, Nv, Nq, nH, Dh, L, P, D,
+                        _ptr(slots, "slots", _F32), _ptr(pair_offsets, "pair_offsets", i32),
+                        _ptr(pair_q, "pair_q", i32), _ptr(workspace, "workspace"),
+                        workspace.numel() * workspace.element_size(), _stream(stream, dev))
+    _check("sca_gather", rc)
+    return slots
+
+
+def msda_gemm_bf16(X, W, bias=None, y_dtype=torch.bfloat16, out=None, stream=None):
+    """Y = X W^T + bias.  X [M,K] bfloat16 (or float32, rounded to bf16 as
+    read); W bfloat16 [N,K]; bias float32 [N] or None.  Returns Y [M,N] of
+    y_dtype (bfloat16 or float32)."""
+    lib = load_library()
+    M, K = X.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=y_dtype, device=X.device)
+    x_dt = MSDA_F32 if X.dtype == torch.float32 else MSDA_BF16
+    y_dt = MSDA_F32 if out.dtype == torch.float32 else MSDA_BF16
+    rc = lib.msda_gemm_bf16(_ptr(X, "X", (torch.float32, torch.bfloat16)), x_dt, _ptr(W, "W", (torch.bfloat16,)),
+                            _ptr(bias, "bias", _F32), _ptr(out, "out", (torch.float32, torch.bfloat16)), y_dt,
+                            M, N, K, _stream(stream, X.device))
+    _check("msda_gemm_bf16", rc)
+    return out

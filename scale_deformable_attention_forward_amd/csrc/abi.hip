@@ -1,0 +1,287 @@
+// C ABI of libmsda.so (declared in include/msda.h): argument checks on the
+// host, then stream-ordered launches.  Nothing here allocates device memory
+// or synchronises the host.
+#include <cstdarg>
+#include <cstdio>
+
+#include "internal.hpp"
+#include "msda.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MSDA_OK;
+  return fail(MSDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kI31 = (int64_t)1 << 31;
+
+// Checks shared by the MSDA-style entry points.  images = number of value images.
+int check_common(const void* value, int value_dtype, const int64_t* shapes, const int64_t* starts, int64_t Nv,
+                 int64_t Nq, int nH, int Dh, int L, int P, const void* out, uint32_t* image_bytes) {
+  // with no queries nothing per query is read or written: those buffers may be null
+  if (!value || !shapes || !starts || (!out && Nq != 0)) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (value_dtype != MSDA_F32 && value_dtype != MSDA_BF16)
+    return fail(MSDA_ERR_INVALID_ARG, "value_dtype %d is neither MSDA_F32 nor MSDA_BF16", value_dtype);
+  if (Nv < 1 || Nq < 0 || nH < 1 || Dh < 1 || L < 1 || P < 1)
+    return fail(MSDA_ERR_INVALID_ARG, "sizes must be positive (Nv=%lld Nq=%lld nH=%d Dh=%d L=%d P=%d)",
+                (long long)Nv, (long long)Nq, nH, Dh, L, P);
+  if (Dh != 32) return fail(MSDA_ERR_UNSUPPORTED, "head width Dh=%d: only 32 is supported", Dh);
+  if (nH > 64) return fail(MSDA_ERR_UNSUPPORTED, "nH=%d: at most 64 heads", nH);
+  if ((int64_t)L * P > 64) return fail(MSDA_ERR_UNSUPPORTED, "L*P=%lld: at most 64 points per head", (long long)L * P);
+  if (Nv >= kI31 || Nq >= kI31) return fail(MSDA_ERR_UNSUPPORTED, "Nv and Nq must be below 2^31");
+  const int64_t elem = value_dtype == MSDA_F32 ? 4 : 2;
+  const int64_t bytes = Nv * nH * Dh * elem;
+  if (bytes >= kI31) return fail(MSDA_ERR_UNSUPPORTED, "one value image is %lld bytes; the limit is 2^31", (long long)bytes);
+  if (!aligned(value, 16) || (Nq != 0 && !aligned(out, 16)))
+    return fail(MSDA_ERR_INVALID_ARG, "value and output must be 16-byte aligned");
+  *image_bytes = (uint32_t)bytes;
+  return MSDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msda_status_string(int status) {
+  switch (status) {
+    case MSDA_OK: return "MSDA_OK";
+    case MSDA_ERR_INVALID_ARG: return "MSDA_ERR_INVALID_ARG";
+    case MSDA_ERR_UNSUPPORTED: return "MSDA_ERR_UNSUPPORTED";
+    case MSDA_ERR_SHAPE: return "MSDA_ERR_SHAPE";
+    case MSDA_ERR_WORKSPACE: return "MSDA_ERR_WORKSPACE";
+    case MSDA_ERR_HIP: return "MSDA_ERR_HIP";
+    default: return "MSDA_ERR_UNKNOWN";
+  }
+}
+
+const char* msda_last_error(void) { return g_last_error; }
+
+static int msda_frames_impl(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                            const int64_t* level_start_index, const float* sampling_locations,
+                            const float* attention_weights, int weight_mode, int64_t B, int64_t F, int64_t Nv,
+                            int64_t Nq, int nH, int Dh, int L, int P, float* out, void* stream) {
+  uint32_t image_bytes = 0;
+  int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, out,
+                        &image_bytes);
+  if (rc != MSDA_OK) return rc;
+  if ((!sampling_locations || !attention_weights) && Nq != 0)
+    return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (B < 1 || F < 1) return fail(MSDA_ERR_INVALID_ARG, "B and F must be positive");
+  if (weight_mode != MSDA_WEIGHTS_PROB && weight_mode != MSDA_WEIGHTS_LOGITS)
+    return fail(MSDA_ERR_INVALID_ARG, "weight_mode %d is neither PROB nor LOGITS", weight_mode);
+  if (Nq != 0 && (!aligned(sampling_locations, 8) || !aligned(attention_weights, 4)))
+    return fail(MSDA_ERR_INVALID_ARG, "sampling_locations must be 8-byte aligned");
+  if (B * F >= kI31 || B * Nq >= kI31 || B * F * Nq * nH >= kI31 / 64)
+    return fail(MSDA_ERR_UNSUPPORTED, "B*F*Nq*nH too large");
+  g_last_error[0] = '\0';
+  if (Nq == 0) return MSDA_OK;
+  msda::GatherArgs a = {};
+  a.value = value;
+  a.image_bytes = image_bytes;
+  a.bf16 = value_dtype == MSDA_BF16;
+  a.shapes = spatial_shapes;
+  a.starts = level_start_index;
+  a.L = L;
+  a.P = P;
+  a.LP = L * P;
+  a.nH = nH;
+  a.Nv = (int)Nv;
+  a.inv_P = 1.0f / (float)P;
+  a.inv_D = 1.0f;
+  a.loc = sampling_locations;
+  a.weights = attention_weights;
+  a.weight_logits = weight_mode == MSDA_WEIGHTS_LOGITS;
+  a.F = (int)F;
+  a.B = B;
+  a.Nq = Nq;
+  a.out = out;
+  return hip_status(msda::launch_msda_gather(a, static_cast<hipStream_t>(stream)), "msda gather launch");
+}
+
+int msda_forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                 const int64_t* level_start_index, const float* sampling_locations,
+                 const float* attention_weights, int weight_mode, int64_t B, int64_t Nv, int64_t Nq, int nH,
+                 int Dh, int L, int P, float* out, void* stream) {
+  return msda_frames_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_locations,
+                          attention_weights, weight_mode, B, 1, Nv, Nq, nH, Dh, L, P, out, stream);
+}
+
+int msda_forward_frames(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                        const int64_t* level_start_index, const float* sampling_locations,
+                        const float* attention_weights, int weight_mode, int64_t B, int64_t F, int64_t Nv,
+                        int64_t Nq, int nH, int Dh, int L, int P, float* out, void* stream) {
+  return msda_frames_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_locations,
+                          attention_weights, weight_mode, B, F, Nv, Nq, nH, Dh, L, P, out, stream);
+}
+
+int sca_workspace_size(int64_t B, int64_t Ncam, int64_t Nq, size_t* bytes) {
+  if (!bytes) return fail(MSDA_ERR_INVALID_ARG, "bytes is null");
+  if (B < 1 || Ncam < 1 || Nq < 0) return fail(MSDA_ERR_INVALID_ARG, "B and Ncam must be positive, Nq >= 0");
+  if (B * Ncam * Nq >= kI31 || B * Ncam >= (1 << 20))
+    return fail(MSDA_ERR_UNSUPPORTED, "B*Ncam*Nq must be below 2^31");
+  *bytes = msda::compact_layout(B, Ncam, Nq).total;
+  return MSDA_OK;
+}
+
+static int check_workspace(int64_t B, int64_t Ncam, int64_t Nq, const void* workspace, size_t workspace_bytes) {
+  size_t need = 0;
+  const int rc = sca_workspace_size(B, Ncam, Nq, &need);
+  if (rc != MSDA_OK) return rc;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(MSDA_ERR_WORKSPACE, "workspace must be >= %zu bytes and 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  return MSDA_OK;
+}
+
+static msda::CompactArgs compact_args(const uint8_t* bev_mask, int64_t B, int64_t Ncam, int64_t Nq, int D,
+                                      int32_t* hit_count, int32_t* pair_offsets, int32_t* pair_q, void* workspace) {
+  const msda::CompactLayout lay = msda::compact_layout(B, Ncam, Nq);
+  char* ws = static_cast<char*>(workspace);
+  msda::CompactArgs c = {};
+  c.bev_mask = bev_mask;
+  c.B = (int)B;
+  c.Ncam = (int)Ncam;
+  c.Nq = (int)Nq;
+  c.D = D;
+  c.cammask = reinterpret_cast<uint32_t*>(ws + lay.cammask);
+  c.hit_count = hit_count;
+  c.tile_counts = reinterpret_cast<int32_t*>(ws + lay.tile_counts);
+  c.tile_offsets = reinterpret_cast<int32_t*>(ws + lay.tile_offsets);
+  c.pair_offsets = pair_offsets ? pair_offsets : reinterpret_cast<int32_t*>(ws + lay.pair_offsets);
+  c.pair_q = pair_q ? pair_q : reinterpret_cast<int32_t*>(ws + lay.pair_q);
+  return c;
+}
+
+int sca_compact(const uint8_t* bev_mask, int64_t B, int64_t Ncam, int64_t Nq, int D, int32_t* hit_count,
+                int32_t* pair_offsets, int32_t* pair_q, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!bev_mask && Nq != 0) return fail(MSDA_ERR_INVALID_ARG, "bev_mask is null");
+  if (B < 1 || Ncam < 1 || D < 1 || Nq < 0) return fail(MSDA_ERR_INVALID_ARG, "B, Ncam and D must be positive");
+  if (Ncam > 32) return fail(MSDA_ERR_UNSUPPORTED, "Ncam=%lld: at most 32 cameras", (long long)Ncam);
+  if ((int64_t)D * Nq * Ncam * B >= ((int64_t)1 << 40)) return fail(MSDA_ERR_UNSUPPORTED, "bev_mask too large");
+  int rc = check_workspace(B, Ncam, Nq, workspace, workspace_bytes);
+  if (rc != MSDA_OK) return rc;
+  g_last_error[0] = '\0';
+  if (Nq == 0) return MSDA_OK;
+  const msda::CompactArgs c = compact_args(bev_mask, B, Ncam, Nq, D, hit_count, pair_offsets, pair_q, workspace);
+  return hip_status(msda::launch_sca_compact(c, msda::compact_layout(B, Ncam, Nq).tiles,
+                                             static_cast<hipStream_t>(stream)),
+                    "sca compaction launch");
+}
+
+int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes, const int64_t* level_start_index,
+               const float* reference_points_cam, const float* sampling_offsets, const float* attention_logits,
+               int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, int D, float* slots,
+               const int32_t* pair_offsets, const int32_t* pair_q, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  uint32_t image_bytes = 0;
+  int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, slots,
+                        &image_bytes);
+  if (rc != MSDA_OK) return rc;
+  if ((!reference_points_cam || !sampling_offsets || !attention_logits) && Nq != 0)
+    return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (B < 1 || Ncam < 1 || D < 1) return fail(MSDA_ERR_INVALID_ARG, "B, Ncam and D must be positive");
+  if (Ncam > 32) return fail(MSDA_ERR_UNSUPPORTED, "Ncam=%lld: at most 32 cameras", (long long)Ncam);
+  if (P % D != 0) return fail(MSDA_ERR_SHAPE, "P=%d is not a multiple of D=%d", P, D);
+  if (Nq != 0 && (!aligned(reference_points_cam, 8) || !aligned(sampling_offsets, 8)))
+    return fail(MSDA_ERR_INVALID_ARG, "reference_points_cam and sampling_offsets must be 8-byte aligned");
+  if (B * Nq * nH >= kI31 / 64) return fail(MSDA_ERR_UNSUPPORTED, "B*Nq*nH too large");
+  rc = check_workspace(B, Ncam, Nq, workspace, workspace_bytes);
+  if (rc != MSDA_OK) return rc;
+  g_last_error[0] = '\0';
+  if (Nq == 0) return MSDA_OK;
+  const msda::CompactArgs c = compact_args(nullptr, B, Ncam, Nq, D, nullptr, const_cast<int32_t*>(pair_offsets),
+                                           const_cast<int32_t*>(pair_q), workspace);
+  msda::GatherArgs a = {};
+  a.value = value;
+  a.image_bytes = image_bytes;
+  a.bf16 = value_dtype == MSDA_BF16;
+  a.shapes = spatial_shapes;
+  a.starts = level_start_index;
+  a.L = L;
+  a.P = P;
+  a.LP = L * P;
+  a.nH = nH;
+  a.Nv = (int)Nv;
+  a.inv_P = 1.0f / (float)P;
+  a.inv_D = 1.0f / (float)D;
+  a.rp = reference_points_cam;
+  a.offsets = sampling_offsets;
+  a.logits = attention_logits;
+  a.cammask = c.cammask;
+  a.pair_offsets = c.pair_offsets;
+  a.pair_q = c.pair_q;
+  a.Ncam = (int)Ncam;
+  a.D = D;
+  a.B = B;
+  a.Nq = Nq;
+  a.out = slots;
+  return hip_status(msda::launch_sca_gather(a, static_cast<hipStream_t>(stream)), "sca gather launch");
+}
+
+int sca_forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                const int64_t* level_start_index, const float* reference_points_cam, const uint8_t* bev_mask,
+                const float* sampling_offsets, const float* attention_logits, int64_t B, int64_t Ncam, int64_t Nv,
+                int64_t Nq, int nH, int Dh, int L, int P, int D, float* slots, int32_t* hit_count,
+                int32_t* pair_offsets, int32_t* pair_q, void* workspace, size_t workspace_bytes, void* stream) {
+  // check everything both stages check before enqueuing either
+  uint32_t image_bytes = 0;
+  int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, slots,
+                        &image_bytes);
+  if (rc != MSDA_OK) return rc;
+  if ((!reference_points_cam || !bev_mask || !sampling_offsets || !attention_logits) && Nq != 0)
+    return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (B < 1 || Ncam < 1 || D < 1) return fail(MSDA_ERR_INVALID_ARG, "B, Ncam and D must be positive");
+  if (Ncam > 32) return fail(MSDA_ERR_UNSUPPORTED, "Ncam=%lld: at most 32 cameras", (long long)Ncam);
+  if (P % D != 0) return fail(MSDA_ERR_SHAPE, "P=%d is not a multiple of D=%d", P, D);
+  if (Nq != 0 && (!aligned(reference_points_cam, 8) || !aligned(sampling_offsets, 8)))
+    return fail(MSDA_ERR_INVALID_ARG, "reference_points_cam and sampling_offsets must be 8-byte aligned");
+  rc = check_workspace(B, Ncam, Nq, workspace, workspace_bytes);
+  if (rc != MSDA_OK) return rc;
+  if (B * Nq * nH >= kI31 / 64) return fail(MSDA_ERR_UNSUPPORTED, "B*Nq*nH too large");
+  rc = sca_compact(bev_mask, B, Ncam, Nq, D, hit_count, pair_offsets, pair_q, workspace, workspace_bytes, stream);
+  if (rc != MSDA_OK) return rc;
+  return sca_gather(value, value_dtype, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets,
+                    attention_logits, B, Ncam, Nv, Nq, nH, Dh, L, P, D, slots, pair_offsets, pair_q, workspace,
+                    workspace_bytes, stream);
+}
+
+int msda_gemm_bf16(const void* X, int x_dtype, const uint16_t* W, const float* bias, void* Y, int y_dtype,
+                   int64_t M, int64_t N, int64_t K, void* stream) {
+  if (!X || !W || !Y) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if ((x_dtype != MSDA_F32 && x_dtype != MSDA_BF16) || (y_dtype != MSDA_F32 && y_dtype != MSDA_BF16))
+    return fail(MSDA_ERR_INVALID_ARG, "x_dtype and y_dtype must be MSDA_F32 or MSDA_BF16");
+  if (M < 0 || N < 1 || K < 1) return fail(MSDA_ERR_INVALID_ARG, "M >= 0, N >= 1 and K >= 1 required");
+  if (K % 32 != 0 || K > 256 || N % 16 != 0 || N > 65536 || M >= kI31)
+    return fail(MSDA_ERR_UNSUPPORTED, "needs K %% 32 == 0, K <= 256, N %% 16 == 0, N <= 65536, M < 2^31 "
+                "(got M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 16) || (bias && !aligned(bias, 4)))
+    return fail(MSDA_ERR_INVALID_ARG, "X, W and Y must be 16-byte aligned");
+  g_last_error[0] = '\0';
+  if (M == 0) return MSDA_OK;
+  msda::GemmArgs g = {};
+  g.X = X;
+  g.x_f32 = x_dtype == MSDA_F32;
+  g.W = W;
+  g.bias = bias;
+  g.Y = Y;
+  g.y_f32 = y_dtype == MSDA_F32;
+  g.M = M;
+  g.N = (int)N;
+  g.K = (int)K;
+  return hip_status(msda::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)), "gemm launch");
+}
+
+}  // extern "C"

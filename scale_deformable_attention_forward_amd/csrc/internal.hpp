@@ -1,0 +1,75 @@
+// Internal launcher interface between the C ABI (abi.hip) and the kernels.
+// Arguments are validated by the caller; launchers only size grids, enqueue
+// on `stream` and return the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msda {
+
+struct GatherArgs {
+  // value images: image i starts at value + i * image_bytes
+  const void* value;
+  uint32_t image_bytes;
+  int bf16;
+  // level table (device, int64) and sizes
+  const int64_t* shapes;
+  const int64_t* starts;
+  int L, P, LP, nH, Nv;
+  float inv_P, inv_D;
+  // MSDA / frames mode: image b*F + f; rows of locations and weights are
+  // indexed by ((b*F + f)*Nq + q)
+  const float* loc;
+  const float* weights;
+  int weight_logits;
+  int F;
+  // SCA mode: images b*Ncam + c; work list from the compaction
+  const float* rp;        // [Ncam][B][Nq][D][2]
+  const float* offsets;   // [B][Nq][nH][L][P][2]
+  const float* logits;    // [B][Nq][nH][L*P]
+  const uint32_t* cammask;  // [B][Nq] bit c = camera c sees the query
+  const int32_t* pair_offsets;  // [B*Ncam + 1]
+  const int32_t* pair_q;
+  int Ncam, D;
+  int64_t B, Nq;
+  float* out;  // [B][Nq][nH*32]
+};
+
+hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream);
+hipError_t launch_sca_gather(const GatherArgs& a, hipStream_t stream);
+
+// SCA compaction: workspace layout and launch.
+struct CompactLayout {
+  size_t cammask, tile_counts, tile_offsets, pair_offsets, pair_q, total;
+  int tiles;  // tiles of the query axis per (b, c)
+};
+CompactLayout compact_layout(int64_t B, int64_t Ncam, int64_t Nq);
+
+struct CompactArgs {
+  const uint8_t* bev_mask;
+  int B, Ncam, Nq, D;
+  uint32_t* cammask;
+  int32_t* hit_count;  // may be null
+  int32_t* tile_counts;
+  int32_t* tile_offsets;
+  int32_t* pair_offsets;
+  int32_t* pair_q;
+};
+hipError_t launch_sca_compact(const CompactArgs& a, int tiles, hipStream_t stream);
+
+// bf16 GEMM on MFMA: Y = X W^T + bias
+struct GemmArgs {
+  const void* X;
+  int x_f32;
+  const uint16_t* W;
+  const float* bias;
+  void* Y;
+  int y_f32;
+  int64_t M;
+  int N, K;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace msda

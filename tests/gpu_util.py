@@ -1,0 +1,76 @@
+"""Helpers for the GPU parity tests: device copies and the tolerances.
+
+Tolerances (written out here, used by every GPU test):
+  fp32 path:  |gpu - oracle| <= 1e-5 * |oracle| + 1e-5 * rms(oracle), element-wise
+              (relative 1e-5; the rms term keeps outputs near zero from
+              demanding more than float32 can hold);
+  bf16 value: |gpu - oracle| <= 1e-2 absolute (unit-scale data, fp32 accumulation);
+  bf16 projection output: |gpu - oracle| <= 2^-7 * |oracle| + 1e-5 (one bf16
+              unit in the last place: fp32 accumulation may move a value
+              across a rounding boundary of the final bf16 rounding);
+  integers (hit counts, pair lists): bit-exact.
+"""
+import sys
+
+import numpy as np
+import torch
+
+
+def announce(msg):
+    """Name the case on the real stderr before a GPU step (survives capture)."""
+    sys.__stderr__.write(f"[gpu case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def dev(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:  # bf16 bit patterns
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    t = torch.from_numpy(a)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def host(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+def bf16_bits_to_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_fp32_close(got, ref, what):
+    got = np.asarray(got, np.float64).reshape(-1)
+    ref = np.asarray(ref, np.float64).reshape(-1)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    err = np.abs(got - ref)
+    tol = 1e-5 * np.abs(ref) + 1e-5 * rms
+    bad = err > tol
+    nrm = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    assert not bad.any(), (f"{what}: {int(bad.sum())}/{bad.size} elements beyond 1e-5 rel; max err "
+                           f"{err.max():.3g} at ref {ref[np.argmax(err)]:.4g}; rms {rms:.3g}; normwise {nrm:.3g}")
+    return nrm
+
+
+def assert_abs_close(got, ref, atol, what):
+    got = np.asarray(got, np.float64).reshape(-1)
+    ref = np.asarray(ref, np.float64).reshape(-1)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    assert not (err > atol).any(), f"{what}: max abs err {err.max():.3g} > {atol}"
+    return float(err.max()) if err.size else 0.0
+
+
+def assert_bf16_ulp_close(got_bits, ref, what):
+    got = bf16_bits_to_f64(got_bits).reshape(-1)
+    ref = np.asarray(ref, np.float64).reshape(-1)
+    err = np.abs(got - ref)
+    tol = 2.0 ** -7 * np.abs(ref) + 1e-5
+    bad = err > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())}/{bad.size} beyond one bf16 ulp; max err {err.max():.3g}"

@@ -487,6 +487,7 @@ def pin_linear_bf16():
     W = tobf(g.normal(size=(N, K)))
     bias = g.normal(size=N).astype(np.float32)
     _close(oracle.linear_bf16(X, W, bias), dec(X) @ dec(W).T + bias.astype(np.float64), 1e-13, "matmul")
+    _close(oracle.linear_bf16_blas(X, W, bias), oracle.linear_bf16(X, W, bias), 1e-13, "blas form = loops")
     eye = tobf(np.eye(K))
     _close(oracle.linear_bf16(X, eye), dec(X), 0.0, "identity")
     Xf = g.normal(size=(M, K)).astype(np.float32)

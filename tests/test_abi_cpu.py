@@ -1,0 +1,177 @@
+"""libmsda.so on a machine without a GPU: the library loads, exports every
+entry point include/msda.h declares, and rejects bad arguments with the
+documented status before touching any device (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msda.h")
+
+OK, INVALID, UNSUPPORTED, SHAPE, WORKSPACE, HIP = 0, 1, 2, 3, 4, 5
+
+_p, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+# fake, never dereferenced, suitably aligned addresses: every call below must
+# fail validation before any access
+A = 0x10000
+B_ = 0x20000
+MIS = 0x10004  # 4-byte but not 16-byte aligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import scale_deformable_attention_forward_amd as m
+    if not os.path.exists(m.library_path()):
+        from scale_deformable_attention_forward_amd import build
+        build.build()
+    return m.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["msda_forward", "msda_forward_frames", "sca_workspace_size", "sca_forward", "msda_gemm_bf16",
+              "msda_status_string", "msda_last_error"]:
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in msda.h but not exported"
+
+
+def test_status_strings(lib):
+    for code, name in [(OK, "MSDA_OK"), (INVALID, "MSDA_ERR_INVALID_ARG"), (UNSUPPORTED, "MSDA_ERR_UNSUPPORTED"),
+                       (SHAPE, "MSDA_ERR_SHAPE"), (WORKSPACE, "MSDA_ERR_WORKSPACE"), (HIP, "MSDA_ERR_HIP")]:
+        assert lib.msda_status_string(code).decode() == name
+    assert lib.msda_status_string(99).decode() == "MSDA_ERR_UNKNOWN"
+
+
+def _msda(lib, value=A, dtype=0, shapes=A, starts=A, loc=A, w=A, mode=1, B=1, Nv=16, Nq=4, nH=8, Dh=32, L=1,
+          P=4, out=B_):
+    return lib.msda_forward(value, dtype, shapes, starts, loc, w, mode, B, Nv, Nq, nH, Dh, L, P, out, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(value=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(loc=None), INVALID),
+    (dict(dtype=7), INVALID),
+    (dict(mode=3), INVALID),
+    (dict(B=0), INVALID),
+    (dict(Nv=0), INVALID),
+    (dict(nH=0), INVALID),
+    (dict(Dh=16), UNSUPPORTED),
+    (dict(L=5, P=13), UNSUPPORTED),
+    (dict(nH=65), UNSUPPORTED),
+    (dict(value=MIS), INVALID),
+    (dict(loc=A + 4), INVALID),
+    (dict(Nv=1 << 31), UNSUPPORTED),
+    (dict(Nv=1 << 21, nH=8), UNSUPPORTED),  # 2^21 * 8 * 32 * 4 bytes = 2 GiB per image
+])
+def test_msda_forward_rejects(lib, kw, code):
+    assert _msda(lib, **kw) == code
+    assert lib.msda_last_error().decode() != ""
+
+
+def test_msda_forward_empty_query_set_is_a_no_op(lib):
+    assert _msda(lib, Nq=0) == OK
+    # with no queries the per-query buffers may be null (torch gives null for empty tensors)
+    assert _msda(lib, Nq=0, out=None, loc=None, w=None) == OK
+    assert _msda(lib, Nq=4, out=None) == INVALID
+
+
+def test_msda_forward_frames_rejects(lib):
+    f = lib.msda_forward_frames
+    assert f(A, 0, A, A, A, A, 1, 1, 0, 16, 4, 8, 32, 1, 4, B_, None) == INVALID  # F = 0
+    assert f(A, 0, A, A, A, A, 1, 1, 2, 16, 4, 8, 64, 1, 4, B_, None) == UNSUPPORTED
+    assert f(A, 0, A, A, A, A, 1, 1, 2, 16, 0, 8, 32, 1, 4, B_, None) == OK  # nothing to do
+
+
+def test_sca_workspace_size(lib):
+    n = _sz(0)
+    assert lib.sca_workspace_size(1, 6, 40000, ctypes.byref(n)) == OK
+    small = n.value
+    assert small >= 4 * 40000 + 4 * 6 * 40000  # camera masks + pair lists at least
+    assert lib.sca_workspace_size(4, 6, 40000, ctypes.byref(n)) == OK
+    assert n.value > small
+    assert lib.sca_workspace_size(0, 6, 10, ctypes.byref(n)) == INVALID
+    assert lib.sca_workspace_size(1, 6, 10, None) == INVALID
+    assert lib.sca_workspace_size(1 << 20, 32, 1 << 20, ctypes.byref(n)) == UNSUPPORTED
+
+
+def _sca(lib, value=A, dtype=0, B=1, Ncam=6, Nv=16, Nq=8, nH=8, Dh=32, L=1, P=8, D=4, slots=B_, ws=A,
+         ws_bytes=1 << 30, rp=A, mask=A, off=A, logits=A):
+    return lib.sca_forward(value, dtype, A, A, rp, mask, off, logits, B, Ncam, Nv, Nq, nH, Dh, L, P, D, slots,
+                           None, None, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), INVALID),
+    (dict(slots=None), INVALID),
+    (dict(Ncam=0), INVALID),
+    (dict(D=0), INVALID),
+    (dict(Ncam=33), UNSUPPORTED),
+    (dict(P=6, D=4), SHAPE),
+    (dict(ws=None), WORKSPACE),
+    (dict(ws_bytes=16), WORKSPACE),
+    (dict(ws=A + 16), WORKSPACE),
+    (dict(rp=A + 4), INVALID),
+    (dict(Dh=64), UNSUPPORTED),
+    (dict(dtype=2), INVALID),
+])
+def test_sca_forward_rejects(lib, kw, code):
+    assert _sca(lib, **kw) == code
+
+
+def test_sca_forward_empty_query_set_is_a_no_op(lib):
+    assert _sca(lib, Nq=0) == OK
+    assert _sca(lib, Nq=0, slots=None, rp=None, mask=None, off=None, logits=None) == OK
+    assert _sca(lib, Nq=3, slots=None) == INVALID
+
+
+def test_sca_stages_reject(lib):
+    n = _sz(0)
+    assert lib.sca_workspace_size(1, 6, 8, ctypes.byref(n)) == OK
+    assert lib.sca_compact(None, 1, 6, 8, 4, None, None, None, A, n.value, None) == INVALID
+    assert lib.sca_compact(A, 1, 33, 8, 4, None, None, None, A, n.value, None) == UNSUPPORTED
+    assert lib.sca_compact(A, 1, 6, 8, 4, None, None, None, A, n.value - 1, None) == WORKSPACE
+    assert lib.sca_compact(A, 1, 6, 0, 4, None, None, None, A, n.value, None) == OK
+    g = lib.sca_gather
+    assert g(A, 0, A, A, A, A, A, 1, 6, 16, 8, 8, 32, 1, 6, 4, B_, None, None, A, n.value, None) == SHAPE
+    assert g(A, 0, A, A, A, A, A, 1, 6, 16, 8, 8, 32, 1, 8, 4, B_, None, None, None, n.value, None) == WORKSPACE
+    assert g(A, 0, A, A, None, A, A, 1, 6, 16, 8, 8, 32, 1, 8, 4, B_, None, None, A, n.value, None) == INVALID
+
+
+@pytest.mark.parametrize("M,N,K,code", [
+    (10, 256, 48, UNSUPPORTED),
+    (10, 256, 512, UNSUPPORTED),
+    (10, 24, 256, UNSUPPORTED),
+    (-1, 256, 256, INVALID),
+    (0, 256, 256, OK),
+])
+def test_gemm_rejects(lib, M, N, K, code):
+    assert lib.msda_gemm_bf16(A, 1, A, None, B_, 1, M, N, K, None) == code
+
+
+def test_gemm_rejects_null_and_dtype(lib):
+    assert lib.msda_gemm_bf16(None, 1, A, None, B_, 1, 4, 256, 256, None) == INVALID
+    assert lib.msda_gemm_bf16(A, 5, A, None, B_, 1, 4, 256, 256, None) == INVALID
+    assert lib.msda_gemm_bf16(MIS, 1, A, None, B_, 1, 4, 256, 256, None) == INVALID
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import scale_deformable_attention_forward_amd as m
+    v = torch.zeros(1, 16, 8, 32)
+    with pytest.raises(ValueError):
+        m.msda_forward(v, torch.zeros(1, 2, dtype=torch.int64), torch.zeros(1, dtype=torch.int64),
+                       torch.zeros(1, 4, 8, 1, 4, 2), torch.zeros(1, 4, 8, 4))
