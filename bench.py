@@ -102,11 +102,11 @@ def sca_workload(bf16=False):
     wl.w = w
 
     def compact():
-        m.sca_compact(d["bev_mask"], ws, hit_count=hit, pair_offsets=offs, pair_q=pq)
+        m.sca_compact(d["bev_mask"], d["reference_points_cam"], ws, hit_count=hit, pair_offsets=offs, pair_q=pq)
 
     def gather():
         m.sca_gather(d["value"], d["spatial_shapes"], d["level_start_index"], d["reference_points_cam"],
-                     d["sampling_offsets"], d["attention_logits"], ws, slots=slots, pair_offsets=offs, pair_q=pq)
+                     d["sampling_offsets"], d["attention_logits"], ws, slots=slots)
 
     wl.pre, wl.kernel = compact, gather
 
@@ -118,9 +118,9 @@ def sca_workload(bf16=False):
         wl.samples = samples
         # effective bytes of one gather launch: 4 nominal corners x 32 channels
         # per sample, the per-query offsets and logits, the anchors of each
-        # pair, the camera masks and pair list, and the output rows
+        # pair, the camera masks and work list, and the output rows
         wl.eff_bytes = (samples * 4 * 32 * elem + B * Nq * nH * L * P * (8 + 4) + n_pairs * D * 8
-                        + B * Nq * 4 + n_pairs * 4 + B * Nq * nH * 32 * 4)
+                        + B * Nq * (4 + 4) + B * Nq * nH * 32 * 4)
         wl.gathered_bytes = samples * 4 * 32 * elem
     wl.finish = finish
     wl.config = {"workload": "BEVFormer-base spatial cross-attention layer, 6 cameras",

@@ -160,28 +160,31 @@ int sca_forward(const void* value, int value_dtype, const int64_t* spatial_shape
 /*
  * Stage 1 of sca_forward on its own: visibility, hit counts and the pair
  * lists ([SCA-note] rebatch and count), written to hit_count / pair_offsets /
- * pair_q when given and always to the workspace.  Since the camera masks do
- * not change between the encoder layers of one frame, one sca_compact can
- * serve several sca_gather calls.
- *   bev_mask, hit_count, pair_offsets, pair_q, workspace: as sca_forward.
+ * pair_q when given, and the work list of stage 2, always in the workspace:
+ * every seen query once, grouped by its first camera and by the image tile
+ * of that camera's first marked anchor, so that neighbouring work items read
+ * neighbouring value rows (reference_points_cam is read for this only).
+ * Since the camera masks and anchors do not change between the encoder
+ * layers of one frame, one sca_compact can serve several sca_gather calls.
+ *   bev_mask, reference_points_cam, hit_count, pair_offsets, pair_q,
+ *   workspace: as sca_forward.
  * Limits: 1 <= Ncam <= 32, D >= 1, B*Ncam*Nq < 2^31.
  */
-int sca_compact(const uint8_t* bev_mask, int64_t B, int64_t Ncam, int64_t Nq, int D, int32_t* hit_count,
-                int32_t* pair_offsets, int32_t* pair_q, void* workspace, size_t workspace_bytes, void* stream);
+int sca_compact(const uint8_t* bev_mask, const float* reference_points_cam, int64_t B, int64_t Ncam, int64_t Nq,
+                int D, int32_t* hit_count, int32_t* pair_offsets, int32_t* pair_q, void* workspace,
+                size_t workspace_bytes, void* stream);
 
 /*
- * Stage 2 of sca_forward on its own: steps 2 and 3 for every pair that
- * sca_compact listed.  The workspace must hold what sca_compact wrote for the
- * same (B, Ncam, Nq), enqueued before on the same stream (or otherwise
- * ordered before this call), and pair_offsets / pair_q must be the buffers
- * given to that sca_compact (NULL if it was given NULL).  slots is fully
- * overwritten.  Other arguments as sca_forward.  One kernel launch.
+ * Stage 2 of sca_forward on its own: steps 2 and 3 for every query on the
+ * work list of the workspace.  The workspace must hold what sca_compact
+ * wrote for the same (B, Ncam, Nq) and the same masks and anchors, enqueued
+ * before on the same stream (or otherwise ordered before this call).  slots
+ * is fully overwritten.  Other arguments as sca_forward.  One kernel launch.
  */
 int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes, const int64_t* level_start_index,
                const float* reference_points_cam, const float* sampling_offsets, const float* attention_logits,
                int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, int D, float* slots,
-               const int32_t* pair_offsets, const int32_t* pair_q, void* workspace, size_t workspace_bytes,
-               void* stream);
+               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Dense projection on matrix cores, bf16 operands and float32 accumulation:

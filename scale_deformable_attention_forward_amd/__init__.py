@@ -59,9 +59,9 @@ def load_library():
     lib.sca_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
     lib.sca_forward.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int,
                                 _int, _p, _p, _p, _p, _p, _sz, _p]
-    lib.sca_compact.argtypes = [_p, _i64, _i64, _i64, _int, _p, _p, _p, _p, _sz, _p]
+    lib.sca_compact.argtypes = [_p, _p, _i64, _i64, _i64, _int, _p, _p, _p, _p, _sz, _p]
     lib.sca_gather.argtypes = [_p, _int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _int,
-                               _p, _p, _p, _p, _sz, _p]
+                               _p, _p, _sz, _p]
     lib.msda_gemm_bf16.argtypes = [_p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p]
     for f in (lib.msda_forward, lib.msda_forward_frames, lib.sca_workspace_size, lib.sca_forward,
               lib.sca_compact, lib.sca_gather, lib.msda_gemm_bf16):
@@ -201,14 +201,17 @@ def sca_forward(value, spatial_shapes, level_start_index, reference_points_cam, 
     return slots
 
 
-def sca_compact(bev_mask, workspace, hit_count=None, pair_offsets=None, pair_q=None, stream=None):
-    """Stage 1 of sca_forward: bev_mask uint8|bool [Ncam,B,Nq,D] -> camera
-    masks and pair lists in `workspace` (and hit_count / pair_offsets /
+def sca_compact(bev_mask, reference_points_cam, workspace, hit_count=None, pair_offsets=None, pair_q=None,
+                stream=None):
+    """Stage 1 of sca_forward: bev_mask uint8|bool [Ncam,B,Nq,D] and
+    reference_points_cam float32 [Ncam,B,Nq,D,2] -> camera masks, pair lists
+    and the ordered work list in `workspace` (and hit_count / pair_offsets /
     pair_q when given)."""
     lib = load_library()
     Ncam, B, Nq, D = bev_mask.shape
     i32 = (torch.int32,)
-    rc = lib.sca_compact(_ptr(bev_mask, "bev_mask", (torch.uint8, torch.bool)), B, Ncam, Nq, D,
+    rc = lib.sca_compact(_ptr(bev_mask, "bev_mask", (torch.uint8, torch.bool)),
+                         _ptr(reference_points_cam, "reference_points_cam", _F32), B, Ncam, Nq, D,
                          _ptr(hit_count, "hit_count", i32), _ptr(pair_offsets, "pair_offsets", i32),
                          _ptr(pair_q, "pair_q", i32), _ptr(workspace, "workspace"),
                          workspace.numel() * workspace.element_size(), _stream(stream, bev_mask.device))
@@ -216,9 +219,9 @@ def sca_compact(bev_mask, workspace, hit_count=None, pair_offsets=None, pair_q=N
 
 
 def sca_gather(value, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets, attention_logits,
-               workspace, slots=None, pair_offsets=None, pair_q=None, stream=None):
+               workspace, slots=None, stream=None):
     """Stage 2 of sca_forward: gather, weighted sums and camera mean for the
-    pairs the preceding sca_compact on `workspace` listed."""
+    queries on the work list the preceding sca_compact left in `workspace`."""
     lib = load_library()
     B, Ncam, Nv, nH, Dh = value.shape
     _, _, Nq, D, _ = reference_points_cam.shape
@@ -226,14 +229,12 @@ def sca_gather(value, spatial_shapes, level_start_index, reference_points_cam, s
     dev = value.device
     if slots is None:
         slots = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=dev)
-    i32 = (torch.int32,)
     rc = lib.sca_gather(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
                         _ptr(level_start_index, "level_start_index", _I64),
                         _ptr(reference_points_cam, "reference_points_cam", _F32),
                         _ptr(sampling_offsets, "sampling_offsets", _F32),
                         _ptr(attention_logits, "attention_logits", _F32), B, Ncam, Nv, Nq, nH, Dh, L, P, D,
-                        _ptr(slots, "slots", _F32), _ptr(pair_offsets, "pair_offsets", i32),
-                        _ptr(pair_q, "pair_q", i32), _ptr(workspace, "workspace"),
+                        _ptr(slots, "slots", _F32), _ptr(workspace, "workspace"),
                         workspace.numel() * workspace.element_size(), _stream(stream, dev))
     _check("sca_gather", rc)
     return slots

@@ -146,28 +146,37 @@ static int check_workspace(int64_t B, int64_t Ncam, int64_t Nq, const void* work
   return MSDA_OK;
 }
 
-static msda::CompactArgs compact_args(const uint8_t* bev_mask, int64_t B, int64_t Ncam, int64_t Nq, int D,
-                                      int32_t* hit_count, int32_t* pair_offsets, int32_t* pair_q, void* workspace) {
+static msda::CompactArgs compact_args(const uint8_t* bev_mask, const float* reference_points_cam, int64_t B,
+                                      int64_t Ncam, int64_t Nq, int D, int32_t* hit_count, int32_t* pair_offsets,
+                                      int32_t* pair_q, void* workspace) {
   const msda::CompactLayout lay = msda::compact_layout(B, Ncam, Nq);
   char* ws = static_cast<char*>(workspace);
   msda::CompactArgs c = {};
   c.bev_mask = bev_mask;
+  c.rp = reference_points_cam;
   c.B = (int)B;
   c.Ncam = (int)Ncam;
   c.Nq = (int)Nq;
   c.D = D;
   c.cammask = reinterpret_cast<uint32_t*>(ws + lay.cammask);
+  c.qkey = reinterpret_cast<int32_t*>(ws + lay.qkey);
   c.hit_count = hit_count;
   c.tile_counts = reinterpret_cast<int32_t*>(ws + lay.tile_counts);
   c.tile_offsets = reinterpret_cast<int32_t*>(ws + lay.tile_offsets);
   c.pair_offsets = pair_offsets ? pair_offsets : reinterpret_cast<int32_t*>(ws + lay.pair_offsets);
   c.pair_q = pair_q ? pair_q : reinterpret_cast<int32_t*>(ws + lay.pair_q);
+  c.bin_hist = reinterpret_cast<int32_t*>(ws + lay.bin_hist);
+  c.bin_offsets = reinterpret_cast<int32_t*>(ws + lay.bin_offsets);
+  c.order = reinterpret_cast<int32_t*>(ws + lay.order);
   return c;
 }
 
-int sca_compact(const uint8_t* bev_mask, int64_t B, int64_t Ncam, int64_t Nq, int D, int32_t* hit_count,
-                int32_t* pair_offsets, int32_t* pair_q, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!bev_mask && Nq != 0) return fail(MSDA_ERR_INVALID_ARG, "bev_mask is null");
+int sca_compact(const uint8_t* bev_mask, const float* reference_points_cam, int64_t B, int64_t Ncam, int64_t Nq,
+                int D, int32_t* hit_count, int32_t* pair_offsets, int32_t* pair_q, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if ((!bev_mask || !reference_points_cam) && Nq != 0) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (Nq != 0 && !aligned(reference_points_cam, 8))
+    return fail(MSDA_ERR_INVALID_ARG, "reference_points_cam must be 8-byte aligned");
   if (B < 1 || Ncam < 1 || D < 1 || Nq < 0) return fail(MSDA_ERR_INVALID_ARG, "B, Ncam and D must be positive");
   if (Ncam > 32) return fail(MSDA_ERR_UNSUPPORTED, "Ncam=%lld: at most 32 cameras", (long long)Ncam);
   if ((int64_t)D * Nq * Ncam * B >= ((int64_t)1 << 40)) return fail(MSDA_ERR_UNSUPPORTED, "bev_mask too large");
@@ -175,7 +184,8 @@ int sca_compact(const uint8_t* bev_mask, int64_t B, int64_t Ncam, int64_t Nq, in
   if (rc != MSDA_OK) return rc;
   g_last_error[0] = '\0';
   if (Nq == 0) return MSDA_OK;
-  const msda::CompactArgs c = compact_args(bev_mask, B, Ncam, Nq, D, hit_count, pair_offsets, pair_q, workspace);
+  const msda::CompactArgs c =
+      compact_args(bev_mask, reference_points_cam, B, Ncam, Nq, D, hit_count, pair_offsets, pair_q, workspace);
   return hip_status(msda::launch_sca_compact(c, msda::compact_layout(B, Ncam, Nq).tiles,
                                              static_cast<hipStream_t>(stream)),
                     "sca compaction launch");
@@ -184,8 +194,7 @@ int sca_compact(const uint8_t* bev_mask, int64_t B, int64_t Ncam, int64_t Nq, in
 int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes, const int64_t* level_start_index,
                const float* reference_points_cam, const float* sampling_offsets, const float* attention_logits,
                int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, int D, float* slots,
-               const int32_t* pair_offsets, const int32_t* pair_q, void* workspace, size_t workspace_bytes,
-               void* stream) {
+               void* workspace, size_t workspace_bytes, void* stream) {
   uint32_t image_bytes = 0;
   int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, slots,
                         &image_bytes);
@@ -202,8 +211,7 @@ int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes
   if (rc != MSDA_OK) return rc;
   g_last_error[0] = '\0';
   if (Nq == 0) return MSDA_OK;
-  const msda::CompactArgs c = compact_args(nullptr, B, Ncam, Nq, D, nullptr, const_cast<int32_t*>(pair_offsets),
-                                           const_cast<int32_t*>(pair_q), workspace);
+  const msda::CompactArgs c = compact_args(nullptr, nullptr, B, Ncam, Nq, D, nullptr, nullptr, nullptr, workspace);
   msda::GatherArgs a = {};
   a.value = value;
   a.image_bytes = image_bytes;
@@ -221,8 +229,8 @@ int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes
   a.offsets = sampling_offsets;
   a.logits = attention_logits;
   a.cammask = c.cammask;
-  a.pair_offsets = c.pair_offsets;
-  a.pair_q = c.pair_q;
+  a.order = c.order;
+  a.n_order = c.bin_offsets + B * Ncam * msda::kOrderBins;
   a.Ncam = (int)Ncam;
   a.D = D;
   a.B = B;
@@ -251,11 +259,11 @@ int sca_forward(const void* value, int value_dtype, const int64_t* spatial_shape
   rc = check_workspace(B, Ncam, Nq, workspace, workspace_bytes);
   if (rc != MSDA_OK) return rc;
   if (B * Nq * nH >= kI31 / 64) return fail(MSDA_ERR_UNSUPPORTED, "B*Nq*nH too large");
-  rc = sca_compact(bev_mask, B, Ncam, Nq, D, hit_count, pair_offsets, pair_q, workspace, workspace_bytes, stream);
+  rc = sca_compact(bev_mask, reference_points_cam, B, Ncam, Nq, D, hit_count, pair_offsets, pair_q, workspace,
+                   workspace_bytes, stream);
   if (rc != MSDA_OK) return rc;
   return sca_gather(value, value_dtype, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets,
-                    attention_logits, B, Ncam, Nv, Nq, nH, Dh, L, P, D, slots, pair_offsets, pair_q, workspace,
-                    workspace_bytes, stream);
+                    attention_logits, B, Ncam, Nv, Nq, nH, Dh, L, P, D, slots, workspace, workspace_bytes, stream);
 }
 
 int msda_gemm_bf16(const void* X, int x_dtype, const uint16_t* W, const float* bias, void* Y, int y_dtype,

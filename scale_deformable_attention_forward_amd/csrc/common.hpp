@@ -13,8 +13,15 @@ constexpr int kXcds = 8;   // MI355X: 8 accelerator dies, each with its own L2
 // or beyond `bytes` returns zeros and makes no memory request, which is how
 // corners outside the map are skipped without a branch.  Word 3 is the gfx9
 // data-format word for untyped 32-bit accesses.
+// The base must be the same in every lane; it is read from the first active
+// lane so that the compiler keeps the descriptor in scalar registers (a
+// descriptor it cannot prove uniform costs a readfirstlane loop per load).
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // Order LDS traffic between the lanes of one wavefront: everything written
@@ -27,6 +34,12 @@ __device__ inline void wave_lds_sync() {
 }
 
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline uint32_t uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ inline int64_t uniform(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Work split for a grid whose size is a multiple of kXcds.  The hardware
 // hands workgroups to the dies round-robin (block i -> die i % 8), so die x

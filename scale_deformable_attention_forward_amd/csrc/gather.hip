@@ -15,20 +15,22 @@
 //     SCA) and up to 8 heads at a time: lane group g = lane / 8 is head
 //     hb + g, and lane j = lane % 8 of the group owns channels 4j..4j+3;
 //   - staging: lane j of group g computes samples k = j, j+8, ... of its head
-//     (softmax, location, the four corners) and writes one (row offset,
-//     weight) pair per corner to LDS; corners outside the map get an offset
-//     past the end of the image and weight 0;
-//   - gather: the group walks its 4*L*P corner rows; per row its 8 lanes read
-//     one 128-byte (fp32) or 64-byte (bf16) head row with one 16- or 8-byte
-//     buffer load each (a skipped corner's load returns zeros and makes no
-//     memory request) and accumulate weight * row into 4 fp32 registers.  A
-//     wave-wide load instruction thus fetches one row for each of 8 heads; no
-//     cross-lane reduction is needed, and the 8 groups' output chunks form
-//     one contiguous 1 KB store per row;
+//     (softmax, location); samples with a corner that can lie inside the map
+//     are live, and the four corners of each live sample become (row
+//     offset, weight) pairs packed densely into the group's LDS area (prefix
+//     sum over its 8 lanes), so samples entirely outside the map cost
+//     nothing later;
+//   - gather: all groups walk the same number of rows (the largest count in
+//     the wave, rounded up to 8; short groups are padded with rows whose
+//     offset lies past the image, which buffer loads turn into zeros without
+//     a memory request).  Per row the group's 8 lanes read one 128-byte
+//     (fp32) or 64-byte (bf16) head row with one 16- or 8-byte buffer load
+//     each and accumulate weight * row into 4 fp32 registers.  A wave-wide
+//     load thus fetches one row for each of 8 heads; no cross-lane reduction
+//     is needed, and the 8 groups' output chunks form one contiguous store;
 //   - the sample geometry (x, y, floor, row index) is computed in fp64 so
 //     that the interpolation fractions are exact to fp32 rounding;
 //     interpolation weights, softmax and accumulation are fp32.
-#include <climits>
 #include <cmath>
 
 #include "common.hpp"
@@ -36,23 +38,28 @@
 
 namespace msda {
 
-constexpr int kHeadSlots = 8;      // heads per wave pass
-constexpr int kSamplesPerLane = 8; // L*P <= 64 = 8 lanes x 8
-constexpr int kUnroll = 8;         // corner rows in flight per lane
+constexpr int kHeadSlots = 8;  // heads per wave pass
+constexpr int kBatch = 8;      // corner rows per load batch
 constexpr int kMaxWavesPerBlock = 4;
 constexpr size_t kMaxBlockLds = 64 * 1024;
 constexpr int kMaxLevels = 64;
 constexpr uint32_t kSkip = 0x80000000u;  // beyond every image (images < 2^31 bytes)
+// samples per lane (template kSPL): 4 when L*P <= 32, 8 when L*P <= 64
 
 struct Level {
   int W, H;
   long long start;
 };
 
-__host__ __device__ inline int rows_padded(int LP) { return (4 * LP + kUnroll - 1) / kUnroll * kUnroll; }
+__host__ __device__ inline int rows_padded(int LP) { return (4 * LP + kBatch - 1) / kBatch * kBatch; }
 // per-head stride of the LDS staging area, in (offset, weight) pairs; odd, so
 // that the 8 groups of a wave hit different LDS banks
 __host__ __device__ inline int meta_stride(int LP) { return rows_padded(LP) + 1; }
+
+// k / n for 0 <= k < 2^16 and 1 <= n <= 64, with inv = 1/n in fp32: the
+// quotient sits at least 0.5/n away from the next integer, far beyond the
+// rounding error of (k + 1/2) * inv.
+__device__ inline int small_div(int k, float inv) { return (int)((k + 0.5f) * inv); }
 
 __device__ inline float group_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 1, 8));
@@ -67,11 +74,12 @@ __device__ inline float group_sum(float v) {
 
 // Weights of the samples k = j + 8i of one head: probabilities as given, or
 // softmax over the head's L*P logits, reduced across the 8 lanes of a group.
-__device__ inline void head_weights(const float* __restrict__ w_row, bool head_ok, int LP, int j,
-                                    bool logits, float (&alpha)[kSamplesPerLane]) {
+template <int kSPL>
+__device__ inline void head_weights(const float* __restrict__ w_row, bool head_ok, int LP, int j, bool logits,
+                                    float (&alpha)[kSPL]) {
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kSamplesPerLane; ++i) {
+  for (int i = 0; i < kSPL; ++i) {
     const int k = j + 8 * i;
     alpha[i] = (head_ok && k < LP) ? w_row[k] : 0.f;
     if (head_ok && k < LP) m = fmaxf(m, alpha[i]);
@@ -80,7 +88,7 @@ __device__ inline void head_weights(const float* __restrict__ w_row, bool head_o
   m = group_max(m);
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < kSamplesPerLane; ++i) {
+  for (int i = 0; i < kSPL; ++i) {
     const int k = j + 8 * i;
     const float e = (head_ok && k < LP) ? expf(alpha[i] - m) : 0.f;
     alpha[i] = e;
@@ -89,14 +97,14 @@ __device__ inline void head_weights(const float* __restrict__ w_row, bool head_o
   s = group_sum(s);
   const float inv = head_ok ? 1.0f / s : 0.f;
 #pragma unroll
-  for (int i = 0; i < kSamplesPerLane; ++i) alpha[i] *= inv;
+  for (int i = 0; i < kSPL; ++i) alpha[i] *= inv;
 }
 
 // The four corners of one sample at continuous level coordinate (x, y):
-// (row offset in bytes within the image, alpha * bilinear weight), written
-// to rows 4k .. 4k+3 of the group's staging area.
-__device__ inline void stage_corners(uint2* __restrict__ rows, int k, double x, double y, float alpha,
-                                     const Level& lv, bool live, int h, int nH, int Nv, uint32_t row_bytes) {
+// (row offset in bytes within the image, alpha * bilinear weight), with
+// offset kSkip for corners outside the level or outside [0, Nv).
+__device__ inline void sample_corners(uint2 (&c)[4], double x, double y, float alpha, const Level& lv, bool live,
+                                      int h, int nH, int Nv, uint32_t row_bytes) {
   // beyond [-2, size+1] every corner is outside anyway; clamping keeps the
   // integer conversions in range (and sends NaN to -2)
   x = fmin(fmax(x, -2.0), (double)lv.W + 1.0);
@@ -114,53 +122,96 @@ __device__ inline void stage_corners(uint2* __restrict__ rows, int k, double x, 
       const int cx = ix + dx, cy = iy + dy;
       const long long pix = base + (long long)dy * lv.W + dx;
       const bool ok = live && cx >= 0 && cx < lv.W && cy >= 0 && cy < lv.H && pix >= 0 && pix < Nv;
-      const uint32_t off = ok ? (uint32_t)((pix * nH + h) * (long long)row_bytes) : kSkip;
-      const float w = ok ? alpha * wx[dx] * wy[dy] : 0.f;
-      rows[4 * k + 2 * dy + dx] = make_uint2(off, __float_as_uint(w));
+      c[2 * dy + dx] = ok ? make_uint2((uint32_t)((pix * nH + h) * (long long)row_bytes),
+                                       __float_as_uint(alpha * wx[dx] * wy[dy]))
+                          : make_uint2(kSkip, 0u);
     }
   }
 }
 
-// Accumulate weight * value row over the group's staged corner rows.
+// A sample is live when at least one of its corners can lie inside the map:
+// -1 <= x < W and -1 <= y < H (a live sample may still contribute nothing;
+// a dead one never does).
+__device__ inline bool sample_live(double x, double y, const Level& lv) {
+  return x >= -1.0 && x < (double)lv.W && y >= -1.0 && y < (double)lv.H;
+}
+
+// Write the four corner rows of the group's live samples densely into `rows`
+// (lane order, then sample order; a prefix sum over the group's 8 lanes
+// places each lane) and pad every group of the wave with skipped rows up to
+// the wave's largest count rounded up to kBatch.  Returns that row count
+// (the same in every lane).  Dead samples cost no row at all.
+template <int kSPL>
+__device__ inline int stage_rows(uint2* __restrict__ rows, const double (&xs)[kSPL], const double (&ys)[kSPL],
+                                 const float (&alpha)[kSPL], uint32_t live, const Level* lv, float inv_P, int j,
+                                 int h, int nH, int Nv, uint32_t row_bytes) {
+  const int n = 4 * __popc(live);
+  int incl = n;
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) {
+    const int v = __shfl_up(incl, d, 8);
+    if (j >= d) incl += v;
+  }
+  const int group_total = __shfl(incl, 7, 8);
+  int wave_max = group_total;
+  wave_max = max(wave_max, __shfl_xor(wave_max, 8));
+  wave_max = max(wave_max, __shfl_xor(wave_max, 16));
+  wave_max = max(wave_max, __shfl_xor(wave_max, 32));
+  const int R = (wave_max + kBatch - 1) / kBatch * kBatch;
+  int pos = incl - n;
+#pragma unroll
+  for (int i = 0; i < kSPL; ++i) {
+    if ((live >> i) & 1u) {
+      const Level L = lv[small_div(j + 8 * i, inv_P)];
+      uint2 c[4];
+      sample_corners(c, xs[i], ys[i], alpha[i], L, true, h, nH, Nv, row_bytes);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) rows[pos + t] = c[t];
+      pos += 4;
+    }
+  }
+  for (int r = group_total + j; r < R; r += 8) rows[r] = make_uint2(kSkip, 0u);
+  return uniform(R);
+}
+
+// Accumulate weight * value row over the group's R staged rows (R a
+// multiple of kBatch), kBatch loads in flight per lane.
 template <bool kBF16>
 __device__ inline void gather_rows(const uint2* __restrict__ rows, int R, __amdgpu_buffer_rsrc_t img, int j,
                                    float4& acc) {
   const uint32_t lane_off = (uint32_t)j * (kBF16 ? 8u : 16u);
-  for (int r = 0; r < R; r += kUnroll) {
-    uint2 m[kUnroll];
+  for (int r = 0; r < R; r += kBatch) {
+    uint2 m[kBatch];
+    uint32_t d[kBatch][kBF16 ? 2 : 4];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) m[u] = rows[r + u];
-    if constexpr (!kBF16) {
-      float4 v[kUnroll];
+    for (int u = 0; u < kBatch; ++u) m[u] = rows[r + u];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const auto raw = __builtin_amdgcn_raw_buffer_load_b128(img, m[u].x + lane_off, 0, 0);
-        v[u] = make_float4(__uint_as_float(raw[0]), __uint_as_float(raw[1]), __uint_as_float(raw[2]),
-                           __uint_as_float(raw[3]));
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const float w = __uint_as_float(m[u].y);
-        acc.x = fmaf(w, v[u].x, acc.x);
-        acc.y = fmaf(w, v[u].y, acc.y);
-        acc.z = fmaf(w, v[u].z, acc.z);
-        acc.w = fmaf(w, v[u].w, acc.w);
-      }
-    } else {
-      uint32_t lo[kUnroll], hi[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
+      if constexpr (kBF16) {
         const auto raw = __builtin_amdgcn_raw_buffer_load_b64(img, m[u].x + lane_off, 0, 0);
-        lo[u] = raw[0];
-        hi[u] = raw[1];
+        d[u][0] = raw[0];
+        d[u][1] = raw[1];
+      } else {
+        const auto raw = __builtin_amdgcn_raw_buffer_load_b128(img, m[u].x + lane_off, 0, 0);
+        d[u][0] = raw[0];
+        d[u][1] = raw[1];
+        d[u][2] = raw[2];
+        d[u][3] = raw[3];
       }
+    }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const float w = __uint_as_float(m[u].y);
-        acc.x = fmaf(w, __uint_as_float(lo[u] << 16), acc.x);
-        acc.y = fmaf(w, __uint_as_float(lo[u] & 0xffff0000u), acc.y);
-        acc.z = fmaf(w, __uint_as_float(hi[u] << 16), acc.z);
-        acc.w = fmaf(w, __uint_as_float(hi[u] & 0xffff0000u), acc.w);
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = __uint_as_float(m[u].y);
+      if constexpr (kBF16) {
+        acc.x = fmaf(w, __uint_as_float(d[u][0] << 16), acc.x);
+        acc.y = fmaf(w, __uint_as_float(d[u][0] & 0xffff0000u), acc.y);
+        acc.z = fmaf(w, __uint_as_float(d[u][1] << 16), acc.z);
+        acc.w = fmaf(w, __uint_as_float(d[u][1] & 0xffff0000u), acc.w);
+      } else {
+        acc.x = fmaf(w, __uint_as_float(d[u][0]), acc.x);
+        acc.y = fmaf(w, __uint_as_float(d[u][1]), acc.y);
+        acc.z = fmaf(w, __uint_as_float(d[u][2]), acc.z);
+        acc.w = fmaf(w, __uint_as_float(d[u][3]), acc.w);
       }
     }
   }
@@ -179,28 +230,25 @@ __device__ inline void load_levels(const GatherArgs& a, Level* lv) {
   __syncthreads();
 }
 
-__device__ inline int small_div(int k, float inv) { return (int)((k + 0.5f) * inv); }
-
-// Padding rows past 4*L*P never change; write them as skipped rows.
-__device__ inline void stage_padding(uint2* rows, int LP, int j) {
-  const int r = 4 * LP + j;
-  if (r < rows_padded(LP)) rows[r] = make_uint2(kSkip, 0u);
+__device__ inline float4 scaled(float4 v, int n) {
+  if (n <= 1) return v;
+  const float f = (float)n;
+  return make_float4(v.x / f, v.y / f, v.z / f, v.w / f);
 }
 
 // ---------------------------------------------------------------------------
 // plain operator and frame mean: item = (b, q); sources = frames f
 // ---------------------------------------------------------------------------
-template <bool kBF16>
+template <bool kBF16, int kSPL>
 __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(GatherArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Level* lv = reinterpret_cast<Level*>(smem);
   load_levels(a, lv);
   const int waves_per_block = blockDim.x / kWave;
-  const int lane = threadIdx.x % kWave, wave = uniform(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave, wave = uniform((int)(threadIdx.x / kWave));
   const int g = lane / 8, j = lane % 8;
-  const int RS = meta_stride(a.LP), R = rows_padded(a.LP);
-  uint2* rows = reinterpret_cast<uint2*>(smem + sizeof(Level) * kMaxLevels) + ((size_t)wave * kHeadSlots + g) * RS;
-  stage_padding(rows, a.LP, j);
+  uint2* rows = reinterpret_cast<uint2*>(smem + sizeof(Level) * kMaxLevels) +
+                ((size_t)wave * kHeadSlots + g) * meta_stride(a.LP);
   const uint32_t row_bytes = kBF16 ? 64u : 128u;
 
   XcdSplit split(a.B * a.Nq, waves_per_block);
@@ -213,90 +261,77 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
       for (int f = 0; f < a.F; ++f) {
         const int64_t img_index = b * a.F + f;
         const int64_t src_row = (img_index * a.Nq + q) * a.nH + (head_ok ? h : 0);
-        float alpha[kSamplesPerLane];
-        head_weights(a.weights + src_row * a.LP, head_ok, a.LP, j, a.weight_logits != 0, alpha);
+        float alpha[kSPL];
+        head_weights<kSPL>(a.weights + src_row * a.LP, head_ok, a.LP, j, a.weight_logits != 0, alpha);
         const float2* loc = reinterpret_cast<const float2*>(a.loc) + src_row * a.LP;
+        double xs[kSPL], ys[kSPL];
+        uint32_t live = 0u;
 #pragma unroll
-        for (int i = 0; i < kSamplesPerLane; ++i) {
+        for (int i = 0; i < kSPL; ++i) {
           const int k = j + 8 * i;
-          if (k < a.LP) {
-            const Level L = lv[small_div(k, a.inv_P)];
-            const float2 s = head_ok ? loc[k] : make_float2(0.f, 0.f);
-            stage_corners(rows, k, (double)s.x * L.W - 0.5, (double)s.y * L.H - 0.5, alpha[i], L, head_ok, h, a.nH,
-                          a.Nv, row_bytes);
-          }
+          const bool valid = head_ok && k < a.LP;
+          const Level L = lv[valid ? small_div(k, a.inv_P) : 0];
+          const float2 s = valid ? loc[k] : make_float2(0.f, 0.f);
+          xs[i] = (double)s.x * L.W - 0.5;
+          ys[i] = (double)s.y * L.H - 0.5;
+          if (valid && sample_live(xs[i], ys[i], L)) live |= 1u << i;
         }
+        const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv, a.inv_P, j, h, a.nH, a.Nv, row_bytes);
         wave_lds_sync();
         const auto img = make_rsrc(static_cast<const char*>(a.value) + img_index * (int64_t)a.image_bytes,
                                    a.image_bytes);
         gather_rows<kBF16>(rows, R, img, j, acc);
         wave_lds_sync();
       }
-      if (head_ok) {
-        if (a.F != 1) {
-          const float n = (float)a.F;
-          acc = make_float4(acc.x / n, acc.y / n, acc.z / n, acc.w / n);
-        }
-        float4* dst = reinterpret_cast<float4*>(a.out + ((item * a.nH + h) * 32)) + j;
-        *dst = acc;
-      }
+      if (head_ok) reinterpret_cast<float4*>(a.out + ((item * a.nH + h) * 32))[j] = scaled(acc, a.F);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// SCA: item = entry of the compacted (b, c, q) pair list; the pair of the
-// first camera that sees q runs the whole query (all its cameras), so each
-// query is written once, by one wave, and no atomics are needed.  Rows of
-// queries that no camera sees are zeroed at the end.
+// SCA: item = entry of the work list sca_compact builds (every seen query
+// once, grouped by first camera and image tile); the wave runs all cameras
+// of its query and averages them in registers, so each query is written
+// once, by one wave, and no atomics are needed.  Rows of queries that no
+// camera sees are zeroed at the end.
 // ---------------------------------------------------------------------------
-template <bool kBF16>
+template <bool kBF16, int kSPL>
 __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void sca_gather_kernel(GatherArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Level* lv = reinterpret_cast<Level*>(smem);
   load_levels(a, lv);
   const int waves_per_block = blockDim.x / kWave;
-  const int lane = threadIdx.x % kWave, wave = uniform(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave, wave = uniform((int)(threadIdx.x / kWave));
   const int g = lane / 8, j = lane % 8;
-  const int RS = meta_stride(a.LP), R = rows_padded(a.LP);
-  uint2* rows = reinterpret_cast<uint2*>(smem + sizeof(Level) * kMaxLevels) + ((size_t)wave * kHeadSlots + g) * RS;
-  stage_padding(rows, a.LP, j);
+  uint2* rows = reinterpret_cast<uint2*>(smem + sizeof(Level) * kMaxLevels) +
+                ((size_t)wave * kHeadSlots + g) * meta_stride(a.LP);
   const uint32_t row_bytes = kBF16 ? 64u : 128u;
-  const int nseg = (int)(a.B * a.Ncam);
-  // the pair lists come from sca_compact; clamp so that a workspace that
+  // the work list comes from sca_compact; clamp so that a workspace that
   // never saw one cannot send a read out of bounds
-  int64_t n_pairs = a.pair_offsets[nseg];
-  n_pairs = n_pairs < 0 ? 0 : (n_pairs > a.B * a.Ncam * a.Nq ? a.B * a.Ncam * a.Nq : n_pairs);
+  const int64_t n_queries = a.B * a.Nq;
+  int64_t n_items = *a.n_order;
+  n_items = n_items < 0 ? 0 : (n_items > n_queries ? n_queries : n_items);
   const uint32_t cam_bits = a.Ncam >= 32 ? 0xffffffffu : ((1u << a.Ncam) - 1u);
 
-  XcdSplit split(n_pairs, waves_per_block);
+  XcdSplit split(n_items, waves_per_block);
   for (int64_t item = split.begin; item < split.end; item += split.stride) {
-    // segment (b, c) of this pair: the last s with pair_offsets[s] <= item
-    int lo = 0, hi = nseg;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.pair_offsets[mid] <= item) lo = mid; else hi = mid;
-    }
-    const int64_t b = lo / a.Ncam;
-    const int c_item = lo % a.Ncam;
-    const int64_t q = a.pair_q[item];
-    if (q < 0 || q >= a.Nq) continue;
-    const int64_t bq = b * a.Nq + q;
-    const uint32_t seen = a.cammask[bq] & cam_bits;
-    if (seen == 0u || __builtin_ctz(seen) != c_item) continue;  // another pair of this query runs it
-    const int hits = __popc(seen);
+    const int64_t bq = uniform((int64_t)a.order[item]);
+    if (bq < 0 || bq >= n_queries) continue;
+    const int64_t b = bq / a.Nq, q = bq % a.Nq;
+    const uint32_t seen = uniform(a.cammask[bq] & cam_bits);
+    if (seen == 0u) continue;
 
     for (int hb = 0; hb < a.nH; hb += kHeadSlots) {
       const int h = hb + g;
       const bool head_ok = h < a.nH;
       const int64_t src_row = bq * a.nH + (head_ok ? h : 0);
       // the query's weights and offsets serve every camera
-      float alpha[kSamplesPerLane];
-      head_weights(a.logits + src_row * a.LP, head_ok, a.LP, j, true, alpha);
-      float2 off[kSamplesPerLane];
+      float alpha[kSPL];
+      head_weights<kSPL>(a.logits + src_row * a.LP, head_ok, a.LP, j, true, alpha);
+      float2 off[kSPL];
       const float2* off_row = reinterpret_cast<const float2*>(a.offsets) + src_row * a.LP;
 #pragma unroll
-      for (int i = 0; i < kSamplesPerLane; ++i) {
+      for (int i = 0; i < kSPL; ++i) {
         const int k = j + 8 * i;
         off[i] = (head_ok && k < a.LP) ? off_row[k] : make_float2(0.f, 0.f);
       }
@@ -304,33 +339,28 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void sca_gather_kernel(Ga
       for (uint32_t rest = seen; rest != 0u; rest &= rest - 1u) {
         const int c = __builtin_ctz(rest);
         const float2* rho = reinterpret_cast<const float2*>(a.rp) + ((c * a.B + b) * a.Nq + q) * a.D;
+        double xs[kSPL], ys[kSPL];
+        uint32_t live = 0u;
 #pragma unroll
-        for (int i = 0; i < kSamplesPerLane; ++i) {
+        for (int i = 0; i < kSPL; ++i) {
           const int k = j + 8 * i;
-          if (k < a.LP) {
-            const Level L = lv[small_div(k, a.inv_P)];
-            const int m = k - a.D * small_div(k, a.inv_D);  // anchor k mod D (P is a multiple of D)
-            const float2 r = rho[m];
-            // x = W*(rho_x + dx/W) - 1/2 = W*rho_x + dx - 1/2, evaluated in fp64
-            const double x = (double)r.x * L.W + (double)off[i].x - 0.5;
-            const double y = (double)r.y * L.H + (double)off[i].y - 0.5;
-            stage_corners(rows, k, x, y, alpha[i], L, head_ok, h, a.nH, a.Nv, row_bytes);
-          }
+          const bool valid = head_ok && k < a.LP;
+          const Level L = lv[valid ? small_div(k, a.inv_P) : 0];
+          const int m = k - a.D * small_div(k, a.inv_D);  // anchor k mod D (P is a multiple of D)
+          const float2 r = valid ? rho[m] : make_float2(0.f, 0.f);
+          // x = W*(rho_x + dx/W) - 1/2 = W*rho_x + dx - 1/2, evaluated in fp64
+          xs[i] = (double)r.x * L.W + (double)off[i].x - 0.5;
+          ys[i] = (double)r.y * L.H + (double)off[i].y - 0.5;
+          if (valid && sample_live(xs[i], ys[i], L)) live |= 1u << i;
         }
+        const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv, a.inv_P, j, h, a.nH, a.Nv, row_bytes);
         wave_lds_sync();
         const auto img = make_rsrc(static_cast<const char*>(a.value) + (b * a.Ncam + c) * (int64_t)a.image_bytes,
                                    a.image_bytes);
         gather_rows<kBF16>(rows, R, img, j, acc);
         wave_lds_sync();
       }
-      if (head_ok) {
-        if (hits > 1) {
-          const float n = (float)hits;
-          acc = make_float4(acc.x / n, acc.y / n, acc.z / n, acc.w / n);
-        }
-        float4* dst = reinterpret_cast<float4*>(a.out + ((bq * a.nH + h) * 32)) + j;
-        *dst = acc;
-      }
+      if (head_ok) reinterpret_cast<float4*>(a.out + ((bq * a.nH + h) * 32))[j] = scaled(acc, __popc(seen));
     }
   }
 
@@ -351,7 +381,8 @@ static int device_cus() {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
       cus = n;
     else
       cus = 256;
@@ -385,10 +416,13 @@ hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream) {
   const int waves = block_waves(a.LP);
   const unsigned grid = grid_for(a.B * a.Nq, waves, 8 * kMaxWavesPerBlock / waves);
   const size_t smem = smem_bytes(a.LP, waves);
-  if (a.bf16)
-    msda_gather_kernel<true><<<grid, waves * kWave, smem, stream>>>(a);
-  else
-    msda_gather_kernel<false><<<grid, waves * kWave, smem, stream>>>(a);
+  if (a.LP <= 32) {
+    if (a.bf16) msda_gather_kernel<true, 4><<<grid, waves * kWave, smem, stream>>>(a);
+    else msda_gather_kernel<false, 4><<<grid, waves * kWave, smem, stream>>>(a);
+  } else {
+    if (a.bf16) msda_gather_kernel<true, 8><<<grid, waves * kWave, smem, stream>>>(a);
+    else msda_gather_kernel<false, 8><<<grid, waves * kWave, smem, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -396,10 +430,13 @@ hipError_t launch_sca_gather(const GatherArgs& a, hipStream_t stream) {
   const int waves = block_waves(a.LP);
   const unsigned grid = grid_for(a.B * a.Ncam * a.Nq, waves, 8 * kMaxWavesPerBlock / waves);
   const size_t smem = smem_bytes(a.LP, waves);
-  if (a.bf16)
-    sca_gather_kernel<true><<<grid, waves * kWave, smem, stream>>>(a);
-  else
-    sca_gather_kernel<false><<<grid, waves * kWave, smem, stream>>>(a);
+  if (a.LP <= 32) {
+    if (a.bf16) sca_gather_kernel<true, 4><<<grid, waves * kWave, smem, stream>>>(a);
+    else sca_gather_kernel<false, 4><<<grid, waves * kWave, smem, stream>>>(a);
+  } else {
+    if (a.bf16) sca_gather_kernel<true, 8><<<grid, waves * kWave, smem, stream>>>(a);
+    else sca_gather_kernel<false, 8><<<grid, waves * kWave, smem, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -30,8 +30,8 @@ struct GatherArgs {
   const float* offsets;   // [B][Nq][nH][L][P][2]
   const float* logits;    // [B][Nq][nH][L*P]
   const uint32_t* cammask;  // [B][Nq] bit c = camera c sees the query
-  const int32_t* pair_offsets;  // [B*Ncam + 1]
-  const int32_t* pair_q;
+  const int32_t* order;     // seen queries b*Nq + q, in locality order
+  const int32_t* n_order;   // device: number of entries in order
   int Ncam, D;
   int64_t B, Nq;
   float* out;  // [B][Nq][nH*32]
@@ -40,22 +40,30 @@ struct GatherArgs {
 hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_sca_gather(const GatherArgs& a, hipStream_t stream);
 
-// SCA compaction: workspace layout and launch.
+// SCA compaction and work ordering: workspace layout and launch.
+// Image-tile grid used to order the gather work (per first camera).
+constexpr int kOrderBinsX = 64, kOrderBinsY = 16, kOrderBins = kOrderBinsX * kOrderBinsY;
+
 struct CompactLayout {
-  size_t cammask, tile_counts, tile_offsets, pair_offsets, pair_q, total;
+  size_t cammask, qkey, tile_counts, tile_offsets, pair_offsets, pair_q, bin_hist, bin_offsets, order, total;
   int tiles;  // tiles of the query axis per (b, c)
 };
 CompactLayout compact_layout(int64_t B, int64_t Ncam, int64_t Nq);
 
 struct CompactArgs {
   const uint8_t* bev_mask;
+  const float* rp;  // [Ncam][B][Nq][D][2], only to order the work
   int B, Ncam, Nq, D;
   uint32_t* cammask;
+  int32_t* qkey;       // [B][Nq] ordering bin of a seen query, -1 if unseen
   int32_t* hit_count;  // may be null
   int32_t* tile_counts;
   int32_t* tile_offsets;
   int32_t* pair_offsets;
   int32_t* pair_q;
+  int32_t* bin_hist;     // [B*Ncam*kOrderBins]
+  int32_t* bin_offsets;  // [B*Ncam*kOrderBins + 1]; the last entry counts the seen queries
+  int32_t* order;        // [B*Nq]
 };
 hipError_t launch_sca_compact(const CompactArgs& a, int tiles, hipStream_t stream);
 

@@ -141,14 +141,17 @@ def test_sca_forward_empty_query_set_is_a_no_op(lib):
 def test_sca_stages_reject(lib):
     n = _sz(0)
     assert lib.sca_workspace_size(1, 6, 8, ctypes.byref(n)) == OK
-    assert lib.sca_compact(None, 1, 6, 8, 4, None, None, None, A, n.value, None) == INVALID
-    assert lib.sca_compact(A, 1, 33, 8, 4, None, None, None, A, n.value, None) == UNSUPPORTED
-    assert lib.sca_compact(A, 1, 6, 8, 4, None, None, None, A, n.value - 1, None) == WORKSPACE
-    assert lib.sca_compact(A, 1, 6, 0, 4, None, None, None, A, n.value, None) == OK
+    c = lib.sca_compact
+    assert c(None, A, 1, 6, 8, 4, None, None, None, A, n.value, None) == INVALID
+    assert c(A, None, 1, 6, 8, 4, None, None, None, A, n.value, None) == INVALID
+    assert c(A, A + 4, 1, 6, 8, 4, None, None, None, A, n.value, None) == INVALID
+    assert c(A, A, 1, 33, 8, 4, None, None, None, A, n.value, None) == UNSUPPORTED
+    assert c(A, A, 1, 6, 8, 4, None, None, None, A, n.value - 1, None) == WORKSPACE
+    assert c(A, A, 1, 6, 0, 4, None, None, None, A, n.value, None) == OK
     g = lib.sca_gather
-    assert g(A, 0, A, A, A, A, A, 1, 6, 16, 8, 8, 32, 1, 6, 4, B_, None, None, A, n.value, None) == SHAPE
-    assert g(A, 0, A, A, A, A, A, 1, 6, 16, 8, 8, 32, 1, 8, 4, B_, None, None, None, n.value, None) == WORKSPACE
-    assert g(A, 0, A, A, None, A, A, 1, 6, 16, 8, 8, 32, 1, 8, 4, B_, None, None, A, n.value, None) == INVALID
+    assert g(A, 0, A, A, A, A, A, 1, 6, 16, 8, 8, 32, 1, 6, 4, B_, A, n.value, None) == SHAPE
+    assert g(A, 0, A, A, A, A, A, 1, 6, 16, 8, 8, 32, 1, 8, 4, B_, None, n.value, None) == WORKSPACE
+    assert g(A, 0, A, A, None, A, A, 1, 6, 16, 8, 8, 32, 1, 8, 4, B_, A, n.value, None) == INVALID
 
 
 @pytest.mark.parametrize("M,N,K,code", [

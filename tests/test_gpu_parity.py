@@ -52,7 +52,7 @@ def run_sca(w, value=None, want_compaction=True):
                      dev(w["bev_mask"]), dev(w["sampling_offsets"]), dev(w["attention_logits"]), slots=slots,
                      hit_count=hit if want_compaction else None, pair_offsets=offs if want_compaction else None,
                      pair_q=pq if want_compaction else None)
-    res = {"slots": host(slots).reshape(B * Nq, -1)}
+    res = {"slots": host(slots).reshape(B * Nq, w["nH"] * w["Dh"])}
     if want_compaction:
         res["hit_count"] = host(hit)
         res["pair_offsets"] = host(offs)
@@ -305,11 +305,12 @@ def test_sca_edge_cases(case):
 
 
 def test_sca_stages_and_compaction_reuse():
-    """sca_compact once, sca_gather twice (two layers sharing one mask) equals
-    sca_forward; the pair lists can live in the workspace only."""
+    """sca_compact once, sca_gather twice (two layers sharing one mask and
+    anchors) equals sca_forward; the pair lists can live in the workspace
+    only."""
     w = _rand_sca(31, 2, 6, 300, ((8, 12), (4, 6)), 8, 8, 4, 0.2)
     ws = torch.empty(msda.sca_workspace_size(2, 6, 300), dtype=torch.uint8, device="cuda")
-    msda.sca_compact(dev(w["bev_mask"]), ws)
+    msda.sca_compact(dev(w["bev_mask"]), dev(w["reference_points_cam"]), ws)
     args = (dev(w["spatial_shapes"]), dev(w["level_start_index"]), dev(w["reference_points_cam"]),
             dev(w["sampling_offsets"]), dev(w["attention_logits"]), ws)
     s1 = host(msda.sca_gather(dev(w["value"]), *args)).reshape(600, -1)
