@@ -2,21 +2,26 @@
 """Benchmark of the BEVFormer-base spatial cross-attention (SCA) forward pass
 on one MI355X, through libmsda.so's C ABI.
 
-Workload (default): BEVFormer-base SCA, fp32 value, batch 1, 6 cameras,
-200x200 BEV queries, 4 levels per camera (116x200, 58x100, 29x50, 15x25),
-8 heads x 32 channels, 8 points per level over 4 pillar anchors; seeded
-synthetic inputs from workloads.bevformer_sca().  One step is the whole hot
-path: visibility + compaction of the (camera, query) pairs (sca_compact) and
-the fused softmax / bilinear gather / weighted sum / camera mean
-(sca_gather).  Inputs are resident in HBM before timing starts.
+Workload (default, "sca"): BEVFormer-base SCA, fp32 value, batch 1, 6
+cameras, 200x200 BEV queries, 4 levels per camera (116x200, 58x100, 29x50,
+15x25), 8 heads x 32 channels, 8 points per level over 4 pillar anchors;
+seeded synthetic inputs from workloads.bevformer_sca().  One step is the
+whole hot path: visibility, compaction and work ordering of the (camera,
+query) pairs (sca_compact) and the fused softmax / bilinear gather /
+weighted sum / camera mean (sca_gather).  Inputs are resident in HBM before
+timing starts.  Other workloads: "layer_bf16" (batch 4, bf16 value
+projection GEMM -> SCA on bf16 value -> bf16 output projection GEMM),
+"sca_bf16", "detr" (Deformable-DETR encoder MSDA), "tsa" (two stacked BEV
+maps, frame mean), "tiny".
 
 Prints one JSON line.  value = bilinear samples per second (one sample = one
 (camera, query, head, level, point) bilinear read of 4 corners x 32
-channels); roofline = the gather kernel's effective bytes (all 4 nominal
-corners of every sample, plus offsets, logits, anchors and output) per
-launch over its average launch time, measured with HIP events recorded on
-the stream the kernel runs on; cpu_baseline = the CPU oracle on the same
-workload.
+channels) over the whole step; roofline = the gather kernel's effective
+bytes (all 4 nominal corners of every sample, plus offsets, logits, anchors,
+work list and output) per launch over its average launch time, measured with
+HIP events recorded on the stream the kernel runs on; breakdown = the same
+events around every part of the step; cpu_baseline = the CPU oracle on the
+same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --calibrate-copy   (a plain device copy of known size, for
@@ -32,14 +37,16 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 GATHER_SOURCES = ["scale_deformable_attention_forward_amd/csrc/gather.hip",
                   "scale_deformable_attention_forward_amd/csrc/common.hpp",
                   "scale_deformable_attention_forward_amd/csrc/internal.hpp"]
+METRIC = "MSDA samples/sec + effective HBM GB/s, BEVFormer-base SCA layer (6 cams)"
 
 
-def source_digest(paths):
+def source_digest(paths=GATHER_SOURCES):
     h = hashlib.sha256()
     for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
@@ -47,15 +54,18 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when the kernel's sources changed since they were taken."""
+def measured_traffic(workload):
+    """Bytes per gather launch moved between L2 and memory (FETCH_SIZE +
+    WRITE_SIZE, calibrated on a plain copy) from the committed rocprofv3
+    counter runs for this workload, or None when there is none or the gather
+    sources changed since it was taken.  Reads served by the memory-side
+    Infinity Cache count too, so this bounds the HBM bytes from above."""
     try:
         with open(COUNTERS_FILE) as f:
-            c = json.load(f)[kernel_key]
+            c = json.load(f)[workload]
     except (OSError, KeyError, ValueError):
         return None
-    if c.get("source_digest") != source_digest(GATHER_SOURCES):
+    if c.get("source_digest") != source_digest():
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -72,58 +82,85 @@ def calibrate_copy():
 
 
 class Workload:
-    """A bench workload: inputs on the device and a step() that runs the hot path."""
+    """Inputs on the device and the step, as a list of named parts.  `main`
+    names the dominant kernel's part; finish() fills in the sample count and
+    the per-launch byte and flop figures after a warm-up."""
+
+    def __init__(self, name):
+        self.name = name
+        self.parts = []
+        self.main = None
+        self.extra = {}
 
 
-def sca_workload(bf16=False):
+def _dev(a):
     import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def sca_workload(kind):
     import torch
     import workloads as W
     import scale_deformable_attention_forward_amd as m
 
-    w = W.bevformer_sca(value_bf16=bf16) if bf16 else W.bevformer_sca()
-    d = {}
-    for k in ("spatial_shapes", "level_start_index", "reference_points_cam", "bev_mask", "sampling_offsets",
-              "attention_logits"):
-        d[k] = torch.from_numpy(np.ascontiguousarray(w[k])).cuda()
-    if bf16:
-        d["value"] = torch.from_numpy(w["value"].view(np.int16)).view(torch.bfloat16).cuda()
+    layer = kind == "layer_bf16"
+    bf16 = kind in ("sca_bf16", "layer_bf16")
+    if layer:
+        w = W.bevformer_sca_bf16()
     else:
-        d["value"] = torch.from_numpy(w["value"]).cuda()
-    B, Ncam, Nq, nH, L, P, D = w["B"], w["Ncam"], w["Nq"], w["nH"], w["L"], w["P"], w["D"]
+        w = W.bevformer_sca(value_bf16=bf16)
+    B, Ncam, Nq, Nv, nH, L, P, D = w["B"], w["Ncam"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"], w["D"]
+    C = nH * 32
+    d = {k: _dev(w[k]) for k in ("spatial_shapes", "level_start_index", "reference_points_cam", "bev_mask",
+                                 "sampling_offsets", "attention_logits")}
+    if layer:
+        d["feat"] = _dev(w["feat"].reshape(-1, C))
+        d["W_v"], d["b_v"], d["W_o"], d["b_o"] = (_dev(w[k]) for k in ("W_v", "b_v", "W_o", "b_o"))
+        d["value"] = torch.empty((B, Ncam, Nv, nH, 32), dtype=torch.bfloat16, device="cuda")
+        d["out"] = torch.empty((B * Nq, C), dtype=torch.float32, device="cuda")
+    else:
+        d["value"] = _dev(w["value"])
     ws = torch.empty(m.sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device="cuda")
-    slots = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
+    slots = torch.empty((B, Nq, C), dtype=torch.float32, device="cuda")
     offs = torch.empty(B * Ncam + 1, dtype=torch.int32, device="cuda")
     pq = torch.empty(B * Ncam * Nq, dtype=torch.int32, device="cuda")
     hit = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
 
-    wl = Workload()
-    wl.name = "sca_bf16" if bf16 else "sca"
-    wl.w = w
-
-    def compact():
-        m.sca_compact(d["bev_mask"], d["reference_points_cam"], ws, hit_count=hit, pair_offsets=offs, pair_q=pq)
-
-    def gather():
-        m.sca_gather(d["value"], d["spatial_shapes"], d["level_start_index"], d["reference_points_cam"],
-                     d["sampling_offsets"], d["attention_logits"], ws, slots=slots)
-
-    wl.pre, wl.kernel = compact, gather
+    wl = Workload(kind)
+    if layer:
+        wl.parts.append(("value_proj", lambda: m.msda_gemm_bf16(d["feat"], d["W_v"], d["b_v"],
+                                                                out=d["value"].view(-1, C))))
+    wl.parts.append(("compact", lambda: m.sca_compact(d["bev_mask"], d["reference_points_cam"], ws, hit_count=hit,
+                                                      pair_offsets=offs, pair_q=pq)))
+    wl.parts.append(("gather", lambda: m.sca_gather(d["value"], d["spatial_shapes"], d["level_start_index"],
+                                                    d["reference_points_cam"], d["sampling_offsets"],
+                                                    d["attention_logits"], ws, slots=slots)))
+    if layer:
+        wl.parts.append(("output_proj", lambda: m.msda_gemm_bf16(slots.view(-1, C), d["W_o"], d["b_o"],
+                                                                 out=d["out"])))
+    wl.main = "gather"
 
     def finish():
-        torch.cuda.synchronize()
         n_pairs = int(offs[-1].item())
         elem = 2 if bf16 else 4
-        samples = n_pairs * nH * L * P
-        wl.samples = samples
+        wl.samples = n_pairs * nH * L * P
         # effective bytes of one gather launch: 4 nominal corners x 32 channels
         # per sample, the per-query offsets and logits, the anchors of each
         # pair, the camera masks and work list, and the output rows
-        wl.eff_bytes = (samples * 4 * 32 * elem + B * Nq * nH * L * P * (8 + 4) + n_pairs * D * 8
-                        + B * Nq * (4 + 4) + B * Nq * nH * 32 * 4)
-        wl.gathered_bytes = samples * 4 * 32 * elem
+        wl.gathered_bytes = wl.samples * 4 * 32 * elem
+        wl.eff_bytes = (wl.gathered_bytes + B * Nq * nH * L * P * (8 + 4) + n_pairs * D * 8 + B * Nq * (4 + 4)
+                        + B * Nq * C * 4)
+        if layer:
+            Mv, Mo = B * Ncam * Nv, B * Nq
+            wl.extra["value_proj"] = {"flop": 2 * Mv * C * C, "bytes": Mv * C * 2 * 2 + C * C * 2}
+            wl.extra["output_proj"] = {"flop": 2 * Mo * C * C, "bytes": Mo * C * 4 * 2 + C * C * 2}
     wl.finish = finish
-    wl.config = {"workload": "BEVFormer-base spatial cross-attention layer, 6 cameras",
+    wl.config = {"workload": "BEVFormer-base spatial cross-attention layer, 6 cameras"
+                 + (", with bf16 value and output projections" if layer else ""),
                  "batch": B, "cameras": Ncam, "bev_queries": "200x200", "levels": "116x200/58x100/29x50/15x25",
                  "heads": nH, "head_dim": 32, "points_per_level": P, "pillar_anchors": D,
                  "value_dtype": "bf16" if bf16 else "fp32", "mask": "azimuth sectors, 1-2 cameras per query"}
@@ -132,6 +169,21 @@ def sca_workload(bf16=False):
 
     def cpu_baseline():
         import oracle
+        if layer:
+            # bounded sample: the value projection of every row (float64
+            # matmul), then SCA and output projection of 4000 sampled queries
+            rows = W.sample_rows(7, B * Nq, 4000)
+            t0 = time.perf_counter()
+            v = oracle.round_to_bf16(oracle.linear_bf16_blas(w["feat"].reshape(-1, C), w["W_v"], w["b_v"]))
+            r = oracle.sca(v.reshape(B, Ncam, Nv, nH, 32), w["spatial_shapes"], w["level_start_index"],
+                           w["reference_points_cam"], w["bev_mask"], w["sampling_offsets"], w["attention_logits"],
+                           rows=rows)
+            oracle.linear_bf16(oracle.round_to_bf16(r["slots"]), w["W_o"], w["b_o"])
+            t = time.perf_counter() - t0
+            n = int(r["hit_count"].reshape(-1)[rows].sum()) * nH * L * P
+            return {"value": n / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
+                    "sample": f"value projection of all rows, then SCA and output projection of 4000 sampled "
+                              f"queries ({n} samples); C loops and a float64 matmul, {t:.1f} s"}
         t0 = time.perf_counter()
         oracle.sca(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
                    w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
@@ -144,39 +196,28 @@ def sca_workload(bf16=False):
 
 
 def msda_workload(which):
-    import numpy as np
     import torch
     import workloads as W
     import scale_deformable_attention_forward_amd as m
 
     if which == "detr":
-        w = W.detr_encoder_msda()
-        F = 1
+        w, F = W.detr_encoder_msda(), 1
     elif which == "tiny":
-        w = W.tiny_msda()
-        F = 1
+        w, F = W.tiny_msda(), 1
     else:
         w = W.temporal_frames()
         F = w["F"]
-    d = {k: torch.from_numpy(np.ascontiguousarray(w[k])).cuda()
-         for k in ("value", "spatial_shapes", "level_start_index", "sampling_locations", "attention_weights")}
+    d = {k: _dev(w[k]) for k in ("value", "spatial_shapes", "level_start_index", "sampling_locations",
+                                 "attention_weights")}
     B, Nq, nH, L, P = w["B"], w["Nq"], w["nH"], w["L"], w["P"]
     out = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
-    wl = Workload()
-    wl.name = which
-    wl.w = w
-
-    def kernel():
-        if F == 1:
-            m.msda_forward(d["value"], d["spatial_shapes"], d["level_start_index"], d["sampling_locations"],
-                           d["attention_weights"], out=out)
-        else:
-            m.msda_forward_frames(d["value"], d["spatial_shapes"], d["level_start_index"], d["sampling_locations"],
-                                  d["attention_weights"], out=out)
-    wl.pre, wl.kernel = (lambda: None), kernel
+    wl = Workload(which)
+    fn = m.msda_forward if F == 1 else m.msda_forward_frames
+    wl.parts.append(("gather", lambda: fn(d["value"], d["spatial_shapes"], d["level_start_index"],
+                                          d["sampling_locations"], d["attention_weights"], out=out)))
+    wl.main = "gather"
 
     def finish():
-        torch.cuda.synchronize()
         wl.samples = B * F * Nq * nH * L * P
         wl.gathered_bytes = wl.samples * 4 * 32 * 4
         wl.eff_bytes = wl.gathered_bytes + wl.samples * (8 + 4) + B * Nq * nH * 32 * 4
@@ -210,7 +251,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="sca", choices=["sca", "sca_bf16", "detr", "tsa", "tiny"])
+    ap.add_argument("--workload", default="sca", choices=["sca", "layer_bf16", "sca_bf16", "detr", "tsa", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -227,35 +268,46 @@ def main():
     import scale_deformable_attention_forward_amd as m
     m.load_library()
 
-    if args.workload.startswith("sca"):
-        wl = sca_workload(bf16=args.workload == "sca_bf16")
-    else:
-        wl = msda_workload(args.workload)
+    wl = sca_workload(args.workload) if args.workload in ("sca", "layer_bf16", "sca_bf16") else \
+        msda_workload(args.workload)
 
     for _ in range(args.warmup):
-        wl.pre()
-        wl.kernel()
+        for _, fn in wl.parts:
+            fn()
+    torch.cuda.synchronize()
     wl.finish()
 
+    # events recorded on torch's current stream, which is the stream the
+    # binding hands to the library, between every part of every step
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    n = len(wl.parts)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        wl.pre()
-        starts[k].record()  # torch's current stream = the stream the binding launches on
-        wl.kernel()
-        ends[k].record()
+        ev[k][0].record()
+        for i, (_, fn) in enumerate(wl.parts):
+            fn()
+            ev[k][i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / K
+    part_ms = {name: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)) / K
+               for i, (name, _) in enumerate(wl.parts)}
+    kernel_ms = part_ms[wl.main]
 
+    breakdown = {}
+    for name, ms in part_ms.items():
+        e = {"ms": ms}
+        if name in wl.extra:
+            e["TFLOP/s"] = wl.extra[name]["flop"] / (ms * 1e-3) / 1e12
+            e["GB/s"] = wl.extra[name]["bytes"] / (ms * 1e-3) / 1e9
+            e["mfma_frac"] = e["TFLOP/s"] / BF16_MFMA_PEAK_TFS
+            e["hbm_frac"] = e["GB/s"] / HBM_PEAK_GBS
+        breakdown[name] = e
     achieved = wl.eff_bytes / (kernel_ms * 1e-3) / 1e9
-    traffic = measured_traffic(wl.kernel_key)
     line = {
-        "metric": "MSDA samples/sec + effective HBM GB/s, BEVFormer-base SCA layer (6 cams)",
+        "metric": METRIC,
         "value": wl.samples / (ms_per_step * 1e-3),
         "unit": "samples/s",
         "n_gpus": 1,
@@ -269,11 +321,12 @@ def main():
         "data": "synthetic (seeded, BEVFormer-shaped; no dataset or trained weights)",
         "config": wl.config,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
                      "kernel": wl.kernel_key.rsplit("_", 1)[0], "kernel_ms": kernel_ms,
                      "effective_bytes_per_launch": wl.eff_bytes, "gathered_bytes_per_launch": wl.gathered_bytes},
         "effective_GBps_per_step": wl.eff_bytes / (ms_per_step * 1e-3) / 1e9,
         "samples_per_step": wl.samples,
+        "breakdown": breakdown,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = wl.cpu_baseline()
