@@ -166,8 +166,11 @@ static msda::CompactArgs compact_args(const uint8_t* bev_mask, const float* refe
   c.pair_offsets = pair_offsets ? pair_offsets : reinterpret_cast<int32_t*>(ws + lay.pair_offsets);
   c.pair_q = pair_q ? pair_q : reinterpret_cast<int32_t*>(ws + lay.pair_q);
   c.bin_hist = reinterpret_cast<int32_t*>(ws + lay.bin_hist);
+  c.seg_seen = reinterpret_cast<int32_t*>(ws + lay.seg_seen);
+  c.seg_pairs = reinterpret_cast<int32_t*>(ws + lay.seg_pairs);
   c.bin_offsets = reinterpret_cast<int32_t*>(ws + lay.bin_offsets);
   c.order = reinterpret_cast<int32_t*>(ws + lay.order);
+  c.clear_ints = lay.clear_ints;
   return c;
 }
 
@@ -230,7 +233,8 @@ int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes
   a.logits = attention_logits;
   a.cammask = c.cammask;
   a.order = c.order;
-  a.n_order = c.bin_offsets + B * Ncam * msda::kOrderBins;
+  a.order_at = c.bin_offsets;
+  a.order_stride = (int)Ncam * msda::kOrderBins;
   a.Ncam = (int)Ncam;
   a.D = D;
   a.B = B;

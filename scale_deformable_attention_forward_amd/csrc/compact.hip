@@ -4,17 +4,18 @@
 // which the gather kernel visits the seen queries.
 //
 // Four small stream-ordered kernels:
-//   0. clear: zero the ordering histogram;
+//   0. clear: zero the ordering histogram and the per-segment totals;
 //   1. visibility: per (b, q) the bit set of cameras that see q (any of the D
 //      anchors marked), the hit count, per (b, c, tile of 256 queries) the
 //      number of seen queries, and for a seen query its ordering bin: the
 //      image tile (kOrderBinsX columns x kOrderBinsY rows, column-major) of
 //      the first marked anchor of its first camera, within the segment
 //      (b, first camera);
-//   2. scan: one workgroup turns the tile counts (in b, c, tile order) into
-//      exclusive offsets -- pair_offsets[b*Ncam + c] is the offset of the
-//      first tile of (b, c) and pair_offsets[B*Ncam] the total -- and the
-//      bin histogram into bin offsets;
+//   2. scan: one workgroup per segment (b, c) turns the segment's tile counts
+//      and bin counts into exclusive offsets, starting from the sums of the
+//      earlier segments' totals (which the visibility kernel accumulated):
+//      pair_offsets[b*Ncam + c] is the offset of the first tile of (b, c)
+//      and pair_offsets[B*Ncam] the total;
 //   3. compact: each query writes its index at tile offset + (seen queries
 //      before it in the tile) for every camera that sees it, so each (b, c)
 //      list comes out in ascending order (deterministic, no atomics); and a
@@ -33,7 +34,8 @@ namespace msda {
 
 constexpr int kTile = 256;  // queries per tile = threads per block
 constexpr int kTileWaves = kTile / kWave;
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = kOrderBins;  // one bin per thread
+static_assert(kScanThreads == 1024, "the scan block holds one segment's bins");
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -54,7 +56,12 @@ CompactLayout compact_layout(int64_t B, int64_t Ncam, int64_t Nq) {
   l.tile_offsets = take(sizeof(int32_t) * segs * (size_t)l.tiles);
   l.pair_offsets = take(sizeof(int32_t) * (segs + 1));
   l.pair_q = take(sizeof(int32_t) * segs * (size_t)Nq);
-  l.bin_hist = take(sizeof(int32_t) * segs * kOrderBins);
+  // bin_hist, seg_seen and seg_pairs back to back (no alignment gaps)
+  l.bin_hist = o;
+  l.seg_seen = l.bin_hist + sizeof(int32_t) * segs * kOrderBins;
+  l.seg_pairs = l.seg_seen + sizeof(int32_t) * segs;
+  l.clear_ints = (int)(segs * kOrderBins + 2 * segs);
+  o = align_up(l.seg_pairs + sizeof(int32_t) * segs, 256);
   l.bin_offsets = take(sizeof(int32_t) * (segs * kOrderBins + 1));
   l.order = take(sizeof(int32_t) * nq);
   l.total = o;
@@ -74,6 +81,7 @@ __device__ inline int tile_bin(float v, int n) {
 template <bool kWordMask>
 __global__ __launch_bounds__(kTile) void sca_visibility_kernel(CompactArgs a, int tiles) {
   __shared__ int wave_counts[kTileWaves][32];
+  __shared__ int first_counts[kTileWaves][32];
   const int tile = blockIdx.x, b = blockIdx.y;
   const int q = tile * kTile + (int)threadIdx.x;
   const bool in_range = q < a.Nq;
@@ -110,55 +118,92 @@ __global__ __launch_bounds__(kTile) void sca_visibility_kernel(CompactArgs a, in
     a.qkey[bq] = key;
   }
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int first = seen != 0u ? __builtin_ctz(seen) : -1;
   for (int c = 0; c < a.Ncam; ++c) {
     const uint64_t bits = __ballot((seen >> c) & 1u);
-    if (lane == 0) wave_counts[wave][c] = __popcll(bits);
+    const uint64_t firsts = __ballot(first == c);
+    if (lane == 0) {
+      wave_counts[wave][c] = __popcll(bits);
+      first_counts[wave][c] = __popcll(firsts);
+    }
   }
   __syncthreads();
   if ((int)threadIdx.x < a.Ncam) {
     const int c = threadIdx.x;
-    int s = 0;
-    for (int w = 0; w < kTileWaves; ++w) s += wave_counts[w][c];
+    int s = 0, f = 0;
+    for (int w = 0; w < kTileWaves; ++w) {
+      s += wave_counts[w][c];
+      f += first_counts[w][c];
+    }
     a.tile_counts[((int64_t)b * a.Ncam + c) * tiles + tile] = s;
+    if (s) atomicAdd(&a.seg_pairs[b * a.Ncam + c], s);
+    if (f) atomicAdd(&a.seg_seen[b * a.Ncam + c], f);
   }
 }
 
-// Exclusive scan of in[0, n) into out[0, n) by one block of kScanThreads;
-// returns the total in every thread.  `every`/`firsts`: out[i] is also
-// written to firsts[i / every] when i % every == 0 (may be null).
-__device__ int block_exclusive_scan(const int32_t* __restrict__ in, int32_t* __restrict__ out, int n, int every,
-                                    int32_t* __restrict__ firsts, int* part) {
-  const int t = threadIdx.x;
-  const int per = (n + kScanThreads - 1) / kScanThreads;
-  const int lo = min(n, t * per), hi = min(n, lo + per);
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += in[i];
-  __syncthreads();  // part[] may still be read by a previous scan
-  part[t] = s;
+// Exclusive scan of one value per thread over the block (kScanThreads);
+// also returns the block total.
+__device__ int block_exclusive_scan(int v, int* total) {
+  __shared__ int wave_sums[kScanThreads / kWave];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int u = __shfl_up(incl, d);
+    if (lane >= d) incl += u;
+  }
+  __syncthreads();  // wave_sums may still be read by a previous scan
+  if (lane == kWave - 1) wave_sums[wave] = incl;
   __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {  // inclusive scan of the partial sums
-    const int v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kScanThreads / kWave; ++w) {
+    const int ws = wave_sums[w];
+    before += w < wave ? ws : 0;
+    all += ws;
   }
-  int run = part[t] - s;
-  for (int i = lo; i < hi; ++i) {
-    if (firsts && i % every == 0) firsts[i / every] = run;
-    out[i] = run;
-    run += in[i];
-  }
-  return part[kScanThreads - 1];
+  *total = all;
+  return before + incl - v;
 }
 
+// Sum of x[0, n) over the block.
+__device__ int block_sum(const int32_t* __restrict__ x, int n) {
+  __shared__ int partial[kScanThreads / kWave];
+  int s = 0;
+  for (int i = threadIdx.x; i < n; i += kScanThreads) s += x[i];
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) s += __shfl_xor(s, d);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) partial[threadIdx.x / kWave] = s;
+  __syncthreads();
+  int all = 0;
+  for (int w = 0; w < kScanThreads / kWave; ++w) all += partial[w];
+  return all;
+}
+
+// One block per segment s = b*Ncam + c.
 __global__ __launch_bounds__(kScanThreads) void sca_scan_kernel(CompactArgs a, int tiles) {
-  __shared__ int part[kScanThreads];
-  const int segs = a.B * a.Ncam;
-  const int pairs = block_exclusive_scan(a.tile_counts, a.tile_offsets, segs * tiles, tiles, a.pair_offsets, part);
-  if (threadIdx.x == 0) a.pair_offsets[segs] = pairs;
-  const int nbins = segs * kOrderBins;
-  const int seen = block_exclusive_scan(a.bin_hist, a.bin_offsets, nbins, 1, nullptr, part);
-  if (threadIdx.x == 0) a.bin_offsets[nbins] = seen;
+  const int s = blockIdx.x, segs = a.B * a.Ncam;
+  const int t = threadIdx.x;
+  const int base_seen = block_sum(a.seg_seen, s);
+  const int base_pairs = block_sum(a.seg_pairs, s);
+  int total = 0;
+  const int64_t bin = (int64_t)s * kOrderBins + t;
+  a.bin_offsets[bin] = base_seen + block_exclusive_scan(a.bin_hist[bin], &total);
+  int run = base_pairs;
+  for (int t0 = 0; t0 < tiles; t0 += kScanThreads) {
+    const int64_t i = (int64_t)s * tiles + t0 + t;
+    const int v = t0 + t < tiles ? a.tile_counts[i] : 0;
+    const int excl = block_exclusive_scan(v, &total);
+    if (t0 + t < tiles) a.tile_offsets[i] = run + excl;
+    run += total;
+  }
+  if (t == 0) {
+    a.pair_offsets[s] = base_pairs;
+    if (s == segs - 1) {
+      a.pair_offsets[segs] = base_pairs + a.seg_pairs[s];
+      a.bin_offsets[(int64_t)segs * kOrderBins] = base_seen + a.seg_seen[s];
+    }
+  }
 }
 
 __global__ __launch_bounds__(kTile) void sca_compact_kernel(CompactArgs a, int tiles) {
@@ -191,8 +236,7 @@ __global__ __launch_bounds__(kTile) void sca_compact_kernel(CompactArgs a, int t
 }
 
 hipError_t launch_sca_compact(const CompactArgs& a, int tiles, hipStream_t stream) {
-  const int nbins = a.B * a.Ncam * kOrderBins;
-  sca_clear_kernel<<<(nbins + kTile - 1) / kTile, kTile, 0, stream>>>(a.bin_hist, nbins);
+  sca_clear_kernel<<<(a.clear_ints + kTile - 1) / kTile, kTile, 0, stream>>>(a.bin_hist, a.clear_ints);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(tiles, a.B);
@@ -203,7 +247,7 @@ hipError_t launch_sca_compact(const CompactArgs& a, int tiles, hipStream_t strea
     sca_visibility_kernel<false><<<grid, kTile, 0, stream>>>(a, tiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  sca_scan_kernel<<<1, kScanThreads, 0, stream>>>(a, tiles);
+  sca_scan_kernel<<<a.B * a.Ncam, kScanThreads, 0, stream>>>(a, tiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   sca_compact_kernel<<<grid, kTile, 0, stream>>>(a, tiles);

@@ -306,15 +306,19 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void sca_gather_kernel(Ga
   uint2* rows = reinterpret_cast<uint2*>(smem + sizeof(Level) * kMaxLevels) +
                 ((size_t)wave * kHeadSlots + g) * meta_stride(a.LP);
   const uint32_t row_bytes = kBF16 ? 64u : 128u;
-  // the work list comes from sca_compact; clamp so that a workspace that
-  // never saw one cannot send a read out of bounds
   const int64_t n_queries = a.B * a.Nq;
-  int64_t n_items = *a.n_order;
-  n_items = n_items < 0 ? 0 : (n_items > n_queries ? n_queries : n_items);
   const uint32_t cam_bits = a.Ncam >= 32 ? 0xffffffffu : ((1u << a.Ncam) - 1u);
 
-  XcdSplit split(n_items, waves_per_block);
-  for (int64_t item = split.begin; item < split.end; item += split.stride) {
+  // Batch item by batch item, each die takes an eighth of the item's work
+  // list, so the dies share one item's value maps at a time.  The list comes
+  // from sca_compact; clamping keeps a workspace that never saw one from
+  // sending a read out of bounds.
+  for (int64_t bi = 0; bi < a.B; ++bi) {
+  int64_t lo = a.order_at[bi * a.order_stride], hi = a.order_at[(bi + 1) * a.order_stride];
+  lo = lo < 0 ? 0 : (lo > n_queries ? n_queries : lo);
+  hi = hi < lo ? lo : (hi > n_queries ? n_queries : hi);
+  XcdSplit split(hi - lo, waves_per_block);
+  for (int64_t item = lo + split.begin; item < lo + split.end; item += split.stride) {
     const int64_t bq = uniform((int64_t)a.order[item]);
     if (bq < 0 || bq >= n_queries) continue;
     const int64_t b = bq / a.Nq, q = bq % a.Nq;
@@ -362,6 +366,7 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void sca_gather_kernel(Ga
       }
       if (head_ok) reinterpret_cast<float4*>(a.out + ((bq * a.nH + h) * 32))[j] = scaled(acc, __popc(seen));
     }
+  }
   }
 
   // queries no camera sees are on no pair list: their rows are zero

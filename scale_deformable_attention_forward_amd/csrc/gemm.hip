@@ -4,22 +4,23 @@
 // 8 个 Head 交互", sections 3 and 11).
 //
 // With K = N = 256 the projection moves 512 B in and 512 B (bf16) or 1 KB
-// (fp32) out per row for 131 kFLOP, well below the bf16 ridge point, so it is
-// bound by HBM, not by the matrix cores.  The design keeps the weights out of
-// the memory stream:
-//   - a block is 4 waves; wave w owns 64 output columns and holds its 64 x K
-//     slice of W in registers as MFMA B operands for the whole (persistent)
-//     kernel;
-//   - the block walks 32-row tiles of X (tiles split per die, contiguous);
-//     each tile is read once from HBM into LDS (fp32 input is rounded to
-//     bf16, ties to even, on the way), and every wave reads its A operands
-//     from there;
-//   - v_mfma_f32_16x16x32_bf16: per tile each wave issues 2 (rows) x 4
-//     (columns) x K/32 instructions; accumulators are 2 x 4 x 4 fp32;
-//   - epilogue adds the bias and stores fp32, or bf16 rounded to nearest even.
+// (fp32) out per row for 131 kFLOP, below the bf16 ridge point, so it is
+// bound by HBM; the design keeps the X stream flowing and W out of it:
+//   - a block is 8 waves over 256 output columns; wave w holds its 32 x K
+//     slice of W in registers as MFMA A operands for the whole persistent
+//     kernel (grid y covers N beyond 256);
+//   - the block walks 64-row tiles of X (tiles split per die, contiguous),
+//     double-buffered in LDS: the loads of tile t+1 are issued before tile t
+//     is multiplied and land in the other buffer afterwards (fp32 X is
+//     rounded to bf16, ties to even, on the way); 16-byte chunks are XOR-
+//     swizzled by row so the MFMA operand reads hit 16 different banks;
+//   - v_mfma_f32_16x16x32_bf16 with W as the A and X as the B operand, so the
+//     result tile is transposed: each lane ends with 4 consecutive output
+//     columns of one row and stores them with one 16-byte (fp32) or 8-byte
+//     (bf16) write, after adding the bias.
 // MFMA operand layout used: lane l supplies row (A) or column (B) l % 16 and
-// 8 consecutive k values of a 32-wide k step; result element (i, j) sits in
-// lane j + 16*(i/4), register i % 4.
+// 8 consecutive k of a 32-wide k step; result element (i, j) sits in lane
+// j + 16*(i/4), register i % 4.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -28,13 +29,15 @@ namespace msda {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 32;            // rows per tile
-constexpr int kGemmWaves = 4;
-constexpr int kColsPerWave = 64;   // 4 MFMA column tiles of 16
+constexpr int kGemmWaves = 8;
+constexpr int kGemmThreads = kGemmWaves * kWave;
+constexpr int kColsPerWave = 32;  // 2 MFMA tiles of 16 columns
 constexpr int kBN = kGemmWaves * kColsPerWave;
+constexpr int kBM = 64;           // rows per tile: 4 MFMA tiles of 16 rows
 constexpr int kMaxK = 256;
 constexpr int kMaxKSteps = kMaxK / 32;
-constexpr int kRowPad = 8;         // bf16 elements of padding per LDS row (spreads banks)
+constexpr int kChunks = kMaxK / 8;                     // 16-byte chunks per row
+constexpr int kLoadsPerThread = kBM * kChunks / kGemmThreads;  // 4
 
 __device__ inline uint32_t bf16_rne_bits(float f) {
   uint32_t u = __float_as_uint(f);
@@ -45,90 +48,130 @@ __device__ inline uint32_t bf16_rne_bits(float f) {
 
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) { return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16); }
 
-__global__ __launch_bounds__(kGemmWaves* kWave) void gemm_bf16_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint16_t xs[kBM][kMaxK + kRowPad];
-  const int lane = threadIdx.x % kWave;
-  const int wave = uniform(threadIdx.x / kWave);
-  const int ksteps = a.K / 32;
-  const int col0 = blockIdx.y * kBN + wave * kColsPerWave;
-  const int lrow = lane % 16, lk = 8 * (lane / 16);
+// swizzled position of 16-byte chunk c of row r inside a tile buffer
+__device__ inline int chunk_at(int r, int c) { return r * kChunks + (c ^ (r & 15)); }
 
-  // this wave's W slice as B operands, resident for the whole kernel
-  bf16x8_t wop[4][kMaxKSteps];
-  float bias[4];
+struct TileLoad {
+  uint4 v[kLoadsPerThread];
+
+  // Issue the loads of rows [m0, m0 + kBM) (rows past M read zero).
+  __device__ inline void issue(const GemmArgs& a, int64_t m0, int row_chunks) {
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int n = col0 + 16 * nt + lrow;
-    bias[nt] = (a.bias && n < a.N) ? a.bias[n] : 0.f;
+    for (int i = 0; i < kLoadsPerThread; ++i) {
+      const int e = threadIdx.x + i * kGemmThreads;
+      const int r = e / kChunks, c = e % kChunks;
+      const int64_t m = m0 + r;
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (c < row_chunks && m < a.M) {
+        if (a.x_f32) {
+          const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.X) + m * a.K + 8 * c);
+          const float4 p = src[0], q = src[1];
+          v[i] = make_uint4(pack_bf16x2(p.x, p.y), pack_bf16x2(p.z, p.w), pack_bf16x2(q.x, q.y),
+                            pack_bf16x2(q.z, q.w));
+        } else {
+          v[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.X) + m * a.K + 8 * c);
+        }
+      }
+    }
+  }
+
+  __device__ inline void store(uint4* buf) const {
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i) {
+      const int e = threadIdx.x + i * kGemmThreads;
+      buf[chunk_at(e / kChunks, e % kChunks)] = v[i];
+    }
+  }
+};
+
+__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs a) {
+  __shared__ uint4 xs[2][kBM * kChunks];  // two 64 x 256 bf16 tiles, 64 KB
+  const int lane = threadIdx.x % kWave;
+  const int wave = uniform((int)(threadIdx.x / kWave));
+  const int ksteps = a.K / 32;
+  const int row_chunks = a.K / 8;
+  const int col0 = blockIdx.y * kBN + wave * kColsPerWave;
+  const int l16 = lane % 16, lg = lane / 16;
+
+  // this wave's W slice as A operands, resident for the whole kernel
+  bf16x8_t wop[2][kMaxKSteps];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = col0 + 16 * nt + l16;
 #pragma unroll
     for (int ks = 0; ks < kMaxKSteps; ++ks) {
       bf16x8_t v = {};
-      if (ks < ksteps && n < a.N) v = *reinterpret_cast<const bf16x8_t*>(a.W + (int64_t)n * a.K + 32 * ks + lk);
+      if (ks < ksteps && n < a.N) v = *reinterpret_cast<const bf16x8_t*>(a.W + (int64_t)n * a.K + 32 * ks + 8 * lg);
       wop[nt][ks] = v;
     }
+  }
+  // bias of the 4 output columns this lane stores per column tile
+  float4 bias[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = col0 + 16 * nt + 4 * lg;
+    bias[nt] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.bias && n < a.N) bias[nt] = make_float4(a.bias[n], a.bias[n + 1], a.bias[n + 2], a.bias[n + 3]);
   }
 
   const int64_t tiles = (a.M + kBM - 1) / kBM;
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds, nlocal = gridDim.x / kXcds;
-  const int64_t t_end = tiles * (xcd + 1) / kXcds;
-  const int chunks = kBM * a.K / 8;  // 8-element chunks per tile
-  const int row_chunks = a.K / 8;
-  for (int64_t t = tiles * xcd / kXcds + local; t < t_end; t += nlocal) {
-    const int64_t m0 = t * kBM;
-    for (int e = threadIdx.x; e < chunks; e += kGemmWaves * kWave) {
-      const int r = e / row_chunks, kc = (e % row_chunks) * 8;
-      const int64_t m = m0 + r;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (m < a.M) {
-        if (a.x_f32) {
-          const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.X) + m * a.K + kc);
-          const float4 p = src[0], q = src[1];
-          v = make_uint4(pack_bf16x2(p.x, p.y), pack_bf16x2(p.z, p.w), pack_bf16x2(q.x, q.y), pack_bf16x2(q.z, q.w));
-        } else {
-          v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.X) + m * a.K + kc);
-        }
-      }
-      *reinterpret_cast<uint4*>(&xs[r][kc]) = v;
-    }
-    __syncthreads();
+  const int64_t t_begin = tiles * xcd / kXcds + local, t_end = tiles * (xcd + 1) / kXcds;
+  if (t_begin >= t_end) return;  // uniform over the block
 
-    f32x4_t acc[2][4];
+  TileLoad next;
+  next.issue(a, t_begin * kBM, row_chunks);
+  next.store(xs[0]);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t t = t_begin; t < t_end; t += nlocal) {
+    const int64_t t_next = t + nlocal;
+    if (t_next < t_end) next.issue(a, t_next * kBM, row_chunks);  // in flight during the MFMAs
+
+    f32x4_t acc[4][2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const uint4* cur = xs[buf];
 #pragma unroll
     for (int ks = 0; ks < kMaxKSteps; ++ks) {
       if (ks < ksteps) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8_t aop = *reinterpret_cast<const bf16x8_t*>(&xs[16 * mt + lrow][32 * ks + lk]);
+        for (int mt = 0; mt < 4; ++mt) {
+          const uint4 raw = cur[chunk_at(16 * mt + l16, 4 * ks + lg)];
+          const bf16x8_t xop = __builtin_bit_cast(bf16x8_t, raw);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, wop[nt][ks], acc[mt][nt], 0, 0, 0);
+          for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop[nt][ks], xop, acc[mt][nt], 0, 0, 0);
         }
       }
     }
-    __syncthreads();  // the next tile overwrites xs
 
+    // acc[mt][nt][i] = Y[m0 + 16 mt + l16][col0 + 16 nt + 4 lg + i]
+    const int64_t m0 = t * kBM;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 4; ++mt) {
+      const int64_t m = m0 + 16 * mt + l16;
+      if (m >= a.M) continue;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int n = col0 + 16 * nt + lrow;
+      for (int nt = 0; nt < 2; ++nt) {
+        const int n = col0 + 16 * nt + 4 * lg;
         if (n >= a.N) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t m = m0 + 16 * mt + 4 * (lane / 16) + i;
-          if (m >= a.M) continue;
-          const float y = acc[mt][nt][i] + bias[nt];
-          if (a.y_f32)
-            static_cast<float*>(a.Y)[m * a.N + n] = y;
-          else
-            static_cast<uint16_t*>(a.Y)[m * a.N + n] = (uint16_t)bf16_rne_bits(y);
+        const float4 y = make_float4(acc[mt][nt][0] + bias[nt].x, acc[mt][nt][1] + bias[nt].y,
+                                     acc[mt][nt][2] + bias[nt].z, acc[mt][nt][3] + bias[nt].w);
+        if (a.y_f32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.Y) + m * a.N + n) = y;
+        } else {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.Y) + m * a.N + n) =
+              make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
         }
       }
     }
+
+    if (t_next < t_end) next.store(xs[buf ^ 1]);
+    __syncthreads();  // the next tile is in place and nobody reads this one any more
+    buf ^= 1;
   }
 }
 
@@ -136,7 +179,8 @@ static int gemm_cus() {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
       cus = n;
     else
       cus = 256;
@@ -146,11 +190,11 @@ static int gemm_cus() {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = (a.M + kBM - 1) / kBM;
-  int64_t bx = (int64_t)gemm_cus() * 2;
+  int64_t bx = (int64_t)gemm_cus();  // one 8-wave block per CU (register-bound)
   if (bx > tiles) bx = tiles;
   bx = (bx + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)bx, (unsigned)((a.N + kBN - 1) / kBN));
-  gemm_bf16_kernel<<<grid, kGemmWaves * kWave, 0, stream>>>(a);
+  gemm_bf16_kernel<<<grid, kGemmThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ struct GatherArgs {
   const float* logits;    // [B][Nq][nH][L*P]
   const uint32_t* cammask;  // [B][Nq] bit c = camera c sees the query
   const int32_t* order;     // seen queries b*Nq + q, in locality order
-  const int32_t* n_order;   // device: number of entries in order
+  const int32_t* order_at;  // device: batch item b's entries are [order_at[b*stride], order_at[(b+1)*stride])
+  int order_stride;
   int Ncam, D;
   int64_t B, Nq;
   float* out;  // [B][Nq][nH*32]
@@ -45,8 +46,11 @@ hipError_t launch_sca_gather(const GatherArgs& a, hipStream_t stream);
 constexpr int kOrderBinsX = 64, kOrderBinsY = 16, kOrderBins = kOrderBinsX * kOrderBinsY;
 
 struct CompactLayout {
-  size_t cammask, qkey, tile_counts, tile_offsets, pair_offsets, pair_q, bin_hist, bin_offsets, order, total;
+  // bin_hist, seg_seen and seg_pairs are adjacent: one clear covers them
+  size_t cammask, qkey, tile_counts, tile_offsets, pair_offsets, pair_q, bin_hist, seg_seen, seg_pairs,
+      bin_offsets, order, total;
   int tiles;  // tiles of the query axis per (b, c)
+  int clear_ints;  // int32 entries from bin_hist on to zero before a compaction
 };
 CompactLayout compact_layout(int64_t B, int64_t Ncam, int64_t Nq);
 
@@ -62,8 +66,11 @@ struct CompactArgs {
   int32_t* pair_offsets;
   int32_t* pair_q;
   int32_t* bin_hist;     // [B*Ncam*kOrderBins]
+  int32_t* seg_seen;     // [B*Ncam] seen queries whose first camera is c, per (b, c)
+  int32_t* seg_pairs;    // [B*Ncam] pairs per (b, c)
   int32_t* bin_offsets;  // [B*Ncam*kOrderBins + 1]; the last entry counts the seen queries
   int32_t* order;        // [B*Nq]
+  int clear_ints;
 };
 hipError_t launch_sca_compact(const CompactArgs& a, int tiles, hipStream_t stream);
 
