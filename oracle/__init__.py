@@ -46,12 +46,15 @@ def _load(path=None):
     lib.oracle_sca.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
                                _int, _int, _p, _i64, _p, _p, _p, _p]
     lib.oracle_linear_bf16.argtypes = [_p, _int, _p, _p, _i64, _i64, _i64, _p]
+    lib.oracle_query_proj.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _i64, _p, _p]
+    lib.oracle_output_proj.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_double, _i64, _i64, _i64, _p]
     lib.oracle_round_to_bf16.argtypes = [_p, _i64, _p]
     lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
     lib.oracle_double_to_bf16.restype = ctypes.c_uint16
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_double.restype = ctypes.c_double
-    for f in (lib.oracle_msda, lib.oracle_msda_frames, lib.oracle_sca, lib.oracle_linear_bf16):
+    for f in (lib.oracle_msda, lib.oracle_msda_frames, lib.oracle_sca, lib.oracle_linear_bf16,
+              lib.oracle_query_proj, lib.oracle_output_proj):
         f.restype = _int
     _lib = lib
     return lib
@@ -181,6 +184,57 @@ def linear_bf16(X, W, bias=None):
     rc = lib.oracle_linear_bf16(xp, xf, wp, bp, M, N, K, Y.ctypes.data_as(_p))
     _check(rc, "oracle_linear_bf16")
     del x, w, b
+    return Y
+
+
+def _opt(a, dtype):
+    if a is None:
+        return None, None
+    return _c(a, dtype)
+
+
+def query_proj(query, query_pos, W_off, b_off, W_att, b_att):
+    """Sampling offsets and attention logits from the query: q~ = query +
+    query_pos in float32, then W_off q~ + b_off and W_att q~ + b_att from bf16
+    operands.  query, query_pos float32 [M,K] (query_pos may be None);
+    W_* uint16 bf16 bits [N_*,K]; b_* float32 [N_*] or None.  Returns
+    (offsets [M,N_off], logits [M,N_att]) float64."""
+    lib = _load()
+    M, K = query.shape
+    N_off, N_att = W_off.shape[0], W_att.shape[0]
+    q, qp = _c(query, np.float32)
+    e, ep = _opt(query_pos, np.float32)
+    wo, wop = _c(W_off, np.uint16)
+    bo, bop = _opt(b_off, np.float32)
+    wa, wap = _c(W_att, np.uint16)
+    ba, bap = _opt(b_att, np.float32)
+    off = np.zeros((M, N_off), np.float64)
+    lg = np.zeros((M, N_att), np.float64)
+    rc = lib.oracle_query_proj(qp, ep, M, K, wop, bop, N_off, wap, bap, N_att, off.ctypes.data_as(_p),
+                               lg.ctypes.data_as(_p))
+    _check(rc, "oracle_query_proj")
+    del q, e, wo, bo, wa, ba
+    return off, lg
+
+
+def output_proj(slots, W, bias=None, residual=None, gamma=None, beta=None, eps=1e-5):
+    """residual + (W bf16(slots) + bias), then the layer norm with gamma and
+    beta when gamma is given.  slots float32 [M,K]; W uint16 [N,K]; bias,
+    gamma, beta float32 [N] or None; residual float32 [M,N] or None.
+    Returns [M,N] float64."""
+    lib = _load()
+    M, K = slots.shape
+    N = W.shape[0]
+    x, xp = _c(slots, np.float32)
+    w, wp = _c(W, np.uint16)
+    b, bp = _opt(bias, np.float32)
+    r, rp = _opt(residual, np.float32)
+    g, gp = _opt(gamma, np.float32)
+    be, bep = _opt(beta, np.float32)
+    Y = np.zeros((M, N), np.float64)
+    rc = lib.oracle_output_proj(xp, wp, bp, rp, gp, bep, float(eps), M, N, K, Y.ctypes.data_as(_p))
+    _check(rc, "oracle_output_proj")
+    del x, w, b, r, g, be
     return Y
 
 

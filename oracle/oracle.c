@@ -45,7 +45,13 @@
  *   - frames (two stacked BEV maps, temporal workload): two independent MSDAs,
  *     each with its own softmax, then the arithmetic mean over frames.  The
  *     pages do not describe this variant; parity of the frame mean rests on
- *     the invariants in the tests (identical frames, zero frame, symmetry).
+ *     the invariants in the tests (identical frames, zero frame, symmetry);
+ *   - bf16 projections: operands rounded to the nearest bf16 (ties to even),
+ *     products summed exactly enough in double; the query-side input is the
+ *     float32 sum query + position embedding ([8-heads] 4);
+ *   - the encoder layer's norm after the residual ([8-heads] 18.7) is the
+ *     plain layer norm over the row (variance with divisor N, eps inside the
+ *     square root, then gamma and beta); the pages name it only.
  */
 #include <math.h>
 #include <stdint.h>
@@ -438,5 +444,82 @@ int oracle_linear_bf16(const void* X, int x_is_f32, const uint16_t* W, const flo
         }
     }
     free(xrow);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Query projections ([8-heads] 4.1, 4.2 and 18.3)                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The vector that predicts the sampling parameters is the query plus its
+ * position embedding ([8-heads] 4).  In the model both are float32 tensors,
+ * so their sum is a float32 tensor: it is formed here with one float32
+ * addition (the file is compiled without contraction or excess precision).
+ * Then offsets = W_off q~ + b_off ([8-heads] 4.1, N_off = heads x levels x
+ * points x 2) and logits = W_att q~ + b_att ([8-heads] 4.2, N_att = heads x
+ * levels x points), each a bf16-operand linear map as in oracle_linear_bf16
+ * (q~ rounded to the nearest bf16).  query_pos may be NULL (no embedding).
+ */
+int oracle_query_proj(const float* query, const float* query_pos, int64_t M, int64_t K,
+                      const uint16_t* W_off, const float* b_off, int64_t N_off,
+                      const uint16_t* W_att, const float* b_att, int64_t N_att,
+                      double* offsets, double* logits)
+{
+    if (!query || !W_off || !W_att || !offsets || !logits || M < 0 || K < 1 || N_off < 1 || N_att < 1)
+        return ORACLE_BAD_ARG;
+    float* qt = (float*)malloc(sizeof(float) * (size_t)K);
+    if (!qt) return ORACLE_BAD_ARG;
+    int rc = ORACLE_OK;
+    for (int64_t i = 0; i < M && rc == ORACLE_OK; ++i) {
+        for (int64_t k = 0; k < K; ++k) {
+            float s = query[i * K + k];
+            if (query_pos) s = s + query_pos[i * K + k];
+            qt[k] = s;
+        }
+        rc = oracle_linear_bf16(qt, 1, W_off, b_off, 1, N_off, K, offsets + i * N_off);
+        if (rc == ORACLE_OK) rc = oracle_linear_bf16(qt, 1, W_att, b_att, 1, N_att, K, logits + i * N_att);
+    }
+    free(qt);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Output projection, residual and the layer's norm ([8-heads] 11, 18.6-7)  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * o = W_o bf16(slots) + b_o (oracle_linear_bf16 with the float32 slots
+ * rounded to the nearest bf16); q^ = residual + o, the dropout on the update
+ * branch being the identity at inference ([8-heads] 18.6; residual may be
+ * NULL: no residual).  With gamma given, the encoder layer's norm that
+ * follows ([8-heads] 18.7): each row of q^ is centred on its mean, divided by
+ * sqrt(variance + eps) with the variance taken over the row's N entries
+ * (divisor N), then multiplied by gamma and shifted by beta (NULL beta: 0).
+ * The pages name the norm but not its formula; this is the plain layer norm.
+ */
+int oracle_output_proj(const float* slots, const uint16_t* W, const float* bias, const float* residual,
+                       const float* gamma, const float* beta, double eps, int64_t M, int64_t N, int64_t K,
+                       double* Y)
+{
+    if (!slots || !W || !Y || M < 0 || N < 1 || K < 1) return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < M; ++i) {
+        double* y = Y + i * N;
+        int rc = oracle_linear_bf16(slots + i * K, 1, W, bias, 1, N, K, y);
+        if (rc != ORACLE_OK) return rc;
+        if (residual)
+            for (int64_t n = 0; n < N; ++n) y[n] += (double)residual[i * N + n];
+        if (gamma) {
+            double mean = 0.0;
+            for (int64_t n = 0; n < N; ++n) mean += y[n];
+            mean /= (double)N;
+            double var = 0.0;
+            for (int64_t n = 0; n < N; ++n) var += (y[n] - mean) * (y[n] - mean);
+            var /= (double)N;
+            double inv = 1.0 / sqrt(var + eps);
+            for (int64_t n = 0; n < N; ++n)
+                y[n] = (y[n] - mean) * inv * (double)gamma[n] + (beta ? (double)beta[n] : 0.0);
+        }
+    }
     return ORACLE_OK;
 }

@@ -494,6 +494,77 @@ def pin_linear_bf16():
     _close(oracle.linear_bf16(Xf, W), dec(tobf(Xf)) @ dec(W).T, 1e-13, "float32 input")
 
 
+def _tobf(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def _dec(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def pin_query_proj():
+    """Offsets and logits from the query ([8-heads] 4.1, 4.2): the predicting
+    vector is the float32 sum query + position embedding (formed here by
+    torch's float32 addition), rounded to bf16; each output is a float64
+    matmul of the decoded operands plus its own bias.  A sum whose exact
+    value lies just above a bf16 tie but whose float32 rounding lands on the
+    tie tells a float32 addition from an exact one."""
+    import torch
+    g = np.random.default_rng(131)
+    M, K, N_off, N_att = 11, 32, 48, 16
+    q = g.normal(size=(M, K)).astype(np.float32)
+    e = g.normal(size=(M, K)).astype(np.float32)
+    W_off, W_att = _tobf(g.normal(size=(N_off, K)) / 6), _tobf(g.normal(size=(N_att, K)) / 6)
+    b_off, b_att = g.normal(size=N_off).astype(np.float32), g.normal(size=N_att).astype(np.float32)
+    qt = (torch.from_numpy(q) + torch.from_numpy(e)).numpy()
+    x = _dec(_tobf(qt))
+    off, lg = oracle.query_proj(q, e, W_off, b_off, W_att, b_att)
+    _close(off, x @ _dec(W_off).T + b_off.astype(np.float64), 1e-13, "offsets")
+    _close(lg, x @ _dec(W_att).T + b_att.astype(np.float64), 1e-13, "logits")
+    off0, _ = oracle.query_proj(q, None, W_off, None, W_att, None)
+    _close(off0, _dec(_tobf(q)) @ _dec(W_off).T, 1e-13, "no embedding, no bias")
+    # 1 + 2^-8 is a bf16 tie (rounds to 1.0); + 2^-30 is lost in float32 but
+    # would lift an exact sum above the tie (to 1 + 2^-7)
+    q1 = np.full((1, K), 1.0 + 2.0 ** -8, np.float32)
+    e1 = np.full((1, K), 2.0 ** -30, np.float32)
+    eye = _tobf(np.eye(K))
+    got, _ = oracle.query_proj(q1, e1, eye, None, eye, None)
+    _close(got, np.ones((1, K)), 0.0, "float32 sum rounded to bf16")
+
+
+def pin_output_proj_layer_norm():
+    """Output projection, residual and the layer norm ([8-heads] 11, 18.6-7):
+    against torch's float64 layer_norm of residual + (decoded bf16 matmul +
+    bias); a closed form (a row of +a/-a has mean 0 and variance a^2, so it
+    maps to +-a/sqrt(a^2+eps) * gamma + beta); without gamma, the plain sum."""
+    import torch
+    g = np.random.default_rng(141)
+    M, K, N = 9, 32, 24
+    slots = g.normal(size=(M, K)).astype(np.float32)
+    W = _tobf(g.normal(size=(N, K)) / 6)
+    bias = g.normal(size=N).astype(np.float32)
+    res = g.normal(size=(M, N)).astype(np.float32)
+    gamma = g.uniform(0.5, 2.0, N).astype(np.float32)
+    beta = g.normal(size=N).astype(np.float32)
+    o = _dec(_tobf(slots)) @ _dec(W).T + bias.astype(np.float64)
+    _close(oracle.output_proj(slots, W, bias), o, 1e-13, "projection")
+    _close(oracle.output_proj(slots, W, bias, res), o + res, 1e-13, "residual")
+    for eps in (1e-5, 0.25):
+        ref = torch.nn.functional.layer_norm(torch.from_numpy(o + res), (N,), torch.from_numpy(gamma).double(),
+                                             torch.from_numpy(beta).double(), eps).numpy()
+        _close(oracle.output_proj(slots, W, bias, res, gamma, beta, eps), ref, 1e-12, f"layer norm eps={eps}")
+    a, eps = 0.75, 0.0625
+    row = np.where(np.arange(N) % 2 == 0, a, -a).astype(np.float32)[None, :]
+    zeroW = np.zeros((N, K), np.uint16)
+    got = oracle.output_proj(slots[:1], zeroW, None, row, np.full(N, 2.0, np.float32),
+                             np.full(N, 0.5, np.float32), eps)
+    _close(got, np.sign(row) * 2.0 * a / np.sqrt(a * a + eps) + 0.5, 1e-14, "alternating row")
+
+
 ALL_PINS = [
     pin_worked_example_two_heads,
     pin_scalar_times_sample,
@@ -510,4 +581,6 @@ ALL_PINS = [
     pin_sca_dense_reformulation,
     pin_bf16_rounding,
     pin_linear_bf16,
+    pin_query_proj,
+    pin_output_proj_layer_norm,
 ]

@@ -41,6 +41,14 @@ MUTANTS = [
     ("bf16_truncates", "rint(x / quantum)", "trunc(x / quantum)"),
     ("bf16_decode_shift", "(uint32_t)bits << 16", "(uint32_t)bits << 15"),
     ("linear_weight_transposed", "W[n * K + k]", "W[k * N + n]"),
+    ("query_pos_dropped", "if (query_pos) s = s + query_pos[i * K + k];", "(void)0;"),
+    ("query_pos_subtracted", "s = s + query_pos[i * K + k];", "s = s - query_pos[i * K + k];"),
+    ("offset_bias_dropped", "W_off, b_off, 1, N_off", "W_off, NULL, 1, N_off"),
+    ("residual_dropped", "y[n] += (double)residual[i * N + n];", "y[n] += 0.0;"),
+    ("norm_unbiased_variance", "var /= (double)N;", "var /= (double)(N - 1);"),
+    ("norm_eps_outside_sqrt", "1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
+    ("norm_mean_kept", "y[n] = (y[n] - mean) * inv", "y[n] = y[n] * inv"),
+    ("norm_gamma_ignored", "* inv * (double)gamma[n]", "* inv * 1.0"),
 ]
 
 

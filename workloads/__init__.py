@@ -16,6 +16,8 @@ Workloads (shapes follow BEVFormer-base and a Deformable-DETR encoder):
                        116x200/58x100/29x50/15x25, P=8, D=4 anchors, fp32 value
   4 temporal frames    B=1, 2 stacked 200x200 BEV maps, one level, P=4 per frame
   5 BEVFormer SCA      as 3 with B=4, bf16 projection input and weights
+    (and the whole layer: offsets and logits projected from the query, the
+    output projection followed by the residual and the layer norm)
 """
 import numpy as np
 
@@ -24,6 +26,7 @@ BEV_CAM_LEVELS = ((116, 200), (58, 100), (29, 50), (15, 25))
 
 # tensor ids inside one workload's seed sequence
 _T_VALUE, _T_REF, _T_OFF, _T_LOGIT, _T_MASK, _T_W_V, _T_W_O, _T_BIAS = range(8)
+_T_QUERY, _T_QPOS, _T_W_OFF, _T_W_ATT, _T_NORM = range(8, 13)
 
 
 def rng(cfg, tensor_id):
@@ -212,6 +215,36 @@ def bevformer_sca_bf16(cfg=5, B=4, bev=200, shapes=BEV_CAM_LEVELS, bias=False, *
     C = nH * Dh
     w["feat"] = bf16_bits_trunc(_normal(rng(cfg, _T_VALUE), (B_, Ncam, Nv, C)))
     w["W_v"], w["b_v"], w["W_o"], w["b_o"] = projection_weights(cfg, C, bias=bias)
+    return w
+
+
+def bevformer_layer_bf16(cfg=5, B=4, bev=200, shapes=BEV_CAM_LEVELS, bias=False, offset_px=2.0, **kw):
+    """Workload 5 widened to the whole attention layer: the sampling offsets
+    and logits come from the query instead of being drawn.  Adds
+    query, query_pos ~ N(0,1) float32 [B,Nq,256]; W_off bf16 [nH*L*P*2, 256]
+    ~ N(0, offset_px^2 / 512) and W_att bf16 [nH*L*P, 256] ~ N(0, 1/512), so
+    that with q~ = query + query_pos (variance 2) the offsets have the
+    N(0, offset_px) cells and the logits the N(0, 1) of workload 3; biases
+    zero (or N(0, 0.1) with bias=True); layer-norm gamma ~ 1 + N(0, 0.1) and
+    beta ~ N(0, 0.1).  The drawn sampling_offsets / attention_logits are
+    removed."""
+    w = bevformer_sca_bf16(cfg=cfg, B=B, bev=bev, shapes=shapes, bias=bias, offset_px=offset_px, **kw)
+    del w["sampling_offsets"], w["attention_logits"]
+    B_, Nq, nH, L, P = w["B"], w["Nq"], w["nH"], w["L"], w["P"]
+    C = nH * w["Dh"]
+    w["query"] = _normal(rng(cfg, _T_QUERY), (B_, Nq, C))
+    w["query_pos"] = _normal(rng(cfg, _T_QPOS), (B_, Nq, C))
+    n_off, n_att = nH * L * P * 2, nH * L * P
+    w["W_off"] = bf16_bits_trunc(_normal(rng(cfg, _T_W_OFF), (n_off, C), offset_px / np.sqrt(2.0 * C)))
+    w["W_att"] = bf16_bits_trunc(_normal(rng(cfg, _T_W_ATT), (n_att, C), 1.0 / np.sqrt(2.0 * C)))
+    if bias:
+        g = rng(cfg, _T_BIAS + 100)
+        w["b_off"], w["b_att"] = _normal(g, (n_off,), 0.1), _normal(g, (n_att,), 0.1)
+    else:
+        w["b_off"], w["b_att"] = np.zeros(n_off, np.float32), np.zeros(n_att, np.float32)
+    g = rng(cfg, _T_NORM)
+    w["gamma"] = (1.0 + _normal(g, (C,), 0.1)).astype(np.float32)
+    w["beta"] = _normal(g, (C,), 0.1)
     return w
 
 
