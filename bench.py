@@ -11,7 +11,9 @@ query) pairs (sca_compact) and the fused softmax / bilinear gather /
 weighted sum / camera mean (sca_gather).  Inputs are resident in HBM before
 timing starts.  Other workloads: "layer_bf16" (batch 4, bf16 value
 projection GEMM -> SCA on bf16 value -> bf16 output projection GEMM),
-"sca_bf16", "detr" (Deformable-DETR encoder MSDA), "tsa" (two stacked BEV
+"layer_full" (the same with the sampling offsets and logits projected from
+query + position embedding in one launch, and the output projection
+followed by the residual and the layer norm), "sca_bf16", "detr" (Deformable-DETR encoder MSDA), "tsa" (two stacked BEV
 maps, frame mean), "tiny".
 
 Prints one JSON line.  value = bilinear samples per second (one sample = one
@@ -107,16 +109,27 @@ def sca_workload(kind):
     import workloads as W
     import scale_deformable_attention_forward_amd as m
 
-    layer = kind == "layer_bf16"
-    bf16 = kind in ("sca_bf16", "layer_bf16")
-    if layer:
+    full = kind == "layer_full"
+    layer = kind in ("layer_bf16", "layer_full")
+    bf16 = kind in ("sca_bf16", "layer_bf16", "layer_full")
+    if full:
+        w = W.bevformer_layer_bf16()
+    elif layer:
         w = W.bevformer_sca_bf16()
     else:
         w = W.bevformer_sca(value_bf16=bf16)
     B, Ncam, Nq, Nv, nH, L, P, D = w["B"], w["Ncam"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"], w["D"]
     C = nH * 32
-    d = {k: _dev(w[k]) for k in ("spatial_shapes", "level_start_index", "reference_points_cam", "bev_mask",
-                                 "sampling_offsets", "attention_logits")}
+    d = {k: _dev(w[k]) for k in ("spatial_shapes", "level_start_index", "reference_points_cam", "bev_mask")}
+    if full:
+        for k in ("query", "query_pos", "W_off", "b_off", "W_att", "b_att", "gamma", "beta"):
+            d[k] = _dev(w[k])
+        d["query"], d["query_pos"] = d["query"].view(-1, C), d["query_pos"].view(-1, C)
+        d["sampling_offsets"] = torch.empty((B, Nq, nH, L, P, 2), dtype=torch.float32, device="cuda")
+        d["attention_logits"] = torch.empty((B, Nq, nH, L * P), dtype=torch.float32, device="cuda")
+    else:
+        d["sampling_offsets"] = _dev(w["sampling_offsets"])
+        d["attention_logits"] = _dev(w["attention_logits"])
     if layer:
         d["feat"] = _dev(w["feat"].reshape(-1, C))
         d["W_v"], d["b_v"], d["W_o"], d["b_o"] = (_dev(w[k]) for k in ("W_v", "b_v", "W_o", "b_o"))
@@ -131,6 +144,10 @@ def sca_workload(kind):
     hit = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
 
     wl = Workload(kind)
+    if full:
+        wl.parts.append(("query_proj", lambda: m.msda_query_proj_bf16(
+            d["query"], d["W_off"], d["b_off"], d["W_att"], d["b_att"], query_pos=d["query_pos"],
+            offsets=d["sampling_offsets"].view(B * Nq, -1), logits=d["attention_logits"].view(B * Nq, -1))))
     if layer:
         wl.parts.append(("value_proj", lambda: m.msda_gemm_bf16(d["feat"], d["W_v"], d["b_v"],
                                                                 out=d["value"].view(-1, C))))
@@ -139,7 +156,11 @@ def sca_workload(kind):
     wl.parts.append(("gather", lambda: m.sca_gather(d["value"], d["spatial_shapes"], d["level_start_index"],
                                                     d["reference_points_cam"], d["sampling_offsets"],
                                                     d["attention_logits"], ws, slots=slots)))
-    if layer:
+    if full:
+        wl.parts.append(("output_proj", lambda: m.msda_output_proj_bf16(
+            slots.view(-1, C), d["W_o"], d["b_o"], residual=d["query"], gamma=d["gamma"], beta=d["beta"],
+            out=d["out"])))
+    elif layer:
         wl.parts.append(("output_proj", lambda: m.msda_gemm_bf16(slots.view(-1, C), d["W_o"], d["b_o"],
                                                                  out=d["out"])))
     wl.main = "gather"
@@ -158,9 +179,16 @@ def sca_workload(kind):
             Mv, Mo = B * Ncam * Nv, B * Nq
             wl.extra["value_proj"] = {"flop": 2 * Mv * C * C, "bytes": Mv * C * 2 * 2 + C * C * 2}
             wl.extra["output_proj"] = {"flop": 2 * Mo * C * C, "bytes": Mo * C * 4 * 2 + C * C * 2}
+        if full:
+            Mq, Nqp = B * Nq, nH * L * P * 3
+            # query and position embedding in, offsets and logits out; the
+            # output side adds the residual read
+            wl.extra["query_proj"] = {"flop": 2 * Mq * Nqp * C, "bytes": Mq * C * 4 * 2 + Mq * Nqp * 4 + Nqp * C * 2}
+            wl.extra["output_proj"]["bytes"] += Mo * C * 4
     wl.finish = finish
     wl.config = {"workload": "BEVFormer-base spatial cross-attention layer, 6 cameras"
-                 + (", with bf16 value and output projections" if layer else ""),
+                 + (", whole layer: bf16 query, value and output projections, residual and layer norm" if full
+                    else ", with bf16 value and output projections" if layer else ""),
                  "batch": B, "cameras": Ncam, "bev_queries": "200x200", "levels": "116x200/58x100/29x50/15x25",
                  "heads": nH, "head_dim": 32, "points_per_level": P, "pillar_anchors": D,
                  "value_dtype": "bf16" if bf16 else "fp32", "mask": "azimuth sectors, 1-2 cameras per query"}
@@ -171,19 +199,34 @@ def sca_workload(kind):
         import oracle
         if layer:
             # bounded sample: the value projection of every row (float64
-            # matmul), then SCA and output projection of 4000 sampled queries
+            # matmul), then (query projections,) SCA and output projection of
+            # 4000 sampled queries
+            import numpy as np
             rows = W.sample_rows(7, B * Nq, 4000)
             t0 = time.perf_counter()
+            if full:
+                q, e = w["query"].reshape(-1, C), w["query_pos"].reshape(-1, C)
+                o_off, o_lg = oracle.query_proj(q[rows], e[rows], w["W_off"], w["b_off"], w["W_att"], w["b_att"])
+                off = np.zeros((B * Nq, o_off.shape[1]), np.float32)
+                lg = np.zeros((B * Nq, o_lg.shape[1]), np.float32)
+                off[rows], lg[rows] = o_off, o_lg
+                off, lg = off.reshape(B, Nq, nH, L, P, 2), lg.reshape(B, Nq, nH, L * P)
+            else:
+                off, lg = w["sampling_offsets"], w["attention_logits"]
             v = oracle.round_to_bf16(oracle.linear_bf16_blas(w["feat"].reshape(-1, C), w["W_v"], w["b_v"]))
             r = oracle.sca(v.reshape(B, Ncam, Nv, nH, 32), w["spatial_shapes"], w["level_start_index"],
-                           w["reference_points_cam"], w["bev_mask"], w["sampling_offsets"], w["attention_logits"],
-                           rows=rows)
-            oracle.linear_bf16(oracle.round_to_bf16(r["slots"]), w["W_o"], w["b_o"])
+                           w["reference_points_cam"], w["bev_mask"], off, lg, rows=rows)
+            if full:
+                oracle.output_proj(r["slots"].astype(np.float32), w["W_o"], w["b_o"], q[rows], w["gamma"],
+                                   w["beta"])
+            else:
+                oracle.linear_bf16(oracle.round_to_bf16(r["slots"]), w["W_o"], w["b_o"])
             t = time.perf_counter() - t0
             n = int(r["hit_count"].reshape(-1)[rows].sum()) * nH * L * P
             return {"value": n / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
-                    "sample": f"value projection of all rows, then SCA and output projection of 4000 sampled "
-                              f"queries ({n} samples); C loops and a float64 matmul, {t:.1f} s"}
+                    "sample": f"value projection of all rows, then {'query projections, ' if full else ''}SCA and "
+                              f"output projection of 4000 sampled queries ({n} samples); C loops and a float64 "
+                              f"matmul, {t:.1f} s"}
         t0 = time.perf_counter()
         oracle.sca(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
                    w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
@@ -251,7 +294,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="sca", choices=["sca", "layer_bf16", "sca_bf16", "detr", "tsa", "tiny"])
+    ap.add_argument("--workload", default="sca", choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "detr", "tsa", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -268,7 +311,7 @@ def main():
     import scale_deformable_attention_forward_amd as m
     m.load_library()
 
-    wl = sca_workload(args.workload) if args.workload in ("sca", "layer_bf16", "sca_bf16") else \
+    wl = sca_workload(args.workload) if args.workload in ("sca", "layer_bf16", "layer_full", "sca_bf16") else \
         msda_workload(args.workload)
 
     for _ in range(args.warmup):

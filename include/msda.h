@@ -202,6 +202,53 @@ int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes
 int msda_gemm_bf16(const void* X, int x_dtype, const uint16_t* W, const float* bias, void* Y,
                    int y_dtype, int64_t M, int64_t N, int64_t K, void* stream);
 
+/*
+ * Sampling offsets and attention logits from the query, in one launch on
+ * matrix cores ([8-heads] 4.1, 4.2 and 18.3):
+ *   q~              = query + query_pos            (float32 addition)
+ *   offsets[M][N_off] = bf16(q~) W_off^T + b_off
+ *   logits [M][N_att] = bf16(q~) W_att^T + b_att
+ * bf16(.) rounds to the nearest bf16, ties to even; products accumulate in
+ * float32.  For BEVFormer-base N_off = 8 heads x 4 levels x 8 points x 2 =
+ * 512 and N_att = 256, laid out as sca_forward's sampling_offsets
+ * [..][nH][L][P][2] and attention_logits [..][nH][L*P].
+ *
+ *   query      device float [M][K], 16-byte aligned
+ *   query_pos  device float [M][K], 16-byte aligned, or NULL (no embedding)
+ *   W_off      device bf16 [N_off][K]; W_att device bf16 [N_att][K]; 16-byte aligned
+ *   b_off, b_att  device float [N_off] / [N_att], or NULL for zero
+ *   offsets, logits  device float [M][N_off] / [M][N_att], 16-byte aligned
+ * Limits: K % 32 == 0 and 32 <= K <= 256; N_off % 32 == 0; N_att % 16 == 0;
+ * N_off + N_att <= 65536; M < 2^31.  The outputs must not overlap the inputs.
+ */
+int msda_query_proj_bf16(const float* query, const float* query_pos, const uint16_t* W_off, const float* b_off,
+                         const uint16_t* W_att, const float* b_att, float* offsets, float* logits, int64_t M,
+                         int64_t K, int64_t N_off, int64_t N_att, void* stream);
+
+/*
+ * Output projection with the residual and the encoder layer's norm
+ * ([8-heads] 11, 18.6 and 18.7; dropout is the identity at inference):
+ *   Y = residual + (bf16(X) W^T + bias)
+ *   with gamma: each row of Y becomes (Y - mean) / sqrt(var + eps) * gamma + beta,
+ *               mean and var (divisor N) taken over the row's N columns.
+ *
+ *   X         device [M][K]; MSDA_F32 (rounded to the nearest bf16, ties to
+ *             even) or MSDA_BF16; 16-byte aligned
+ *   W         device bf16 [N][K], 16-byte aligned
+ *   bias      device float [N], or NULL for zero
+ *   residual  device float [M][N], 16-byte aligned, or NULL (no residual);
+ *             may be the same buffer as Y (each element is read before the
+ *             same thread writes it)
+ *   gamma, beta  device float [N], or NULL: no norm (beta needs gamma; NULL
+ *             beta with gamma is a zero shift)
+ *   eps       finite, >= 0 (the usual choice is 1e-5)
+ *   Y         device float [M][N], 16-byte aligned
+ * Limits: as msda_gemm_bf16; the norm needs N == 256.
+ */
+int msda_output_proj_bf16(const void* X, int x_dtype, const uint16_t* W, const float* bias, const float* residual,
+                          const float* gamma, const float* beta, float eps, float* Y, int64_t M, int64_t N,
+                          int64_t K, void* stream);
+
 /* Name of a status code (host; static string). */
 const char* msda_status_string(int status);
 

@@ -63,6 +63,8 @@ def load_library():
     lib.sca_gather.argtypes = [_p, _int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _int,
                                _p, _p, _sz, _p]
     lib.msda_gemm_bf16.argtypes = [_p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p]
+    lib.msda_query_proj_bf16.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]
+    lib.msda_output_proj_bf16.argtypes = [_p, _int, _p, _p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p]
     for f in (lib.msda_forward, lib.msda_forward_frames, lib.sca_workspace_size, lib.sca_forward,
               lib.sca_compact, lib.sca_gather, lib.msda_gemm_bf16):
         f.restype = _int
@@ -255,4 +257,48 @@ def msda_gemm_bf16(X, W, bias=None, y_dtype=torch.bfloat16, out=None, stream=Non
                             _ptr(bias, "bias", _F32), _ptr(out, "out", (torch.float32, torch.bfloat16)), y_dt,
                             M, N, K, _stream(stream, X.device))
     _check("msda_gemm_bf16", rc)
+    return out
+
+
+def msda_query_proj_bf16(query, W_off, b_off, W_att, b_att, query_pos=None, offsets=None, logits=None,
+                         stream=None):
+    """Sampling offsets and attention logits from the query in one launch:
+    q~ = query + query_pos (float32), offsets = bf16(q~) W_off^T + b_off,
+    logits = bf16(q~) W_att^T + b_att.  query, query_pos float32 [M,K];
+    W_* bfloat16 [N_*,K]; b_* float32 [N_*] or None.  Returns (offsets
+    [M,N_off], logits [M,N_att]) float32."""
+    lib = load_library()
+    M, K = query.shape
+    N_off, N_att = W_off.shape[0], W_att.shape[0]
+    if offsets is None:
+        offsets = torch.empty((M, N_off), dtype=torch.float32, device=query.device)
+    if logits is None:
+        logits = torch.empty((M, N_att), dtype=torch.float32, device=query.device)
+    rc = lib.msda_query_proj_bf16(_ptr(query, "query", _F32), _ptr(query_pos, "query_pos", _F32),
+                                  _ptr(W_off, "W_off", (torch.bfloat16,)), _ptr(b_off, "b_off", _F32),
+                                  _ptr(W_att, "W_att", (torch.bfloat16,)), _ptr(b_att, "b_att", _F32),
+                                  _ptr(offsets, "offsets", _F32), _ptr(logits, "logits", _F32), M, K, N_off, N_att,
+                                  _stream(stream, query.device))
+    _check("msda_query_proj_bf16", rc)
+    return offsets, logits
+
+
+def msda_output_proj_bf16(X, W, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, out=None, stream=None):
+    """residual + (bf16(X) W^T + bias), then, with gamma, the layer norm of
+    each row (divisor N, eps inside the square root) scaled by gamma and
+    shifted by beta.  X float32 or bfloat16 [M,K]; W bfloat16 [N,K];
+    residual float32 [M,N] (may be `out`); bias, gamma, beta float32 [N].
+    Returns float32 [M,N]."""
+    lib = load_library()
+    M, K = X.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    x_dt = MSDA_F32 if X.dtype == torch.float32 else MSDA_BF16
+    rc = lib.msda_output_proj_bf16(_ptr(X, "X", (torch.float32, torch.bfloat16)), x_dt,
+                                   _ptr(W, "W", (torch.bfloat16,)), _ptr(bias, "bias", _F32),
+                                   _ptr(residual, "residual", _F32), _ptr(gamma, "gamma", _F32),
+                                   _ptr(beta, "beta", _F32), float(eps), _ptr(out, "out", _F32), M, N, K,
+                                   _stream(stream, X.device))
+    _check("msda_output_proj_bf16", rc)
     return out

@@ -1,9 +1,11 @@
 // C ABI of libmsda.so (declared in include/msda.h): argument checks on the
 // host, then stream-ordered launches.  Nothing here allocates device memory
 // or synchronises the host.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 
+#include "gemm.hpp"
 #include "internal.hpp"
 #include "msda.h"
 
@@ -49,6 +51,26 @@ int check_common(const void* value, int value_dtype, const int64_t* shapes, cons
     return fail(MSDA_ERR_INVALID_ARG, "value and output must be 16-byte aligned");
   *image_bytes = (uint32_t)bytes;
   return MSDA_OK;
+}
+
+int check_gemm_sizes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 1 || K < 1) return fail(MSDA_ERR_INVALID_ARG, "M >= 0, N >= 1 and K >= 1 required");
+  if (K % 32 != 0 || K > 256 || N % 16 != 0 || N > 65536 || M >= kI31)
+    return fail(MSDA_ERR_UNSUPPORTED, "needs K %% 32 == 0, K <= 256, N %% 16 == 0, N <= 65536, M < 2^31 "
+                "(got M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
+  return MSDA_OK;
+}
+
+// one output of N columns; callers fill in W, bias, Y and the epilogue
+msda::GemmArgs gemm_args(const void* X, bool x_f32, int64_t M, int64_t N, int64_t K) {
+  msda::GemmArgs g = {};
+  g.X = X;
+  g.x_f32 = x_f32;
+  g.M = M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.N1 = (int)N;
+  return g;
 }
 
 }  // namespace
@@ -275,25 +297,75 @@ int msda_gemm_bf16(const void* X, int x_dtype, const uint16_t* W, const float* b
   if (!X || !W || !Y) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
   if ((x_dtype != MSDA_F32 && x_dtype != MSDA_BF16) || (y_dtype != MSDA_F32 && y_dtype != MSDA_BF16))
     return fail(MSDA_ERR_INVALID_ARG, "x_dtype and y_dtype must be MSDA_F32 or MSDA_BF16");
-  if (M < 0 || N < 1 || K < 1) return fail(MSDA_ERR_INVALID_ARG, "M >= 0, N >= 1 and K >= 1 required");
-  if (K % 32 != 0 || K > 256 || N % 16 != 0 || N > 65536 || M >= kI31)
-    return fail(MSDA_ERR_UNSUPPORTED, "needs K %% 32 == 0, K <= 256, N %% 16 == 0, N <= 65536, M < 2^31 "
-                "(got M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
+  int rc = check_gemm_sizes(M, N, K);
+  if (rc != MSDA_OK) return rc;
   if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 16) || (bias && !aligned(bias, 4)))
     return fail(MSDA_ERR_INVALID_ARG, "X, W and Y must be 16-byte aligned");
   g_last_error[0] = '\0';
   if (M == 0) return MSDA_OK;
-  msda::GemmArgs g = {};
-  g.X = X;
-  g.x_f32 = x_dtype == MSDA_F32;
-  g.W = W;
-  g.bias = bias;
-  g.Y = Y;
+  msda::GemmArgs g = gemm_args(X, x_dtype == MSDA_F32, M, N, K);
+  g.W1 = W;
+  g.bias1 = bias;
+  g.Y1 = Y;
   g.y_f32 = y_dtype == MSDA_F32;
-  g.M = M;
-  g.N = (int)N;
-  g.K = (int)K;
   return hip_status(msda::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)), "gemm launch");
+}
+
+int msda_query_proj_bf16(const float* query, const float* query_pos, const uint16_t* W_off, const float* b_off,
+                         const uint16_t* W_att, const float* b_att, float* offsets, float* logits, int64_t M,
+                         int64_t K, int64_t N_off, int64_t N_att, void* stream) {
+  if (!query || !W_off || !W_att || !offsets || !logits) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (N_off < 1 || N_att < 1) return fail(MSDA_ERR_INVALID_ARG, "N_off >= 1 and N_att >= 1 required");
+  if (N_off % 32 != 0)
+    return fail(MSDA_ERR_UNSUPPORTED, "N_off %% 32 == 0 required (got %lld)", (long long)N_off);
+  int rc = check_gemm_sizes(M, N_off + N_att, K);
+  if (rc != MSDA_OK) return rc;
+  if (!aligned(query, 16) || (query_pos && !aligned(query_pos, 16)) || !aligned(W_off, 16) ||
+      !aligned(W_att, 16) || !aligned(offsets, 16) || !aligned(logits, 16) || (b_off && !aligned(b_off, 4)) ||
+      (b_att && !aligned(b_att, 4)))
+    return fail(MSDA_ERR_INVALID_ARG, "query, query_pos, weights and outputs must be 16-byte aligned");
+  g_last_error[0] = '\0';
+  if (M == 0) return MSDA_OK;
+  msda::GemmArgs g = gemm_args(query, true, M, N_off + N_att, K);
+  g.X_add = query_pos;
+  g.N1 = (int)N_off;
+  g.W1 = W_off;
+  g.bias1 = b_off;
+  g.Y1 = offsets;
+  g.W2 = W_att;
+  g.bias2 = b_att;
+  g.Y2 = logits;
+  g.y_f32 = 1;
+  return hip_status(msda::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)), "query projection launch");
+}
+
+int msda_output_proj_bf16(const void* X, int x_dtype, const uint16_t* W, const float* bias, const float* residual,
+                          const float* gamma, const float* beta, float eps, float* Y, int64_t M, int64_t N,
+                          int64_t K, void* stream) {
+  if (!X || !W || !Y) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (x_dtype != MSDA_F32 && x_dtype != MSDA_BF16)
+    return fail(MSDA_ERR_INVALID_ARG, "x_dtype must be MSDA_F32 or MSDA_BF16");
+  if (beta && !gamma) return fail(MSDA_ERR_INVALID_ARG, "beta given without gamma");
+  int rc = check_gemm_sizes(M, N, K);
+  if (rc != MSDA_OK) return rc;
+  if (gamma && N != msda::kGemmNormCols)
+    return fail(MSDA_ERR_UNSUPPORTED, "the layer norm needs N == %d (got %lld)", msda::kGemmNormCols, (long long)N);
+  if (gamma && !(eps >= 0.0f && eps < INFINITY)) return fail(MSDA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 16) || (residual && !aligned(residual, 16)) ||
+      (bias && !aligned(bias, 4)) || (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)))
+    return fail(MSDA_ERR_INVALID_ARG, "X, W, Y and residual must be 16-byte aligned");
+  g_last_error[0] = '\0';
+  if (M == 0) return MSDA_OK;
+  msda::GemmArgs g = gemm_args(X, x_dtype == MSDA_F32, M, N, K);
+  g.W1 = W;
+  g.bias1 = bias;
+  g.Y1 = Y;
+  g.y_f32 = 1;
+  g.residual = residual;
+  g.gamma = gamma;
+  g.beta = beta;
+  g.eps = eps;
+  return hip_status(msda::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)), "output projection launch");
 }
 
 }  // extern "C"

@@ -74,17 +74,4 @@ struct CompactArgs {
 };
 hipError_t launch_sca_compact(const CompactArgs& a, int tiles, hipStream_t stream);
 
-// bf16 GEMM on MFMA: Y = X W^T + bias
-struct GemmArgs {
-  const void* X;
-  int x_f32;
-  const uint16_t* W;
-  const float* bias;
-  void* Y;
-  int y_f32;
-  int64_t M;
-  int N, K;
-};
-hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream);
-
 }  // namespace msda

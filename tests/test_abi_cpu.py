@@ -39,7 +39,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["msda_forward", "msda_forward_frames", "sca_workspace_size", "sca_forward", "msda_gemm_bf16",
-              "msda_status_string", "msda_last_error"]:
+              "msda_query_proj_bf16", "msda_output_proj_bf16", "msda_status_string", "msda_last_error"]:
         assert n in names, n
 
 
@@ -169,6 +169,46 @@ def test_gemm_rejects_null_and_dtype(lib):
     assert lib.msda_gemm_bf16(None, 1, A, None, B_, 1, 4, 256, 256, None) == INVALID
     assert lib.msda_gemm_bf16(A, 5, A, None, B_, 1, 4, 256, 256, None) == INVALID
     assert lib.msda_gemm_bf16(MIS, 1, A, None, B_, 1, 4, 256, 256, None) == INVALID
+
+
+def _qp(lib, q=A, pos=None, Wo=A, bo=None, Wa=A, ba=None, off=B_, lg=B_, M=4, K=256, No=512, Na=256):
+    return lib.msda_query_proj_bf16(q, pos, Wo, bo, Wa, ba, off, lg, M, K, No, Na, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID),
+    (dict(Wa=None), INVALID),
+    (dict(lg=None), INVALID),
+    (dict(pos=MIS), INVALID),
+    (dict(No=0), INVALID),
+    (dict(No=48), UNSUPPORTED),   # offsets must fill whole 32-column wave slices
+    (dict(Na=24), UNSUPPORTED),
+    (dict(K=48), UNSUPPORTED),
+    (dict(M=-2), INVALID),
+    (dict(M=0), OK),
+])
+def test_query_proj_rejects(lib, kw, code):
+    assert _qp(lib, **kw) == code
+
+
+def _op(lib, X=A, dt=0, W=A, bias=None, res=None, gamma=None, beta=None, eps=1e-5, Y=B_, M=4, N=256, K=256):
+    return lib.msda_output_proj_bf16(X, dt, W, bias, res, gamma, beta, ctypes.c_float(eps), Y, M, N, K, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), INVALID),
+    (dict(Y=None), INVALID),
+    (dict(dt=4), INVALID),
+    (dict(beta=A), INVALID),              # beta without gamma
+    (dict(gamma=A, N=512), UNSUPPORTED),  # the norm needs one 256-column row per block
+    (dict(gamma=A, eps=-1.0), INVALID),
+    (dict(gamma=A, eps=float("nan")), INVALID),
+    (dict(res=MIS), INVALID),
+    (dict(N=24), UNSUPPORTED),
+    (dict(M=0, gamma=A, beta=A, res=A), OK),
+])
+def test_output_proj_rejects(lib, kw, code):
+    assert _op(lib, **kw) == code
 
 
 def test_binding_refuses_cpu_tensors():
