@@ -191,3 +191,23 @@ def test_whole_layer_bf16():
     ref_out = oracle.output_proj(ref["slots"].astype(np.float32), w["W_o"], w["b_o"], q[rows], w["gamma"],
                                  w["beta"], 1e-5)
     assert_abs_close(got[rows], ref_out, 1e-2, "whole layer output (sampled queries)")
+
+
+def test_float32_to_bf16_rounding_on_ties():
+    """float32 X is rounded to bf16 on the way into the matrix cores: an
+    identity W returns the rounded input (bf16 output, exact).  Ties and near
+    ties around several binades must round to nearest, ties to even, as
+    torch's float32 -> bfloat16 conversion does."""
+    K = 64
+    base = np.array([1.0, 1.5, -2.0, 3.0e-3, 7.0e5, -1.25e-20], np.float64)
+    steps = np.array([0.5, 1.5, 2.5, 0.5 + 2.0 ** -10, 0.5 - 2.0 ** -10, 0.0, 1.0, 3.5])
+    vals = []
+    for b in base:
+        ulp = 2.0 ** (np.floor(np.log2(abs(b))) - 7)  # bf16 spacing at b
+        vals += [b + s * ulp * np.sign(b) for s in steps]
+    X = np.resize(np.array(vals, np.float32), (8, K))
+    eye = np.zeros((K, K), np.uint16)
+    eye[np.arange(K), np.arange(K)] = 0x3F80
+    y = msda.msda_gemm_bf16(dev(X), dev(eye), None, y_dtype=torch.bfloat16)
+    ref = torch.from_numpy(X).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(host(y), ref)
