@@ -22,8 +22,13 @@ channels) over the whole step; roofline = the gather kernel's effective
 bytes (all 4 nominal corners of every sample, plus offsets, logits, anchors,
 work list and output) per launch over its average launch time, measured with
 HIP events recorded on the stream the kernel runs on; breakdown = the same
-events around every part of the step; cpu_baseline = the CPU oracle on the
-same workload.
+events around every part of the step (mean, p10/p50/p90); cold = the same
+step after a 1 GiB write that evicts L2 and the memory-side cache (the
+headline is warm, back to back, as a layer runs inside a network);
+batch_items_per_s = batch items (scenes) per second; roofline also carries
+the bytes of the corners that fall inside their map, which are the only ones
+the kernel actually reads; cpu_baseline = the CPU oracle on the same
+workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --calibrate-copy   (a plain device copy of known size, for
@@ -93,6 +98,24 @@ class Workload:
         self.parts = []
         self.main = None
         self.extra = {}
+        self.batch = 1
+        self.inbounds_corners = None  # corners inside their map, per gather launch
+
+
+def count_inbounds(shapes, x, y):
+    """Corners of bilinear samples that fall inside their level's map.  x, y:
+    continuous pixel coordinates (W*s_x - 1/2, H*s_y - 1/2) of shape
+    [..., L, P]; shapes [L, 2] as (H, W).  Measurement metadata only."""
+    import numpy as np
+    H = shapes[:, 0].astype(np.float64)[:, None]
+    Wd = shapes[:, 1].astype(np.float64)[:, None]
+    x0, y0 = np.floor(x), np.floor(y)
+    n = 0
+    for dx in (0, 1):
+        inx = (x0 + dx >= 0) & (x0 + dx < Wd)
+        for dy in (0, 1):
+            n += int(np.count_nonzero(inx & (y0 + dy >= 0) & (y0 + dy < H)))
+    return n
 
 
 def _dev(a):
@@ -166,7 +189,25 @@ def sca_workload(kind):
     wl.main = "gather"
 
     def finish():
+        import numpy as np
         n_pairs = int(offs[-1].item())
+        # corners inside their map: per visible pair, from the offsets the
+        # gather reads (read back after the warm-up for the whole layer)
+        off_h = d["sampling_offsets"].cpu().numpy() if full else w["sampling_offsets"]
+        ss = w["spatial_shapes"]
+        WH = np.stack([ss[:, 1], ss[:, 0]], -1).astype(np.float32)  # (W, H) per level
+        anchor = np.arange(P) % D
+        n_in = 0
+        for b in range(B):
+            for c in range(Ncam):
+                qs = np.nonzero(w["bev_mask"][c, b].any(-1))[0]
+                rho = w["reference_points_cam"][c, b, qs][:, anchor]  # [q, P, 2]
+                for l in range(L):
+                    loc = rho[:, None, :, :] + off_h[b, qs][:, :, l] / WH[l]  # [q, nH, P, 2]
+                    x = loc[..., 0].astype(np.float64) * WH[l, 0] - 0.5
+                    y = loc[..., 1].astype(np.float64) * WH[l, 1] - 0.5
+                    n_in += count_inbounds(ss[l:l + 1], x[..., None, :], y[..., None, :])
+        wl.inbounds_corners = n_in
         elem = 2 if bf16 else 4
         wl.samples = n_pairs * nH * L * P
         # effective bytes of one gather launch: 4 nominal corners x 32 channels
@@ -186,6 +227,7 @@ def sca_workload(kind):
             wl.extra["query_proj"] = {"flop": 2 * Mq * Nqp * C, "bytes": Mq * C * 4 * 2 + Mq * Nqp * 4 + Nqp * C * 2}
             wl.extra["output_proj"]["bytes"] += Mo * C * 4
     wl.finish = finish
+    wl.batch = B
     wl.config = {"workload": "BEVFormer-base spatial cross-attention layer, 6 cameras"
                  + (", whole layer: bf16 query, value and output projections, residual and layer norm" if full
                     else ", with bf16 value and output projections" if layer else ""),
@@ -239,6 +281,7 @@ def sca_workload(kind):
 
 
 def msda_workload(which):
+    import numpy as np
     import torch
     import workloads as W
     import scale_deformable_attention_forward_amd as m
@@ -262,9 +305,15 @@ def msda_workload(which):
 
     def finish():
         wl.samples = B * F * Nq * nH * L * P
+        ss = w["spatial_shapes"]
+        loc = w["sampling_locations"]
+        Wd = ss[:, 1].astype(np.float64)[:, None]
+        H = ss[:, 0].astype(np.float64)[:, None]
+        wl.inbounds_corners = count_inbounds(ss, loc[..., 0] * Wd - 0.5, loc[..., 1] * H - 0.5)
         wl.gathered_bytes = wl.samples * 4 * 32 * 4
         wl.eff_bytes = wl.gathered_bytes + wl.samples * (8 + 4) + B * Nq * nH * 32 * 4
     wl.finish = finish
+    wl.batch = B
     names = {"detr": "Deformable-DETR encoder MSDA, 4 levels 100x150/50x75/25x38/13x19, Nq=Nv=19947",
              "tiny": "tiny MSDA, 256 queries, one 32x32 level",
              "tsa": "temporal self-attention, 2 stacked 200x200 BEV maps, mean over frames"}
@@ -296,6 +345,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sca", choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "detr", "tsa", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=5,
+                    help="steps timed after a 1 GiB write that evicts the caches (0: none)")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
 
@@ -335,13 +386,39 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    part_ms = {name: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)) / K
-               for i, (name, _) in enumerate(wl.parts)}
+    import numpy as np
+    per_step = {name: np.array([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)])
+                for i, (name, _) in enumerate(wl.parts)}
+    step_ms = np.array([ev[k][0].elapsed_time(ev[k][n]) for k in range(K)])
+    part_ms = {name: float(v.mean()) for name, v in per_step.items()}
     kernel_ms = part_ms[wl.main]
+
+    def pct(v):
+        return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
+                "p90": float(np.percentile(v, 90))}
+
+    # cold: a 1 GiB write before each step evicts the inputs from L2 and
+    # the memory-side cache, so the step starts from HBM
+    cold = None
+    if args.cold_reps > 0:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.cold_reps)]
+        for r in range(args.cold_reps):
+            scratch.fill_(float(r))
+            cev[r][0].record()
+            for i, (_, fn) in enumerate(wl.parts):
+                fn()
+                cev[r][i + 1].record()
+        torch.cuda.synchronize()
+        del scratch
+        cold = {"reps": args.cold_reps,
+                "step_ms": pct(np.array([cev[r][0].elapsed_time(cev[r][n]) for r in range(args.cold_reps)]))}
+        for i, (name, _) in enumerate(wl.parts):
+            cold[name + "_ms"] = pct(np.array([cev[r][i].elapsed_time(cev[r][i + 1]) for r in range(args.cold_reps)]))
 
     breakdown = {}
     for name, ms in part_ms.items():
-        e = {"ms": ms}
+        e = {"ms": ms, **pct(per_step[name])}
         if name in wl.extra:
             e["TFLOP/s"] = wl.extra[name]["flop"] / (ms * 1e-3) / 1e12
             e["GB/s"] = wl.extra[name]["bytes"] / (ms * 1e-3) / 1e9
@@ -369,8 +446,14 @@ def main():
                      "effective_bytes_per_launch": wl.eff_bytes, "gathered_bytes_per_launch": wl.gathered_bytes},
         "effective_GBps_per_step": wl.eff_bytes / (ms_per_step * 1e-3) / 1e9,
         "samples_per_step": wl.samples,
+        "batch_items_per_s": wl.batch / (ms_per_step * 1e-3),
+        "step_ms_events": pct(step_ms),
         "breakdown": breakdown,
+        "cold": cold,
     }
+    if wl.inbounds_corners is not None:
+        elem = 2 if "bf16" in wl.dtype else 4
+        line["roofline"]["gathered_bytes_in_bounds_per_launch"] = wl.inbounds_corners * 32 * elem
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = wl.cpu_baseline()
     print(json.dumps(line), flush=True)

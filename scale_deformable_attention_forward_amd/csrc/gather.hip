@@ -407,41 +407,54 @@ static int block_waves(int LP) {
   return w;
 }
 
-// Blocks for n_items (an upper bound when the count lives on the device):
-// at most blocks_per_cu per compute unit, a multiple of the die count.
-static unsigned grid_for(int64_t n_items, int waves, int blocks_per_cu) {
+// Blocks for n_items (an upper bound when the count lives on the device),
+// a multiple of the die count.
+//   - SCA (resident_only): no more than the chip holds at once, so that every
+//     block is resident from the start and all waves sweep the locality-
+//     ordered work together.  A grid larger than that runs in rounds: a block
+//     of the first round goes on to later batch items while the next round
+//     starts on the first, and several items' value maps compete for L2.
+//   - MSDA: up to 8 blocks of 4 waves per compute unit, more than are
+//     resident: with few queries per wave, blocks that start late balance
+//     the tail.
+template <typename Kernel>
+static unsigned grid_for(Kernel kernel, int64_t n_items, int waves, size_t smem, bool resident_only) {
+  int per_cu = 8 * kMaxWavesPerBlock / waves;
+  if (resident_only &&
+      (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, waves * kWave, smem) != hipSuccess || per_cu < 1))
+    per_cu = 1;
   int64_t need = (n_items + waves - 1) / waves;
-  const int64_t cap = (int64_t)device_cus() * blocks_per_cu;
+  const int64_t cap = (int64_t)device_cus() * per_cu;
   if (need > cap) need = cap;
   if (need < 1) need = 1;
   return (unsigned)((need + kXcds - 1) / kXcds * kXcds);
 }
 
+template <typename Kernel>
+static void launch(Kernel kernel, int64_t n_items, int waves, size_t smem, bool resident_only, const GatherArgs& a,
+                   hipStream_t stream) {
+  kernel<<<grid_for(kernel, n_items, waves, smem, resident_only), waves * kWave, smem, stream>>>(a);
+}
+
 hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream) {
   const int waves = block_waves(a.LP);
-  const unsigned grid = grid_for(a.B * a.Nq, waves, 8 * kMaxWavesPerBlock / waves);
   const size_t smem = smem_bytes(a.LP, waves);
-  if (a.LP <= 32) {
-    if (a.bf16) msda_gather_kernel<true, 4><<<grid, waves * kWave, smem, stream>>>(a);
-    else msda_gather_kernel<false, 4><<<grid, waves * kWave, smem, stream>>>(a);
-  } else {
-    if (a.bf16) msda_gather_kernel<true, 8><<<grid, waves * kWave, smem, stream>>>(a);
-    else msda_gather_kernel<false, 8><<<grid, waves * kWave, smem, stream>>>(a);
-  }
+  const int64_t n = a.B * a.Nq;
+  if (a.LP <= 32)
+    launch(a.bf16 ? msda_gather_kernel<true, 4> : msda_gather_kernel<false, 4>, n, waves, smem, false, a, stream);
+  else
+    launch(a.bf16 ? msda_gather_kernel<true, 8> : msda_gather_kernel<false, 8>, n, waves, smem, false, a, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_sca_gather(const GatherArgs& a, hipStream_t stream) {
   const int waves = block_waves(a.LP);
-  const unsigned grid = grid_for(a.B * a.Ncam * a.Nq, waves, 8 * kMaxWavesPerBlock / waves);
   const size_t smem = smem_bytes(a.LP, waves);
-  if (a.LP <= 32) {
-    if (a.bf16) sca_gather_kernel<true, 4><<<grid, waves * kWave, smem, stream>>>(a);
-    else sca_gather_kernel<false, 4><<<grid, waves * kWave, smem, stream>>>(a);
-  } else {
-    if (a.bf16) sca_gather_kernel<true, 8><<<grid, waves * kWave, smem, stream>>>(a);
-    else sca_gather_kernel<false, 8><<<grid, waves * kWave, smem, stream>>>(a);
-  }
+  const int64_t n = a.B * a.Nq;
+  if (a.LP <= 32)
+    launch(a.bf16 ? sca_gather_kernel<true, 4> : sca_gather_kernel<false, 4>, n, waves, smem, true, a, stream);
+  else
+    launch(a.bf16 ? sca_gather_kernel<true, 8> : sca_gather_kernel<false, 8>, n, waves, smem, true, a, stream);
   return hipGetLastError();
 }
 
