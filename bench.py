@@ -13,7 +13,10 @@ timing starts.  Other workloads: "layer_bf16" (batch 4, bf16 value
 projection GEMM -> SCA on bf16 value -> bf16 output projection GEMM),
 "layer_full" (the same with the sampling offsets and logits projected from
 query + position embedding in one launch, and the output projection
-followed by the residual and the layer norm), "sca_bf16", "detr" (Deformable-DETR encoder MSDA), "tsa" (two stacked BEV
+followed by the residual and the layer norm), "sca_bf16", "sca_rebatch"
+(workload 3 through the padded rebatch flow of the SCA note, an A/B
+baseline: per-camera segments padded to the longest, the operator over all
+of them, scatter-add and divide), "detr" (Deformable-DETR encoder MSDA), "tsa" (two stacked BEV
 maps, frame mean), "tiny".
 
 Prints one JSON line.  value = bilinear samples per second (one sample = one
@@ -280,6 +283,87 @@ def sca_workload(kind):
     return wl
 
 
+def rebatch_workload():
+    """Workload 3 through the padded rebatch flow (A/B baseline): compaction,
+    the longest segment read back to the host, rebatch, the MSDA operator over
+    B*Ncam padded segments, scatter-add per camera and divide."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import scale_deformable_attention_forward_amd as m
+
+    w = W.bevformer_sca()
+    B, Ncam, Nq, Nv, nH, L, P, D = w["B"], w["Ncam"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"], w["D"]
+    C = nH * 32
+    d = {k: _dev(w[k]) for k in ("value", "spatial_shapes", "level_start_index", "reference_points_cam", "bev_mask",
+                                 "sampling_offsets", "attention_logits")}
+    ws = torch.empty(m.sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device="cuda")
+    hit = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
+    offs = torch.empty(B * Ncam + 1, dtype=torch.int32, device="cuda")
+    pq = torch.empty(B * Ncam * Nq, dtype=torch.int32, device="cuda")
+    S = nH * L * P
+    # padded buffers sized for the largest possible segment; each step uses
+    # the leading [B*Ncam, max_len] part
+    loc_buf = torch.empty(B * Ncam * Nq * S * 2, dtype=torch.float32, device="cuda")
+    lg_buf = torch.empty(B * Ncam * Nq * S, dtype=torch.float32, device="cuda")
+    rows_buf = torch.empty(B * Ncam * Nq * C, dtype=torch.float32, device="cuda")
+    slots = torch.empty((B, Nq, C), dtype=torch.float32, device="cuda")
+    st = {}
+
+    def read_max_len():
+        o = offs.cpu().numpy()
+        st["ml"] = int((o[1:] - o[:-1]).max())
+
+    def views():
+        ml = st["ml"]
+        n = B * Ncam * ml
+        return (loc_buf[:n * S * 2].view(B * Ncam, ml, nH, L, P, 2), lg_buf[:n * S].view(B * Ncam, ml, nH, L * P),
+                rows_buf[:n * C].view(B * Ncam, ml, C))
+
+    wl = Workload("sca_rebatch")
+    wl.parts.append(("compact", lambda: m.sca_compact(d["bev_mask"], d["reference_points_cam"], ws, hit_count=hit,
+                                                      pair_offsets=offs, pair_q=pq)))
+    wl.parts.append(("max_len", read_max_len))
+    wl.parts.append(("rebatch", lambda: m.sca_rebatch(offs, pq, d["reference_points_cam"], d["sampling_offsets"],
+                                                      d["attention_logits"], d["spatial_shapes"], st["ml"],
+                                                      *views()[:2])))
+    wl.parts.append(("msda", lambda: m.msda_forward(d["value"].view(B * Ncam, Nv, nH, 32), d["spatial_shapes"],
+                                                    d["level_start_index"], views()[0], views()[1],
+                                                    out=views()[2])))
+    wl.parts.append(("scatter_mean", lambda: m.sca_scatter_mean(views()[2], offs, pq, hit, Nq, slots=slots)))
+    wl.main = "msda"
+
+    def finish():
+        n_pairs = int(offs[-1].item())
+        wl.samples = n_pairs * S
+        padded = B * Ncam * st["ml"] * S
+        wl.gathered_bytes = padded * 4 * 32 * 4
+        wl.eff_bytes = wl.gathered_bytes + padded * 12 + B * Ncam * st["ml"] * C * 4
+        wl.extra_info = {"max_len": st["ml"], "padded_rows": B * Ncam * st["ml"], "pairs": n_pairs,
+                         "padded_samples": padded}
+    wl.finish = finish
+    wl.batch = B
+    wl.config = {"workload": "BEVFormer-base spatial cross-attention layer, 6 cameras, padded rebatch flow "
+                             "(A/B baseline for the fused path)",
+                 "batch": B, "cameras": Ncam, "bev_queries": "200x200", "levels": "116x200/58x100/29x50/15x25",
+                 "heads": nH, "head_dim": 32, "points_per_level": P, "pillar_anchors": D, "value_dtype": "fp32",
+                 "mask": "azimuth sectors, 1-2 cameras per query"}
+    wl.dtype = "fp32"
+    wl.kernel_key = "msda_gather_kernel_fp32"
+
+    def cpu_baseline():
+        import oracle
+        t0 = time.perf_counter()
+        oracle.sca(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
+                   w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
+        t = time.perf_counter() - t0
+        return {"value": wl.samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole workload (all {B * Nq} queries, {wl.samples} samples), "
+                          f"single-threaded C, {t:.1f} s"}
+    wl.cpu_baseline = cpu_baseline
+    return wl
+
+
 def msda_workload(which):
     import numpy as np
     import torch
@@ -343,7 +427,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="sca", choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "detr", "tsa", "tiny"])
+    ap.add_argument("--workload", default="sca", choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "detr", "tsa",
+                                                          "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="steps timed after a 1 GiB write that evicts the caches (0: none)")
@@ -362,8 +447,12 @@ def main():
     import scale_deformable_attention_forward_amd as m
     m.load_library()
 
-    wl = sca_workload(args.workload) if args.workload in ("sca", "layer_bf16", "layer_full", "sca_bf16") else \
-        msda_workload(args.workload)
+    if args.workload in ("sca", "layer_bf16", "layer_full", "sca_bf16"):
+        wl = sca_workload(args.workload)
+    elif args.workload == "sca_rebatch":
+        wl = rebatch_workload()
+    else:
+        wl = msda_workload(args.workload)
 
     for _ in range(args.warmup):
         for _, fn in wl.parts:
@@ -451,6 +540,8 @@ def main():
         "breakdown": breakdown,
         "cold": cold,
     }
+    if getattr(wl, "extra_info", None):
+        line["config"].update(wl.extra_info)
     if wl.inbounds_corners is not None:
         elem = 2 if "bf16" in wl.dtype else 4
         line["roofline"]["gathered_bytes_in_bounds_per_launch"] = wl.inbounds_corners * 32 * elem

@@ -249,6 +249,43 @@ int msda_output_proj_bf16(const void* X, int x_dtype, const uint16_t* W, const f
                           const float* gamma, const float* beta, float eps, float* Y, int64_t M, int64_t N,
                           int64_t K, void* stream);
 
+/*
+ * Padded "rebatch" form of SCA, an A/B baseline for sca_gather ([SCA-note]
+ * rebatch, scatter, count and divide code; locations as in [8-heads] 5 and
+ * 18.4).  With the pair lists of sca_compact and max_len >= the longest
+ * (batch item, camera) segment (the note takes the maximum on the host):
+ *
+ *   sca_rebatch      for every padded row (segment bc = b*Ncam + c, position
+ *                    i < max_len): sampling_locations[bc][i][h][l][p] =
+ *                    rho[c][b][q][p mod D] + (dx / W_l, dy / H_l) in float32
+ *                    and logits_out[bc][i][h][l*P+p] = attention_logits[b][q][..],
+ *                    q = pair_q[pair_offsets[bc] + i]; rows i >= segment
+ *                    length get zeros.  Then msda_forward over the B*Ncam
+ *                    segments (value [B][Ncam][Nv][nH][Dh] viewed as B*Ncam
+ *                    images, Nq = max_len, weights as logits) gives rows
+ *                    [B*Ncam][max_len][nH*Dh].
+ *   sca_scatter_mean slots = 0; for each camera c in ascending order, slots[b][q]
+ *                    += rows[b*Ncam + c][i] over its segment; then slots[b][q]
+ *                    /= max(1, hit_count[b][q]).
+ *
+ *   pair_offsets, pair_q, hit_count  device int32, as written by sca_compact
+ *   reference_points_cam, sampling_offsets, attention_logits, spatial_shapes
+ *                    as for sca_forward (device)
+ *   sampling_locations device float [B*Ncam][max_len][nH][L][P][2]; logits_out
+ *                    device float [B*Ncam][max_len][nH][L*P]; rows device float
+ *                    [B*Ncam][max_len][C]; slots device float [B][Nq][C]
+ * Alignment: (x, y) arrays 8 bytes; rows and slots 16 bytes.  C % 4 == 0.
+ * A segment longer than max_len is cut at max_len (rows past it are neither
+ * written nor added): pass the true maximum.
+ */
+int sca_rebatch(const int32_t* pair_offsets, const int32_t* pair_q, const float* reference_points_cam,
+                const float* sampling_offsets, const float* attention_logits, const int64_t* spatial_shapes,
+                int64_t B, int64_t Ncam, int64_t Nq, int nH, int L, int P, int D, int64_t max_len,
+                float* sampling_locations, float* logits_out, void* stream);
+int sca_scatter_mean(const float* rows, const int32_t* pair_offsets, const int32_t* pair_q,
+                     const int32_t* hit_count, int64_t B, int64_t Ncam, int64_t Nq, int64_t C, int64_t max_len,
+                     float* slots, void* stream);
+
 /* Name of a status code (host; static string). */
 const char* msda_status_string(int status);
 

@@ -63,6 +63,8 @@ def load_library():
     lib.sca_gather.argtypes = [_p, _int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _int,
                                _p, _p, _sz, _p]
     lib.msda_gemm_bf16.argtypes = [_p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p]
+    lib.sca_rebatch.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _int, _int, _int, _int, _i64, _p, _p, _p]
+    lib.sca_scatter_mean.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p]
     lib.msda_query_proj_bf16.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]
     lib.msda_output_proj_bf16.argtypes = [_p, _int, _p, _p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p]
     for f in (lib.msda_forward, lib.msda_forward_frames, lib.sca_workspace_size, lib.sca_forward,
@@ -302,3 +304,75 @@ def msda_output_proj_bf16(X, W, bias=None, residual=None, gamma=None, beta=None,
                                    _stream(stream, X.device))
     _check("msda_output_proj_bf16", rc)
     return out
+
+
+def sca_rebatch(pair_offsets, pair_q, reference_points_cam, sampling_offsets, attention_logits, spatial_shapes,
+                max_len, sampling_locations=None, logits_out=None, stream=None):
+    """Padded rebatch of the pair lists (A/B baseline): sampling locations
+    rho + offset / (W, H) and logits for every row of the [B*Ncam, max_len]
+    segments (zeros past a segment's end).  Returns (sampling_locations
+    [B*Ncam, max_len, nH, L, P, 2], logits [B*Ncam, max_len, nH, L*P])."""
+    lib = load_library()
+    Ncam, B, Nq, D, _ = reference_points_cam.shape
+    _, _, nH, L, P, _ = sampling_offsets.shape
+    dev = reference_points_cam.device
+    if sampling_locations is None:
+        sampling_locations = torch.empty((B * Ncam, max_len, nH, L, P, 2), dtype=torch.float32, device=dev)
+    if logits_out is None:
+        logits_out = torch.empty((B * Ncam, max_len, nH, L * P), dtype=torch.float32, device=dev)
+    i32 = (torch.int32,)
+    rc = lib.sca_rebatch(_ptr(pair_offsets, "pair_offsets", i32), _ptr(pair_q, "pair_q", i32),
+                         _ptr(reference_points_cam, "reference_points_cam", _F32),
+                         _ptr(sampling_offsets, "sampling_offsets", _F32),
+                         _ptr(attention_logits, "attention_logits", _F32),
+                         _ptr(spatial_shapes, "spatial_shapes", _I64), B, Ncam, Nq, nH, L, P, D, max_len,
+                         _ptr(sampling_locations, "sampling_locations", _F32), _ptr(logits_out, "logits_out", _F32),
+                         _stream(stream, dev))
+    _check("sca_rebatch", rc)
+    return sampling_locations, logits_out
+
+
+def sca_scatter_mean(rows, pair_offsets, pair_q, hit_count, Nq, slots=None, stream=None):
+    """slots[b, q] = mean over the cameras that see q of their segment rows
+    (zero where no camera does).  rows float32 [B*Ncam, max_len, C];
+    hit_count int32 [B, Nq].  Returns slots float32 [B, Nq, C]."""
+    lib = load_library()
+    BN, max_len, C = rows.shape
+    B = hit_count.shape[0]
+    Ncam = BN // max(B, 1)
+    if slots is None:
+        slots = torch.empty((B, Nq, C), dtype=torch.float32, device=rows.device)
+    i32 = (torch.int32,)
+    rc = lib.sca_scatter_mean(_ptr(rows, "rows", _F32), _ptr(pair_offsets, "pair_offsets", i32),
+                              _ptr(pair_q, "pair_q", i32), _ptr(hit_count, "hit_count", i32), B, Ncam, Nq, C, max_len,
+                              _ptr(slots, "slots", _F32), _stream(stream, rows.device))
+    _check("sca_scatter_mean", rc)
+    return slots
+
+
+def sca_forward_rebatch(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
+                        attention_logits, workspace=None, stream=None):
+    """SCA through the padded rebatch flow (A/B baseline for sca_forward):
+    sca_compact, the longest segment read back to the host (as the note's
+    code does), sca_rebatch, msda_forward over the B*Ncam segments,
+    sca_scatter_mean.  Same arguments and result as sca_forward; returns
+    (slots, max_len)."""
+    B, Ncam, Nv, nH, Dh = value.shape
+    _, _, Nq, D, _ = reference_points_cam.shape
+    dev = value.device
+    if workspace is None:
+        workspace = torch.empty(sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device=dev)
+    hit = torch.empty((B, Nq), dtype=torch.int32, device=dev)
+    offs = torch.empty(B * Ncam + 1, dtype=torch.int32, device=dev)
+    pq = torch.empty(max(1, B * Ncam * Nq), dtype=torch.int32, device=dev)
+    sca_compact(bev_mask, reference_points_cam, workspace, hit_count=hit, pair_offsets=offs, pair_q=pq,
+                stream=stream)
+    o = offs.cpu().numpy()  # the host reads the segment bounds back, as the note's code does
+    max_len = int((o[1:] - o[:-1]).max()) if B * Ncam > 0 else 0
+    loc, lg = sca_rebatch(offs, pq, reference_points_cam, sampling_offsets, attention_logits, spatial_shapes,
+                          max_len, stream=stream)
+    rows = msda_forward(value.view(B * Ncam, Nv, nH, Dh), spatial_shapes, level_start_index, loc, lg,
+                        weight_mode=MSDA_WEIGHTS_LOGITS, stream=stream) if max_len > 0 else \
+        torch.empty((B * Ncam, 0, nH * Dh), dtype=torch.float32, device=dev)
+    slots = sca_scatter_mean(rows.view(B * Ncam, max_len, nH * Dh), offs, pq, hit, Nq, stream=stream)
+    return slots, max_len

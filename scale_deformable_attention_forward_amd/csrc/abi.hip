@@ -7,6 +7,7 @@
 
 #include "gemm.hpp"
 #include "internal.hpp"
+#include "rebatch.hpp"
 #include "msda.h"
 
 namespace {
@@ -366,6 +367,45 @@ int msda_output_proj_bf16(const void* X, int x_dtype, const uint16_t* W, const f
   g.beta = beta;
   g.eps = eps;
   return hip_status(msda::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)), "output projection launch");
+}
+
+int sca_rebatch(const int32_t* pair_offsets, const int32_t* pair_q, const float* reference_points_cam,
+                const float* sampling_offsets, const float* attention_logits, const int64_t* spatial_shapes,
+                int64_t B, int64_t Ncam, int64_t Nq, int nH, int L, int P, int D, int64_t max_len,
+                float* sampling_locations, float* logits_out, void* stream) {
+  if (B < 0 || Ncam < 1 || Nq < 0 || nH < 1 || L < 1 || P < 1 || D < 1 || max_len < 0)
+    return fail(MSDA_ERR_INVALID_ARG, "B, Nq, max_len >= 0 and Ncam, nH, L, P, D >= 1 required");
+  if (P % D != 0) return fail(MSDA_ERR_SHAPE, "P=%d is not a multiple of D=%d", P, D);
+  if (Ncam > 32 || B * Ncam >= kI31 || Nq >= kI31 || B * Ncam * max_len >= kI31)
+    return fail(MSDA_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  const bool rows = B * Ncam * max_len > 0;
+  if (!pair_offsets || !spatial_shapes || (rows && (!pair_q || !reference_points_cam || !sampling_offsets ||
+                                                    !attention_logits || !sampling_locations || !logits_out)))
+    return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(reference_points_cam, 8) || !aligned(sampling_offsets, 8) || !aligned(sampling_locations, 8))
+    return fail(MSDA_ERR_INVALID_ARG, "(x, y) arrays must be 8-byte aligned");
+  g_last_error[0] = '\0';
+  msda::RebatchArgs r = {pair_offsets, pair_q, reference_points_cam, sampling_offsets, attention_logits,
+                         spatial_shapes, B, Ncam, Nq, nH, L, P, D, max_len, sampling_locations, logits_out};
+  return hip_status(msda::launch_sca_rebatch(r, static_cast<hipStream_t>(stream)), "rebatch launch");
+}
+
+int sca_scatter_mean(const float* rows, const int32_t* pair_offsets, const int32_t* pair_q,
+                     const int32_t* hit_count, int64_t B, int64_t Ncam, int64_t Nq, int64_t C, int64_t max_len,
+                     float* slots, void* stream) {
+  if (B < 0 || Ncam < 1 || Nq < 0 || C < 4 || max_len < 0)
+    return fail(MSDA_ERR_INVALID_ARG, "B, Nq, max_len >= 0, Ncam >= 1 and C >= 4 required");
+  if (C % 4 != 0) return fail(MSDA_ERR_UNSUPPORTED, "C %% 4 == 0 required (got %lld)", (long long)C);
+  if (B * Ncam >= kI31 || B * Nq >= kI31 || B * Ncam * max_len >= kI31)
+    return fail(MSDA_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  const bool any = B * Nq > 0;
+  if (any && (!slots || !hit_count || !pair_offsets || (max_len > 0 && (!rows || !pair_q))))
+    return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if ((rows && !aligned(rows, 16)) || (slots && !aligned(slots, 16)))
+    return fail(MSDA_ERR_INVALID_ARG, "rows and slots must be 16-byte aligned");
+  g_last_error[0] = '\0';
+  msda::ScatterArgs a = {rows, pair_offsets, pair_q, hit_count, B, Ncam, Nq, C, max_len, slots};
+  return hip_status(msda::launch_sca_scatter_mean(a, static_cast<hipStream_t>(stream)), "scatter launch");
 }
 
 }  // extern "C"

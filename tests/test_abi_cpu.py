@@ -39,7 +39,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["msda_forward", "msda_forward_frames", "sca_workspace_size", "sca_forward", "msda_gemm_bf16",
-              "msda_query_proj_bf16", "msda_output_proj_bf16", "msda_status_string", "msda_last_error"]:
+              "msda_query_proj_bf16", "msda_output_proj_bf16", "sca_rebatch", "sca_scatter_mean",
+              "msda_status_string", "msda_last_error"]:
         assert n in names, n
 
 
@@ -209,6 +210,42 @@ def _op(lib, X=A, dt=0, W=A, bias=None, res=None, gamma=None, beta=None, eps=1e-
 ])
 def test_output_proj_rejects(lib, kw, code):
     assert _op(lib, **kw) == code
+
+
+def _rb(lib, po=A, pq=A, rp=A, off=A, lg=A, ss=A, B=1, Ncam=6, Nq=16, nH=8, L=4, P=8, D=4, ml=8, loc=B_, lo=B_):
+    return lib.sca_rebatch(po, pq, rp, off, lg, ss, B, Ncam, Nq, nH, L, P, D, ml, loc, lo, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(po=None), INVALID),
+    (dict(loc=None), INVALID),
+    (dict(ss=None), INVALID),
+    (dict(P=6), SHAPE),
+    (dict(Ncam=0), INVALID),
+    (dict(ml=-1), INVALID),
+    (dict(Ncam=33), UNSUPPORTED),
+    (dict(rp=A + 4), INVALID),
+    (dict(ml=0, pq=None, rp=None, off=None, lg=None, loc=None, lo=None), OK),  # no rows: nothing to do
+])
+def test_rebatch_rejects(lib, kw, code):
+    assert _rb(lib, **kw) == code
+
+
+def _sm(lib, rows=A, po=A, pq=A, hit=A, B=1, Ncam=6, Nq=16, C=256, ml=8, slots=B_):
+    return lib.sca_scatter_mean(rows, po, pq, hit, B, Ncam, Nq, C, ml, slots, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(slots=None), INVALID),
+    (dict(hit=None), INVALID),
+    (dict(rows=None), INVALID),
+    (dict(C=6), UNSUPPORTED),
+    (dict(C=0), INVALID),
+    (dict(rows=MIS), INVALID),
+    (dict(B=0, slots=None, hit=None, po=None, rows=None, pq=None), OK),
+])
+def test_scatter_mean_rejects(lib, kw, code):
+    assert _sm(lib, **kw) == code
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,120 @@
+"""The padded rebatch form of SCA (an A/B baseline for the fused path),
+against the oracle: the note's flow -- segment lists, locations materialised
+as float32 tensors for every padded row, the MSDA operator over all B*Ncam
+segments, scatter-add per camera and divide by the hit count.  Every call
+goes through the C ABI (via the ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import announce, assert_fp32_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+msda = pytest.importorskip("scale_deformable_attention_forward_amd")
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    announce(request.node.nodeid)
+    yield
+    torch.cuda.synchronize()
+
+
+def rebatch_reference(w):
+    """The note's flow on the CPU: segment lists from the oracle's compaction,
+    locations rho + offset / (W, H) formed in float32 (the operator takes them
+    as a float32 tensor), the oracle's MSDA over every padded row, then the
+    per-camera scatter-add in ascending camera order and the divide, in
+    float64.  Returns (loc, logits, slots [B*Nq, C], max_len)."""
+    value = w["value"]
+    B, Ncam, Nv, nH, Dh = value.shape
+    Nq, L, P, D = w["Nq"], w["L"], w["P"], w["D"]
+    comp = oracle.sca(value, w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
+                      w["bev_mask"], w["sampling_offsets"], w["attention_logits"], want_slots=False)
+    offs, pq, hit = comp["pair_offsets"], comp["pair_q"], comp["hit_count"]
+    max_len = int(np.diff(offs).max()) if offs.size > 1 else 0
+    ss = w["spatial_shapes"]
+    WH = np.stack([ss[:, 1], ss[:, 0]], -1).astype(np.float32)  # (W, H) per level
+    anchor = np.arange(P) % D
+    loc = np.zeros((B * Ncam, max_len, nH, L, P, 2), np.float32)
+    lg = np.zeros((B * Ncam, max_len, nH, L * P), np.float32)
+    for b in range(B):
+        for c in range(Ncam):
+            bc = b * Ncam + c
+            qs = pq[offs[bc]:offs[bc + 1]]
+            rho = w["reference_points_cam"][c, b][qs][:, anchor]  # [n, P, 2]
+            loc[bc, :len(qs)] = rho[:, None, None] + w["sampling_offsets"][b, qs] / WH[None, None, :, None, :]
+            lg[bc, :len(qs)] = w["attention_logits"][b, qs]
+    C = nH * Dh
+    slots = np.zeros((B * Nq, C), np.float64)
+    if max_len > 0:
+        rows = oracle.msda(value.reshape(B * Ncam, Nv, nH, Dh), w["spatial_shapes"], w["level_start_index"], loc, lg,
+                           weights_are_logits=True).reshape(B * Ncam, max_len, C)
+        for c in range(Ncam):
+            for b in range(B):
+                bc = b * Ncam + c
+                qs = pq[offs[bc]:offs[bc + 1]]
+                slots[b * Nq + qs] += rows[bc, :len(qs)]
+    slots /= np.maximum(hit.reshape(-1), 1)[:, None]
+    return loc, lg, slots, max_len
+
+
+def run_rebatch(w):
+    d = {k: dev(w[k]) for k in ("value", "spatial_shapes", "level_start_index", "reference_points_cam", "bev_mask",
+                                "sampling_offsets", "attention_logits")}
+    slots, max_len = msda.sca_forward_rebatch(d["value"], d["spatial_shapes"], d["level_start_index"],
+                                              d["reference_points_cam"], d["bev_mask"], d["sampling_offsets"],
+                                              d["attention_logits"])
+    return host(slots).reshape(-1, w["nH"] * w["Dh"]), max_len, d
+
+
+def test_rebatch_bevformer_sca_full():
+    """Workload 3 through the padded flow: max_len equals the longest segment,
+    the materialised locations and logits are bit-identical to the float32
+    definition, and the slots match the oracle's run of the same flow."""
+    w = W.bevformer_sca()
+    loc_ref, lg_ref, slots_ref, max_len_ref = rebatch_reference(w)
+    got, max_len, d = run_rebatch(w)
+    assert max_len == max_len_ref
+    B, Ncam, Nq = w["B"], w["Ncam"], w["Nq"]
+    hit = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
+    offs = torch.empty(B * Ncam + 1, dtype=torch.int32, device="cuda")
+    pq = torch.empty(B * Ncam * Nq, dtype=torch.int32, device="cuda")
+    ws = torch.empty(msda.sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device="cuda")
+    msda.sca_compact(d["bev_mask"], d["reference_points_cam"], ws, hit_count=hit, pair_offsets=offs, pair_q=pq)
+    loc, lg = msda.sca_rebatch(offs, pq, d["reference_points_cam"], d["sampling_offsets"], d["attention_logits"],
+                               d["spatial_shapes"], max_len)
+    assert np.array_equal(host(loc), loc_ref), "rebatched locations differ from the float32 definition"
+    assert np.array_equal(host(lg), lg_ref), "rebatched logits differ"
+    assert_fp32_close(got, slots_ref, "rebatch flow slots")
+
+
+REBATCH_EDGE = [
+    # id, B, Ncam, bev, shapes, P, D
+    ("two_items_masks_differ", 2, 6, 12, ((8, 12), (4, 6)), 4, 2),
+    ("one_camera", 1, 1, 9, ((6, 7),), 4, 4),
+    ("many_cameras_D1", 2, 9, 8, ((5, 5), (3, 3)), 3, 1),
+]
+
+
+@pytest.mark.parametrize("case", REBATCH_EDGE, ids=[c[0] for c in REBATCH_EDGE])
+def test_rebatch_edge_cases(case):
+    _, B, Ncam, bev, shapes, P, D = case
+    w = W.bevformer_sca(cfg=40 + B + Ncam, B=B, Ncam=Ncam, bev=bev, shapes=shapes, P=P, D=D)
+    _, _, slots_ref, max_len_ref = rebatch_reference(w)
+    got, max_len, _ = run_rebatch(w)
+    assert max_len == max_len_ref
+    assert_fp32_close(got, slots_ref, "rebatch flow slots")
+
+
+def test_rebatch_no_camera_sees_anything():
+    """Empty segments everywhere: max_len = 0, nothing is gathered and the
+    slots are zero."""
+    w = W.bevformer_sca(cfg=47, B=2, Ncam=3, bev=6, shapes=((4, 4),), P=4, D=2)
+    w["bev_mask"][:] = 0
+    got, max_len, _ = run_rebatch(w)
+    assert max_len == 0
+    assert not got.any()
