@@ -48,13 +48,17 @@ def _load(path=None):
     lib.oracle_linear_bf16.argtypes = [_p, _int, _p, _p, _i64, _i64, _i64, _p]
     lib.oracle_query_proj.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _i64, _p, _p]
     lib.oracle_output_proj.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_double, _i64, _i64, _i64, _p]
+    lib.oracle_msda_backward.argtypes = [_p, _int, _p, _p, _p, _p, _int, _p, _i64, _i64, _i64, _int, _int, _int,
+                                         _int, _p, _p, _p]
+    lib.oracle_sca_backward.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int,
+                                        _int, _int, _int, _p, _p, _p]
     lib.oracle_round_to_bf16.argtypes = [_p, _i64, _p]
     lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
     lib.oracle_double_to_bf16.restype = ctypes.c_uint16
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_double.restype = ctypes.c_double
     for f in (lib.oracle_msda, lib.oracle_msda_frames, lib.oracle_sca, lib.oracle_linear_bf16,
-              lib.oracle_query_proj, lib.oracle_output_proj):
+              lib.oracle_query_proj, lib.oracle_output_proj, lib.oracle_msda_backward, lib.oracle_sca_backward):
         f.restype = _int
     _lib = lib
     return lib
@@ -185,6 +189,58 @@ def linear_bf16(X, W, bias=None):
     _check(rc, "oracle_linear_bf16")
     del x, w, b
     return Y
+
+
+def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights, grad_out,
+                  weights_are_logits=False):
+    """Gradients of msda() for d loss / d out = grad_out [B,Nq,nH*Dh].
+    Returns (grad_value [B,Nv,nH,Dh], grad_locations [B,Nq,nH,L,P,2],
+    grad_weights [B,Nq,nH,L*P]) float64; grad_weights is with respect to the
+    weights as given (logits or probabilities)."""
+    lib = _load()
+    B, Nv, nH, Dh = value.shape
+    _, Nq, _, L, P, _ = sampling_locations.shape
+    v, vp, vb = _value(value)
+    ss, ssp = _c(spatial_shapes, np.int64)
+    ls, lsp = _c(level_start_index, np.int64)
+    loc, locp = _c(sampling_locations, np.float32)
+    w, wp = _c(attention_weights, np.float32)
+    go, gop = _c(grad_out, np.float32)
+    gv = np.zeros((B, Nv, nH, Dh), np.float64)
+    gl = np.zeros((B, Nq, nH, L, P, 2), np.float64)
+    gw = np.zeros((B, Nq, nH, L * P), np.float64)
+    rc = lib.oracle_msda_backward(vp, vb, ssp, lsp, locp, wp, int(bool(weights_are_logits)), gop, B, Nv, Nq, nH, Dh,
+                                  L, P, gv.ctypes.data_as(_p), gl.ctypes.data_as(_p), gw.ctypes.data_as(_p))
+    _check(rc, "oracle_msda_backward")
+    del v, ss, ls, loc, w, go
+    return gv, gl, gw
+
+
+def sca_backward(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
+                 attention_logits, grad_slots):
+    """Gradients of sca() for d loss / d slots = grad_slots [B,Nq,nH*Dh].
+    Returns (grad_value [B,Ncam,Nv,nH,Dh], grad_offsets [B,Nq,nH,L,P,2],
+    grad_logits [B,Nq,nH,L*P]) float64."""
+    lib = _load()
+    B, Ncam, Nv, nH, Dh = value.shape
+    _, _, Nq, D, _ = reference_points_cam.shape
+    _, _, _, L, P, _ = sampling_offsets.shape
+    v, vp, vb = _value(value)
+    ss, ssp = _c(spatial_shapes, np.int64)
+    ls, lsp = _c(level_start_index, np.int64)
+    rpc, rpcp = _c(reference_points_cam, np.float32)
+    bm, bmp = _c(bev_mask, np.uint8)
+    off, offp = _c(sampling_offsets, np.float32)
+    lg, lgp = _c(attention_logits, np.float32)
+    go, gop = _c(grad_slots, np.float32)
+    gv = np.zeros((B, Ncam, Nv, nH, Dh), np.float64)
+    goff = np.zeros((B, Nq, nH, L, P, 2), np.float64)
+    glg = np.zeros((B, Nq, nH, L * P), np.float64)
+    rc = lib.oracle_sca_backward(vp, vb, ssp, lsp, rpcp, bmp, offp, lgp, gop, B, Ncam, Nv, Nq, nH, Dh, L, P, D,
+                                 gv.ctypes.data_as(_p), goff.ctypes.data_as(_p), glg.ctypes.data_as(_p))
+    _check(rc, "oracle_sca_backward")
+    del v, ss, ls, rpc, bm, off, lg, go
+    return gv, goff, glg
 
 
 def _opt(a, dtype):

@@ -51,7 +51,11 @@
  *     float32 sum query + position embedding ([8-heads] 4);
  *   - the encoder layer's norm after the residual ([8-heads] 18.7) is the
  *     plain layer norm over the row (variance with divisor N, eps inside the
- *     square root, then gamma and beta); the pages name it only.
+ *     square root, then gamma and beta); the pages name it only;
+ *   - backward pass ([8-heads] 4.3 says only that offsets and weights are
+ *     learned by back-propagation): the derivatives of the forward
+ *     definitions; at an integer x or y, where bilinear sampling has a kink,
+ *     the derivative of the cell floor(x), floor(y) is taken.
  */
 #include <math.h>
 #include <stdint.h>
@@ -521,5 +525,215 @@ int oracle_output_proj(const float* slots, const uint16_t* W, const float* bias,
                 y[n] = (y[n] - mean) * inv * (double)gamma[n] + (beta ? (double)beta[n] : 0.0);
         }
     }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass                                                             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages say only that the offsets and the weights are learned by back-
+ * propagation ([8-heads] 4.3).  The gradients here are the derivatives of the
+ * forward definitions above, by the chain rule.  For one head of one query,
+ *   out = sum_k alpha_k * S_k,   S_k = sum over corners c of w_c * V[c],
+ *   x = W*sx - 1/2, y = H*sy - 1/2, fx = x - floor(x), fy = y - floor(y),
+ *   w_c = (i ? fx : 1-fx) * (j ? fy : 1-fy)  for corner (floor(x)+i, floor(y)+j);
+ * so, with g = d loss / d out,
+ *   d loss / d alpha_k = <S_k, g>,
+ *   d loss / d V[c]   += alpha_k * w_c * g,
+ *   d loss / d x       = alpha_k * sum_c <V[c], g> * d w_c / d x,
+ *       d w_c / d x = (i ? 1 : -1) * (j ? fy : 1-fy),  d w_c / d y = (i ? fx : 1-fx) * (j ? 1 : -1),
+ *   d x / d sx = W,  d y / d sy = H;
+ * through the softmax, d loss / d a_i = alpha_i * (d loss / d alpha_i - sum_k alpha_k d loss / d alpha_k).
+ * Corners outside the map hold no value (zero padding) and contribute to none
+ * of these.  Where x or y is an integer the sampled function has a kink; the
+ * derivative taken is the one of the cell floor(x), floor(y) (its right-hand
+ * derivative), the plainest reading.
+ */
+
+/* One sample's backward: adds alpha * w_c * g to the value gradient of each
+ * corner (grad_img laid out as the value image, may be NULL) and returns
+ * <S, g>, <dS/dx, g> and <dS/dy, g>. */
+static void bilinear_backward(const ValueImage* v, double* grad_img, int64_t H, int64_t W, int64_t start,
+                              int64_t h, double sx, double sy, double weight, const double* g,
+                              double* dot_s, double* dot_x, double* dot_y)
+{
+    double x = (double)W * sx - 0.5;
+    double y = (double)H * sy - 0.5;
+    double x0 = floor(x), y0 = floor(y);
+    double fx = x - x0, fy = y - y0;
+    *dot_s = *dot_x = *dot_y = 0.0;
+    for (int j = 0; j < 2; ++j) {
+        for (int i = 0; i < 2; ++i) {
+            double cx = x0 + i, cy = y0 + j;
+            if (cx < 0.0 || cx >= (double)W || cy < 0.0 || cy >= (double)H) continue;
+            double w = (i ? fx : 1.0 - fx) * (j ? fy : 1.0 - fy);
+            double wx = (i ? 1.0 : -1.0) * (j ? fy : 1.0 - fy);
+            double wy = (i ? fx : 1.0 - fx) * (j ? 1.0 : -1.0);
+            int64_t pixel = start + (int64_t)cy * W + (int64_t)cx;
+            for (int64_t d = 0; d < v->Dh; ++d) {
+                double vg = value_at(v, pixel, h, d) * g[d];
+                *dot_s += w * vg;
+                *dot_x += wx * vg;
+                *dot_y += wy * vg;
+                if (grad_img) grad_img[(pixel * v->nH + h) * v->Dh + d] += weight * w * g[d];
+            }
+        }
+    }
+}
+
+/* d loss / d weights of one query: through the softmax of each head for
+ * logits, as is for probabilities. */
+static void weights_backward(const double* alpha, const double* dalpha, int nH, int LP, int are_logits,
+                             double* grad_w)
+{
+    for (int h = 0; h < nH; ++h) {
+        const double* a = alpha + (int64_t)h * LP;
+        const double* da = dalpha + (int64_t)h * LP;
+        double* gw = grad_w + (int64_t)h * LP;
+        if (!are_logits) {
+            for (int i = 0; i < LP; ++i) gw[i] = da[i];
+            continue;
+        }
+        double dot = 0.0;
+        for (int i = 0; i < LP; ++i) dot += a[i] * da[i];
+        for (int i = 0; i < LP; ++i) gw[i] = a[i] * (da[i] - dot);
+    }
+}
+
+/*
+ * Gradients of the MSDA operator (oracle_msda) for d loss / d out = grad_out.
+ *   grad_out        [B][Nq][nH*Dh]
+ *   grad_value      [B][Nv][nH][Dh]        overwritten
+ *   grad_locations  [B][Nq][nH][L][P][2]   with respect to the normalised (x, y)
+ *   grad_weights    [B][Nq][nH][L*P]       with respect to attention_weights as given
+ *                                          (logits or probabilities)
+ */
+int oracle_msda_backward(const void* value, int value_bf16, const int64_t* spatial_shapes,
+                         const int64_t* level_start_index, const float* sampling_locations,
+                         const float* attention_weights, int weights_are_logits, const float* grad_out,
+                         int64_t B, int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P,
+                         double* grad_value, double* grad_locations, double* grad_weights)
+{
+    if (!value || !spatial_shapes || !level_start_index || !sampling_locations || !attention_weights ||
+        !grad_out || !grad_value || !grad_locations || !grad_weights)
+        return ORACLE_BAD_ARG;
+    if (B < 1 || Nv < 1 || Nq < 0 || nH < 1 || Dh < 1 || L < 1 || P < 1) return ORACLE_BAD_ARG;
+    if (!levels_ok(spatial_shapes, level_start_index, L, Nv)) return ORACLE_BAD_ARG;
+    const int LP = L * P;
+    const int64_t C = (int64_t)nH * Dh;
+    for (int64_t i = 0; i < B * Nv * C; ++i) grad_value[i] = 0.0;
+    double* alpha = (double*)malloc(sizeof(double) * (size_t)nH * LP);
+    double* dalpha = (double*)malloc(sizeof(double) * (size_t)nH * LP);
+    double* g = (double*)malloc(sizeof(double) * (size_t)Dh);
+    if (!alpha || !dalpha || !g) { free(alpha); free(dalpha); free(g); return ORACLE_BAD_ARG; }
+    const size_t elem = value_bf16 ? 2 : 4;
+    for (int64_t bq = 0; bq < B * Nq; ++bq) {
+        int64_t b = bq / Nq;
+        ValueImage img = {(const char*)value + (size_t)(b * Nv * C) * elem, value_bf16, nH, Dh};
+        double* grad_img = grad_value + b * Nv * C;
+        head_weights(attention_weights + bq * nH * LP, nH, LP, weights_are_logits, alpha);
+        for (int h = 0; h < nH; ++h) {
+            for (int d = 0; d < Dh; ++d) g[d] = (double)grad_out[bq * C + (int64_t)h * Dh + d];
+            for (int l = 0; l < L; ++l) {
+                int64_t H = spatial_shapes[2 * l], W = spatial_shapes[2 * l + 1];
+                for (int k = 0; k < P; ++k) {
+                    int64_t at = ((bq * nH + h) * L + l) * P + k;
+                    const float* s = sampling_locations + at * 2;
+                    double a = alpha[(int64_t)h * LP + l * P + k];
+                    double ds, dx, dy;
+                    bilinear_backward(&img, grad_img, H, W, level_start_index[l], h, (double)s[0], (double)s[1],
+                                      a, g, &ds, &dx, &dy);
+                    dalpha[(int64_t)h * LP + l * P + k] = ds;
+                    grad_locations[at * 2 + 0] = a * (double)W * dx;
+                    grad_locations[at * 2 + 1] = a * (double)H * dy;
+                }
+            }
+        }
+        weights_backward(alpha, dalpha, nH, LP, weights_are_logits, grad_weights + bq * nH * LP);
+    }
+    free(alpha); free(dalpha); free(g);
+    return ORACLE_OK;
+}
+
+/*
+ * Gradients of spatial cross-attention (oracle_sca) for d loss / d slots =
+ * grad_slots.  The camera mean divides each seeing camera's contribution by
+ * the hit count; a location is s = rho + (dx / W, dy / H), so an offset in
+ * cells moves x and y one for one (d x / d dx = W * (1/W) = 1).  Offsets and
+ * logits serve every camera, so their gradients sum over the cameras.
+ *   grad_slots    [B][Nq][nH*Dh]
+ *   grad_value    [B][Ncam][Nv][nH][Dh]   overwritten
+ *   grad_offsets  [B][Nq][nH][L][P][2]    in cells; zero for queries no camera sees
+ *   grad_logits   [B][Nq][nH][L*P]        likewise
+ */
+int oracle_sca_backward(const void* value, int value_bf16, const int64_t* spatial_shapes,
+                        const int64_t* level_start_index, const float* reference_points_cam,
+                        const uint8_t* bev_mask, const float* sampling_offsets, const float* attention_logits,
+                        const float* grad_slots, int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int Dh,
+                        int L, int P, int D, double* grad_value, double* grad_offsets, double* grad_logits)
+{
+    if (!value || !spatial_shapes || !level_start_index || !reference_points_cam || !bev_mask ||
+        !sampling_offsets || !attention_logits || !grad_slots || !grad_value || !grad_offsets || !grad_logits)
+        return ORACLE_BAD_ARG;
+    if (B < 1 || Ncam < 1 || Nv < 1 || Nq < 0 || nH < 1 || Dh < 1 || L < 1 || P < 1 || D < 1 || P % D != 0)
+        return ORACLE_BAD_ARG;
+    if (!levels_ok(spatial_shapes, level_start_index, L, Nv)) return ORACLE_BAD_ARG;
+    const int LP = L * P;
+    const int64_t C = (int64_t)nH * Dh;
+    for (int64_t i = 0; i < B * Ncam * Nv * C; ++i) grad_value[i] = 0.0;
+    double* alpha = (double*)malloc(sizeof(double) * (size_t)nH * LP);
+    double* dalpha = (double*)malloc(sizeof(double) * (size_t)nH * LP);
+    double* g = (double*)malloc(sizeof(double) * (size_t)Dh);
+    if (!alpha || !dalpha || !g) { free(alpha); free(dalpha); free(g); return ORACLE_BAD_ARG; }
+    const size_t elem = value_bf16 ? 2 : 4;
+    for (int64_t bq = 0; bq < B * Nq; ++bq) {
+        int64_t b = bq / Nq, q = bq % Nq;
+        double* goff = grad_offsets + bq * nH * LP * 2;
+        double* glog = grad_logits + bq * nH * LP;
+        for (int64_t i = 0; i < (int64_t)nH * LP * 2; ++i) goff[i] = 0.0;
+        for (int64_t i = 0; i < (int64_t)nH * LP; ++i) dalpha[i] = 0.0;
+        /* the cameras that see the query (step 1 of the forward) */
+        int hits = 0;
+        for (int64_t c = 0; c < Ncam; ++c) {
+            int any = 0;
+            for (int m = 0; m < D; ++m) any |= bev_mask[((c * B + b) * Nq + q) * D + m] != 0;
+            hits += any;
+        }
+        head_weights(attention_logits + bq * nH * LP, nH, LP, 1, alpha);
+        double n = hits > 1 ? (double)hits : 1.0;
+        for (int64_t c = 0; c < Ncam && hits > 0; ++c) {
+            int any = 0;
+            for (int m = 0; m < D; ++m) any |= bev_mask[((c * B + b) * Nq + q) * D + m] != 0;
+            if (!any) continue;
+            ValueImage img = {(const char*)value + (size_t)((b * Ncam + c) * Nv * C) * elem, value_bf16, nH, Dh};
+            double* grad_img = grad_value + (b * Ncam + c) * Nv * C;
+            const float* rho = reference_points_cam + ((c * B + b) * Nq + q) * D * 2;
+            for (int h = 0; h < nH; ++h) {
+                /* d slots / d (camera c's sum) = 1 / n */
+                for (int d = 0; d < Dh; ++d) g[d] = (double)grad_slots[bq * C + (int64_t)h * Dh + d] / n;
+                for (int l = 0; l < L; ++l) {
+                    int64_t H = spatial_shapes[2 * l], W = spatial_shapes[2 * l + 1];
+                    for (int k = 0; k < P; ++k) {
+                        int m = k % D;
+                        int64_t at = ((int64_t)h * L + l) * P + k;
+                        const float* off = sampling_offsets + (bq * nH * LP + at) * 2;
+                        double sx = (double)rho[m * 2 + 0] + (double)off[0] / (double)W;
+                        double sy = (double)rho[m * 2 + 1] + (double)off[1] / (double)H;
+                        double a = alpha[(int64_t)h * LP + l * P + k];
+                        double ds, dx, dy;
+                        bilinear_backward(&img, grad_img, H, W, level_start_index[l], h, sx, sy, a, g, &ds, &dx,
+                                          &dy);
+                        dalpha[(int64_t)h * LP + l * P + k] += ds;
+                        goff[at * 2 + 0] += a * dx;
+                        goff[at * 2 + 1] += a * dy;
+                    }
+                }
+            }
+        }
+        weights_backward(alpha, dalpha, nH, LP, 1, glog);
+    }
+    free(alpha); free(dalpha); free(g);
     return ORACLE_OK;
 }

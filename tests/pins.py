@@ -565,6 +565,154 @@ def pin_output_proj_layer_norm():
     _close(got, np.sign(row) * 2.0 * a / np.sqrt(a * a + eps) + 0.5, 1e-14, "alternating row")
 
 
+# ---------------------------------------------------------------------------
+# backward pass: derivatives of the forward definitions ([8-heads] 4.3 says
+# only that offsets and weights are learned by back-propagation)
+# ---------------------------------------------------------------------------
+
+_STEP = 2.0 ** -10  # float32-exact step for locations / logits
+
+
+def _interior_coord(g, n, size, lo=0.3, hi=0.7, outside=0.15):
+    """Continuous coordinates on a map of `size` cells whose fractional part
+    lies in [lo, hi] (so a step of at most 1/128 cell stays in the cell, where
+    bilinear sampling is linear); a share of them in the cell left of the map
+    (corner -1 outside) or right of it, to cover zero padding."""
+    cell = g.integers(0, size, n).astype(np.float64)
+    edge = g.random(n) < outside
+    cell[edge] = np.where(g.random(int(edge.sum())) < 0.5, -1.0, float(size - 1))
+    return cell + g.uniform(lo, hi, n)
+
+
+def _bwd_msda_case(seed, B=2, Nq=4, shapes=((5, 8), (3, 4)), nH=3, Dh=4, P=3):
+    ss, starts, Nv = level_table(shapes)
+    L = len(ss)
+    g = np.random.default_rng(seed)
+    value = g.normal(size=(B, Nv, nH, Dh)).astype(np.float32)
+    loc = np.zeros((B, Nq, nH, L, P, 2), np.float64)
+    for l in range(L):
+        H, W = ss[l]
+        n = B * Nq * nH * P
+        x = _interior_coord(g, n, W).reshape(B, Nq, nH, P)
+        y = _interior_coord(g, n, H).reshape(B, Nq, nH, P)
+        loc[:, :, :, l, :, 0] = (x + 0.5) / W
+        loc[:, :, :, l, :, 1] = (y + 0.5) / H
+    loc = (np.round(loc * 2.0 ** 20) / 2.0 ** 20).astype(np.float32)  # s +- step stays exact in float32
+    logits = (np.round(g.normal(size=(B, Nq, nH, L * P)) * 2.0 ** 12) / 2.0 ** 12).astype(np.float32)
+    probs = (np.round(g.uniform(0.0, 0.5, size=(B, Nq, nH, L * P)) * 2.0 ** 12) / 2.0 ** 12).astype(np.float32)
+    grad_out = g.normal(size=(B, Nq, nH * Dh)).astype(np.float32)
+    return value, ss, starts, loc, logits, probs, grad_out
+
+
+def _loss(grad_out, out):
+    return float(np.sum(grad_out.reshape(out.shape).astype(np.float64) * out))
+
+
+def pin_msda_backward():
+    """MSDA gradients against facts outside the backward code: the output is
+    linear in the value and in the probabilities (adjoint identities); central
+    differences of the forward oracle in every location coordinate (exact: the
+    sampled function is linear inside a cell) and in every logit; the gradient
+    through a softmax sums to zero over a head."""
+    value, ss, starts, loc, logits, probs, gout = _bwd_msda_case(151)
+    g = np.random.default_rng(152)
+    for weights, are_logits in ((logits, True), (probs, False)):
+        gv, gl, gw = oracle.msda_backward(value, ss, starts, loc, weights, gout, weights_are_logits=are_logits)
+        fwd = lambda v=value, lc=loc, w=weights: oracle.msda(v, ss, starts, lc, w, weights_are_logits=are_logits)
+        dv = g.normal(size=value.shape).astype(np.float32)
+        _close(np.sum(gv * dv), _loss(gout, fwd(v=dv)), 1e-11, "value adjoint")
+        if not are_logits:
+            da = g.normal(size=probs.shape).astype(np.float32)
+            _close(np.sum(gw * da), _loss(gout, fwd(w=da)), 1e-11, "probability adjoint")
+        else:
+            _close(gw.reshape(-1, gw.shape[-1]).sum(-1), np.zeros(gw.size // gw.shape[-1]), 1e-13,
+                   "softmax gradient sums to zero")
+        fd = np.zeros(loc.size)
+        for i in range(loc.size):
+            up, dn = loc.copy().reshape(-1), loc.copy().reshape(-1)
+            up[i] += _STEP
+            dn[i] -= _STEP
+            fd[i] = (_loss(gout, fwd(lc=up.reshape(loc.shape))) - _loss(gout, fwd(lc=dn.reshape(loc.shape)))) / (2 * _STEP)
+        _close(gl.reshape(-1), fd, 1e-9, "location central differences")
+        if are_logits:
+            fd = np.zeros(weights.size)
+            for i in range(weights.size):
+                up, dn = weights.copy().reshape(-1), weights.copy().reshape(-1)
+                up[i] += _STEP
+                dn[i] -= _STEP
+                fd[i] = (_loss(gout, fwd(w=up.reshape(weights.shape))) -
+                         _loss(gout, fwd(w=dn.reshape(weights.shape)))) / (2 * _STEP)
+            _close(gw.reshape(-1), fd, 2e-6, "logit central differences")
+
+
+def _bwd_sca_case(seed, B=2, Ncam=3, Nq=6, shapes=((6, 8), (3, 4)), nH=2, Dh=4, P=4, D=2):
+    ss, starts, Nv = level_table(shapes)
+    L = len(ss)
+    g = np.random.default_rng(seed)
+    value = g.normal(size=(B, Ncam, Nv, nH, Dh)).astype(np.float32)
+    mask = (g.random((Ncam, B, Nq, D)) < 0.45).astype(np.uint8)
+    mask[:, 0, 0] = 0  # a query no camera sees
+    mask[:, 1, 1] = 1  # a query every camera sees
+    # anchors at exact multiples of 1/64 of the unit square; offsets in cells
+    # so that every x = W*rho + dx - 1/2 has a fractional part in [0.3, 0.7]
+    rho = (g.integers(8, 56, size=(Ncam, B, Nq, D, 2)) / 64.0).astype(np.float32)
+    off = np.zeros((B, Nq, nH, L, P, 2), np.float64)
+    for l in range(L):
+        H, W = ss[l]
+        for ax, size in ((0, W), (1, H)):
+            base = rho[..., ax].astype(np.float64) * size - 0.5  # [Ncam, B, Nq, D]
+            # one offset per (b, q, h, point) must suit every camera: pick the
+            # fraction against camera 0's anchor and check the others below
+            want = np.floor(base[0]) + g.uniform(0.3, 0.7, base[0].shape)  # [B, Nq, D]
+            for k in range(P):
+                off[:, :, :, l, k, ax] = (want[:, :, None, k % D] - base[0][:, :, None, k % D]
+                                          + g.integers(-2, 3, (B, Nq, nH)))
+    off = (np.round(off * 2.0 ** 12) / 2.0 ** 12).astype(np.float32)
+    logits = (np.round(g.normal(size=(B, Nq, nH, L * P)) * 2.0 ** 12) / 2.0 ** 12).astype(np.float32)
+    grad = g.normal(size=(B, Nq, nH * Dh)).astype(np.float32)
+    return value, ss, starts, rho, mask, off, logits, grad
+
+
+def pin_sca_backward():
+    """SCA gradients: linear in the value (adjoint identity); central
+    differences in every offset coordinate whose sample stays inside its cell
+    for every camera (exact) and in every logit; zero for a query no camera
+    sees; the gradient through each head's softmax sums to zero."""
+    value, ss, starts, rho, mask, off, logits, gout = _bwd_sca_case(161)
+    gv, goff, glg = oracle.sca_backward(value, ss, starts, rho, mask, off, logits, gout)
+    fwd = lambda v=value, o=off, lg=logits: oracle.sca(v, ss, starts, rho, mask, o, lg)["slots"]
+    dv = np.random.default_rng(162).normal(size=value.shape).astype(np.float32)
+    _close(np.sum(gv * dv), _loss(gout, fwd(v=dv)), 1e-11, "value adjoint")
+    assert not goff[0, 0].any() and not glg[0, 0].any(), "unseen query has a gradient"
+    _close(glg.reshape(-1, glg.shape[-1]).sum(-1), np.zeros(glg.size // glg.shape[-1]), 1e-13, "softmax sums")
+    step = 2.0 ** -8
+    W_ = np.array([s[1] for s in ss], np.float64)
+    H_ = np.array([s[0] for s in ss], np.float64)
+    B, Ncam, Nv, nH, Dh = value.shape
+    Nq, D = rho.shape[2], rho.shape[3]
+    checked = 0
+    for idx in np.ndindex(off.shape):
+        b, q, h, l, k, ax = idx
+        size = W_[l] if ax == 0 else H_[l]
+        base = rho[:, b, q, k % D, ax].astype(np.float64) * size + off[idx] - 0.5  # x per camera
+        frac = base - np.floor(base)
+        if np.any((frac < 0.1) | (frac > 0.9)):
+            continue  # a camera's sample sits near a cell edge: the step could cross it
+        up, dn = off.copy(), off.copy()
+        up[idx] += step
+        dn[idx] -= step
+        fd = (_loss(gout, fwd(o=up)) - _loss(gout, fwd(o=dn))) / (2 * step)
+        _close(goff[idx], fd, 1e-9, f"offset central difference {idx}")
+        checked += 1
+    assert checked > off.size // 2, checked
+    for idx in list(np.ndindex(logits.shape))[::3]:
+        up, dn = logits.copy(), logits.copy()
+        up[idx] += _STEP
+        dn[idx] -= _STEP
+        fd = (_loss(gout, fwd(lg=up)) - _loss(gout, fwd(lg=dn))) / (2 * _STEP)
+        _close(glg[idx], fd, 2e-6, f"logit central difference {idx}")
+
+
 ALL_PINS = [
     pin_worked_example_two_heads,
     pin_scalar_times_sample,
@@ -583,4 +731,6 @@ ALL_PINS = [
     pin_linear_bf16,
     pin_query_proj,
     pin_output_proj_layer_norm,
+    pin_msda_backward,
+    pin_sca_backward,
 ]

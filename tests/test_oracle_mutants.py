@@ -49,6 +49,17 @@ MUTANTS = [
     ("norm_eps_outside_sqrt", "1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
     ("norm_mean_kept", "y[n] = (y[n] - mean) * inv", "y[n] = y[n] * inv"),
     ("norm_gamma_ignored", "* inv * (double)gamma[n]", "* inv * 1.0"),
+    ("bwd_dx_sign", "double wx = (i ? 1.0 : -1.0)", "double wx = (i ? -1.0 : 1.0)"),
+    ("bwd_dy_uses_fy", "double wy = (i ? fx : 1.0 - fx) * (j ? 1.0 : -1.0);",
+     "double wy = (i ? fy : 1.0 - fy) * (j ? 1.0 : -1.0);"),
+    ("bwd_location_not_scaled", "grad_locations[at * 2 + 0] = a * (double)W * dx;",
+     "grad_locations[at * 2 + 0] = a * dx;"),
+    ("bwd_value_weight_dropped", "+= weight * w * g[d];", "+= w * g[d];"),
+    ("bwd_softmax_not_centred", "gw[i] = a[i] * (da[i] - dot);", "gw[i] = a[i] * da[i];"),
+    ("bwd_sample_from_x_slope", "*dot_s += w * vg;", "*dot_s += wx * vg;"),
+    ("bwd_camera_mean_dropped", "(double)grad_slots[bq * C + (int64_t)h * Dh + d] / n;",
+     "(double)grad_slots[bq * C + (int64_t)h * Dh + d] / 1.0;"),
+    ("bwd_offset_scaled_by_width", "goff[at * 2 + 0] += a * dx;", "goff[at * 2 + 0] += a * dx * (double)W;"),
 ]
 
 

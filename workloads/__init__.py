@@ -26,7 +26,7 @@ BEV_CAM_LEVELS = ((116, 200), (58, 100), (29, 50), (15, 25))
 
 # tensor ids inside one workload's seed sequence
 _T_VALUE, _T_REF, _T_OFF, _T_LOGIT, _T_MASK, _T_W_V, _T_W_O, _T_BIAS = range(8)
-_T_QUERY, _T_QPOS, _T_W_OFF, _T_W_ATT, _T_NORM = range(8, 13)
+_T_QUERY, _T_QPOS, _T_W_OFF, _T_W_ATT, _T_NORM, _T_GRAD = range(8, 14)
 
 
 def rng(cfg, tensor_id):
@@ -246,6 +246,12 @@ def bevformer_layer_bf16(cfg=5, B=4, bev=200, shapes=BEV_CAM_LEVELS, bias=False,
     w["gamma"] = (1.0 + _normal(g, (C,), 0.1)).astype(np.float32)
     w["beta"] = _normal(g, (C,), 0.1)
     return w
+
+
+def upstream_gradient(cfg, shape):
+    """d loss / d output for the backward pass: N(0, 1) float32 of `shape`,
+    drawn from its own generator of workload `cfg`."""
+    return _normal(rng(cfg, _T_GRAD), shape)
 
 
 def sample_rows(cfg, total, n):
