@@ -16,8 +16,10 @@ query + position embedding in one launch, and the output projection
 followed by the residual and the layer norm), "sca_bf16", "sca_rebatch"
 (workload 3 through the padded rebatch flow of the SCA note, an A/B
 baseline: per-camera segments padded to the longest, the operator over all
-of them, scatter-add and divide), "detr" (Deformable-DETR encoder MSDA), "tsa" (two stacked BEV
-maps, frame mean), "tiny".
+of them, scatter-add and divide), "sca_train" and "detr_train" (forward and
+backward of workload 3's SCA and of the DETR encoder MSDA; the roofline
+then describes the backward kernel), "detr" (Deformable-DETR encoder MSDA),
+"tsa" (two stacked BEV maps, frame mean), "tiny".
 
 Prints one JSON line.  value = bilinear samples per second (one sample = one
 (camera, query, head, level, point) bilinear read of 4 corners x 32
@@ -364,6 +366,98 @@ def rebatch_workload():
     return wl
 
 
+def train_workload(which):
+    """Forward and backward of one step: "sca_train" (workload 3: compaction,
+    SCA forward, SCA backward) or "detr_train" (workload 2: MSDA forward and
+    backward).  The upstream gradient is seeded N(0, 1)."""
+    import torch
+    import workloads as W
+    import scale_deformable_attention_forward_amd as m
+
+    wl = Workload(which)
+    if which == "sca_train":
+        w = W.bevformer_sca()
+        B, Ncam, Nq, Nv, nH, L, P, D = w["B"], w["Ncam"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"], w["D"]
+        d = {k: _dev(w[k]) for k in ("value", "spatial_shapes", "level_start_index", "reference_points_cam",
+                                     "bev_mask", "sampling_offsets", "attention_logits")}
+        gout = _dev(W.upstream_gradient(3, (B, Nq, nH * 32)))
+        ws = torch.empty(m.sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device="cuda")
+        slots = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
+        offs = torch.empty(B * Ncam + 1, dtype=torch.int32, device="cuda")
+        gv = torch.empty((B, Ncam, Nv, nH, 32), dtype=torch.float32, device="cuda")
+        go = torch.empty_like(d["sampling_offsets"])
+        gl = torch.empty_like(d["attention_logits"])
+        args = (d["spatial_shapes"], d["level_start_index"], d["reference_points_cam"])
+        wl.parts.append(("compact", lambda: m.sca_compact(d["bev_mask"], d["reference_points_cam"], ws,
+                                                          pair_offsets=offs)))
+        wl.parts.append(("forward", lambda: m.sca_gather(d["value"], *args, d["sampling_offsets"],
+                                                         d["attention_logits"], ws, slots=slots)))
+        wl.parts.append(("backward", lambda: m.sca_backward(d["value"], *args, d["sampling_offsets"],
+                                                            d["attention_logits"], gout, ws, grad_value=gv,
+                                                            grad_offsets=go, grad_logits=gl)))
+        names = "BEVFormer-base spatial cross-attention layer, 6 cameras, forward + backward"
+        pairs = lambda: int(offs[-1].item())
+        n_images = B * Ncam
+    else:
+        w = W.detr_encoder_msda()
+        B, Nq, Nv, nH, L, P = w["B"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"]
+        d = {k: _dev(w[k]) for k in ("value", "spatial_shapes", "level_start_index", "sampling_locations",
+                                     "attention_weights")}
+        gout = _dev(W.upstream_gradient(2, (B, Nq, nH * 32)))
+        out = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
+        gv = torch.empty((B, Nv, nH, 32), dtype=torch.float32, device="cuda")
+        gloc = torch.empty_like(d["sampling_locations"])
+        gw = torch.empty_like(d["attention_weights"])
+        fargs = (d["value"], d["spatial_shapes"], d["level_start_index"], d["sampling_locations"],
+                 d["attention_weights"])
+        wl.parts.append(("forward", lambda: m.msda_forward(*fargs, out=out)))
+        wl.parts.append(("backward", lambda: m.msda_backward(*fargs, gout, grad_value=gv, grad_locations=gloc,
+                                                             grad_weights=gw)))
+        names = "Deformable-DETR encoder MSDA, 4 levels 100x150/50x75/25x38/13x19, Nq=Nv=19947, forward + backward"
+        pairs = lambda: B * Nq
+        n_images = B
+    wl.main = "backward"
+
+    def finish():
+        n = pairs()
+        wl.samples = n * nH * L * P
+        # backward: the corner rows read (as the forward) and the same rows of
+        # value gradient added to, the per-query inputs and upstream gradient
+        # read, the offset / location and weight gradients written, and the
+        # value gradient zeroed first
+        S = wl.samples
+        wl.gathered_bytes = S * 4 * 32 * 4
+        wl.eff_bytes = (2 * wl.gathered_bytes + B * Nq * nH * L * P * (8 + 4) * 2 + B * Nq * nH * 32 * 4
+                        + n_images * Nv * nH * 32 * 4)
+    wl.finish = finish
+    wl.batch = B
+    wl.config = {"workload": names, "batch": B, "queries": Nq, "heads": nH, "head_dim": 32, "levels": L,
+                 "points_per_level": P, "value_dtype": "fp32", "pass": "forward + backward"}
+    wl.dtype = "fp32"
+    wl.kernel_key = ("sca_backward_kernel" if which == "sca_train" else "msda_backward_kernel") + "_fp32"
+
+    def cpu_baseline():
+        import oracle
+        t0 = time.perf_counter()
+        g = gout.cpu().numpy()
+        if which == "sca_train":
+            oracle.sca(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
+                       w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
+            oracle.sca_backward(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
+                                w["bev_mask"], w["sampling_offsets"], w["attention_logits"], g)
+        else:
+            oracle.msda(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
+                        w["attention_weights"], True)
+            oracle.msda_backward(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
+                                 w["attention_weights"], g, weights_are_logits=True)
+        t = time.perf_counter() - t0
+        return {"value": wl.samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole workload, forward and backward ({wl.samples} samples), "
+                          f"single-threaded C, {t:.1f} s"}
+    wl.cpu_baseline = cpu_baseline
+    return wl
+
+
 def msda_workload(which):
     import numpy as np
     import torch
@@ -427,8 +521,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="sca", choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "detr", "tsa",
-                                                          "tiny"])
+    ap.add_argument("--workload", default="sca", choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "sca_train",
+                                                          "detr", "detr_train", "tsa", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="steps timed after a 1 GiB write that evicts the caches (0: none)")
@@ -451,6 +545,8 @@ def main():
         wl = sca_workload(args.workload)
     elif args.workload == "sca_rebatch":
         wl = rebatch_workload()
+    elif args.workload in ("sca_train", "detr_train"):
+        wl = train_workload(args.workload)
     else:
         wl = msda_workload(args.workload)
 

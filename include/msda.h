@@ -286,6 +286,51 @@ int sca_scatter_mean(const float* rows, const int32_t* pair_offsets, const int32
                      const int32_t* hit_count, int64_t B, int64_t Ncam, int64_t Nq, int64_t C, int64_t max_len,
                      float* slots, void* stream);
 
+/*
+ * Backward pass of the MSDA operator.  The pages say only that the offsets
+ * and weights are learned by back-propagation ([8-heads] 4.3); these are the
+ * derivatives of msda_forward's definition ([8-heads] 4.2, 6, 8) for the
+ * upstream gradient grad_out = d loss / d out:
+ *   grad_value              d loss / d value, float32 [B][Nv][nH][Dh] whatever
+ *                           value's type; overwritten (zeroed first)
+ *   grad_sampling_locations d loss / d sampling_locations, [B][Nq][nH][L][P][2]
+ *   grad_attention_weights  d loss / d attention_weights as given:
+ *                           probabilities (MSDA_WEIGHTS_PROB) or logits through
+ *                           each head's softmax (MSDA_WEIGHTS_LOGITS), [B][Nq][nH][L*P]
+ * At an integer continuous coordinate, where bilinear sampling has a kink,
+ * the derivative of the cell floor(x), floor(y) is used.
+ *   grad_out   device float [B][Nq][nH*Dh], 16-byte aligned
+ *   grad_value device, 16-byte aligned; one image (Nv*nH*Dh*4 bytes) < 2 GiB
+ *   the gradients of locations and weights: device float, 8- and 4-byte aligned
+ * Other arguments and limits as msda_forward.  grad_value is accumulated with
+ * float32 atomics, so its last bits vary from run to run; the other outputs
+ * are each written once.
+ */
+int msda_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                  const int64_t* level_start_index, const float* sampling_locations, const float* attention_weights,
+                  int weight_mode, const float* grad_out, int64_t B, int64_t Nv, int64_t Nq, int nH, int Dh, int L,
+                  int P, float* grad_value, float* grad_sampling_locations, float* grad_attention_weights,
+                  void* stream);
+
+/*
+ * Backward pass of spatial cross-attention (sca_gather's definition,
+ * [8-heads] 4.2, 5, 6, 8, 10), for grad_slots = d loss / d slots.  Each
+ * seeing camera's share is divided by the hit count; offsets and logits serve
+ * every camera of a query, so their gradients sum over the cameras:
+ *   grad_value    float32 [B][Ncam][Nv][nH][Dh], overwritten (zeroed first)
+ *   grad_offsets  d loss / d sampling_offsets (in cells), [B][Nq][nH][L][P][2]
+ *   grad_logits   d loss / d attention_logits, [B][Nq][nH][L*P]
+ * Queries no camera sees get zero offset and logit gradients.  The workspace
+ * must hold the result of sca_compact for the same bev_mask and
+ * reference_points_cam (as for sca_gather).  Alignment, limits and the
+ * run-to-run variation of grad_value as msda_backward.
+ */
+int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                 const int64_t* level_start_index, const float* reference_points_cam, const float* sampling_offsets,
+                 const float* attention_logits, const float* grad_slots, int64_t B, int64_t Ncam, int64_t Nv,
+                 int64_t Nq, int nH, int Dh, int L, int P, int D, float* grad_value, float* grad_offsets,
+                 float* grad_logits, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Name of a status code (host; static string). */
 const char* msda_status_string(int status);
 

@@ -63,6 +63,10 @@ def load_library():
     lib.sca_gather.argtypes = [_p, _int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _int,
                                _p, _p, _sz, _p]
     lib.msda_gemm_bf16.argtypes = [_p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p]
+    lib.msda_backward.argtypes = [_p, _int, _p, _p, _p, _p, _int, _p, _i64, _i64, _i64, _int, _int, _int, _int, _p,
+                                  _p, _p, _p]
+    lib.sca_backward.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int,
+                                 _int, _p, _p, _p, _p, _sz, _p]
     lib.sca_rebatch.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _int, _int, _int, _int, _i64, _p, _p, _p]
     lib.sca_scatter_mean.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p]
     lib.msda_query_proj_bf16.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]
@@ -376,3 +380,61 @@ def sca_forward_rebatch(value, spatial_shapes, level_start_index, reference_poin
         torch.empty((B * Ncam, 0, nH * Dh), dtype=torch.float32, device=dev)
     slots = sca_scatter_mean(rows.view(B * Ncam, max_len, nH * Dh), offs, pq, hit, Nq, stream=stream)
     return slots, max_len
+
+
+def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights, grad_out,
+                  weight_mode=MSDA_WEIGHTS_LOGITS, grad_value=None, grad_locations=None, grad_weights=None,
+                  stream=None):
+    """Gradients of msda_forward for grad_out = d loss / d out [B,Nq,nH*Dh].
+    Returns (grad_value float32 [B,Nv,nH,Dh], grad_locations [B,Nq,nH,L,P,2],
+    grad_weights [B,Nq,nH,L*P]); grad_weights is with respect to the weights
+    as given (logits or probabilities, per weight_mode)."""
+    lib = load_library()
+    B, Nv, nH, Dh = value.shape
+    _, Nq, _, L, P, _ = sampling_locations.shape
+    dev = value.device
+    if grad_value is None:
+        grad_value = torch.empty((B, Nv, nH, Dh), dtype=torch.float32, device=dev)
+    if grad_locations is None:
+        grad_locations = torch.empty_like(sampling_locations)
+    if grad_weights is None:
+        grad_weights = torch.empty_like(attention_weights)
+    rc = lib.msda_backward(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
+                           _ptr(level_start_index, "level_start_index", _I64),
+                           _ptr(sampling_locations, "sampling_locations", _F32),
+                           _ptr(attention_weights, "attention_weights", _F32), int(weight_mode),
+                           _ptr(grad_out, "grad_out", _F32), B, Nv, Nq, nH, Dh, L, P,
+                           _ptr(grad_value, "grad_value", _F32), _ptr(grad_locations, "grad_locations", _F32),
+                           _ptr(grad_weights, "grad_weights", _F32), _stream(stream, dev))
+    _check("msda_backward", rc)
+    return grad_value, grad_locations, grad_weights
+
+
+def sca_backward(value, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets, attention_logits,
+                 grad_slots, workspace, grad_value=None, grad_offsets=None, grad_logits=None, stream=None):
+    """Gradients of SCA for grad_slots = d loss / d slots [B,Nq,nH*Dh].  The
+    workspace must hold sca_compact's result for the same mask and anchors.
+    Returns (grad_value float32 [B,Ncam,Nv,nH,Dh], grad_offsets
+    [B,Nq,nH,L,P,2], grad_logits [B,Nq,nH,L*P])."""
+    lib = load_library()
+    B, Ncam, Nv, nH, Dh = value.shape
+    _, _, Nq, D, _ = reference_points_cam.shape
+    _, _, _, L, P, _ = sampling_offsets.shape
+    dev = value.device
+    if grad_value is None:
+        grad_value = torch.empty((B, Ncam, Nv, nH, Dh), dtype=torch.float32, device=dev)
+    if grad_offsets is None:
+        grad_offsets = torch.empty_like(sampling_offsets)
+    if grad_logits is None:
+        grad_logits = torch.empty_like(attention_logits)
+    rc = lib.sca_backward(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
+                          _ptr(level_start_index, "level_start_index", _I64),
+                          _ptr(reference_points_cam, "reference_points_cam", _F32),
+                          _ptr(sampling_offsets, "sampling_offsets", _F32),
+                          _ptr(attention_logits, "attention_logits", _F32), _ptr(grad_slots, "grad_slots", _F32),
+                          B, Ncam, Nv, Nq, nH, Dh, L, P, D, _ptr(grad_value, "grad_value", _F32),
+                          _ptr(grad_offsets, "grad_offsets", _F32), _ptr(grad_logits, "grad_logits", _F32),
+                          _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                          _stream(stream, dev))
+    _check("sca_backward", rc)
+    return grad_value, grad_offsets, grad_logits

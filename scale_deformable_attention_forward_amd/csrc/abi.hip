@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 
+#include "backward.hpp"
 #include "gemm.hpp"
 #include "internal.hpp"
 #include "rebatch.hpp"
@@ -406,6 +407,123 @@ int sca_scatter_mean(const float* rows, const int32_t* pair_offsets, const int32
   g_last_error[0] = '\0';
   msda::ScatterArgs a = {rows, pair_offsets, pair_q, hit_count, B, Ncam, Nq, C, max_len, slots};
   return hip_status(msda::launch_sca_scatter_mean(a, static_cast<hipStream_t>(stream)), "scatter launch");
+}
+
+// Checks of the gradient image shared by the backward entry points: float32
+// [images][Nv][nH][Dh], each image addressed through one descriptor.
+static int check_grad_value(const float* grad_value, int64_t Nv, int nH, int Dh, uint32_t* grad_image_bytes) {
+  if (!grad_value) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  const int64_t bytes = Nv * nH * Dh * 4;
+  if (bytes >= kI31) return fail(MSDA_ERR_UNSUPPORTED, "one gradient image is %lld bytes; the limit is 2^31",
+                                 (long long)bytes);
+  if (!aligned(grad_value, 16)) return fail(MSDA_ERR_INVALID_ARG, "grad_value must be 16-byte aligned");
+  *grad_image_bytes = (uint32_t)bytes;
+  return MSDA_OK;
+}
+
+int msda_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                  const int64_t* level_start_index, const float* sampling_locations, const float* attention_weights,
+                  int weight_mode, const float* grad_out, int64_t B, int64_t Nv, int64_t Nq, int nH, int Dh, int L,
+                  int P, float* grad_value, float* grad_sampling_locations, float* grad_attention_weights,
+                  void* stream) {
+  uint32_t image_bytes = 0, grad_bytes = 0;
+  int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, grad_out,
+                        &image_bytes);
+  if (rc != MSDA_OK) return rc;
+  if (B < 1) return fail(MSDA_ERR_INVALID_ARG, "B must be positive");
+  rc = check_grad_value(grad_value, Nv, nH, Dh, &grad_bytes);
+  if (rc != MSDA_OK) return rc;
+  if (Nq != 0 && (!sampling_locations || !attention_weights || !grad_sampling_locations || !grad_attention_weights))
+    return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (weight_mode != MSDA_WEIGHTS_PROB && weight_mode != MSDA_WEIGHTS_LOGITS)
+    return fail(MSDA_ERR_INVALID_ARG, "weight_mode %d is neither PROB nor LOGITS", weight_mode);
+  if (Nq != 0 && (!aligned(sampling_locations, 8) || !aligned(grad_sampling_locations, 8) ||
+                  !aligned(attention_weights, 4) || !aligned(grad_attention_weights, 4)))
+    return fail(MSDA_ERR_INVALID_ARG, "(x, y) arrays must be 8-byte aligned");
+  if (B >= kI31 || B * Nq >= kI31 || B * Nq * nH >= kI31 / 64) return fail(MSDA_ERR_UNSUPPORTED, "B*Nq*nH too large");
+  g_last_error[0] = '\0';
+  msda::BackwardArgs a = {};
+  a.value = value;
+  a.image_bytes = image_bytes;
+  a.bf16 = value_dtype == MSDA_BF16;
+  a.grad_value = grad_value;
+  a.grad_image_bytes = grad_bytes;
+  a.images = B;
+  a.shapes = spatial_shapes;
+  a.starts = level_start_index;
+  a.L = L;
+  a.P = P;
+  a.LP = L * P;
+  a.nH = nH;
+  a.Nv = (int)Nv;
+  a.inv_P = 1.0f / (float)P;
+  a.inv_D = 1.0f;
+  a.B = B;
+  a.Nq = Nq;
+  a.grad_out = grad_out;
+  a.loc = sampling_locations;
+  a.weights = attention_weights;
+  a.weight_logits = weight_mode == MSDA_WEIGHTS_LOGITS;
+  a.grad_loc = grad_sampling_locations;
+  a.grad_weights = grad_attention_weights;
+  return hip_status(msda::launch_msda_backward(a, static_cast<hipStream_t>(stream)), "msda backward launch");
+}
+
+int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                 const int64_t* level_start_index, const float* reference_points_cam, const float* sampling_offsets,
+                 const float* attention_logits, const float* grad_slots, int64_t B, int64_t Ncam, int64_t Nv,
+                 int64_t Nq, int nH, int Dh, int L, int P, int D, float* grad_value, float* grad_offsets,
+                 float* grad_logits, void* workspace, size_t workspace_bytes, void* stream) {
+  uint32_t image_bytes = 0, grad_bytes = 0;
+  int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, grad_slots,
+                        &image_bytes);
+  if (rc != MSDA_OK) return rc;
+  if (B < 1 || Ncam < 1 || D < 1) return fail(MSDA_ERR_INVALID_ARG, "B, Ncam and D must be positive");
+  rc = check_grad_value(grad_value, Nv, nH, Dh, &grad_bytes);
+  if (rc != MSDA_OK) return rc;
+  if (Nq != 0 && (!reference_points_cam || !sampling_offsets || !attention_logits || !grad_offsets || !grad_logits))
+    return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (Ncam > 32) return fail(MSDA_ERR_UNSUPPORTED, "Ncam=%lld: at most 32 cameras", (long long)Ncam);
+  if (P % D != 0) return fail(MSDA_ERR_SHAPE, "P=%d is not a multiple of D=%d", P, D);
+  if (Nq != 0 && (!aligned(reference_points_cam, 8) || !aligned(sampling_offsets, 8) || !aligned(grad_offsets, 8) ||
+                  !aligned(grad_logits, 4)))
+    return fail(MSDA_ERR_INVALID_ARG, "(x, y) arrays must be 8-byte aligned");
+  if (B * Ncam >= kI31 || B * Nq * nH >= kI31 / 64) return fail(MSDA_ERR_UNSUPPORTED, "B*Nq*nH too large");
+  rc = check_workspace(B, Ncam, Nq, workspace, workspace_bytes);
+  if (rc != MSDA_OK) return rc;
+  g_last_error[0] = '\0';
+  const msda::CompactArgs c = compact_args(nullptr, nullptr, B, Ncam, Nq, D, nullptr, nullptr, nullptr, workspace);
+  msda::BackwardArgs a = {};
+  a.value = value;
+  a.image_bytes = image_bytes;
+  a.bf16 = value_dtype == MSDA_BF16;
+  a.grad_value = grad_value;
+  a.grad_image_bytes = grad_bytes;
+  a.images = B * Ncam;
+  a.shapes = spatial_shapes;
+  a.starts = level_start_index;
+  a.L = L;
+  a.P = P;
+  a.LP = L * P;
+  a.nH = nH;
+  a.Nv = (int)Nv;
+  a.inv_P = 1.0f / (float)P;
+  a.inv_D = 1.0f / (float)D;
+  a.B = B;
+  a.Nq = Nq;
+  a.grad_out = grad_slots;
+  a.rp = reference_points_cam;
+  a.offsets = sampling_offsets;
+  a.logits = attention_logits;
+  a.cammask = c.cammask;
+  a.order = c.order;
+  a.order_at = c.bin_offsets;
+  a.order_stride = (int)Ncam * msda::kOrderBins;
+  a.Ncam = (int)Ncam;
+  a.D = D;
+  a.grad_offsets = grad_offsets;
+  a.grad_logits = grad_logits;
+  return hip_status(msda::launch_sca_backward(a, static_cast<hipStream_t>(stream)), "sca backward launch");
 }
 
 }  // extern "C"

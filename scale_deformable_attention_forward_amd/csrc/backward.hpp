@@ -1,0 +1,47 @@
+// Launcher interface of the backward pass (backward.hip).  Arguments are
+// validated by the caller (abi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msda {
+
+struct BackwardArgs {
+  // value images (image i starts at value + i * image_bytes) and their
+  // gradient (float32, image i starts at grad_value + i * grad_image_bytes)
+  const void* value;
+  uint32_t image_bytes;
+  int bf16;
+  float* grad_value;
+  uint32_t grad_image_bytes;
+  int64_t images;  // number of images (B for MSDA, B * Ncam for SCA)
+  const int64_t* shapes;
+  const int64_t* starts;
+  int L, P, LP, nH, Nv;
+  float inv_P, inv_D;
+  int64_t B, Nq;
+  const float* grad_out;  // [B][Nq][nH*32]
+  // MSDA: weights and locations per (b, q); outputs per (b, q)
+  const float* loc;
+  const float* weights;
+  int weight_logits;
+  float* grad_loc;      // [B][Nq][nH][L][P][2]
+  float* grad_weights;  // [B][Nq][nH][L*P]
+  // SCA: anchors, offsets, logits, the compaction's camera masks and work list
+  const float* rp;
+  const float* offsets;
+  const float* logits;
+  const uint32_t* cammask;
+  const int32_t* order;
+  const int32_t* order_at;
+  int order_stride;
+  int Ncam, D;
+  float* grad_offsets;  // [B][Nq][nH][L][P][2]
+  float* grad_logits;   // [B][Nq][nH][L*P]
+};
+
+hipError_t launch_msda_backward(const BackwardArgs& a, hipStream_t stream);
+hipError_t launch_sca_backward(const BackwardArgs& a, hipStream_t stream);
+
+}  // namespace msda

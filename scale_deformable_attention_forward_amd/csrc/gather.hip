@@ -35,70 +35,17 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "sampling.hpp"
 
 namespace msda {
 
-constexpr int kHeadSlots = 8;  // heads per wave pass
-constexpr int kBatch = 8;      // corner rows per load batch
+constexpr int kBatch = 8;  // corner rows per load batch
 constexpr int kMaxWavesPerBlock = 4;
-constexpr size_t kMaxBlockLds = 64 * 1024;
-constexpr int kMaxLevels = 64;
-constexpr uint32_t kSkip = 0x80000000u;  // beyond every image (images < 2^31 bytes)
-// samples per lane (template kSPL): 4 when L*P <= 32, 8 when L*P <= 64
-
-struct Level {
-  int W, H;
-  long long start;
-};
 
 __host__ __device__ inline int rows_padded(int LP) { return (4 * LP + kBatch - 1) / kBatch * kBatch; }
 // per-head stride of the LDS staging area, in (offset, weight) pairs; odd, so
 // that the 8 groups of a wave hit different LDS banks
 __host__ __device__ inline int meta_stride(int LP) { return rows_padded(LP) + 1; }
-
-// k / n for 0 <= k < 2^16 and 1 <= n <= 64, with inv = 1/n in fp32: the
-// quotient sits at least 0.5/n away from the next integer, far beyond the
-// rounding error of (k + 1/2) * inv.
-__device__ inline int small_div(int k, float inv) { return (int)((k + 0.5f) * inv); }
-
-__device__ inline float group_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, 8));
-  v = fmaxf(v, __shfl_xor(v, 2, 8));
-  return fmaxf(v, __shfl_xor(v, 4, 8));
-}
-__device__ inline float group_sum(float v) {
-  v += __shfl_xor(v, 1, 8);
-  v += __shfl_xor(v, 2, 8);
-  return v + __shfl_xor(v, 4, 8);
-}
-
-// Weights of the samples k = j + 8i of one head: probabilities as given, or
-// softmax over the head's L*P logits, reduced across the 8 lanes of a group.
-template <int kSPL>
-__device__ inline void head_weights(const float* __restrict__ w_row, bool head_ok, int LP, int j, bool logits,
-                                    float (&alpha)[kSPL]) {
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kSPL; ++i) {
-    const int k = j + 8 * i;
-    alpha[i] = (head_ok && k < LP) ? w_row[k] : 0.f;
-    if (head_ok && k < LP) m = fmaxf(m, alpha[i]);
-  }
-  if (!logits) return;
-  m = group_max(m);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < kSPL; ++i) {
-    const int k = j + 8 * i;
-    const float e = (head_ok && k < LP) ? expf(alpha[i] - m) : 0.f;
-    alpha[i] = e;
-    s += e;
-  }
-  s = group_sum(s);
-  const float inv = head_ok ? 1.0f / s : 0.f;
-#pragma unroll
-  for (int i = 0; i < kSPL; ++i) alpha[i] *= inv;
-}
 
 // The four corners of one sample at continuous level coordinate (x, y):
 // (row offset in bytes within the image, alpha * bilinear weight), with
@@ -127,13 +74,6 @@ __device__ inline void sample_corners(uint2 (&c)[4], double x, double y, float a
                           : make_uint2(kSkip, 0u);
     }
   }
-}
-
-// A sample is live when at least one of its corners can lie inside the map:
-// -1 <= x < W and -1 <= y < H (a live sample may still contribute nothing;
-// a dead one never does).
-__device__ inline bool sample_live(double x, double y, const Level& lv) {
-  return x >= -1.0 && x < (double)lv.W && y >= -1.0 && y < (double)lv.H;
 }
 
 // Write the four corner rows of the group's live samples densely into `rows`
@@ -217,19 +157,6 @@ __device__ inline void gather_rows(const uint2* __restrict__ rows, int R, __amdg
   }
 }
 
-__device__ inline void load_levels(const GatherArgs& a, Level* lv) {
-  for (int l = threadIdx.x; l < a.L; l += blockDim.x) {
-    const long long H = a.shapes[2 * l], W = a.shapes[2 * l + 1], s = a.starts[l];
-    Level v;
-    const bool ok = H >= 1 && W >= 1 && H <= (1 << 30) && W <= (1 << 30);
-    v.W = ok ? (int)W : 0;  // an unusable level samples nothing
-    v.H = ok ? (int)H : 0;
-    v.start = s < -(1ll << 40) ? -(1ll << 40) : (s > (1ll << 40) ? (1ll << 40) : s);
-    lv[l] = v;
-  }
-  __syncthreads();
-}
-
 __device__ inline float4 scaled(float4 v, int n) {
   if (n <= 1) return v;
   const float f = (float)n;
@@ -243,7 +170,7 @@ template <bool kBF16, int kSPL>
 __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(GatherArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Level* lv = reinterpret_cast<Level*>(smem);
-  load_levels(a, lv);
+  load_levels(a.shapes, a.starts, a.L, lv);
   const int waves_per_block = blockDim.x / kWave;
   const int lane = threadIdx.x % kWave, wave = uniform((int)(threadIdx.x / kWave));
   const int g = lane / 8, j = lane % 8;
@@ -299,7 +226,7 @@ template <bool kBF16, int kSPL>
 __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void sca_gather_kernel(GatherArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Level* lv = reinterpret_cast<Level*>(smem);
-  load_levels(a, lv);
+  load_levels(a.shapes, a.starts, a.L, lv);
   const int waves_per_block = blockDim.x / kWave;
   const int lane = threadIdx.x % kWave, wave = uniform((int)(threadIdx.x / kWave));
   const int g = lane / 8, j = lane % 8;

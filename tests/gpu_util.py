@@ -8,7 +8,17 @@ Tolerances (written out here, used by every GPU test):
   bf16 projection output: |gpu - oracle| <= 2^-7 * |oracle| + 1e-5 (one bf16
               unit in the last place: fp32 accumulation may move a value
               across a rounding boundary of the final bf16 rounding);
-  integers (hit counts, pair lists): bit-exact.
+  integers (hit counts, pair lists): bit-exact;
+  scatter-accumulated sums (value gradients, summed with float32 atomics
+              in no fixed order over up to ~10^3 contributions per element):
+              |gpu - oracle| <= 1e-5 * (m + rms(m)), m = the element's sum of
+              its contributions' magnitudes.  Float32 summation error is
+              relative to what is summed, not to the possibly cancelled total;
+              the rms term plays the part it plays in the fp32 bar: each
+              contribution alpha * w * g carries an absolute error of about
+              3e-8 * alpha * |g| from the float32 interpolation weight, so an
+              element fed only by a few small-weight corners cannot meet a
+              bound relative to its own small sum.
 """
 import sys
 
@@ -74,3 +84,23 @@ def assert_bf16_ulp_close(got_bits, ref, what):
     tol = 2.0 ** -7 * np.abs(ref) + 1e-5
     bad = err > tol
     assert not bad.any(), f"{what}: {int(bad.sum())}/{bad.size} beyond one bf16 ulp; max err {err.max():.3g}"
+
+
+def assert_sum_close(got, ref, abs_sum, what):
+    """Scatter-accumulated sums: |got - ref| <= 1e-5 * (abs_sum + rms(abs_sum))
+    element-wise, abs_sum = the sum of the magnitudes of each element's
+    contributions; elements with no contribution must be exactly zero."""
+    got = np.asarray(got, np.float64).reshape(-1)
+    ref = np.asarray(ref, np.float64).reshape(-1)
+    abs_sum = np.asarray(abs_sum, np.float64).reshape(-1)
+    assert got.shape == ref.shape == abs_sum.shape, (what, got.shape, ref.shape, abs_sum.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    assert not got[abs_sum == 0].any(), f"{what}: nonzero where nothing contributes"
+    rms = float(np.sqrt(np.mean(abs_sum ** 2))) if abs_sum.size else 0.0
+    tol = 1e-5 * (abs_sum + rms)
+    bad = err > tol
+    worst = float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
+    assert not bad.any(), (f"{what}: {int(bad.sum())}/{bad.size} elements beyond the bar (worst err/tol "
+                           f"{worst:.3g}; rms of the magnitudes {rms:.3g})")
+    return worst

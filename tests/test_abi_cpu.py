@@ -40,6 +40,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["msda_forward", "msda_forward_frames", "sca_workspace_size", "sca_forward", "msda_gemm_bf16",
               "msda_query_proj_bf16", "msda_output_proj_bf16", "sca_rebatch", "sca_scatter_mean",
+              "msda_backward", "sca_backward",
               "msda_status_string", "msda_last_error"]:
         assert n in names, n
 
@@ -246,6 +247,38 @@ def _sm(lib, rows=A, po=A, pq=A, hit=A, B=1, Ncam=6, Nq=16, C=256, ml=8, slots=B
 ])
 def test_scatter_mean_rejects(lib, kw, code):
     assert _sm(lib, **kw) == code
+
+
+def _mb(lib, value=A, dtype=0, ss=A, st=A, loc=A, w=A, mode=1, go=A, B=1, Nv=16, Nq=4, nH=8, Dh=32, L=1, P=4,
+        gv=B_, gl=B_, gw=B_):
+    return lib.msda_backward(value, dtype, ss, st, loc, w, mode, go, B, Nv, Nq, nH, Dh, L, P, gv, gl, gw, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gv=None), INVALID),
+    (dict(go=None), INVALID),
+    (dict(gl=None), INVALID),
+    (dict(mode=7), INVALID),
+    (dict(B=0), INVALID),
+    (dict(Dh=16), UNSUPPORTED),
+    (dict(gv=MIS), INVALID),
+    (dict(gl=A + 4), INVALID),
+    (dict(Nv=1 << 21, dtype=1), UNSUPPORTED),  # bf16 value fits, its float32 gradient image does not
+])
+def test_msda_backward_rejects(lib, kw, code):
+    assert _mb(lib, **kw) == code
+
+
+def test_sca_backward_rejects(lib):
+    n = _sz(0)
+    assert lib.sca_workspace_size(1, 6, 16, ctypes.byref(n)) == OK
+    b = lib.sca_backward
+    args = [A, 0, A, A, A, A, A, A, 1, 6, 16, 8, 8, 32, 1, 8, 4, B_, B_, B_, A, n.value, None]
+    assert b(*args[:17], None, *args[18:]) == INVALID                 # grad_value
+    assert b(*args[:16], 6, *args[17:]) == SHAPE                      # P % D
+    assert b(*args[:20], None, *args[21:]) == WORKSPACE               # workspace
+    assert b(*args[:9], 33, *args[10:]) == UNSUPPORTED                # cameras
+    assert b(*args[:7], None, *args[8:]) == INVALID                   # grad_slots
 
 
 def test_binding_refuses_cpu_tensors():

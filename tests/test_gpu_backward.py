@@ -1,0 +1,162 @@
+"""Backward pass of the MSDA operator and of SCA against the oracle's
+gradients, element by element, on the same seeded inputs (workloads at full
+size and the forward tests' edge cases).  Every call goes through the C ABI
+(via the ctypes binding).
+
+Tolerance: the float32 bar of the forward tests (1e-5 relative plus 1e-5 of
+the output's rms) for the location / offset and weight / logit gradients.
+The value gradient sums each row's contributions from every sample that
+touches it (up to ~10^3 in workload 3's coarse levels) with float32 atomics
+in no fixed order, so its bar is 1e-5 of the sum of the contributions'
+magnitudes plus 1e-5 of that sum's rms over the elements (gpu_util explains
+the rms term); the oracle gives the sum exactly: contributions are
+alpha * w * g with alpha, w >= 0, so the oracle's value gradient for |g| is
+that sum."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import announce, assert_fp32_close, assert_sum_close, dev, host
+from test_gpu_parity import MSDA_EDGE, SCA_EDGE, _rand_msda, _rand_sca
+
+pytestmark = pytest.mark.gpu
+
+msda = pytest.importorskip("scale_deformable_attention_forward_amd")
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    announce(request.node.nodeid)
+    yield
+    torch.cuda.synchronize()
+
+
+def _grad_out(seed, B, Nq, C):
+    return np.random.default_rng(seed).normal(size=(B, Nq, C)).astype(np.float32)
+
+
+def check_msda_backward(w, gout, logits, what):
+    mode = msda.MSDA_WEIGHTS_LOGITS if logits else msda.MSDA_WEIGHTS_PROB
+    gv, gl, gw = msda.msda_backward(dev(w["value"]), dev(w["spatial_shapes"]), dev(w["level_start_index"]),
+                                    dev(w["sampling_locations"]), dev(w["attention_weights"]), dev(gout),
+                                    weight_mode=mode)
+    rv, rl, rw = oracle.msda_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
+                                      w["sampling_locations"], w["attention_weights"], gout, weights_are_logits=logits)
+    mag, _, _ = oracle.msda_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
+                                     w["sampling_locations"], w["attention_weights"], np.abs(gout),
+                                     weights_are_logits=logits)
+    if not logits:  # probabilities may be negative: the magnitude needs |alpha|
+        mag, _, _ = oracle.msda_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
+                                         w["sampling_locations"], np.abs(w["attention_weights"]), np.abs(gout),
+                                         weights_are_logits=False)
+    assert_sum_close(host(gv), rv, mag, what + ": grad value")
+    assert_fp32_close(host(gl), rl, what + ": grad locations")
+    assert_fp32_close(host(gw), rw, what + ": grad weights")
+
+
+def test_tiny_msda_backward_all_modes():
+    w = W.tiny_msda()
+    gout = _grad_out(1, w["B"], w["Nq"], 256)
+    check_msda_backward(w, gout, True, "logits")
+    probs = np.random.default_rng(2).uniform(0, 0.2, w["attention_weights"].shape).astype(np.float32)
+    check_msda_backward(dict(w, attention_weights=probs), gout, False, "probabilities")
+    wb = dict(w, value=W.bf16_bits_trunc(w["value"]))
+    check_msda_backward(wb, gout, True, "bf16 value")
+
+
+def test_detr_encoder_msda_backward_full():
+    """Workload 2 at full size: all 19947 queries, 4 levels."""
+    w = W.detr_encoder_msda()
+    gout = W.upstream_gradient(2, (w["B"], w["Nq"], 256))
+    check_msda_backward(w, gout, True, "DETR encoder")
+
+
+@pytest.mark.parametrize("case", MSDA_EDGE, ids=[c[0] for c in MSDA_EDGE])
+def test_msda_backward_edge_cases(case):
+    _, seed, B, Nq, shapes, nH, P = case
+    w = _rand_msda(seed, B, Nq, shapes, nH, P)
+    gout = _grad_out(seed + 100, B, Nq, nH * 32)
+    check_msda_backward(w, gout, True, case[0])
+    probs = np.abs(w["attention_weights"]) / 8
+    check_msda_backward(dict(w, attention_weights=probs), gout, False, case[0] + " probabilities")
+
+
+def test_msda_backward_empty_query_set():
+    """No queries: the value gradient is zero (overwritten), nothing else is touched."""
+    w = _rand_msda(5, 1, 0, ((4, 4),), 8, 4)
+    gv = torch.full((1, w["Nv"], 8, 32), float("nan"), device="cuda")
+    empty = torch.empty(0, device="cuda")
+    gv, _, _ = msda.msda_backward(dev(w["value"]), dev(w["spatial_shapes"]), dev(w["level_start_index"]),
+                                  dev(w["sampling_locations"]), dev(w["attention_weights"]), empty.view(1, 0, 256),
+                                  grad_value=gv)
+    assert not host(gv).any()
+
+
+def test_msda_backward_repeatable():
+    """Locations and weights gradients are written once each: bitwise equal
+    over two runs; the atomically accumulated value gradient agrees to the
+    float32 bar."""
+    w = _rand_msda(6, 2, 300, ((16, 24), (8, 12)), 8, 4)
+    gout = _grad_out(7, 2, 300, 256)
+    args = (dev(w["value"]), dev(w["spatial_shapes"]), dev(w["level_start_index"]), dev(w["sampling_locations"]),
+            dev(w["attention_weights"]), dev(gout))
+    a = [host(t) for t in msda.msda_backward(*args)]
+    b = [host(t) for t in msda.msda_backward(*args)]
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+    mag, _, _ = oracle.msda_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
+                                     w["sampling_locations"], w["attention_weights"], np.abs(gout),
+                                     weights_are_logits=True)
+    assert_sum_close(a[0], b[0], 2 * mag, "value gradient, two runs")
+
+
+# ---------------------------------------------------------------------------
+# SCA
+# ---------------------------------------------------------------------------
+
+def run_sca_backward(w, gout):
+    B, Ncam, Nq = w["B"], w["Ncam"], w["Nq"]
+    ws = torch.empty(msda.sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device="cuda")
+    msda.sca_compact(dev(w["bev_mask"]), dev(w["reference_points_cam"]), ws)
+    go = torch.full((B, Nq, w["nH"], w["L"], w["P"], 2), float("nan"), device="cuda")
+    gl = torch.full((B, Nq, w["nH"], w["L"] * w["P"]), float("nan"), device="cuda")
+    gv, go, gl = msda.sca_backward(dev(w["value"]), dev(w["spatial_shapes"]), dev(w["level_start_index"]),
+                                   dev(w["reference_points_cam"]), dev(w["sampling_offsets"]),
+                                   dev(w["attention_logits"]), dev(gout), ws, grad_offsets=go, grad_logits=gl)
+    return host(gv), host(go), host(gl)
+
+
+def check_sca_backward(w, gout, what):
+    gv, go, gl = run_sca_backward(w, gout)
+    rv, ro, rl = oracle.sca_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
+                                     w["reference_points_cam"], w["bev_mask"], w["sampling_offsets"],
+                                     w["attention_logits"], gout)
+    mag, _, _ = oracle.sca_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
+                                    w["reference_points_cam"], w["bev_mask"], w["sampling_offsets"],
+                                    w["attention_logits"], np.abs(gout))
+    assert_sum_close(gv, rv, mag, what + ": grad value")
+    assert_fp32_close(go, ro, what + ": grad offsets")
+    assert_fp32_close(gl, rl, what + ": grad logits")
+
+
+def test_bevformer_sca_backward_full():
+    """Workload 3 at full size: 40000 queries, 6 cameras."""
+    w = W.bevformer_sca()
+    gout = W.upstream_gradient(3, (w["B"], w["Nq"], 256))
+    check_sca_backward(w, gout, "workload 3")
+
+
+def test_bevformer_sca_backward_bf16_value():
+    """Workload 3's shapes with a bf16 value map, batch 2 at 100x100 queries."""
+    w = W.bevformer_sca(cfg=33, B=2, bev=100, value_bf16=True)
+    gout = W.upstream_gradient(33, (w["B"], w["Nq"], 256))
+    check_sca_backward(w, gout, "bf16 value")
+
+
+@pytest.mark.parametrize("case", SCA_EDGE, ids=[c[0] for c in SCA_EDGE])
+def test_sca_backward_edge_cases(case):
+    _, seed, B, Ncam, Nq, shapes, nH, P, D, pm = case
+    w = _rand_sca(seed, B, Ncam, Nq, shapes, nH, P, D, pm)
+    gout = _grad_out(seed + 200, B, Nq, nH * 32)
+    check_sca_backward(w, gout, case[0])
