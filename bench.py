@@ -52,9 +52,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
-GATHER_SOURCES = ["scale_deformable_attention_forward_amd/csrc/gather.hip",
-                  "scale_deformable_attention_forward_amd/csrc/common.hpp",
-                  "scale_deformable_attention_forward_amd/csrc/internal.hpp"]
+_CSRC = "scale_deformable_attention_forward_amd/csrc/"
+GATHER_SOURCES = [_CSRC + f for f in ("gather.hip", "sampling.hpp", "common.hpp", "internal.hpp")]
+BACKWARD_SOURCES = [_CSRC + f for f in ("backward.hip", "backward.hpp", "sampling.hpp", "common.hpp")]
+KERNEL_SOURCES = {"sca_gather_kernel": GATHER_SOURCES, "msda_gather_kernel": GATHER_SOURCES,
+                  "sca_backward_kernel": BACKWARD_SOURCES, "msda_backward_kernel": BACKWARD_SOURCES}
 METRIC = "MSDA samples/sec + effective HBM GB/s, BEVFormer-base SCA layer (6 cams)"
 
 
@@ -66,18 +68,19 @@ def source_digest(paths=GATHER_SOURCES):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """Bytes per gather launch moved between L2 and memory (FETCH_SIZE +
-    WRITE_SIZE, calibrated on a plain copy) from the committed rocprofv3
-    counter runs for this workload, or None when there is none or the gather
-    sources changed since it was taken.  Reads served by the memory-side
-    Infinity Cache count too, so this bounds the HBM bytes from above."""
+def measured_traffic(workload, kernel):
+    """Bytes per launch of the workload's main kernel moved between L2 and
+    memory (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy) from the
+    committed rocprofv3 counter runs, or None when there is none or the
+    kernel's sources changed since it was taken.  Reads served by the
+    memory-side Infinity Cache count too, so this bounds the HBM bytes from
+    above."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)[workload]
     except (OSError, KeyError, ValueError):
         return None
-    if c.get("source_digest") != source_digest():
+    if c.get("source_digest") != source_digest(KERNEL_SOURCES.get(kernel, GATHER_SOURCES)):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -626,7 +629,7 @@ def main():
         "data": "synthetic (seeded, BEVFormer-shaped; no dataset or trained weights)",
         "config": wl.config,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, wl.kernel_key.rsplit("_", 1)[0]),
                      "kernel": wl.kernel_key.rsplit("_", 1)[0], "kernel_ms": kernel_ms,
                      "effective_bytes_per_launch": wl.eff_bytes, "gathered_bytes_per_launch": wl.gathered_bytes},
         "effective_GBps_per_step": wl.eff_bytes / (ms_per_step * 1e-3) / 1e9,
