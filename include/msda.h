@@ -1,7 +1,14 @@
 /*
  * msda.h -- C ABI of libmsda.so: multi-scale deformable attention (MSDA) and
- * BEVFormer spatial cross-attention (SCA), forward pass, on AMD Instinct
- * MI355X (gfx950).
+ * BEVFormer spatial cross-attention (SCA) on AMD Instinct MI355X (gfx950):
+ *   msda_forward, msda_forward_frames        the MSDA operator (and a mean over frames)
+ *   sca_workspace_size, sca_compact,
+ *   sca_gather, sca_forward                  SCA: visibility, compaction, sampling, camera mean
+ *   msda_gemm_bf16, msda_query_proj_bf16,
+ *   msda_output_proj_bf16                    the layer's bf16 projections on matrix cores
+ *   sca_rebatch, sca_scatter_mean            the padded rebatch form of SCA (an A/B baseline)
+ *   msda_backward, sca_backward              gradients of the MSDA operator and of SCA
+ *   msda_status_string, msda_last_error      status reporting
  *
  * Sources, cited by page title and section:
  *   [8-heads]  "BEV(三) BEVFormer：Query 参数如何与 Feature 的 8 个 Head 交互"
@@ -24,8 +31,9 @@
  *    reports a failed launch (the stream may then hold part of the work).
  *    msda_status_string() names a code; msda_last_error() gives the message
  *    of the calling thread's last failure.
- *  - With Nq = 0 nothing is enqueued and the per-query buffers (locations,
- *    weights, offsets, logits, masks, anchors, outputs) may be NULL.
+ *  - With Nq = 0 nothing is enqueued (the backward entry points still zero
+ *    their value gradient) and the per-query buffers (locations, weights,
+ *    offsets, logits, masks, anchors, outputs) may be NULL.
  *  - Floating-point inputs must be finite.  Sample locations may lie
  *    anywhere (outside the map they read zeros).
  *  - Shared limits: head width Dh = 32; L*P <= 64 sampling points per head;
