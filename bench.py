@@ -14,11 +14,11 @@ projection GEMM -> SCA on bf16 value -> bf16 output projection GEMM),
 "layer_full" (the same with the sampling offsets and logits projected from
 query + position embedding in one launch, and the output projection
 followed by the residual and the layer norm), "sca_bf16", "sca_rebatch"
-(workload 3 through the padded rebatch flow of the SCA note, an A/B
-baseline: per-camera segments padded to the longest, the operator over all
-of them, scatter-add and divide), "sca_train" and "detr_train" (forward and
-backward of workload 3's SCA and of the DETR encoder MSDA; the roofline
-then describes the backward kernel), "detr" (Deformable-DETR encoder MSDA),
+(the default workload through the padded rebatch flow of the SCA note, an
+A/B baseline: per-camera segments padded to the longest, the operator over
+all of them, scatter-add and divide), "sca_train" and "detr_train" (forward
+and backward of the default SCA layer and of the DETR encoder MSDA; the
+roofline then describes the backward kernel), "detr" (Deformable-DETR encoder MSDA),
 "tsa" (two stacked BEV maps, frame mean), "tiny".
 
 Prints one JSON line.  value = bilinear samples per second (one sample = one
@@ -289,9 +289,10 @@ def sca_workload(kind):
 
 
 def rebatch_workload():
-    """Workload 3 through the padded rebatch flow (A/B baseline): compaction,
-    the longest segment read back to the host, rebatch, the MSDA operator over
-    B*Ncam padded segments, scatter-add per camera and divide."""
+    """The BEVFormer-base SCA workload through the padded rebatch flow (A/B
+    baseline): compaction, the longest segment read back to the host,
+    rebatch, the MSDA operator over B*Ncam padded segments, scatter-add per
+    camera and divide."""
     import numpy as np
     import torch
     import workloads as W
@@ -370,9 +371,10 @@ def rebatch_workload():
 
 
 def train_workload(which):
-    """Forward and backward of one step: "sca_train" (workload 3: compaction,
-    SCA forward, SCA backward) or "detr_train" (workload 2: MSDA forward and
-    backward).  The upstream gradient is seeded N(0, 1)."""
+    """Forward and backward of one step: "sca_train" (the BEVFormer-base SCA
+    workload: compaction, SCA forward, SCA backward) or "detr_train" (the
+    DETR-encoder workload: MSDA forward and backward).  The upstream gradient
+    is seeded N(0, 1)."""
     import torch
     import workloads as W
     import scale_deformable_attention_forward_amd as m
@@ -524,8 +526,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="sca", choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "sca_train",
-                                                          "detr", "detr_train", "tsa", "tiny"])
+    ap.add_argument("--workload", default="sca",
+                    choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "sca_train", "detr",
+                             "detr_train", "tsa", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="steps timed after a 1 GiB write that evicts the caches (0: none)")
@@ -533,7 +536,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
@@ -629,7 +632,8 @@ def main():
         "data": "synthetic (seeded, BEVFormer-shaped; no dataset or trained weights)",
         "config": wl.config,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, wl.kernel_key.rsplit("_", 1)[0]),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(wl.name, wl.kernel_key.rsplit("_", 1)[0]),
                      "kernel": wl.kernel_key.rsplit("_", 1)[0], "kernel_ms": kernel_ms,
                      "effective_bytes_per_launch": wl.eff_bytes, "gathered_bytes_per_launch": wl.gathered_bytes},
         "effective_GBps_per_step": wl.eff_bytes / (ms_per_step * 1e-3) / 1e9,

@@ -632,7 +632,8 @@ def pin_msda_backward():
             up, dn = loc.copy().reshape(-1), loc.copy().reshape(-1)
             up[i] += _STEP
             dn[i] -= _STEP
-            fd[i] = (_loss(gout, fwd(lc=up.reshape(loc.shape))) - _loss(gout, fwd(lc=dn.reshape(loc.shape)))) / (2 * _STEP)
+            fd[i] = (_loss(gout, fwd(lc=up.reshape(loc.shape))) -
+                     _loss(gout, fwd(lc=dn.reshape(loc.shape)))) / (2 * _STEP)
         _close(gl.reshape(-1), fd, 1e-9, "location central differences")
         if are_logits:
             fd = np.zeros(weights.size)

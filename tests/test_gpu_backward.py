@@ -6,7 +6,7 @@ size and the forward tests' edge cases).  Every call goes through the C ABI
 Tolerance: the float32 bar of the forward tests (1e-5 relative plus 1e-5 of
 the output's rms) for the location / offset and weight / logit gradients.
 The value gradient sums each row's contributions from every sample that
-touches it (up to ~10^3 in workload 3's coarse levels) with float32 atomics
+touches it (up to ~10^3 in the BEVFormer-base SCA workload's coarse levels) with float32 atomics
 in no fixed order, so its bar is 1e-5 of the sum of the contributions'
 magnitudes plus 1e-5 of that sum's rms over the elements (gpu_util explains
 the rms term); the oracle gives the sum exactly: contributions are
@@ -67,7 +67,7 @@ def test_tiny_msda_backward_all_modes():
 
 
 def test_detr_encoder_msda_backward_full():
-    """Workload 2 at full size: all 19947 queries, 4 levels."""
+    """The DETR-encoder workload at full size: all 19947 queries, 4 levels."""
     w = W.detr_encoder_msda()
     gout = W.upstream_gradient(2, (w["B"], w["Nq"], 256))
     check_msda_backward(w, gout, True, "DETR encoder")
@@ -141,14 +141,14 @@ def check_sca_backward(w, gout, what):
 
 
 def test_bevformer_sca_backward_full():
-    """Workload 3 at full size: 40000 queries, 6 cameras."""
+    """The BEVFormer-base SCA workload at full size: 40000 queries, 6 cameras."""
     w = W.bevformer_sca()
     gout = W.upstream_gradient(3, (w["B"], w["Nq"], 256))
-    check_sca_backward(w, gout, "workload 3")
+    check_sca_backward(w, gout, "BEVFormer-base SCA")
 
 
 def test_bevformer_sca_backward_bf16_value():
-    """Workload 3's shapes with a bf16 value map, batch 2 at 100x100 queries."""
+    """The BEVFormer-base SCA workload's shapes with a bf16 value map, batch 2 at 100x100 queries."""
     w = W.bevformer_sca(cfg=33, B=2, bev=100, value_bf16=True)
     gout = W.upstream_gradient(33, (w["B"], w["Nq"], 256))
     check_sca_backward(w, gout, "bf16 value")

@@ -1,7 +1,7 @@
 """The attention layer around the sampling core, against the CPU oracle:
 query projections (sampling offsets and logits from query + position
 embedding, one launch), the output projection with the residual and the
-layer norm, and the whole layer chained on workload 5's shapes.  Every call
+layer norm, and the whole layer chained on the batch-4 bf16 layer workload's shapes.  Every call
 goes through the C ABI (via the ctypes binding)."""
 import numpy as np
 import pytest
@@ -37,7 +37,7 @@ def _rows_with_tail(cfg, M, n):
 # ---------------------------------------------------------------------------
 
 def test_query_proj_full_size():
-    """Workload 5's query path: M = 4 x 40000 queries, K = 256, offsets 512 and
+    """The batch-4 bf16 layer workload's query path: M = 4 x 40000 queries, K = 256, offsets 512 and
     logits 256 columns, with position embedding and biases.  Sampled rows and
     the ragged tail against the oracle, float32 tolerance."""
     w = W.bevformer_layer_bf16(bias=True)
@@ -91,7 +91,7 @@ def _out_case(seed, M, N, K):
 
 
 def test_output_proj_residual_norm_full_size():
-    """Workload 5's output side: M = 160000 slots rows, K = N = 256, residual
+    """The batch-4 bf16 layer workload's output side: M = 160000 slots rows, K = N = 256, residual
     and layer norm; sampled rows and the tail, float32 tolerance."""
     M = 4 * 40000
     c = _out_case(71, M, 256, 256)
@@ -150,7 +150,7 @@ def test_output_proj_norm_constant_rows():
 
 
 # ---------------------------------------------------------------------------
-# the whole layer on workload 5's shapes
+# the whole layer on the batch-4 bf16 layer workload's shapes
 # ---------------------------------------------------------------------------
 
 def test_whole_layer_bf16():

@@ -79,22 +79,22 @@ def check_compaction(got, ref, what):
 
 def test_tiny_msda_fp32_logits_and_probabilities():
     w = W.tiny_msda()
-    assert_fp32_close(run_msda(w), oracle_msda(w), "workload 1, logits")
+    assert_fp32_close(run_msda(w), oracle_msda(w), "tiny MSDA, logits")
     p = _softmax(w["attention_weights"])
-    assert_fp32_close(run_msda(w, msda.MSDA_WEIGHTS_PROB, p), oracle_msda(w, False, p), "workload 1, probabilities")
+    assert_fp32_close(run_msda(w, msda.MSDA_WEIGHTS_PROB, p), oracle_msda(w, False, p), "tiny MSDA, probabilities")
 
 
 def test_tiny_msda_bf16_value():
     w = W.msda_workload(1, 1, 256, ((32, 32),), P=4, value_bf16=True)
-    assert_abs_close(run_msda(w), oracle_msda(w), 1e-2, "workload 1, bf16 value")
+    assert_abs_close(run_msda(w), oracle_msda(w), 1e-2, "tiny MSDA, bf16 value")
     # tighter than the bf16 bar: the bf16 values are decoded exactly, only fp32 accumulation differs
-    assert_fp32_close(run_msda(w), oracle_msda(w), "workload 1, bf16 value (exact decode)")
+    assert_fp32_close(run_msda(w), oracle_msda(w), "tiny MSDA, bf16 value (exact decode)")
 
 
 def test_detr_encoder_msda_full():
     w = W.detr_encoder_msda()
     got = run_msda(w)
-    assert_fp32_close(got, oracle_msda(w), "workload 2 (Deformable-DETR encoder), all 19947 queries")
+    assert_fp32_close(got, oracle_msda(w), "DETR encoder, all 19947 queries")
 
 
 def test_temporal_frames_full():
@@ -103,20 +103,20 @@ def test_temporal_frames_full():
                                    dev(w["sampling_locations"]), dev(w["attention_weights"]))
     ref = oracle.msda_frames(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
                              w["attention_weights"], True)
-    assert_fp32_close(host(out).reshape(-1, 256), ref, "workload 4 (two stacked BEV maps), all 40000 queries")
+    assert_fp32_close(host(out).reshape(-1, 256), ref, "two stacked BEV maps, all 40000 queries")
 
 
 def test_bevformer_sca_full():
     w = W.bevformer_sca()
     got = run_sca(w)
     ref = oracle_sca(w)
-    check_compaction(got, ref, "workload 3")
+    check_compaction(got, ref, "BEVFormer-base SCA")
     assert ref["pair_offsets"][-1] > 40000  # queries seen by two cameras exist
-    assert_fp32_close(got["slots"], ref["slots"], "workload 3 (BEVFormer-base SCA), all 40000 queries")
+    assert_fp32_close(got["slots"], ref["slots"], "BEVFormer-base SCA, all 40000 queries")
 
 
 def test_bevformer_sca_bf16_layer_with_projections():
-    """Workload 5: value projection (bf16 GEMM) -> SCA on bf16 value -> output
+    """The batch-4 bf16 layer workload: value projection (bf16 GEMM) -> SCA on bf16 value -> output
     projection (bf16 GEMM from fp32 slots).  The oracle runs its own chain:
     fp64 projection rounded to bf16, SCA on that, fp64 projection of the
     bf16-rounded slots.  Checked on sampled rows at full size."""
@@ -136,13 +136,13 @@ def test_bevformer_sca_bf16_layer_with_projections():
     got = run_sca(w, value=value_gpu)
     rows = W.sample_rows(55, B * Nq, 3000)
     ref = oracle_sca(w, value=ref_value, rows=rows)
-    check_compaction(got, ref, "workload 5")
-    assert_abs_close(got["slots"][rows], ref["slots"], 1e-2, "workload 5 SCA slots (sampled rows)")
+    check_compaction(got, ref, "batch-4 bf16 layer")
+    assert_abs_close(got["slots"][rows], ref["slots"], 1e-2, "batch-4 bf16 layer SCA slots (sampled rows)")
 
     slots_gpu = torch.from_numpy(got["slots"]).cuda()
     o = msda.msda_gemm_bf16(slots_gpu, dev(w["W_o"]), dev(w["b_o"]), y_dtype=torch.float32)
     ref_o = oracle.linear_bf16(oracle.round_to_bf16(ref["slots"]), w["W_o"], w["b_o"])
-    assert_abs_close(host(o)[rows], ref_o, 1e-2, "workload 5 output projection (sampled rows)")
+    assert_abs_close(host(o)[rows], ref_o, 1e-2, "batch-4 bf16 layer output projection (sampled rows)")
 
 
 # ---------------------------------------------------------------------------

@@ -72,7 +72,7 @@ def run_rebatch(w):
 
 
 def test_rebatch_bevformer_sca_full():
-    """Workload 3 through the padded flow: max_len equals the longest segment,
+    """The BEVFormer-base SCA workload through the padded flow: max_len equals the longest segment,
     the materialised locations and logits are bit-identical to the float32
     definition, and the slots match the oracle's run of the same flow."""
     w = W.bevformer_sca()

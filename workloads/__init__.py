@@ -98,19 +98,19 @@ def _reference(cfg, B, Nq, kind):
 
 
 def tiny_msda():
-    """Workload 1: B=1, 256 queries, one 32x32 level, 8x32, P=4."""
+    """Tiny MSDA: B=1, 256 queries, one 32x32 level, 8x32, P=4."""
     return msda_workload(1, 1, 256, ((32, 32),), P=4)
 
 
 def detr_encoder_msda():
-    """Workload 2: Deformable-DETR encoder shapes, Nq = Nv = 19947, P=4."""
+    """Deformable-DETR encoder shapes, Nq = Nv = 19947, P=4."""
     w = msda_workload(2, 1, 19947, DETR_LEVELS, P=4)
     assert w["Nv"] == 19947
     return w
 
 
 def temporal_frames(cfg=4, B=1, bev=200, F=2, nH=8, Dh=32, P=4):
-    """Workload 4: F stacked BEV maps (one level bev x bev), BEV-centre
+    """F stacked BEV maps (one level bev x bev), BEV-centre
     reference points, per-frame offsets and logits.  Frames are an inner batch
     axis: value [B,F,Nv,nH,Dh], locations [B,F,Nq,nH,1,P,2],
     logits [B,F,Nq,nH,P]."""
@@ -168,7 +168,7 @@ def camera_visibility(cfg, B, Ncam=6, bev=200, D=4, yaw_step_deg=60.0, half_fov_
 
 def bevformer_sca(cfg=3, B=1, Ncam=6, bev=200, shapes=BEV_CAM_LEVELS, nH=8, Dh=32, P=8, D=4,
                   value_bf16=False, offset_px=2.0):
-    """Workload 3 (and the MSDA part of 5): SCA inputs.
+    """BEVFormer-base SCA inputs (also the sampling part of the batch-4 bf16 layer).
 
     value ~ N(0,1) [B,Ncam,Nv,nH,Dh] (fp32, or bf16 bits by truncation);
     sampling_offsets ~ N(0, offset_px) cells [B,Nq,nH,L,P,2];
@@ -206,7 +206,7 @@ def projection_weights(cfg, C=256, bias=False):
 
 
 def bevformer_sca_bf16(cfg=5, B=4, bev=200, shapes=BEV_CAM_LEVELS, bias=False, **kw):
-    """Workload 5: SCA at B=4 whose value comes from a bf16 value projection.
+    """Batch-4 SCA layer whose value comes from a bf16 value projection.
     Adds feat (bf16 bits [B,Ncam,Nv,256], N(0,1)), W_v/b_v/W_o/b_o; 'value' is
     left out: it is the projection's output."""
     w = bevformer_sca(cfg=cfg, B=B, bev=bev, shapes=shapes, **kw)
@@ -219,12 +219,12 @@ def bevformer_sca_bf16(cfg=5, B=4, bev=200, shapes=BEV_CAM_LEVELS, bias=False, *
 
 
 def bevformer_layer_bf16(cfg=5, B=4, bev=200, shapes=BEV_CAM_LEVELS, bias=False, offset_px=2.0, **kw):
-    """Workload 5 widened to the whole attention layer: the sampling offsets
+    """The batch-4 bf16 layer widened to the whole attention layer: the sampling offsets
     and logits come from the query instead of being drawn.  Adds
     query, query_pos ~ N(0,1) float32 [B,Nq,256]; W_off bf16 [nH*L*P*2, 256]
     ~ N(0, offset_px^2 / 512) and W_att bf16 [nH*L*P, 256] ~ N(0, 1/512), so
     that with q~ = query + query_pos (variance 2) the offsets have the
-    N(0, offset_px) cells and the logits the N(0, 1) of workload 3; biases
+    N(0, offset_px) cells and the logits the N(0, 1) of the BEVFormer-base SCA workload; biases
     zero (or N(0, 0.1) with bias=True); layer-norm gamma ~ 1 + N(0, 0.1) and
     beta ~ N(0, 0.1).  The drawn sampling_offsets / attention_logits are
     removed."""
