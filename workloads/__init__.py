@@ -1,23 +1,26 @@
-"""Seeded synthetic inputs for the five workloads (and smaller variants).
+"""Seeded synthetic inputs for the workloads (and smaller variants).
 
 This module is shared by the tests, the smoke check and the benchmark.  It
 draws random inputs only: it holds none of the method's arithmetic, imports
 neither the oracle nor the HIP library, and both sides receive the very same
 arrays.
 
-Seeding: every tensor of workload ``cfg`` is drawn from its own generator
-``np.random.default_rng(np.random.SeedSequence([cfg, tensor_id]))``, so a
-tensor does not change when another one is added or resized.
+Seeding: every tensor of a workload is drawn from its own generator
+``np.random.default_rng(np.random.SeedSequence([cfg, tensor_id]))``, with
+``cfg`` the workload's seed id, so a tensor does not change when another one
+is added or resized.
 
-Workloads (shapes follow BEVFormer-base and a Deformable-DETR encoder):
-  1 tiny MSDA          B=1, Nq=256, one 32x32 level, 8 heads x 32, P=4
-  2 DETR encoder MSDA  B=1, levels 100x150/50x75/25x38/13x19, Nq=Nv=19947, P=4
-  3 BEVFormer SCA      B=1, 6 cameras, 200x200 BEV queries, levels
-                       116x200/58x100/29x50/15x25, P=8, D=4 anchors, fp32 value
-  4 temporal frames    B=1, 2 stacked 200x200 BEV maps, one level, P=4 per frame
-  5 BEVFormer SCA      as 3 with B=4, bf16 projection input and weights
-    (and the whole layer: offsets and logits projected from the query, the
-    output projection followed by the residual and the layer norm)
+Workloads (seed id, generator; shapes follow BEVFormer-base and a
+Deformable-DETR encoder):
+  1 tiny_msda           B=1, Nq=256, one 32x32 level, 8 heads x 32, P=4
+  2 detr_encoder_msda   B=1, levels 100x150/50x75/25x38/13x19, Nq=Nv=19947, P=4
+  3 bevformer_sca       B=1, 6 cameras, 200x200 BEV queries, levels
+                        116x200/58x100/29x50/15x25, P=8, D=4 anchors, fp32 value
+  4 temporal_frames     B=1, 2 stacked 200x200 BEV maps, one level, P=4 per frame
+  5 bevformer_sca_bf16  the SCA layer at B=4 with bf16 projection input and weights;
+    bevformer_layer_bf16 the same layer whole: offsets and logits projected
+                        from the query, the output projection followed by the
+                        residual and the layer norm
 """
 import numpy as np
 
