@@ -86,28 +86,47 @@ __global__ __launch_bounds__(kTile) void sca_visibility_kernel(CompactArgs a, in
   const int q = tile * kTile + (int)threadIdx.x;
   const bool in_range = q < a.Nq;
   uint32_t seen = 0;
-  int first_anchor = 0;
+  int first_anchor = 0, key = -1;
   if (in_range) {
-    for (int c = 0; c < a.Ncam; ++c) {
-      const int64_t at = (((int64_t)c * a.B + b) * a.Nq + q) * a.D;
-      int marked = -1;  // first marked anchor of this camera
-      if (kWordMask) {  // D % 4 == 0 and the mask is 4-byte aligned
-        const uint32_t* m = reinterpret_cast<const uint32_t*>(a.bev_mask + at);
-        for (int k = 0; k < a.D / 4 && marked < 0; ++k)
-          if (m[k] != 0u) marked = 4 * k + __builtin_ctz(m[k]) / 8;
-      } else {
-        for (int k = 0; k < a.D && marked < 0; ++k)
-          if (a.bev_mask[at + k] != 0) marked = k;
-      }
+    const int64_t cam_stride = (int64_t)a.B * a.Nq * a.D;  // mask bytes between cameras
+    const uint8_t* mq = a.bev_mask + ((int64_t)b * a.Nq + q) * a.D;
+    auto note = [&](int c, int marked) {
       if (marked >= 0) {
         if (seen == 0u) first_anchor = marked;
         seen |= 1u << c;
+      }
+    };
+    if (kWordMask) {  // D % 4 == 0 and the mask is 4-byte aligned
+      // the first word (4 anchors) of 8 cameras at a time: the loads go out together
+      constexpr int kCams = 8;
+      const int words = a.D / 4;
+      for (int c0 = 0; c0 < a.Ncam; c0 += kCams) {
+        uint32_t w0[kCams];
+#pragma unroll
+        for (int u = 0; u < kCams; ++u)
+          w0[u] = c0 + u < a.Ncam ? *reinterpret_cast<const uint32_t*>(mq + (c0 + u) * cam_stride) : 0u;
+#pragma unroll
+        for (int u = 0; u < kCams; ++u) {
+          if (c0 + u >= a.Ncam) break;
+          const uint32_t* m = reinterpret_cast<const uint32_t*>(mq + (c0 + u) * cam_stride);
+          int marked = w0[u] != 0u ? __builtin_ctz(w0[u]) / 8 : -1;
+          for (int k = 1; k < words && marked < 0; ++k)
+            if (m[k] != 0u) marked = 4 * k + __builtin_ctz(m[k]) / 8;
+          note(c0 + u, marked);
+        }
+      }
+    } else {
+      for (int c = 0; c < a.Ncam; ++c) {
+        const uint8_t* m = mq + c * cam_stride;
+        int marked = -1;  // first marked anchor of this camera
+        for (int k = 0; k < a.D && marked < 0; ++k)
+          if (m[k] != 0) marked = k;
+        note(c, marked);
       }
     }
     const int64_t bq = (int64_t)b * a.Nq + q;
     a.cammask[bq] = seen;
     if (a.hit_count) a.hit_count[bq] = __popc(seen);
-    int key = -1;
     if (seen != 0u) {
       const int c0 = __builtin_ctz(seen);
       const float2 r = reinterpret_cast<const float2*>(a.rp)[(((int64_t)c0 * a.B + b) * a.Nq + q) * a.D + first_anchor];
@@ -208,9 +227,12 @@ __global__ __launch_bounds__(kScanThreads) void sca_scan_kernel(CompactArgs a, i
 
 __global__ __launch_bounds__(kTile) void sca_compact_kernel(CompactArgs a, int tiles) {
   __shared__ int wave_counts[kTileWaves][32];
+  __shared__ int tile_start[32];
   const int tile = blockIdx.x, b = blockIdx.y;
   const int q = tile * kTile + (int)threadIdx.x;
   const int64_t bq = (int64_t)b * a.Nq + q;
+  if ((int)threadIdx.x < a.Ncam)  // loaded alongside the masks, used after the ballots
+    tile_start[threadIdx.x] = a.tile_offsets[((int64_t)b * a.Ncam + threadIdx.x) * tiles + tile];
   const uint32_t seen = q < a.Nq ? a.cammask[bq] : 0u;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   for (int c = 0; c < a.Ncam; ++c) {
@@ -224,7 +246,7 @@ __global__ __launch_bounds__(kTile) void sca_compact_kernel(CompactArgs a, int t
     if ((seen >> c) & 1u) {
       int rank = __popcll(bits & below);
       for (int w = 0; w < wave; ++w) rank += wave_counts[w][c];
-      a.pair_q[a.tile_offsets[((int64_t)b * a.Ncam + c) * tiles + tile] + rank] = q;
+      a.pair_q[tile_start[c] + rank] = q;
     }
   }
   if (seen != 0u) {
