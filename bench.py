@@ -17,8 +17,10 @@ followed by the residual and the layer norm), "sca_bf16", "sca_rebatch"
 (the default workload through the padded rebatch flow of the SCA note, an
 A/B baseline: per-camera segments padded to the longest, the operator over
 all of them, scatter-add and divide), "sca_train" and "detr_train" (forward
-and backward of the default SCA layer and of the DETR encoder MSDA; the
-roofline then describes the backward kernel), "detr" (Deformable-DETR encoder MSDA),
+and backward of the default SCA layer and of the DETR encoder MSDA, the
+value gradient by the deterministic transpose gather; "_atomic" variants
+accumulate it with float32 atomics instead; the roofline then describes the
+backward kernel), "detr" (Deformable-DETR encoder MSDA),
 "tsa" (two stacked BEV maps, frame mean), "tiny".
 
 Prints one JSON line.  value = bilinear samples per second (one sample = one
@@ -54,7 +56,7 @@ BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 _CSRC = "scale_deformable_attention_forward_amd/csrc/"
 GATHER_SOURCES = [_CSRC + f for f in ("gather.hip", "sampling.hpp", "common.hpp", "internal.hpp")]
-BACKWARD_SOURCES = [_CSRC + f for f in ("backward.hip", "backward.hpp", "sampling.hpp", "common.hpp")]
+BACKWARD_SOURCES = [_CSRC + f for f in ("backward.hip", "backward.hpp", "sampling.hpp", "common.hpp", "vgrad.hpp")]
 KERNEL_SOURCES = {"sca_gather_kernel": GATHER_SOURCES, "msda_gather_kernel": GATHER_SOURCES,
                   "sca_backward_kernel": BACKWARD_SOURCES, "msda_backward_kernel": BACKWARD_SOURCES}
 METRIC = "MSDA samples/sec + effective HBM GB/s, BEVFormer-base SCA layer (6 cams)"
@@ -374,12 +376,15 @@ def train_workload(which):
     """Forward and backward of one step: "sca_train" (the BEVFormer-base SCA
     workload: compaction, SCA forward, SCA backward) or "detr_train" (the
     DETR-encoder workload: MSDA forward and backward).  The upstream gradient
-    is seeded N(0, 1)."""
+    is seeded N(0, 1).  The gradient workspace is made once, for every camera
+    seeing every query (no read-back of the pair count)."""
     import torch
     import workloads as W
     import scale_deformable_attention_forward_amd as m
 
     wl = Workload(which)
+    atomic = which.endswith("_atomic")
+    which = which.replace("_atomic", "")
     if which == "sca_train":
         w = W.bevformer_sca()
         B, Ncam, Nq, Nv, nH, L, P, D = w["B"], w["Ncam"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"], w["D"]
@@ -392,6 +397,8 @@ def train_workload(which):
         gv = torch.empty((B, Ncam, Nv, nH, 32), dtype=torch.float32, device="cuda")
         go = torch.empty_like(d["sampling_offsets"])
         gl = torch.empty_like(d["attention_logits"])
+        gws = None if atomic else torch.empty(m.sca_backward_workspace_size(B, Ncam, Nv, Nq, nH, L, P),
+                                              dtype=torch.uint8, device="cuda")
         args = (d["spatial_shapes"], d["level_start_index"], d["reference_points_cam"])
         wl.parts.append(("compact", lambda: m.sca_compact(d["bev_mask"], d["reference_points_cam"], ws,
                                                           pair_offsets=offs)))
@@ -399,8 +406,10 @@ def train_workload(which):
                                                          d["attention_logits"], ws, slots=slots)))
         wl.parts.append(("backward", lambda: m.sca_backward(d["value"], *args, d["sampling_offsets"],
                                                             d["attention_logits"], gout, ws, grad_value=gv,
-                                                            grad_offsets=go, grad_logits=gl)))
+                                                            grad_offsets=go, grad_logits=gl, grad_workspace=gws,
+                                                            atomic=atomic)))
         names = "BEVFormer-base spatial cross-attention layer, 6 cameras, forward + backward"
+        names += " (value gradient by float32 atomics)" if atomic else ""
         pairs = lambda: int(offs[-1].item())
         n_images = B * Ncam
     else:
@@ -413,12 +422,15 @@ def train_workload(which):
         gv = torch.empty((B, Nv, nH, 32), dtype=torch.float32, device="cuda")
         gloc = torch.empty_like(d["sampling_locations"])
         gw = torch.empty_like(d["attention_weights"])
+        gws = None if atomic else torch.empty(m.msda_backward_workspace_size(B, Nv, Nq, nH, L, P),
+                                              dtype=torch.uint8, device="cuda")
         fargs = (d["value"], d["spatial_shapes"], d["level_start_index"], d["sampling_locations"],
                  d["attention_weights"])
         wl.parts.append(("forward", lambda: m.msda_forward(*fargs, out=out)))
         wl.parts.append(("backward", lambda: m.msda_backward(*fargs, gout, grad_value=gv, grad_locations=gloc,
-                                                             grad_weights=gw)))
+                                                             grad_weights=gw, grad_workspace=gws, atomic=atomic)))
         names = "Deformable-DETR encoder MSDA, 4 levels 100x150/50x75/25x38/13x19, Nq=Nv=19947, forward + backward"
+        names += " (value gradient by float32 atomics)" if atomic else ""
         pairs = lambda: B * Nq
         n_images = B
     wl.main = "backward"
@@ -426,10 +438,11 @@ def train_workload(which):
     def finish():
         n = pairs()
         wl.samples = n * nH * L * P
-        # backward: the corner rows read (as the forward) and the same rows of
-        # value gradient added to, the per-query inputs and upstream gradient
-        # read, the offset / location and weight gradients written, and the
-        # value gradient zeroed first
+        # backward: the corner rows read (as the forward) and, per corner, one
+        # upstream-gradient row read into the value gradient (or, with atomics,
+        # one value-gradient row added to), the per-query inputs and upstream
+        # gradient read, the offset / location and weight gradients written,
+        # and the value gradient written once (or zeroed first)
         S = wl.samples
         wl.gathered_bytes = S * 4 * 32 * 4
         wl.eff_bytes = (2 * wl.gathered_bytes + B * Nq * nH * L * P * (8 + 4) * 2 + B * Nq * nH * 32 * 4
@@ -437,7 +450,8 @@ def train_workload(which):
     wl.finish = finish
     wl.batch = B
     wl.config = {"workload": names, "batch": B, "queries": Nq, "heads": nH, "head_dim": 32, "levels": L,
-                 "points_per_level": P, "value_dtype": "fp32", "pass": "forward + backward"}
+                 "points_per_level": P, "value_dtype": "fp32", "pass": "forward + backward",
+                 "value_gradient": "float32 atomics" if atomic else "transpose gather (deterministic)"}
     wl.dtype = "fp32"
     wl.kernel_key = ("sca_backward_kernel" if which == "sca_train" else "msda_backward_kernel") + "_fp32"
 
@@ -528,7 +542,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sca",
                     choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "sca_train", "detr",
-                             "detr_train", "tsa", "tiny"])
+                             "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="steps timed after a 1 GiB write that evicts the caches (0: none)")
@@ -551,7 +565,7 @@ def main():
         wl = sca_workload(args.workload)
     elif args.workload == "sca_rebatch":
         wl = rebatch_workload()
-    elif args.workload in ("sca_train", "detr_train"):
+    elif args.workload in ("sca_train", "detr_train", "sca_train_atomic", "detr_train_atomic"):
         wl = train_workload(args.workload)
     else:
         wl = msda_workload(args.workload)

@@ -7,7 +7,9 @@
  *   msda_gemm_bf16, msda_query_proj_bf16,
  *   msda_output_proj_bf16                    the layer's bf16 projections on matrix cores
  *   sca_rebatch, sca_scatter_mean            the padded rebatch form of SCA (an A/B baseline)
- *   msda_backward, sca_backward              gradients of the MSDA operator and of SCA
+ *   msda_backward, sca_backward,
+ *   msda_backward_workspace_size,
+ *   sca_backward_workspace_size              gradients of the MSDA operator and of SCA
  *   msda_status_string, msda_last_error      status reporting
  *
  * Sources, cited by page title and section:
@@ -300,7 +302,7 @@ int sca_scatter_mean(const float* rows, const int32_t* pair_offsets, const int32
  * derivatives of msda_forward's definition ([8-heads] 4.2, 6, 8) for the
  * upstream gradient grad_out = d loss / d out:
  *   grad_value              d loss / d value, float32 [B][Nv][nH][Dh] whatever
- *                           value's type; overwritten (zeroed first)
+ *                           value's type; every element written
  *   grad_sampling_locations d loss / d sampling_locations, [B][Nq][nH][L][P][2]
  *   grad_attention_weights  d loss / d attention_weights as given:
  *                           probabilities (MSDA_WEIGHTS_PROB) or logits through
@@ -310,34 +312,66 @@ int sca_scatter_mean(const float* rows, const int32_t* pair_offsets, const int32
  *   grad_out   device float [B][Nq][nH*Dh], 16-byte aligned
  *   grad_value device, 16-byte aligned; one image (Nv*nH*Dh*4 bytes) < 2 GiB
  *   the gradients of locations and weights: device float, 8- and 4-byte aligned
- * Other arguments and limits as msda_forward.  grad_value is accumulated with
- * float32 atomics, so its last bits vary from run to run; the other outputs
- * are each written once.
+ *   grad_workspace  device, >= msda_backward_workspace_size() bytes, 256-byte
+ *              aligned, contents on entry irrelevant; or NULL.
+ * The value gradient of a row is a sum over the samples of many queries.
+ * With grad_workspace it is computed as a transpose gather: every sample
+ * writes a record keyed by its cell, the records are sorted by key (a stable
+ * radix sort) and each row sums the records of its four neighbouring cells in
+ * a fixed order and is written once -- no atomics, and grad_value is the same
+ * bit for bit from run to run.  This needs the level table to fit its maps in
+ * Nv rows (sum over levels of W*H <= Nv, as in any consistent table);
+ * otherwise grad_value is filled with NaN.  With grad_workspace NULL,
+ * grad_value is zeroed and accumulated with float32 atomics (its last bits
+ * then vary from run to run).  The other outputs are each written once.
+ * Other arguments and limits as msda_forward; B*Nq*nH*L*P < 2^28 with a
+ * gradient workspace.
  */
 int msda_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                   const int64_t* level_start_index, const float* sampling_locations, const float* attention_weights,
                   int weight_mode, const float* grad_out, int64_t B, int64_t Nv, int64_t Nq, int nH, int Dh, int L,
                   int P, float* grad_value, float* grad_sampling_locations, float* grad_attention_weights,
-                  void* stream);
+                  void* grad_workspace, size_t grad_workspace_bytes, void* stream);
+
+/* Bytes of msda_backward's gradient workspace (host; no device work).  About
+ * 40 bytes per sample (B*Nq*nH*L*P) plus 8 per cell key
+ * (B*(2*Nv + 2*L)*nH) and 2 MiB. */
+int msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int nH, int L, int P, size_t* bytes);
 
 /*
  * Backward pass of spatial cross-attention (sca_gather's definition,
  * [8-heads] 4.2, 5, 6, 8, 10), for grad_slots = d loss / d slots.  Each
  * seeing camera's share is divided by the hit count; offsets and logits serve
  * every camera of a query, so their gradients sum over the cameras:
- *   grad_value    float32 [B][Ncam][Nv][nH][Dh], overwritten (zeroed first)
+ *   grad_value    float32 [B][Ncam][Nv][nH][Dh], every element written
  *   grad_offsets  d loss / d sampling_offsets (in cells), [B][Nq][nH][L][P][2]
  *   grad_logits   d loss / d attention_logits, [B][Nq][nH][L*P]
  * Queries no camera sees get zero offset and logit gradients.  The workspace
  * must hold the result of sca_compact for the same bev_mask and
- * reference_points_cam (as for sca_gather).  Alignment, limits and the
- * run-to-run variation of grad_value as msda_backward.
+ * reference_points_cam (as for sca_gather).
+ *   max_pairs       capacity of grad_workspace in camera-query pairs; <= 0
+ *                   means every camera seeing every query (B*Nq*Ncam).  If
+ *                   the compaction found more pairs, grad_value is filled
+ *                   with NaN.
+ *   grad_workspace  device, >= sca_backward_workspace_size() bytes for the
+ *                   same max_pairs, 256-byte aligned; or NULL (atomics).
+ * The value gradient is built as for msda_backward (deterministic with a
+ * gradient workspace, float32 atomics without); alignment and limits as
+ * msda_backward, with max_pairs*nH*L*P < 2^28.
  */
 int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                  const int64_t* level_start_index, const float* reference_points_cam, const float* sampling_offsets,
                  const float* attention_logits, const float* grad_slots, int64_t B, int64_t Ncam, int64_t Nv,
                  int64_t Nq, int nH, int Dh, int L, int P, int D, float* grad_value, float* grad_offsets,
-                 float* grad_logits, void* workspace, size_t workspace_bytes, void* stream);
+                 float* grad_logits, void* workspace, size_t workspace_bytes, int64_t max_pairs,
+                 void* grad_workspace, size_t grad_workspace_bytes, void* stream);
+
+/* Bytes of sca_backward's gradient workspace for up to max_pairs camera-query
+ * pairs (<= 0: B*Nq*Ncam) (host; no device work): about 40 bytes per sample
+ * slot (pairs*nH*L*P), 8 per cell key (B*Ncam*(2*Nv + 2*L)*nH), 4 per
+ * camera-query entry (Ncam*B*Nq) and 2 MiB. */
+int sca_backward_workspace_size(int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int L, int P,
+                                int64_t max_pairs, size_t* bytes);
 
 /* Name of a status code (host; static string). */
 const char* msda_status_string(int status);

@@ -64,9 +64,11 @@ def load_library():
                                _p, _p, _sz, _p]
     lib.msda_gemm_bf16.argtypes = [_p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p]
     lib.msda_backward.argtypes = [_p, _int, _p, _p, _p, _p, _int, _p, _i64, _i64, _i64, _int, _int, _int, _int, _p,
-                                  _p, _p, _p]
+                                  _p, _p, _p, _sz, _p]
     lib.sca_backward.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int,
-                                 _int, _p, _p, _p, _p, _sz, _p]
+                                 _int, _p, _p, _p, _p, _sz, _i64, _p, _sz, _p]
+    lib.msda_backward_workspace_size.argtypes = [_i64, _i64, _i64, _int, _int, _int, ctypes.POINTER(_sz)]
+    lib.sca_backward_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _int, _int, _int, _i64, ctypes.POINTER(_sz)]
     lib.sca_rebatch.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _int, _int, _int, _int, _i64, _p, _p, _p]
     lib.sca_scatter_mean.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p]
     lib.msda_query_proj_bf16.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]
@@ -382,13 +384,38 @@ def sca_forward_rebatch(value, spatial_shapes, level_start_index, reference_poin
     return slots, max_len
 
 
+def msda_backward_workspace_size(B, Nv, Nq, nH, L, P):
+    lib = load_library()
+    n = _sz(0)
+    _check("msda_backward_workspace_size",
+           lib.msda_backward_workspace_size(int(B), int(Nv), int(Nq), int(nH), int(L), int(P), ctypes.byref(n)))
+    return n.value
+
+
+def sca_backward_workspace_size(B, Ncam, Nv, Nq, nH, L, P, max_pairs=0):
+    lib = load_library()
+    n = _sz(0)
+    _check("sca_backward_workspace_size",
+           lib.sca_backward_workspace_size(int(B), int(Ncam), int(Nv), int(Nq), int(nH), int(L), int(P),
+                                           int(max_pairs), ctypes.byref(n)))
+    return n.value
+
+
+def _grad_workspace(given, nbytes, dev):
+    if given is not None:
+        return given
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+
+
 def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights, grad_out,
                   weight_mode=MSDA_WEIGHTS_LOGITS, grad_value=None, grad_locations=None, grad_weights=None,
-                  stream=None):
+                  grad_workspace=None, atomic=False, stream=None):
     """Gradients of msda_forward for grad_out = d loss / d out [B,Nq,nH*Dh].
     Returns (grad_value float32 [B,Nv,nH,Dh], grad_locations [B,Nq,nH,L,P,2],
     grad_weights [B,Nq,nH,L*P]); grad_weights is with respect to the weights
-    as given (logits or probabilities, per weight_mode)."""
+    as given (logits or probabilities, per weight_mode).  The value gradient
+    is a deterministic transpose gather through a gradient workspace (made
+    here unless given), or float32 atomics with atomic=True."""
     lib = load_library()
     B, Nv, nH, Dh = value.shape
     _, Nq, _, L, P, _ = sampling_locations.shape
@@ -399,23 +426,32 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, 
         grad_locations = torch.empty_like(sampling_locations)
     if grad_weights is None:
         grad_weights = torch.empty_like(attention_weights)
+    gws, gws_bytes = None, 0
+    if not atomic:
+        gws = _grad_workspace(grad_workspace, msda_backward_workspace_size(B, Nv, Nq, nH, L, P), dev)
+        gws_bytes = gws.numel() * gws.element_size()
     rc = lib.msda_backward(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
                            _ptr(level_start_index, "level_start_index", _I64),
                            _ptr(sampling_locations, "sampling_locations", _F32),
                            _ptr(attention_weights, "attention_weights", _F32), int(weight_mode),
                            _ptr(grad_out, "grad_out", _F32), B, Nv, Nq, nH, Dh, L, P,
                            _ptr(grad_value, "grad_value", _F32), _ptr(grad_locations, "grad_locations", _F32),
-                           _ptr(grad_weights, "grad_weights", _F32), _stream(stream, dev))
+                           _ptr(grad_weights, "grad_weights", _F32),
+                           None if gws is None else _ptr(gws, "grad_workspace"), gws_bytes, _stream(stream, dev))
     _check("msda_backward", rc)
     return grad_value, grad_locations, grad_weights
 
 
 def sca_backward(value, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets, attention_logits,
-                 grad_slots, workspace, grad_value=None, grad_offsets=None, grad_logits=None, stream=None):
+                 grad_slots, workspace, grad_value=None, grad_offsets=None, grad_logits=None, max_pairs=0,
+                 grad_workspace=None, atomic=False, stream=None):
     """Gradients of SCA for grad_slots = d loss / d slots [B,Nq,nH*Dh].  The
     workspace must hold sca_compact's result for the same mask and anchors.
     Returns (grad_value float32 [B,Ncam,Nv,nH,Dh], grad_offsets
-    [B,Nq,nH,L,P,2], grad_logits [B,Nq,nH,L*P])."""
+    [B,Nq,nH,L,P,2], grad_logits [B,Nq,nH,L*P]).  The value gradient is a
+    deterministic transpose gather through a gradient workspace for up to
+    max_pairs camera-query pairs (0: every camera seeing every query), made
+    here unless given, or float32 atomics with atomic=True."""
     lib = load_library()
     B, Ncam, Nv, nH, Dh = value.shape
     _, _, Nq, D, _ = reference_points_cam.shape
@@ -427,6 +463,11 @@ def sca_backward(value, spatial_shapes, level_start_index, reference_points_cam,
         grad_offsets = torch.empty_like(sampling_offsets)
     if grad_logits is None:
         grad_logits = torch.empty_like(attention_logits)
+    gws, gws_bytes = None, 0
+    if not atomic:
+        need = sca_backward_workspace_size(B, Ncam, Nv, Nq, nH, L, P, max_pairs)
+        gws = _grad_workspace(grad_workspace, need, dev)
+        gws_bytes = gws.numel() * gws.element_size()
     rc = lib.sca_backward(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
                           _ptr(level_start_index, "level_start_index", _I64),
                           _ptr(reference_points_cam, "reference_points_cam", _F32),
@@ -435,6 +476,7 @@ def sca_backward(value, spatial_shapes, level_start_index, reference_points_cam,
                           B, Ncam, Nv, Nq, nH, Dh, L, P, D, _ptr(grad_value, "grad_value", _F32),
                           _ptr(grad_offsets, "grad_offsets", _F32), _ptr(grad_logits, "grad_logits", _F32),
                           _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                          int(max_pairs), None if gws is None else _ptr(gws, "grad_workspace"), gws_bytes,
                           _stream(stream, dev))
     _check("sca_backward", rc)
     return grad_value, grad_offsets, grad_logits

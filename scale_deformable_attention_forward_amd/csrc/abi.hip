@@ -9,6 +9,7 @@
 #include "gemm.hpp"
 #include "internal.hpp"
 #include "rebatch.hpp"
+#include "vgrad.hpp"
 #include "msda.h"
 
 namespace {
@@ -421,11 +422,106 @@ static int check_grad_value(const float* grad_value, int64_t Nv, int nH, int Dh,
   return MSDA_OK;
 }
 
+// Layout of the workspace of the deterministic value gradient, after the
+// size checks shared by the size queries and the entry points.
+static int vgrad_plan(int64_t images, int64_t Nv, int64_t L, int64_t nH, int64_t slots, int64_t pair_of_entries,
+                      msda::VgradLayout* lay) {
+  if (slots < 0 || slots >= ((int64_t)1 << 28))
+    return fail(MSDA_ERR_UNSUPPORTED, "%lld sample records: at most 2^28 fit one workspace", (long long)slots);
+  const int64_t per_image = (2 * Nv + 2 * L) * nH;  // corner keys per image, bounded
+  if (per_image >= kI31 || images > (kI31 - 1) / per_image)
+    return fail(MSDA_ERR_UNSUPPORTED, "corner keys of the value gradient exceed 2^31");
+  *lay = msda::vgrad_layout(images, Nv, (int)L, (int)nH, slots, pair_of_entries);
+  return MSDA_OK;
+}
+
+static int vgrad_sizes_ok(int64_t B, int64_t Nv, int64_t Nq, int nH, int L, int P) {
+  if (B < 1 || Nv < 1 || Nq < 0 || nH < 1 || L < 1 || P < 1)
+    return fail(MSDA_ERR_INVALID_ARG, "sizes must be positive");
+  if (nH > 64 || (int64_t)L * P > 64 || Nv >= kI31 || Nq >= kI31 || B >= kI31)
+    return fail(MSDA_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  return MSDA_OK;
+}
+
+int msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int nH, int L, int P, size_t* bytes) {
+  if (!bytes) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  int rc = vgrad_sizes_ok(B, Nv, Nq, nH, L, P);
+  if (rc != MSDA_OK) return rc;
+  msda::VgradLayout lay;
+  rc = vgrad_plan(B, Nv, L, nH, B * Nq * nH * L * P, 0, &lay);
+  if (rc != MSDA_OK) return rc;
+  *bytes = lay.total;
+  return MSDA_OK;
+}
+
+static int64_t sca_pair_capacity(int64_t B, int64_t Ncam, int64_t Nq, int64_t max_pairs) {
+  const int64_t all = B * Nq * Ncam;
+  return max_pairs > 0 && max_pairs < all ? max_pairs : all;
+}
+
+int sca_backward_workspace_size(int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int L, int P,
+                                int64_t max_pairs, size_t* bytes) {
+  if (!bytes) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  int rc = vgrad_sizes_ok(B, Nv, Nq, nH, L, P);
+  if (rc != MSDA_OK) return rc;
+  if (Ncam < 1 || Ncam > 32) return fail(MSDA_ERR_UNSUPPORTED, "Ncam=%lld: 1 to 32 cameras", (long long)Ncam);
+  msda::VgradLayout lay;
+  rc = vgrad_plan(B * Ncam, Nv, L, nH, sca_pair_capacity(B, Ncam, Nq, max_pairs) * nH * L * P, Ncam * B * Nq, &lay);
+  if (rc != MSDA_OK) return rc;
+  *bytes = lay.total;
+  return MSDA_OK;
+}
+
+// The state, sort buffers and geometry of the transpose gather.
+static msda::VgradArgs vgrad_args(const msda::VgradLayout& lay, void* workspace, const int64_t* shapes,
+                                  const int64_t* starts, int L, int nH, int64_t Nv, int64_t images,
+                                  const float* grad_out, int64_t grad_rows, float* grad_value) {
+  char* ws = static_cast<char*>(workspace);
+  msda::VgradArgs v = {};
+  for (int i = 0; i < 2; ++i) {
+    v.keys[i] = reinterpret_cast<uint32_t*>(ws + lay.keys[i]);
+    v.vals[i] = reinterpret_cast<msda::VgradRec*>(ws + lay.vals[i]);
+  }
+  v.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
+  v.digit_totals = reinterpret_cast<uint32_t*>(ws + lay.digit_totals);
+  v.ranges = reinterpret_cast<int2*>(ws + lay.ranges);
+  v.state = reinterpret_cast<msda::VgradState*>(ws + lay.state);
+  v.pair_of = reinterpret_cast<int32_t*>(ws + lay.pair_of);
+  v.slots = lay.slots;
+  v.key_bound = lay.key_bound;
+  v.passes = lay.passes;
+  v.shapes = shapes;
+  v.starts = starts;
+  v.L = L;
+  v.nH = nH;
+  v.Nv = (int)Nv;
+  v.images = images;
+  v.grad_out = grad_out;
+  v.grad_out_bytes = (uint32_t)(grad_rows * 128);
+  v.grad_value = grad_value;
+  return v;
+}
+
+static int check_grad_workspace(const msda::VgradLayout& lay, const void* ws, size_t bytes) {
+  if (bytes < lay.total || !aligned(ws, 256))
+    return fail(MSDA_ERR_WORKSPACE, "gradient workspace must be >= %zu bytes and 256-byte aligned (got %zu)",
+                lay.total, bytes);
+  return MSDA_OK;
+}
+
+static void set_records(msda::BackwardArgs& a, const msda::VgradArgs& v, int64_t max_pairs) {
+  a.rec_keys = v.keys[0];
+  a.rec_vals = v.vals[0];
+  a.key_bound = v.key_bound;
+  a.pair_of = v.pair_of;
+  a.max_pairs = max_pairs;
+}
+
 int msda_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                   const int64_t* level_start_index, const float* sampling_locations, const float* attention_weights,
                   int weight_mode, const float* grad_out, int64_t B, int64_t Nv, int64_t Nq, int nH, int Dh, int L,
                   int P, float* grad_value, float* grad_sampling_locations, float* grad_attention_weights,
-                  void* stream) {
+                  void* grad_workspace, size_t grad_workspace_bytes, void* stream) {
   uint32_t image_bytes = 0, grad_bytes = 0;
   int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, grad_out,
                         &image_bytes);
@@ -441,6 +537,12 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
                   !aligned(attention_weights, 4) || !aligned(grad_attention_weights, 4)))
     return fail(MSDA_ERR_INVALID_ARG, "(x, y) arrays must be 8-byte aligned");
   if (B >= kI31 || B * Nq >= kI31 || B * Nq * nH >= kI31 / 64) return fail(MSDA_ERR_UNSUPPORTED, "B*Nq*nH too large");
+  msda::VgradLayout lay = {};
+  if (grad_workspace) {
+    rc = vgrad_plan(B, Nv, L, nH, B * Nq * nH * L * P, 0, &lay);
+    if (rc == MSDA_OK) rc = check_grad_workspace(lay, grad_workspace, grad_workspace_bytes);
+    if (rc != MSDA_OK) return rc;
+  }
   g_last_error[0] = '\0';
   msda::BackwardArgs a = {};
   a.value = value;
@@ -466,14 +568,24 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
   a.weight_logits = weight_mode == MSDA_WEIGHTS_LOGITS;
   a.grad_loc = grad_sampling_locations;
   a.grad_weights = grad_attention_weights;
-  return hip_status(msda::launch_msda_backward(a, static_cast<hipStream_t>(stream)), "msda backward launch");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!grad_workspace) return hip_status(msda::launch_msda_backward(a, st), "msda backward launch");
+  msda::VgradArgs v = vgrad_args(lay, grad_workspace, spatial_shapes, level_start_index, L, nH, Nv, B, grad_out,
+                                 B * Nq * nH, grad_value);
+  v.LP = L * P;
+  set_records(a, v, B * Nq);
+  rc = hip_status(msda::launch_vgrad_setup(v, false, st), "value gradient setup");
+  if (rc == MSDA_OK) rc = hip_status(msda::launch_msda_backward(a, st), "msda backward launch");
+  if (rc == MSDA_OK) rc = hip_status(msda::launch_vgrad_rows(v, st), "value gradient rows");
+  return rc;
 }
 
 int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                  const int64_t* level_start_index, const float* reference_points_cam, const float* sampling_offsets,
                  const float* attention_logits, const float* grad_slots, int64_t B, int64_t Ncam, int64_t Nv,
                  int64_t Nq, int nH, int Dh, int L, int P, int D, float* grad_value, float* grad_offsets,
-                 float* grad_logits, void* workspace, size_t workspace_bytes, void* stream) {
+                 float* grad_logits, void* workspace, size_t workspace_bytes, int64_t max_pairs,
+                 void* grad_workspace, size_t grad_workspace_bytes, void* stream) {
   uint32_t image_bytes = 0, grad_bytes = 0;
   int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, grad_slots,
                         &image_bytes);
@@ -491,6 +603,13 @@ int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shap
   if (B * Ncam >= kI31 || B * Nq * nH >= kI31 / 64) return fail(MSDA_ERR_UNSUPPORTED, "B*Nq*nH too large");
   rc = check_workspace(B, Ncam, Nq, workspace, workspace_bytes);
   if (rc != MSDA_OK) return rc;
+  const int64_t pairs_cap = sca_pair_capacity(B, Ncam, Nq, max_pairs);
+  msda::VgradLayout lay = {};
+  if (grad_workspace) {
+    rc = vgrad_plan(B * Ncam, Nv, L, nH, pairs_cap * nH * L * P, Ncam * B * Nq, &lay);
+    if (rc == MSDA_OK) rc = check_grad_workspace(lay, grad_workspace, grad_workspace_bytes);
+    if (rc != MSDA_OK) return rc;
+  }
   g_last_error[0] = '\0';
   const msda::CompactArgs c = compact_args(nullptr, nullptr, B, Ncam, Nq, D, nullptr, nullptr, nullptr, workspace);
   msda::BackwardArgs a = {};
@@ -523,7 +642,24 @@ int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shap
   a.D = D;
   a.grad_offsets = grad_offsets;
   a.grad_logits = grad_logits;
-  return hip_status(msda::launch_sca_backward(a, static_cast<hipStream_t>(stream)), "sca backward launch");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!grad_workspace) return hip_status(msda::launch_sca_backward(a, st), "sca backward launch");
+  msda::VgradArgs v = vgrad_args(lay, grad_workspace, spatial_shapes, level_start_index, L, nH, Nv, B * Ncam,
+                                 grad_slots, B * Nq * nH, grad_value);
+  v.LP = L * P;
+  v.cammask = c.cammask;
+  v.tile_offsets = c.tile_offsets;
+  v.tile_counts = c.tile_counts;
+  v.B = (int)B;
+  v.Ncam = (int)Ncam;
+  v.Nq = (int)Nq;
+  v.tiles = msda::compact_layout(B, Ncam, Nq).tiles;
+  v.max_pairs = pairs_cap;
+  set_records(a, v, pairs_cap);
+  rc = hip_status(msda::launch_vgrad_setup(v, true, st), "value gradient setup");
+  if (rc == MSDA_OK) rc = hip_status(msda::launch_sca_backward(a, st), "sca backward launch");
+  if (rc == MSDA_OK) rc = hip_status(msda::launch_vgrad_rows(v, st), "value gradient rows");
+  return rc;
 }
 
 }  // extern "C"

@@ -37,6 +37,7 @@
 #include "backward.hpp"
 #include "common.hpp"
 #include "sampling.hpp"
+#include "vgrad.hpp"
 
 namespace msda {
 
@@ -148,9 +149,10 @@ __device__ inline void transpose_grad(float4 g4, int lane, float (&gt)[4]) {
 }
 
 // Walk the group's S staged samples (two at a time).  res[s] receives
-// (<S, g>, <dS/dx, g>, <dS/dy, g>) of record s; the value gradient of every
-// corner gets alpha * w_c * g, as whole-row atomics (transpose_grad).
-template <bool kBF16>
+// (<S, g>, <dS/dx, g>, <dS/dy, g>) of record s; with kAtomics the value
+// gradient of every corner gets alpha * w_c * g, as whole-row atomics
+// (transpose_grad).
+template <bool kBF16, bool kAtomics>
 __device__ inline void walk_samples(const SampleRec* __restrict__ recs, float4* __restrict__ res, int S, float4 g4,
                                     const float (&gt)[4], __amdgpu_buffer_rsrc_t img, __amdgpu_buffer_rsrc_t gimg,
                                     int lane) {
@@ -182,6 +184,7 @@ __device__ inline void walk_samples(const SampleRec* __restrict__ recs, float4* 
       dx = group_sum(dx);
       dy = group_sum(dy);
       if (j == 0) res[s + u] = make_float4(ds, dx, dy, 0.f);
+      if (!kAtomics) continue;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float coef = r[u].alpha * wxs[c & 1] * wys[c >> 1];
@@ -196,6 +199,42 @@ __device__ inline void walk_samples(const SampleRec* __restrict__ recs, float4* 
         }
       }
     }
+  }
+}
+
+// The records of one head's samples for the transpose gather of the value
+// gradient (vgrad.hip): slot slot0 + k for sample k, key kDeadKey when no
+// corner is inside the map.  The cell and fractions are those of
+// sample_rows_of; alpha is divided by the query's hit count (SCA).
+template <int kSPL>
+__device__ inline void emit_records(const BackwardArgs& a, const Level* lv, const long long* ext, int64_t image,
+                                    int64_t slot0, uint32_t src, int hits, const double (&xs)[kSPL],
+                                    const double (&ys)[kSPL], const float (&alpha)[kSPL], uint32_t live, int j,
+                                    int h) {
+  VgradRec* vals = static_cast<VgradRec*>(a.rec_vals);
+#pragma unroll
+  for (int i = 0; i < kSPL; ++i) {
+    const int k = j + 8 * i;
+    if (k >= a.LP) continue;
+    uint32_t key = kDeadKey;
+    if ((live >> i) & 1u) {
+      const int l = small_div(k, a.inv_P);
+      const Level L = lv[l];
+      const double x = fmin(fmax(xs[i], -2.0), (double)L.W + 1.0);
+      const double y = fmin(fmax(ys[i], -2.0), (double)L.H + 1.0);
+      const double xf = floor(x), yf = floor(y);
+      VgradRec r;
+      r.src = src;
+      r.alpha = hits > 1 ? alpha[i] / (float)hits : alpha[i];
+      r.fx = (float)(x - xf);
+      r.fy = (float)(y - yf);
+      const uint64_t kk = corner_key(image, ext[a.L], ext[l], L.W, (int)xf + 1, (int)yf + 1, a.nH, h);
+      if (kk < (uint64_t)a.key_bound) {
+        key = (uint32_t)kk;
+        vals[slot0 + k] = r;
+      }
+    }
+    a.rec_keys[slot0 + k] = key;
   }
 }
 
@@ -238,14 +277,16 @@ __device__ inline void weights_grad(const float (&alpha)[kSPL], const float (&ds
 // ---------------------------------------------------------------------------
 // MSDA operator: item = (b, q)
 // ---------------------------------------------------------------------------
-template <bool kBF16, int kSPL>
+template <bool kBF16, int kSPL, bool kEmit>
 __global__ __launch_bounds__(kBwdMaxWaves* kWave) void msda_backward_kernel(BackwardArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ long long ext[kMaxLevels + 1];
   const int waves_per_block = blockDim.x / kWave;
   const int lane = threadIdx.x % kWave, wave = uniform((int)(threadIdx.x / kWave));
   const int g = lane / 8, j = lane % 8;
   BwdLds m(smem, a.LP, wave, g, waves_per_block);
   load_levels(a.shapes, a.starts, a.L, m.lv);
+  if (kEmit) load_corner_starts(m.lv, a.L, ext);
 
   XcdSplit split(a.B * a.Nq, waves_per_block);
   for (int64_t item = split.begin; item < split.end; item += split.stride) {
@@ -278,8 +319,10 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave) void msda_backward_kernel(Back
       }
       int pos[kSPL];
       const int S = stage_samples<kSPL>(m.recs, xs, ys, alpha, live, m.lv, a.inv_P, j, h, a.nH, a.Nv, pos);
+      if (kEmit && head_ok)
+        emit_records<kSPL>(a, m.lv, ext, b, src_row * a.LP, (uint32_t)src_row, 1, xs, ys, alpha, live, j, h);
       wave_lds_sync();
-      walk_samples<kBF16>(m.recs, m.res, S, g4, gt, img, gimg, lane);
+      walk_samples<kBF16, !kEmit>(m.recs, m.res, S, g4, gt, img, gimg, lane);
       wave_lds_sync();
       float ds[kSPL], gw[kSPL];
 #pragma unroll
@@ -309,14 +352,16 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave) void msda_backward_kernel(Back
 // of its query, sums the offset and logit gradients over them, and writes
 // them once.  Queries no camera sees get zero gradients at the end.
 // ---------------------------------------------------------------------------
-template <bool kBF16, int kSPL>
+template <bool kBF16, int kSPL, bool kEmit>
 __global__ __launch_bounds__(kBwdMaxWaves* kWave) void sca_backward_kernel(BackwardArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ long long ext[kMaxLevels + 1];
   const int waves_per_block = blockDim.x / kWave;
   const int lane = threadIdx.x % kWave, wave = uniform((int)(threadIdx.x / kWave));
   const int g = lane / 8, j = lane % 8;
   BwdLds m(smem, a.LP, wave, g, waves_per_block);
   load_levels(a.shapes, a.starts, a.L, m.lv);
+  if (kEmit) load_corner_starts(m.lv, a.L, ext);
   const int64_t n_queries = a.B * a.Nq;
   const uint32_t cam_bits = a.Ncam >= 32 ? 0xffffffffu : ((1u << a.Ncam) - 1u);
 
@@ -376,13 +421,19 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave) void sca_backward_kernel(Backw
           }
           int pos[kSPL];
           const int S = stage_samples<kSPL>(m.recs, xs, ys, alpha, live, m.lv, a.inv_P, j, h, a.nH, a.Nv, pos);
-          wave_lds_sync();
           const int64_t image = b * a.Ncam + c;
+          if (kEmit) {
+            const int64_t pair = uniform((int64_t)a.pair_of[(c * a.B + b) * a.Nq + q]);
+            if (head_ok && pair >= 0 && pair < a.max_pairs)
+              emit_records<kSPL>(a, m.lv, ext, image, (pair * a.nH + h) * a.LP, (uint32_t)src_row, hits, xs, ys,
+                                 alpha, live, j, h);
+          }
+          wave_lds_sync();
           const auto img = make_rsrc(static_cast<const char*>(a.value) + image * (int64_t)a.image_bytes,
                                      a.image_bytes);
           const auto gimg = make_rsrc(reinterpret_cast<char*>(a.grad_value) + image * (int64_t)a.grad_image_bytes,
                                       a.grad_image_bytes);
-          walk_samples<kBF16>(m.recs, m.res, S, g4, gt, img, gimg, lane);
+          walk_samples<kBF16, !kEmit>(m.recs, m.res, S, g4, gt, img, gimg, lane);
           wave_lds_sync();
 #pragma unroll
           for (int i = 0; i < kSPL; ++i) {
@@ -475,19 +526,37 @@ static void zero_grad_value(const BackwardArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_msda_backward(const BackwardArgs& a, hipStream_t stream) {
-  zero_grad_value(a, stream);
   const int64_t n = a.B * a.Nq;
+  if (a.rec_keys) {  // records for the transpose gather: grad_value is written later, whole
+    if (a.LP <= 32)
+      return launch(a.bf16 ? msda_backward_kernel<true, 4, true> : msda_backward_kernel<false, 4, true>, n, a.LP, a,
+                    stream);
+    return launch(a.bf16 ? msda_backward_kernel<true, 8, true> : msda_backward_kernel<false, 8, true>, n, a.LP, a,
+                  stream);
+  }
+  zero_grad_value(a, stream);
   if (a.LP <= 32)
-    return launch(a.bf16 ? msda_backward_kernel<true, 4> : msda_backward_kernel<false, 4>, n, a.LP, a, stream);
-  return launch(a.bf16 ? msda_backward_kernel<true, 8> : msda_backward_kernel<false, 8>, n, a.LP, a, stream);
+    return launch(a.bf16 ? msda_backward_kernel<true, 4, false> : msda_backward_kernel<false, 4, false>, n, a.LP, a,
+                  stream);
+  return launch(a.bf16 ? msda_backward_kernel<true, 8, false> : msda_backward_kernel<false, 8, false>, n, a.LP, a,
+                stream);
 }
 
 hipError_t launch_sca_backward(const BackwardArgs& a, hipStream_t stream) {
-  zero_grad_value(a, stream);
   const int64_t n = a.B * a.Nq;
+  if (a.rec_keys) {
+    if (a.LP <= 32)
+      return launch(a.bf16 ? sca_backward_kernel<true, 4, true> : sca_backward_kernel<false, 4, true>, n, a.LP, a,
+                    stream);
+    return launch(a.bf16 ? sca_backward_kernel<true, 8, true> : sca_backward_kernel<false, 8, true>, n, a.LP, a,
+                  stream);
+  }
+  zero_grad_value(a, stream);
   if (a.LP <= 32)
-    return launch(a.bf16 ? sca_backward_kernel<true, 4> : sca_backward_kernel<false, 4>, n, a.LP, a, stream);
-  return launch(a.bf16 ? sca_backward_kernel<true, 8> : sca_backward_kernel<false, 8>, n, a.LP, a, stream);
+    return launch(a.bf16 ? sca_backward_kernel<true, 4, false> : sca_backward_kernel<false, 4, false>, n, a.LP, a,
+                  stream);
+  return launch(a.bf16 ? sca_backward_kernel<true, 8, false> : sca_backward_kernel<false, 8, false>, n, a.LP, a,
+                stream);
 }
 
 }  // namespace msda

@@ -39,6 +39,15 @@ struct BackwardArgs {
   int Ncam, D;
   float* grad_offsets;  // [B][Nq][nH][L][P][2]
   float* grad_logits;   // [B][Nq][nH][L*P]
+  // When rec_keys is set, the value gradient is not accumulated here: every
+  // sample writes its record (vgrad.hpp) at slot (pair * nH + h) * LP + k,
+  // pair = (b, q) for MSDA and pair_of[c][b][q] for SCA (pairs at or past
+  // max_pairs write nothing), and vgrad.hip builds grad_value from them.
+  uint32_t* rec_keys;
+  void* rec_vals;
+  int64_t key_bound;
+  const int32_t* pair_of;
+  int64_t max_pairs;
 };
 
 hipError_t launch_msda_backward(const BackwardArgs& a, hipStream_t stream);

@@ -32,7 +32,7 @@
 
 namespace msda {
 
-constexpr int kTile = 256;  // queries per tile = threads per block
+constexpr int kTile = kQueryTile;  // queries per tile = threads per block
 constexpr int kTileWaves = kTile / kWave;
 constexpr int kScanThreads = kOrderBins;  // one bin per thread
 static_assert(kScanThreads == 1024, "the scan block holds one segment's bins");

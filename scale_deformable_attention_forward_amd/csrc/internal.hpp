@@ -42,6 +42,7 @@ hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_sca_gather(const GatherArgs& a, hipStream_t stream);
 
 // SCA compaction and work ordering: workspace layout and launch.
+constexpr int kQueryTile = 256;  // queries per tile of the compaction (and its pair ranking)
 // Image-tile grid used to order the gather work (per first camera).
 constexpr int kOrderBinsX = 64, kOrderBinsY = 16, kOrderBins = kOrderBinsX * kOrderBinsY;
 

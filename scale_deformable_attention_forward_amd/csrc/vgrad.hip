@@ -1,0 +1,411 @@
+// Value gradient of the backward pass as a transpose gather, with no atomics
+// and a fixed summation order.
+//
+// "BEV(三) BEVFormer：Query 参数如何与 Feature 的 8 个 Head 交互" (sections 4.2,
+// 6, 8) defines the forward as sums of alpha_k * w_c * V_c over the samples k
+// of a query-head and the four corners c of each; so the gradient of a value
+// row is the sum, over every (sample, corner) that reads the row, of
+// alpha_k * w_c * g, g the upstream gradient of that query-head (for SCA
+// divided by the query's hit count, section 10 of the same page and the
+// Tencent Cloud SCA note, article 2321140).  Instead of scattering these
+// terms with atomics:
+//   1. the backward kernel writes one record per sample, at a slot fixed by
+//      (pair, head, sample): the key of its corner (x0 + 1, y0 + 1) in a
+//      corner grid of (W + 1) x (H + 1) keys per level and head (every sample
+//      with a corner inside its map has such a key), and (source row,
+//      alpha, fx, fy);
+//   2. a stable LSD radix sort (8-bit digits; each of kSortWaves waves owns
+//      a contiguous range, ranks its keys with ballots, and writes them after
+//      the records of the same digit from earlier waves) orders the records
+//      by key, dead samples dropped in the first pass;
+//   3. the (first, end) range of every key is recorded;
+//   4. one 8-lane group per value row (pixel (x, y) of level l, head h)
+//      sums, for the corners (dx, dy) = (0,0), (1,0), (0,1), (1,1) in turn,
+//      the records of key (x + 1 - dx, y + 1 - dy) in sorted order, and
+//      writes the row once.
+// The order of every sum is fixed by the slots, so grad_value is the same
+// bit for bit from run to run.
+#include "common.hpp"
+#include "internal.hpp"
+#include "sampling.hpp"
+#include "vgrad.hpp"
+
+namespace msda {
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+VgradLayout vgrad_layout(int64_t images, int64_t Nv, int L, int nH, int64_t slots, int64_t pair_of_entries) {
+  VgradLayout l = {};
+  l.slots = slots;
+  // (W + 1)(H + 1) <= 2 W H + 2 for W, H >= 1, so a level table whose maps fit
+  // in Nv rows has at most 2 Nv + 2 L corner keys per image and head
+  l.key_bound = images * (2 * Nv + 2 * (int64_t)L) * nH;
+  int bits = 1;
+  while (bits < 62 && ((int64_t)1 << bits) < l.key_bound) ++bits;
+  l.passes = (bits + 7) / 8;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  l.keys[0] = take(sizeof(uint32_t) * (size_t)slots);
+  l.keys[1] = take(sizeof(uint32_t) * (size_t)slots);
+  l.vals[0] = take(sizeof(VgradRec) * (size_t)slots);
+  l.vals[1] = take(sizeof(VgradRec) * (size_t)slots);
+  l.counts = take(sizeof(uint32_t) * (size_t)kDigits * kSortWaves);
+  l.digit_totals = take(sizeof(uint32_t) * kDigits);
+  l.ranges = take(sizeof(int2) * (size_t)l.key_bound);
+  l.pair_of = take(sizeof(int32_t) * (size_t)pair_of_entries);
+  l.state = take(sizeof(VgradState));
+  l.total = o;
+  return l;
+}
+
+// ---------------------------------------------------------------------------
+// setup: state, SCA pair indices
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void vgrad_setup_kernel(VgradArgs a, int sca) {
+  __shared__ Level lv[kMaxLevels];
+  __shared__ long long ext[kMaxLevels + 1];
+  load_levels(a.shapes, a.starts, a.L, lv);
+  load_corner_starts(lv, a.L, ext);
+  if (threadIdx.x != 0) return;
+  int status = 0;
+  const long long per_image = ext[a.L];  // corner keys per image and head
+  if (per_image > a.key_bound || a.images * per_image > a.key_bound || a.images * per_image * a.nH > a.key_bound)
+    status |= kVgradKeysOverflow;
+  int64_t items = a.slots;
+  if (sca) {
+    // the pair lists end where the last tile of the last (b, c) segment ends
+    const int64_t last = (int64_t)a.B * a.Ncam * a.tiles - 1;
+    int64_t pairs = last >= 0 ? (int64_t)a.tile_offsets[last] + a.tile_counts[last] : 0;
+    if (pairs > a.max_pairs) {
+      status |= kVgradPairsOverflow;
+      pairs = a.max_pairs;
+    }
+    items = pairs * a.nH * a.LP;
+  }
+  a.state->n_items = items;
+  a.state->n_live = 0;
+  a.state->status = status;
+}
+
+// pair_of[c][b][q] = index of (b, c, q) in the compaction's pair lists: the
+// tile's offset in the (b, c) list plus the seen queries before q in the tile
+// (the ranking of sca_compact_kernel)
+__global__ __launch_bounds__(kQueryTile) void vgrad_pair_of_kernel(VgradArgs a) {
+  constexpr int kTileWaves = kQueryTile / kWave;
+  __shared__ int wave_counts[kTileWaves][32];
+  __shared__ int tile_start[32];
+  const int tile = blockIdx.x, b = blockIdx.y;
+  const int q = tile * kQueryTile + (int)threadIdx.x;
+  const int64_t bq = (int64_t)b * a.Nq + q;
+  if ((int)threadIdx.x < a.Ncam)
+    tile_start[threadIdx.x] = a.tile_offsets[((int64_t)b * a.Ncam + threadIdx.x) * a.tiles + tile];
+  const uint32_t seen = q < a.Nq ? a.cammask[bq] : 0u;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  for (int c = 0; c < a.Ncam; ++c) {
+    const uint64_t bits = __ballot((seen >> c) & 1u);
+    if (lane == 0) wave_counts[wave][c] = __popcll(bits);
+  }
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int c = 0; c < a.Ncam; ++c) {
+    const uint64_t bits = __ballot((seen >> c) & 1u);
+    if ((seen >> c) & 1u) {
+      int rank = __popcll(bits & below);
+      for (int w = 0; w < wave; ++w) rank += wave_counts[w][c];
+      a.pair_of[((int64_t)c * a.B + b) * a.Nq + q] = tile_start[c] + rank;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// radix sort passes
+// ---------------------------------------------------------------------------
+__device__ inline void wave_range(int64_t n, int64_t w, int64_t* lo, int64_t* hi) {
+  *lo = n * w / kSortWaves;
+  *hi = n * (w + 1) / kSortWaves;
+}
+
+constexpr int kSortBlock = 256;  // 4 waves
+constexpr int kSortUnroll = 8;   // keys per lane in flight
+
+// digit counts of each wave's range -> counts[digit][wave]
+template <bool kFirst>
+__global__ __launch_bounds__(kSortBlock) void vgrad_hist_kernel(VgradArgs a, int src, int shift) {
+  __shared__ uint32_t h[kSortBlock / kWave][kDigits];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t w = (int64_t)blockIdx.x * (kSortBlock / kWave) + wave;
+  const int64_t n = uniform(kFirst ? a.state->n_items : a.state->n_live);
+  int64_t lo, hi;
+  wave_range(n, w, &lo, &hi);
+  for (int d = lane; d < kDigits; d += kWave) h[wave][d] = 0u;
+  wave_lds_sync();
+  const uint32_t* keys = a.keys[src];
+  for (int64_t base = lo; base < hi; base += kSortUnroll * kWave) {
+    uint32_t k[kSortUnroll];
+#pragma unroll
+    for (int u = 0; u < kSortUnroll; ++u) {
+      const int64_t i = base + u * kWave + lane;
+      k[u] = i < hi ? keys[i] : kDeadKey;
+    }
+#pragma unroll
+    for (int u = 0; u < kSortUnroll; ++u)
+      if (k[u] != kDeadKey) atomicAdd(&h[wave][(k[u] >> shift) & (kDigits - 1)], 1u);
+  }
+  wave_lds_sync();
+  for (int d = lane; d < kDigits; d += kWave) a.counts[(int64_t)d * kSortWaves + w] = h[wave][d];
+}
+
+// one block per digit: counts[d][*] -> exclusive offsets among the waves,
+// digit_totals[d] = the digit's total
+constexpr int kScanBlock = 1024;
+__global__ __launch_bounds__(kScanBlock) void vgrad_scan_kernel(VgradArgs a) {
+  constexpr int kPer = kSortWaves / kScanBlock;
+  __shared__ uint32_t wave_sums[kScanBlock / kWave];
+  const int d = blockIdx.x, t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  uint32_t* row = a.counts + (int64_t)d * kSortWaves;
+  uint32_t v[kPer], s = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    v[u] = row[t * kPer + u];
+    s += v[u];
+  }
+  uint32_t incl = s;
+#pragma unroll
+  for (int k = 1; k < kWave; k <<= 1) {
+    const uint32_t y = __shfl_up(incl, k);
+    if (lane >= k) incl += y;
+  }
+  if (lane == kWave - 1) wave_sums[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+  for (int w = 0; w < kScanBlock / kWave; ++w) {
+    const uint32_t x = wave_sums[w];
+    before += w < wave ? x : 0u;
+    total += x;
+  }
+  uint32_t run = before + incl - s;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    row[t * kPer + u] = run;
+    run += v[u];
+  }
+  if (t == 0) a.digit_totals[d] = total;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// stable scatter of each wave's range: a key goes after every key of a lower
+// digit, after the keys of its digit in earlier waves, and after those of its
+// digit earlier in its own range
+template <bool kFirst>
+__global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, int src, int shift) {
+  __shared__ uint32_t cur[kSortBlock / kWave][kDigits];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t w = (int64_t)blockIdx.x * (kSortBlock / kWave) + wave;
+  const int64_t n = uniform(kFirst ? a.state->n_items : a.state->n_live);
+  int64_t lo, hi;
+  wave_range(n, w, &lo, &hi);
+  // digit bases: exclusive scan of the 256 digit totals, 4 digits per lane
+  uint32_t tot[kDigits / kWave], s = 0;
+#pragma unroll
+  for (int u = 0; u < kDigits / kWave; ++u) {
+    tot[u] = a.digit_totals[lane * (kDigits / kWave) + u];
+    s += tot[u];
+  }
+  uint32_t incl = s;
+#pragma unroll
+  for (int k = 1; k < kWave; k <<= 1) {
+    const uint32_t y = __shfl_up(incl, k);
+    if (lane >= k) incl += y;
+  }
+  uint32_t run = incl - s;
+#pragma unroll
+  for (int u = 0; u < kDigits / kWave; ++u) {
+    const int d = lane * (kDigits / kWave) + u;
+    cur[wave][d] = run + a.counts[(int64_t)d * kSortWaves + w];
+    run += tot[u];
+  }
+  if (kFirst && w == 0 && lane == kWave - 1) a.state->n_live = incl;  // records that survive the first pass
+  wave_lds_sync();
+
+  const int dst = src ^ 1;
+  const uint32_t* keys = a.keys[src];
+  const VgradRec* vals = a.vals[src];
+  // stores through descriptors sized to the buffers: a position past the end
+  // is dropped by the hardware
+  const auto okeys = make_rsrc(a.keys[dst], (uint32_t)(a.slots * sizeof(uint32_t)));
+  const auto ovals = make_rsrc(a.vals[dst], (uint32_t)(a.slots * sizeof(VgradRec)));
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  for (int64_t base = lo; base < hi; base += kSortUnroll * kWave) {
+    uint32_t k[kSortUnroll];
+    VgradRec v[kSortUnroll];
+#pragma unroll
+    for (int u = 0; u < kSortUnroll; ++u) {
+      const int64_t i = base + u * kWave + lane;
+      k[u] = i < hi ? keys[i] : kDeadKey;
+      v[u] = k[u] != kDeadKey ? vals[i] : VgradRec{0u, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kSortUnroll; ++u) {
+      const bool live = k[u] != kDeadKey;
+      const uint32_t d = (k[u] >> shift) & (kDigits - 1);
+      uint64_t peers = __ballot(live);  // live lanes with the same digit
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const bool set = (d >> bit) & 1u;
+        const uint64_t m = __ballot(set);
+        peers &= set ? m : ~m;
+      }
+      if (live) {
+        const uint32_t pos = cur[wave][d] + (uint32_t)__popcll(peers & below);
+        __builtin_amdgcn_raw_buffer_store_b32(k[u], okeys, pos * (uint32_t)sizeof(uint32_t), 0, 0);
+        const u32x4 pv = {v[u].src, __float_as_uint(v[u].alpha), __float_as_uint(v[u].fx), __float_as_uint(v[u].fy)};
+        __builtin_amdgcn_raw_buffer_store_b128(pv, ovals, pos * (uint32_t)sizeof(VgradRec), 0, 0);
+      }
+      wave_lds_sync();  // every lane has read its digit's position
+      if (live && (peers & below) == 0ull) cur[wave][d] += (uint32_t)__popcll(peers);
+      wave_lds_sync();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// key ranges and value rows
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void vgrad_clear_ranges_kernel(VgradArgs a) {
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < a.key_bound;
+       k += (int64_t)gridDim.x * blockDim.x)
+    a.ranges[k] = make_int2(0, 0);
+}
+
+__global__ __launch_bounds__(256) void vgrad_ranges_kernel(VgradArgs a, int buf) {
+  const uint32_t* keys = a.keys[buf];
+  const int64_t n = uniform(a.state->n_live);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t k = keys[i];
+    if ((int64_t)k >= a.key_bound) continue;
+    if (i == 0 || keys[i - 1] != k) a.ranges[k].x = (int)i;
+    if (i == n - 1 || keys[i + 1] != k) a.ranges[k].y = (int)(i + 1);
+  }
+}
+
+__global__ __launch_bounds__(256) void vgrad_rows_kernel(VgradArgs a, int buf) {
+  __shared__ Level lv[kMaxLevels];
+  __shared__ long long ext[kMaxLevels + 1];
+  load_levels(a.shapes, a.starts, a.L, lv);
+  load_corner_starts(lv, a.L, ext);
+  const int j = threadIdx.x % 8;
+  const int64_t groups = (int64_t)gridDim.x * blockDim.x / 8;
+  const int64_t per_image = (int64_t)a.Nv * a.nH;
+  const int64_t rows = a.images * per_image;
+  const long long next = ext[a.L];
+  const bool poisoned = uniform(a.state->status) != 0;
+  const VgradRec* vals = a.vals[buf];
+  const auto grad = make_rsrc(a.grad_out, a.grad_out_bytes);
+  for (int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 8; row < rows; row += groups) {
+    const int64_t image = row / per_image;
+    const int64_t rem = row - image * per_image;
+    const int pix = (int)(rem / a.nH), h = (int)(rem - (int64_t)(rem / a.nH) * a.nH);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int l = 0; l < a.L; ++l) {
+      const Level L = lv[l];
+      const long long off = (long long)pix - L.start;
+      if (L.W <= 0 || off < 0 || off >= (long long)L.W * L.H) continue;
+      const int y = (int)(off / L.W), x = (int)(off - (long long)y * L.W);
+      int2 r[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint64_t key = corner_key(image, next, ext[l], L.W, x + 1 - (c & 1), y + 1 - (c >> 1), a.nH, h);
+        r[c] = key < (uint64_t)a.key_bound ? a.ranges[key] : make_int2(0, 0);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int dx = c & 1, dy = c >> 1;
+        for (int i0 = r[c].x; i0 < r[c].y; i0 += 8) {
+          const int cnt = min(8, r[c].y - i0);
+          const VgradRec mine = j < cnt ? vals[i0 + j] : VgradRec{0u, 0.f, 0.f, 0.f};
+          float coef[8];
+          float4 g[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const uint32_t src = (uint32_t)__shfl((int)mine.src, t, 8);
+            const float al = __shfl(mine.alpha, t, 8), fx = __shfl(mine.fx, t, 8), fy = __shfl(mine.fy, t, 8);
+            coef[t] = t < cnt ? al * (dx ? fx : 1.f - fx) * (dy ? fy : 1.f - fy) : 0.f;
+            const uint32_t at = t < cnt ? src * 128u + (uint32_t)j * 16u : kSkip;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(grad, at, 0, 0);
+            g[t] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                               __uint_as_float(v[3]));
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            acc.x = fmaf(coef[t], g[t].x, acc.x);
+            acc.y = fmaf(coef[t], g[t].y, acc.y);
+            acc.z = fmaf(coef[t], g[t].z, acc.z);
+            acc.w = fmaf(coef[t], g[t].w, acc.w);
+          }
+        }
+      }
+    }
+    if (poisoned) acc = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+    reinterpret_cast<float4*>(a.grad_value)[row * 8 + j] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static int vgrad_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+hipError_t launch_vgrad_setup(const VgradArgs& a, bool sca, hipStream_t stream) {
+  vgrad_setup_kernel<<<1, 256, 0, stream>>>(a, sca ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !sca || a.tiles == 0) return e;
+  vgrad_pair_of_kernel<<<dim3(a.tiles, a.B), kQueryTile, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
+  const unsigned sort_blocks = kSortWaves / (kSortBlock / kWave);
+  int src = 0;
+  for (int p = 0; p < a.passes; ++p) {
+    const int shift = 8 * p;
+    if (p == 0)
+      vgrad_hist_kernel<true><<<sort_blocks, kSortBlock, 0, stream>>>(a, src, shift);
+    else
+      vgrad_hist_kernel<false><<<sort_blocks, kSortBlock, 0, stream>>>(a, src, shift);
+    vgrad_scan_kernel<<<kDigits, kScanBlock, 0, stream>>>(a);
+    if (p == 0)
+      vgrad_scatter_kernel<true><<<sort_blocks, kSortBlock, 0, stream>>>(a, src, shift);
+    else
+      vgrad_scatter_kernel<false><<<sort_blocks, kSortBlock, 0, stream>>>(a, src, shift);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    src ^= 1;
+  }
+  const int64_t cap = (int64_t)vgrad_cus() * 8;
+  int64_t blocks = (a.key_bound + 255) / 256;
+  vgrad_clear_ranges_kernel<<<(unsigned)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap), 256, 0, stream>>>(a);
+  vgrad_ranges_kernel<<<(unsigned)cap, 256, 0, stream>>>(a, src);
+  const int64_t rows = a.images * (int64_t)a.Nv * a.nH;
+  blocks = (rows + 31) / 32;  // 32 rows per block of 256 threads
+  const int64_t row_cap = (int64_t)vgrad_cus() * 16;
+  vgrad_rows_kernel<<<(unsigned)(blocks < row_cap ? (blocks > 0 ? blocks : 1) : row_cap), 256, 0, stream>>>(a, src);
+  return hipGetLastError();
+}
+
+}  // namespace msda

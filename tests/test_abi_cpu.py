@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["msda_forward", "msda_forward_frames", "sca_workspace_size", "sca_forward", "msda_gemm_bf16",
               "msda_query_proj_bf16", "msda_output_proj_bf16", "sca_rebatch", "sca_scatter_mean",
-              "msda_backward", "sca_backward",
+              "msda_backward", "sca_backward", "msda_backward_workspace_size", "sca_backward_workspace_size",
               "msda_status_string", "msda_last_error"]:
         assert n in names, n
 
@@ -250,8 +250,15 @@ def test_scatter_mean_rejects(lib, kw, code):
 
 
 def _mb(lib, value=A, dtype=0, ss=A, st=A, loc=A, w=A, mode=1, go=A, B=1, Nv=16, Nq=4, nH=8, Dh=32, L=1, P=4,
-        gv=B_, gl=B_, gw=B_):
-    return lib.msda_backward(value, dtype, ss, st, loc, w, mode, go, B, Nv, Nq, nH, Dh, L, P, gv, gl, gw, None)
+        gv=B_, gl=B_, gw=B_, gws=None, gws_bytes=0):
+    return lib.msda_backward(value, dtype, ss, st, loc, w, mode, go, B, Nv, Nq, nH, Dh, L, P, gv, gl, gw, gws,
+                             gws_bytes, None)
+
+
+def _mb_ws(lib, B=1, Nv=16, Nq=4, nH=8, L=1, P=4):
+    n = _sz(0)
+    rc = lib.msda_backward_workspace_size(B, Nv, Nq, nH, L, P, ctypes.byref(n))
+    return rc, n.value
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -269,16 +276,49 @@ def test_msda_backward_rejects(lib, kw, code):
     assert _mb(lib, **kw) == code
 
 
+def test_backward_workspace_sizes(lib):
+    """Gradient workspace sizes: about 40 bytes per sample slot plus 8 per cell
+    key, growing with every size; invalid or oversized requests are refused."""
+    rc, small = _mb_ws(lib)
+    assert rc == OK and small > 2 * 4 * 4 * 8 * 40
+    rc, more_q = _mb_ws(lib, Nq=400)
+    assert rc == OK and more_q - small >= 396 * 8 * 4 * 40
+    rc, more_v = _mb_ws(lib, Nv=1600)
+    assert rc == OK and more_v - small >= (2 * 1600 - 2 * 16) * 8 * 8
+    assert _mb_ws(lib, B=0)[0] == INVALID
+    assert _mb_ws(lib, Nq=1 << 26)[0] == UNSUPPORTED  # 2^26 * 32 sample records
+    n = _sz(0)
+    assert lib.msda_backward_workspace_size(1, 16, 4, 8, 1, 4, None) == INVALID
+    assert lib.sca_backward_workspace_size(1, 6, 16, 4, 8, 1, 4, 0, ctypes.byref(n)) == OK
+    every = n.value
+    assert lib.sca_backward_workspace_size(1, 6, 16, 4, 8, 1, 4, 5, ctypes.byref(n)) == OK
+    assert every - n.value >= (24 - 5) * 8 * 4 * 40 - 4 * 256  # 24 pairs at most; buffers 256-aligned
+    assert lib.sca_backward_workspace_size(1, 33, 16, 4, 8, 1, 4, 0, ctypes.byref(n)) == UNSUPPORTED
+
+
+def test_msda_backward_rejects_small_gradient_workspace(lib):
+    rc, need = _mb_ws(lib)
+    assert rc == OK
+    assert _mb(lib, gws=A, gws_bytes=need - 1) == WORKSPACE
+    assert _mb(lib, gws=A + 16, gws_bytes=need) == WORKSPACE  # not 256-byte aligned
+
+
 def test_sca_backward_rejects(lib):
     n = _sz(0)
     assert lib.sca_workspace_size(1, 6, 16, ctypes.byref(n)) == OK
     b = lib.sca_backward
-    args = [A, 0, A, A, A, A, A, A, 1, 6, 16, 8, 8, 32, 1, 8, 4, B_, B_, B_, A, n.value, None]
+    args = [A, 0, A, A, A, A, A, A, 1, 6, 16, 8, 8, 32, 1, 8, 4, B_, B_, B_, A, n.value, 0, None, 0, None]
     assert b(*args[:17], None, *args[18:]) == INVALID                 # grad_value
     assert b(*args[:16], 6, *args[17:]) == SHAPE                      # P % D
     assert b(*args[:20], None, *args[21:]) == WORKSPACE               # workspace
     assert b(*args[:9], 33, *args[10:]) == UNSUPPORTED                # cameras
     assert b(*args[:7], None, *args[8:]) == INVALID                   # grad_slots
+    g = _sz(0)
+    assert lib.sca_backward_workspace_size(1, 6, 16, 8, 8, 1, 8, 0, ctypes.byref(g)) == OK
+    assert b(*args[:23], A, g.value - 1, None) == WORKSPACE           # gradient workspace too small
+    assert lib.sca_backward_workspace_size(1, 6, 16, 8, 8, 1, 8, 3, ctypes.byref(g)) == OK
+    assert b(*args[:22], 3, A, g.value - 1, None) == WORKSPACE        # ... sized for max_pairs = 3
+
 
 
 def test_binding_refuses_cpu_tensors():

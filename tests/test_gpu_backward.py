@@ -6,12 +6,13 @@ size and the forward tests' edge cases).  Every call goes through the C ABI
 Tolerance: the float32 bar of the forward tests (1e-5 relative plus 1e-5 of
 the output's rms) for the location / offset and weight / logit gradients.
 The value gradient sums each row's contributions from every sample that
-touches it (up to ~10^3 in the BEVFormer-base SCA workload's coarse levels) with float32 atomics
-in no fixed order, so its bar is 1e-5 of the sum of the contributions'
-magnitudes plus 1e-5 of that sum's rms over the elements (gpu_util explains
-the rms term); the oracle gives the sum exactly: contributions are
-alpha * w * g with alpha, w >= 0, so the oracle's value gradient for |g| is
-that sum."""
+touches it (up to ~10^3 in the BEVFormer-base SCA workload's coarse levels)
+in float32 -- in a fixed order by the transpose gather (the default), in no
+fixed order with atomics -- so its bar is 1e-5 of the sum of the
+contributions' magnitudes plus 1e-5 of that sum's rms over the elements
+(gpu_util explains the rms term); the oracle gives the sum exactly:
+contributions are alpha * w * g with alpha, w >= 0, so the oracle's value
+gradient for |g| is that sum."""
 import numpy as np
 import pytest
 import torch
@@ -37,11 +38,11 @@ def _grad_out(seed, B, Nq, C):
     return np.random.default_rng(seed).normal(size=(B, Nq, C)).astype(np.float32)
 
 
-def check_msda_backward(w, gout, logits, what):
+def check_msda_backward(w, gout, logits, what, atomic=False):
     mode = msda.MSDA_WEIGHTS_LOGITS if logits else msda.MSDA_WEIGHTS_PROB
     gv, gl, gw = msda.msda_backward(dev(w["value"]), dev(w["spatial_shapes"]), dev(w["level_start_index"]),
                                     dev(w["sampling_locations"]), dev(w["attention_weights"]), dev(gout),
-                                    weight_mode=mode)
+                                    weight_mode=mode, atomic=atomic)
     rv, rl, rw = oracle.msda_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
                                       w["sampling_locations"], w["attention_weights"], gout, weights_are_logits=logits)
     mag, _, _ = oracle.msda_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
@@ -73,6 +74,13 @@ def test_detr_encoder_msda_backward_full():
     check_msda_backward(w, gout, True, "DETR encoder")
 
 
+def test_detr_encoder_msda_backward_atomic():
+    """The same with the value gradient accumulated by float32 atomics."""
+    w = W.detr_encoder_msda()
+    gout = W.upstream_gradient(2, (w["B"], w["Nq"], 256))
+    check_msda_backward(w, gout, True, "DETR encoder, atomics", atomic=True)
+
+
 @pytest.mark.parametrize("case", MSDA_EDGE, ids=[c[0] for c in MSDA_EDGE])
 def test_msda_backward_edge_cases(case):
     _, seed, B, Nq, shapes, nH, P = case
@@ -83,39 +91,52 @@ def test_msda_backward_edge_cases(case):
     check_msda_backward(dict(w, attention_weights=probs), gout, False, case[0] + " probabilities")
 
 
-def test_msda_backward_empty_query_set():
+@pytest.mark.parametrize("atomic", [False, True], ids=["gather", "atomic"])
+def test_msda_backward_empty_query_set(atomic):
     """No queries: the value gradient is zero (overwritten), nothing else is touched."""
     w = _rand_msda(5, 1, 0, ((4, 4),), 8, 4)
     gv = torch.full((1, w["Nv"], 8, 32), float("nan"), device="cuda")
     empty = torch.empty(0, device="cuda")
     gv, _, _ = msda.msda_backward(dev(w["value"]), dev(w["spatial_shapes"]), dev(w["level_start_index"]),
                                   dev(w["sampling_locations"]), dev(w["attention_weights"]), empty.view(1, 0, 256),
-                                  grad_value=gv)
+                                  grad_value=gv, atomic=atomic)
     assert not host(gv).any()
 
 
 def test_msda_backward_repeatable():
-    """Locations and weights gradients are written once each: bitwise equal
-    over two runs; the atomically accumulated value gradient agrees to the
-    float32 bar."""
+    """With the transpose gather every output, the value gradient included, is
+    the same bit for bit over two runs (one of them into a workspace full of
+    stale records from a different call); with atomics the locations and
+    weights gradients still are, and the value gradient agrees to the float32
+    bar."""
     w = _rand_msda(6, 2, 300, ((16, 24), (8, 12)), 8, 4)
     gout = _grad_out(7, 2, 300, 256)
     args = (dev(w["value"]), dev(w["spatial_shapes"]), dev(w["level_start_index"]), dev(w["sampling_locations"]),
             dev(w["attention_weights"]), dev(gout))
-    a = [host(t) for t in msda.msda_backward(*args)]
-    b = [host(t) for t in msda.msda_backward(*args)]
-    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+    ws = torch.empty(msda.msda_backward_workspace_size(2, w["Nv"], 300, 8, 2, 4), dtype=torch.uint8, device="cuda")
+    a = [host(t) for t in msda.msda_backward(*args, grad_workspace=ws)]
+    other = _rand_msda(16, 2, 300, ((16, 24), (8, 12)), 8, 4)
+    msda.msda_backward(dev(other["value"]), *args[1:3], dev(other["sampling_locations"]),
+                       dev(other["attention_weights"]), args[5], grad_workspace=ws)
+    b = [host(t) for t in msda.msda_backward(*args, grad_workspace=ws)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    c = [host(t) for t in msda.msda_backward(*args, atomic=True)]
+    d = [host(t) for t in msda.msda_backward(*args, atomic=True)]
+    assert np.array_equal(c[1], d[1]) and np.array_equal(c[2], d[2])
+    assert np.array_equal(a[1], c[1]) and np.array_equal(a[2], c[2])
     mag, _, _ = oracle.msda_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
                                      w["sampling_locations"], w["attention_weights"], np.abs(gout),
                                      weights_are_logits=True)
-    assert_sum_close(a[0], b[0], 2 * mag, "value gradient, two runs")
+    assert_sum_close(c[0], d[0], 2 * mag, "value gradient with atomics, two runs")
+    assert_sum_close(a[0], c[0], 2 * mag, "value gradient, gather against atomics")
 
 
 # ---------------------------------------------------------------------------
 # SCA
 # ---------------------------------------------------------------------------
 
-def run_sca_backward(w, gout):
+def run_sca_backward(w, gout, **kw):
     B, Ncam, Nq = w["B"], w["Ncam"], w["Nq"]
     ws = torch.empty(msda.sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device="cuda")
     msda.sca_compact(dev(w["bev_mask"]), dev(w["reference_points_cam"]), ws)
@@ -123,12 +144,12 @@ def run_sca_backward(w, gout):
     gl = torch.full((B, Nq, w["nH"], w["L"] * w["P"]), float("nan"), device="cuda")
     gv, go, gl = msda.sca_backward(dev(w["value"]), dev(w["spatial_shapes"]), dev(w["level_start_index"]),
                                    dev(w["reference_points_cam"]), dev(w["sampling_offsets"]),
-                                   dev(w["attention_logits"]), dev(gout), ws, grad_offsets=go, grad_logits=gl)
+                                   dev(w["attention_logits"]), dev(gout), ws, grad_offsets=go, grad_logits=gl, **kw)
     return host(gv), host(go), host(gl)
 
 
-def check_sca_backward(w, gout, what):
-    gv, go, gl = run_sca_backward(w, gout)
+def check_sca_backward(w, gout, what, **kw):
+    gv, go, gl = run_sca_backward(w, gout, **kw)
     rv, ro, rl = oracle.sca_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
                                      w["reference_points_cam"], w["bev_mask"], w["sampling_offsets"],
                                      w["attention_logits"], gout)
@@ -160,3 +181,41 @@ def test_sca_backward_edge_cases(case):
     w = _rand_sca(seed, B, Ncam, Nq, shapes, nH, P, D, pm)
     gout = _grad_out(seed + 200, B, Nq, nH * 32)
     check_sca_backward(w, gout, case[0])
+
+
+def test_bevformer_sca_backward_atomic():
+    """The full-size SCA workload with the value gradient accumulated by float32 atomics."""
+    w = W.bevformer_sca()
+    gout = W.upstream_gradient(3, (w["B"], w["Nq"], 256))
+    check_sca_backward(w, gout, "BEVFormer-base SCA, atomics", atomic=True)
+
+
+def _pair_count(w):
+    return int(w["bev_mask"].any(-1).sum())
+
+
+def test_sca_backward_repeatable_and_exact_capacity():
+    """A gradient workspace sized for exactly the pairs the compaction finds
+    gives the same bits as one sized for every camera seeing every query, and
+    two runs agree bit for bit."""
+    w = _rand_sca(61, 2, 6, 300, ((12, 20), (6, 10)), 8, 8, 4, 0.6)
+    gout = _grad_out(62, 2, 300, 256)
+    n = _pair_count(w)
+    a = run_sca_backward(w, gout)
+    b = run_sca_backward(w, gout, max_pairs=n)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    check_sca_backward(w, gout, "exact capacity", max_pairs=n)
+
+
+def test_sca_backward_too_few_pairs_gives_nan():
+    """A gradient workspace for fewer pairs than the compaction finds: the
+    value gradient is all NaN (the other outputs do not depend on it)."""
+    w = _rand_sca(63, 1, 6, 200, ((12, 20), (6, 10)), 8, 8, 4, 0.6)
+    gout = _grad_out(64, 1, 200, 256)
+    n = _pair_count(w)
+    assert n > 1
+    gv, go, gl = run_sca_backward(w, gout, max_pairs=n - 1)
+    assert np.isnan(gv).all()
+    _, ro, rl = run_sca_backward(w, gout)
+    assert np.array_equal(go, ro) and np.array_equal(gl, rl)
