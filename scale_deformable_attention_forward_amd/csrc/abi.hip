@@ -485,6 +485,7 @@ static msda::VgradArgs vgrad_args(const msda::VgradLayout& lay, void* workspace,
   v.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
   v.digit_totals = reinterpret_cast<uint32_t*>(ws + lay.digit_totals);
   v.ranges = reinterpret_cast<int2*>(ws + lay.ranges);
+  v.long_row = reinterpret_cast<uint8_t*>(ws + lay.long_row);
   v.state = reinterpret_cast<msda::VgradState*>(ws + lay.state);
   v.pair_of = reinterpret_cast<int32_t*>(ws + lay.pair_of);
   v.slots = lay.slots;

@@ -21,8 +21,10 @@
 //   3. the (first, end) range of every key is recorded;
 //   4. one 8-lane group per value row (pixel (x, y) of level l, head h)
 //      sums, for the corners (dx, dy) = (0,0), (1,0), (0,1), (1,1) in turn,
-//      the records of key (x + 1 - dx, y + 1 - dy) in sorted order, and
-//      writes the row once.
+//      the records of key (x + 1 - dx, y + 1 - dy) in sorted order (the four
+//      lists walked as one sequence, 8 records per step, the next step's
+//      records loading with this step's gradient rows), and writes the row
+//      once.
 // The order of every sum is fixed by the slots, so grad_value is the same
 // bit for bit from run to run.
 #include "common.hpp"
@@ -42,7 +44,7 @@ VgradLayout vgrad_layout(int64_t images, int64_t Nv, int L, int nH, int64_t slot
   l.key_bound = images * (2 * Nv + 2 * (int64_t)L) * nH;
   int bits = 1;
   while (bits < 62 && ((int64_t)1 << bits) < l.key_bound) ++bits;
-  l.passes = (bits + 7) / 8;
+  l.passes = (bits + kDigitBits - 1) / kDigitBits;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -56,6 +58,7 @@ VgradLayout vgrad_layout(int64_t images, int64_t Nv, int L, int nH, int64_t slot
   l.counts = take(sizeof(uint32_t) * (size_t)kDigits * kSortWaves);
   l.digit_totals = take(sizeof(uint32_t) * kDigits);
   l.ranges = take(sizeof(int2) * (size_t)l.key_bound);
+  l.long_row = take((size_t)images * (size_t)Nv * (size_t)nH);
   l.pair_of = take(sizeof(int32_t) * (size_t)pair_of_entries);
   l.state = take(sizeof(VgradState));
   l.total = o;
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
   const int64_t n = uniform(kFirst ? a.state->n_items : a.state->n_live);
   int64_t lo, hi;
   wave_range(n, w, &lo, &hi);
-  // digit bases: exclusive scan of the 256 digit totals, 4 digits per lane
+  // digit bases: exclusive scan of the digit totals, kDigits / 64 per lane
   uint32_t tot[kDigits / kWave], s = 0;
 #pragma unroll
   for (int u = 0; u < kDigits / kWave; ++u) {
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
       const uint32_t d = (k[u] >> shift) & (kDigits - 1);
       uint64_t peers = __ballot(live);  // live lanes with the same digit
 #pragma unroll
-      for (int bit = 0; bit < 8; ++bit) {
+      for (int bit = 0; bit < kDigitBits; ++bit) {
         const bool set = (d >> bit) & 1u;
         const uint64_t m = __ballot(set);
         peers &= set ? m : ~m;
@@ -293,65 +296,178 @@ __global__ __launch_bounds__(256) void vgrad_ranges_kernel(VgradArgs a, int buf)
   }
 }
 
+// The four corner lists of a value row at one level, walked as one sequence:
+// record i is list c's (i - p[c])-th, p[0] = 0.
+struct RowLists {
+  int2 r[4];
+  int p1, p2, p3, T;
+};
+
+__device__ inline RowLists row_lists(const VgradArgs& a, const long long* ext, int l, int W, int64_t image, int x,
+                                     int y, int h) {
+  RowLists s;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint64_t key = corner_key(image, ext[a.L], ext[l], W, x + 1 - (c & 1), y + 1 - (c >> 1), a.nH, h);
+    s.r[c] = key < (uint64_t)a.key_bound ? a.ranges[key] : make_int2(0, 0);
+  }
+  s.p1 = s.r[0].y - s.r[0].x;
+  s.p2 = s.p1 + s.r[1].y - s.r[1].x;
+  s.p3 = s.p2 + s.r[2].y - s.r[2].x;
+  s.T = s.p3 + s.r[3].y - s.r[3].x;
+  return s;
+}
+
+// Sum of alpha * w_c * g over the records [b, min(b + 8, i1)) of the
+// sequence for b = i0, i0 + step, ... < i1, for the 8-lane group (lane j:
+// channels 4j..4j+3): lane j loads record b + j (the next step's records
+// load while this step's gradient rows do), the group shares (source row,
+// coefficient), and every lane adds its 4 channels of the rows in record
+// order.
+__device__ inline float4 sum_records(const RowLists& s, int i0, int i1, int step, const VgradRec* __restrict__ vals,
+                                     __amdgpu_buffer_rsrc_t grad, int j) {
+  auto fetch = [&](int i, VgradRec& rec, int& c) {
+    c = (i >= s.p1) + (i >= s.p2) + (i >= s.p3);
+    const int at = c == 0 ? s.r[0].x + i : (c == 1 ? s.r[1].x + i - s.p1 : (c == 2 ? s.r[2].x + i - s.p2 : s.r[3].x + i - s.p3));
+    rec = i < i1 ? vals[at] : VgradRec{0u, 0.f, 0.f, 0.f};  // (a step never reaches past b + 8)
+  };
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  VgradRec cur;
+  int ccur;
+  fetch(i0 + j, cur, ccur);
+  for (int b = i0; b < i1; b += step) {
+    // the coefficient of corner c: alpha * (dx ? fx : 1 - fx) * (dy ? fy : 1 - fy)
+    const float wx = (ccur & 1) ? cur.fx : 1.f - cur.fx, wy = (ccur >> 1) ? cur.fy : 1.f - cur.fy;
+    const float coef_mine = b + j < i1 ? cur.alpha * wx * wy : 0.f;
+    const uint32_t src_mine = cur.src;
+    VgradRec nxt;
+    int cn;
+    fetch(b + step + j, nxt, cn);
+    float coef[8];
+    float4 g[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t src = (uint32_t)__shfl((int)src_mine, t, 8);
+      coef[t] = __shfl(coef_mine, t, 8);
+      const uint32_t at = b + t < i1 ? src * 128u + (uint32_t)j * 16u : kSkip;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(grad, at, 0, 0);
+      g[t] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc.x = fmaf(coef[t], g[t].x, acc.x);
+      acc.y = fmaf(coef[t], g[t].y, acc.y);
+      acc.z = fmaf(coef[t], g[t].z, acc.z);
+      acc.w = fmaf(coef[t], g[t].w, acc.w);
+    }
+    cur = nxt;
+    ccur = cn;
+  }
+  return acc;
+}
+
+// Level, pixel and head of value row `row`; returns false for a row no level covers.
+struct RowPlace {
+  int64_t image;
+  int pix, h;
+};
+__device__ inline RowPlace row_place(int64_t row, int Nv, int nH) {
+  RowPlace p;
+  const int64_t per_image = (int64_t)Nv * nH;
+  p.image = row / per_image;
+  const int rem = (int)(row - p.image * per_image);
+  p.pix = rem / nH;
+  p.h = rem - p.pix * nH;
+  return p;
+}
+
+// One 8-lane group per row: the first kRowChunk records of each of its level
+// sequences; a row with more (at some level) is flagged for the long-row pass,
+// which adds the rest.  Rows are split by die (block i runs on die i % 8): die
+// x takes the contiguous eighth x of the rows, so the upstream-gradient rows
+// its records read (neighbouring queries) share its L2.
 __global__ __launch_bounds__(256) void vgrad_rows_kernel(VgradArgs a, int buf) {
   __shared__ Level lv[kMaxLevels];
   __shared__ long long ext[kMaxLevels + 1];
   load_levels(a.shapes, a.starts, a.L, lv);
   load_corner_starts(lv, a.L, ext);
   const int j = threadIdx.x % 8;
-  const int64_t groups = (int64_t)gridDim.x * blockDim.x / 8;
-  const int64_t per_image = (int64_t)a.Nv * a.nH;
-  const int64_t rows = a.images * per_image;
-  const long long next = ext[a.L];
+  const int64_t rows = a.images * (int64_t)a.Nv * a.nH;
+  const int die = blockIdx.x % kXcds, local = blockIdx.x / kXcds, nlocal = gridDim.x / kXcds;
+  const int64_t lo = rows * die / kXcds, hi = rows * (die + 1) / kXcds;
+  const int64_t stride = (int64_t)nlocal * (blockDim.x / 8);
   const bool poisoned = uniform(a.state->status) != 0;
   const VgradRec* vals = a.vals[buf];
   const auto grad = make_rsrc(a.grad_out, a.grad_out_bytes);
-  for (int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 8; row < rows; row += groups) {
-    const int64_t image = row / per_image;
-    const int64_t rem = row - image * per_image;
-    const int pix = (int)(rem / a.nH), h = (int)(rem - (int64_t)(rem / a.nH) * a.nH);
+  for (int64_t row = lo + (int64_t)local * (blockDim.x / 8) + threadIdx.x / 8; row < hi; row += stride) {
+    const RowPlace pl = row_place(row, a.Nv, a.nH);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool more = false;
     for (int l = 0; l < a.L; ++l) {
       const Level L = lv[l];
-      const long long off = (long long)pix - L.start;
+      const long long off = (long long)pl.pix - L.start;
       if (L.W <= 0 || off < 0 || off >= (long long)L.W * L.H) continue;
       const int y = (int)(off / L.W), x = (int)(off - (long long)y * L.W);
-      int2 r[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint64_t key = corner_key(image, next, ext[l], L.W, x + 1 - (c & 1), y + 1 - (c >> 1), a.nH, h);
-        r[c] = key < (uint64_t)a.key_bound ? a.ranges[key] : make_int2(0, 0);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int dx = c & 1, dy = c >> 1;
-        for (int i0 = r[c].x; i0 < r[c].y; i0 += 8) {
-          const int cnt = min(8, r[c].y - i0);
-          const VgradRec mine = j < cnt ? vals[i0 + j] : VgradRec{0u, 0.f, 0.f, 0.f};
-          float coef[8];
-          float4 g[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const uint32_t src = (uint32_t)__shfl((int)mine.src, t, 8);
-            const float al = __shfl(mine.alpha, t, 8), fx = __shfl(mine.fx, t, 8), fy = __shfl(mine.fy, t, 8);
-            coef[t] = t < cnt ? al * (dx ? fx : 1.f - fx) * (dy ? fy : 1.f - fy) : 0.f;
-            const uint32_t at = t < cnt ? src * 128u + (uint32_t)j * 16u : kSkip;
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(grad, at, 0, 0);
-            g[t] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
-                               __uint_as_float(v[3]));
-          }
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            acc.x = fmaf(coef[t], g[t].x, acc.x);
-            acc.y = fmaf(coef[t], g[t].y, acc.y);
-            acc.z = fmaf(coef[t], g[t].z, acc.z);
-            acc.w = fmaf(coef[t], g[t].w, acc.w);
-          }
-        }
-      }
+      const RowLists s = row_lists(a, ext, l, L.W, pl.image, x, y, pl.h);
+      const float4 part = sum_records(s, 0, min(s.T, kRowChunk), 8, vals, grad, j);
+      acc = make_float4(acc.x + part.x, acc.y + part.y, acc.z + part.z, acc.w + part.w);
+      more |= s.T > kRowChunk;
     }
     if (poisoned) acc = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
     reinterpret_cast<float4*>(a.grad_value)[row * 8 + j] = acc;
+    if (j == 0) a.long_row[row] = more ? 1 : 0;
+  }
+}
+
+// Rows flagged by vgrad_rows_kernel: one wave per row at a time, its 8 groups
+// taking the 8-record steps after the first kRowChunk records in turn (group
+// g the steps g, g + 8, ...), summed across the groups in a fixed pairwise
+// order and added to the first kRowChunk records' sum.  Wave w looks at the rows
+// w, w + waves, ... (64 flags per look), so the consecutive long rows of a
+// coarse level spread over all waves.
+__global__ __launch_bounds__(256) void vgrad_long_rows_kernel(VgradArgs a, int buf) {
+  __shared__ Level lv[kMaxLevels];
+  __shared__ long long ext[kMaxLevels + 1];
+  load_levels(a.shapes, a.starts, a.L, lv);
+  load_corner_starts(lv, a.L, ext);
+  if (uniform(a.state->status) != 0) return;  // every row is NaN already
+  const int lane = threadIdx.x % kWave, g = lane / 8, j = lane % 8;
+  const int64_t rows = a.images * (int64_t)a.Nv * a.nH;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const int64_t w = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const VgradRec* vals = a.vals[buf];
+  const auto grad = make_rsrc(a.grad_out, a.grad_out_bytes);
+  for (int64_t base = w; base < rows; base += waves * kWave) {
+    const int64_t mine = base + (int64_t)lane * waves;
+    uint64_t todo = __ballot(mine < rows && a.long_row[mine] != 0);
+    while (todo) {
+      const int who = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int64_t row = base + (int64_t)who * waves;
+      const RowPlace pl = row_place(row, a.Nv, a.nH);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int l = 0; l < a.L; ++l) {
+        const Level L = lv[l];
+        const long long off = (long long)pl.pix - L.start;
+        if (L.W <= 0 || off < 0 || off >= (long long)L.W * L.H) continue;
+        const int y = (int)(off / L.W), x = (int)(off - (long long)y * L.W);
+        const RowLists s = row_lists(a, ext, l, L.W, pl.image, x, y, pl.h);
+        const float4 part = sum_records(s, kRowChunk + 8 * g, s.T, 64, vals, grad, j);
+        acc = make_float4(acc.x + part.x, acc.y + part.y, acc.z + part.z, acc.w + part.w);
+      }
+#pragma unroll
+      for (int d = 8; d < kWave; d <<= 1) {  // groups (0+1), (2+3), ..., then pairs of those
+        acc.x += __shfl_xor(acc.x, d);
+        acc.y += __shfl_xor(acc.y, d);
+        acc.z += __shfl_xor(acc.z, d);
+        acc.w += __shfl_xor(acc.w, d);
+      }
+      if (g == 0) {
+        float4* out = reinterpret_cast<float4*>(a.grad_value) + row * 8 + j;
+        const float4 first = *out;
+        *out = make_float4(first.x + acc.x, first.y + acc.y, first.z + acc.z, first.w + acc.w);
+      }
+    }
   }
 }
 
@@ -383,7 +499,7 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
   const unsigned sort_blocks = kSortWaves / (kSortBlock / kWave);
   int src = 0;
   for (int p = 0; p < a.passes; ++p) {
-    const int shift = 8 * p;
+    const int shift = kDigitBits * p;
     if (p == 0)
       vgrad_hist_kernel<true><<<sort_blocks, kSortBlock, 0, stream>>>(a, src, shift);
     else
@@ -404,7 +520,10 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
   const int64_t rows = a.images * (int64_t)a.Nv * a.nH;
   blocks = (rows + 31) / 32;  // 32 rows per block of 256 threads
   const int64_t row_cap = (int64_t)vgrad_cus() * 16;
-  vgrad_rows_kernel<<<(unsigned)(blocks < row_cap ? (blocks > 0 ? blocks : 1) : row_cap), 256, 0, stream>>>(a, src);
+  blocks = blocks < row_cap ? blocks : row_cap;
+  blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // a multiple of the die count
+  vgrad_rows_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a, src);
+  vgrad_long_rows_kernel<<<(unsigned)(vgrad_cus() * 8), 256, 0, stream>>>(a, src);
   return hipGetLastError();
 }
 

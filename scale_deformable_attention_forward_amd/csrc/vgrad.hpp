@@ -14,7 +14,9 @@ namespace msda {
 
 constexpr uint32_t kDeadKey = 0xffffffffu;  // a sample with no corner inside its map
 constexpr int kSortWaves = 2048;            // waves of a sort pass, each owning a contiguous range
-constexpr int kDigits = 256;                // 8 key bits per pass
+constexpr int kDigitBits = 8;               // key bits per sort pass
+constexpr int kDigits = 1 << kDigitBits;
+constexpr int kRowChunk = 128;              // records of a value row the first pass sums (one 8-lane group)
 
 // Payload of a sample record: the upstream gradient row it scales (b*Nq + q)*nH + h,
 // its attention weight (for SCA divided by the query's hit count) and its
@@ -39,10 +41,10 @@ struct VgradState {
 // counts, per-key ranges of the sorted records, the SCA pair index of each
 // (camera, query) and the state.
 struct VgradLayout {
-  size_t keys[2], vals[2], counts, digit_totals, ranges, pair_of, state, total;
+  size_t keys[2], vals[2], counts, digit_totals, ranges, long_row, pair_of, state, total;
   int64_t slots;      // record capacity
   int64_t key_bound;  // keys are below this
-  int passes;         // 8-bit digit passes covering key_bound - 1
+  int passes;         // kDigitBits-bit digit passes covering key_bound - 1
 };
 // images: B (MSDA) or B*Ncam (SCA); pair_of_entries: Ncam*B*Nq (SCA) or 0
 VgradLayout vgrad_layout(int64_t images, int64_t Nv, int L, int nH, int64_t slots, int64_t pair_of_entries);
@@ -54,6 +56,7 @@ struct VgradArgs {
   uint32_t* counts;        // [kDigits][kSortWaves]
   uint32_t* digit_totals;  // [kDigits]
   int2* ranges;            // [key_bound] (first, end) of each key's records
+  uint8_t* long_row;       // [images*Nv*nH] rows with more than kRowChunk records at a level
   VgradState* state;
   int64_t slots, key_bound;
   int passes;
