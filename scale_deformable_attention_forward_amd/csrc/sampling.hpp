@@ -25,15 +25,25 @@ struct Level {
 // rounding error of (k + 1/2) * inv.
 __device__ inline int small_div(int k, float inv) { return (int)((k + 0.5f) * inv); }
 
+// Lane exchanges inside a group of 8 as DPP moves (VALU, no LDS traffic):
+// quad_perm(1,0,3,2) swaps lanes i and i^1, quad_perm(2,3,0,1) lanes i and
+// i^2, row_half_mirror lanes i and 7-i (which, once each quad holds one
+// value, is the other quad's).  All 8 lanes of a group are active together.
+template <int kCtrl>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1, kDppXor2 = 0x4e, kDppHalfMirror = 0x141;
+
 __device__ inline float group_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, 8));
-  v = fmaxf(v, __shfl_xor(v, 2, 8));
-  return fmaxf(v, __shfl_xor(v, 4, 8));
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  return fmaxf(v, dpp<kDppHalfMirror>(v));
 }
 __device__ inline float group_sum(float v) {
-  v += __shfl_xor(v, 1, 8);
-  v += __shfl_xor(v, 2, 8);
-  return v + __shfl_xor(v, 4, 8);
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  return v + dpp<kDppHalfMirror>(v);
 }
 
 // Weights of the samples k = j + 8i of one head: probabilities as given, or
