@@ -366,26 +366,31 @@ __device__ inline float4 sum_records(const RowLists& s, int i0, int i1, int step
   return acc;
 }
 
-// Level, pixel and head of value row `row`; returns false for a row no level covers.
+// The row passes visit value rows head-major: visit index r is (image, head,
+// pixel) = (r / (nH Nv), r / Nv % nH, r % Nv), the gradient row
+// (image * Nv + pixel) * nH + head.  Rows of one head read only that head's
+// upstream-gradient rows, so the rows a die works on at a time need about
+// (queries seeing one camera) x 128 bytes of them: they stay in its L2.
 struct RowPlace {
-  int64_t image;
+  int64_t image, row;
   int pix, h;
 };
-__device__ inline RowPlace row_place(int64_t row, int Nv, int nH) {
+__device__ inline RowPlace row_place(int64_t r, int Nv, int nH) {
   RowPlace p;
   const int64_t per_image = (int64_t)Nv * nH;
-  p.image = row / per_image;
-  const int rem = (int)(row - p.image * per_image);
-  p.pix = rem / nH;
-  p.h = rem - p.pix * nH;
+  p.image = r / per_image;
+  const int rem = (int)(r - p.image * per_image);
+  p.h = rem / Nv;
+  p.pix = rem - p.h * Nv;
+  p.row = (p.image * Nv + p.pix) * nH + p.h;
   return p;
 }
 
 // One 8-lane group per row: the first kRowChunk records of each of its level
 // sequences; a row with more (at some level) is flagged for the long-row pass,
 // which adds the rest.  Rows are split by die (block i runs on die i % 8): die
-// x takes the contiguous eighth x of the rows, so the upstream-gradient rows
-// its records read (neighbouring queries) share its L2.
+// x takes the contiguous eighth x of the visit order, so the upstream-gradient
+// rows its records read share its L2.
 __global__ __launch_bounds__(256) void vgrad_rows_kernel(VgradArgs a, int buf) {
   __shared__ Level lv[kMaxLevels];
   __shared__ long long ext[kMaxLevels + 1];
@@ -399,8 +404,8 @@ __global__ __launch_bounds__(256) void vgrad_rows_kernel(VgradArgs a, int buf) {
   const bool poisoned = uniform(a.state->status) != 0;
   const VgradRec* vals = a.vals[buf];
   const auto grad = make_rsrc(a.grad_out, a.grad_out_bytes);
-  for (int64_t row = lo + (int64_t)local * (blockDim.x / 8) + threadIdx.x / 8; row < hi; row += stride) {
-    const RowPlace pl = row_place(row, a.Nv, a.nH);
+  for (int64_t r = lo + (int64_t)local * (blockDim.x / 8) + threadIdx.x / 8; r < hi; r += stride) {
+    const RowPlace pl = row_place(r, a.Nv, a.nH);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     bool more = false;
     for (int l = 0; l < a.L; ++l) {
@@ -414,17 +419,18 @@ __global__ __launch_bounds__(256) void vgrad_rows_kernel(VgradArgs a, int buf) {
       more |= s.T > kRowChunk;
     }
     if (poisoned) acc = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
-    reinterpret_cast<float4*>(a.grad_value)[row * 8 + j] = acc;
-    if (j == 0) a.long_row[row] = more ? 1 : 0;
+    reinterpret_cast<float4*>(a.grad_value)[pl.row * 8 + j] = acc;
+    if (j == 0) a.long_row[r] = more ? 1 : 0;
   }
 }
 
 // Rows flagged by vgrad_rows_kernel: one wave per row at a time, its 8 groups
 // taking the 8-record steps after the first kRowChunk records in turn (group
 // g the steps g, g + 8, ...), summed across the groups in a fixed pairwise
-// order and added to the first kRowChunk records' sum.  Wave w looks at the rows
-// w, w + waves, ... (64 flags per look), so the consecutive long rows of a
-// coarse level spread over all waves.
+// order and added to the first kRowChunk records' sum.  Rows are split by
+// die as in vgrad_rows_kernel; inside a die, wave w looks at the rows
+// w, w + waves, ... of its eighth (64 flags per look), so the consecutive
+// long rows of a coarse level spread over the die's waves.
 __global__ __launch_bounds__(256) void vgrad_long_rows_kernel(VgradArgs a, int buf) {
   __shared__ Level lv[kMaxLevels];
   __shared__ long long ext[kMaxLevels + 1];
@@ -433,18 +439,19 @@ __global__ __launch_bounds__(256) void vgrad_long_rows_kernel(VgradArgs a, int b
   if (uniform(a.state->status) != 0) return;  // every row is NaN already
   const int lane = threadIdx.x % kWave, g = lane / 8, j = lane % 8;
   const int64_t rows = a.images * (int64_t)a.Nv * a.nH;
-  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  const int64_t w = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int die = blockIdx.x % kXcds, local = blockIdx.x / kXcds, nlocal = gridDim.x / kXcds;
+  const int64_t lo = rows * die / kXcds, hi = rows * (die + 1) / kXcds;
+  const int64_t waves = (int64_t)nlocal * (blockDim.x / kWave);
+  const int64_t w = (int64_t)local * (blockDim.x / kWave) + threadIdx.x / kWave;
   const VgradRec* vals = a.vals[buf];
   const auto grad = make_rsrc(a.grad_out, a.grad_out_bytes);
-  for (int64_t base = w; base < rows; base += waves * kWave) {
+  for (int64_t base = lo + w; base < hi; base += waves * kWave) {
     const int64_t mine = base + (int64_t)lane * waves;
-    uint64_t todo = __ballot(mine < rows && a.long_row[mine] != 0);
+    uint64_t todo = __ballot(mine < hi && a.long_row[mine] != 0);
     while (todo) {
       const int who = __builtin_ctzll(todo);
       todo &= todo - 1;
-      const int64_t row = base + (int64_t)who * waves;
-      const RowPlace pl = row_place(row, a.Nv, a.nH);
+      const RowPlace pl = row_place(base + (int64_t)who * waves, a.Nv, a.nH);
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int l = 0; l < a.L; ++l) {
         const Level L = lv[l];
@@ -463,7 +470,7 @@ __global__ __launch_bounds__(256) void vgrad_long_rows_kernel(VgradArgs a, int b
         acc.w += __shfl_xor(acc.w, d);
       }
       if (g == 0) {
-        float4* out = reinterpret_cast<float4*>(a.grad_value) + row * 8 + j;
+        float4* out = reinterpret_cast<float4*>(a.grad_value) + pl.row * 8 + j;
         const float4 first = *out;
         *out = make_float4(first.x + acc.x, first.y + acc.y, first.z + acc.z, first.w + acc.w);
       }
@@ -523,7 +530,7 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
   blocks = blocks < row_cap ? blocks : row_cap;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // a multiple of the die count
   vgrad_rows_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a, src);
-  vgrad_long_rows_kernel<<<(unsigned)(vgrad_cus() * 8), 256, 0, stream>>>(a, src);
+  vgrad_long_rows_kernel<<<(unsigned)((vgrad_cus() * 8 + kXcds - 1) / kXcds * kXcds), 256, 0, stream>>>(a, src);
   return hipGetLastError();
 }
 

@@ -219,3 +219,40 @@ def test_sca_backward_too_few_pairs_gives_nan():
     assert np.isnan(gv).all()
     _, ro, rl = run_sca_backward(w, gout)
     assert np.array_equal(go, ro) and np.array_equal(gl, rl)
+
+
+def _msda_with_levels(seed, Nq, shapes, starts, Nv, nH=8, P=4):
+    g = np.random.default_rng(seed)
+    ss = np.asarray(shapes, np.int64).reshape(-1, 2)
+    L = len(ss)
+    return {"value": g.normal(size=(1, Nv, nH, 32)).astype(np.float32), "spatial_shapes": ss,
+            "level_start_index": np.asarray(starts, np.int64),
+            "sampling_locations": g.uniform(-0.2, 1.2, (1, Nq, nH, L, P, 2)).astype(np.float32),
+            "attention_weights": g.normal(size=(1, Nq, nH, L * P)).astype(np.float32),
+            "B": 1, "Nq": Nq, "Nv": Nv, "nH": nH, "Dh": 32, "L": L, "P": P}
+
+
+def test_msda_backward_overlapping_levels():
+    """Levels whose rows overlap (level 1 reuses rows 4..7 of level 0): a value
+    row's gradient sums the samples of every level that reads it."""
+    w = _msda_with_levels(71, 60, ((4, 4), (2, 2)), (0, 4), 16)
+    gout = _grad_out(72, 1, 60, 256)
+    check_msda_backward(w, gout, True, "overlapping levels")
+
+
+def test_msda_backward_level_table_beyond_key_range():
+    """Four 2x2 levels on the same 4 rows: their cell corners (4 x 9) exceed the
+    2 Nv + 2 L keys the gradient workspace provides, so the transpose gather
+    fills grad_value with NaN; the atomic path and the other gradients are
+    unaffected."""
+    w = _msda_with_levels(73, 30, ((2, 2),) * 4, (0, 0, 0, 0), 4)
+    gout = _grad_out(74, 1, 30, 256)
+    args = (dev(w["value"]), dev(w["spatial_shapes"]), dev(w["level_start_index"]), dev(w["sampling_locations"]),
+            dev(w["attention_weights"]), dev(gout))
+    gv, gl, gw = (host(t) for t in msda.msda_backward(*args))
+    assert np.isnan(gv).all()
+    _, rl, rw = oracle.msda_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
+                                     w["sampling_locations"], w["attention_weights"], gout, weights_are_logits=True)
+    assert_fp32_close(gl, rl, "grad locations")
+    assert_fp32_close(gw, rw, "grad weights")
+    check_msda_backward(w, gout, True, "shared 2x2 levels, atomics", atomic=True)
