@@ -335,7 +335,8 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
 
 /* Bytes of msda_backward's gradient workspace (host; no device work).  About
  * 40 bytes per sample (B*Nq*nH*L*P) plus 8 per cell key
- * (B*(2*Nv + 2*L)*nH) and 2 MiB. */
+ * (B*(2*Nv + 2*L)*nH), 1 KiB of digit counts per 2048 samples, and a byte per
+ * value row. */
 int msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int nH, int L, int P, size_t* bytes);
 
 /*
@@ -369,7 +370,8 @@ int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shap
 /* Bytes of sca_backward's gradient workspace for up to max_pairs camera-query
  * pairs (<= 0: B*Nq*Ncam) (host; no device work): about 40 bytes per sample
  * slot (pairs*nH*L*P), 8 per cell key (B*Ncam*(2*Nv + 2*L)*nH), 4 per
- * camera-query entry (Ncam*B*Nq) and 2 MiB. */
+ * camera-query entry (Ncam*B*Nq), 1 KiB of digit counts per 2048 sample slots
+ * and a byte per value row. */
 int sca_backward_workspace_size(int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int L, int P,
                                 int64_t max_pairs, size_t* bytes);
 

@@ -490,6 +490,7 @@ static msda::VgradArgs vgrad_args(const msda::VgradLayout& lay, void* workspace,
   v.pair_of = reinterpret_cast<int32_t*>(ws + lay.pair_of);
   v.slots = lay.slots;
   v.key_bound = lay.key_bound;
+  v.sort_tiles = lay.sort_tiles;
   v.passes = lay.passes;
   v.shapes = shapes;
   v.starts = starts;

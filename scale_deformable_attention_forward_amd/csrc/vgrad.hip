@@ -14,10 +14,11 @@
 //      corner grid of (W + 1) x (H + 1) keys per level and head (every sample
 //      with a corner inside its map has such a key), and (source row,
 //      alpha, fx, fy);
-//   2. a stable LSD radix sort (8-bit digits; each of kSortWaves waves owns
-//      a contiguous range, ranks its keys with ballots, and writes them after
-//      the records of the same digit from earlier waves) orders the records
-//      by key, dead samples dropped in the first pass;
+//   2. a stable LSD radix sort (8-bit digits; a block ranks a tile of
+//      kSortTile records in slot order with ballots, stages them in LDS in
+//      digit order and writes each digit's run after the same digit's
+//      records of earlier tiles, consecutive lanes to consecutive addresses)
+//      orders the records by key, dead samples dropped in the first pass;
 //   3. the (first, end) range of every key is recorded;
 //   4. one 8-lane group per value row (pixel (x, y) of level l, head h)
 //      sums, for the corners (dx, dy) = (0,0), (1,0), (0,1), (1,1) in turn,
@@ -55,7 +56,9 @@ VgradLayout vgrad_layout(int64_t images, int64_t Nv, int L, int nH, int64_t slot
   l.keys[1] = take(sizeof(uint32_t) * (size_t)slots);
   l.vals[0] = take(sizeof(VgradRec) * (size_t)slots);
   l.vals[1] = take(sizeof(VgradRec) * (size_t)slots);
-  l.counts = take(sizeof(uint32_t) * (size_t)kDigits * kSortWaves);
+  l.sort_tiles = (slots + kSortTile - 1) / kSortTile;
+  if (l.sort_tiles < 1) l.sort_tiles = 1;
+  l.counts = take(sizeof(uint32_t) * (size_t)kDigits * (size_t)l.sort_tiles);
   l.digit_totals = take(sizeof(uint32_t) * kDigits);
   l.ranges = take(sizeof(int2) * (size_t)l.key_bound);
   l.long_row = take((size_t)images * (size_t)Nv * (size_t)nH);
@@ -125,57 +128,75 @@ __global__ __launch_bounds__(kQueryTile) void vgrad_pair_of_kernel(VgradArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// radix sort passes
+// radix sort passes: block b ranks and writes tile b (slots b * kSortTile ..)
 // ---------------------------------------------------------------------------
-__device__ inline void wave_range(int64_t n, int64_t w, int64_t* lo, int64_t* hi) {
-  *lo = n * w / kSortWaves;
-  *hi = n * (w + 1) / kSortWaves;
+constexpr int kSortBlock = 256;                   // threads per tile, one per digit
+constexpr int kSortPer = kSortTile / kSortBlock;  // records per thread
+static_assert(kSortBlock == kDigits, "one thread per digit");
+
+// Exclusive scan of one value per thread over a kSortBlock block; *total is
+// the block's sum.  Synchronises.
+__device__ inline uint32_t sort_block_scan(uint32_t v, uint32_t* total) {
+  __shared__ uint32_t wave_sums[kSortBlock / kWave];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  uint32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  __syncthreads();  // wave_sums may still be read by a previous scan
+  if (lane == kWave - 1) wave_sums[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kSortBlock / kWave; ++w) {
+    before += w < wave ? wave_sums[w] : 0u;
+    all += wave_sums[w];
+  }
+  *total = all;
+  return before + incl - v;
 }
 
-constexpr int kSortBlock = 256;  // 4 waves
-constexpr int kSortUnroll = 8;   // keys per lane in flight
+__device__ inline uint32_t digit_of(uint32_t key, int shift) { return (key >> shift) & (kDigits - 1); }
 
-// digit counts of each wave's range -> counts[digit][wave]
+// digit counts of each tile -> counts[digit][tile]
 template <bool kFirst>
 __global__ __launch_bounds__(kSortBlock) void vgrad_hist_kernel(VgradArgs a, int src, int shift) {
-  __shared__ uint32_t h[kSortBlock / kWave][kDigits];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t w = (int64_t)blockIdx.x * (kSortBlock / kWave) + wave;
+  __shared__ uint32_t h[kDigits];
   const int64_t n = uniform(kFirst ? a.state->n_items : a.state->n_live);
-  int64_t lo, hi;
-  wave_range(n, w, &lo, &hi);
-  for (int d = lane; d < kDigits; d += kWave) h[wave][d] = 0u;
-  wave_lds_sync();
+  const int64_t tile = blockIdx.x, t0 = tile * kSortTile;
+  if (t0 >= n) return;
+  const int t = threadIdx.x;
+  h[t] = 0u;
+  __syncthreads();
   const uint32_t* keys = a.keys[src];
-  for (int64_t base = lo; base < hi; base += kSortUnroll * kWave) {
-    uint32_t k[kSortUnroll];
+  uint32_t k[kSortPer];
 #pragma unroll
-    for (int u = 0; u < kSortUnroll; ++u) {
-      const int64_t i = base + u * kWave + lane;
-      k[u] = i < hi ? keys[i] : kDeadKey;
-    }
-#pragma unroll
-    for (int u = 0; u < kSortUnroll; ++u)
-      if (k[u] != kDeadKey) atomicAdd(&h[wave][(k[u] >> shift) & (kDigits - 1)], 1u);
+  for (int u = 0; u < kSortPer; ++u) {
+    const int64_t i = t0 + u * kSortBlock + t;
+    k[u] = i < n ? keys[i] : kDeadKey;
   }
-  wave_lds_sync();
-  for (int d = lane; d < kDigits; d += kWave) a.counts[(int64_t)d * kSortWaves + w] = h[wave][d];
+#pragma unroll
+  for (int u = 0; u < kSortPer; ++u)
+    if (k[u] != kDeadKey) atomicAdd(&h[digit_of(k[u], shift)], 1u);
+  __syncthreads();
+  a.counts[(int64_t)t * a.sort_tiles + tile] = h[t];
 }
 
-// one block per digit: counts[d][*] -> exclusive offsets among the waves,
-// digit_totals[d] = the digit's total
+// one block per digit: counts[d][tile] -> exclusive offsets over the tiles in
+// use, digit_totals[d] = the digit's total
 constexpr int kScanBlock = 1024;
-__global__ __launch_bounds__(kScanBlock) void vgrad_scan_kernel(VgradArgs a) {
-  constexpr int kPer = kSortWaves / kScanBlock;
+__global__ __launch_bounds__(kScanBlock) void vgrad_scan_kernel(VgradArgs a, int first) {
   __shared__ uint32_t wave_sums[kScanBlock / kWave];
+  const int64_t n = uniform(first ? a.state->n_items : a.state->n_live);
+  const int64_t tiles = (n + kSortTile - 1) / kSortTile;
   const int d = blockIdx.x, t = threadIdx.x, lane = t % kWave, wave = t / kWave;
-  uint32_t* row = a.counts + (int64_t)d * kSortWaves;
-  uint32_t v[kPer], s = 0;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    v[u] = row[t * kPer + u];
-    s += v[u];
-  }
+  uint32_t* row = a.counts + (int64_t)d * a.sort_tiles;
+  const int64_t per = (tiles + kScanBlock - 1) / kScanBlock;  // tiles per thread, contiguous
+  const int64_t c0 = (int64_t)t * per, c1 = c0 + per < tiles ? c0 + per : tiles;
+  uint32_t s = 0;
+  for (int64_t c = c0; c < c1; ++c) s += row[c];
   uint32_t incl = s;
 #pragma unroll
   for (int k = 1; k < kWave; k <<= 1) {
@@ -191,88 +212,109 @@ __global__ __launch_bounds__(kScanBlock) void vgrad_scan_kernel(VgradArgs a) {
     total += x;
   }
   uint32_t run = before + incl - s;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    row[t * kPer + u] = run;
-    run += v[u];
+  for (int64_t c = c0; c < c1; ++c) {
+    const uint32_t v = row[c];
+    row[c] = run;
+    run += v;
   }
   if (t == 0) a.digit_totals[d] = total;
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// stable scatter of each wave's range: a key goes after every key of a lower
-// digit, after the keys of its digit in earlier waves, and after those of its
-// digit earlier in its own range
+// Stable scatter of tile b.  Records are ranked in slot order, kSortBlock at
+// a time (wave by wave, lane by lane: ballots give the lanes of a wave with
+// the same digit, per-wave digit counts in LDS the waves before), placed in
+// LDS in (digit, rank) order, and written out in that order: the tile's
+// records of digit d go to consecutive addresses after every record of a
+// lower digit and after digit d's records of earlier tiles.
 template <bool kFirst>
 __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, int src, int shift) {
-  __shared__ uint32_t cur[kSortBlock / kWave][kDigits];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t w = (int64_t)blockIdx.x * (kSortBlock / kWave) + wave;
+  constexpr int kWaves = kSortBlock / kWave;
+  __shared__ uint32_t skeys[kSortTile];
+  __shared__ VgradRec svals[kSortTile];
+  __shared__ uint32_t cnt[kWaves][kDigits];
+  __shared__ uint32_t run[kDigits];
+  __shared__ uint32_t local_off[kDigits];
+  __shared__ uint32_t base[kDigits];
   const int64_t n = uniform(kFirst ? a.state->n_items : a.state->n_live);
-  int64_t lo, hi;
-  wave_range(n, w, &lo, &hi);
-  // digit bases: exclusive scan of the digit totals, kDigits / 64 per lane
-  uint32_t tot[kDigits / kWave], s = 0;
-#pragma unroll
-  for (int u = 0; u < kDigits / kWave; ++u) {
-    tot[u] = a.digit_totals[lane * (kDigits / kWave) + u];
-    s += tot[u];
-  }
-  uint32_t incl = s;
-#pragma unroll
-  for (int k = 1; k < kWave; k <<= 1) {
-    const uint32_t y = __shfl_up(incl, k);
-    if (lane >= k) incl += y;
-  }
-  uint32_t run = incl - s;
-#pragma unroll
-  for (int u = 0; u < kDigits / kWave; ++u) {
-    const int d = lane * (kDigits / kWave) + u;
-    cur[wave][d] = run + a.counts[(int64_t)d * kSortWaves + w];
-    run += tot[u];
-  }
-  if (kFirst && w == 0 && lane == kWave - 1) a.state->n_live = incl;  // records that survive the first pass
-  wave_lds_sync();
+  const int64_t tile = blockIdx.x, t0 = tile * kSortTile;
+  if (t0 >= n) return;
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
 
-  const int dst = src ^ 1;
+  // where digit t's records of this tile start
+  uint32_t all = 0;
+  const uint32_t lower = sort_block_scan(a.digit_totals[t], &all);
+  base[t] = lower + a.counts[(int64_t)t * a.sort_tiles + tile];
+  run[t] = 0u;
+  if (kFirst && tile == 0 && t == 0) a.state->n_live = all;  // records that survive the first pass
+
   const uint32_t* keys = a.keys[src];
   const VgradRec* vals = a.vals[src];
+  uint32_t k[kSortPer], rank[kSortPer];
+  VgradRec v[kSortPer];
+#pragma unroll
+  for (int u = 0; u < kSortPer; ++u) {
+    const int64_t i = t0 + u * kSortBlock + t;
+    k[u] = i < n ? keys[i] : kDeadKey;
+    v[u] = k[u] != kDeadKey ? vals[i] : VgradRec{0u, 0.f, 0.f, 0.f};
+  }
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) cnt[w][t] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kSortPer; ++u) {
+    const bool live = k[u] != kDeadKey;
+    const uint32_t d = digit_of(k[u], shift);
+    uint64_t peers = __ballot(live);  // live lanes of this wave with the same digit
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool set = (d >> bit) & 1u;
+      const uint64_t m = __ballot(set);
+      peers &= set ? m : ~m;
+    }
+    if (live && (peers & below) == 0ull) cnt[wave][d] = (uint32_t)__popcll(peers);
+    __syncthreads();
+    if (live) {
+      uint32_t r = run[d] + (uint32_t)__popcll(peers & below);
+      for (int w = 0; w < wave; ++w) r += cnt[w][d];
+      rank[u] = r;
+    }
+    __syncthreads();
+    uint32_t add = 0;  // digit t's records in this step; its counts are cleared for the next
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      add += cnt[w][t];
+      cnt[w][t] = 0u;
+    }
+    run[t] += add;
+    __syncthreads();
+  }
+  uint32_t tile_live = 0;
+  local_off[t] = sort_block_scan(run[t], &tile_live);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kSortPer; ++u) {
+    if (k[u] == kDeadKey) continue;
+    const uint32_t lp = local_off[digit_of(k[u], shift)] + rank[u];
+    skeys[lp] = k[u];
+    svals[lp] = v[u];
+  }
+  __syncthreads();
   // stores through descriptors sized to the buffers: a position past the end
   // is dropped by the hardware
+  const int dst = src ^ 1;
   const auto okeys = make_rsrc(a.keys[dst], (uint32_t)(a.slots * sizeof(uint32_t)));
   const auto ovals = make_rsrc(a.vals[dst], (uint32_t)(a.slots * sizeof(VgradRec)));
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-  for (int64_t base = lo; base < hi; base += kSortUnroll * kWave) {
-    uint32_t k[kSortUnroll];
-    VgradRec v[kSortUnroll];
-#pragma unroll
-    for (int u = 0; u < kSortUnroll; ++u) {
-      const int64_t i = base + u * kWave + lane;
-      k[u] = i < hi ? keys[i] : kDeadKey;
-      v[u] = k[u] != kDeadKey ? vals[i] : VgradRec{0u, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int u = 0; u < kSortUnroll; ++u) {
-      const bool live = k[u] != kDeadKey;
-      const uint32_t d = (k[u] >> shift) & (kDigits - 1);
-      uint64_t peers = __ballot(live);  // live lanes with the same digit
-#pragma unroll
-      for (int bit = 0; bit < kDigitBits; ++bit) {
-        const bool set = (d >> bit) & 1u;
-        const uint64_t m = __ballot(set);
-        peers &= set ? m : ~m;
-      }
-      if (live) {
-        const uint32_t pos = cur[wave][d] + (uint32_t)__popcll(peers & below);
-        __builtin_amdgcn_raw_buffer_store_b32(k[u], okeys, pos * (uint32_t)sizeof(uint32_t), 0, 0);
-        const u32x4 pv = {v[u].src, __float_as_uint(v[u].alpha), __float_as_uint(v[u].fx), __float_as_uint(v[u].fy)};
-        __builtin_amdgcn_raw_buffer_store_b128(pv, ovals, pos * (uint32_t)sizeof(VgradRec), 0, 0);
-      }
-      wave_lds_sync();  // every lane has read its digit's position
-      if (live && (peers & below) == 0ull) cur[wave][d] += (uint32_t)__popcll(peers);
-      wave_lds_sync();
-    }
+  for (uint32_t j = t; j < tile_live; j += kSortBlock) {
+    const uint32_t key = skeys[j];
+    const uint32_t d = digit_of(key, shift);
+    const uint32_t pos = base[d] + (j - local_off[d]);
+    const VgradRec r = svals[j];
+    __builtin_amdgcn_raw_buffer_store_b32(key, okeys, pos * (uint32_t)sizeof(uint32_t), 0, 0);
+    const u32x4 pv = {r.src, __float_as_uint(r.alpha), __float_as_uint(r.fx), __float_as_uint(r.fy)};
+    __builtin_amdgcn_raw_buffer_store_b128(pv, ovals, pos * (uint32_t)sizeof(VgradRec), 0, 0);
   }
 }
 
@@ -503,19 +545,19 @@ hipError_t launch_vgrad_setup(const VgradArgs& a, bool sca, hipStream_t stream) 
 }
 
 hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
-  const unsigned sort_blocks = kSortWaves / (kSortBlock / kWave);
+  const unsigned tiles = (unsigned)a.sort_tiles;  // blocks past the records in use return at once
   int src = 0;
   for (int p = 0; p < a.passes; ++p) {
     const int shift = kDigitBits * p;
     if (p == 0)
-      vgrad_hist_kernel<true><<<sort_blocks, kSortBlock, 0, stream>>>(a, src, shift);
+      vgrad_hist_kernel<true><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
     else
-      vgrad_hist_kernel<false><<<sort_blocks, kSortBlock, 0, stream>>>(a, src, shift);
-    vgrad_scan_kernel<<<kDigits, kScanBlock, 0, stream>>>(a);
+      vgrad_hist_kernel<false><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
+    vgrad_scan_kernel<<<kDigits, kScanBlock, 0, stream>>>(a, p == 0 ? 1 : 0);
     if (p == 0)
-      vgrad_scatter_kernel<true><<<sort_blocks, kSortBlock, 0, stream>>>(a, src, shift);
+      vgrad_scatter_kernel<true><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
     else
-      vgrad_scatter_kernel<false><<<sort_blocks, kSortBlock, 0, stream>>>(a, src, shift);
+      vgrad_scatter_kernel<false><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     src ^= 1;

@@ -13,7 +13,7 @@
 namespace msda {
 
 constexpr uint32_t kDeadKey = 0xffffffffu;  // a sample with no corner inside its map
-constexpr int kSortWaves = 2048;            // waves of a sort pass, each owning a contiguous range
+constexpr int kSortTile = 2048;             // records a block of a sort pass ranks and writes together
 constexpr int kDigitBits = 8;               // key bits per sort pass
 constexpr int kDigits = 1 << kDigitBits;
 constexpr int kRowChunk = 128;              // records of a value row the first pass sums (one 8-lane group)
@@ -43,6 +43,7 @@ struct VgradState {
 struct VgradLayout {
   size_t keys[2], vals[2], counts, digit_totals, ranges, long_row, pair_of, state, total;
   int64_t slots;      // record capacity
+  int64_t sort_tiles;  // ceil(slots / kSortTile)
   int64_t key_bound;  // keys are below this
   int passes;         // kDigitBits-bit digit passes covering key_bound - 1
 };
@@ -53,12 +54,13 @@ struct VgradArgs {
   // records and sort buffers
   uint32_t* keys[2];
   VgradRec* vals[2];
-  uint32_t* counts;        // [kDigits][kSortWaves]
+  uint32_t* counts;        // [kDigits][sort_tiles]
   uint32_t* digit_totals;  // [kDigits]
   int2* ranges;            // [key_bound] (first, end) of each key's records
   uint8_t* long_row;       // [images*Nv*nH] rows with more than kRowChunk records at a level
   VgradState* state;
   int64_t slots, key_bound;
+  int64_t sort_tiles;  // tiles of kSortTile slots the buffers hold
   int passes;
   // geometry
   const int64_t* shapes;

@@ -280,7 +280,7 @@ def test_backward_workspace_sizes(lib):
     """Gradient workspace sizes: about 40 bytes per sample slot plus 8 per cell
     key, growing with every size; invalid or oversized requests are refused."""
     rc, small = _mb_ws(lib)
-    assert rc == OK and small > 2 * 4 * 4 * 8 * 40
+    assert rc == OK and small >= 4 * 8 * 4 * 40  # 128 sample slots
     rc, more_q = _mb_ws(lib, Nq=400)
     assert rc == OK and more_q - small >= 396 * 8 * 4 * 40
     rc, more_v = _mb_ws(lib, Nv=1600)
