@@ -33,9 +33,9 @@
  *    reports a failed launch (the stream may then hold part of the work).
  *    msda_status_string() names a code; msda_last_error() gives the message
  *    of the calling thread's last failure.
- *  - With Nq = 0 nothing is enqueued (the backward entry points still zero
- *    their value gradient) and the per-query buffers (locations, weights,
- *    offsets, logits, masks, anchors, outputs) may be NULL.
+ *  - With Nq = 0 nothing is enqueued (the backward entry points still fill
+ *    their value gradient with zeros) and the per-query buffers (locations,
+ *    weights, offsets, logits, masks, anchors, outputs) may be NULL.
  *  - Floating-point inputs must be finite.  Sample locations may lie
  *    anywhere (outside the map they read zeros).
  *  - Shared limits: head width Dh = 32; L*P <= 64 sampling points per head;
