@@ -45,6 +45,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -62,11 +63,18 @@ KERNEL_SOURCES = {"sca_gather_kernel": GATHER_SOURCES, "msda_gather_kernel": GAT
 METRIC = "MSDA samples/sec + effective HBM GB/s, BEVFormer-base SCA layer (6 cams)"
 
 
+_CODE_TOKENS = re.compile(r'''"(?:\\.|[^"\\\n])*"|'(?:\\.|[^'\\\n])*'|//[^\n]*|/\*.*?\*/|(?:[^\s"'/]|/(?![/*]))+''', re.S)
+
+
 def source_digest(paths=GATHER_SOURCES):
+    """Hash of the kernel sources' code: comments and layout do not count,
+    so a comment edit keeps a counter run valid; any code change does not."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            toks = [t for t in _CODE_TOKENS.findall(f.read()) if not t.startswith(("//", "/*"))]
+        h.update("\n".join(toks).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

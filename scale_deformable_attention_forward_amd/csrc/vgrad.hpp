@@ -37,7 +37,7 @@ struct VgradState {
   int32_t pad;
 };
 
-// Workspace: two key and two payload buffers (sort ping-pong), per-wave digit
+// Workspace: two key and two payload buffers (sort ping-pong), per-tile digit
 // counts, per-key ranges of the sorted records, the SCA pair index of each
 // (camera, query) and the state.
 struct VgradLayout {

@@ -1,0 +1,68 @@
+"""Host logic of bench.py (no GPU): the kernel-source digest that gates the
+stored counter traffic, the traffic lookup, the in-map corner count used as
+measurement metadata, and the refusal of more than one GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _digest_of(tmp_path, text):
+    (tmp_path / "k.hip").write_text(text)
+    old = bench.ROOT
+    bench.ROOT = str(tmp_path)
+    try:
+        return bench.source_digest(["k.hip"])
+    finally:
+        bench.ROOT = old
+
+
+def test_source_digest_ignores_comments_and_layout(tmp_path):
+    base = _digest_of(tmp_path, 'int f(int a) {\n  return a + 1;  // one\n}\nconst char* s = "//x";\n')
+    assert _digest_of(tmp_path, '// header\nint f(int a) { return a + 1; /* two */ }\n'
+                                'const char* s = "//x";\n') == base
+    # code changes, including inside a string that looks like a comment, change it
+    assert _digest_of(tmp_path, 'int f(int a) {\n  return a + 2;\n}\nconst char* s = "//x";\n') != base
+    assert _digest_of(tmp_path, 'int f(int a) {\n  return a + 1;\n}\nconst char* s = "//y";\n') != base
+    assert _digest_of(tmp_path, 'int f(int a) {\n  return a+1;\n}\nconst char* s = "//x";\n') != base
+
+
+def test_measured_traffic_only_for_matching_sources(tmp_path, monkeypatch):
+    digest = bench.source_digest(bench.GATHER_SOURCES)
+    counters = {"w": {"kernel": "sca_gather_kernel", "source_digest": digest, "hbm_bytes_per_launch": 123.0},
+                "stale": {"kernel": "sca_gather_kernel", "source_digest": "0" * 16, "hbm_bytes_per_launch": 5.0}}
+    path = tmp_path / "counters.json"
+    path.write_text(json.dumps(counters))
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(path))
+    assert bench.measured_traffic("w", "sca_gather_kernel") == 123.0
+    assert bench.measured_traffic("stale", "sca_gather_kernel") is None
+    assert bench.measured_traffic("missing", "sca_gather_kernel") is None
+    # the backward kernels are gated by their own sources
+    assert bench.measured_traffic("w", "sca_backward_kernel") is None
+
+
+def test_count_inbounds_against_brute_force():
+    g = np.random.default_rng(5)
+    shapes = np.array([[3, 4], [1, 1], [2, 7]])
+    x = g.uniform(-2, 8, (10, 3, 5))
+    y = g.uniform(-2, 4, (10, 3, 5))
+    n = 0
+    for idx in np.ndindex(x.shape):
+        H, Wd = shapes[idx[1]]
+        x0, y0 = int(np.floor(x[idx])), int(np.floor(y[idx]))
+        n += sum(0 <= x0 + dx < Wd and 0 <= y0 + dy < H for dx in (0, 1) for dy in (0, 1))
+    assert bench.count_inbounds(shapes, x, y) == n
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
