@@ -95,6 +95,18 @@ def measured_traffic(workload, kernel):
     return c.get("hbm_bytes_per_launch")
 
 
+def host_cpu():
+    """The host the CPU baseline ran on: processor model and the cores this
+    process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"host_cpu": model, "host_cores_available": len(os.sched_getaffinity(0))}
+
+
 def calibrate_copy():
     import torch
     n = 1 << 28  # 256 Mi floats = 1 GiB
@@ -671,7 +683,7 @@ def main():
         elem = 2 if "bf16" in wl.dtype else 4
         line["roofline"]["gathered_bytes_in_bounds_per_launch"] = wl.inbounds_corners * 32 * elem
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = wl.cpu_baseline()
+        line["cpu_baseline"] = {**wl.cpu_baseline(), **host_cpu()}
     print(json.dumps(line), flush=True)
 
 

@@ -66,3 +66,9 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_host_cpu_names_the_cores_it_may_use():
+    h = bench.host_cpu()
+    assert h["host_cores_available"] >= 1
+    assert h["host_cpu"] is None or isinstance(h["host_cpu"], str)

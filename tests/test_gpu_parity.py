@@ -318,6 +318,13 @@ def test_sca_stages_and_compaction_reuse():
     s2 = host(msda.sca_gather(dev(v2), *args)).reshape(600, -1)
     assert_fp32_close(s1, oracle_sca(w)["slots"], "stage path, layer 1")
     assert_fp32_close(s2, oracle_sca(w, value=v2)["slots"], "stage path, layer 2")
+    # every launch claims its work items from counters in the workspace and
+    # leaves them at zero: later launches into NaN-filled outputs still
+    # write every row, with the same bits
+    for k in range(4):
+        out = torch.full((2, 300, 256), float("nan"), dtype=torch.float32, device="cuda")
+        msda.sca_gather(dev(w["value"]), *args, slots=out)
+        assert np.array_equal(host(out).reshape(600, -1), s1), f"stage path, repeat {k}"
 
 
 def test_sca_deterministic():
