@@ -316,16 +316,16 @@ int sca_scatter_mean(const float* rows, const int32_t* pair_offsets, const int32
  *              aligned, contents on entry irrelevant; or NULL.
  * The value gradient of a row is a sum over the samples of many queries.
  * With grad_workspace it is computed as a transpose gather: every sample
- * writes a record keyed by its cell, the records are sorted by key (a stable
- * radix sort) and each row sums the records of its four neighbouring cells in
- * a fixed order and is written once -- no atomics, and grad_value is the same
- * bit for bit from run to run.  This needs the level table to fit its maps in
+ * writes a record keyed by its cell, the records of each (image, head) are
+ * sorted by key (a stable radix sort) and each row sums the records of its
+ * four neighbouring cells in a fixed order and is written once -- no
+ * atomics, and grad_value is the same bit for bit from run to run.  This needs the level table to fit its maps in
  * Nv rows (sum over levels of W*H <= Nv, as in any consistent table);
  * otherwise grad_value is filled with NaN.  With grad_workspace NULL,
  * grad_value is zeroed and accumulated with float32 atomics (its last bits
  * then vary from run to run).  The other outputs are each written once.
- * Other arguments and limits as msda_forward; B*Nq*nH*L*P < 2^28 with a
- * gradient workspace.
+ * Other arguments and limits as msda_forward; with a gradient workspace, at
+ * most 2^28 record slots: B*nH*ceil(Nq*L*P / 2048)*2048 < 2^28.
  */
 int msda_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                   const int64_t* level_start_index, const float* sampling_locations, const float* attention_weights,
@@ -334,9 +334,10 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
                   void* grad_workspace, size_t grad_workspace_bytes, void* stream);
 
 /* Bytes of msda_backward's gradient workspace (host; no device work).  About
- * 40 bytes per sample (B*Nq*nH*L*P) plus 8 per cell key
- * (B*(2*Nv + 2*L)*nH), 1 KiB of digit counts per 2048 samples, and a byte per
- * value row. */
+ * 40 bytes per record slot -- each (image, head) holds its Nq*L*P samples
+ * rounded up to a multiple of 2048 -- plus 8 per cell key
+ * (B*(2*Nv + 2*L)*nH), 1 KiB of digit counts per 2048 slots, 1 KiB per
+ * (image, head), and a byte per value row. */
 int msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int nH, int L, int P, size_t* bytes);
 
 /*
@@ -358,7 +359,8 @@ int msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int nH, int 
  *                   same max_pairs, 256-byte aligned; or NULL (atomics).
  * The value gradient is built as for msda_backward (deterministic with a
  * gradient workspace, float32 atomics without); alignment and limits as
- * msda_backward, with max_pairs*nH*L*P < 2^28.
+ * msda_backward, with at most 2^28 record slots (see
+ * sca_backward_workspace_size).
  */
 int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                  const int64_t* level_start_index, const float* reference_points_cam, const float* sampling_offsets,
@@ -368,10 +370,12 @@ int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shap
                  void* grad_workspace, size_t grad_workspace_bytes, void* stream);
 
 /* Bytes of sca_backward's gradient workspace for up to max_pairs camera-query
- * pairs (<= 0: B*Nq*Ncam) (host; no device work): about 40 bytes per sample
- * slot (pairs*nH*L*P), 8 per cell key (B*Ncam*(2*Nv + 2*L)*nH), 4 per
- * camera-query entry (Ncam*B*Nq), 1 KiB of digit counts per 2048 sample slots
- * and a byte per value row. */
+ * pairs (<= 0: B*Nq*Ncam) (host; no device work): about 40 bytes per record
+ * slot -- pairs*nH*L*P samples plus up to 2048 per (image, head), since each
+ * (b, c, head) starts a new block of 2048 (at most 2^28 slots) -- 8 per cell
+ * key (B*Ncam*(2*Nv + 2*L)*nH), 4 per camera-query entry (Ncam*B*Nq), 1 KiB
+ * of digit counts per 2048 slots, 1 KiB per (image, head), and a byte per
+ * value row. */
 int sca_backward_workspace_size(int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int L, int P,
                                 int64_t max_pairs, size_t* bytes);
 

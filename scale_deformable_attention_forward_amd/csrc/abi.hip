@@ -424,14 +424,18 @@ static int check_grad_value(const float* grad_value, int64_t Nv, int nH, int Dh,
 
 // Layout of the workspace of the deterministic value gradient, after the
 // size checks shared by the size queries and the entry points.
-static int vgrad_plan(int64_t images, int64_t Nv, int64_t L, int64_t nH, int64_t slots, int64_t pair_of_entries,
-                      msda::VgradLayout* lay) {
-  if (slots < 0 || slots >= ((int64_t)1 << 28))
-    return fail(MSDA_ERR_UNSUPPORTED, "%lld sample records: at most 2^28 fit one workspace", (long long)slots);
+static int vgrad_plan(int64_t images, int64_t Nv, int64_t L, int64_t nH, int64_t records, int64_t pair_of_entries,
+                      int64_t per_segment, msda::VgradLayout* lay) {
+  constexpr int64_t kMaxSlots = (int64_t)1 << 28;
+  if (records < 0 || records >= kMaxSlots)
+    return fail(MSDA_ERR_UNSUPPORTED, "%lld sample records: at most 2^28 fit one workspace", (long long)records);
   const int64_t per_image = (2 * Nv + 2 * L) * nH;  // corner keys per image, bounded
   if (per_image >= kI31 || images > (kI31 - 1) / per_image)
     return fail(MSDA_ERR_UNSUPPORTED, "corner keys of the value gradient exceed 2^31");
-  *lay = msda::vgrad_layout(images, Nv, (int)L, (int)nH, slots, pair_of_entries);
+  *lay = msda::vgrad_layout(images, Nv, (int)L, (int)nH, records, pair_of_entries, per_segment);
+  if (lay->slots >= kMaxSlots)
+    return fail(MSDA_ERR_UNSUPPORTED, "%lld record slots (each image and head starts a tile of %d): at most 2^28",
+                (long long)lay->slots, msda::kSortTile);
   return MSDA_OK;
 }
 
@@ -448,7 +452,7 @@ int msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int nH, int 
   int rc = vgrad_sizes_ok(B, Nv, Nq, nH, L, P);
   if (rc != MSDA_OK) return rc;
   msda::VgradLayout lay;
-  rc = vgrad_plan(B, Nv, L, nH, B * Nq * nH * L * P, 0, &lay);
+  rc = vgrad_plan(B, Nv, L, nH, B * Nq * nH * L * P, 0, Nq * L * P, &lay);
   if (rc != MSDA_OK) return rc;
   *bytes = lay.total;
   return MSDA_OK;
@@ -466,7 +470,7 @@ int sca_backward_workspace_size(int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq,
   if (rc != MSDA_OK) return rc;
   if (Ncam < 1 || Ncam > 32) return fail(MSDA_ERR_UNSUPPORTED, "Ncam=%lld: 1 to 32 cameras", (long long)Ncam);
   msda::VgradLayout lay;
-  rc = vgrad_plan(B * Ncam, Nv, L, nH, sca_pair_capacity(B, Ncam, Nq, max_pairs) * nH * L * P, Ncam * B * Nq, &lay);
+  rc = vgrad_plan(B * Ncam, Nv, L, nH, sca_pair_capacity(B, Ncam, Nq, max_pairs) * nH * L * P, Ncam * B * Nq, 0, &lay);
   if (rc != MSDA_OK) return rc;
   *bytes = lay.total;
   return MSDA_OK;
@@ -483,14 +487,19 @@ static msda::VgradArgs vgrad_args(const msda::VgradLayout& lay, void* workspace,
     v.vals[i] = reinterpret_cast<msda::VgradRec*>(ws + lay.vals[i]);
   }
   v.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
+  v.tile_seg = reinterpret_cast<int32_t*>(ws + lay.tile_seg);
   v.digit_totals = reinterpret_cast<uint32_t*>(ws + lay.digit_totals);
+  v.seg_tile = reinterpret_cast<int32_t*>(ws + lay.seg_tile);
+  v.seg_items = reinterpret_cast<int32_t*>(ws + lay.seg_items);
+  v.seg_live = reinterpret_cast<int32_t*>(ws + lay.seg_live);
+  v.pair_start = reinterpret_cast<int32_t*>(ws + lay.pair_start);
   v.ranges = reinterpret_cast<int2*>(ws + lay.ranges);
   v.long_row = reinterpret_cast<uint8_t*>(ws + lay.long_row);
   v.state = reinterpret_cast<msda::VgradState*>(ws + lay.state);
   v.pair_of = reinterpret_cast<int32_t*>(ws + lay.pair_of);
-  v.slots = lay.slots;
-  v.key_bound = lay.key_bound;
+  v.segments = lay.segments;
   v.sort_tiles = lay.sort_tiles;
+  v.key_bound = lay.key_bound;
   v.passes = lay.passes;
   v.shapes = shapes;
   v.starts = starts;
@@ -514,7 +523,9 @@ static int check_grad_workspace(const msda::VgradLayout& lay, const void* ws, si
 static void set_records(msda::BackwardArgs& a, const msda::VgradArgs& v, int64_t max_pairs) {
   a.rec_keys = v.keys[0];
   a.rec_vals = v.vals[0];
-  a.key_bound = v.key_bound;
+  a.rec_slots = (uint32_t)(v.sort_tiles * msda::kSortTile);
+  a.seg_tile = v.seg_tile;
+  a.pair_start = v.pair_start;
   a.pair_of = v.pair_of;
   a.max_pairs = max_pairs;
 }
@@ -541,7 +552,7 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
   if (B >= kI31 || B * Nq >= kI31 || B * Nq * nH >= kI31 / 64) return fail(MSDA_ERR_UNSUPPORTED, "B*Nq*nH too large");
   msda::VgradLayout lay = {};
   if (grad_workspace) {
-    rc = vgrad_plan(B, Nv, L, nH, B * Nq * nH * L * P, 0, &lay);
+    rc = vgrad_plan(B, Nv, L, nH, B * Nq * nH * L * P, 0, Nq * L * P, &lay);
     if (rc == MSDA_OK) rc = check_grad_workspace(lay, grad_workspace, grad_workspace_bytes);
     if (rc != MSDA_OK) return rc;
   }
@@ -575,6 +586,8 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
   msda::VgradArgs v = vgrad_args(lay, grad_workspace, spatial_shapes, level_start_index, L, nH, Nv, B, grad_out,
                                  B * Nq * nH, grad_value);
   v.LP = L * P;
+  v.B = (int)B;
+  v.Nq = (int)Nq;
   set_records(a, v, B * Nq);
   rc = hip_status(msda::launch_vgrad_setup(v, false, st), "value gradient setup");
   if (rc == MSDA_OK) rc = hip_status(msda::launch_msda_backward(a, st), "msda backward launch");
@@ -608,7 +621,7 @@ int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shap
   const int64_t pairs_cap = sca_pair_capacity(B, Ncam, Nq, max_pairs);
   msda::VgradLayout lay = {};
   if (grad_workspace) {
-    rc = vgrad_plan(B * Ncam, Nv, L, nH, pairs_cap * nH * L * P, Ncam * B * Nq, &lay);
+    rc = vgrad_plan(B * Ncam, Nv, L, nH, pairs_cap * nH * L * P, Ncam * B * Nq, 0, &lay);
     if (rc == MSDA_OK) rc = check_grad_workspace(lay, grad_workspace, grad_workspace_bytes);
     if (rc != MSDA_OK) return rc;
   }

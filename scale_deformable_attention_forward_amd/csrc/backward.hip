@@ -207,15 +207,14 @@ __device__ inline void walk_samples(const SampleRec* __restrict__ recs, float4* 
 // corner is inside the map.  The cell and fractions are those of
 // sample_rows_of; alpha is divided by the query's hit count (SCA).
 template <int kSPL>
-__device__ inline void emit_records(const BackwardArgs& a, const Level* lv, const long long* ext, int64_t image,
-                                    int64_t slot0, uint32_t src, int hits, const double (&xs)[kSPL],
-                                    const double (&ys)[kSPL], const float (&alpha)[kSPL], uint32_t live, int j,
-                                    int h) {
+__device__ inline void emit_records(const BackwardArgs& a, const Level* lv, const long long* ext, uint32_t slot0,
+                                    uint32_t src, int hits, const double (&xs)[kSPL], const double (&ys)[kSPL],
+                                    const float (&alpha)[kSPL], uint32_t live, int j) {
   VgradRec* vals = static_cast<VgradRec*>(a.rec_vals);
 #pragma unroll
   for (int i = 0; i < kSPL; ++i) {
     const int k = j + 8 * i;
-    if (k >= a.LP) continue;
+    if (k >= a.LP || slot0 + k >= a.rec_slots) continue;
     uint32_t key = kDeadKey;
     if ((live >> i) & 1u) {
       const int l = small_div(k, a.inv_P);
@@ -228,14 +227,23 @@ __device__ inline void emit_records(const BackwardArgs& a, const Level* lv, cons
       r.alpha = hits > 1 ? alpha[i] / (float)hits : alpha[i];
       r.fx = (float)(x - xf);
       r.fy = (float)(y - yf);
-      const uint64_t kk = corner_key(image, ext[a.L], ext[l], L.W, (int)xf + 1, (int)yf + 1, a.nH, h);
-      if (kk < (uint64_t)a.key_bound) {
-        key = (uint32_t)kk;
-        vals[slot0 + k] = r;
-      }
+      // (a level table whose corner keys pass 2^32 is flagged by the setup:
+      // the value gradient is NaN then, whatever the keys)
+      key = corner_key(ext[l], L.W, (int)xf + 1, (int)yf + 1);
+      vals[slot0 + k] = r;
     }
     a.rec_keys[slot0 + k] = key;
   }
+}
+
+// First record slot of pair `local` (its index among the image's pairs) and
+// head h of an image: every head of an image has as many records, so its
+// segments take equally many tiles from the image's first one on.
+__device__ inline uint32_t record_slot(const BackwardArgs& a, int64_t image, int h, int64_t local) {
+  const int64_t s = image * a.nH;
+  const uint32_t first = (uint32_t)uniform(a.seg_tile[s]);
+  const uint32_t tiles = (uint32_t)uniform(a.seg_tile[s + 1]) - first;
+  return (first + (uint32_t)h * tiles) * (uint32_t)kSortTile + (uint32_t)local * (uint32_t)a.LP;
 }
 
 // LDS: the level table, then per wave and head group its sample records and
@@ -320,7 +328,9 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave) void msda_backward_kernel(Back
       int pos[kSPL];
       const int S = stage_samples<kSPL>(m.recs, xs, ys, alpha, live, m.lv, a.inv_P, j, h, a.nH, a.Nv, pos);
       if (kEmit && head_ok)
-        emit_records<kSPL>(a, m.lv, ext, b, src_row * a.LP, (uint32_t)src_row, 1, xs, ys, alpha, live, j, h);
+        emit_records<kSPL>(a, m.lv, ext,
+                           record_slot(a, b, h, item - b * a.Nq),
+                           (uint32_t)src_row, 1, xs, ys, alpha, live, j);
       wave_lds_sync();
       walk_samples<kBF16, !kEmit>(m.recs, m.res, S, g4, gt, img, gimg, lane);
       wave_lds_sync();
@@ -352,8 +362,9 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave) void msda_backward_kernel(Back
 // of its query, sums the offset and logit gradients over them, and writes
 // them once.  Queries no camera sees get zero gradients at the end.
 // ---------------------------------------------------------------------------
+// For L*P > 32 the kernel is held to 2 waves per SIMD (256 registers).
 template <bool kBF16, int kSPL, bool kEmit>
-__global__ __launch_bounds__(kBwdMaxWaves* kWave) void sca_backward_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kBwdMaxWaves* kWave, kSPL == 8 ? 2 : 1) void sca_backward_kernel(BackwardArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ long long ext[kMaxLevels + 1];
   const int waves_per_block = blockDim.x / kWave;
@@ -425,8 +436,9 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave) void sca_backward_kernel(Backw
           if (kEmit) {
             const int64_t pair = uniform((int64_t)a.pair_of[(c * a.B + b) * a.Nq + q]);
             if (head_ok && pair >= 0 && pair < a.max_pairs)
-              emit_records<kSPL>(a, m.lv, ext, image, (pair * a.nH + h) * a.LP, (uint32_t)src_row, hits, xs, ys,
-                                 alpha, live, j, h);
+              emit_records<kSPL>(a, m.lv, ext,
+                                 record_slot(a, image, h, pair - uniform(a.pair_start[image])),
+                                 (uint32_t)src_row, hits, xs, ys, alpha, live, j);
           }
           wave_lds_sync();
           const auto img = make_rsrc(static_cast<const char*>(a.value) + image * (int64_t)a.image_bytes,

@@ -40,12 +40,16 @@ struct BackwardArgs {
   float* grad_offsets;  // [B][Nq][nH][L][P][2]
   float* grad_logits;   // [B][Nq][nH][L*P]
   // When rec_keys is set, the value gradient is not accumulated here: every
-  // sample writes its record (vgrad.hpp) at slot (pair * nH + h) * LP + k,
-  // pair = (b, q) for MSDA and pair_of[c][b][q] for SCA (pairs at or past
-  // max_pairs write nothing), and vgrad.hip builds grad_value from them.
+  // sample writes its record (vgrad.hpp) in the segment of its (image, head)
+  // s = image * nH + h, at slot seg_tile[s] * kSortTile + local * LP + k,
+  // local = q for MSDA and pair_of[c][b][q] - pair_start[image] for SCA
+  // (pairs at or past max_pairs write nothing), and vgrad.hip builds
+  // grad_value from them.
   uint32_t* rec_keys;
   void* rec_vals;
-  int64_t key_bound;
+  uint32_t rec_slots;  // slots the record buffers hold (below 2^28)
+  const int32_t* seg_tile;
+  const int32_t* pair_start;
   const int32_t* pair_of;
   int64_t max_pairs;
 };

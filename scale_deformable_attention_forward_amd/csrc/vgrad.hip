@@ -10,16 +10,19 @@
 // Tencent Cloud SCA note, article 2321140).  Instead of scattering these
 // terms with atomics:
 //   1. the backward kernel writes one record per sample, at a slot fixed by
-//      (pair, head, sample): the key of its corner (x0 + 1, y0 + 1) in a
-//      corner grid of (W + 1) x (H + 1) keys per level and head (every sample
-//      with a corner inside its map has such a key), and (source row,
-//      alpha, fx, fy);
-//   2. a stable LSD radix sort (8-bit digits; a block ranks a tile of
+//      (image, head, pair, sample): records of one (image, head) form a
+//      segment that starts on a sort tile.  A record holds the key of the
+//      sample's corner (x0 + 1, y0 + 1) in the image's corner grids of
+//      (W + 1) x (H + 1) keys per level (every sample with a corner inside
+//      its map has such a key) and (source row, alpha, fx, fy);
+//   2. a stable LSD radix sort of every segment at once (8-bit digits, two
+//      passes for corner grids below 2^16 keys; a block ranks a tile of
 //      kSortTile records in slot order with ballots, stages them in LDS in
-//      digit order and writes each digit's run after the same digit's
-//      records of earlier tiles, consecutive lanes to consecutive addresses)
-//      orders the records by key, dead samples dropped in the first pass;
-//   3. the (first, end) range of every key is recorded;
+//      digit order and writes each digit's run after the segment's records
+//      of lower digits and the same digit's records of the segment's earlier
+//      tiles, consecutive lanes to consecutive addresses) orders each
+//      segment by key, dead samples dropped in the first pass;
+//   3. the (first, end) range of every (segment, key) is recorded;
 //   4. one 8-lane group per value row (pixel (x, y) of level l, head h)
 //      sums, for the corners (dx, dy) = (0,0), (1,0), (0,1), (1,1) in turn,
 //      the records of key (x + 1 - dx, y + 1 - dy) in sorted order (the four
@@ -37,14 +40,22 @@ namespace msda {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-VgradLayout vgrad_layout(int64_t images, int64_t Nv, int L, int nH, int64_t slots, int64_t pair_of_entries) {
+VgradLayout vgrad_layout(int64_t images, int64_t Nv, int L, int nH, int64_t records, int64_t pair_of_entries,
+                         int64_t per_segment) {
   VgradLayout l = {};
-  l.slots = slots;
+  l.segments = images * nH;
+  // every segment starts on a tile: with per_segment records each, exactly
+  // that many tiles; otherwise at most one partly used tile each
+  l.sort_tiles = per_segment > 0 ? l.segments * ((per_segment + kSortTile - 1) / kSortTile)
+                                 : (records + kSortTile - 1) / kSortTile + l.segments;
+  if (l.sort_tiles < 1) l.sort_tiles = 1;
+  l.slots = l.sort_tiles * kSortTile;
   // (W + 1)(H + 1) <= 2 W H + 2 for W, H >= 1, so a level table whose maps fit
   // in Nv rows has at most 2 Nv + 2 L corner keys per image and head
-  l.key_bound = images * (2 * Nv + 2 * (int64_t)L) * nH;
+  const int64_t corners = 2 * Nv + 2 * (int64_t)L;
+  l.key_bound = l.segments * corners;
   int bits = 1;
-  while (bits < 62 && ((int64_t)1 << bits) < l.key_bound) ++bits;
+  while (bits < 62 && ((int64_t)1 << bits) < corners) ++bits;
   l.passes = (bits + kDigitBits - 1) / kDigitBits;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -52,14 +63,17 @@ VgradLayout vgrad_layout(int64_t images, int64_t Nv, int L, int nH, int64_t slot
     o = align_up(o + bytes, 256);
     return at;
   };
-  l.keys[0] = take(sizeof(uint32_t) * (size_t)slots);
-  l.keys[1] = take(sizeof(uint32_t) * (size_t)slots);
-  l.vals[0] = take(sizeof(VgradRec) * (size_t)slots);
-  l.vals[1] = take(sizeof(VgradRec) * (size_t)slots);
-  l.sort_tiles = (slots + kSortTile - 1) / kSortTile;
-  if (l.sort_tiles < 1) l.sort_tiles = 1;
+  l.keys[0] = take(sizeof(uint32_t) * (size_t)l.slots);
+  l.keys[1] = take(sizeof(uint32_t) * (size_t)l.slots);
+  l.vals[0] = take(sizeof(VgradRec) * (size_t)l.slots);
+  l.vals[1] = take(sizeof(VgradRec) * (size_t)l.slots);
   l.counts = take(sizeof(uint32_t) * (size_t)kDigits * (size_t)l.sort_tiles);
-  l.digit_totals = take(sizeof(uint32_t) * kDigits);
+  l.tile_seg = take(sizeof(int32_t) * (size_t)l.sort_tiles);
+  l.digit_totals = take(sizeof(uint32_t) * kDigits * (size_t)l.segments);
+  l.seg_tile = take(sizeof(int32_t) * (size_t)(l.segments + 1));
+  l.seg_items = take(sizeof(int32_t) * (size_t)l.segments);
+  l.seg_live = take(sizeof(int32_t) * (size_t)l.segments);
+  l.pair_start = take(sizeof(int32_t) * (size_t)images);
   l.ranges = take(sizeof(int2) * (size_t)l.key_bound);
   l.long_row = take((size_t)images * (size_t)Nv * (size_t)nH);
   l.pair_of = take(sizeof(int32_t) * (size_t)pair_of_entries);
@@ -69,32 +83,96 @@ VgradLayout vgrad_layout(int64_t images, int64_t Nv, int L, int nH, int64_t slot
 }
 
 // ---------------------------------------------------------------------------
+// block scan used by setup and the sort passes
+// ---------------------------------------------------------------------------
+constexpr int kSortBlock = 256;                   // threads per tile, one per digit
+constexpr int kSortPer = kSortTile / kSortBlock;  // records per thread
+static_assert(kSortBlock == kDigits, "one thread per digit");
+
+// Exclusive scan of one value per thread over a kSortBlock block; *total is
+// the block's sum.  Synchronises.
+__device__ inline uint32_t sort_block_scan(uint32_t v, uint32_t* total) {
+  __shared__ uint32_t wave_sums[kSortBlock / kWave];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  uint32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  __syncthreads();  // wave_sums may still be read by a previous scan
+  if (lane == kWave - 1) wave_sums[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kSortBlock / kWave; ++w) {
+    before += w < wave ? wave_sums[w] : 0u;
+    all += wave_sums[w];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// ---------------------------------------------------------------------------
 // setup: state, SCA pair indices
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void vgrad_setup_kernel(VgradArgs a, int sca) {
+// One block of kSortBlock threads: the state, and the segments: the pairs of
+// each image (MSDA: its Nq queries; SCA: its (b, c) pair list, cut at
+// max_pairs), each segment's record slots and first tile, and the segment of
+// every tile (each thread writes its segment's).
+__global__ __launch_bounds__(kSortBlock) void vgrad_setup_kernel(VgradArgs a, int sca) {
   __shared__ Level lv[kMaxLevels];
   __shared__ long long ext[kMaxLevels + 1];
   load_levels(a.shapes, a.starts, a.L, lv);
   load_corner_starts(lv, a.L, ext);
-  if (threadIdx.x != 0) return;
+  const int t = threadIdx.x;
   int status = 0;
   const long long per_image = ext[a.L];  // corner keys per image and head
-  if (per_image > a.key_bound || a.images * per_image > a.key_bound || a.images * per_image * a.nH > a.key_bound)
-    status |= kVgradKeysOverflow;
-  int64_t items = a.slots;
-  if (sca) {
-    // the pair lists end where the last tile of the last (b, c) segment ends
-    const int64_t last = (int64_t)a.B * a.Ncam * a.tiles - 1;
-    int64_t pairs = last >= 0 ? (int64_t)a.tile_offsets[last] + a.tile_counts[last] : 0;
-    if (pairs > a.max_pairs) {
-      status |= kVgradPairsOverflow;
-      pairs = a.max_pairs;
+  if (per_image >= (long long)kDeadKey || per_image > a.key_bound / a.segments) status |= kVgradKeysOverflow;
+  // SCA: the pair lists end where the last tile of the last (b, c) segment ends
+  const int64_t last = (int64_t)a.B * a.Ncam * a.tiles - 1;
+  const int64_t all_pairs = sca ? (last >= 0 ? (int64_t)a.tile_offsets[last] + a.tile_counts[last] : 0) : 0;
+  if (sca && all_pairs > a.max_pairs) status |= kVgradPairsOverflow;
+  int64_t run = 0;  // tiles of the segments before the current chunk
+  for (int64_t s0 = 0; s0 < a.segments; s0 += kSortBlock) {
+    const int64_t s = s0 + t;
+    int64_t tiles = 0;
+    if (s < a.segments) {
+      const int64_t image = s / a.nH;
+      int64_t first = image * a.Nq, n = a.Nq;
+      if (sca) {
+        first = 0;
+        n = 0;
+        if (a.tiles > 0) {
+          first = a.tile_offsets[image * a.tiles];
+          const int64_t end = image + 1 < a.images ? (int64_t)a.tile_offsets[(image + 1) * a.tiles] : all_pairs;
+          const int64_t f = first < a.max_pairs ? first : a.max_pairs, e = end < a.max_pairs ? end : a.max_pairs;
+          n = e > f ? e - f : 0;
+        }
+      }
+      if (s % a.nH == 0) a.pair_start[image] = (int32_t)first;
+      const int64_t items = n * a.LP;
+      a.seg_items[s] = (int32_t)items;
+      tiles = (items + kSortTile - 1) / kSortTile;
     }
-    items = pairs * a.nH * a.LP;
+    uint32_t chunk = 0;
+    const uint32_t before = sort_block_scan((uint32_t)tiles, &chunk);
+    if (s < a.segments) {
+      // never past the capacity (the caller sized it), clamped regardless
+      const int64_t at = run + before < a.sort_tiles ? run + before : a.sort_tiles;
+      const int64_t end = at + tiles < a.sort_tiles ? at + tiles : a.sort_tiles;
+      a.seg_tile[s] = (int32_t)at;
+      for (int64_t tile = at; tile < end; ++tile) a.tile_seg[tile] = (int32_t)s;  // the segment of its tiles
+    }
+    run += chunk;
   }
-  a.state->n_items = items;
-  a.state->n_live = 0;
-  a.state->status = status;
+  if (run > a.sort_tiles) status |= kVgradPairsOverflow;
+  if (t == 0) {
+    a.seg_tile[a.segments] = (int32_t)(run < a.sort_tiles ? run : a.sort_tiles);
+    a.state->corner_keys = per_image;
+    a.state->tiles = run < a.sort_tiles ? run : a.sort_tiles;
+    a.state->status = status;
+  }
 }
 
 // pair_of[c][b][q] = index of (b, c, q) in the compaction's pair lists: the
@@ -129,44 +207,33 @@ __global__ __launch_bounds__(kQueryTile) void vgrad_pair_of_kernel(VgradArgs a) 
 
 // ---------------------------------------------------------------------------
 // radix sort passes: block b ranks and writes tile b (slots b * kSortTile ..)
+// of the segment the tile belongs to
 // ---------------------------------------------------------------------------
-constexpr int kSortBlock = 256;                   // threads per tile, one per digit
-constexpr int kSortPer = kSortTile / kSortBlock;  // records per thread
-static_assert(kSortBlock == kDigits, "one thread per digit");
-
-// Exclusive scan of one value per thread over a kSortBlock block; *total is
-// the block's sum.  Synchronises.
-__device__ inline uint32_t sort_block_scan(uint32_t v, uint32_t* total) {
-  __shared__ uint32_t wave_sums[kSortBlock / kWave];
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  uint32_t incl = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
-  __syncthreads();  // wave_sums may still be read by a previous scan
-  if (lane == kWave - 1) wave_sums[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kSortBlock / kWave; ++w) {
-    before += w < wave ? wave_sums[w] : 0u;
-    all += wave_sums[w];
-  }
-  *total = all;
-  return before + incl - v;
-}
-
 __device__ inline uint32_t digit_of(uint32_t key, int shift) { return (key >> shift) & (kDigits - 1); }
 
-// digit counts of each tile -> counts[digit][tile]
+// Where tile `tile` lies: its segment s, the segment's first slot and the
+// records of the segment from the tile's first slot on (the backward
+// kernel's slots before the first pass, the live records after it).
+struct TileInSegment {
+  int64_t s, seg0, n;
+};
+template <bool kFirst>
+__device__ inline TileInSegment tile_in_segment(const VgradArgs& a, int64_t tile) {
+  TileInSegment r;
+  r.s = a.tile_seg[tile];
+  r.seg0 = (int64_t)a.seg_tile[r.s] * kSortTile;
+  r.n = (int64_t)(kFirst ? a.seg_items[r.s] : a.seg_live[r.s]) - (tile * kSortTile - r.seg0);
+  return r;
+}
+
+// digit counts of each tile in use -> counts[digit][tile]
 template <bool kFirst>
 __global__ __launch_bounds__(kSortBlock) void vgrad_hist_kernel(VgradArgs a, int src, int shift) {
   __shared__ uint32_t h[kDigits];
-  const int64_t n = uniform(kFirst ? a.state->n_items : a.state->n_live);
-  const int64_t tile = blockIdx.x, t0 = tile * kSortTile;
-  if (t0 >= n) return;
+  const int64_t tile = blockIdx.x;
+  if (tile >= uniform(a.seg_tile[a.segments])) return;
+  const TileInSegment ts = tile_in_segment<kFirst>(a, tile);
+  const int64_t t0 = tile * kSortTile, n = uniform(ts.n);
   const int t = threadIdx.x;
   h[t] = 0u;
   __syncthreads();
@@ -174,8 +241,8 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_hist_kernel(VgradArgs a, int
   uint32_t k[kSortPer];
 #pragma unroll
   for (int u = 0; u < kSortPer; ++u) {
-    const int64_t i = t0 + u * kSortBlock + t;
-    k[u] = i < n ? keys[i] : kDeadKey;
+    const int i = u * kSortBlock + t;
+    k[u] = i < n ? keys[t0 + i] : kDeadKey;
   }
 #pragma unroll
   for (int u = 0; u < kSortPer; ++u)
@@ -184,40 +251,31 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_hist_kernel(VgradArgs a, int
   a.counts[(int64_t)t * a.sort_tiles + tile] = h[t];
 }
 
-// one block per digit: counts[d][tile] -> exclusive offsets over the tiles in
-// use, digit_totals[d] = the digit's total
-constexpr int kScanBlock = 1024;
-__global__ __launch_bounds__(kScanBlock) void vgrad_scan_kernel(VgradArgs a, int first) {
-  __shared__ uint32_t wave_sums[kScanBlock / kWave];
-  const int64_t n = uniform(first ? a.state->n_items : a.state->n_live);
-  const int64_t tiles = (n + kSortTile - 1) / kSortTile;
-  const int d = blockIdx.x, t = threadIdx.x, lane = t % kWave, wave = t / kWave;
-  uint32_t* row = a.counts + (int64_t)d * a.sort_tiles;
-  const int64_t per = (tiles + kScanBlock - 1) / kScanBlock;  // tiles per thread, contiguous
-  const int64_t c0 = (int64_t)t * per, c1 = c0 + per < tiles ? c0 + per : tiles;
-  uint32_t s = 0;
-  for (int64_t c = c0; c < c1; ++c) s += row[c];
-  uint32_t incl = s;
+// Block (s, g), 4 waves: wave w scans digit d = 4 g + w over segment s's
+// tiles, counts[d][tile] -> the exclusive offset of the tile's d-records in
+// the segment's d-records; digit_totals[s][d] = the segment's d-records.
+__global__ __launch_bounds__(kSortBlock) void vgrad_scan_kernel(VgradArgs a) {
+  const int64_t s = blockIdx.x;
+  const int d = (int)blockIdx.y * (kSortBlock / kWave) + (int)threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t t0 = a.seg_tile[s], tiles = a.seg_tile[s + 1] - t0;
+  uint32_t* row = a.counts + (int64_t)d * a.sort_tiles + t0;
+  const int64_t per = (tiles + kWave - 1) / kWave;  // tiles per lane, contiguous
+  const int64_t c0 = lane * per, c1 = c0 + per < tiles ? c0 + per : tiles;
+  uint32_t sum = 0;
+  for (int64_t c = c0; c < c1; ++c) sum += row[c];
+  uint32_t incl = sum;
 #pragma unroll
   for (int k = 1; k < kWave; k <<= 1) {
     const uint32_t y = __shfl_up(incl, k);
     if (lane >= k) incl += y;
   }
-  if (lane == kWave - 1) wave_sums[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, total = 0;
-  for (int w = 0; w < kScanBlock / kWave; ++w) {
-    const uint32_t x = wave_sums[w];
-    before += w < wave ? x : 0u;
-    total += x;
-  }
-  uint32_t run = before + incl - s;
+  uint32_t run = incl - sum;
   for (int64_t c = c0; c < c1; ++c) {
     const uint32_t v = row[c];
     row[c] = run;
     run += v;
   }
-  if (t == 0) a.digit_totals[d] = total;
+  if (lane == kWave - 1) a.digit_totals[s * kDigits + d] = incl;
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -226,8 +284,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // a time (wave by wave, lane by lane: ballots give the lanes of a wave with
 // the same digit, per-wave digit counts in LDS the waves before), placed in
 // LDS in (digit, rank) order, and written out in that order: the tile's
-// records of digit d go to consecutive addresses after every record of a
-// lower digit and after digit d's records of earlier tiles.
+// records of digit d go to consecutive addresses after every record of the
+// segment with a lower digit and after digit d's records of the segment's
+// earlier tiles.
 template <bool kFirst>
 __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, int src, int shift) {
   constexpr int kWaves = kSortBlock / kWave;
@@ -237,17 +296,19 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
   __shared__ uint32_t run[kDigits];
   __shared__ uint32_t local_off[kDigits];
   __shared__ uint32_t base[kDigits];
-  const int64_t n = uniform(kFirst ? a.state->n_items : a.state->n_live);
-  const int64_t tile = blockIdx.x, t0 = tile * kSortTile;
-  if (t0 >= n) return;
+  const int64_t tile = blockIdx.x;
+  if (tile >= uniform(a.seg_tile[a.segments])) return;
+  const TileInSegment ts = tile_in_segment<kFirst>(a, tile);
+  const int64_t t0 = tile * kSortTile, n = uniform(ts.n);
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
 
-  // where digit t's records of this tile start
+  // where digit t's records of this tile start: after the segment's records
+  // of lower digits and the digit's records of the segment's earlier tiles
   uint32_t all = 0;
-  const uint32_t lower = sort_block_scan(a.digit_totals[t], &all);
-  base[t] = lower + a.counts[(int64_t)t * a.sort_tiles + tile];
+  const uint32_t lower = sort_block_scan(a.digit_totals[ts.s * kDigits + t], &all);
+  base[t] = (uint32_t)ts.seg0 + lower + a.counts[(int64_t)t * a.sort_tiles + tile];
   run[t] = 0u;
-  if (kFirst && tile == 0 && t == 0) a.state->n_live = all;  // records that survive the first pass
+  if (kFirst && t0 == ts.seg0 && t == 0) a.seg_live[ts.s] = (int32_t)all;  // records that survive the first pass
 
   const uint32_t* keys = a.keys[src];
   const VgradRec* vals = a.vals[src];
@@ -255,9 +316,9 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
   VgradRec v[kSortPer];
 #pragma unroll
   for (int u = 0; u < kSortPer; ++u) {
-    const int64_t i = t0 + u * kSortBlock + t;
-    k[u] = i < n ? keys[i] : kDeadKey;
-    v[u] = k[u] != kDeadKey ? vals[i] : VgradRec{0u, 0.f, 0.f, 0.f};
+    const int i = u * kSortBlock + t;
+    k[u] = i < n ? keys[t0 + i] : kDeadKey;
+    v[u] = k[u] != kDeadKey ? vals[t0 + i] : VgradRec{0u, 0.f, 0.f, 0.f};
   }
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
@@ -305,8 +366,8 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
   // stores through descriptors sized to the buffers: a position past the end
   // is dropped by the hardware
   const int dst = src ^ 1;
-  const auto okeys = make_rsrc(a.keys[dst], (uint32_t)(a.slots * sizeof(uint32_t)));
-  const auto ovals = make_rsrc(a.vals[dst], (uint32_t)(a.slots * sizeof(VgradRec)));
+  const auto okeys = make_rsrc(a.keys[dst], (uint32_t)(a.sort_tiles * kSortTile * sizeof(uint32_t)));
+  const auto ovals = make_rsrc(a.vals[dst], (uint32_t)(a.sort_tiles * kSortTile * sizeof(VgradRec)));
   for (uint32_t j = t; j < tile_live; j += kSortBlock) {
     const uint32_t key = skeys[j];
     const uint32_t d = digit_of(key, shift);
@@ -327,14 +388,23 @@ __global__ __launch_bounds__(256) void vgrad_clear_ranges_kernel(VgradArgs a) {
     a.ranges[k] = make_int2(0, 0);
 }
 
+// Block per tile: the (first, end) slots of each (segment, key) run of the
+// sorted records.
 __global__ __launch_bounds__(256) void vgrad_ranges_kernel(VgradArgs a, int buf) {
   const uint32_t* keys = a.keys[buf];
-  const int64_t n = uniform(a.state->n_live);
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const uint32_t k = keys[i];
-    if ((int64_t)k >= a.key_bound) continue;
-    if (i == 0 || keys[i - 1] != k) a.ranges[k].x = (int)i;
-    if (i == n - 1 || keys[i + 1] != k) a.ranges[k].y = (int)(i + 1);
+  const int64_t tile = blockIdx.x;
+  const long long next = a.state->corner_keys;
+  if (tile < uniform(a.seg_tile[a.segments])) {
+    const TileInSegment ts = tile_in_segment<false>(a, tile);
+    const int64_t t0 = tile * kSortTile, end = t0 + (ts.n < kSortTile ? ts.n : kSortTile);
+    const int64_t seg_end = t0 + ts.n;  // one past the segment's last record
+    for (int64_t i = t0 + threadIdx.x; i < end; i += blockDim.x) {
+      const uint32_t k = keys[i];
+      const uint64_t key = segment_key(ts.s, next, k);
+      if (key >= (uint64_t)a.key_bound) continue;
+      if (i == ts.seg0 || keys[i - 1] != k) a.ranges[key].x = (int)i;
+      if (i == seg_end - 1 || keys[i + 1] != k) a.ranges[key].y = (int)(i + 1);
+    }
   }
 }
 
@@ -350,7 +420,8 @@ __device__ inline RowLists row_lists(const VgradArgs& a, const long long* ext, i
   RowLists s;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const uint64_t key = corner_key(image, ext[a.L], ext[l], W, x + 1 - (c & 1), y + 1 - (c >> 1), a.nH, h);
+    const uint64_t key =
+        segment_key(image * a.nH + h, ext[a.L], corner_key(ext[l], W, x + 1 - (c & 1), y + 1 - (c >> 1)));
     s.r[c] = key < (uint64_t)a.key_bound ? a.ranges[key] : make_int2(0, 0);
   }
   s.p1 = s.r[0].y - s.r[0].x;
@@ -537,7 +608,7 @@ static int vgrad_cus() {
 }
 
 hipError_t launch_vgrad_setup(const VgradArgs& a, bool sca, hipStream_t stream) {
-  vgrad_setup_kernel<<<1, 256, 0, stream>>>(a, sca ? 1 : 0);
+  vgrad_setup_kernel<<<1, kSortBlock, 0, stream>>>(a, sca ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !sca || a.tiles == 0) return e;
   vgrad_pair_of_kernel<<<dim3(a.tiles, a.B), kQueryTile, 0, stream>>>(a);
@@ -553,7 +624,7 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
       vgrad_hist_kernel<true><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
     else
       vgrad_hist_kernel<false><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
-    vgrad_scan_kernel<<<kDigits, kScanBlock, 0, stream>>>(a, p == 0 ? 1 : 0);
+    vgrad_scan_kernel<<<dim3((unsigned)a.segments, kDigits / (kSortBlock / kWave)), kSortBlock, 0, stream>>>(a);
     if (p == 0)
       vgrad_scatter_kernel<true><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
     else
@@ -565,7 +636,7 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
   const int64_t cap = (int64_t)vgrad_cus() * 8;
   int64_t blocks = (a.key_bound + 255) / 256;
   vgrad_clear_ranges_kernel<<<(unsigned)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap), 256, 0, stream>>>(a);
-  vgrad_ranges_kernel<<<(unsigned)cap, 256, 0, stream>>>(a, src);
+  vgrad_ranges_kernel<<<(unsigned)a.sort_tiles, 256, 0, stream>>>(a, src);
   const int64_t rows = a.images * (int64_t)a.Nv * a.nH;
   blocks = (rows + 31) / 32;  // 32 rows per block of 256 threads
   const int64_t row_cap = (int64_t)vgrad_cus() * 16;

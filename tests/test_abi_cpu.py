@@ -277,22 +277,29 @@ def test_msda_backward_rejects(lib, kw, code):
 
 
 def test_backward_workspace_sizes(lib):
-    """Gradient workspace sizes: about 40 bytes per sample slot plus 8 per cell
-    key, growing with every size; invalid or oversized requests are refused."""
+    """Gradient workspace sizes: about 40 bytes per record slot (each (image,
+    head) rounded up to 2048 slots) plus 8 per cell key, growing with every
+    size; invalid or oversized requests are refused."""
+    tile = 2048 * 40  # the sort buffers of one tile of record slots
     rc, small = _mb_ws(lib)
-    assert rc == OK and small >= 4 * 8 * 4 * 40  # 128 sample slots
-    rc, more_q = _mb_ws(lib, Nq=400)
-    assert rc == OK and more_q - small >= 396 * 8 * 4 * 40
+    assert rc == OK and small >= 8 * tile  # 8 heads, 16 samples each: one tile each
+    rc, same = _mb_ws(lib, Nq=500)
+    assert rc == OK and same == small  # 2000 samples per head still fit one tile
+    rc, more_q = _mb_ws(lib, Nq=4000)
+    assert rc == OK and more_q - small >= (8 - 1) * 8 * tile  # 16000 samples per head: 8 tiles
     rc, more_v = _mb_ws(lib, Nv=1600)
     assert rc == OK and more_v - small >= (2 * 1600 - 2 * 16) * 8 * 8
     assert _mb_ws(lib, B=0)[0] == INVALID
     assert _mb_ws(lib, Nq=1 << 26)[0] == UNSUPPORTED  # 2^26 * 32 sample records
+    assert _mb_ws(lib, B=1 << 14, Nq=1)[0] == UNSUPPORTED  # 2^17 (image, head) tiles of 2048 slots
     n = _sz(0)
     assert lib.msda_backward_workspace_size(1, 16, 4, 8, 1, 4, None) == INVALID
-    assert lib.sca_backward_workspace_size(1, 6, 16, 4, 8, 1, 4, 0, ctypes.byref(n)) == OK
+    # SCA: B=1, 6 cameras, 4096 queries, 8 heads, L*P = 4
+    assert lib.sca_backward_workspace_size(1, 6, 16, 4096, 8, 1, 4, 0, ctypes.byref(n)) == OK
     every = n.value
-    assert lib.sca_backward_workspace_size(1, 6, 16, 4, 8, 1, 4, 5, ctypes.byref(n)) == OK
-    assert every - n.value >= (24 - 5) * 8 * 4 * 40 - 4 * 256  # 24 pairs at most; buffers 256-aligned
+    assert every >= (6 * 4096 * 8 * 4 // 2048 + 48) * tile
+    assert lib.sca_backward_workspace_size(1, 6, 16, 4096, 8, 1, 4, 5, ctypes.byref(n)) == OK
+    assert every - n.value >= (6 * 4096 * 8 * 4 // 2048 - 1) * tile  # 5 pairs: one tile of samples at most
     assert lib.sca_backward_workspace_size(1, 33, 16, 4, 8, 1, 4, 0, ctypes.byref(n)) == UNSUPPORTED
 
 
