@@ -1,5 +1,5 @@
 """Multi-scale deformable attention and BEVFormer spatial cross-attention,
-forward pass, on AMD Instinct MI355X (gfx950).
+forward and backward passes, on AMD Instinct MI355X (gfx950).
 
 This module is the thin Python binding of libmsda.so (C ABI in
 include/msda.h).  It only marshals torch tensors into pointers and sizes:
@@ -8,8 +8,14 @@ provides device memory and the current stream.  If the library is missing,
 importing works but every call raises: there is no fallback path.
 
 Functions (same names as the C entry points):
-  msda_forward, msda_forward_frames, sca_workspace_size, sca_forward,
-  sca_compact, sca_gather, msda_gemm_bf16, msda_status_string, msda_last_error
+  operator:     msda_forward, msda_forward_frames, msda_backward,
+                msda_backward_workspace_size
+  SCA:          sca_workspace_size, sca_forward, sca_compact, sca_gather,
+                sca_backward, sca_backward_workspace_size
+  padded flow:  sca_rebatch, sca_scatter_mean (and sca_forward_rebatch, which
+                chains them with the compaction and msda_forward)
+  projections:  msda_gemm_bf16, msda_query_proj_bf16, msda_output_proj_bf16
+  status:       msda_status_string, msda_last_error
 """
 import ctypes
 import os
@@ -19,7 +25,9 @@ import torch
 __all__ = [
     "MsdaError", "MSDA_F32", "MSDA_BF16", "MSDA_WEIGHTS_PROB", "MSDA_WEIGHTS_LOGITS",
     "library_path", "load_library", "msda_forward", "msda_forward_frames", "sca_workspace_size",
-    "sca_forward", "sca_compact", "sca_gather", "msda_gemm_bf16", "msda_status_string", "msda_last_error",
+    "sca_forward", "sca_compact", "sca_gather", "msda_gemm_bf16", "msda_query_proj_bf16", "msda_output_proj_bf16",
+    "sca_rebatch", "sca_scatter_mean", "sca_forward_rebatch", "msda_backward_workspace_size",
+    "sca_backward_workspace_size", "msda_backward", "sca_backward", "msda_status_string", "msda_last_error",
 ]
 
 MSDA_F32, MSDA_BF16 = 0, 1

@@ -50,6 +50,13 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), f"{name} declared in msda.h but not exported"
 
 
+def test_binding_has_every_entry_point_by_name():
+    """The Python binding carries the C entry points under the same names."""
+    import scale_deformable_attention_forward_amd as m
+    for name in declared_functions():
+        assert name in m.__all__ and callable(getattr(m, name)), f"{name} missing from the binding"
+
+
 def test_status_strings(lib):
     for code, name in [(OK, "MSDA_OK"), (INVALID, "MSDA_ERR_INVALID_ARG"), (UNSUPPORTED, "MSDA_ERR_UNSUPPORTED"),
                        (SHAPE, "MSDA_ERR_SHAPE"), (WORKSPACE, "MSDA_ERR_WORKSPACE"), (HIP, "MSDA_ERR_HIP")]:
