@@ -183,6 +183,25 @@ def test_sca_backward_edge_cases(case):
     check_sca_backward(w, gout, case[0])
 
 
+def test_sca_backward_many_uneven_segments():
+    """The value gradient's records are kept per (image, head): 4 x 8 cameras x
+    16 heads = 512 segments (more than one block of the setup handles at a
+    time), of unequal sizes -- camera 0 sees every query (two sort tiles per
+    head), camera 7 none (empty segments), the others about a third."""
+    w = _rand_sca(41, 4, 8, 300, ((6, 10), (3, 5)), 16, 4, 2, 0.2)
+    w["bev_mask"][0] = 1
+    w["bev_mask"][7] = 0
+    gout = _grad_out(241, 4, 300, 16 * 32)
+    check_sca_backward(w, gout, "512 uneven segments")
+
+
+def test_msda_backward_many_segments():
+    """40 batch items x 8 heads = 320 segments of one sort tile each."""
+    w = _rand_msda(42, 40, 50, ((4, 4),), 8, 2)
+    gout = _grad_out(242, 40, 50, 256)
+    check_msda_backward(w, gout, True, "320 segments")
+
+
 def test_bevformer_sca_backward_atomic():
     """The full-size SCA workload with the value gradient accumulated by float32 atomics."""
     w = W.bevformer_sca()
