@@ -280,13 +280,15 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scan_kernel(VgradArgs a) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Stable scatter of tile b.  Records are ranked in slot order, kSortBlock at
+// Stable scatter of a tile.  Records are ranked in slot order, kSortBlock at
 // a time (wave by wave, lane by lane: ballots give the lanes of a wave with
 // the same digit, per-wave digit counts in LDS the waves before), placed in
 // LDS in (digit, rank) order, and written out in that order: the tile's
 // records of digit d go to consecutive addresses after every record of the
 // segment with a lower digit and after digit d's records of the segment's
-// earlier tiles.
+// earlier tiles.  Blocks are persistent (tiles blockIdx.x, + gridDim.x, ...):
+// the next tile's keys load while this tile is ranked, its records while
+// this tile is written.
 template <bool kFirst>
 __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, int src, int shift) {
   constexpr int kWaves = kSortBlock / kWave;
@@ -296,86 +298,119 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
   __shared__ uint32_t run[kDigits];
   __shared__ uint32_t local_off[kDigits];
   __shared__ uint32_t base[kDigits];
-  const int64_t tile = blockIdx.x;
-  if (tile >= uniform(a.seg_tile[a.segments])) return;
-  const TileInSegment ts = tile_in_segment<kFirst>(a, tile);
-  const int64_t t0 = tile * kSortTile, n = uniform(ts.n);
+  const int64_t used = uniform(a.seg_tile[a.segments]);
+  int64_t tile = blockIdx.x;
+  if (tile >= used) return;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-
-  // where digit t's records of this tile start: after the segment's records
-  // of lower digits and the digit's records of the segment's earlier tiles
-  uint32_t all = 0;
-  const uint32_t lower = sort_block_scan(a.digit_totals[ts.s * kDigits + t], &all);
-  base[t] = (uint32_t)ts.seg0 + lower + a.counts[(int64_t)t * a.sort_tiles + tile];
-  run[t] = 0u;
-  if (kFirst && t0 == ts.seg0 && t == 0) a.seg_live[ts.s] = (int32_t)all;  // records that survive the first pass
-
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
   const uint32_t* keys = a.keys[src];
   const VgradRec* vals = a.vals[src];
-  uint32_t k[kSortPer], rank[kSortPer];
-  VgradRec v[kSortPer];
-#pragma unroll
-  for (int u = 0; u < kSortPer; ++u) {
-    const int i = u * kSortBlock + t;
-    k[u] = i < n ? keys[t0 + i] : kDeadKey;
-    v[u] = k[u] != kDeadKey ? vals[t0 + i] : VgradRec{0u, 0.f, 0.f, 0.f};
-  }
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) cnt[w][t] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < kSortPer; ++u) {
-    const bool live = k[u] != kDeadKey;
-    const uint32_t d = digit_of(k[u], shift);
-    uint64_t peers = __ballot(live);  // live lanes of this wave with the same digit
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool set = (d >> bit) & 1u;
-      const uint64_t m = __ballot(set);
-      peers &= set ? m : ~m;
-    }
-    if (live && (peers & below) == 0ull) cnt[wave][d] = (uint32_t)__popcll(peers);
-    __syncthreads();
-    if (live) {
-      uint32_t r = run[d] + (uint32_t)__popcll(peers & below);
-      for (int w = 0; w < wave; ++w) r += cnt[w][d];
-      rank[u] = r;
-    }
-    __syncthreads();
-    uint32_t add = 0;  // digit t's records in this step; its counts are cleared for the next
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      add += cnt[w][t];
-      cnt[w][t] = 0u;
-    }
-    run[t] += add;
-    __syncthreads();
-  }
-  uint32_t tile_live = 0;
-  local_off[t] = sort_block_scan(run[t], &tile_live);
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < kSortPer; ++u) {
-    if (k[u] == kDeadKey) continue;
-    const uint32_t lp = local_off[digit_of(k[u], shift)] + rank[u];
-    skeys[lp] = k[u];
-    svals[lp] = v[u];
-  }
-  __syncthreads();
   // stores through descriptors sized to the buffers: a position past the end
   // is dropped by the hardware
   const int dst = src ^ 1;
   const auto okeys = make_rsrc(a.keys[dst], (uint32_t)(a.sort_tiles * kSortTile * sizeof(uint32_t)));
   const auto ovals = make_rsrc(a.vals[dst], (uint32_t)(a.sort_tiles * kSortTile * sizeof(VgradRec)));
-  for (uint32_t j = t; j < tile_live; j += kSortBlock) {
-    const uint32_t key = skeys[j];
-    const uint32_t d = digit_of(key, shift);
-    const uint32_t pos = base[d] + (j - local_off[d]);
-    const VgradRec r = svals[j];
-    __builtin_amdgcn_raw_buffer_store_b32(key, okeys, pos * (uint32_t)sizeof(uint32_t), 0, 0);
-    const u32x4 pv = {r.src, __float_as_uint(r.alpha), __float_as_uint(r.fx), __float_as_uint(r.fy)};
-    __builtin_amdgcn_raw_buffer_store_b128(pv, ovals, pos * (uint32_t)sizeof(VgradRec), 0, 0);
+
+  // the next tile's keys (dead past its segment's records) and records
+  uint32_t k[kSortPer];
+  VgradRec v[kSortPer];
+  TileInSegment ts = tile_in_segment<kFirst>(a, tile);
+  auto fetch_keys = [&](int64_t tl, const TileInSegment& x, uint32_t (&kk)[kSortPer]) {
+    const int64_t n = uniform(x.n);
+#pragma unroll
+    for (int u = 0; u < kSortPer; ++u) {
+      const int i = u * kSortBlock + t;
+      kk[u] = i < n ? keys[tl * kSortTile + i] : kDeadKey;
+    }
+  };
+  auto fetch_vals = [&](int64_t tl, const uint32_t (&kk)[kSortPer], VgradRec (&vv)[kSortPer]) {
+#pragma unroll
+    for (int u = 0; u < kSortPer; ++u)
+      vv[u] = kk[u] != kDeadKey ? vals[tl * kSortTile + u * kSortBlock + t] : VgradRec{0u, 0.f, 0.f, 0.f};
+  };
+  fetch_keys(tile, ts, k);
+  fetch_vals(tile, k, v);
+
+  for (;;) {
+    const int64_t next = tile + gridDim.x;
+    const bool more = next < used;
+    TileInSegment tn = ts;
+    uint32_t kn[kSortPer];
+    if (more) {
+      tn = tile_in_segment<kFirst>(a, next);
+      fetch_keys(next, tn, kn);
+    }
+
+    // where digit t's records of this tile start: after the segment's records
+    // of lower digits and the digit's records of the segment's earlier tiles
+    uint32_t all = 0;
+    const uint32_t lower = sort_block_scan(a.digit_totals[ts.s * kDigits + t], &all);
+    base[t] = (uint32_t)ts.seg0 + lower + a.counts[(int64_t)t * a.sort_tiles + tile];
+    run[t] = 0u;
+    if (kFirst && tile * kSortTile == ts.seg0 && t == 0) a.seg_live[ts.s] = (int32_t)all;  // survivors of pass 1
+    uint32_t rank[kSortPer];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) cnt[w][t] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kSortPer; ++u) {
+      const bool live = k[u] != kDeadKey;
+      const uint32_t d = digit_of(k[u], shift);
+      uint64_t peers = __ballot(live);  // live lanes of this wave with the same digit
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const bool set = (d >> bit) & 1u;
+        const uint64_t m = __ballot(set);
+        peers &= set ? m : ~m;
+      }
+      if (live && (peers & below) == 0ull) cnt[wave][d] = (uint32_t)__popcll(peers);
+      __syncthreads();
+      if (live) {
+        uint32_t r = run[d] + (uint32_t)__popcll(peers & below);
+        for (int w = 0; w < wave; ++w) r += cnt[w][d];
+        rank[u] = r;
+      }
+      __syncthreads();
+      uint32_t add = 0;  // digit t's records in this step; its counts are cleared for the next
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        add += cnt[w][t];
+        cnt[w][t] = 0u;
+      }
+      run[t] += add;
+      __syncthreads();
+    }
+    uint32_t tile_live = 0;
+    local_off[t] = sort_block_scan(run[t], &tile_live);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kSortPer; ++u) {
+      if (k[u] == kDeadKey) continue;
+      const uint32_t lp = local_off[digit_of(k[u], shift)] + rank[u];
+      skeys[lp] = k[u];
+      svals[lp] = v[u];
+    }
+    __syncthreads();
+    VgradRec vn[kSortPer];
+    if (more) fetch_vals(next, kn, vn);
+    for (uint32_t j = t; j < tile_live; j += kSortBlock) {
+      const uint32_t key = skeys[j];
+      const uint32_t d = digit_of(key, shift);
+      const uint32_t pos = base[d] + (j - local_off[d]);
+      const VgradRec r = svals[j];
+      __builtin_amdgcn_raw_buffer_store_b32(key, okeys, pos * (uint32_t)sizeof(uint32_t), 0, 0);
+      const u32x4 pv = {r.src, __float_as_uint(r.alpha), __float_as_uint(r.fx), __float_as_uint(r.fy)};
+      __builtin_amdgcn_raw_buffer_store_b128(pv, ovals, pos * (uint32_t)sizeof(VgradRec), 0, 0);
+    }
+    if (!more) break;
+    __syncthreads();  // the next tile rewrites the staging area and the digit tables
+    tile = next;
+    ts = tn;
+#pragma unroll
+    for (int u = 0; u < kSortPer; ++u) {
+      k[u] = kn[u];
+      v[u] = vn[u];
+    }
   }
 }
 
@@ -617,6 +652,15 @@ hipError_t launch_vgrad_setup(const VgradArgs& a, bool sca, hipStream_t stream) 
 
 hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
   const unsigned tiles = (unsigned)a.sort_tiles;  // blocks past the records in use return at once
+  // the scatter's blocks are persistent: as many as are resident at once
+  static int scatter_per_cu = 0;
+  if (scatter_per_cu == 0 &&
+      (hipOccupancyMaxActiveBlocksPerMultiprocessor(&scatter_per_cu, vgrad_scatter_kernel<false>, kSortBlock, 0) !=
+           hipSuccess ||
+       scatter_per_cu < 1))
+    scatter_per_cu = 1;
+  const int64_t resident = (int64_t)vgrad_cus() * scatter_per_cu;
+  const unsigned scatter_blocks = (unsigned)(a.sort_tiles < resident ? a.sort_tiles : resident);
   int src = 0;
   for (int p = 0; p < a.passes; ++p) {
     const int shift = kDigitBits * p;
@@ -626,9 +670,9 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
       vgrad_hist_kernel<false><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
     vgrad_scan_kernel<<<dim3((unsigned)a.segments, kDigits / (kSortBlock / kWave)), kSortBlock, 0, stream>>>(a);
     if (p == 0)
-      vgrad_scatter_kernel<true><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
+      vgrad_scatter_kernel<true><<<scatter_blocks, kSortBlock, 0, stream>>>(a, src, shift);
     else
-      vgrad_scatter_kernel<false><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
+      vgrad_scatter_kernel<false><<<scatter_blocks, kSortBlock, 0, stream>>>(a, src, shift);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     src ^= 1;
