@@ -280,10 +280,11 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scan_kernel(VgradArgs a) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Stable scatter of a tile.  Records are ranked in slot order, kSortBlock at
-// a time (wave by wave, lane by lane: ballots give the lanes of a wave with
-// the same digit, per-wave digit counts in LDS the waves before), placed in
-// LDS in (digit, rank) order, and written out in that order: the tile's
+// Stable scatter of a tile.  Wave w ranks the tile's records w * 512 ..
+// w * 512 + 511 in slot order, 64 at a time (ballots give the lanes with the
+// same digit; the wave's own digit counts in LDS the records before), the
+// waves' counts give each wave's offset within a digit, and the records are
+// placed in LDS in (digit, rank) order and written out in that order: the tile's
 // records of digit d go to consecutive addresses after every record of the
 // segment with a lower digit and after digit d's records of the segment's
 // earlier tiles.  Blocks are persistent (tiles blockIdx.x, + gridDim.x, ...):
@@ -295,7 +296,6 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
   __shared__ uint32_t skeys[kSortTile];
   __shared__ VgradRec svals[kSortTile];
   __shared__ uint32_t cnt[kWaves][kDigits];
-  __shared__ uint32_t run[kDigits];
   __shared__ uint32_t local_off[kDigits];
   __shared__ uint32_t base[kDigits];
   const int64_t used = uniform(a.seg_tile[a.segments]);
@@ -315,18 +315,21 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
   uint32_t k[kSortPer];
   VgradRec v[kSortPer];
   TileInSegment ts = tile_in_segment<kFirst>(a, tile);
+  // wave w holds the tile's records w * kWavePer + u * kWave + lane, u < kSortPer
+  constexpr int kWavePer = kSortTile / kWaves;
+  const int mine = wave * kWavePer + lane;
   auto fetch_keys = [&](int64_t tl, const TileInSegment& x, uint32_t (&kk)[kSortPer]) {
     const int64_t n = uniform(x.n);
 #pragma unroll
     for (int u = 0; u < kSortPer; ++u) {
-      const int i = u * kSortBlock + t;
+      const int i = mine + u * kWave;
       kk[u] = i < n ? keys[tl * kSortTile + i] : kDeadKey;
     }
   };
   auto fetch_vals = [&](int64_t tl, const uint32_t (&kk)[kSortPer], VgradRec (&vv)[kSortPer]) {
 #pragma unroll
     for (int u = 0; u < kSortPer; ++u)
-      vv[u] = kk[u] != kDeadKey ? vals[tl * kSortTile + u * kSortBlock + t] : VgradRec{0u, 0.f, 0.f, 0.f};
+      vv[u] = kk[u] != kDeadKey ? vals[tl * kSortTile + mine + u * kWave] : VgradRec{0u, 0.f, 0.f, 0.f};
   };
   fetch_keys(tile, ts, k);
   fetch_vals(tile, k, v);
@@ -346,8 +349,10 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
     uint32_t all = 0;
     const uint32_t lower = sort_block_scan(a.digit_totals[ts.s * kDigits + t], &all);
     base[t] = (uint32_t)ts.seg0 + lower + a.counts[(int64_t)t * a.sort_tiles + tile];
-    run[t] = 0u;
     if (kFirst && tile * kSortTile == ts.seg0 && t == 0) a.seg_live[ts.s] = (int32_t)all;  // survivors of pass 1
+    // each wave ranks its own records against its own digit counts
+    // (cnt[wave][d]: its records of digit d so far); the waves' counts are
+    // then turned into each wave's offset within the digit
     uint32_t rank[kSortPer];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) cnt[w][t] = 0u;
@@ -363,30 +368,28 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
         const uint64_t m = __ballot(set);
         peers &= set ? m : ~m;
       }
-      if (live && (peers & below) == 0ull) cnt[wave][d] = (uint32_t)__popcll(peers);
-      __syncthreads();
-      if (live) {
-        uint32_t r = run[d] + (uint32_t)__popcll(peers & below);
-        for (int w = 0; w < wave; ++w) r += cnt[w][d];
-        rank[u] = r;
-      }
-      __syncthreads();
-      uint32_t add = 0;  // digit t's records in this step; its counts are cleared for the next
+      const uint32_t before_me = live ? cnt[wave][d] : 0u;  // read by every peer before the leader adds
+      wave_lds_sync();
+      if (live) rank[u] = before_me + (uint32_t)__popcll(peers & below);
+      if (live && (peers & below) == 0ull) cnt[wave][d] = before_me + (uint32_t)__popcll(peers);
+      wave_lds_sync();
+    }
+    __syncthreads();
+    uint32_t digit_all = 0;  // digit t's records in the tile; cnt[w][t] becomes wave w's offset in the digit
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        add += cnt[w][t];
-        cnt[w][t] = 0u;
-      }
-      run[t] += add;
-      __syncthreads();
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t c = cnt[w][t];
+      cnt[w][t] = digit_all;
+      digit_all += c;
     }
     uint32_t tile_live = 0;
-    local_off[t] = sort_block_scan(run[t], &tile_live);
+    local_off[t] = sort_block_scan(digit_all, &tile_live);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kSortPer; ++u) {
       if (k[u] == kDeadKey) continue;
-      const uint32_t lp = local_off[digit_of(k[u], shift)] + rank[u];
+      const uint32_t d = digit_of(k[u], shift);
+      const uint32_t lp = local_off[d] + cnt[wave][d] + rank[u];
       skeys[lp] = k[u];
       svals[lp] = v[u];
     }
