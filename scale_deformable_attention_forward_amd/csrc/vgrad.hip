@@ -48,7 +48,9 @@ VgradLayout vgrad_layout(int64_t images, int64_t Nv, int L, int nH, int64_t reco
   // that many tiles; otherwise at most one partly used tile each
   l.sort_tiles = per_segment > 0 ? l.segments * ((per_segment + kSortTile - 1) / kSortTile)
                                  : (records + kSortTile - 1) / kSortTile + l.segments;
-  if (l.sort_tiles < 1) l.sort_tiles = 1;
+  // a multiple of kHistTiles, so that each digit's counts of a histogram
+  // block's tiles are one aligned run
+  l.sort_tiles = (l.sort_tiles + kHistTiles - 1) / kHistTiles * kHistTiles;
   l.slots = l.sort_tiles * kSortTile;
   // (W + 1)(H + 1) <= 2 W H + 2 for W, H >= 1, so a level table whose maps fit
   // in Nv rows has at most 2 Nv + 2 L corner keys per image and head
@@ -226,29 +228,42 @@ __device__ inline TileInSegment tile_in_segment(const VgradArgs& a, int64_t tile
   return r;
 }
 
-// digit counts of each tile in use -> counts[digit][tile]
+// digit counts of each tile in use -> counts[digit][tile]; block b counts
+// the tiles b * kHistTiles .. + kHistTiles - 1 and writes each digit's counts
+// of them as one run
 template <bool kFirst>
 __global__ __launch_bounds__(kSortBlock) void vgrad_hist_kernel(VgradArgs a, int src, int shift) {
-  __shared__ uint32_t h[kDigits];
-  const int64_t tile = blockIdx.x;
-  if (tile >= uniform(a.seg_tile[a.segments])) return;
-  const TileInSegment ts = tile_in_segment<kFirst>(a, tile);
-  const int64_t t0 = tile * kSortTile, n = uniform(ts.n);
+  __shared__ uint32_t h[kHistTiles][kDigits];
+  __shared__ int64_t tile_n[kHistTiles];
+  const int64_t used = uniform(a.seg_tile[a.segments]);
+  const int64_t tile0 = (int64_t)blockIdx.x * kHistTiles;
+  if (tile0 >= used) return;
   const int t = threadIdx.x;
-  h[t] = 0u;
+#pragma unroll
+  for (int u = 0; u < kHistTiles; ++u) h[u][t] = 0u;
+  // records of each tile (0 past the tiles in use)
+  if (t < kHistTiles) tile_n[t] = tile0 + t < used ? tile_in_segment<kFirst>(a, tile0 + t).n : 0;
   __syncthreads();
   const uint32_t* keys = a.keys[src];
-  uint32_t k[kSortPer];
+  uint32_t k[kHistTiles][kSortPer];
 #pragma unroll
-  for (int u = 0; u < kSortPer; ++u) {
-    const int i = u * kSortBlock + t;
-    k[u] = i < n ? keys[t0 + i] : kDeadKey;
+  for (int u = 0; u < kHistTiles; ++u) {
+    const int64_t n = tile_n[u];
+#pragma unroll
+    for (int e = 0; e < kSortPer; ++e) {
+      const int i = e * kSortBlock + t;
+      k[u][e] = i < n ? keys[(tile0 + u) * kSortTile + i] : kDeadKey;
+    }
   }
 #pragma unroll
-  for (int u = 0; u < kSortPer; ++u)
-    if (k[u] != kDeadKey) atomicAdd(&h[digit_of(k[u], shift)], 1u);
+  for (int u = 0; u < kHistTiles; ++u)
+#pragma unroll
+    for (int e = 0; e < kSortPer; ++e)
+      if (k[u][e] != kDeadKey) atomicAdd(&h[u][digit_of(k[u][e], shift)], 1u);
   __syncthreads();
-  a.counts[(int64_t)t * a.sort_tiles + tile] = h[t];
+  uint32_t* row = a.counts + (int64_t)t * a.sort_tiles + tile0;  // kHistTiles-aligned: sort_tiles is a multiple
+#pragma unroll
+  for (int u = 0; u < kHistTiles; ++u) row[u] = h[u][t];
 }
 
 // Block (s, g), 4 waves: wave w scans digit d = 4 g + w over segment s's
@@ -654,8 +669,9 @@ hipError_t launch_vgrad_setup(const VgradArgs& a, bool sca, hipStream_t stream) 
 }
 
 hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
-  const unsigned tiles = (unsigned)a.sort_tiles;  // blocks past the records in use return at once
-  // the scatter's blocks are persistent: as many as are resident at once
+  // blocks past the tiles in use return at once; the scatter's blocks are
+  // persistent: as many as are resident at once
+  const unsigned hist_blocks = (unsigned)(a.sort_tiles / kHistTiles);
   static int scatter_per_cu = 0;
   if (scatter_per_cu == 0 &&
       (hipOccupancyMaxActiveBlocksPerMultiprocessor(&scatter_per_cu, vgrad_scatter_kernel<false>, kSortBlock, 0) !=
@@ -668,9 +684,9 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
   for (int p = 0; p < a.passes; ++p) {
     const int shift = kDigitBits * p;
     if (p == 0)
-      vgrad_hist_kernel<true><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
+      vgrad_hist_kernel<true><<<hist_blocks, kSortBlock, 0, stream>>>(a, src, shift);
     else
-      vgrad_hist_kernel<false><<<tiles, kSortBlock, 0, stream>>>(a, src, shift);
+      vgrad_hist_kernel<false><<<hist_blocks, kSortBlock, 0, stream>>>(a, src, shift);
     vgrad_scan_kernel<<<dim3((unsigned)a.segments, kDigits / (kSortBlock / kWave)), kSortBlock, 0, stream>>>(a);
     if (p == 0)
       vgrad_scatter_kernel<true><<<scatter_blocks, kSortBlock, 0, stream>>>(a, src, shift);

@@ -23,6 +23,7 @@ constexpr int kSortTile = 2048;             // records a block of a sort pass ra
 constexpr int kDigitBits = 8;               // key bits per sort pass
 constexpr int kDigits = 1 << kDigitBits;
 constexpr int kRowChunk = 128;              // records of a value row the first pass sums (one 8-lane group)
+constexpr int kHistTiles = 8;               // sort tiles one histogram block counts
 
 // Payload of a sample record: the upstream gradient row it scales (b*Nq + q)*nH + h,
 // its attention weight (for SCA divided by the query's hit count) and its

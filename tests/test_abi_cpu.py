@@ -306,7 +306,8 @@ def test_backward_workspace_sizes(lib):
     every = n.value
     assert every >= (6 * 4096 * 8 * 4 // 2048 + 48) * tile
     assert lib.sca_backward_workspace_size(1, 6, 16, 4096, 8, 1, 4, 5, ctypes.byref(n)) == OK
-    assert every - n.value >= (6 * 4096 * 8 * 4 // 2048 - 1) * tile  # 5 pairs: one tile of samples at most
+    # 5 pairs: one tile of samples at most (tiles are allocated in eights)
+    assert every - n.value >= (6 * 4096 * 8 * 4 // 2048 - 8) * tile
     assert lib.sca_backward_workspace_size(1, 33, 16, 4, 8, 1, 4, 0, ctypes.byref(n)) == UNSUPPORTED
 
 
