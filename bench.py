@@ -164,6 +164,9 @@ def sca_workload(kind):
 
     full = kind == "layer_full"
     layer = kind in ("layer_bf16", "layer_full")
+    # one frame of the encoder: one compaction (the masks and anchors do not
+    # change between layers) and the gathers of 6 layers
+    layers = 6 if kind == "sca_frame6" else 1
     bf16 = kind in ("sca_bf16", "layer_bf16", "layer_full")
     if full:
         w = W.bevformer_layer_bf16()
@@ -209,6 +212,15 @@ def sca_workload(kind):
     wl.parts.append(("gather", lambda: m.sca_gather(d["value"], d["spatial_shapes"], d["level_start_index"],
                                                     d["reference_points_cam"], d["sampling_offsets"],
                                                     d["attention_logits"], ws, slots=slots)))
+    # layers 2..6 of a frame: their own value maps, offsets and logits (the
+    # first layer's, shifted and scaled on the device: synthetic, like it)
+    for li in range(1, layers):
+        v_l = torch.roll(d["value"], shifts=997 * li, dims=2).contiguous()
+        o_l = (d["sampling_offsets"] * (1.0 - 0.1 * li)).contiguous()
+        g_l = torch.roll(d["attention_logits"], shifts=li, dims=-1).contiguous()
+        s_l = torch.empty_like(slots)
+        wl.parts.append((f"gather_{li + 1}", lambda v_l=v_l, o_l=o_l, g_l=g_l, s_l=s_l: m.sca_gather(
+            v_l, d["spatial_shapes"], d["level_start_index"], d["reference_points_cam"], o_l, g_l, ws, slots=s_l)))
     if full:
         wl.parts.append(("output_proj", lambda: m.msda_output_proj_bf16(
             slots.view(-1, C), d["W_o"], d["b_o"], residual=d["query"], gamma=d["gamma"], beta=d["beta"],
@@ -239,11 +251,11 @@ def sca_workload(kind):
                     n_in += count_inbounds(ss[l:l + 1], x[..., None, :], y[..., None, :])
         wl.inbounds_corners = n_in
         elem = 2 if bf16 else 4
-        wl.samples = n_pairs * nH * L * P
+        wl.samples = n_pairs * nH * L * P * layers
         # effective bytes of one gather launch: 4 nominal corners x 32 channels
         # per sample, the per-query offsets and logits, the anchors of each
         # pair, the camera masks and work list, and the output rows
-        wl.gathered_bytes = wl.samples * 4 * 32 * elem
+        wl.gathered_bytes = n_pairs * nH * L * P * 4 * 32 * elem  # one launch (the first layer's)
         wl.eff_bytes = (wl.gathered_bytes + B * Nq * nH * L * P * (8 + 4) + n_pairs * D * 8 + B * Nq * (4 + 4)
                         + B * Nq * C * 4)
         if layer:
@@ -260,7 +272,9 @@ def sca_workload(kind):
     wl.batch = B
     wl.config = {"workload": "BEVFormer-base spatial cross-attention layer, 6 cameras"
                  + (", whole layer: bf16 query, value and output projections, residual and layer norm" if full
-                    else ", with bf16 value and output projections" if layer else ""),
+                    else ", with bf16 value and output projections" if layer
+                    else "; one frame: one compaction serving 6 encoder layers, each with its own value maps, "
+                         "offsets and logits" if layers > 1 else ""),
                  "batch": B, "cameras": Ncam, "bev_queries": "200x200", "levels": "116x200/58x100/29x50/15x25",
                  "heads": nH, "head_dim": 32, "points_per_level": P, "pillar_anchors": D,
                  "value_dtype": "bf16" if bf16 else "fp32", "mask": "azimuth sectors, 1-2 cameras per query"}
@@ -303,8 +317,9 @@ def sca_workload(kind):
         oracle.sca(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
                    w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
         t = time.perf_counter() - t0
-        return {"value": wl.samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
-                "sample": f"the whole workload (all {B * Nq} queries, {wl.samples} samples), "
+        n = wl.samples // layers
+        return {"value": n / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole workload (all {B * Nq} queries, {n} samples{', the first layer' if layers > 1 else ''}), "
                           f"single-threaded C, {t:.1f} s"}
     wl.cpu_baseline = cpu_baseline
     return wl
@@ -385,8 +400,9 @@ def rebatch_workload():
         oracle.sca(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
                    w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
         t = time.perf_counter() - t0
-        return {"value": wl.samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
-                "sample": f"the whole workload (all {B * Nq} queries, {wl.samples} samples), "
+        n = wl.samples // layers
+        return {"value": n / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole workload (all {B * Nq} queries, {n} samples{', the first layer' if layers > 1 else ''}), "
                           f"single-threaded C, {t:.1f} s"}
     wl.cpu_baseline = cpu_baseline
     return wl
@@ -562,7 +578,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sca",
                     choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "sca_train", "detr",
-                             "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny"])
+                             "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny", "sca_frame6"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="steps timed after a 1 GiB write that evicts the caches (0: none)")
@@ -581,7 +597,7 @@ def main():
     import scale_deformable_attention_forward_amd as m
     m.load_library()
 
-    if args.workload in ("sca", "layer_bf16", "layer_full", "sca_bf16"):
+    if args.workload in ("sca", "layer_bf16", "layer_full", "sca_bf16", "sca_frame6"):
         wl = sca_workload(args.workload)
     elif args.workload == "sca_rebatch":
         wl = rebatch_workload()
