@@ -410,8 +410,9 @@ def rebatch_workload():
 
 def train_workload(which):
     """Forward and backward of one step: "sca_train" (the BEVFormer-base SCA
-    workload: compaction, SCA forward, SCA backward) or "detr_train" (the
-    DETR-encoder workload: MSDA forward and backward).  The upstream gradient
+    workload: compaction, SCA forward, SCA backward), "detr_train" (the
+    DETR-encoder workload: MSDA forward and backward) or "tsa_train" (the
+    temporal workload: the frame mean's forward and backward).  The upstream gradient
     is seeded N(0, 1).  The gradient workspace is made once, for every camera
     seeing every query (no read-back of the pair count)."""
     import torch
@@ -448,6 +449,28 @@ def train_workload(which):
         names += " (value gradient by float32 atomics)" if atomic else ""
         pairs = lambda: int(offs[-1].item())
         n_images = B * Ncam
+    elif which == "tsa_train":
+        w = W.temporal_frames()
+        B, F, Nq, Nv, nH, L, P = w["B"], w["F"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"]
+        d = {k: _dev(w[k]) for k in ("value", "spatial_shapes", "level_start_index", "sampling_locations",
+                                     "attention_weights")}
+        gout = _dev(W.upstream_gradient(4, (B, Nq, nH * 32)))
+        out = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
+        gv = torch.empty((B, F, Nv, nH, 32), dtype=torch.float32, device="cuda")
+        gloc = torch.empty_like(d["sampling_locations"])
+        gw = torch.empty_like(d["attention_weights"])
+        gws = None if atomic else torch.empty(m.msda_backward_workspace_size(B * F, Nv, Nq, nH, L, P),
+                                              dtype=torch.uint8, device="cuda")
+        fargs = (d["value"], d["spatial_shapes"], d["level_start_index"], d["sampling_locations"],
+                 d["attention_weights"])
+        wl.parts.append(("forward", lambda: m.msda_forward_frames(*fargs, out=out)))
+        wl.parts.append(("backward", lambda: m.msda_backward_frames(*fargs, gout, grad_value=gv, grad_locations=gloc,
+                                                                    grad_weights=gw, grad_workspace=gws,
+                                                                    atomic=atomic)))
+        names = ("temporal self-attention, 2 stacked 200x200 BEV maps, mean over frames, forward + backward"
+                 + (" (value gradient by float32 atomics)" if atomic else ""))
+        pairs = lambda: B * F * Nq
+        n_images = B * F
     else:
         w = W.detr_encoder_msda()
         B, Nq, Nv, nH, L, P = w["B"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"]
@@ -481,13 +504,16 @@ def train_workload(which):
         # and the value gradient written once (or zeroed first)
         S = wl.samples
         wl.gathered_bytes = S * 4 * 32 * 4
-        wl.eff_bytes = (2 * wl.gathered_bytes + B * Nq * nH * L * P * (8 + 4) * 2 + B * Nq * nH * 32 * 4
+        rows = B * Nq * (F if which == "tsa_train" else 1)  # rows of locations / offsets and weights
+        wl.eff_bytes = (2 * wl.gathered_bytes + rows * nH * L * P * (8 + 4) * 2 + B * Nq * nH * 32 * 4
                         + n_images * Nv * nH * 32 * 4)
     wl.finish = finish
     wl.batch = B
     wl.config = {"workload": names, "batch": B, "queries": Nq, "heads": nH, "head_dim": 32, "levels": L,
                  "points_per_level": P, "value_dtype": "fp32", "pass": "forward + backward",
                  "value_gradient": "float32 atomics" if atomic else "transpose gather (deterministic)"}
+    if which == "tsa_train":
+        wl.config["frames"] = F
     wl.dtype = "fp32"
     wl.kernel_key = ("sca_backward_kernel" if which == "sca_train" else "msda_backward_kernel") + "_fp32"
 
@@ -500,6 +526,11 @@ def train_workload(which):
                        w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
             oracle.sca_backward(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
                                 w["bev_mask"], w["sampling_offsets"], w["attention_logits"], g)
+        elif which == "tsa_train":
+            oracle.msda_frames(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
+                               w["attention_weights"], True)
+            oracle.msda_frames_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
+                                        w["sampling_locations"], w["attention_weights"], g, weights_are_logits=True)
         else:
             oracle.msda(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
                         w["attention_weights"], True)
@@ -578,7 +609,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sca",
                     choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "sca_train", "detr",
-                             "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny", "sca_frame6"])
+                             "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny", "sca_frame6",
+                             "tsa_train", "tsa_train_atomic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="steps timed after a 1 GiB write that evicts the caches (0: none)")
@@ -601,7 +633,8 @@ def main():
         wl = sca_workload(args.workload)
     elif args.workload == "sca_rebatch":
         wl = rebatch_workload()
-    elif args.workload in ("sca_train", "detr_train", "sca_train_atomic", "detr_train_atomic"):
+    elif args.workload in ("sca_train", "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa_train",
+                           "tsa_train_atomic"):
         wl = train_workload(args.workload)
     else:
         wl = msda_workload(args.workload)

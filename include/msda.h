@@ -9,7 +9,9 @@
  *   sca_rebatch, sca_scatter_mean            the padded rebatch form of SCA (an A/B baseline)
  *   msda_backward, sca_backward,
  *   msda_backward_workspace_size,
- *   sca_backward_workspace_size              gradients of the MSDA operator and of SCA
+ *   msda_backward_frames,
+ *   sca_backward_workspace_size              gradients of the MSDA operator (also of its
+ *                                            frame mean) and of SCA
  *   msda_status_string, msda_last_error      status reporting
  *
  * Sources, cited by page title and section:
@@ -339,6 +341,27 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
  * (B*(2*Nv + 2*L)*nH), 1 KiB of digit counts per 2048 slots, 1 KiB per
  * (image, head), and a byte per value row. */
 int msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int nH, int L, int P, size_t* bytes);
+
+/*
+ * Backward pass of msda_forward_frames (the mean over F stacked value maps,
+ * each frame with its own softmax): out[b][q] is the mean of the F per-frame
+ * operators, so frame f's gradients are msda_backward's for the upstream
+ * gradient grad_out[b] / F:
+ *   grad_value              float32 [B][F][Nv][nH][Dh], every element written
+ *   grad_sampling_locations [B][F][Nq][nH][L][P][2]
+ *   grad_attention_weights  [B][F][Nq][nH][L*P], as given (probabilities or logits)
+ *   grad_out                device float [B][Nq][nH*Dh], 16-byte aligned
+ *   grad_workspace          >= msda_backward_workspace_size(B*F, Nv, Nq, nH, L, P)
+ *                           bytes, or NULL (float32 atomics)
+ * Other arguments, the value gradient's determinism and the limits as
+ * msda_backward with B*F images.
+ */
+int msda_backward_frames(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                         const int64_t* level_start_index, const float* sampling_locations,
+                         const float* attention_weights, int weight_mode, const float* grad_out, int64_t B, int64_t F,
+                         int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, float* grad_value,
+                         float* grad_sampling_locations, float* grad_attention_weights, void* grad_workspace,
+                         size_t grad_workspace_bytes, void* stream);
 
 /*
  * Backward pass of spatial cross-attention (sca_gather's definition,

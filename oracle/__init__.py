@@ -216,6 +216,26 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, 
     return gv, gl, gw
 
 
+def msda_frames_backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights, grad_out,
+                         weights_are_logits=True):
+    """Gradients of msda_frames() for d loss / d out = grad_out [B,Nq,nH*Dh].
+    out is the mean of the F per-frame operators, so frame f's gradients are
+    msda_backward()'s of that frame for grad_out, divided by F (the division
+    is done on the float64 results: exact).  Returns (grad_value
+    [B,F,Nv,nH,Dh], grad_locations [B,F,Nq,nH,L,P,2], grad_weights
+    [B,F,Nq,nH,L*P]) float64."""
+    B, F, Nv, nH, Dh = value.shape
+    _, _, Nq, _, L, P, _ = sampling_locations.shape
+    gv = np.zeros((B, F, Nv, nH, Dh), np.float64)
+    gl = np.zeros((B, F, Nq, nH, L, P, 2), np.float64)
+    gw = np.zeros((B, F, Nq, nH, L * P), np.float64)
+    for f in range(F):
+        v, l, w = msda_backward(value[:, f], spatial_shapes, level_start_index, sampling_locations[:, f],
+                                attention_weights[:, f], grad_out, weights_are_logits=weights_are_logits)
+        gv[:, f], gl[:, f], gw[:, f] = v / F, l / F, w / F
+    return gv, gl, gw
+
+
 def sca_backward(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
                  attention_logits, grad_slots):
     """Gradients of sca() for d loss / d slots = grad_slots [B,Nq,nH*Dh].

@@ -9,7 +9,7 @@ importing works but every call raises: there is no fallback path.
 
 Functions (same names as the C entry points):
   operator:     msda_forward, msda_forward_frames, msda_backward,
-                msda_backward_workspace_size
+                msda_backward_frames, msda_backward_workspace_size
   SCA:          sca_workspace_size, sca_forward, sca_compact, sca_gather,
                 sca_backward, sca_backward_workspace_size
   padded flow:  sca_rebatch, sca_scatter_mean (and sca_forward_rebatch, which
@@ -27,7 +27,8 @@ __all__ = [
     "library_path", "load_library", "msda_forward", "msda_forward_frames", "sca_workspace_size",
     "sca_forward", "sca_compact", "sca_gather", "msda_gemm_bf16", "msda_query_proj_bf16", "msda_output_proj_bf16",
     "sca_rebatch", "sca_scatter_mean", "sca_forward_rebatch", "msda_backward_workspace_size",
-    "sca_backward_workspace_size", "msda_backward", "sca_backward", "msda_status_string", "msda_last_error",
+    "sca_backward_workspace_size", "msda_backward", "msda_backward_frames", "sca_backward", "msda_status_string",
+    "msda_last_error",
 ]
 
 MSDA_F32, MSDA_BF16 = 0, 1
@@ -73,6 +74,8 @@ def load_library():
     lib.msda_gemm_bf16.argtypes = [_p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p]
     lib.msda_backward.argtypes = [_p, _int, _p, _p, _p, _p, _int, _p, _i64, _i64, _i64, _int, _int, _int, _int, _p,
                                   _p, _p, _p, _sz, _p]
+    lib.msda_backward_frames.argtypes = [_p, _int, _p, _p, _p, _p, _int, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
+                                         _int, _p, _p, _p, _p, _sz, _p]
     lib.sca_backward.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int,
                                  _int, _p, _p, _p, _p, _sz, _i64, _p, _sz, _p]
     lib.msda_backward_workspace_size.argtypes = [_i64, _i64, _i64, _int, _int, _int, ctypes.POINTER(_sz)]
@@ -447,6 +450,42 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, 
                            _ptr(grad_weights, "grad_weights", _F32),
                            None if gws is None else _ptr(gws, "grad_workspace"), gws_bytes, _stream(stream, dev))
     _check("msda_backward", rc)
+    return grad_value, grad_locations, grad_weights
+
+
+def msda_backward_frames(value, spatial_shapes, level_start_index, sampling_locations, attention_weights, grad_out,
+                         weight_mode=MSDA_WEIGHTS_LOGITS, grad_value=None, grad_locations=None, grad_weights=None,
+                         grad_workspace=None, atomic=False, stream=None):
+    """Gradients of msda_forward_frames for grad_out = d loss / d out
+    [B,Nq,nH*Dh]: value [B,F,Nv,nH,Dh], locations [B,F,Nq,nH,L,P,2], weights
+    [B,F,Nq,nH,L*P].  Returns (grad_value float32 [B,F,Nv,nH,Dh],
+    grad_locations, grad_weights) shaped as their inputs; the value gradient
+    as for msda_backward (gradient workspace of B*F images)."""
+    lib = load_library()
+    B, F, Nv, nH, Dh = value.shape
+    _, _, Nq, _, L, P, _ = sampling_locations.shape
+    dev = value.device
+    if grad_value is None:
+        grad_value = torch.empty((B, F, Nv, nH, Dh), dtype=torch.float32, device=dev)
+    if grad_locations is None:
+        grad_locations = torch.empty_like(sampling_locations)
+    if grad_weights is None:
+        grad_weights = torch.empty_like(attention_weights)
+    gws, gws_bytes = None, 0
+    if not atomic:
+        gws = _grad_workspace(grad_workspace, msda_backward_workspace_size(B * F, Nv, Nq, nH, L, P), dev)
+        gws_bytes = gws.numel() * gws.element_size()
+    rc = lib.msda_backward_frames(_ptr(value, "value"), _value_dtype(value),
+                                  _ptr(spatial_shapes, "spatial_shapes", _I64),
+                                  _ptr(level_start_index, "level_start_index", _I64),
+                                  _ptr(sampling_locations, "sampling_locations", _F32),
+                                  _ptr(attention_weights, "attention_weights", _F32), int(weight_mode),
+                                  _ptr(grad_out, "grad_out", _F32), B, F, Nv, Nq, nH, Dh, L, P,
+                                  _ptr(grad_value, "grad_value", _F32), _ptr(grad_locations, "grad_locations", _F32),
+                                  _ptr(grad_weights, "grad_weights", _F32),
+                                  None if gws is None else _ptr(gws, "grad_workspace"), gws_bytes,
+                                  _stream(stream, dev))
+    _check("msda_backward_frames", rc)
     return grad_value, grad_locations, grad_weights
 
 

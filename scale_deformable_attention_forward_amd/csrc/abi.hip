@@ -530,16 +530,20 @@ static void set_records(msda::BackwardArgs& a, const msda::VgradArgs& v, int64_t
   a.max_pairs = max_pairs;
 }
 
-int msda_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
-                  const int64_t* level_start_index, const float* sampling_locations, const float* attention_weights,
-                  int weight_mode, const float* grad_out, int64_t B, int64_t Nv, int64_t Nq, int nH, int Dh, int L,
-                  int P, float* grad_value, float* grad_sampling_locations, float* grad_attention_weights,
-                  void* grad_workspace, size_t grad_workspace_bytes, void* stream) {
+// The operator's backward over B batch items of F frames each (images
+// b * F + f; F = 1 is the plain operator): frame f's gradients are the
+// operator's for the upstream gradient grad_out[b] / F.
+static int msda_backward_impl(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                              const int64_t* level_start_index, const float* sampling_locations,
+                              const float* attention_weights, int weight_mode, const float* grad_out, int64_t B,
+                              int64_t F, int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, float* grad_value,
+                              float* grad_sampling_locations, float* grad_attention_weights, void* grad_workspace,
+                              size_t grad_workspace_bytes, void* stream) {
   uint32_t image_bytes = 0, grad_bytes = 0;
   int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, grad_out,
                         &image_bytes);
   if (rc != MSDA_OK) return rc;
-  if (B < 1) return fail(MSDA_ERR_INVALID_ARG, "B must be positive");
+  if (B < 1 || F < 1) return fail(MSDA_ERR_INVALID_ARG, "B and F must be positive");
   rc = check_grad_value(grad_value, Nv, nH, Dh, &grad_bytes);
   if (rc != MSDA_OK) return rc;
   if (Nq != 0 && (!sampling_locations || !attention_weights || !grad_sampling_locations || !grad_attention_weights))
@@ -549,10 +553,12 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
   if (Nq != 0 && (!aligned(sampling_locations, 8) || !aligned(grad_sampling_locations, 8) ||
                   !aligned(attention_weights, 4) || !aligned(grad_attention_weights, 4)))
     return fail(MSDA_ERR_INVALID_ARG, "(x, y) arrays must be 8-byte aligned");
-  if (B >= kI31 || B * Nq >= kI31 || B * Nq * nH >= kI31 / 64) return fail(MSDA_ERR_UNSUPPORTED, "B*Nq*nH too large");
+  if (B >= kI31 || F >= kI31 || B * F >= kI31 || B * F * Nq * nH >= kI31 / 64)
+    return fail(MSDA_ERR_UNSUPPORTED, "B*F*Nq*nH too large");
+  const int64_t I = B * F;  // images
   msda::VgradLayout lay = {};
   if (grad_workspace) {
-    rc = vgrad_plan(B, Nv, L, nH, B * Nq * nH * L * P, 0, Nq * L * P, &lay);
+    rc = vgrad_plan(I, Nv, L, nH, I * Nq * nH * L * P, 0, Nq * L * P, &lay);
     if (rc == MSDA_OK) rc = check_grad_workspace(lay, grad_workspace, grad_workspace_bytes);
     if (rc != MSDA_OK) return rc;
   }
@@ -563,7 +569,7 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
   a.bf16 = value_dtype == MSDA_BF16;
   a.grad_value = grad_value;
   a.grad_image_bytes = grad_bytes;
-  a.images = B;
+  a.images = I;
   a.shapes = spatial_shapes;
   a.starts = level_start_index;
   a.L = L;
@@ -573,8 +579,9 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
   a.Nv = (int)Nv;
   a.inv_P = 1.0f / (float)P;
   a.inv_D = 1.0f;
-  a.B = B;
+  a.B = I;
   a.Nq = Nq;
+  a.F = (int)F;
   a.grad_out = grad_out;
   a.loc = sampling_locations;
   a.weights = attention_weights;
@@ -583,16 +590,39 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
   a.grad_weights = grad_attention_weights;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (!grad_workspace) return hip_status(msda::launch_msda_backward(a, st), "msda backward launch");
-  msda::VgradArgs v = vgrad_args(lay, grad_workspace, spatial_shapes, level_start_index, L, nH, Nv, B, grad_out,
+  msda::VgradArgs v = vgrad_args(lay, grad_workspace, spatial_shapes, level_start_index, L, nH, Nv, I, grad_out,
                                  B * Nq * nH, grad_value);
   v.LP = L * P;
-  v.B = (int)B;
+  v.B = (int)I;
   v.Nq = (int)Nq;
-  set_records(a, v, B * Nq);
+  set_records(a, v, I * Nq);
   rc = hip_status(msda::launch_vgrad_setup(v, false, st), "value gradient setup");
   if (rc == MSDA_OK) rc = hip_status(msda::launch_msda_backward(a, st), "msda backward launch");
   if (rc == MSDA_OK) rc = hip_status(msda::launch_vgrad_rows(v, st), "value gradient rows");
   return rc;
+}
+
+int msda_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                  const int64_t* level_start_index, const float* sampling_locations, const float* attention_weights,
+                  int weight_mode, const float* grad_out, int64_t B, int64_t Nv, int64_t Nq, int nH, int Dh, int L,
+                  int P, float* grad_value, float* grad_sampling_locations, float* grad_attention_weights,
+                  void* grad_workspace, size_t grad_workspace_bytes, void* stream) {
+  return msda_backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_locations,
+                            attention_weights, weight_mode, grad_out, B, 1, Nv, Nq, nH, Dh, L, P, grad_value,
+                            grad_sampling_locations, grad_attention_weights, grad_workspace, grad_workspace_bytes,
+                            stream);
+}
+
+int msda_backward_frames(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                         const int64_t* level_start_index, const float* sampling_locations,
+                         const float* attention_weights, int weight_mode, const float* grad_out, int64_t B, int64_t F,
+                         int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, float* grad_value,
+                         float* grad_sampling_locations, float* grad_attention_weights, void* grad_workspace,
+                         size_t grad_workspace_bytes, void* stream) {
+  return msda_backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_locations,
+                            attention_weights, weight_mode, grad_out, B, F, Nv, Nq, nH, Dh, L, P, grad_value,
+                            grad_sampling_locations, grad_attention_weights, grad_workspace, grad_workspace_bytes,
+                            stream);
 }
 
 int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,

@@ -283,7 +283,8 @@ __device__ inline void weights_grad(const float (&alpha)[kSPL], const float (&ds
 }
 
 // ---------------------------------------------------------------------------
-// MSDA operator: item = (b, q)
+// MSDA operator: item = (image, q), image = b * F + f; the frame-mean variant
+// (F > 1) takes frame f's share grad_out[b][q] / F of the upstream gradient
 // ---------------------------------------------------------------------------
 template <bool kBF16, int kSPL, bool kEmit>
 __global__ __launch_bounds__(kBwdMaxWaves* kWave) void msda_backward_kernel(BackwardArgs a) {
@@ -306,10 +307,16 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave) void msda_backward_kernel(Back
       const int h = hb + g;
       const bool head_ok = h < a.nH;
       const int64_t src_row = item * a.nH + (head_ok ? h : 0);
+      // the upstream-gradient row (b, q) of this image's batch item
+      const int64_t grad_row = a.F > 1 ? ((b / a.F) * a.Nq + (item - b * a.Nq)) * a.nH + (head_ok ? h : 0) : src_row;
       float alpha[kSPL];
       head_weights<kSPL>(a.weights + src_row * a.LP, head_ok, a.LP, j, a.weight_logits != 0, alpha);
-      const float4 g4 = head_ok ? reinterpret_cast<const float4*>(a.grad_out + src_row * 32)[j]
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 g4 = head_ok ? reinterpret_cast<const float4*>(a.grad_out + grad_row * 32)[j]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (a.F > 1) {
+        const float n = (float)a.F;
+        g4 = make_float4(g4.x / n, g4.y / n, g4.z / n, g4.w / n);
+      }
       float gt[4];
       transpose_grad(g4, lane, gt);
       const float2* loc = reinterpret_cast<const float2*>(a.loc) + src_row * a.LP;
@@ -330,7 +337,7 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave) void msda_backward_kernel(Back
       if (kEmit && head_ok)
         emit_records<kSPL>(a, m.lv, ext,
                            record_slot(a, b, h, item - b * a.Nq),
-                           (uint32_t)src_row, 1, xs, ys, alpha, live, j);
+                           (uint32_t)grad_row, a.F, xs, ys, alpha, live, j);
       wave_lds_sync();
       walk_samples<kBF16, !kEmit>(m.recs, m.res, S, g4, gt, img, gimg, lane);
       wave_lds_sync();

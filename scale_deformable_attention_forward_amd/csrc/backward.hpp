@@ -21,7 +21,8 @@ struct BackwardArgs {
   int L, P, LP, nH, Nv;
   float inv_P, inv_D;
   int64_t B, Nq;
-  const float* grad_out;  // [B][Nq][nH*32]
+  int F;                  // MSDA: frames per batch item (images b * F + f, B counting images), 1 otherwise
+  const float* grad_out;  // [B / F][Nq][nH*32]
   // MSDA: weights and locations per (b, q); outputs per (b, q)
   const float* loc;
   const float* weights;

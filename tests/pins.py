@@ -646,6 +646,34 @@ def pin_msda_backward():
             _close(gw.reshape(-1), fd, 2e-6, "logit central differences")
 
 
+def pin_msda_frames_backward():
+    """Gradients of the frame mean (F = 3, not a power of two) against its
+    forward oracle: the value adjoint identity, and central differences of
+    msda_frames in every location coordinate and every logit."""
+    F = 3
+    cases = [_bwd_msda_case(161 + f, B=1, Nq=3, shapes=((4, 6), (2, 3)), nH=2, Dh=4, P=2) for f in range(F)]
+    value = np.stack([c[0] for c in cases], 1)  # [B, F, Nv, nH, Dh]
+    ss, starts = cases[0][1], cases[0][2]
+    loc = np.stack([c[3] for c in cases], 1)
+    logits = np.stack([c[4] for c in cases], 1)
+    gout = cases[0][6]
+    gv, gl, gw = oracle.msda_frames_backward(value, ss, starts, loc, logits, gout)
+    fwd = lambda v=value, lc=loc, w=logits: oracle.msda_frames(v, ss, starts, lc, w)
+    dv = np.random.default_rng(162).normal(size=value.shape).astype(np.float32)
+    _close(np.sum(gv * dv), _loss(gout, fwd(v=dv)), 1e-11, "frames value adjoint")
+    for arr, grad, tol, what in ((loc, gl, 1e-9, "frames location central differences"),
+                                 (logits, gw, 2e-6, "frames logit central differences")):
+        fd = np.zeros(arr.size)
+        for i in range(arr.size):
+            up, dn = arr.copy().reshape(-1), arr.copy().reshape(-1)
+            up[i] += _STEP
+            dn[i] -= _STEP
+            kw_up = {"lc": up.reshape(arr.shape)} if arr is loc else {"w": up.reshape(arr.shape)}
+            kw_dn = {"lc": dn.reshape(arr.shape)} if arr is loc else {"w": dn.reshape(arr.shape)}
+            fd[i] = (_loss(gout, fwd(**kw_up)) - _loss(gout, fwd(**kw_dn))) / (2 * _STEP)
+        _close(grad.reshape(-1), fd, tol, what)
+
+
 def _bwd_sca_case(seed, B=2, Ncam=3, Nq=6, shapes=((6, 8), (3, 4)), nH=2, Dh=4, P=4, D=2):
     ss, starts, Nv = level_table(shapes)
     L = len(ss)
@@ -733,5 +761,6 @@ ALL_PINS = [
     pin_query_proj,
     pin_output_proj_layer_norm,
     pin_msda_backward,
+    pin_msda_frames_backward,
     pin_sca_backward,
 ]

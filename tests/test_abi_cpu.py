@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["msda_forward", "msda_forward_frames", "sca_workspace_size", "sca_forward", "msda_gemm_bf16",
               "msda_query_proj_bf16", "msda_output_proj_bf16", "sca_rebatch", "sca_scatter_mean",
-              "msda_backward", "sca_backward", "msda_backward_workspace_size", "sca_backward_workspace_size",
+              "msda_backward", "msda_backward_frames", "sca_backward", "msda_backward_workspace_size",
+              "sca_backward_workspace_size",
               "msda_status_string", "msda_last_error"]:
         assert n in names, n
 
@@ -260,6 +261,34 @@ def _mb(lib, value=A, dtype=0, ss=A, st=A, loc=A, w=A, mode=1, go=A, B=1, Nv=16,
         gv=B_, gl=B_, gw=B_, gws=None, gws_bytes=0):
     return lib.msda_backward(value, dtype, ss, st, loc, w, mode, go, B, Nv, Nq, nH, Dh, L, P, gv, gl, gw, gws,
                              gws_bytes, None)
+
+
+def _mbf(lib, F=2, gws=None, gws_bytes=0, **kw):
+    """msda_backward_frames with _mb's defaults."""
+    a = dict(value=A, dtype=0, ss=A, st=A, loc=A, w=A, mode=1, go=A, B=1, Nv=16, Nq=4, nH=8, Dh=32, L=1, P=4,
+             gv=B_, gl=B_, gw=B_)
+    a.update(kw)
+    return lib.msda_backward_frames(a["value"], a["dtype"], a["ss"], a["st"], a["loc"], a["w"], a["mode"], a["go"],
+                                    a["B"], F, a["Nv"], a["Nq"], a["nH"], a["Dh"], a["L"], a["P"], a["gv"], a["gl"],
+                                    a["gw"], gws, gws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(F=0), INVALID),
+    (dict(B=0), INVALID),
+    (dict(gv=None), INVALID),
+    (dict(mode=7), INVALID),
+    (dict(Dh=16), UNSUPPORTED),
+    (dict(F=1 << 31), UNSUPPORTED),
+])
+def test_msda_backward_frames_rejects(lib, kw, code):
+    assert _mbf(lib, **kw) == code
+
+
+def test_msda_backward_frames_workspace_is_that_of_b_times_f_images(lib):
+    rc, need = _mb_ws(lib, B=3 * 2)
+    assert rc == OK
+    assert _mbf(lib, F=2, B=3, gws=A, gws_bytes=need - 1) == WORKSPACE
 
 
 def _mb_ws(lib, B=1, Nv=16, Nq=4, nH=8, L=1, P=4):

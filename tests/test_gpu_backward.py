@@ -161,6 +161,47 @@ def check_sca_backward(w, gout, what, **kw):
     assert_fp32_close(gl, rl, what + ": grad logits")
 
 
+def check_frames_backward(w, gout, what, logits=True, atomic=False):
+    mode = msda.MSDA_WEIGHTS_LOGITS if logits else msda.MSDA_WEIGHTS_PROB
+    args = (w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"], w["attention_weights"])
+    gv, gl, gw = (host(t) for t in msda.msda_backward_frames(*(dev(x) for x in args), dev(gout), weight_mode=mode,
+                                                              atomic=atomic))
+    rv, rl, rw = oracle.msda_frames_backward(*args, gout, weights_are_logits=logits)
+    wmag = w["attention_weights"] if logits else np.abs(w["attention_weights"])
+    mag = oracle.msda_frames_backward(*args[:4], wmag, np.abs(gout), weights_are_logits=logits)[0]
+    assert_sum_close(gv, rv, mag, what + ": grad value")
+    assert_fp32_close(gl, rl, what + ": grad locations")
+    assert_fp32_close(gw, rw, what + ": grad weights")
+    return gv
+
+
+def test_temporal_frames_backward_full():
+    """The frame mean's backward on the temporal workload at full size: two
+    stacked 200x200 BEV maps, all 40000 queries, both value-gradient paths."""
+    w = W.temporal_frames()
+    gout = W.upstream_gradient(4, (w["B"], w["Nq"], 256))
+    check_frames_backward(w, gout, "two stacked BEV maps")
+    check_frames_backward(w, gout, "two stacked BEV maps, atomics", atomic=True)
+
+
+def test_msda_frames_backward_three_frames():
+    """Three frames (the division is not by a power of two), batch 2, two
+    levels: logits, probabilities and a bf16 value map."""
+    g = np.random.default_rng(43)
+    B, F, Nq, nH, P = 2, 3, 37, 4, 3
+    shapes = ((5, 7), (3, 2))
+    ss, starts, Nv = W.level_table(shapes)
+    w = {"value": g.normal(size=(B, F, Nv, nH, 32)).astype(np.float32), "spatial_shapes": ss,
+         "level_start_index": starts,
+         "sampling_locations": g.uniform(-0.2, 1.2, (B, F, Nq, nH, 2, P, 2)).astype(np.float32),
+         "attention_weights": g.normal(size=(B, F, Nq, nH, 2 * P)).astype(np.float32)}
+    gout = _grad_out(243, B, Nq, nH * 32)
+    check_frames_backward(w, gout, "three frames")
+    check_frames_backward(dict(w, attention_weights=g.uniform(0, 0.3, w["attention_weights"].shape)
+                               .astype(np.float32)), gout, "three frames, probabilities", logits=False)
+    check_frames_backward(dict(w, value=W.bf16_bits_trunc(w["value"])), gout, "three frames, bf16 value")
+
+
 def test_bevformer_sca_backward_full():
     """The BEVFormer-base SCA workload at full size: 40000 queries, 6 cameras."""
     w = W.bevformer_sca()
