@@ -5,7 +5,11 @@ the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares
 no code with the HIP library and imports nothing from it.
 
 The arithmetic lives in ``oracle.c`` (plain loops, IEEE double); this module
-only marshals numpy arrays into it.  Every function returns float64 arrays.
+only marshals numpy arrays into it, apart from two compositions written out
+here: ``linear_bf16_blas`` (the bf16 projection with a float64 matmul as its
+contraction step) and ``msda_frames_backward`` (each frame's
+``msda_backward``, divided by the frame count).  Every function returns
+float64 arrays.
 """
 import ctypes
 import os
