@@ -172,6 +172,13 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_setup_kernel(VgradArgs a, in
   if (t == 0) {
     a.seg_tile[a.segments] = (int32_t)(run < a.sort_tiles ? run : a.sort_tiles);
     a.state->corner_keys = per_image;
+    // digit passes the keys below per_image need (the host launches enough
+    // for the bound 2 Nv + 2 L; the launches past these return at once)
+    int bits = 1;
+    while (bits < 62 && (1ll << bits) < per_image) ++bits;
+    const int need = (bits + kDigitBits - 1) / kDigitBits;
+    a.state->passes = need < a.passes ? need : a.passes;
+    a.state->sorted = 0;
     a.state->tiles = run < a.sort_tiles ? run : a.sort_tiles;
     a.state->status = status;
   }
@@ -237,7 +244,7 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_hist_kernel(VgradArgs a, int
   __shared__ int64_t tile_n[kHistTiles];
   const int64_t used = uniform(a.seg_tile[a.segments]);
   const int64_t tile0 = (int64_t)blockIdx.x * kHistTiles;
-  if (tile0 >= used) return;
+  if (tile0 >= used || shift >= kDigitBits * uniform(a.state->passes)) return;
   const int t = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < kHistTiles; ++u) h[u][t] = 0u;
@@ -269,7 +276,8 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_hist_kernel(VgradArgs a, int
 // Block (s, g), 4 waves: wave w scans digit d = 4 g + w over segment s's
 // tiles, counts[d][tile] -> the exclusive offset of the tile's d-records in
 // the segment's d-records; digit_totals[s][d] = the segment's d-records.
-__global__ __launch_bounds__(kSortBlock) void vgrad_scan_kernel(VgradArgs a) {
+__global__ __launch_bounds__(kSortBlock) void vgrad_scan_kernel(VgradArgs a, int shift) {
+  if (shift >= kDigitBits * uniform(a.state->passes)) return;
   const int64_t s = blockIdx.x;
   const int d = (int)blockIdx.y * (kSortBlock / kWave) + (int)threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t0 = a.seg_tile[s], tiles = a.seg_tile[s + 1] - t0;
@@ -315,8 +323,9 @@ __global__ __launch_bounds__(kSortBlock) void vgrad_scatter_kernel(VgradArgs a, 
   __shared__ uint32_t base[kDigits];
   const int64_t used = uniform(a.seg_tile[a.segments]);
   int64_t tile = blockIdx.x;
-  if (tile >= used) return;
+  if (tile >= used || shift >= kDigitBits * uniform(a.state->passes)) return;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  if (tile == 0 && t == 0) a.state->sorted = src ^ 1;  // read by the kernels after the sort
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
   const uint32_t* keys = a.keys[src];
   const VgradRec* vals = a.vals[src];
@@ -443,8 +452,8 @@ __global__ __launch_bounds__(256) void vgrad_clear_ranges_kernel(VgradArgs a) {
 
 // Block per tile: the (first, end) slots of each (segment, key) run of the
 // sorted records.
-__global__ __launch_bounds__(256) void vgrad_ranges_kernel(VgradArgs a, int buf) {
-  const uint32_t* keys = a.keys[buf];
+__global__ __launch_bounds__(256) void vgrad_ranges_kernel(VgradArgs a) {
+  const uint32_t* keys = a.keys[uniform(a.state->sorted) & 1];
   const int64_t tile = blockIdx.x;
   const long long next = a.state->corner_keys;
   if (tile < uniform(a.seg_tile[a.segments])) {
@@ -557,7 +566,7 @@ __device__ inline RowPlace row_place(int64_t r, int Nv, int nH) {
 // which adds the rest.  Rows are split by die (block i runs on die i % 8): die
 // x takes the contiguous eighth x of the visit order, so the upstream-gradient
 // rows its records read share its L2.
-__global__ __launch_bounds__(256) void vgrad_rows_kernel(VgradArgs a, int buf) {
+__global__ __launch_bounds__(256) void vgrad_rows_kernel(VgradArgs a) {
   __shared__ Level lv[kMaxLevels];
   __shared__ long long ext[kMaxLevels + 1];
   load_levels(a.shapes, a.starts, a.L, lv);
@@ -568,7 +577,7 @@ __global__ __launch_bounds__(256) void vgrad_rows_kernel(VgradArgs a, int buf) {
   const int64_t lo = rows * die / kXcds, hi = rows * (die + 1) / kXcds;
   const int64_t stride = (int64_t)nlocal * (blockDim.x / 8);
   const bool poisoned = uniform(a.state->status) != 0;
-  const VgradRec* vals = a.vals[buf];
+  const VgradRec* vals = a.vals[uniform(a.state->sorted) & 1];
   const auto grad = make_rsrc(a.grad_out, a.grad_out_bytes);
   for (int64_t r = lo + (int64_t)local * (blockDim.x / 8) + threadIdx.x / 8; r < hi; r += stride) {
     const RowPlace pl = row_place(r, a.Nv, a.nH);
@@ -597,7 +606,7 @@ __global__ __launch_bounds__(256) void vgrad_rows_kernel(VgradArgs a, int buf) {
 // die as in vgrad_rows_kernel; inside a die, wave w looks at the rows
 // w, w + waves, ... of its eighth (64 flags per look), so the consecutive
 // long rows of a coarse level spread over the die's waves.
-__global__ __launch_bounds__(256) void vgrad_long_rows_kernel(VgradArgs a, int buf) {
+__global__ __launch_bounds__(256) void vgrad_long_rows_kernel(VgradArgs a) {
   __shared__ Level lv[kMaxLevels];
   __shared__ long long ext[kMaxLevels + 1];
   load_levels(a.shapes, a.starts, a.L, lv);
@@ -609,7 +618,7 @@ __global__ __launch_bounds__(256) void vgrad_long_rows_kernel(VgradArgs a, int b
   const int64_t lo = rows * die / kXcds, hi = rows * (die + 1) / kXcds;
   const int64_t waves = (int64_t)nlocal * (blockDim.x / kWave);
   const int64_t w = (int64_t)local * (blockDim.x / kWave) + threadIdx.x / kWave;
-  const VgradRec* vals = a.vals[buf];
+  const VgradRec* vals = a.vals[uniform(a.state->sorted) & 1];
   const auto grad = make_rsrc(a.grad_out, a.grad_out_bytes);
   for (int64_t base = lo + w; base < hi; base += waves * kWave) {
     const int64_t mine = base + (int64_t)lane * waves;
@@ -687,7 +696,8 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
       vgrad_hist_kernel<true><<<hist_blocks, kSortBlock, 0, stream>>>(a, src, shift);
     else
       vgrad_hist_kernel<false><<<hist_blocks, kSortBlock, 0, stream>>>(a, src, shift);
-    vgrad_scan_kernel<<<dim3((unsigned)a.segments, kDigits / (kSortBlock / kWave)), kSortBlock, 0, stream>>>(a);
+    vgrad_scan_kernel<<<dim3((unsigned)a.segments, kDigits / (kSortBlock / kWave)), kSortBlock, 0, stream>>>(a,
+                                                                                                        shift);
     if (p == 0)
       vgrad_scatter_kernel<true><<<scatter_blocks, kSortBlock, 0, stream>>>(a, src, shift);
     else
@@ -699,14 +709,14 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
   const int64_t cap = (int64_t)vgrad_cus() * 8;
   int64_t blocks = (a.key_bound + 255) / 256;
   vgrad_clear_ranges_kernel<<<(unsigned)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap), 256, 0, stream>>>(a);
-  vgrad_ranges_kernel<<<(unsigned)a.sort_tiles, 256, 0, stream>>>(a, src);
+  vgrad_ranges_kernel<<<(unsigned)a.sort_tiles, 256, 0, stream>>>(a);
   const int64_t rows = a.images * (int64_t)a.Nv * a.nH;
   blocks = (rows + 31) / 32;  // 32 rows per block of 256 threads
   const int64_t row_cap = (int64_t)vgrad_cus() * 16;
   blocks = blocks < row_cap ? blocks : row_cap;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // a multiple of the die count
-  vgrad_rows_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a, src);
-  vgrad_long_rows_kernel<<<(unsigned)((vgrad_cus() * 8 + kXcds - 1) / kXcds * kXcds), 256, 0, stream>>>(a, src);
+  vgrad_rows_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a);
+  vgrad_long_rows_kernel<<<(unsigned)((vgrad_cus() * 8 + kXcds - 1) / kXcds * kXcds), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -41,6 +41,8 @@ struct VgradState {
   int64_t corner_keys;  // corner keys per image and head: the levels' (W + 1)(H + 1) summed
   int64_t tiles;        // sort tiles in use
   int32_t status;
+  int32_t passes;       // digit passes the corner keys need (the launches past them return at once)
+  int32_t sorted;       // the key / record buffer the last pass wrote
   int32_t pad;
 };
 
