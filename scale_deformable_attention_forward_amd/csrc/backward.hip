@@ -21,19 +21,22 @@
 // 4j..4j+3 of the upstream gradient and of every corner row.  Staging packs
 // the group's live samples (corner rows, cell fractions, weight) densely into
 // LDS; the group walks them two at a time (8 corner loads in flight), forms
-// <V_c, g> for the four corners, turns them into <S, g>, <dS/dx, g>,
-// <dS/dy, g> with an 8-lane reduction, and adds alpha * w_c * g into the
-// value gradient with float32 buffer atomics, each instruction covering two
-// whole 128-byte rows (the 8 heads' rows are exchanged across the wave with
-// shuffles; a corner outside the map has an offset past the image, and the
-// hardware drops that add).  Each lane then
-// turns its own samples' results into location / offset and weight / logit
-// gradients and writes them once.
+// <V_c, g> for the four corners and turns them into <S, g>, <dS/dx, g>,
+// <dS/dy, g> with an 8-lane reduction.  Each lane then turns its own
+// samples' results into location / offset and weight / logit gradients and
+// writes them once, in a fixed order.
 //
 // The value gradient is a scatter: samples of different queries hit the same
-// rows, so it is accumulated with atomics, whose order -- and so the last
-// bits of grad_value -- varies from run to run.  Every other output is
-// written once, by one lane, in a fixed order.
+// rows.  By default (kEmit) these kernels only write, per sample, a corner
+// key and a record (source row, weight, cell fractions) for the transpose
+// gather of vgrad.hip, which sums every value row in a fixed order, so
+// grad_value is the same bit for bit on every run.  Without a records buffer
+// (the A/B variant) the walk adds alpha * w_c * g into the value gradient
+// with float32 buffer atomics, each instruction covering two whole 128-byte
+// rows (the 8 heads' rows are exchanged across the wave with shuffles; a
+// corner outside the map has an offset past the image, and the hardware
+// drops that add); their order, and so the last bits of grad_value, varies
+// from run to run.
 #include "backward.hpp"
 #include "common.hpp"
 #include "sampling.hpp"
