@@ -21,7 +21,10 @@
 //      digit order and writes each digit's run after the segment's records
 //      of lower digits and the same digit's records of the segment's earlier
 //      tiles, consecutive lanes to consecutive addresses) orders each
-//      segment by key, dead samples dropped in the first pass;
+//      segment by key, dead samples dropped in the first pass (the host
+//      launches the passes the bound 2 Nv + 2 L on the key count needs; the
+//      setup kernel, which reads the level table, lets only the passes the
+//      real count needs do work, and the others return at once);
 //   3. the (first, end) range of every (segment, key) is recorded;
 //   4. one 8-lane group per value row (pixel (x, y) of level l, head h)
 //      sums, for the corners (dx, dy) = (0,0), (1,0), (0,1), (1,1) in turn,
