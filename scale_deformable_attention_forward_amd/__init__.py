@@ -4,8 +4,10 @@ forward and backward passes, on AMD Instinct MI355X (gfx950).
 This module is the thin Python binding of libmsda.so (C ABI in
 include/msda.h).  It only marshals torch tensors into pointers and sizes:
 every step of the computation runs in the library's HIP kernels.  PyTorch
-provides device memory and the current stream.  If the library is missing,
-importing works but every call raises: there is no fallback path.
+provides device memory and the stream: torch's current one, or the one given
+as `stream=` (a torch.cuda.Stream or a raw handle), which is made current for
+the call so that what the call allocates belongs to it.  If the library is
+missing, importing works but every call raises: there is no fallback path.
 
 Functions (same names as the C entry points):
   operator:     msda_forward, msda_forward_frames, msda_backward,
@@ -18,6 +20,7 @@ Functions (same names as the C entry points):
   status:       msda_status_string, msda_last_error
 """
 import ctypes
+import functools
 import os
 
 import torch
@@ -130,6 +133,24 @@ def _value_dtype(value):
     raise TypeError(f"value must be float32 or bfloat16, got {value.dtype}")
 
 
+def _given_stream(fn):
+    """Run fn with its `stream` argument (a torch.cuda.Stream or a raw
+    hipStream_t handle) made torch's current stream for the call: the outputs
+    and workspaces fn allocates then belong to that stream in torch's caching
+    allocator (a workspace freed on return is not handed to other work before
+    the stream's kernels are done), and a read-back through torch is ordered
+    after the launches."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        if not isinstance(stream, torch.cuda.Stream):
+            stream = torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(stream):
+            return fn(*args, **kw)
+    return call
+
+
 def _stream(stream, device):
     if stream is None:
         return torch.cuda.current_stream(device).cuda_stream
@@ -140,6 +161,7 @@ _I64 = (torch.int64,)
 _F32 = (torch.float32,)
 
 
+@_given_stream
 def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
                  weight_mode=MSDA_WEIGHTS_LOGITS, out=None, stream=None):
     """value [B,Nv,nH,Dh] (float32|bfloat16); spatial_shapes int64 [L,2] (H,W);
@@ -159,6 +181,7 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, a
     return out
 
 
+@_given_stream
 def msda_forward_frames(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
                         weight_mode=MSDA_WEIGHTS_LOGITS, out=None, stream=None):
     """value [B,F,Nv,nH,Dh]; sampling_locations [B,F,Nq,nH,L,P,2];
@@ -186,6 +209,7 @@ def sca_workspace_size(B, Ncam, Nq):
     return n.value
 
 
+@_given_stream
 def sca_forward(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
                 attention_logits, slots=None, hit_count=None, pair_offsets=None, pair_q=None, workspace=None,
                 stream=None):
@@ -222,6 +246,7 @@ def sca_forward(value, spatial_shapes, level_start_index, reference_points_cam, 
     return slots
 
 
+@_given_stream
 def sca_compact(bev_mask, reference_points_cam, workspace, hit_count=None, pair_offsets=None, pair_q=None,
                 stream=None):
     """Stage 1 of sca_forward: bev_mask uint8|bool [Ncam,B,Nq,D] and
@@ -239,6 +264,7 @@ def sca_compact(bev_mask, reference_points_cam, workspace, hit_count=None, pair_
     _check("sca_compact", rc)
 
 
+@_given_stream
 def sca_gather(value, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets, attention_logits,
                workspace, slots=None, stream=None):
     """Stage 2 of sca_forward: gather, weighted sums and camera mean for the
@@ -261,6 +287,7 @@ def sca_gather(value, spatial_shapes, level_start_index, reference_points_cam, s
     return slots
 
 
+@_given_stream
 def msda_gemm_bf16(X, W, bias=None, y_dtype=torch.bfloat16, out=None, stream=None):
     """Y = X W^T + bias.  X [M,K] bfloat16 (or float32, rounded to bf16 as
     read); W bfloat16 [N,K]; bias float32 [N] or None.  Returns Y [M,N] of
@@ -279,6 +306,7 @@ def msda_gemm_bf16(X, W, bias=None, y_dtype=torch.bfloat16, out=None, stream=Non
     return out
 
 
+@_given_stream
 def msda_query_proj_bf16(query, W_off, b_off, W_att, b_att, query_pos=None, offsets=None, logits=None,
                          stream=None):
     """Sampling offsets and attention logits from the query in one launch:
@@ -302,6 +330,7 @@ def msda_query_proj_bf16(query, W_off, b_off, W_att, b_att, query_pos=None, offs
     return offsets, logits
 
 
+@_given_stream
 def msda_output_proj_bf16(X, W, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, out=None, stream=None):
     """residual + (bf16(X) W^T + bias), then, with gamma, the layer norm of
     each row (divisor N, eps inside the square root) scaled by gamma and
@@ -323,6 +352,7 @@ def msda_output_proj_bf16(X, W, bias=None, residual=None, gamma=None, beta=None,
     return out
 
 
+@_given_stream
 def sca_rebatch(pair_offsets, pair_q, reference_points_cam, sampling_offsets, attention_logits, spatial_shapes,
                 max_len, sampling_locations=None, logits_out=None, stream=None):
     """Padded rebatch of the pair lists (A/B baseline): sampling locations
@@ -349,6 +379,7 @@ def sca_rebatch(pair_offsets, pair_q, reference_points_cam, sampling_offsets, at
     return sampling_locations, logits_out
 
 
+@_given_stream
 def sca_scatter_mean(rows, pair_offsets, pair_q, hit_count, Nq, slots=None, stream=None):
     """slots[b, q] = mean over the cameras that see q of their segment rows
     (zero where no camera does).  rows float32 [B*Ncam, max_len, C];
@@ -367,6 +398,7 @@ def sca_scatter_mean(rows, pair_offsets, pair_q, hit_count, Nq, slots=None, stre
     return slots
 
 
+@_given_stream
 def sca_forward_rebatch(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
                         attention_logits, workspace=None, stream=None):
     """SCA through the padded rebatch flow (A/B baseline for sca_forward):
@@ -418,6 +450,7 @@ def _grad_workspace(given, nbytes, dev):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
 
 
+@_given_stream
 def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights, grad_out,
                   weight_mode=MSDA_WEIGHTS_LOGITS, grad_value=None, grad_locations=None, grad_weights=None,
                   grad_workspace=None, atomic=False, stream=None):
@@ -453,6 +486,7 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, 
     return grad_value, grad_locations, grad_weights
 
 
+@_given_stream
 def msda_backward_frames(value, spatial_shapes, level_start_index, sampling_locations, attention_weights, grad_out,
                          weight_mode=MSDA_WEIGHTS_LOGITS, grad_value=None, grad_locations=None, grad_weights=None,
                          grad_workspace=None, atomic=False, stream=None):
@@ -489,6 +523,7 @@ def msda_backward_frames(value, spatial_shapes, level_start_index, sampling_loca
     return grad_value, grad_locations, grad_weights
 
 
+@_given_stream
 def sca_backward(value, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets, attention_logits,
                  grad_slots, workspace, grad_value=None, grad_offsets=None, grad_logits=None, max_pairs=0,
                  grad_workspace=None, atomic=False, stream=None):
