@@ -125,6 +125,23 @@ def _ptr(t, name, dtypes=None):
     return t.data_ptr()
 
 
+def _numel(t, name, n, at_least=False):
+    """Element count of a tensor the C call reads (exactly n) or writes (at
+    least n) as flat contiguous memory: a smaller one would send the kernels
+    past its end."""
+    if t is None:
+        return
+    k = t.numel()
+    if k < n or (not at_least and k != n):
+        raise ValueError(f"{name}: {'at least ' if at_least else ''}{n} elements expected, got {k} "
+                         f"(shape {tuple(t.shape)})")
+
+
+def _levels(spatial_shapes, level_start_index, L):
+    _numel(spatial_shapes, "spatial_shapes", 2 * L)
+    _numel(level_start_index, "level_start_index", L)
+
+
 def _value_dtype(value):
     if value.dtype == torch.float32:
         return MSDA_F32
@@ -170,6 +187,10 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, a
     lib = load_library()
     B, Nv, nH, Dh = value.shape
     _, Nq, _, L, P, _ = sampling_locations.shape
+    _levels(spatial_shapes, level_start_index, L)
+    _numel(sampling_locations, "sampling_locations", B * Nq * nH * L * P * 2)
+    _numel(attention_weights, "attention_weights", B * Nq * nH * L * P)
+    _numel(out, "out", B * Nq * nH * Dh, at_least=True)
     if out is None:
         out = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=value.device)
     rc = lib.msda_forward(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
@@ -190,6 +211,10 @@ def msda_forward_frames(value, spatial_shapes, level_start_index, sampling_locat
     lib = load_library()
     B, F, Nv, nH, Dh = value.shape
     _, _, Nq, _, L, P, _ = sampling_locations.shape
+    _levels(spatial_shapes, level_start_index, L)
+    _numel(sampling_locations, "sampling_locations", B * F * Nq * nH * L * P * 2)
+    _numel(attention_weights, "attention_weights", B * F * Nq * nH * L * P)
+    _numel(out, "out", B * Nq * nH * Dh, at_least=True)
     if out is None:
         out = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=value.device)
     rc = lib.msda_forward_frames(_ptr(value, "value"), _value_dtype(value),
@@ -209,6 +234,20 @@ def sca_workspace_size(B, Ncam, Nq):
     return n.value
 
 
+def _sca_inputs(B, Ncam, Nq, D, nH, L, P, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets,
+                attention_logits):
+    _levels(spatial_shapes, level_start_index, L)
+    _numel(reference_points_cam, "reference_points_cam", Ncam * B * Nq * D * 2)
+    _numel(sampling_offsets, "sampling_offsets", B * Nq * nH * L * P * 2)
+    _numel(attention_logits, "attention_logits", B * Nq * nH * L * P)
+
+
+def _sca_outputs(B, Ncam, Nq, hit_count, pair_offsets, pair_q):
+    _numel(hit_count, "hit_count", B * Nq, at_least=True)
+    _numel(pair_offsets, "pair_offsets", B * Ncam + 1, at_least=True)
+    _numel(pair_q, "pair_q", B * Ncam * Nq, at_least=True)
+
+
 @_given_stream
 def sca_forward(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
                 attention_logits, slots=None, hit_count=None, pair_offsets=None, pair_q=None, workspace=None,
@@ -225,9 +264,14 @@ def sca_forward(value, spatial_shapes, level_start_index, reference_points_cam, 
     B, Ncam, Nv, nH, Dh = value.shape
     _, _, Nq, D, _ = reference_points_cam.shape
     _, _, _, L, P, _ = sampling_offsets.shape
+    _sca_inputs(B, Ncam, Nq, D, nH, L, P, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets,
+                attention_logits)
+    _numel(slots, "slots", B * Nq * nH * Dh, at_least=True)
     dev = value.device
     if slots is None:
         slots = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=dev)
+    _sca_outputs(B, Ncam, Nq, hit_count, pair_offsets, pair_q)
+    _numel(bev_mask, "bev_mask", Ncam * B * Nq * D)
     need = sca_workspace_size(B, Ncam, Nq)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -255,6 +299,8 @@ def sca_compact(bev_mask, reference_points_cam, workspace, hit_count=None, pair_
     pair_q when given)."""
     lib = load_library()
     Ncam, B, Nq, D = bev_mask.shape
+    _numel(reference_points_cam, "reference_points_cam", Ncam * B * Nq * D * 2)
+    _sca_outputs(B, Ncam, Nq, hit_count, pair_offsets, pair_q)
     i32 = (torch.int32,)
     rc = lib.sca_compact(_ptr(bev_mask, "bev_mask", (torch.uint8, torch.bool)),
                          _ptr(reference_points_cam, "reference_points_cam", _F32), B, Ncam, Nq, D,
@@ -273,6 +319,9 @@ def sca_gather(value, spatial_shapes, level_start_index, reference_points_cam, s
     B, Ncam, Nv, nH, Dh = value.shape
     _, _, Nq, D, _ = reference_points_cam.shape
     _, _, _, L, P, _ = sampling_offsets.shape
+    _sca_inputs(B, Ncam, Nq, D, nH, L, P, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets,
+                attention_logits)
+    _numel(slots, "slots", B * Nq * nH * Dh, at_least=True)
     dev = value.device
     if slots is None:
         slots = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=dev)
@@ -295,6 +344,9 @@ def msda_gemm_bf16(X, W, bias=None, y_dtype=torch.bfloat16, out=None, stream=Non
     lib = load_library()
     M, K = X.shape
     N = W.shape[0]
+    _numel(W, "W", N * K)
+    _numel(bias, "bias", N)
+    _numel(out, "out", M * N, at_least=True)
     if out is None:
         out = torch.empty((M, N), dtype=y_dtype, device=X.device)
     x_dt = MSDA_F32 if X.dtype == torch.float32 else MSDA_BF16
@@ -317,6 +369,13 @@ def msda_query_proj_bf16(query, W_off, b_off, W_att, b_att, query_pos=None, offs
     lib = load_library()
     M, K = query.shape
     N_off, N_att = W_off.shape[0], W_att.shape[0]
+    _numel(query_pos, "query_pos", M * K)
+    _numel(W_off, "W_off", N_off * K)
+    _numel(W_att, "W_att", N_att * K)
+    _numel(b_off, "b_off", N_off)
+    _numel(b_att, "b_att", N_att)
+    _numel(offsets, "offsets", M * N_off, at_least=True)
+    _numel(logits, "logits", M * N_att, at_least=True)
     if offsets is None:
         offsets = torch.empty((M, N_off), dtype=torch.float32, device=query.device)
     if logits is None:
@@ -340,6 +399,11 @@ def msda_output_proj_bf16(X, W, bias=None, residual=None, gamma=None, beta=None,
     lib = load_library()
     M, K = X.shape
     N = W.shape[0]
+    _numel(W, "W", N * K)
+    for t, name in ((bias, "bias"), (gamma, "gamma"), (beta, "beta")):
+        _numel(t, name, N)
+    _numel(residual, "residual", M * N)
+    _numel(out, "out", M * N, at_least=True)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=X.device)
     x_dt = MSDA_F32 if X.dtype == torch.float32 else MSDA_BF16
@@ -362,6 +426,12 @@ def sca_rebatch(pair_offsets, pair_q, reference_points_cam, sampling_offsets, at
     lib = load_library()
     Ncam, B, Nq, D, _ = reference_points_cam.shape
     _, _, nH, L, P, _ = sampling_offsets.shape
+    _numel(spatial_shapes, "spatial_shapes", 2 * L)
+    _numel(sampling_offsets, "sampling_offsets", B * Nq * nH * L * P * 2)
+    _numel(attention_logits, "attention_logits", B * Nq * nH * L * P)
+    _numel(pair_offsets, "pair_offsets", B * Ncam + 1)
+    _numel(sampling_locations, "sampling_locations", B * Ncam * max_len * nH * L * P * 2, at_least=True)
+    _numel(logits_out, "logits_out", B * Ncam * max_len * nH * L * P, at_least=True)
     dev = reference_points_cam.device
     if sampling_locations is None:
         sampling_locations = torch.empty((B * Ncam, max_len, nH, L, P, 2), dtype=torch.float32, device=dev)
@@ -388,6 +458,11 @@ def sca_scatter_mean(rows, pair_offsets, pair_q, hit_count, Nq, slots=None, stre
     BN, max_len, C = rows.shape
     B = hit_count.shape[0]
     Ncam = BN // max(B, 1)
+    if B * Ncam != BN:
+        raise ValueError(f"rows: {BN} segments is not a multiple of the batch {B} of hit_count")
+    _numel(hit_count, "hit_count", B * Nq)
+    _numel(pair_offsets, "pair_offsets", B * Ncam + 1)
+    _numel(slots, "slots", B * Nq * C, at_least=True)
     if slots is None:
         slots = torch.empty((B, Nq, C), dtype=torch.float32, device=rows.device)
     i32 = (torch.int32,)
@@ -450,6 +525,17 @@ def _grad_workspace(given, nbytes, dev):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
 
 
+def _grads_of(samples, locations, weights, grad_out, n_out, grad_value, n_value, grad_locations, grad_weights,
+              out_name="grad_out"):
+    """Sizes of a backward call's sample inputs, upstream gradient and outputs."""
+    _numel(locations, "sampling locations / offsets", 2 * samples)
+    _numel(weights, "attention weights / logits", samples)
+    _numel(grad_out, out_name, n_out)
+    _numel(grad_value, "grad_value", n_value, at_least=True)
+    _numel(grad_locations, "grad_locations / grad_offsets", 2 * samples, at_least=True)
+    _numel(grad_weights, "grad_weights / grad_logits", samples, at_least=True)
+
+
 @_given_stream
 def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights, grad_out,
                   weight_mode=MSDA_WEIGHTS_LOGITS, grad_value=None, grad_locations=None, grad_weights=None,
@@ -463,6 +549,9 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, 
     lib = load_library()
     B, Nv, nH, Dh = value.shape
     _, Nq, _, L, P, _ = sampling_locations.shape
+    _levels(spatial_shapes, level_start_index, L)
+    _grads_of(B * Nq * nH * L * P, sampling_locations, attention_weights, grad_out, B * Nq * nH * Dh, grad_value,
+              B * Nv * nH * Dh, grad_locations, grad_weights)
     dev = value.device
     if grad_value is None:
         grad_value = torch.empty((B, Nv, nH, Dh), dtype=torch.float32, device=dev)
@@ -498,6 +587,9 @@ def msda_backward_frames(value, spatial_shapes, level_start_index, sampling_loca
     lib = load_library()
     B, F, Nv, nH, Dh = value.shape
     _, _, Nq, _, L, P, _ = sampling_locations.shape
+    _levels(spatial_shapes, level_start_index, L)
+    _grads_of(B * F * Nq * nH * L * P, sampling_locations, attention_weights, grad_out, B * Nq * nH * Dh,
+              grad_value, B * F * Nv * nH * Dh, grad_locations, grad_weights)
     dev = value.device
     if grad_value is None:
         grad_value = torch.empty((B, F, Nv, nH, Dh), dtype=torch.float32, device=dev)
@@ -538,6 +630,10 @@ def sca_backward(value, spatial_shapes, level_start_index, reference_points_cam,
     B, Ncam, Nv, nH, Dh = value.shape
     _, _, Nq, D, _ = reference_points_cam.shape
     _, _, _, L, P, _ = sampling_offsets.shape
+    _sca_inputs(B, Ncam, Nq, D, nH, L, P, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets,
+                attention_logits)
+    _grads_of(B * Nq * nH * L * P, sampling_offsets, attention_logits, grad_slots, B * Nq * nH * Dh, grad_value,
+              B * Ncam * Nv * nH * Dh, grad_offsets, grad_logits, out_name="grad_slots")
     dev = value.device
     if grad_value is None:
         grad_value = torch.empty((B, Ncam, Nv, nH, Dh), dtype=torch.float32, device=dev)

@@ -372,3 +372,48 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         m.msda_forward(v, torch.zeros(1, 2, dtype=torch.int64), torch.zeros(1, dtype=torch.int64),
                        torch.zeros(1, 4, 8, 1, 4, 2), torch.zeros(1, 4, 8, 4))
+
+
+def _binding_calls():
+    """(call, the tensor whose size is wrong) for the Python binding, on CPU
+    tensors: the size checks come before any device use, so the calls raise
+    without a GPU; with every size right they stop at the device check."""
+    import torch
+    import scale_deformable_attention_forward_amd as m
+    i64, bf = torch.int64, torch.bfloat16
+    ss, st = torch.zeros(1, 2, dtype=i64), torch.zeros(1, dtype=i64)
+    v, loc, w = torch.zeros(1, 16, 8, 32), torch.zeros(1, 4, 8, 1, 4, 2), torch.zeros(1, 4, 8, 4)
+    go = torch.zeros(1, 4, 256)
+    sv, rho, mask = torch.zeros(1, 2, 16, 8, 32), torch.zeros(2, 1, 5, 4, 2), torch.zeros(2, 1, 5, 4, dtype=torch.uint8)
+    off, lg, ws = torch.zeros(1, 5, 8, 1, 4, 2), torch.zeros(1, 5, 8, 4), torch.zeros(64, dtype=torch.uint8)
+    X, Wt = torch.zeros(10, 32, dtype=bf), torch.zeros(16, 32, dtype=bf)
+    return {
+        None: lambda: m.msda_forward(v, ss, st, loc, w),
+        "attention_weights": lambda: m.msda_forward(v, ss, st, loc, torch.zeros(1, 4, 8, 3)),
+        "spatial_shapes": lambda: m.msda_forward(v, torch.zeros(2, 2, dtype=i64), st, loc, w),
+        "level_start_index": lambda: m.msda_forward(v, ss, torch.zeros(2, dtype=i64), loc, w),
+        "out": lambda: m.msda_forward(v, ss, st, loc, w, out=torch.zeros(1, 4, 255)),
+        "grad_out": lambda: m.msda_backward(v, ss, st, loc, w, torch.zeros(1, 4, 200)),
+        "grad_value": lambda: m.msda_backward(v, ss, st, loc, w, go, grad_value=torch.zeros(1, 15, 8, 32)),
+        "reference_points_cam": lambda: m.sca_forward(sv, ss, st, torch.zeros(3, 1, 5, 4, 2), mask, off, lg),
+        "bev_mask": lambda: m.sca_forward(sv, ss, st, rho, torch.zeros(2, 1, 5, 3, dtype=torch.uint8), off, lg),
+        "sampling_offsets": lambda: m.sca_gather(sv, ss, st, rho, torch.zeros(1, 5, 8, 1, 4, 2)[:, :4], lg, ws),
+        "pair_q": lambda: m.sca_compact(mask, rho, ws, pair_q=torch.zeros(9, dtype=torch.int32)),
+        "grad_slots": lambda: m.sca_backward(sv, ss, st, rho, off, lg, torch.zeros(1, 5, 255), ws),
+        "W": lambda: m.msda_gemm_bf16(X, torch.zeros(16, 31, dtype=bf)),
+        "residual": lambda: m.msda_output_proj_bf16(X, Wt, residual=torch.zeros(10, 15)),
+        "W_att": lambda: m.msda_query_proj_bf16(torch.zeros(10, 32), Wt, None, torch.zeros(8, 30, dtype=bf), None),
+        "rows": lambda: m.sca_scatter_mean(torch.zeros(3, 2, 256), torch.zeros(3, dtype=torch.int32),
+                                           torch.zeros(4, dtype=torch.int32), torch.zeros(2, 5, dtype=torch.int32), 5),
+    }
+
+
+@pytest.mark.parametrize("wrong", list(_binding_calls()), ids=lambda w: w or "all_right")
+def test_binding_checks_element_counts(wrong):
+    call = _binding_calls()[wrong]
+    if wrong is None:
+        with pytest.raises(ValueError, match="GPU device"):
+            call()
+    else:
+        with pytest.raises(ValueError, match=f"^{wrong}: "):
+            call()
