@@ -12,6 +12,18 @@
 #include "vgrad.hpp"
 #include "msda.h"
 
+int msda::device_cu_count() {
+  // initialised once (C++ guarantees one thread runs the initialiser)
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      return n;
+    return 256;
+  }();
+  return cus;
+}
+
 namespace {
 
 thread_local char g_last_error[512] = "";

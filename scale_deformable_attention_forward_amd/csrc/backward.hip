@@ -503,18 +503,6 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* p, int64_t n4) {
     p[e] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-static int bwd_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
-}
 
 static int bwd_waves(int LP) {
   int w = kBwdMaxWaves;
@@ -531,7 +519,7 @@ static hipError_t launch(Kernel kernel, int64_t n_items, int LP, const BackwardA
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, waves * kWave, smem) != hipSuccess || per_cu < 1)
     per_cu = 1;
   int64_t need = (n_items + waves - 1) / waves;
-  const int64_t cap = (int64_t)bwd_cus() * per_cu;
+  const int64_t cap = (int64_t)device_cu_count() * per_cu;
   if (need > cap) need = cap;
   if (need < 1) need = 1;
   const unsigned grid = (unsigned)((need + kXcds - 1) / kXcds * kXcds);

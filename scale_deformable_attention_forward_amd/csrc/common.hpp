@@ -9,6 +9,12 @@ namespace msda {
 constexpr int kWave = 64;  // CDNA wavefront width
 constexpr int kXcds = 8;   // MI355X: 8 accelerator dies, each with its own L2
 
+// Compute units of the device current at the first call (256 when the
+// runtime cannot say), read once per process; safe to call from several
+// threads.  Grids sized from it assume every device the library runs on has
+// as many.
+int device_cu_count();
+
 // Raw buffer resource over [base, base + bytes).  A load whose offset is at
 // or beyond `bytes` returns zeros and makes no memory request, which is how
 // corners outside the map are skipped without a branch.  Word 3 is the gfx9

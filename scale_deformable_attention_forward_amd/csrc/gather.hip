@@ -312,18 +312,6 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void s
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-static int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
-}
 
 static size_t smem_bytes(int LP, int waves) {
   return sizeof(Level) * kMaxLevels + sizeof(uint2) * (size_t)waves * kHeadSlots * meta_stride(LP);
@@ -354,7 +342,7 @@ static unsigned grid_for(Kernel kernel, int64_t n_items, int waves, size_t smem,
       (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, waves * kWave, smem) != hipSuccess || per_cu < 1))
     per_cu = 1;
   int64_t need = (n_items + waves - 1) / waves;
-  const int64_t cap = (int64_t)device_cus() * per_cu;
+  const int64_t cap = (int64_t)device_cu_count() * per_cu;
   if (need > cap) need = cap;
   if (need < 1) need = 1;
   return (unsigned)((need + kXcds - 1) / kXcds * kXcds);

@@ -370,18 +370,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
-static int gemm_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
-}
 
 template <bool kXF32, bool kXAdd, bool kRes, bool kNorm, bool kYF32>
 static hipError_t launch(const GemmArgs& a, hipStream_t stream) {
@@ -390,7 +378,7 @@ static hipError_t launch(const GemmArgs& a, hipStream_t stream) {
   const int64_t gy = (a.N + kBN - 1) / kBN;
   // one 8-wave block per CU (register-bound); with several column blocks the
   // x extent is cut so that all of them fit on the chip at once
-  int64_t bx = gemm_cus() / gy / kXcds * kXcds;
+  int64_t bx = device_cu_count() / gy / kXcds * kXcds;
   if (bx < kXcds) bx = kXcds;
   const int64_t tiles_up = (tiles + kXcds - 1) / kXcds * kXcds;
   if (bx > tiles_up) bx = tiles_up;

@@ -659,18 +659,6 @@ __global__ __launch_bounds__(256) void vgrad_long_rows_kernel(VgradArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-static int vgrad_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
-}
 
 hipError_t launch_vgrad_setup(const VgradArgs& a, bool sca, hipStream_t stream) {
   vgrad_setup_kernel<<<1, kSortBlock, 0, stream>>>(a, sca ? 1 : 0);
@@ -684,13 +672,14 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
   // blocks past the tiles in use return at once; the scatter's blocks are
   // persistent: as many as are resident at once
   const unsigned hist_blocks = (unsigned)(a.sort_tiles / kHistTiles);
-  static int scatter_per_cu = 0;
-  if (scatter_per_cu == 0 &&
-      (hipOccupancyMaxActiveBlocksPerMultiprocessor(&scatter_per_cu, vgrad_scatter_kernel<false>, kSortBlock, 0) !=
-           hipSuccess ||
-       scatter_per_cu < 1))
-    scatter_per_cu = 1;
-  const int64_t resident = (int64_t)vgrad_cus() * scatter_per_cu;
+  static const int scatter_per_cu = [] {  // initialised once, by one thread
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, vgrad_scatter_kernel<false>, kSortBlock, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    return n;
+  }();
+  const int64_t resident = (int64_t)device_cu_count() * scatter_per_cu;
   const unsigned scatter_blocks = (unsigned)(a.sort_tiles < resident ? a.sort_tiles : resident);
   int src = 0;
   for (int p = 0; p < a.passes; ++p) {
@@ -709,17 +698,17 @@ hipError_t launch_vgrad_rows(const VgradArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     src ^= 1;
   }
-  const int64_t cap = (int64_t)vgrad_cus() * 8;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
   int64_t blocks = (a.key_bound + 255) / 256;
   vgrad_clear_ranges_kernel<<<(unsigned)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap), 256, 0, stream>>>(a);
   vgrad_ranges_kernel<<<(unsigned)a.sort_tiles, 256, 0, stream>>>(a);
   const int64_t rows = a.images * (int64_t)a.Nv * a.nH;
   blocks = (rows + 31) / 32;  // 32 rows per block of 256 threads
-  const int64_t row_cap = (int64_t)vgrad_cus() * 16;
+  const int64_t row_cap = (int64_t)device_cu_count() * 16;
   blocks = blocks < row_cap ? blocks : row_cap;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // a multiple of the die count
   vgrad_rows_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a);
-  vgrad_long_rows_kernel<<<(unsigned)((vgrad_cus() * 8 + kXcds - 1) / kXcds * kXcds), 256, 0, stream>>>(a);
+  vgrad_long_rows_kernel<<<(unsigned)((device_cu_count() * 8 + kXcds - 1) / kXcds * kXcds), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
