@@ -30,6 +30,13 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it asynchronously; no entry point synchronises the
  *    host.  Buffers must stay valid until the stream has finished the work.
+ *    Every entry point enqueues kernels only (no memset or copy nodes), so
+ *    it can be captured into a HIP graph and replayed.
+ *  - Entry points may be called from several host threads at once.  Calls
+ *    that share a workspace must be ordered (the same stream, or events):
+ *    concurrent ones would overwrite each other's scratch.  The library
+ *    reads the compute-unit count of the device current at its first call
+ *    and sizes grids from it for every device.
  *  - Arguments are checked on the host before anything is enqueued.  A
  *    non-zero return means nothing was enqueued, except MSDA_ERR_HIP, which
  *    reports a failed launch (the stream may then hold part of the work).
