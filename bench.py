@@ -16,12 +16,14 @@ query + position embedding in one launch, and the output projection
 followed by the residual and the layer norm), "sca_bf16", "sca_rebatch"
 (the default workload through the padded rebatch flow of the SCA note, an
 A/B baseline: per-camera segments padded to the longest, the operator over
-all of them, scatter-add and divide), "sca_train" and "detr_train" (forward
-and backward of the default SCA layer and of the DETR encoder MSDA, the
-value gradient by the deterministic transpose gather; "_atomic" variants
-accumulate it with float32 atomics instead; the roofline then describes the
-backward kernel), "detr" (Deformable-DETR encoder MSDA),
-"tsa" (two stacked BEV maps, frame mean), "tiny".
+all of them, scatter-add and divide), "sca_train", "detr_train" and
+"tsa_train" (forward and backward of the default SCA layer, of the DETR
+encoder MSDA and of the two-frame mean, the value gradient by the
+deterministic transpose gather; "_atomic" variants accumulate it with
+float32 atomics instead; the roofline then describes the backward kernel),
+"detr" (Deformable-DETR encoder MSDA), "tsa" (two stacked BEV maps, frame
+mean), "sca_frame6" (one frame of the encoder: one compaction serving six
+SCA layers, each with its own value maps, offsets and logits), "tiny".
 
 Prints one JSON line.  value = bilinear samples per second (one sample = one
 (camera, query, head, level, point) bilinear read of 4 corners x 32
