@@ -162,7 +162,8 @@ def _given_stream(fn):
         if stream is None:
             return fn(*args, **kw)
         if not isinstance(stream, torch.cuda.Stream):
-            stream = torch.cuda.ExternalStream(int(stream))
+            # handle 0 is the null stream, which is torch's default stream
+            stream = torch.cuda.default_stream() if int(stream) == 0 else torch.cuda.ExternalStream(int(stream))
         with torch.cuda.stream(stream):
             return fn(*args, **kw)
     return call

@@ -152,6 +152,23 @@ CASES = [
 ]
 
 
+def test_raw_handles_and_the_null_stream():
+    """stream= also takes a raw hipStream_t handle, 0 being the null stream
+    (torch's default stream)."""
+    make, call = CASES[0][1], CASES[0][2]
+    src = {k: dev(v) for k, v in make().items()}
+    ref = [host(t) for t in _tensors_of(call(src, None))]
+    s = torch.cuda.Stream()
+    for handle in (0, s.cuda_stream):
+        got = _tensors_of(call(src, handle))
+        torch.cuda.synchronize()
+        assert all(a.tobytes() == host(b).tobytes() for a, b in zip(ref, got)), handle
+
+
+def _tensors_of(r):
+    return r if isinstance(r, tuple) else (r,)
+
+
 def _outputs(r):
     ts = r if isinstance(r, tuple) else (r,)
     return [host(x) for x in ts]
