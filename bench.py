@@ -27,17 +27,27 @@ SCA layers, each with its own value maps, offsets and logits), "tiny".
 
 Prints one JSON line.  value = bilinear samples per second (one sample = one
 (camera, query, head, level, point) bilinear read of 4 corners x 32
-channels) over the whole step; roofline = the gather kernel's effective
-bytes (all 4 nominal corners of every sample, plus offsets, logits, anchors,
-work list and output) per launch over its average launch time, measured with
-HIP events recorded on the stream the kernel runs on; breakdown = the same
-events around every part of the step (mean, p10/p50/p90); cold = the same
-step after a 1 GiB write that evicts L2 and the memory-side cache (the
-headline is warm, back to back, as a layer runs inside a network);
-batch_items_per_s = batch items (scenes) per second; roofline also carries
-the bytes of the corners that fall inside their map, which are the only ones
-the kernel actually reads; cpu_baseline = the CPU oracle on the same
-workload.
+channels) over the whole step.  Kernel figures come from HIP events
+recorded on the stream the kernels run on:
+  roofline         the main kernel against the 8 TB/s HBM peak, on the bytes
+                   one launch must move at least once (every value map, the
+                   per-query offsets or locations and weights, anchors,
+                   masks and output); traffic = the bytes it moved beyond L2
+                   in the committed counter run, while its sources match;
+  roofline_onchip  the corner rows inside their map that the kernel reads,
+                   per second, against the same kernel's rate when every
+                   one of them sits in L2 (the level sides divided by 8,
+                   same samples and work order), measured in the same run:
+                   the ceiling of its vector-memory path;
+  effective        all 4 nominal corners x 32 channels of every sample plus
+                   metadata and output, per second: most of these bytes
+                   come from L1 and L2, so it is a rate, not a fraction;
+breakdown = the same events around every part of the step (mean,
+p10/p50/p90); cold = the same step after a 1 GiB write that evicts L2 and
+the memory-side cache (the headline is warm, back to back, as a layer runs
+inside a network); batch_items_per_s = batch items (scenes) per second;
+cpu_baseline = the CPU oracle on the same workload (or a bounded sample of
+it), on one thread and on every core this process may use.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --calibrate-copy   (a plain device copy of known size, for
@@ -120,6 +130,150 @@ def calibrate_copy():
     print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4}))
 
 
+def _query_chunks(n, k):
+    """k contiguous ranges covering range(n) (empty ones dropped)."""
+    import numpy as np
+    return [r for r in np.array_split(np.arange(n, dtype=np.int64), k) if len(r)]
+
+
+def time_oracle(phases, n_samples, what, cores=None):
+    """Times the CPU oracle over a bounded sample of a workload, given as
+    phases of independent tasks (a phase may use what the one before
+    wrote): first every task one after the other on one thread, then each
+    phase's tasks spread over every core this process may use.  ctypes
+    releases the interpreter lock while the C oracle runs, and numpy's BLAS
+    is held to one thread per task, so the second figure is the same oracle
+    on `cores` threads; the oracle itself is not changed for it."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    cores = cores or len(os.sched_getaffinity(0))
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for phase in phases:
+            for task in phase:
+                task()
+        t_one = time.perf_counter() - t0
+        with ThreadPoolExecutor(cores) as ex:
+            t0 = time.perf_counter()
+            for phase in phases:
+                list(ex.map(lambda task: task(), phase))
+            t_all = time.perf_counter() - t0
+    tasks = sum(len(p) for p in phases)
+    return {"value": n_samples / t_all, "unit": "samples/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what} ({n_samples} samples); {tasks} independent tasks on {cores} threads "
+                      f"{t_all:.2f} s, on one thread {t_one:.2f} s",
+            "seconds": t_all, "single_thread": {"value": n_samples / t_one, "cores": 1, "seconds": t_one}}
+
+
+def _sca_samples(w, rows=None):
+    """Bilinear samples of an SCA workload: every (camera, query) pair a
+    camera sees, times heads x levels x points (restricted to flat query
+    rows b*Nq + q when given).  Measurement metadata only."""
+    import numpy as np
+    hit = w["bev_mask"].any(-1).sum(0).reshape(-1)  # cameras seeing each (b, q)
+    if rows is not None:
+        hit = hit[rows]
+    return int(hit.sum()) * w["nH"] * w["L"] * w["P"]
+
+
+def sca_cpu_baseline(w, kind, cores=None, sampled_queries=4000):
+    """The oracle on an SCA workload: the whole of it for the single-layer
+    kinds; for the batch-4 layers the value projection of every row, then
+    (the query projections,) SCA and the output projection of
+    `sampled_queries` sampled queries."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    B, Ncam, Nq, Nv, nH, L, P = w["B"], w["Ncam"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"]
+    C = nH * 32
+    k = 4 * (cores or len(os.sched_getaffinity(0)))
+    geo = (w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"], w["bev_mask"])
+    if kind not in ("layer_bf16", "layer_full"):
+        value = w["value"]
+        tasks = [lambda r=r: oracle.sca(value, *geo, w["sampling_offsets"], w["attention_logits"], rows=r)
+                 for r in _query_chunks(B * Nq, k)]
+        what = f"the whole workload: all {B * Nq} queries" + (" of the first of the six layers"
+                                                              if kind == "sca_frame6" else "")
+        return time_oracle([tasks], _sca_samples(w), what, cores)
+    full = kind == "layer_full"
+    rows = W.sample_rows(7, B * Nq, sampled_queries)
+    feat = w["feat"].reshape(-1, C)
+    v = np.empty((B * Ncam * Nv, C), np.uint16)
+
+    def value_proj(r):
+        v[r] = oracle.round_to_bf16(oracle.linear_bf16_blas(feat[r], w["W_v"], w["b_v"]))
+    phases = [[lambda r=r: value_proj(r) for r in _query_chunks(B * Ncam * Nv, k)]]
+    if full:
+        q, e = w["query"].reshape(-1, C), w["query_pos"].reshape(-1, C)
+        off_rows = np.zeros((B * Nq, nH * L * P * 2), np.float32)
+        lg_rows = np.zeros((B * Nq, nH * L * P), np.float32)
+
+        def query_proj(r):
+            off_rows[r], lg_rows[r] = oracle.query_proj(q[r], e[r], w["W_off"], w["b_off"], w["W_att"], w["b_att"])
+        phases.append([lambda r=r: query_proj(r) for r in np.array_split(rows, k) if len(r)])
+        off, lg = off_rows.reshape(B, Nq, nH, L, P, 2), lg_rows.reshape(B, Nq, nH, L * P)
+    else:
+        off, lg = w["sampling_offsets"], w["attention_logits"]
+
+    def sca_and_output(r):
+        slots = oracle.sca(v.reshape(B, Ncam, Nv, nH, 32), *geo, off, lg, rows=r)["slots"]
+        if full:
+            oracle.output_proj(slots.astype(np.float32), w["W_o"], w["b_o"], q[r], w["gamma"], w["beta"])
+        else:
+            oracle.linear_bf16(oracle.round_to_bf16(slots), w["W_o"], w["b_o"])
+    phases.append([lambda r=r: sca_and_output(r) for r in np.array_split(rows, k) if len(r)])
+    what = (f"value projection of all {B * Ncam * Nv} rows, then {'query projections, ' if full else ''}SCA and "
+            f"output projection of {len(rows)} sampled queries; C loops and a float64 matmul")
+    return time_oracle(phases, _sca_samples(w, rows), what, cores)
+
+
+def msda_cpu_baseline(w, cores=None):
+    """The oracle's MSDA operator (or frame mean) over the whole workload."""
+    import oracle
+    k = 4 * (cores or len(os.sched_getaffinity(0)))
+    B, Nq, nH, L, P = w["B"], w["Nq"], w["nH"], w["L"], w["P"]
+    F = w.get("F", 1)
+    args = (w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"], w["attention_weights"])
+    fn = oracle.msda if F == 1 else oracle.msda_frames
+    tasks = [lambda r=r: fn(*args, True, rows=r) for r in _query_chunks(B * Nq, k)]
+    return time_oracle([tasks], B * F * Nq * nH * L * P, f"the whole workload: all {B * Nq} queries", cores)
+
+
+def train_cpu_baseline(w, which, grad, cores=None):
+    """The oracle's forward and backward over the whole workload, split into
+    query ranges, each run as a smaller problem of its own (the value
+    gradient of the whole is the sum of the ranges' ones; the timing keeps
+    them apart).  One range per core: each backward call fills a float64
+    value gradient of the whole map."""
+    import oracle
+    cores = cores or len(os.sched_getaffinity(0))
+    B, Nq, nH, L, P = w["B"], w["Nq"], w["nH"], w["L"], w["P"]
+    ranges = [slice(int(r[0]), int(r[-1]) + 1) for r in _query_chunks(Nq, cores)]
+    if which == "sca_train":
+        def task(s):
+            a = (w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"][:, :, s],
+                 w["bev_mask"][:, :, s], w["sampling_offsets"][:, s], w["attention_logits"][:, s])
+            oracle.sca(*a)
+            oracle.sca_backward(*a, grad[:, s])
+        n = _sca_samples(w)
+    elif which == "tsa_train":
+        def task(s):
+            a = (w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"][:, :, s],
+                 w["attention_weights"][:, :, s])
+            oracle.msda_frames(*a, True)
+            oracle.msda_frames_backward(*a, grad[:, s], weights_are_logits=True)
+        n = B * w["F"] * Nq * nH * L * P
+    else:
+        def task(s):
+            a = (w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"][:, s],
+                 w["attention_weights"][:, s])
+            oracle.msda(*a, True)
+            oracle.msda_backward(*a, grad[:, s], weights_are_logits=True)
+        n = B * Nq * nH * L * P
+    return time_oracle([[lambda s=s: task(s) for s in ranges]], n,
+                       f"the whole workload, forward and backward, over {len(ranges)} query ranges", cores)
+
+
 class Workload:
     """Inputs on the device and the step, as a list of named parts.  `main`
     names the dominant kernel's part; finish() fills in the sample count and
@@ -132,6 +286,8 @@ class Workload:
         self.extra = {}
         self.batch = 1
         self.inbounds_corners = None  # corners inside their map, per gather launch
+        self.unique_bytes = None  # bytes one launch of the main part must move at least once
+        self.onchip = None  # callable: the main kernel's rate with every corner row in L2
 
 
 def count_inbounds(shapes, x, y):
@@ -148,6 +304,104 @@ def count_inbounds(shapes, x, y):
         for dy in (0, 1):
             n += int(np.count_nonzero(inx & (y0 + dy >= 0) & (y0 + dy < H)))
     return n
+
+
+def sca_inbounds_corners(w, shapes, offsets):
+    """In-map corners of one SCA gather launch: every seen (camera, query)
+    pair's samples at anchor rho[p mod D] + offset / (W_l, H_l) on the
+    level table `shapes` (measurement metadata only)."""
+    import numpy as np
+    B, Ncam, L, P, D = w["B"], w["Ncam"], w["L"], w["P"], w["D"]
+    WH = np.stack([shapes[:, 1], shapes[:, 0]], -1).astype(np.float32)  # (W, H) per level
+    anchor = np.arange(P) % D
+    n_in = 0
+    for b in range(B):
+        for c in range(Ncam):
+            qs = np.nonzero(w["bev_mask"][c, b].any(-1))[0]
+            rho = w["reference_points_cam"][c, b, qs][:, anchor]  # [q, P, 2]
+            for l in range(L):
+                loc = rho[:, None, :, :] + offsets[b, qs][:, :, l] / WH[l]  # [q, nH, P, 2]
+                x = loc[..., 0].astype(np.float64) * WH[l, 0] - 0.5
+                y = loc[..., 1].astype(np.float64) * WH[l, 1] - 0.5
+                n_in += count_inbounds(shapes[l:l + 1], x[..., None, :], y[..., None, :])
+    return n_in
+
+
+CEILING_SHRINK = 8  # level sides divided by this for the on-chip ceiling
+
+
+def small_levels(shapes):
+    """The level table with every side divided by CEILING_SHRINK (rounded
+    up): every workload's value maps then fit in one die's L2 (the SCA
+    workload's six cameras: 3.2 MB in float32)."""
+    import numpy as np
+    ss = np.maximum(1, -(-np.asarray(shapes, np.int64) // CEILING_SHRINK))
+    starts = np.concatenate([[0], np.cumsum(ss[:, 0] * ss[:, 1])[:-1]]).astype(np.int64)
+    return ss.astype(np.int64), starts, int((ss[:, 0] * ss[:, 1]).sum())
+
+
+def _mean_launch_ms(fn, reps=20, warm=5):
+    """Mean duration of fn's launches, from HIP events recorded around each
+    on torch's current stream (the stream the binding launches on)."""
+    import numpy as np
+    import torch
+    for _ in range(warm):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
+
+def _ceiling(inb_bytes, ms, shapes):
+    return {"GBps": inb_bytes / (ms * 1e-3) / 1e9, "kernel_ms": ms, "inbounds_bytes_per_launch": inb_bytes,
+            "levels": "/".join(f"{h}x{wd}" for h, wd in shapes.tolist()),
+            "how": f"the same kernel on the same samples and work order, with every level side divided by "
+                   f"{CEILING_SHRINK} (offsets in cells scaled with it, so each sample keeps its normalised "
+                   f"location): every value map fits in L2, so nothing waits on memory beyond it"}
+
+
+def sca_onchip_ceiling(w, d, ws, offsets, bf16):
+    """The SCA gather kernel's rate of in-map corner bytes when every corner
+    row it reads sits in L2: the measured ceiling of the vector-memory path
+    for this kernel and sample mix."""
+    import numpy as np
+    import torch
+    import scale_deformable_attention_forward_amd as m
+    ss, starts, Nv = small_levels(w["spatial_shapes"])
+    scale = np.stack([ss[:, 1] / w["spatial_shapes"][:, 1], ss[:, 0] / w["spatial_shapes"][:, 0]], -1)
+    off = (offsets * scale[None, None, None, :, None, :]).astype(np.float32)
+    g = torch.Generator(device="cuda").manual_seed(12345)
+    value = torch.randn((w["B"], w["Ncam"], Nv, w["nH"], 32), generator=g, device="cuda")
+    value = value.to(torch.bfloat16) if bf16 else value
+    dss, dst, doff = _dev(ss), _dev(starts), _dev(off)
+    slots = torch.empty((w["B"], w["Nq"], w["nH"] * 32), dtype=torch.float32, device="cuda")
+    ms = _mean_launch_ms(lambda: m.sca_gather(value, dss, dst, d["reference_points_cam"], doff,
+                                              d["attention_logits"], ws, slots=slots))
+    return _ceiling(sca_inbounds_corners(w, ss, off) * 32 * (2 if bf16 else 4), ms, ss)
+
+
+def msda_onchip_ceiling(w, d, F):
+    """As sca_onchip_ceiling, for the operator (or frame mean): the same
+    normalised locations on the shrunken level table."""
+    import numpy as np
+    import torch
+    import scale_deformable_attention_forward_amd as m
+    ss, starts, Nv = small_levels(w["spatial_shapes"])
+    B, Nq, nH = w["B"], w["Nq"], w["nH"]
+    g = torch.Generator(device="cuda").manual_seed(12345)
+    value = torch.randn(((B, F) if F > 1 else (B,)) + (Nv, nH, 32), generator=g, device="cuda")
+    dss, dst = _dev(ss), _dev(starts)
+    out = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
+    fn = m.msda_forward if F == 1 else m.msda_forward_frames
+    ms = _mean_launch_ms(lambda: fn(value, dss, dst, d["sampling_locations"], d["attention_weights"], out=out))
+    loc = w["sampling_locations"]
+    inb = count_inbounds(ss, loc[..., 0] * ss[:, 1].astype(np.float64)[:, None] - 0.5,
+                         loc[..., 1] * ss[:, 0].astype(np.float64)[:, None] - 0.5)
+    return _ceiling(inb * 32 * 4, ms, ss)
 
 
 def _dev(a):
@@ -238,20 +492,7 @@ def sca_workload(kind):
         # corners inside their map: per visible pair, from the offsets the
         # gather reads (read back after the warm-up for the whole layer)
         off_h = d["sampling_offsets"].cpu().numpy() if full else w["sampling_offsets"]
-        ss = w["spatial_shapes"]
-        WH = np.stack([ss[:, 1], ss[:, 0]], -1).astype(np.float32)  # (W, H) per level
-        anchor = np.arange(P) % D
-        n_in = 0
-        for b in range(B):
-            for c in range(Ncam):
-                qs = np.nonzero(w["bev_mask"][c, b].any(-1))[0]
-                rho = w["reference_points_cam"][c, b, qs][:, anchor]  # [q, P, 2]
-                for l in range(L):
-                    loc = rho[:, None, :, :] + off_h[b, qs][:, :, l] / WH[l]  # [q, nH, P, 2]
-                    x = loc[..., 0].astype(np.float64) * WH[l, 0] - 0.5
-                    y = loc[..., 1].astype(np.float64) * WH[l, 1] - 0.5
-                    n_in += count_inbounds(ss[l:l + 1], x[..., None, :], y[..., None, :])
-        wl.inbounds_corners = n_in
+        wl.inbounds_corners = sca_inbounds_corners(w, w["spatial_shapes"], off_h)
         elem = 2 if bf16 else 4
         wl.samples = n_pairs * nH * L * P * layers
         # effective bytes of one gather launch: 4 nominal corners x 32 channels
@@ -260,6 +501,12 @@ def sca_workload(kind):
         wl.gathered_bytes = n_pairs * nH * L * P * 4 * 32 * elem  # one launch (the first layer's)
         wl.eff_bytes = (wl.gathered_bytes + B * Nq * nH * L * P * (8 + 4) + n_pairs * D * 8 + B * Nq * (4 + 4)
                         + B * Nq * C * 4)
+        # what one gather launch must move at least once: every value map,
+        # the per-query offsets and logits, the seen pairs' anchors, the
+        # camera masks and work list, and the output rows
+        wl.unique_bytes = (B * Ncam * Nv * C * elem + B * Nq * nH * L * P * (8 + 4) + n_pairs * D * 8
+                           + B * Nq * (4 + 4) + B * Nq * C * 4)
+        wl.onchip = lambda: sca_onchip_ceiling(w, d, ws, off_h, bf16)
         if layer:
             Mv, Mo = B * Ncam * Nv, B * Nq
             wl.extra["value_proj"] = {"flop": 2 * Mv * C * C, "bytes": Mv * C * 2 * 2 + C * C * 2}
@@ -283,47 +530,7 @@ def sca_workload(kind):
     wl.dtype = "fp32 accumulate, bf16 value" if bf16 else "fp32"
     wl.kernel_key = "sca_gather_kernel_bf16" if bf16 else "sca_gather_kernel_fp32"
 
-    def cpu_baseline():
-        import oracle
-        if layer:
-            # bounded sample: the value projection of every row (float64
-            # matmul), then (query projections,) SCA and output projection of
-            # 4000 sampled queries
-            import numpy as np
-            rows = W.sample_rows(7, B * Nq, 4000)
-            t0 = time.perf_counter()
-            if full:
-                q, e = w["query"].reshape(-1, C), w["query_pos"].reshape(-1, C)
-                o_off, o_lg = oracle.query_proj(q[rows], e[rows], w["W_off"], w["b_off"], w["W_att"], w["b_att"])
-                off = np.zeros((B * Nq, o_off.shape[1]), np.float32)
-                lg = np.zeros((B * Nq, o_lg.shape[1]), np.float32)
-                off[rows], lg[rows] = o_off, o_lg
-                off, lg = off.reshape(B, Nq, nH, L, P, 2), lg.reshape(B, Nq, nH, L * P)
-            else:
-                off, lg = w["sampling_offsets"], w["attention_logits"]
-            v = oracle.round_to_bf16(oracle.linear_bf16_blas(w["feat"].reshape(-1, C), w["W_v"], w["b_v"]))
-            r = oracle.sca(v.reshape(B, Ncam, Nv, nH, 32), w["spatial_shapes"], w["level_start_index"],
-                           w["reference_points_cam"], w["bev_mask"], off, lg, rows=rows)
-            if full:
-                oracle.output_proj(r["slots"].astype(np.float32), w["W_o"], w["b_o"], q[rows], w["gamma"],
-                                   w["beta"])
-            else:
-                oracle.linear_bf16(oracle.round_to_bf16(r["slots"]), w["W_o"], w["b_o"])
-            t = time.perf_counter() - t0
-            n = int(r["hit_count"].reshape(-1)[rows].sum()) * nH * L * P
-            return {"value": n / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
-                    "sample": f"value projection of all rows, then {'query projections, ' if full else ''}SCA and "
-                              f"output projection of 4000 sampled queries ({n} samples); C loops and a float64 "
-                              f"matmul, {t:.1f} s"}
-        t0 = time.perf_counter()
-        oracle.sca(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
-                   w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
-        t = time.perf_counter() - t0
-        n = wl.samples // layers
-        return {"value": n / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
-                "sample": f"the whole workload (all {B * Nq} queries, {n} samples{', the first layer' if layers > 1 else ''}), "
-                          f"single-threaded C, {t:.1f} s"}
-    wl.cpu_baseline = cpu_baseline
+    wl.cpu_baseline = lambda: sca_cpu_baseline(w, "layer_full" if full else "layer_bf16" if layer else kind)
     return wl
 
 
@@ -384,6 +591,7 @@ def rebatch_workload():
         padded = B * Ncam * st["ml"] * S
         wl.gathered_bytes = padded * 4 * 32 * 4
         wl.eff_bytes = wl.gathered_bytes + padded * 12 + B * Ncam * st["ml"] * C * 4
+        wl.unique_bytes = B * Ncam * Nv * C * 4 + padded * 12 + B * Ncam * st["ml"] * C * 4
         wl.extra_info = {"max_len": st["ml"], "padded_rows": B * Ncam * st["ml"], "pairs": n_pairs,
                          "padded_samples": padded}
     wl.finish = finish
@@ -396,17 +604,7 @@ def rebatch_workload():
     wl.dtype = "fp32"
     wl.kernel_key = "msda_gather_kernel_fp32"
 
-    def cpu_baseline():
-        import oracle
-        t0 = time.perf_counter()
-        oracle.sca(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
-                   w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
-        t = time.perf_counter() - t0
-        n = wl.samples // layers
-        return {"value": n / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
-                "sample": f"the whole workload (all {B * Nq} queries, {n} samples{', the first layer' if layers > 1 else ''}), "
-                          f"single-threaded C, {t:.1f} s"}
-    wl.cpu_baseline = cpu_baseline
+    wl.cpu_baseline = lambda: sca_cpu_baseline(w, "sca")
     return wl
 
 
@@ -429,7 +627,8 @@ def train_workload(which):
         B, Ncam, Nq, Nv, nH, L, P, D = w["B"], w["Ncam"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"], w["D"]
         d = {k: _dev(w[k]) for k in ("value", "spatial_shapes", "level_start_index", "reference_points_cam",
                                      "bev_mask", "sampling_offsets", "attention_logits")}
-        gout = _dev(W.upstream_gradient(3, (B, Nq, nH * 32)))
+        grad = W.upstream_gradient(3, (B, Nq, nH * 32))
+        gout = _dev(grad)
         ws = torch.empty(m.sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device="cuda")
         slots = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
         offs = torch.empty(B * Ncam + 1, dtype=torch.int32, device="cuda")
@@ -456,7 +655,8 @@ def train_workload(which):
         B, F, Nq, Nv, nH, L, P = w["B"], w["F"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"]
         d = {k: _dev(w[k]) for k in ("value", "spatial_shapes", "level_start_index", "sampling_locations",
                                      "attention_weights")}
-        gout = _dev(W.upstream_gradient(4, (B, Nq, nH * 32)))
+        grad = W.upstream_gradient(4, (B, Nq, nH * 32))
+        gout = _dev(grad)
         out = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
         gv = torch.empty((B, F, Nv, nH, 32), dtype=torch.float32, device="cuda")
         gloc = torch.empty_like(d["sampling_locations"])
@@ -478,7 +678,8 @@ def train_workload(which):
         B, Nq, Nv, nH, L, P = w["B"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"]
         d = {k: _dev(w[k]) for k in ("value", "spatial_shapes", "level_start_index", "sampling_locations",
                                      "attention_weights")}
-        gout = _dev(W.upstream_gradient(2, (B, Nq, nH * 32)))
+        grad = W.upstream_gradient(2, (B, Nq, nH * 32))
+        gout = _dev(grad)
         out = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
         gv = torch.empty((B, Nv, nH, 32), dtype=torch.float32, device="cuda")
         gloc = torch.empty_like(d["sampling_locations"])
@@ -509,6 +710,10 @@ def train_workload(which):
         rows = B * Nq * (F if which == "tsa_train" else 1)  # rows of locations / offsets and weights
         wl.eff_bytes = (2 * wl.gathered_bytes + rows * nH * L * P * (8 + 4) * 2 + B * Nq * nH * 32 * 4
                         + n_images * Nv * nH * 32 * 4)
+        # the backward must read the value maps, the per-query inputs and the
+        # upstream gradient once and write the three gradients once
+        wl.unique_bytes = (n_images * Nv * nH * 32 * 4 * 2 + rows * nH * L * P * (8 + 4) * 2
+                           + B * Nq * nH * 32 * 4)
     wl.finish = finish
     wl.batch = B
     wl.config = {"workload": names, "batch": B, "queries": Nq, "heads": nH, "head_dim": 32, "levels": L,
@@ -519,30 +724,7 @@ def train_workload(which):
     wl.dtype = "fp32"
     wl.kernel_key = ("sca_backward_kernel" if which == "sca_train" else "msda_backward_kernel") + "_fp32"
 
-    def cpu_baseline():
-        import oracle
-        t0 = time.perf_counter()
-        g = gout.cpu().numpy()
-        if which == "sca_train":
-            oracle.sca(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
-                       w["bev_mask"], w["sampling_offsets"], w["attention_logits"])
-            oracle.sca_backward(w["value"], w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
-                                w["bev_mask"], w["sampling_offsets"], w["attention_logits"], g)
-        elif which == "tsa_train":
-            oracle.msda_frames(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
-                               w["attention_weights"], True)
-            oracle.msda_frames_backward(w["value"], w["spatial_shapes"], w["level_start_index"],
-                                        w["sampling_locations"], w["attention_weights"], g, weights_are_logits=True)
-        else:
-            oracle.msda(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
-                        w["attention_weights"], True)
-            oracle.msda_backward(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
-                                 w["attention_weights"], g, weights_are_logits=True)
-        t = time.perf_counter() - t0
-        return {"value": wl.samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
-                "sample": f"the whole workload, forward and backward ({wl.samples} samples), "
-                          f"single-threaded C, {t:.1f} s"}
-    wl.cpu_baseline = cpu_baseline
+    wl.cpu_baseline = lambda: train_cpu_baseline(w, which, grad)
     return wl
 
 
@@ -578,6 +760,8 @@ def msda_workload(which):
         wl.inbounds_corners = count_inbounds(ss, loc[..., 0] * Wd - 0.5, loc[..., 1] * H - 0.5)
         wl.gathered_bytes = wl.samples * 4 * 32 * 4
         wl.eff_bytes = wl.gathered_bytes + wl.samples * (8 + 4) + B * Nq * nH * 32 * 4
+        wl.unique_bytes = w["value"].nbytes + wl.samples * (8 + 4) + B * Nq * nH * 32 * 4
+        wl.onchip = lambda: msda_onchip_ceiling(w, d, F)
     wl.finish = finish
     wl.batch = B
     names = {"detr": "Deformable-DETR encoder MSDA, 4 levels 100x150/50x75/25x38/13x19, Nq=Nv=19947",
@@ -588,19 +772,7 @@ def msda_workload(which):
     wl.dtype = "fp32"
     wl.kernel_key = "msda_gather_kernel_fp32"
 
-    def cpu_baseline():
-        import oracle
-        t0 = time.perf_counter()
-        if F == 1:
-            oracle.msda(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
-                        w["attention_weights"], True)
-        else:
-            oracle.msda_frames(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
-                               w["attention_weights"], True)
-        t = time.perf_counter() - t0
-        return {"value": wl.samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
-                "sample": f"the whole workload ({wl.samples} samples), single-threaded C, {t:.1f} s"}
-    wl.cpu_baseline = cpu_baseline
+    wl.cpu_baseline = lambda: msda_cpu_baseline(w)
     return wl
 
 
@@ -614,6 +786,8 @@ def main():
                              "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny", "sca_frame6",
                              "tsa_train", "tsa_train_atomic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-onchip-ceiling", action="store_true",
+                    help="skip the L2-resident run of the main kernel behind roofline_onchip")
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="steps timed after a 1 GiB write that evicts the caches (0: none)")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -701,7 +875,8 @@ def main():
             e["mfma_frac"] = e["TFLOP/s"] / BF16_MFMA_PEAK_TFS
             e["hbm_frac"] = e["GB/s"] / HBM_PEAK_GBS
         breakdown[name] = e
-    achieved = wl.eff_bytes / (kernel_ms * 1e-3) / 1e9
+    kernel_s = kernel_ms * 1e-3
+    achieved = wl.unique_bytes / kernel_s / 1e9
     line = {
         "metric": METRIC,
         "value": wl.samples / (ms_per_step * 1e-3),
@@ -716,12 +891,19 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded, BEVFormer-shaped; no dataset or trained weights)",
         "config": wl.config,
+        # HBM roofline on the bytes the launch must move at least once
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(wl.name, wl.kernel_key.rsplit("_", 1)[0]),
                      "kernel": wl.kernel_key.rsplit("_", 1)[0], "kernel_ms": kernel_ms,
-                     "effective_bytes_per_launch": wl.eff_bytes, "gathered_bytes_per_launch": wl.gathered_bytes},
-        "effective_GBps_per_step": wl.eff_bytes / (ms_per_step * 1e-3) / 1e9,
+                     "bytes_per_launch": wl.unique_bytes},
+        # effective bytes: all 4 nominal corners x 32 channels of every sample
+        # plus metadata and output, mostly served from L1 and L2: a rate, not
+        # a fraction of any memory's peak
+        "effective": {"bytes_per_launch": wl.eff_bytes, "gathered_bytes_per_launch": wl.gathered_bytes,
+                      "GBps": wl.eff_bytes / kernel_s / 1e9,
+                      "GBps_per_step": wl.eff_bytes / (ms_per_step * 1e-3) / 1e9,
+                      "times_hbm_peak": wl.eff_bytes / kernel_s / 1e9 / HBM_PEAK_GBS},
         "samples_per_step": wl.samples,
         "batch_items_per_s": wl.batch / (ms_per_step * 1e-3),
         "step_ms_events": pct(step_ms),
@@ -732,7 +914,17 @@ def main():
         line["config"].update(wl.extra_info)
     if wl.inbounds_corners is not None:
         elem = 2 if "bf16" in wl.dtype else 4
-        line["roofline"]["gathered_bytes_in_bounds_per_launch"] = wl.inbounds_corners * 32 * elem
+        inb = wl.inbounds_corners * 32 * elem
+        line["effective"]["gathered_bytes_in_bounds_per_launch"] = inb
+        if wl.onchip is not None and not args.no_onchip_ceiling:
+            # the corner rows the kernel reads, against the same kernel's
+            # rate when every one of them sits in L2
+            c = wl.onchip()
+            got = inb / kernel_s / 1e9
+            line["roofline_onchip"] = {"bound": "vector memory path (L1 / texture units)", "achieved": got,
+                                       "peak": c["GBps"], "unit": "GB/s", "frac": got / c["GBps"],
+                                       "kernel": line["roofline"]["kernel"], "bytes_per_launch": inb,
+                                       "ceiling": c}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = {**wl.cpu_baseline(), **host_cpu()}
     print(json.dumps(line), flush=True)

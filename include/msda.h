@@ -2,8 +2,8 @@
  * msda.h -- C ABI of libmsda.so: multi-scale deformable attention (MSDA) and
  * BEVFormer spatial cross-attention (SCA) on AMD Instinct MI355X (gfx950):
  *   msda_forward, msda_forward_frames        the MSDA operator (and a mean over frames)
- *   sca_workspace_size, sca_compact,
- *   sca_gather, sca_forward                  SCA: visibility, compaction, sampling, camera mean
+ *   sca_workspace_size (sca_plan_workspace),
+ *   sca_compact, sca_gather, sca_forward     SCA: visibility, compaction, sampling, camera mean
  *   msda_gemm_bf16, msda_query_proj_bf16,
  *   msda_output_proj_bf16                    the layer's bf16 projections on matrix cores
  *   sca_rebatch, sca_scatter_mean            the padded rebatch form of SCA (an A/B baseline)
@@ -129,6 +129,14 @@ int msda_forward_frames(const void* value, int value_dtype, const int64_t* spati
  * device.  Returns MSDA_OK and writes *bytes, or MSDA_ERR_INVALID_ARG.
  */
 int sca_workspace_size(int64_t B, int64_t Ncam, int64_t Nq, size_t* bytes);
+
+/*
+ * The same query under the name of the planning step: the bytes of SCA
+ * scratch (camera masks, pair lists, work order) that sca_forward,
+ * sca_compact and sca_gather need for (B, Ncam, Nq).  Identical results and
+ * status codes to sca_workspace_size.
+ */
+int sca_plan_workspace(int64_t B, int64_t Ncam, int64_t Nq, size_t* bytes);
 
 /*
  * Spatial cross-attention forward, from the camera masks to the camera mean
@@ -287,7 +295,11 @@ int msda_output_proj_bf16(const void* X, int x_dtype, const uint16_t* W, const f
  *                    += rows[b*Ncam + c][i] over its segment; then slots[b][q]
  *                    /= max(1, hit_count[b][q]).
  *
- *   pair_offsets, pair_q, hit_count  device int32, as written by sca_compact
+ *   pair_offsets, pair_q, hit_count  device int32, as written by sca_compact;
+ *                    pair_q holds B*Ncam*Nq entries.  Segment bounds are
+ *                    clamped to them and entries outside [0, Nq) are
+ *                    skipped, so a malformed list reads and writes nothing
+ *                    out of bounds (its result is then meaningless)
  *   reference_points_cam, sampling_offsets, attention_logits, spatial_shapes
  *                    as for sca_forward (device)
  *   sampling_locations device float [B*Ncam][max_len][nH][L][P][2]; logits_out

@@ -12,8 +12,8 @@ missing, importing works but every call raises: there is no fallback path.
 Functions (same names as the C entry points):
   operator:     msda_forward, msda_forward_frames, msda_backward,
                 msda_backward_frames, msda_backward_workspace_size
-  SCA:          sca_workspace_size, sca_forward, sca_compact, sca_gather,
-                sca_backward, sca_backward_workspace_size
+  SCA:          sca_workspace_size (also as sca_plan_workspace), sca_forward,
+                sca_compact, sca_gather, sca_backward, sca_backward_workspace_size
   padded flow:  sca_rebatch, sca_scatter_mean (and sca_forward_rebatch, which
                 chains them with the compaction and msda_forward)
   projections:  msda_gemm_bf16, msda_query_proj_bf16, msda_output_proj_bf16
@@ -27,7 +27,7 @@ import torch
 
 __all__ = [
     "MsdaError", "MSDA_F32", "MSDA_BF16", "MSDA_WEIGHTS_PROB", "MSDA_WEIGHTS_LOGITS",
-    "library_path", "load_library", "msda_forward", "msda_forward_frames", "sca_workspace_size",
+    "library_path", "load_library", "msda_forward", "msda_forward_frames", "sca_workspace_size", "sca_plan_workspace",
     "sca_forward", "sca_compact", "sca_gather", "msda_gemm_bf16", "msda_query_proj_bf16", "msda_output_proj_bf16",
     "sca_rebatch", "sca_scatter_mean", "sca_forward_rebatch", "msda_backward_workspace_size",
     "sca_backward_workspace_size", "msda_backward", "msda_backward_frames", "sca_backward", "msda_status_string",
@@ -69,6 +69,7 @@ def load_library():
     lib.msda_forward_frames.argtypes = [_p, _int, _p, _p, _p, _p, _int, _i64, _i64, _i64, _i64, _int, _int, _int,
                                         _int, _p, _p]
     lib.sca_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
+    lib.sca_plan_workspace.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
     lib.sca_forward.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int,
                                 _int, _p, _p, _p, _p, _p, _sz, _p]
     lib.sca_compact.argtypes = [_p, _p, _i64, _i64, _i64, _int, _p, _p, _p, _p, _sz, _p]
@@ -87,7 +88,7 @@ def load_library():
     lib.sca_scatter_mean.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p]
     lib.msda_query_proj_bf16.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]
     lib.msda_output_proj_bf16.argtypes = [_p, _int, _p, _p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p]
-    for f in (lib.msda_forward, lib.msda_forward_frames, lib.sca_workspace_size, lib.sca_forward,
+    for f in (lib.msda_forward, lib.msda_forward_frames, lib.sca_workspace_size, lib.sca_plan_workspace, lib.sca_forward,
               lib.sca_compact, lib.sca_gather, lib.msda_gemm_bf16):
         f.restype = _int
     lib.msda_status_string.argtypes = [_int]
@@ -232,6 +233,14 @@ def sca_workspace_size(B, Ncam, Nq):
     lib = load_library()
     n = _sz(0)
     _check("sca_workspace_size", lib.sca_workspace_size(int(B), int(Ncam), int(Nq), ctypes.byref(n)))
+    return n.value
+
+
+def sca_plan_workspace(B, Ncam, Nq):
+    """sca_workspace_size under the planning step's name (same result)."""
+    lib = load_library()
+    n = _sz(0)
+    _check("sca_plan_workspace", lib.sca_plan_workspace(int(B), int(Ncam), int(Nq), ctypes.byref(n)))
     return n.value
 
 
@@ -431,6 +440,7 @@ def sca_rebatch(pair_offsets, pair_q, reference_points_cam, sampling_offsets, at
     _numel(sampling_offsets, "sampling_offsets", B * Nq * nH * L * P * 2)
     _numel(attention_logits, "attention_logits", B * Nq * nH * L * P)
     _numel(pair_offsets, "pair_offsets", B * Ncam + 1)
+    _numel(pair_q, "pair_q", B * Ncam * Nq, at_least=True)
     _numel(sampling_locations, "sampling_locations", B * Ncam * max_len * nH * L * P * 2, at_least=True)
     _numel(logits_out, "logits_out", B * Ncam * max_len * nH * L * P, at_least=True)
     dev = reference_points_cam.device
@@ -463,6 +473,7 @@ def sca_scatter_mean(rows, pair_offsets, pair_q, hit_count, Nq, slots=None, stre
         raise ValueError(f"rows: {BN} segments is not a multiple of the batch {B} of hit_count")
     _numel(hit_count, "hit_count", B * Nq)
     _numel(pair_offsets, "pair_offsets", B * Ncam + 1)
+    _numel(pair_q, "pair_q", B * Ncam * Nq, at_least=True)
     _numel(slots, "slots", B * Nq * C, at_least=True)
     if slots is None:
         slots = torch.empty((B, Nq, C), dtype=torch.float32, device=rows.device)

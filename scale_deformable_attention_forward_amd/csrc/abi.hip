@@ -173,6 +173,10 @@ int sca_workspace_size(int64_t B, int64_t Ncam, int64_t Nq, size_t* bytes) {
   return MSDA_OK;
 }
 
+int sca_plan_workspace(int64_t B, int64_t Ncam, int64_t Nq, size_t* bytes) {
+  return sca_workspace_size(B, Ncam, Nq, bytes);
+}
+
 static int check_workspace(int64_t B, int64_t Ncam, int64_t Nq, const void* workspace, size_t workspace_bytes) {
   size_t need = 0;
   const int rc = sca_workspace_size(B, Ncam, Nq, &need);

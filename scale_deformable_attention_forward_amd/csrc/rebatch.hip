@@ -22,6 +22,18 @@
 
 namespace msda {
 
+// Start and length of segment bc of the pair lists, clamped to the n_pairs
+// entries pair_q can hold: a malformed pair_offsets array then reads and
+// writes nothing out of bounds (the rows it names are simply not added).
+__device__ inline void segment_bounds(const int32_t* pair_offsets, int64_t bc, int64_t n_pairs, int64_t* lo,
+                                      int64_t* len) {
+  int64_t s = pair_offsets[bc], e = pair_offsets[bc + 1];
+  s = s < 0 ? 0 : (s > n_pairs ? n_pairs : s);
+  e = e < s ? s : (e > n_pairs ? n_pairs : e);
+  *lo = s;
+  *len = e - s;
+}
+
 // one wavefront per padded row (segment bc, position i)
 __global__ __launch_bounds__(256) void sca_rebatch_kernel(RebatchArgs a) {
   const int lane = threadIdx.x % kWave;
@@ -32,9 +44,11 @@ __global__ __launch_bounds__(256) void sca_rebatch_kernel(RebatchArgs a) {
   for (int64_t r = wave0; r < rows; r += nwaves) {
     const int64_t bc = r / a.max_len, i = r % a.max_len;
     const int64_t b = bc / a.Ncam, c = bc % a.Ncam;
-    const int64_t lo = a.pair_offsets[bc], len = a.pair_offsets[bc + 1] - lo;
-    const bool live = i < len;
-    const int64_t q = live ? a.pair_q[lo + i] : 0;
+    int64_t lo, len;
+    segment_bounds(a.pair_offsets, bc, a.B * a.Ncam * a.Nq, &lo, &len);
+    int64_t q = i < len ? a.pair_q[lo + i] : -1;
+    const bool live = q >= 0 && q < a.Nq;  // an entry outside [0, Nq) is a padded row
+    q = live ? q : 0;
     float2* loc = reinterpret_cast<float2*>(a.loc_out) + r * S;
     float* w = a.logits_out + r * S;
     for (int s = lane; s < S; s += kWave) {
@@ -71,9 +85,11 @@ __global__ __launch_bounds__(256) void sca_scatter_kernel(ScatterArgs a, int c) 
   for (int64_t t = wave0; t < n; t += nwaves) {
     const int64_t b = t / a.max_len, i = t % a.max_len;
     const int64_t bc = b * a.Ncam + c;
-    const int64_t lo = a.pair_offsets[bc], len = a.pair_offsets[bc + 1] - lo;
+    int64_t lo, len;
+    segment_bounds(a.pair_offsets, bc, a.B * a.Ncam * a.Nq, &lo, &len);
     if (i >= len) continue;  // uniform over the wavefront
     const int64_t q = a.pair_q[lo + i];
+    if (q < 0 || q >= a.Nq) continue;
     const float4* src = reinterpret_cast<const float4*>(a.rows + (bc * a.max_len + i) * a.C);
     float4* dst = reinterpret_cast<float4*>(a.slots + (b * a.Nq + q) * a.C);
     for (int64_t e = lane; e < C4; e += kWave) {

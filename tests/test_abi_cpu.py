@@ -36,6 +36,27 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
 
 
+# the calls the boundary is planned around: the operator, the SCA workspace
+# query, the SCA forward, the bf16 projection and the status names
+PLANNED_BOUNDARY = ["msda_forward", "sca_plan_workspace", "sca_forward", "msda_gemm_bf16", "msda_status_string"]
+
+
+def test_header_declares_the_planned_boundary_names():
+    names = declared_functions()
+    for n in PLANNED_BOUNDARY:
+        assert n in names, n
+
+
+def test_plan_workspace_equals_workspace_size(lib):
+    for B, Ncam, Nq in [(1, 6, 40000), (4, 6, 40000), (2, 1, 0), (3, 32, 17)]:
+        a, b = _sz(0), _sz(0)
+        assert lib.sca_plan_workspace(B, Ncam, Nq, ctypes.byref(a)) == OK
+        assert lib.sca_workspace_size(B, Ncam, Nq, ctypes.byref(b)) == OK
+        assert a.value == b.value > 0
+    assert lib.sca_plan_workspace(0, 6, 10, ctypes.byref(_sz(0))) == INVALID
+    assert lib.sca_plan_workspace(1, 6, 10, None) == INVALID
+
+
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["msda_forward", "msda_forward_frames", "sca_workspace_size", "sca_forward", "msda_gemm_bf16",
@@ -375,7 +396,7 @@ def test_binding_refuses_cpu_tensors():
 
 
 def _binding_calls():
-    """(call, the tensor whose size is wrong) for the Python binding, on CPU
+    """(call, the tensor whose size is wrong, before any '/') for the Python binding, on CPU
     tensors: the size checks come before any device use, so the calls raise
     without a GPU; with every size right they stop at the device check."""
     import torch
@@ -405,6 +426,11 @@ def _binding_calls():
         "W_att": lambda: m.msda_query_proj_bf16(torch.zeros(10, 32), Wt, None, torch.zeros(8, 30, dtype=bf), None),
         "rows": lambda: m.sca_scatter_mean(torch.zeros(3, 2, 256), torch.zeros(3, dtype=torch.int32),
                                            torch.zeros(4, dtype=torch.int32), torch.zeros(2, 5, dtype=torch.int32), 5),
+        # pair lists shorter than B*Ncam*Nq entries would let a kernel read past them
+        "pair_q/scatter_mean": lambda: m.sca_scatter_mean(torch.zeros(2, 3, 256), torch.zeros(3, dtype=torch.int32),
+                                             torch.zeros(9, dtype=torch.int32), torch.zeros(1, 5, dtype=torch.int32), 5),
+        "pair_q/rebatch": lambda: m.sca_rebatch(torch.zeros(3, dtype=torch.int32), torch.zeros(9, dtype=torch.int32), rho,
+                                         off, lg, ss, 2),
     }
 
 
@@ -415,5 +441,5 @@ def test_binding_checks_element_counts(wrong):
         with pytest.raises(ValueError, match="GPU device"):
             call()
     else:
-        with pytest.raises(ValueError, match=f"^{wrong}: "):
+        with pytest.raises(ValueError, match=f"^{wrong.split('/')[0]}: "):
             call()
