@@ -20,7 +20,9 @@ Tolerances (written out here, used by every GPU test):
               element fed only by a few small-weight corners cannot meet a
               bound relative to its own small sum.
 """
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -104,3 +106,14 @@ def assert_sum_close(got, ref, abs_sum, what):
     assert not bad.any(), (f"{what}: {int(bad.sum())}/{bad.size} elements beyond the bar (worst err/tol "
                            f"{worst:.3g}; rms of the magnitudes {rms:.3g})")
     return worst
+
+
+def oracle_by_rows(fn, rows, threads=None):
+    """The oracle over many rows at once: fn(chunk) -> array [len(chunk), ...]
+    for contiguous chunks of `rows`, run on the host's cores (ctypes releases
+    the interpreter lock while the C oracle runs), stacked in row order."""
+    n = threads or min(16, len(os.sched_getaffinity(0)))
+    rows = np.asarray(rows, np.int64)
+    chunks = [c for c in np.array_split(rows, 4 * n) if len(c)]
+    with ThreadPoolExecutor(n) as ex:
+        return np.concatenate(list(ex.map(fn, chunks)))

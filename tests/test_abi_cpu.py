@@ -443,3 +443,4 @@ def test_binding_checks_element_counts(wrong):
     else:
         with pytest.raises(ValueError, match=f"^{wrong.split('/')[0]}: "):
             call()
+

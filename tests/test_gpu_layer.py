@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import announce, assert_abs_close, assert_fp32_close, dev, host
+from gpu_util import announce, assert_abs_close, assert_fp32_close, dev, host, oracle_by_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -27,29 +27,31 @@ def _bf16(g, shape, scale):
     return W.bf16_bits_trunc(g.normal(size=shape).astype(np.float32) * np.float32(scale))
 
 
-def _rows_with_tail(cfg, M, n):
-    """Sampled rows plus the last rows (the ragged tail tile)."""
-    return np.unique(np.concatenate([W.sample_rows(cfg, M, n), np.arange(max(0, M - 70), M)])).astype(np.int64)
-
-
 # ---------------------------------------------------------------------------
 # query projections
 # ---------------------------------------------------------------------------
 
+def _query_proj_rows(w, q, e):
+    """The oracle's offsets and logits of every row, side by side."""
+    n_off = w["W_off"].shape[0]
+    both = oracle_by_rows(lambda r: np.concatenate(oracle.query_proj(q[r], e[r], w["W_off"], w["b_off"], w["W_att"],
+                                                                     w["b_att"]), axis=1), np.arange(q.shape[0]))
+    return both[:, :n_off], both[:, n_off:]
+
+
 def test_query_proj_full_size():
     """The batch-4 bf16 layer workload's query path: M = 4 x 40000 queries, K = 256, offsets 512 and
-    logits 256 columns, with position embedding and biases.  Sampled rows and
-    the ragged tail against the oracle, float32 tolerance."""
+    logits 256 columns, with position embedding and biases.  Every row
+    against the oracle, float32 tolerance."""
     w = W.bevformer_layer_bf16(bias=True)
     q = w["query"].reshape(-1, 256)
     e = w["query_pos"].reshape(-1, 256)
     M = q.shape[0]
     off, lg = msda.msda_query_proj_bf16(dev(q), dev(w["W_off"]), dev(w["b_off"]), dev(w["W_att"]), dev(w["b_att"]),
                                         query_pos=dev(e))
-    rows = _rows_with_tail(61, M, 3000)
-    ref_off, ref_lg = oracle.query_proj(q[rows], e[rows], w["W_off"], w["b_off"], w["W_att"], w["b_att"])
-    assert_fp32_close(host(off)[rows], ref_off, "sampling offsets (sampled rows)")
-    assert_fp32_close(host(lg)[rows], ref_lg, "attention logits (sampled rows)")
+    ref_off, ref_lg = _query_proj_rows(w, q, e)
+    assert_fp32_close(host(off), ref_off, f"sampling offsets, all {M} rows")
+    assert_fp32_close(host(lg), ref_lg, f"attention logits, all {M} rows")
 
 
 QP_EDGE = [
@@ -92,14 +94,14 @@ def _out_case(seed, M, N, K):
 
 def test_output_proj_residual_norm_full_size():
     """The batch-4 bf16 layer workload's output side: M = 160000 slots rows, K = N = 256, residual
-    and layer norm; sampled rows and the tail, float32 tolerance."""
+    and layer norm; every row, float32 tolerance."""
     M = 4 * 40000
     c = _out_case(71, M, 256, 256)
     y = msda.msda_output_proj_bf16(dev(c["X"]), dev(c["W"]), dev(c["bias"]), residual=dev(c["res"]),
                                    gamma=dev(c["gamma"]), beta=dev(c["beta"]), eps=1e-5)
-    rows = _rows_with_tail(72, M, 3000)
-    ref = oracle.output_proj(c["X"][rows], c["W"], c["bias"], c["res"][rows], c["gamma"], c["beta"], 1e-5)
-    assert_fp32_close(host(y)[rows], ref, "projection + residual + norm (sampled rows)")
+    ref = oracle_by_rows(lambda r: oracle.output_proj(c["X"][r], c["W"], c["bias"], c["res"][r], c["gamma"],
+                                                      c["beta"], 1e-5), np.arange(M))
+    assert_fp32_close(host(y), ref, f"projection + residual + norm, all {M} rows")
 
 
 OP_EDGE = [
@@ -157,7 +159,7 @@ def test_whole_layer_bf16():
     """query -> offsets and logits (one launch); feat -> bf16 value; bev_mask ->
     compaction; sampling and camera mean; output projection + residual +
     layer norm.  The oracle runs its own chain (its own projections, its own
-    bf16 value) on sampled queries; 1e-2 absolute on the unit-scale result."""
+    bf16 value) on every query; 1e-2 absolute on the unit-scale result."""
     w = W.bevformer_layer_bf16(bias=True)
     B, Ncam, Nq, Nv = w["B"], w["Ncam"], w["Nq"], w["Nv"]
     C = 256
@@ -177,20 +179,18 @@ def test_whole_layer_bf16():
                                      gamma=dev(w["gamma"]), beta=dev(w["beta"]), eps=1e-5)
     got = host(out)
 
-    rows = W.sample_rows(81, B * Nq, 2000)
-    # oracle chain: offsets and logits of the sampled queries only (the
-    # oracle's SCA reads no other query's), its own value, its own slots
-    ref_off, ref_lg = oracle.query_proj(q[rows], e[rows], w["W_off"], w["b_off"], w["W_att"], w["b_att"])
-    off_full = np.zeros((B * Nq, 8 * L * P * 2), np.float32)
-    lg_full = np.zeros((B * Nq, 8 * L * P), np.float32)
-    off_full[rows] = ref_off
-    lg_full[rows] = ref_lg
+    # oracle chain on every query: its own offsets and logits, its own bf16
+    # value, its own slots, its own output projection + residual + norm
+    ref_off, ref_lg = _query_proj_rows(w, q, e)
+    ref_off = ref_off.astype(np.float32).reshape(B, Nq, 8, L, P, 2)
+    ref_lg = ref_lg.astype(np.float32).reshape(B, Nq, 8, L * P)
     ref_value = oracle.round_to_bf16(oracle.linear_bf16_blas(feat, w["W_v"], w["b_v"])).reshape(B, Ncam, Nv, 8, 32)
-    ref = oracle.sca(ref_value, w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
-                     w["bev_mask"], off_full.reshape(B, Nq, 8, L, P, 2), lg_full.reshape(B, Nq, 8, L * P), rows=rows)
-    ref_out = oracle.output_proj(ref["slots"].astype(np.float32), w["W_o"], w["b_o"], q[rows], w["gamma"],
-                                 w["beta"], 1e-5)
-    assert_abs_close(got[rows], ref_out, 1e-2, "whole layer output (sampled queries)")
+    ref_slots = oracle_by_rows(lambda r: oracle.sca(ref_value, w["spatial_shapes"], w["level_start_index"],
+                                                    w["reference_points_cam"], w["bev_mask"], ref_off, ref_lg,
+                                                    rows=r)["slots"], np.arange(B * Nq))
+    ref_out = oracle_by_rows(lambda r: oracle.output_proj(ref_slots[r].astype(np.float32), w["W_o"], w["b_o"], q[r],
+                                                          w["gamma"], w["beta"], 1e-5), np.arange(B * Nq))
+    assert_abs_close(got, ref_out, 1e-2, f"whole layer output, all {B * Nq} queries")
 
 
 def test_float32_to_bf16_rounding_on_ties():

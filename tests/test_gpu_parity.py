@@ -8,7 +8,7 @@ import torch
 import oracle
 import workloads as W
 from gpu_util import (announce, assert_abs_close, assert_bf16_ulp_close, assert_fp32_close, bf16_bits_to_f64, dev,
-                      host)
+                      host, oracle_by_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -119,30 +119,37 @@ def test_bevformer_sca_bf16_layer_with_projections():
     """The batch-4 bf16 layer workload: value projection (bf16 GEMM) -> SCA on bf16 value -> output
     projection (bf16 GEMM from fp32 slots).  The oracle runs its own chain:
     fp64 projection rounded to bf16, SCA on that, fp64 projection of the
-    bf16-rounded slots.  Checked on sampled rows at full size."""
+    bf16-rounded slots.  Every row of every stage is compared."""
     w = W.bevformer_sca_bf16(bias=True)
     B, Ncam, Nq, Nv = w["B"], w["Ncam"], w["Nq"], w["Nv"]
     C = 256
     feat = w["feat"].reshape(-1, C)
     M = feat.shape[0]
     v = msda.msda_gemm_bf16(dev(feat), dev(w["W_v"]), dev(w["b_v"]), y_dtype=torch.bfloat16)
+    v_host = host(v)
+    # every one of the 739,800 rows against the float64-matmul form of the
+    # oracle's projection, and sampled rows against its plain-loop form
+    proj = oracle.linear_bf16_blas(feat, w["W_v"], w["b_v"])
+    assert_bf16_ulp_close(v_host, proj, f"value projection, all {M} rows")
     rows_v = W.sample_rows(5, M, 2048)
-    ref_v = oracle.linear_bf16(feat[rows_v], w["W_v"], w["b_v"])
-    assert_bf16_ulp_close(host(v)[rows_v], ref_v, "value projection (sampled rows)")
+    assert_bf16_ulp_close(v_host[rows_v], oracle.linear_bf16(feat[rows_v], w["W_v"], w["b_v"]),
+                          "value projection (sampled rows, loop form)")
 
     # oracle value: its own projection, rounded to bf16, for every row
-    ref_value = oracle.round_to_bf16(oracle.linear_bf16_blas(feat, w["W_v"], w["b_v"])).reshape(B, Ncam, Nv, 8, 32)
+    ref_value = oracle.round_to_bf16(proj).reshape(B, Ncam, Nv, 8, 32)
+    del proj
     value_gpu = v.view(B, Ncam, Nv, 8, 32)
     got = run_sca(w, value=value_gpu)
-    rows = W.sample_rows(55, B * Nq, 3000)
-    ref = oracle_sca(w, value=ref_value, rows=rows)
+    ref = oracle.sca(ref_value, w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
+                     w["bev_mask"], w["sampling_offsets"], w["attention_logits"], want_slots=False)
     check_compaction(got, ref, "batch-4 bf16 layer")
-    assert_abs_close(got["slots"][rows], ref["slots"], 1e-2, "batch-4 bf16 layer SCA slots (sampled rows)")
+    ref_slots = oracle_by_rows(lambda r: oracle_sca(w, value=ref_value, rows=r)["slots"], np.arange(B * Nq))
+    assert_abs_close(got["slots"], ref_slots, 1e-2, f"batch-4 bf16 layer SCA slots, all {B * Nq} queries")
 
     slots_gpu = torch.from_numpy(got["slots"]).cuda()
     o = msda.msda_gemm_bf16(slots_gpu, dev(w["W_o"]), dev(w["b_o"]), y_dtype=torch.float32)
-    ref_o = oracle.linear_bf16(oracle.round_to_bf16(ref["slots"]), w["W_o"], w["b_o"])
-    assert_abs_close(host(o)[rows], ref_o, 1e-2, "batch-4 bf16 layer output projection (sampled rows)")
+    ref_o = oracle.linear_bf16_blas(oracle.round_to_bf16(ref_slots), w["W_o"], w["b_o"])
+    assert_abs_close(host(o), ref_o, 1e-2, f"batch-4 bf16 layer output projection, all {B * Nq} rows")
 
 
 # ---------------------------------------------------------------------------
