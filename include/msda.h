@@ -4,6 +4,7 @@
  *   msda_forward, msda_forward_frames        the MSDA operator (and a mean over frames)
  *   sca_workspace_size (sca_plan_workspace),
  *   sca_compact, sca_gather, sca_forward     SCA: visibility, compaction, sampling, camera mean
+ *   sca_forward_noalloc                      sca_forward with its workspace in a static device array
  *   msda_gemm_bf16, msda_query_proj_bf16,
  *   msda_output_proj_bf16                    the layer's bf16 projections on matrix cores
  *   sca_rebatch, sca_scatter_mean            the padded rebatch form of SCA (an A/B baseline)
@@ -420,6 +421,35 @@ int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shap
  * value row. */
 int sca_backward_workspace_size(int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int L, int P,
                                 int64_t max_pairs, size_t* bytes);
+
+/*
+ * sca_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, results and checks as sca_forward, with the SCA
+ * workspace taken from a static device array of MSDA_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) instead of a caller's buffer.  Nothing is allocated, by this call
+ * or by the library: each device the library runs on holds its own copy of
+ * the array from the first call on it until the process ends (that first
+ * call looks up the array's address, with the device current).
+ *   Arguments: as sca_forward, without workspace and workspace_bytes; the
+ *   caller still provides every input and output.
+ *   Limit: sca_workspace_size(B, Ncam, Nq) <= MSDA_NOALLOC_SCRATCH_BYTES
+ *   (6 cameras x 40000 queries need 1.43 MiB per batch item: up to B = 11);
+ *   beyond it MSDA_ERR_UNSUPPORTED, with nothing enqueued.
+ *   Every call on one device shares that device's array, which keeps the
+ *   last call's contents (each call clears what it needs cleared): calls
+ *   that can overlap on one device -- other streams, other host threads --
+ *   race and give wrong results; order them (one stream, or events).
+ *   One sca_forward_noalloc and later sca_gather calls cannot share the
+ *   array: use sca_forward with a workspace for a compaction that serves
+ *   several layers.
+ */
+#define MSDA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int sca_forward_noalloc(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                        const int64_t* level_start_index, const float* reference_points_cam,
+                        const uint8_t* bev_mask, const float* sampling_offsets, const float* attention_logits,
+                        int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, int D,
+                        float* slots, int32_t* hit_count, int32_t* pair_offsets, int32_t* pair_q, void* stream);
 
 /* Name of a status code (host; static string). */
 const char* msda_status_string(int status);

@@ -13,6 +13,7 @@ Functions (same names as the C entry points):
   operator:     msda_forward, msda_forward_frames, msda_backward,
                 msda_backward_frames, msda_backward_workspace_size
   SCA:          sca_workspace_size (also as sca_plan_workspace), sca_forward,
+                sca_forward_noalloc (workspace in a static device array),
                 sca_compact, sca_gather, sca_backward, sca_backward_workspace_size
   padded flow:  sca_rebatch, sca_scatter_mean (and sca_forward_rebatch, which
                 chains them with the compaction and msda_forward)
@@ -28,7 +29,7 @@ import torch
 __all__ = [
     "MsdaError", "MSDA_F32", "MSDA_BF16", "MSDA_WEIGHTS_PROB", "MSDA_WEIGHTS_LOGITS",
     "library_path", "load_library", "msda_forward", "msda_forward_frames", "sca_workspace_size", "sca_plan_workspace",
-    "sca_forward", "sca_compact", "sca_gather", "msda_gemm_bf16", "msda_query_proj_bf16", "msda_output_proj_bf16",
+    "sca_forward", "sca_forward_noalloc", "sca_compact", "sca_gather", "msda_gemm_bf16", "msda_query_proj_bf16", "msda_output_proj_bf16",
     "sca_rebatch", "sca_scatter_mean", "sca_forward_rebatch", "msda_backward_workspace_size",
     "sca_backward_workspace_size", "msda_backward", "msda_backward_frames", "sca_backward", "msda_status_string",
     "msda_last_error",
@@ -72,6 +73,8 @@ def load_library():
     lib.sca_plan_workspace.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
     lib.sca_forward.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int,
                                 _int, _p, _p, _p, _p, _p, _sz, _p]
+    lib.sca_forward_noalloc.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
+                                        _int, _int, _p, _p, _p, _p, _p]
     lib.sca_compact.argtypes = [_p, _p, _i64, _i64, _i64, _int, _p, _p, _p, _p, _sz, _p]
     lib.sca_gather.argtypes = [_p, _int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _int,
                                _p, _p, _sz, _p]
@@ -89,6 +92,7 @@ def load_library():
     lib.msda_query_proj_bf16.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]
     lib.msda_output_proj_bf16.argtypes = [_p, _int, _p, _p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p]
     for f in (lib.msda_forward, lib.msda_forward_frames, lib.sca_workspace_size, lib.sca_plan_workspace, lib.sca_forward,
+              lib.sca_forward_noalloc,
               lib.sca_compact, lib.sca_gather, lib.msda_gemm_bf16):
         f.restype = _int
     lib.msda_status_string.argtypes = [_int]
@@ -297,6 +301,39 @@ def sca_forward(value, spatial_shapes, level_start_index, reference_points_cam, 
                          _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                          _stream(stream, dev))
     _check("sca_forward", rc)
+    return slots
+
+
+@_given_stream
+def sca_forward_noalloc(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
+                        attention_logits, slots, hit_count=None, pair_offsets=None, pair_q=None, stream=None):
+    """sca_forward with the SCA workspace in the library's static device
+    array (16 MiB per device): neither the library nor this binding
+    allocates, so slots must be given.  Calls that may overlap on one device
+    race on that array; order them."""
+    lib = load_library()
+    B, Ncam, Nv, nH, Dh = value.shape
+    _, _, Nq, D, _ = reference_points_cam.shape
+    _, _, _, L, P, _ = sampling_offsets.shape
+    _sca_inputs(B, Ncam, Nq, D, nH, L, P, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets,
+                attention_logits)
+    if slots is None:
+        raise ValueError("slots: sca_forward_noalloc allocates nothing; pass the output tensor")
+    _numel(slots, "slots", B * Nq * nH * Dh, at_least=True)
+    _sca_outputs(B, Ncam, Nq, hit_count, pair_offsets, pair_q)
+    _numel(bev_mask, "bev_mask", Ncam * B * Nq * D)
+    i32 = (torch.int32,)
+    rc = lib.sca_forward_noalloc(_ptr(value, "value"), _value_dtype(value),
+                                 _ptr(spatial_shapes, "spatial_shapes", _I64),
+                                 _ptr(level_start_index, "level_start_index", _I64),
+                                 _ptr(reference_points_cam, "reference_points_cam", _F32),
+                                 _ptr(bev_mask, "bev_mask", (torch.uint8, torch.bool)),
+                                 _ptr(sampling_offsets, "sampling_offsets", _F32),
+                                 _ptr(attention_logits, "attention_logits", _F32), B, Ncam, Nv, Nq, nH, Dh, L, P, D,
+                                 _ptr(slots, "slots", _F32), _ptr(hit_count, "hit_count", i32),
+                                 _ptr(pair_offsets, "pair_offsets", i32), _ptr(pair_q, "pair_q", i32),
+                                 _stream(stream, value.device))
+    _check("sca_forward_noalloc", rc)
     return slots
 
 

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "backward.hpp"
 #include "gemm.hpp"
@@ -721,6 +722,64 @@ int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shap
   if (rc == MSDA_OK) rc = hip_status(msda::launch_sca_backward(a, st), "sca backward launch");
   if (rc == MSDA_OK) rc = hip_status(msda::launch_vgrad_rows(v, st), "value gradient rows");
   return rc;
+}
+
+// ---------------------------------------------------------------------------
+// sca_forward_noalloc: the SCA workspace in a static device array
+// ---------------------------------------------------------------------------
+// Each device the library runs on holds its own copy of this array from the
+// first call on it until the process ends.  In host code `scratch` names a
+// host-side stand-in: its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MSDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on its
+// first use on that device).
+int scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MSDA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MSDA_ERR_HIP, "hipGetSymbolAddress(scratch) returned no address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MSDA_OK;
+}
+
+}  // namespace
+
+int sca_forward_noalloc(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                        const int64_t* level_start_index, const float* reference_points_cam, const uint8_t* bev_mask,
+                        const float* sampling_offsets, const float* attention_logits, int64_t B, int64_t Ncam,
+                        int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, int D, float* slots, int32_t* hit_count,
+                        int32_t* pair_offsets, int32_t* pair_q, void* stream) {
+  size_t need = 0;
+  int rc = sca_workspace_size(B, Ncam, Nq, &need);
+  if (rc != MSDA_OK) return rc;
+  if (need > (size_t)MSDA_NOALLOC_SCRATCH_BYTES)
+    return fail(MSDA_ERR_UNSUPPORTED,
+                "B=%lld Ncam=%lld Nq=%lld needs %zu bytes of SCA scratch; sca_forward_noalloc holds %zu "
+                "(use sca_forward with a workspace)", (long long)B, (long long)Ncam, (long long)Nq, need,
+                (size_t)MSDA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  rc = scratch_for_current_device(&ws);
+  if (rc != MSDA_OK) return rc;
+  return sca_forward(value, value_dtype, spatial_shapes, level_start_index, reference_points_cam, bev_mask,
+                     sampling_offsets, attention_logits, B, Ncam, Nv, Nq, nH, Dh, L, P, D, slots, hit_count,
+                     pair_offsets, pair_q, ws, (size_t)MSDA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -444,3 +444,13 @@ def test_binding_checks_element_counts(wrong):
         with pytest.raises(ValueError, match=f"^{wrong.split('/')[0]}: "):
             call()
 
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """sca_forward_noalloc refuses, before any device call, a problem whose
+    SCA workspace exceeds the static scratch array (16 MiB)."""
+    need = _sz(0)
+    assert lib.sca_workspace_size(12, 6, 40000, ctypes.byref(need)) == OK and need.value > 16 << 20
+    args = (A, 0, A, A, A, A, A, A)
+    assert lib.sca_forward_noalloc(*args, 12, 6, 16, 40000, 8, 32, 4, 8, 4, B_, None, None, None, None) == UNSUPPORTED
+    assert "sca_forward_noalloc holds" in lib.msda_last_error().decode()
+    assert lib.sca_forward_noalloc(*args, 0, 6, 16, 4, 8, 32, 4, 8, 4, B_, None, None, None, None) == INVALID
