@@ -5,11 +5,13 @@ the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares
 no code with the HIP library and imports nothing from it.
 
 The arithmetic lives in ``oracle.c`` (plain loops, IEEE double); this module
-only marshals numpy arrays into it, apart from two compositions written out
-here: ``linear_bf16_blas`` (the bf16 projection with a float64 matmul as its
-contraction step) and ``msda_frames_backward`` (each frame's
-``msda_backward``, divided by the frame count).  Every function returns
-float64 arrays.
+only marshals numpy arrays into it, apart from three compositions written
+out here: ``linear_bf16_blas`` (the bf16 projection with a float64 matmul as
+its contraction step), ``msda_frames_backward`` (each frame's
+``msda_backward``, divided by the frame count) and ``sca_rebatch`` (the SCA
+note's padded flow: the compaction's segments, float32 locations, the
+operator over every padded row, the scatter-add and the divide).  Every
+function returns float64 arrays.
 """
 import ctypes
 import os
@@ -345,3 +347,58 @@ def bf16_to_float64(bits):
     lib = _load()
     flat = np.ascontiguousarray(bits, np.uint16).ravel()
     return np.array([lib.oracle_bf16_to_double(int(b)) for b in flat], np.float64).reshape(np.shape(bits))
+
+
+def sca_rebatch(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
+                attention_logits):
+    """Spatial cross-attention through the padded flow of the Tencent Cloud
+    SCA note (article 2321140: its rebatch code and its scatter / count /
+    divide code), step by step:
+      1. the compaction of sca(): per (batch item, camera), in b-major order,
+         the ascending list of the queries the camera sees, and the hit counts;
+      2. max_len = the longest list; every list is padded to it;
+      3. rebatch: for row i of segment (b, c), query q = list[i], the sampling
+         locations rho[c][b][q][p mod D] + (dx / W_l, dy / H_l) formed as the
+         float32 tensor the operator takes ("BEV(三) BEVFormer：Query 参数如何与
+         Feature 的 8 个 Head 交互", sections 5 and 18.4), and the query's logits;
+         padded rows are zero;
+      4. the operator msda() over the B*Ncam segments (value image b*Ncam + c);
+      5. scatter: each camera, in ascending order, adds its segment's rows to
+         the slots of its queries (padded rows are never added);
+      6. count and divide: slots / max(1, hit count).
+    Same arguments as sca().  Returns dict with sampling_locations
+    [B*Ncam, max_len, nH, L, P, 2] float32, logits [B*Ncam, max_len, nH, L*P]
+    float32, slots [B*Nq, nH*Dh] float64, max_len, and the compaction
+    (hit_count, pair_offsets, pair_q)."""
+    B, Ncam, Nv, nH, Dh = value.shape
+    _, _, Nq, D, _ = reference_points_cam.shape
+    _, _, _, L, P, _ = sampling_offsets.shape
+    comp = sca(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
+               attention_logits, want_slots=False)
+    offs, pq, hit = comp["pair_offsets"], comp["pair_q"], comp["hit_count"]
+    max_len = int(np.diff(offs).max()) if offs.size > 1 else 0
+    ss = np.asarray(spatial_shapes)
+    WH = np.stack([ss[:, 1], ss[:, 0]], -1).astype(np.float32)  # (W, H) per level
+    anchor = np.arange(P) % D
+    loc = np.zeros((B * Ncam, max_len, nH, L, P, 2), np.float32)
+    lg = np.zeros((B * Ncam, max_len, nH, L * P), np.float32)
+    for b in range(B):
+        for c in range(Ncam):
+            bc = b * Ncam + c
+            qs = pq[offs[bc]:offs[bc + 1]]
+            rho = reference_points_cam[c, b][qs][:, anchor]  # [n, P, 2]
+            loc[bc, :len(qs)] = rho[:, None, None] + sampling_offsets[b, qs] / WH[None, None, :, None, :]
+            lg[bc, :len(qs)] = attention_logits[b, qs]
+    C = nH * Dh
+    slots = np.zeros((B * Nq, C), np.float64)
+    if max_len > 0:
+        rows = msda(value.reshape(B * Ncam, Nv, nH, Dh), spatial_shapes, level_start_index, loc, lg,
+                    weights_are_logits=True).reshape(B * Ncam, max_len, C)
+        for c in range(Ncam):
+            for b in range(B):
+                bc = b * Ncam + c
+                qs = pq[offs[bc]:offs[bc + 1]]
+                slots[b * Nq + qs] += rows[bc, :len(qs)]
+    slots /= np.maximum(hit.reshape(-1), 1)[:, None]
+    return {"sampling_locations": loc, "logits": lg, "slots": slots, "max_len": max_len, "hit_count": hit,
+            "pair_offsets": offs, "pair_q": pq}

@@ -453,6 +453,37 @@ def pin_sca_dense_reformulation():
            oracle.sca(v_same, ss, starts, rho_same, one, off, logits)["slots"], 1e-12, "identical cameras")
 
 
+def pin_sca_rebatch_equals_fused_on_exact_locations():
+    """The SCA note's padded flow (oracle.sca_rebatch) against the fused
+    oracle.sca: with power-of-two level sides and anchors and offsets on a
+    coarse binary grid, rho + dx/W is exact in float32, so materialising the
+    locations loses nothing and both forms must agree bit for bit --
+    segments, padding (never added back), camera order and divide included.
+    Segments of unequal length and an empty one exercise the padding."""
+    shapes = ((8, 16), (4, 8))
+    ss, starts, Nv = level_table(shapes)
+    B, Ncam, Nq, D, P, nH, Dh = 2, 4, 11, 2, 4, 2, 3
+    L = len(ss)
+    g = np.random.default_rng(113)
+    value = g.normal(size=(B, Ncam, Nv, nH, Dh)).astype(np.float32)
+    mask = (g.random((Ncam, B, Nq, D)) < 0.4).astype(np.uint8)
+    mask[2, 1] = 0  # camera 2 sees nothing of batch item 1
+    rho = (g.integers(-100, 1124, (Ncam, B, Nq, D, 2)) / 1024.0).astype(np.float32)
+    off = (np.round(g.normal(0, 1.5, (B, Nq, nH, L, P, 2)) * 256) / 256).astype(np.float32)
+    logits = g.normal(size=(B, Nq, nH, L * P)).astype(np.float32)
+    args = (value, ss, starts, rho, mask, off, logits)
+    fused = oracle.sca(*args)
+    pad = oracle.sca_rebatch(*args)
+    lens = np.diff(pad["pair_offsets"])
+    assert lens.min() == 0 and len(set(lens.tolist())) > 2, "padding is exercised"
+    assert pad["max_len"] == lens.max()
+    for k in ("hit_count", "pair_offsets", "pair_q"):
+        assert np.array_equal(pad[k], fused[k]), k
+    for bc, n in enumerate(lens):
+        assert not pad["sampling_locations"][bc, n:].any() and not pad["logits"][bc, n:].any(), "padded rows"
+    assert np.array_equal(pad["slots"], fused["slots"]), "padded flow differs from the fused definition"
+
+
 # ---------------------------------------------------------------------------
 # bf16 and the projections ([8-heads] 3 and 11)
 # ---------------------------------------------------------------------------
@@ -756,6 +787,7 @@ ALL_PINS = [
     pin_sca_compaction_brute_force,
     pin_sca_exact_gather_and_camera_mean,
     pin_sca_dense_reformulation,
+    pin_sca_rebatch_equals_fused_on_exact_locations,
     pin_bf16_rounding,
     pin_linear_bf16,
     pin_query_proj,

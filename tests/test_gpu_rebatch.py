@@ -24,42 +24,11 @@ def _name_the_case(request):
 
 
 def rebatch_reference(w):
-    """The note's flow on the CPU: segment lists from the oracle's compaction,
-    locations rho + offset / (W, H) formed in float32 (the operator takes them
-    as a float32 tensor), the oracle's MSDA over every padded row, then the
-    per-camera scatter-add in ascending camera order and the divide, in
-    float64.  Returns (loc, logits, slots [B*Nq, C], max_len)."""
-    value = w["value"]
-    B, Ncam, Nv, nH, Dh = value.shape
-    Nq, L, P, D = w["Nq"], w["L"], w["P"], w["D"]
-    comp = oracle.sca(value, w["spatial_shapes"], w["level_start_index"], w["reference_points_cam"],
-                      w["bev_mask"], w["sampling_offsets"], w["attention_logits"], want_slots=False)
-    offs, pq, hit = comp["pair_offsets"], comp["pair_q"], comp["hit_count"]
-    max_len = int(np.diff(offs).max()) if offs.size > 1 else 0
-    ss = w["spatial_shapes"]
-    WH = np.stack([ss[:, 1], ss[:, 0]], -1).astype(np.float32)  # (W, H) per level
-    anchor = np.arange(P) % D
-    loc = np.zeros((B * Ncam, max_len, nH, L, P, 2), np.float32)
-    lg = np.zeros((B * Ncam, max_len, nH, L * P), np.float32)
-    for b in range(B):
-        for c in range(Ncam):
-            bc = b * Ncam + c
-            qs = pq[offs[bc]:offs[bc + 1]]
-            rho = w["reference_points_cam"][c, b][qs][:, anchor]  # [n, P, 2]
-            loc[bc, :len(qs)] = rho[:, None, None] + w["sampling_offsets"][b, qs] / WH[None, None, :, None, :]
-            lg[bc, :len(qs)] = w["attention_logits"][b, qs]
-    C = nH * Dh
-    slots = np.zeros((B * Nq, C), np.float64)
-    if max_len > 0:
-        rows = oracle.msda(value.reshape(B * Ncam, Nv, nH, Dh), w["spatial_shapes"], w["level_start_index"], loc, lg,
-                           weights_are_logits=True).reshape(B * Ncam, max_len, C)
-        for c in range(Ncam):
-            for b in range(B):
-                bc = b * Ncam + c
-                qs = pq[offs[bc]:offs[bc + 1]]
-                slots[b * Nq + qs] += rows[bc, :len(qs)]
-    slots /= np.maximum(hit.reshape(-1), 1)[:, None]
-    return loc, lg, slots, max_len
+    """The oracle's run of the note's flow: (locations, logits, slots
+    [B*Nq, C], max_len)."""
+    r = oracle.sca_rebatch(*[w[k] for k in ("value", "spatial_shapes", "level_start_index", "reference_points_cam",
+                                            "bev_mask", "sampling_offsets", "attention_logits")])
+    return r["sampling_locations"], r["logits"], r["slots"], r["max_len"]
 
 
 def run_rebatch(w):
