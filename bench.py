@@ -384,7 +384,7 @@ def sca_onchip_ceiling(w, d, ws, offsets, bf16):
     return _ceiling(sca_inbounds_corners(w, ss, off) * 32 * (2 if bf16 else 4), ms, ss)
 
 
-def msda_onchip_ceiling(w, d, F):
+def msda_onchip_ceiling(w, d, F, plan=None):
     """As sca_onchip_ceiling, for the operator (or frame mean): the same
     normalised locations on the shrunken level table."""
     import numpy as np
@@ -396,8 +396,12 @@ def msda_onchip_ceiling(w, d, F):
     value = torch.randn(((B, F) if F > 1 else (B,)) + (Nv, nH, 32), generator=g, device="cuda")
     dss, dst = _dev(ss), _dev(starts)
     out = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
-    fn = m.msda_forward if F == 1 else m.msda_forward_frames
-    ms = _mean_launch_ms(lambda: fn(value, dss, dst, d["sampling_locations"], d["attention_weights"], out=out))
+    if plan is not None:  # the same work order as the measured gather
+        ms = _mean_launch_ms(lambda: m.msda_gather(value, dss, dst, d["sampling_locations"], d["attention_weights"],
+                                                   plan, out=out))
+    else:
+        fn = m.msda_forward if F == 1 else m.msda_forward_frames
+        ms = _mean_launch_ms(lambda: fn(value, dss, dst, d["sampling_locations"], d["attention_weights"], out=out))
     loc = w["sampling_locations"]
     inb = count_inbounds(ss, loc[..., 0] * ss[:, 1].astype(np.float64)[:, None] - 0.5,
                          loc[..., 1] * ss[:, 0].astype(np.float64)[:, None] - 0.5)
@@ -734,9 +738,11 @@ def msda_workload(which):
     import workloads as W
     import scale_deformable_attention_forward_amd as m
 
-    if which == "detr":
+    planned = not which.endswith("_unplanned")
+    base = which.replace("_unplanned", "")
+    if base == "detr":
         w, F = W.detr_encoder_msda(), 1
-    elif which == "tiny":
+    elif base == "tiny":
         w, F = W.tiny_msda(), 1
     else:
         w = W.temporal_frames()
@@ -746,9 +752,17 @@ def msda_workload(which):
     B, Nq, nH, L, P = w["B"], w["Nq"], w["nH"], w["L"], w["P"]
     out = torch.empty((B, Nq, nH * 32), dtype=torch.float32, device="cuda")
     wl = Workload(which)
-    fn = m.msda_forward if F == 1 else m.msda_forward_frames
-    wl.parts.append(("gather", lambda: fn(d["value"], d["spatial_shapes"], d["level_start_index"],
-                                          d["sampling_locations"], d["attention_weights"], out=out)))
+    args = (d["value"], d["spatial_shapes"], d["level_start_index"], d["sampling_locations"], d["attention_weights"])
+    if planned:
+        # the locality plan, from each query's first sampling location, is
+        # part of every step
+        row = nH * L * P * 2
+        plan = torch.empty(m.msda_plan_size(B, Nq), dtype=torch.uint8, device="cuda")
+        wl.parts.append(("plan", lambda: m.msda_plan(d["sampling_locations"], B, Nq, F * Nq * row, row, plan=plan)))
+        wl.parts.append(("gather", lambda: m.msda_gather(*args, plan, out=out)))
+    else:
+        fn = m.msda_forward if F == 1 else m.msda_forward_frames
+        wl.parts.append(("gather", lambda: fn(*args, out=out)))
     wl.main = "gather"
 
     def finish():
@@ -761,13 +775,15 @@ def msda_workload(which):
         wl.gathered_bytes = wl.samples * 4 * 32 * 4
         wl.eff_bytes = wl.gathered_bytes + wl.samples * (8 + 4) + B * Nq * nH * 32 * 4
         wl.unique_bytes = w["value"].nbytes + wl.samples * (8 + 4) + B * Nq * nH * 32 * 4
-        wl.onchip = lambda: msda_onchip_ceiling(w, d, F)
+        wl.onchip = lambda: msda_onchip_ceiling(w, d, F, plan if planned else None)
     wl.finish = finish
     wl.batch = B
     names = {"detr": "Deformable-DETR encoder MSDA, 4 levels 100x150/50x75/25x38/13x19, Nq=Nv=19947",
              "tiny": "tiny MSDA, 256 queries, one 32x32 level",
              "tsa": "temporal self-attention, 2 stacked 200x200 BEV maps, mean over frames"}
-    wl.config = {"workload": names[which], "batch": B, "queries": Nq, "heads": nH, "head_dim": 32,
+    wl.config = {"workload": names[base] + (", locality plan + planned gather" if planned
+                                            else ", queries in input order (no plan)"),
+                 "batch": B, "queries": Nq, "heads": nH, "head_dim": 32,
                  "levels": L, "points_per_level": P, "frames": F, "value_dtype": "fp32"}
     wl.dtype = "fp32"
     wl.kernel_key = "msda_gather_kernel_fp32"
@@ -784,7 +800,7 @@ def main():
     ap.add_argument("--workload", default="sca",
                     choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "sca_train", "detr",
                              "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny", "sca_frame6",
-                             "tsa_train", "tsa_train_atomic"])
+                             "tsa_train", "tsa_train_atomic", "detr_unplanned", "tsa_unplanned", "tiny_unplanned"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-onchip-ceiling", action="store_true",
                     help="skip the L2-resident run of the main kernel behind roofline_onchip")

@@ -2,6 +2,7 @@
  * msda.h -- C ABI of libmsda.so: multi-scale deformable attention (MSDA) and
  * BEVFormer spatial cross-attention (SCA) on AMD Instinct MI355X (gfx950):
  *   msda_forward, msda_forward_frames        the MSDA operator (and a mean over frames)
+ *   msda_plan_size, msda_plan, msda_gather   the operator in a locality order
  *   sca_workspace_size (sca_plan_workspace),
  *   sca_compact, sca_gather, sca_forward     SCA: visibility, compaction, sampling, camera mean
  *   sca_forward_noalloc                      sca_forward with its workspace in a static device array
@@ -124,6 +125,51 @@ int msda_forward_frames(const void* value, int value_dtype, const int64_t* spati
                         const int64_t* level_start_index, const float* sampling_locations,
                         const float* attention_weights, int weight_mode, int64_t B, int64_t F,
                         int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, float* out, void* stream);
+
+/*
+ * Locality plan of the operator: the order in which msda_gather visits the
+ * queries of each batch item.  The sampling locations of a query cluster
+ * around its reference point on every level ([8-heads] 4.3 and 5: offsets of
+ * a few cells around it), so queries visited in order of position read
+ * neighbouring value rows one after the other.  Each batch item's queries
+ * are sorted by the tile (64 x 64 tiles of the normalised square, taken in
+ * Morton order) of the point standing for the query:
+ *   point of (b, q) = points[b*batch_stride + q*point_stride + {0, 1}]
+ * (normalised (x, y), clamped to [0, 1]; strides in float elements, even).
+ * For the operator's own sampling_locations [B][Nq][nH][L][P][2] that is the
+ * first sample of head 0: batch_stride = Nq*nH*L*P*2, point_stride =
+ * nH*L*P*2; for frames [B][F][Nq]..., batch_stride = F*Nq*nH*L*P*2; for
+ * reference points [B][Nq][2], 2*Nq and 2.  A plan built from the reference
+ * points serves every layer that shares them.
+ *
+ * msda_plan_size: bytes of the plan buffer for (B, Nq) (host; no device
+ *   work): the visiting order, B*Nq int32, then 16 KiB of tile counters per
+ *   batch item.
+ * msda_plan: fills the plan buffer (device, >= msda_plan_size() bytes,
+ *   256-byte aligned; contents on entry irrelevant).  Its first B*Nq int32
+ *   are the visiting order: entries [b*Nq, (b+1)*Nq) are batch item b's flat
+ *   query indices b*Nq + q, each once (within a tile the order varies from
+ *   run to run; results do not depend on it).  points: device float, 8-byte
+ *   aligned.  Four small kernels.  B < 65536, B*Nq < 2^31.
+ */
+int msda_plan_size(int64_t B, int64_t Nq, size_t* bytes);
+int msda_plan(const float* points, int64_t batch_stride, int64_t point_stride, int64_t B, int64_t Nq, void* plan,
+              size_t plan_bytes, void* stream);
+
+/*
+ * msda_forward_frames (F = 1: msda_forward) visiting the queries in the
+ * order of the plan that msda_plan wrote for the same B and Nq, enqueued
+ * before on the same stream (or otherwise ordered before this call); plan
+ * and plan_bytes as for msda_plan.  Every output row is written by exactly
+ * the arithmetic of msda_forward_frames, so the result is the same bit for
+ * bit; only the order of the work, and so the cache reuse, changes.  Order
+ * entries outside [0, B*Nq) are skipped (their queries' rows are then not
+ * written).  Other arguments as msda_forward_frames.
+ */
+int msda_gather(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                const int64_t* level_start_index, const float* sampling_locations,
+                const float* attention_weights, int weight_mode, int64_t B, int64_t F, int64_t Nv, int64_t Nq,
+                int nH, int Dh, int L, int P, float* out, const void* plan, size_t plan_bytes, void* stream);
 
 /*
  * Workspace bytes sca_forward needs for (B, Ncam, Nq).  Host only; touches no

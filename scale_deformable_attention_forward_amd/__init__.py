@@ -10,7 +10,8 @@ the call so that what the call allocates belongs to it.  If the library is
 missing, importing works but every call raises: there is no fallback path.
 
 Functions (same names as the C entry points):
-  operator:     msda_forward, msda_forward_frames, msda_backward,
+  operator:     msda_forward, msda_forward_frames, msda_plan and msda_gather
+                (the operator in a locality order), msda_backward,
                 msda_backward_frames, msda_backward_workspace_size
   SCA:          sca_workspace_size (also as sca_plan_workspace), sca_forward,
                 sca_forward_noalloc (workspace in a static device array),
@@ -28,7 +29,9 @@ import torch
 
 __all__ = [
     "MsdaError", "MSDA_F32", "MSDA_BF16", "MSDA_WEIGHTS_PROB", "MSDA_WEIGHTS_LOGITS",
-    "library_path", "load_library", "msda_forward", "msda_forward_frames", "sca_workspace_size", "sca_plan_workspace",
+    "library_path", "load_library", "msda_forward", "msda_forward_frames", "msda_plan_size", "msda_plan",
+    "msda_gather", "plan_order",
+    "sca_workspace_size", "sca_plan_workspace",
     "sca_forward", "sca_forward_noalloc", "sca_compact", "sca_gather", "msda_gemm_bf16", "msda_query_proj_bf16", "msda_output_proj_bf16",
     "sca_rebatch", "sca_scatter_mean", "sca_forward_rebatch", "msda_backward_workspace_size",
     "sca_backward_workspace_size", "msda_backward", "msda_backward_frames", "sca_backward", "msda_status_string",
@@ -69,6 +72,10 @@ def load_library():
     lib.msda_forward.argtypes = [_p, _int, _p, _p, _p, _p, _int, _i64, _i64, _i64, _int, _int, _int, _int, _p, _p]
     lib.msda_forward_frames.argtypes = [_p, _int, _p, _p, _p, _p, _int, _i64, _i64, _i64, _i64, _int, _int, _int,
                                         _int, _p, _p]
+    lib.msda_plan_size.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
+    lib.msda_plan.argtypes = [_p, _i64, _i64, _i64, _i64, _p, _sz, _p]
+    lib.msda_gather.argtypes = [_p, _int, _p, _p, _p, _p, _int, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _p, _p,
+                                _sz, _p]
     lib.sca_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
     lib.sca_plan_workspace.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
     lib.sca_forward.argtypes = [_p, _int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int,
@@ -91,7 +98,9 @@ def load_library():
     lib.sca_scatter_mean.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p]
     lib.msda_query_proj_bf16.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]
     lib.msda_output_proj_bf16.argtypes = [_p, _int, _p, _p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p]
-    for f in (lib.msda_forward, lib.msda_forward_frames, lib.sca_workspace_size, lib.sca_plan_workspace, lib.sca_forward,
+    for f in (lib.msda_forward, lib.msda_forward_frames, lib.msda_plan_size, lib.msda_plan, lib.msda_gather,
+              lib.sca_workspace_size,
+              lib.sca_plan_workspace, lib.sca_forward,
               lib.sca_forward_noalloc,
               lib.sca_compact, lib.sca_gather, lib.msda_gemm_bf16):
         f.restype = _int
@@ -230,6 +239,69 @@ def msda_forward_frames(value, spatial_shapes, level_start_index, sampling_locat
                                  _ptr(attention_weights, "attention_weights", _F32), int(weight_mode), B, F, Nv, Nq,
                                  nH, Dh, L, P, _ptr(out, "out", _F32), _stream(stream, value.device))
     _check("msda_forward_frames", rc)
+    return out
+
+
+def msda_plan_size(B, Nq):
+    """Bytes of the plan buffer msda_plan fills for (B, Nq)."""
+    lib = load_library()
+    n = _sz(0)
+    _check("msda_plan_size", lib.msda_plan_size(int(B), int(Nq), ctypes.byref(n)))
+    return n.value
+
+
+@_given_stream
+def msda_plan(points, B, Nq, batch_stride, point_stride, plan=None, stream=None):
+    """Locality plan of the operator: each batch item's queries ordered by
+    the tile of the point standing for query (b, q), points[b*batch_stride +
+    q*point_stride + {0,1}] (float32, strides in elements).  Returns the plan
+    buffer (uint8 [msda_plan_size(B, Nq)]); its first B*Nq int32 are the
+    flat query indices in visiting order (plan_order() views them)."""
+    lib = load_library()
+    if Nq > 0:
+        _numel(points, "points", (B - 1) * batch_stride + (Nq - 1) * point_stride + 2, at_least=True)
+    need = msda_plan_size(B, Nq)
+    if plan is None:
+        plan = torch.empty(need, dtype=torch.uint8, device=points.device)
+    rc = lib.msda_plan(_ptr(points, "points", _F32), int(batch_stride), int(point_stride), int(B), int(Nq),
+                       _ptr(plan, "plan"), plan.numel() * plan.element_size(), _stream(stream, points.device))
+    _check("msda_plan", rc)
+    return plan
+
+
+def plan_order(plan, B, Nq):
+    """The visiting order held by a plan buffer: int32 [B*Nq] (a view)."""
+    return plan.view(torch.uint8)[:4 * B * Nq].view(torch.int32)
+
+
+@_given_stream
+def msda_gather(value, spatial_shapes, level_start_index, sampling_locations, attention_weights, plan,
+                weight_mode=MSDA_WEIGHTS_LOGITS, out=None, stream=None):
+    """msda_forward (value [B,Nv,nH,Dh]) or msda_forward_frames (value
+    [B,F,Nv,nH,Dh], locations [B,F,Nq,..]) visiting the queries in the order
+    of the plan buffer msda_plan filled for the same B and Nq.  Same result,
+    bit for bit.  Returns out float32 [B,Nq,nH*Dh]."""
+    lib = load_library()
+    if value.dim() == 4:
+        B, Nv, nH, Dh = value.shape
+        F = 1
+        _, Nq, _, L, P, _ = sampling_locations.shape
+    else:
+        B, F, Nv, nH, Dh = value.shape
+        _, _, Nq, _, L, P, _ = sampling_locations.shape
+    _levels(spatial_shapes, level_start_index, L)
+    _numel(sampling_locations, "sampling_locations", B * F * Nq * nH * L * P * 2)
+    _numel(attention_weights, "attention_weights", B * F * Nq * nH * L * P)
+    _numel(out, "out", B * Nq * nH * Dh, at_least=True)
+    if out is None:
+        out = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=value.device)
+    rc = lib.msda_gather(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
+                         _ptr(level_start_index, "level_start_index", _I64),
+                         _ptr(sampling_locations, "sampling_locations", _F32),
+                         _ptr(attention_weights, "attention_weights", _F32), int(weight_mode), B, F, Nv, Nq, nH, Dh,
+                         L, P, _ptr(out, "out", _F32), _ptr(plan, "plan"), plan.numel() * plan.element_size(),
+                         _stream(stream, value.device))
+    _check("msda_gather", rc)
     return out
 
 

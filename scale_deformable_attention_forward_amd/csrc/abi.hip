@@ -110,7 +110,8 @@ const char* msda_last_error(void) { return g_last_error; }
 static int msda_frames_impl(const void* value, int value_dtype, const int64_t* spatial_shapes,
                             const int64_t* level_start_index, const float* sampling_locations,
                             const float* attention_weights, int weight_mode, int64_t B, int64_t F, int64_t Nv,
-                            int64_t Nq, int nH, int Dh, int L, int P, float* out, void* stream) {
+                            int64_t Nq, int nH, int Dh, int L, int P, float* out, const int32_t* plan,
+                            void* stream) {
   uint32_t image_bytes = 0;
   int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, out,
                         &image_bytes);
@@ -143,6 +144,8 @@ static int msda_frames_impl(const void* value, int value_dtype, const int64_t* s
   a.weights = attention_weights;
   a.weight_logits = weight_mode == MSDA_WEIGHTS_LOGITS;
   a.F = (int)F;
+  a.inv_LP = 1.0f / (float)(L * P);
+  a.plan = plan;
   a.B = B;
   a.Nq = Nq;
   a.out = out;
@@ -154,7 +157,7 @@ int msda_forward(const void* value, int value_dtype, const int64_t* spatial_shap
                  const float* attention_weights, int weight_mode, int64_t B, int64_t Nv, int64_t Nq, int nH,
                  int Dh, int L, int P, float* out, void* stream) {
   return msda_frames_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_locations,
-                          attention_weights, weight_mode, B, 1, Nv, Nq, nH, Dh, L, P, out, stream);
+                          attention_weights, weight_mode, B, 1, Nv, Nq, nH, Dh, L, P, out, nullptr, stream);
 }
 
 int msda_forward_frames(const void* value, int value_dtype, const int64_t* spatial_shapes,
@@ -162,7 +165,46 @@ int msda_forward_frames(const void* value, int value_dtype, const int64_t* spati
                         const float* attention_weights, int weight_mode, int64_t B, int64_t F, int64_t Nv,
                         int64_t Nq, int nH, int Dh, int L, int P, float* out, void* stream) {
   return msda_frames_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_locations,
-                          attention_weights, weight_mode, B, F, Nv, Nq, nH, Dh, L, P, out, stream);
+                          attention_weights, weight_mode, B, F, Nv, Nq, nH, Dh, L, P, out, nullptr, stream);
+}
+
+int msda_plan_size(int64_t B, int64_t Nq, size_t* bytes) {
+  if (!bytes) return fail(MSDA_ERR_INVALID_ARG, "bytes is null");
+  if (B < 1 || Nq < 0) return fail(MSDA_ERR_INVALID_ARG, "B >= 1 and Nq >= 0 required");
+  if (B * Nq >= kI31 || B >= 65536) return fail(MSDA_ERR_UNSUPPORTED, "B*Nq must be below 2^31 and B below 65536");
+  *bytes = msda::plan_bytes(B, Nq);
+  return MSDA_OK;
+}
+
+int msda_plan(const float* points, int64_t batch_stride, int64_t point_stride, int64_t B, int64_t Nq, void* plan,
+              size_t plan_bytes, void* stream) {
+  size_t need = 0;
+  int rc = msda_plan_size(B, Nq, &need);
+  if (rc != MSDA_OK) return rc;
+  if (Nq != 0 && !points) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (batch_stride < 0 || point_stride < 0 || ((batch_stride | point_stride) & 1))
+    return fail(MSDA_ERR_INVALID_ARG, "strides must be even and >= 0 (float elements; points are float pairs)");
+  if (Nq != 0 && !aligned(points, 8)) return fail(MSDA_ERR_INVALID_ARG, "points must be 8-byte aligned");
+  if (!plan || plan_bytes < need || !aligned(plan, 256))
+    return fail(MSDA_ERR_WORKSPACE, "plan must be >= %zu bytes and 256-byte aligned (got %zu)", need, plan_bytes);
+  g_last_error[0] = '\0';
+  if (Nq == 0) return MSDA_OK;
+  msda::PlanArgs a = {points, batch_stride, point_stride, (int)B, (int)Nq, static_cast<int32_t*>(plan),
+                      reinterpret_cast<int32_t*>(static_cast<char*>(plan) + msda::plan_bins_offset(B, Nq))};
+  return hip_status(msda::launch_msda_plan(a, static_cast<hipStream_t>(stream)), "msda plan launch");
+}
+
+int msda_gather(const void* value, int value_dtype, const int64_t* spatial_shapes, const int64_t* level_start_index,
+                const float* sampling_locations, const float* attention_weights, int weight_mode, int64_t B,
+                int64_t F, int64_t Nv, int64_t Nq, int nH, int Dh, int L, int P, float* out, const void* plan,
+                size_t plan_bytes, void* stream) {
+  size_t need = 0;
+  if (Nq != 0 && B >= 1 && Nq > 0 && msda_plan_size(B, Nq, &need) == MSDA_OK &&
+      (!plan || plan_bytes < need || !aligned(plan, 256)))
+    return fail(MSDA_ERR_WORKSPACE, "plan must be >= %zu bytes and 256-byte aligned (got %zu)", need, plan_bytes);
+  return msda_frames_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_locations,
+                          attention_weights, weight_mode, B, F, Nv, Nq, nH, Dh, L, P, out,
+                          static_cast<const int32_t*>(plan), stream);
 }
 
 int sca_workspace_size(int64_t B, int64_t Ncam, int64_t Nq, size_t* bytes) {

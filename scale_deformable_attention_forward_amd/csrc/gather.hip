@@ -80,10 +80,12 @@ __device__ inline void sample_corners(uint2 (&c)[4], double x, double y, float a
 // (lane order, then sample order; a prefix sum over the group's 8 lanes
 // places each lane) and pad every group of the wave with skipped rows up to
 // the wave's largest count rounded up to kBatch.  Returns that row count
-// (the same in every lane).  Dead samples cost no row at all.
-template <int kSPL>
+// (the same in every lane).  Dead samples cost no row at all.  where(i)
+// gives sample i's level index and the byte offset of its image within the
+// buffer the gather reads (non-zero when one buffer holds several frames).
+template <int kSPL, typename Where>
 __device__ inline int stage_rows(uint2* __restrict__ rows, const double (&xs)[kSPL], const double (&ys)[kSPL],
-                                 const float (&alpha)[kSPL], uint32_t live, const Level* lv, float inv_P, int j,
+                                 const float (&alpha)[kSPL], uint32_t live, const Level* lv, Where where, int j,
                                  int h, int nH, int Nv, uint32_t row_bytes) {
   const int n = 4 * __popc(live);
   int incl = n;
@@ -102,11 +104,15 @@ __device__ inline int stage_rows(uint2* __restrict__ rows, const double (&xs)[kS
 #pragma unroll
   for (int i = 0; i < kSPL; ++i) {
     if ((live >> i) & 1u) {
-      const Level L = lv[small_div(j + 8 * i, inv_P)];
+      const int2 at = where(i);
       uint2 c[4];
-      sample_corners(c, xs[i], ys[i], alpha[i], L, true, h, nH, Nv, row_bytes);
+      sample_corners(c, xs[i], ys[i], alpha[i], lv[at.x], true, h, nH, Nv, row_bytes);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) rows[pos + t] = c[t];
+      for (int t = 0; t < 4; ++t) {
+        // skipped corners keep their offset past every image
+        if (c[t].x != kSkip) c[t].x += (uint32_t)at.y;
+        rows[pos + t] = c[t];
+      }
       pos += 4;
     }
   }
@@ -166,7 +172,72 @@ __device__ inline float4 scaled(float4 v, int n) {
 // ---------------------------------------------------------------------------
 // plain operator and frame mean: item = (b, q); sources = frames f
 // ---------------------------------------------------------------------------
-template <bool kBF16, int kSPL>
+// Weights of one head's flat samples t = j + 8i < F*LP over F frames: frame
+// f = t / LP holds samples [f*LP, (f+1)*LP) and has its own softmax, reduced
+// over the lanes of the group that hold its samples.  fr[i] = frame of
+// sample i, or -1 for no sample.
+template <int kSPL>
+__device__ inline void frame_weights(const float* __restrict__ w0, int64_t frame_stride, bool head_ok, int LP,
+                                     int F, float inv_LP, int j, bool logits, float (&alpha)[kSPL],
+                                     int (&fr)[kSPL]) {
+  const int FLP = F * LP;
+#pragma unroll
+  for (int i = 0; i < kSPL; ++i) {
+    const int t = j + 8 * i;
+    const bool valid = head_ok && t < FLP;
+    const int f = valid ? small_div(t, inv_LP) : -1;
+    fr[i] = f;
+    alpha[i] = valid ? w0[f * frame_stride + (t - f * LP)] : 0.f;
+  }
+  if (!logits) return;
+  for (int f = 0; f < F; ++f) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kSPL; ++i)
+      if (fr[i] == f) m = fmaxf(m, alpha[i]);
+    m = group_max(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSPL; ++i)
+      if (fr[i] == f) {
+        alpha[i] = expf(alpha[i] - m);
+        sum += alpha[i];
+      }
+    const float inv = 1.0f / group_sum(sum);
+#pragma unroll
+    for (int i = 0; i < kSPL; ++i)
+      if (fr[i] == f) alpha[i] *= inv;
+  }
+}
+
+// Work items of the operator: the queries (b, q) in index order, or, with a
+// plan from msda_plan, batch item by batch item in the plan's locality
+// order.  Each die takes a contiguous eighth of a batch item's items.
+template <typename Body>
+__device__ inline void for_each_msda_item(const GatherArgs& a, int waves_per_block, Body body) {
+  const int64_t n_queries = a.B * a.Nq;
+  if (!a.plan) {
+    XcdSplit split(n_queries, waves_per_block);
+    for (int64_t item = split.begin; item < split.end; item += split.stride) body(item);
+    return;
+  }
+  for (int64_t bi = 0; bi < a.B; ++bi) {
+    const int64_t lo = bi * a.Nq;
+    XcdSplit split(a.Nq, waves_per_block);
+    for (int64_t i = lo + split.begin; i < lo + split.end; i += split.stride) {
+      // entries outside [0, B*Nq) are skipped: a foreign plan never sends a
+      // read out of bounds (its queries' rows are then left unwritten)
+      const int64_t item = uniform((int64_t)a.plan[i]);
+      if (item >= 0 && item < n_queries) body(item);
+    }
+  }
+}
+
+// kFlat: all F frames' samples of a head are staged together and gathered
+// in one pass through one buffer descriptor spanning the batch item's F
+// images (needs F*L*P <= 8*kSPL and F images under 2^31 bytes); otherwise
+// frame by frame.
+template <bool kBF16, int kSPL, bool kFlat>
 __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(GatherArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Level* lv = reinterpret_cast<Level*>(smem);
@@ -175,44 +246,84 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
   const int lane = threadIdx.x % kWave, wave = uniform((int)(threadIdx.x / kWave));
   const int g = lane / 8, j = lane % 8;
   uint2* rows = reinterpret_cast<uint2*>(smem + sizeof(Level) * kMaxLevels) +
-                ((size_t)wave * kHeadSlots + g) * meta_stride(a.LP);
+                ((size_t)wave * kHeadSlots + g) * meta_stride(kFlat ? a.F * a.LP : a.LP);
   const uint32_t row_bytes = kBF16 ? 64u : 128u;
+  const int64_t frame_rows = a.Nq * a.nH;  // rows of locations / weights per frame
 
-  XcdSplit split(a.B * a.Nq, waves_per_block);
-  for (int64_t item = split.begin; item < split.end; item += split.stride) {
+  for_each_msda_item(a, waves_per_block, [&](int64_t item) {
     const int64_t b = item / a.Nq, q = item % a.Nq;
     for (int hb = 0; hb < a.nH; hb += kHeadSlots) {
       const int h = hb + g;
       const bool head_ok = h < a.nH;
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int f = 0; f < a.F; ++f) {
-        const int64_t img_index = b * a.F + f;
-        const int64_t src_row = (img_index * a.Nq + q) * a.nH + (head_ok ? h : 0);
+      if constexpr (kFlat) {
+        const int64_t src_row = (b * a.F * a.Nq + q) * a.nH + (head_ok ? h : 0);  // frame 0
+        const int64_t stride = frame_rows * a.LP;                                // elements per frame
         float alpha[kSPL];
-        head_weights<kSPL>(a.weights + src_row * a.LP, head_ok, a.LP, j, a.weight_logits != 0, alpha);
+        int fr[kSPL];
+        frame_weights<kSPL>(a.weights + src_row * a.LP, stride, head_ok, a.LP, a.F, a.inv_LP, j,
+                            a.weight_logits != 0, alpha, fr);
         const float2* loc = reinterpret_cast<const float2*>(a.loc) + src_row * a.LP;
         double xs[kSPL], ys[kSPL];
         uint32_t live = 0u;
 #pragma unroll
         for (int i = 0; i < kSPL; ++i) {
-          const int k = j + 8 * i;
-          const bool valid = head_ok && k < a.LP;
-          const Level L = lv[valid ? small_div(k, a.inv_P) : 0];
-          const float2 s = valid ? loc[k] : make_float2(0.f, 0.f);
+          const int f = fr[i] < 0 ? 0 : fr[i];
+          const int k = j + 8 * i - f * a.LP;
+          const Level L = lv[fr[i] < 0 ? 0 : small_div(k, a.inv_P)];
+          const float2 s = fr[i] >= 0 ? loc[f * stride + k] : make_float2(0.f, 0.f);
           xs[i] = (double)s.x * L.W - 0.5;
           ys[i] = (double)s.y * L.H - 0.5;
-          if (valid && sample_live(xs[i], ys[i], L)) live |= 1u << i;
+          if (fr[i] >= 0 && sample_live(xs[i], ys[i], L)) live |= 1u << i;
         }
-        const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv, a.inv_P, j, h, a.nH, a.Nv, row_bytes);
+        const int LP = a.LP;
+        const float inv_LP = a.inv_LP, inv_P = a.inv_P;
+        const uint32_t image_bytes = a.image_bytes;
+        const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv,
+                                       [&](int i) {
+                                         const int t = j + 8 * i;
+                                         const int f = small_div(t, inv_LP);
+                                         return make_int2(small_div(t - f * LP, inv_P), (int)(f * image_bytes));
+                                       },
+                                       j, h, a.nH, a.Nv, row_bytes);
         wave_lds_sync();
-        const auto img = make_rsrc(static_cast<const char*>(a.value) + img_index * (int64_t)a.image_bytes,
-                                   a.image_bytes);
+        const auto img = make_rsrc(static_cast<const char*>(a.value) + b * a.F * (int64_t)a.image_bytes,
+                                   (uint32_t)(a.F * (int64_t)a.image_bytes));
         gather_rows<kBF16>(rows, R, img, j, acc);
         wave_lds_sync();
+      } else {
+        for (int f = 0; f < a.F; ++f) {
+          const int64_t img_index = b * a.F + f;
+          const int64_t src_row = (img_index * a.Nq + q) * a.nH + (head_ok ? h : 0);
+          float alpha[kSPL];
+          head_weights<kSPL>(a.weights + src_row * a.LP, head_ok, a.LP, j, a.weight_logits != 0, alpha);
+          const float2* loc = reinterpret_cast<const float2*>(a.loc) + src_row * a.LP;
+          double xs[kSPL], ys[kSPL];
+          uint32_t live = 0u;
+#pragma unroll
+          for (int i = 0; i < kSPL; ++i) {
+            const int k = j + 8 * i;
+            const bool valid = head_ok && k < a.LP;
+            const Level L = lv[valid ? small_div(k, a.inv_P) : 0];
+            const float2 s = valid ? loc[k] : make_float2(0.f, 0.f);
+            xs[i] = (double)s.x * L.W - 0.5;
+            ys[i] = (double)s.y * L.H - 0.5;
+            if (valid && sample_live(xs[i], ys[i], L)) live |= 1u << i;
+          }
+          const float inv_P = a.inv_P;
+          const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv,
+                                         [&](int i) { return make_int2(small_div(j + 8 * i, inv_P), 0); }, j, h,
+                                         a.nH, a.Nv, row_bytes);
+          wave_lds_sync();
+          const auto img = make_rsrc(static_cast<const char*>(a.value) + img_index * (int64_t)a.image_bytes,
+                                     a.image_bytes);
+          gather_rows<kBF16>(rows, R, img, j, acc);
+          wave_lds_sync();
+        }
       }
       if (head_ok) reinterpret_cast<float4*>(a.out + ((item * a.nH + h) * 32))[j] = scaled(acc, a.F);
     }
-  }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -287,7 +398,10 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void s
           ys[i] = (double)r.y * L.H + (double)off[i].y - 0.5;
           if (valid && sample_live(xs[i], ys[i], L)) live |= 1u << i;
         }
-        const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv, a.inv_P, j, h, a.nH, a.Nv, row_bytes);
+        const float inv_P = a.inv_P;
+        const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv,
+                                       [&](int i) { return make_int2(small_div(j + 8 * i, inv_P), 0); }, j, h, a.nH,
+                                       a.Nv, row_bytes);
         wave_lds_sync();
         const auto img = make_rsrc(static_cast<const char*>(a.value) + (b * a.Ncam + c) * (int64_t)a.image_bytes,
                                    a.image_bytes);
@@ -354,14 +468,42 @@ static void launch(Kernel kernel, int64_t n_items, int waves, size_t smem, bool 
   kernel<<<grid_for(kernel, n_items, waves, smem, resident_only), waves * kWave, smem, stream>>>(a);
 }
 
-hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream) {
-  const int waves = block_waves(a.LP);
-  const size_t smem = smem_bytes(a.LP, waves);
-  const int64_t n = a.B * a.Nq;
-  if (a.LP <= 32)
-    launch(a.bf16 ? msda_gather_kernel<true, 4> : msda_gather_kernel<false, 4>, n, waves, smem, false, a, stream);
+// The operator's kernel for kSPL samples per lane (8 * kSPL per head and pass).
+template <int kSPL, bool kFlat>
+static void launch_msda_spl(const GatherArgs& a, int waves, size_t smem, bool resident, hipStream_t stream) {
+  launch(a.bf16 ? msda_gather_kernel<true, kSPL, kFlat> : msda_gather_kernel<false, kSPL, kFlat>, a.B * a.Nq,
+         waves, smem, resident, a, stream);
+}
+
+template <bool kFlat>
+static void launch_msda_staged(const GatherArgs& a, int staged, int waves, size_t smem, bool resident,
+                               hipStream_t stream) {
+  // as few samples per lane as the head's staged samples need: unused
+  // sample slots still cost their (masked) staging instructions
+  if (staged <= 8)
+    launch_msda_spl<1, kFlat>(a, waves, smem, resident, stream);
+  else if (staged <= 16)
+    launch_msda_spl<2, kFlat>(a, waves, smem, resident, stream);
+  else if (staged <= 32)
+    launch_msda_spl<4, kFlat>(a, waves, smem, resident, stream);
   else
-    launch(a.bf16 ? msda_gather_kernel<true, 8> : msda_gather_kernel<false, 8>, n, waves, smem, false, a, stream);
+    launch_msda_spl<8, kFlat>(a, waves, smem, resident, stream);
+}
+
+hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream) {
+  // all frames in one pass when their samples fit one staging area and
+  // their images one buffer descriptor (offset kSkip must lie beyond them)
+  const bool flat = (int64_t)a.F * a.LP <= 64 && (int64_t)a.F * a.image_bytes < (int64_t)kSkip;
+  const int staged = flat ? a.F * a.LP : a.LP;
+  const int waves = block_waves(staged);
+  const size_t smem = smem_bytes(staged, waves);
+  // a plan orders the work for locality: all waves resident, so that they
+  // sweep the ordered list together
+  const bool resident = a.plan != nullptr;
+  if (flat)
+    launch_msda_staged<true>(a, staged, waves, smem, resident, stream);
+  else
+    launch_msda_staged<false>(a, staged, waves, smem, resident, stream);
   return hipGetLastError();
 }
 

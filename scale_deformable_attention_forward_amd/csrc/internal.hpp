@@ -25,6 +25,10 @@ struct GatherArgs {
   const float* weights;
   int weight_logits;
   int F;
+  float inv_LP;
+  // optional locality plan (msda_plan): entries [b*Nq, (b+1)*Nq) hold batch
+  // item b's queries b*Nq + q in the order to visit them
+  const int32_t* plan;
   // SCA mode: images b*Ncam + c; work list from the compaction
   const float* rp;        // [Ncam][B][Nq][D][2]
   const float* offsets;   // [B][Nq][nH][L][P][2]
@@ -39,6 +43,22 @@ struct GatherArgs {
 };
 
 hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream);
+
+// Locality plan of the operator (plan.hip): point of query (b, q) at
+// points[b*batch_stride + q*point_stride] (x, y normalised); the plan buffer
+// holds the visiting order [B*Nq] and, 256-byte aligned after it, the tile
+// counters [B*kPlanBins].
+constexpr int kPlanBins = 64 * 64;
+inline size_t plan_bins_offset(int64_t B, int64_t Nq) { return ((size_t)(B * Nq) * 4 + 255) / 256 * 256; }
+inline size_t plan_bytes(int64_t B, int64_t Nq) { return plan_bins_offset(B, Nq) + (size_t)B * kPlanBins * 4; }
+struct PlanArgs {
+  const float* points;
+  int64_t batch_stride, point_stride;
+  int B, Nq;
+  int32_t* order;
+  int32_t* bins;
+};
+hipError_t launch_msda_plan(const PlanArgs& a, hipStream_t stream);
 hipError_t launch_sca_gather(const GatherArgs& a, hipStream_t stream);
 
 // SCA compaction and work ordering: workspace layout and launch.

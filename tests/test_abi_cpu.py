@@ -445,6 +445,7 @@ def test_binding_checks_element_counts(wrong):
             call()
 
 
+
 def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
     """sca_forward_noalloc refuses, before any device call, a problem whose
     SCA workspace exceeds the static scratch array (16 MiB)."""
@@ -454,3 +455,36 @@ def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
     assert lib.sca_forward_noalloc(*args, 12, 6, 16, 40000, 8, 32, 4, 8, 4, B_, None, None, None, None) == UNSUPPORTED
     assert "sca_forward_noalloc holds" in lib.msda_last_error().decode()
     assert lib.sca_forward_noalloc(*args, 0, 6, 16, 4, 8, 32, 4, 8, 4, B_, None, None, None, None) == INVALID
+
+
+def test_msda_plan_rejects(lib):
+    st = None
+    n = _sz(0)
+    assert lib.msda_plan_size(2, 1000, ctypes.byref(n)) == OK and n.value == 8192 + 2 * 4096 * 4
+    assert lib.msda_plan_size(0, 10, ctypes.byref(n)) == INVALID
+    assert lib.msda_plan_size(1 << 16, 1, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.msda_plan_size(1, 10, None) == INVALID
+    assert lib.msda_plan_size(1, 20, ctypes.byref(n)) == OK
+    size = n.value
+    assert lib.msda_plan(None, 40, 2, 1, 20, B_, size, st) == INVALID        # null points
+    assert lib.msda_plan(A, 40, 2, 1, 20, None, size, st) == WORKSPACE      # null plan
+    assert lib.msda_plan(A, 40, 2, 1, 20, B_, size - 1, st) == WORKSPACE    # plan too small
+    assert lib.msda_plan(A, 40, 2, 1, 20, B_ + 16, size, st) == WORKSPACE   # plan not 256-byte aligned
+    assert lib.msda_plan(A, 40, 3, 1, 20, B_, size, st) == INVALID          # odd point stride
+    assert lib.msda_plan(A, -2, 2, 1, 20, B_, size, st) == INVALID          # negative stride
+    assert lib.msda_plan(MIS + 2, 40, 2, 1, 20, B_, size, st) == INVALID    # points not 8-byte aligned
+    assert lib.msda_plan(A, 40, 2, 0, 20, B_, size, st) == INVALID          # no batch
+    assert lib.msda_plan(None, 0, 2, 1, 0, B_, 1 << 20, st) == OK           # no queries: nothing to do
+
+
+def test_msda_gather_rejects(lib):
+    n = _sz(0)
+    assert lib.msda_plan_size(1, 4, ctypes.byref(n)) == OK
+    g = lambda plan=B_, size=n.value, F=2, Dh=32: lib.msda_gather(A, 0, A, A, A, A, 1, 1, F, 16, 4, 8, Dh, 1, 4,
+                                                                   B_, plan, size, None)
+    assert g(plan=None) == WORKSPACE                # a plan is required
+    assert g(size=n.value - 4) == WORKSPACE         # a plan buffer too small
+    assert g(plan=B_ + 64) == WORKSPACE             # misaligned plan
+    assert g(F=0) == INVALID                        # no frames
+    assert g(Dh=16) == UNSUPPORTED
+    assert lib.msda_gather(A, 0, A, A, None, None, 1, 1, 2, 16, 0, 8, 32, 1, 4, None, None, 0, None) == OK  # Nq = 0

@@ -115,3 +115,26 @@ def test_sca_largest_images_forward(big):
     ref = oracle.sca(value, big["ss"], big["starts"], rho, mask, off, logits)
     assert np.array_equal(host(hit), ref["hit_count"]), "hit counts"
     assert_fp32_close(host(slots).reshape(B * Nq, -1), ref["slots"], "slots")
+
+
+@pytest.mark.parametrize("side,flat", [(1023, True), (1024, False)])
+def test_frames_buffer_over_two_images(side, flat):
+    """Two stacked frames of one level side x side (8 float32 heads): at 1023
+    the two images, 2,143,291,392 bytes, are staged and gathered through one
+    buffer of just under 2^31 bytes; at 1024 they are exactly 2^31 and go
+    frame by frame.  Half of the queries sample the last rows and columns of
+    both frames."""
+    B, F, Nq = 1, 2, 256
+    ss, starts, Nv = W.level_table(((side, side),))
+    assert (F * Nv * NH * 32 * 4 < 1 << 31) == flat
+    g = np.random.default_rng(np.random.SeedSequence([951, side]))
+    value = g.random((B, F, Nv, NH, 32), dtype=np.float32)
+    value -= 0.5
+    loc = _far_corner_locations(g, (B * F, Nq, NH, 1, P, 2)).reshape(B, F, Nq, NH, 1, P, 2)
+    logits = g.normal(size=(B, F, Nq, NH, P)).astype(np.float32)
+    vd = dev(value)
+    out = host(msda.msda_forward_frames(vd, dev(ss), dev(starts), dev(loc), dev(logits))).reshape(B * Nq, -1)
+    del vd
+    torch.cuda.empty_cache()
+    ref = oracle.msda_frames(value, ss, starts, loc, logits, True)
+    assert_fp32_close(out, ref, f"two frames of {side} x {side}")
