@@ -132,7 +132,7 @@ int msda_forward_frames(const void* value, int value_dtype, const int64_t* spati
  * around its reference point on every level ([8-heads] 4.3 and 5: offsets of
  * a few cells around it), so queries visited in order of position read
  * neighbouring value rows one after the other.  Each batch item's queries
- * are sorted by the tile (64 x 64 tiles of the normalised square, taken in
+ * are sorted by the tile (32 x 32 tiles of the normalised square, taken in
  * Morton order) of the point standing for the query:
  *   point of (b, q) = points[b*batch_stride + q*point_stride + {0, 1}]
  * (normalised (x, y), clamped to [0, 1]; strides in float elements, even).
@@ -143,14 +143,14 @@ int msda_forward_frames(const void* value, int value_dtype, const int64_t* spati
  * points serves every layer that shares them.
  *
  * msda_plan_size: bytes of the plan buffer for (B, Nq) (host; no device
- *   work): the visiting order, B*Nq int32, then 16 KiB of tile counters per
- *   batch item.
+ *   work): the visiting order, B*Nq int32, then 64 KiB of tile counts per
+ *   batch item (16 chunks of its queries x 1024 tiles).
  * msda_plan: fills the plan buffer (device, >= msda_plan_size() bytes,
  *   256-byte aligned; contents on entry irrelevant).  Its first B*Nq int32
  *   are the visiting order: entries [b*Nq, (b+1)*Nq) are batch item b's flat
  *   query indices b*Nq + q, each once (within a tile the order varies from
  *   run to run; results do not depend on it).  points: device float, 8-byte
- *   aligned.  Four small kernels.  B < 65536, B*Nq < 2^31.
+ *   aligned.  Two small kernels.  B < 65536, B*Nq < 2^31.
  */
 int msda_plan_size(int64_t B, int64_t Nq, size_t* bytes);
 int msda_plan(const float* points, int64_t batch_stride, int64_t point_stride, int64_t B, int64_t Nq, void* plan,
@@ -480,7 +480,7 @@ int sca_backward_workspace_size(int64_t B, int64_t Ncam, int64_t Nv, int64_t Nq,
  *   Arguments: as sca_forward, without workspace and workspace_bytes; the
  *   caller still provides every input and output.
  *   Limit: sca_workspace_size(B, Ncam, Nq) <= MSDA_NOALLOC_SCRATCH_BYTES
- *   (6 cameras x 40000 queries need 1.43 MiB per batch item: up to B = 11);
+ *   (6 cameras x 40000 queries need 1.48 MiB per batch item: up to B = 10);
  *   beyond it MSDA_ERR_UNSUPPORTED, with nothing enqueued.
  *   Every call on one device shares that device's array, which keeps the
  *   last call's contents (each call clears what it needs cleared): calls

@@ -254,6 +254,9 @@ static msda::CompactArgs compact_args(const uint8_t* bev_mask, const float* refe
   c.seg_pairs = reinterpret_cast<int32_t*>(ws + lay.seg_pairs);
   c.bin_offsets = reinterpret_cast<int32_t*>(ws + lay.bin_offsets);
   c.order = reinterpret_cast<int32_t*>(ws + lay.order);
+  c.bin_cost = reinterpret_cast<uint64_t*>(ws + lay.bin_cost);
+  c.seg_cost = reinterpret_cast<uint64_t*>(ws + lay.seg_cost);
+  c.die_bounds = reinterpret_cast<int32_t*>(ws + lay.die_bounds);
   c.clear_ints = lay.clear_ints;
   return c;
 }
@@ -317,8 +320,7 @@ int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes
   a.logits = attention_logits;
   a.cammask = c.cammask;
   a.order = c.order;
-  a.order_at = c.bin_offsets;
-  a.order_stride = (int)Ncam * msda::kOrderBins;
+  a.die_bounds = c.die_bounds;
   a.Ncam = (int)Ncam;
   a.D = D;
   a.B = B;
@@ -740,8 +742,7 @@ int sca_backward(const void* value, int value_dtype, const int64_t* spatial_shap
   a.logits = attention_logits;
   a.cammask = c.cammask;
   a.order = c.order;
-  a.order_at = c.bin_offsets;
-  a.order_stride = (int)Ncam * msda::kOrderBins;
+  a.die_bounds = c.die_bounds;
   a.Ncam = (int)Ncam;
   a.D = D;
   a.grad_offsets = grad_offsets;

@@ -387,11 +387,8 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave, kSPL == 8 ? 2 : 1) void sca_ba
   const uint32_t cam_bits = a.Ncam >= 32 ? 0xffffffffu : ((1u << a.Ncam) - 1u);
 
   for (int64_t bi = 0; bi < a.B; ++bi) {
-    int64_t lo = a.order_at[bi * a.order_stride], hi = a.order_at[(bi + 1) * a.order_stride];
-    lo = lo < 0 ? 0 : (lo > n_queries ? n_queries : lo);
-    hi = hi < lo ? lo : (hi > n_queries ? n_queries : hi);
-    XcdSplit split(hi - lo, waves_per_block);
-    for (int64_t item = lo + split.begin; item < lo + split.end; item += split.stride) {
+    const DieShare split(a.die_bounds + bi * kDieBounds, n_queries, waves_per_block);
+    for (int64_t item = split.begin; item < split.end; item += split.stride) {
       const int64_t bq = uniform((int64_t)a.order[item]);
       if (bq < 0 || bq >= n_queries) continue;
       const int64_t b = bq / a.Nq, q = bq % a.Nq;

@@ -35,8 +35,7 @@ struct BackwardArgs {
   const float* logits;
   const uint32_t* cammask;
   const int32_t* order;
-  const int32_t* order_at;
-  int order_stride;
+  const int32_t* die_bounds;  // [B][kDieBounds], as sca_compact left them
   int Ncam, D;
   float* grad_offsets;  // [B][Nq][nH][L][P][2]
   float* grad_logits;   // [B][Nq][nH][L*P]

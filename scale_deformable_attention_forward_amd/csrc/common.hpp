@@ -8,6 +8,7 @@ namespace msda {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 constexpr int kXcds = 8;   // MI355X: 8 accelerator dies, each with its own L2
+constexpr int kDieBounds = kXcds + 1;  // entries of a per-die split of a list (DieShare)
 
 // Compute units of the device current at the first call (256 when the
 // runtime cannot say), read once per process; safe to call from several
@@ -62,6 +63,25 @@ struct XcdSplit {
     const int64_t lo = n_items * xcd / kXcds;
     end = n_items * (xcd + 1) / kXcds;
     begin = lo + (int64_t)local * waves_per_block + wave;
+    stride = (int64_t)nlocal * waves_per_block;
+  }
+};
+
+// The same walk over a range given per die: die x takes the work-list
+// entries [bounds[x], bounds[x+1]) (clamped to [0, n_items], so that bounds
+// from another call never send a read out of bounds).
+struct DieShare {
+  int64_t begin, end, stride;
+  __device__ DieShare(const int32_t* bounds, int64_t n_items, int waves_per_block) {
+    const int xcd = blockIdx.x % kXcds;
+    const int local = blockIdx.x / kXcds;
+    const int nlocal = gridDim.x / kXcds;
+    const int wave = uniform(threadIdx.x / kWave);
+    int64_t lo = bounds[xcd], hi = bounds[xcd + 1];
+    lo = lo < 0 ? 0 : (lo > n_items ? n_items : lo);
+    hi = hi < lo ? lo : (hi > n_items ? n_items : hi);
+    begin = lo + (int64_t)local * waves_per_block + wave;
+    end = hi;
     stride = (int64_t)nlocal * waves_per_block;
   }
 };

@@ -350,16 +350,14 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void s
   const int64_t n_queries = a.B * a.Nq;
   const uint32_t cam_bits = a.Ncam >= 32 ? 0xffffffffu : ((1u << a.Ncam) - 1u);
 
-  // Batch item by batch item, each die takes an eighth of the item's work
-  // list, so the dies share one item's value maps at a time.  The list comes
-  // from sca_compact; clamping keeps a workspace that never saw one from
-  // sending a read out of bounds.
+  // Batch item by batch item, each die takes its share of the item's work
+  // list (contiguous, of equal estimated cost), so the dies share one item's
+  // value maps at a time.  The list and the shares come from sca_compact;
+  // clamping keeps a workspace that never saw one from sending a read out
+  // of bounds.
   for (int64_t bi = 0; bi < a.B; ++bi) {
-  int64_t lo = a.order_at[bi * a.order_stride], hi = a.order_at[(bi + 1) * a.order_stride];
-  lo = lo < 0 ? 0 : (lo > n_queries ? n_queries : lo);
-  hi = hi < lo ? lo : (hi > n_queries ? n_queries : hi);
-  XcdSplit split(hi - lo, waves_per_block);
-  for (int64_t item = lo + split.begin; item < lo + split.end; item += split.stride) {
+  const DieShare split(a.die_bounds + bi * kDieBounds, n_queries, waves_per_block);
+  for (int64_t item = split.begin; item < split.end; item += split.stride) {
     const int64_t bq = uniform((int64_t)a.order[item]);
     if (bq < 0 || bq >= n_queries) continue;
     const int64_t b = bq / a.Nq, q = bq % a.Nq;

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace msda {
 
 struct GatherArgs {
@@ -34,9 +36,8 @@ struct GatherArgs {
   const float* offsets;   // [B][Nq][nH][L][P][2]
   const float* logits;    // [B][Nq][nH][L*P]
   const uint32_t* cammask;  // [B][Nq] bit c = camera c sees the query
-  const int32_t* order;     // seen queries b*Nq + q, in locality order
-  const int32_t* order_at;  // device: batch item b's entries are [order_at[b*stride], order_at[(b+1)*stride])
-  int order_stride;
+  const int32_t* order;       // seen queries b*Nq + q, in locality order
+  const int32_t* die_bounds;  // [B][kDieBounds]: die x's entries of batch item b, cost-balanced
   int Ncam, D;
   int64_t B, Nq;
   float* out;  // [B][Nq][nH*32]
@@ -47,10 +48,13 @@ hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream);
 // Locality plan of the operator (plan.hip): point of query (b, q) at
 // points[b*batch_stride + q*point_stride] (x, y normalised); the plan buffer
 // holds the visiting order [B*Nq] and, 256-byte aligned after it, the tile
-// counters [B*kPlanBins].
-constexpr int kPlanBins = 64 * 64;
+// histograms of each batch item's kPlanChunks chunks [B][kPlanChunks][kPlanBins].
+constexpr int kPlanBins = 32 * 32;
+constexpr int kPlanChunks = 16;
 inline size_t plan_bins_offset(int64_t B, int64_t Nq) { return ((size_t)(B * Nq) * 4 + 255) / 256 * 256; }
-inline size_t plan_bytes(int64_t B, int64_t Nq) { return plan_bins_offset(B, Nq) + (size_t)B * kPlanBins * 4; }
+inline size_t plan_bytes(int64_t B, int64_t Nq) {
+  return plan_bins_offset(B, Nq) + (size_t)B * kPlanChunks * kPlanBins * 4;
+}
 struct PlanArgs {
   const float* points;
   int64_t batch_stride, point_stride;
@@ -66,12 +70,17 @@ constexpr int kQueryTile = 256;  // queries per tile of the compaction (and its 
 // Image-tile grid used to order the gather work (per first camera).
 constexpr int kOrderBinsX = 64, kOrderBinsY = 16, kOrderBins = kOrderBinsX * kOrderBinsY;
 
+// Each seen query also carries a work estimate, its cost: over the cameras
+// that see it, 1 + the camera's marked anchors (an unmarked anchor projects
+// outside the image, so its samples cost nothing).  The gather's split of a
+// batch item's work list over the dies follows the summed cost.
 struct CompactLayout {
-  // bin_hist, seg_seen and seg_pairs are adjacent: one clear covers them
-  size_t cammask, qkey, tile_counts, tile_offsets, pair_offsets, pair_q, bin_hist, seg_seen, seg_pairs,
-      bin_offsets, order, total;
+  // bin_hist, seg_seen, seg_pairs, bin_cost and seg_cost are adjacent: one
+  // clear covers them
+  size_t cammask, qkey, tile_counts, tile_offsets, pair_offsets, pair_q, bin_hist, seg_seen, seg_pairs, bin_cost,
+      seg_cost, bin_offsets, order, die_bounds, total;
   int tiles;  // tiles of the query axis per (b, c)
-  int clear_ints;  // int32 entries from bin_hist on to zero before a compaction
+  int clear_ints;  // int32 words from bin_hist on to zero before a compaction
 };
 CompactLayout compact_layout(int64_t B, int64_t Ncam, int64_t Nq);
 
@@ -91,6 +100,9 @@ struct CompactArgs {
   int32_t* seg_pairs;    // [B*Ncam] pairs per (b, c)
   int32_t* bin_offsets;  // [B*Ncam*kOrderBins + 1]; the last entry counts the seen queries
   int32_t* order;        // [B*Nq]
+  uint64_t* bin_cost;    // [B*Ncam*kOrderBins] summed cost of each ordering bin
+  uint64_t* seg_cost;    // [B*Ncam] summed cost of the seen queries whose first camera is c, per (b, c)
+  int32_t* die_bounds;   // [B][kDieBounds]: die x takes work-list entries [x, x+1) of its batch item
   int clear_ints;
 };
 hipError_t launch_sca_compact(const CompactArgs& a, int tiles, hipStream_t stream);

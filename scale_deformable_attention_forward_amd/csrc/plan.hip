@@ -13,25 +13,29 @@
 // split of a batch item's list into eight contiguous shares then gives each
 // die a compact region of the maps.
 //
-// A counting sort in four small stream-ordered kernels, spread over the
-// chip (a single workgroup per batch item spent ~50 us fetching the points'
-// cache lines through one compute unit):
-//   0. clear the tile counters of every batch item;
-//   1. count: one thread per query adds one to its tile's counter;
-//   2. scan: one workgroup per batch item turns the counters into the first
-//      slot of each tile;
-//   3. place: every query takes the next slot of its tile (the order inside
-//      a tile varies from run to run, which changes only which wave computes
-//      a query, never a result).
+// A counting sort in two stream-ordered kernels over kPlanChunks chunks of
+// each batch item's queries (kernel launches, not the sort's work, are what
+// a small plan costs: four kernels took ~18 us for 20,000 queries, one
+// workgroup per batch item ~50 us, its points' cache lines all fetched
+// through one compute unit):
+//   1. count: each chunk's workgroup builds its tile histogram in LDS and
+//      writes all of it (no clearing needed);
+//   2. place: each chunk's workgroup reads every chunk's histogram, forms in
+//      LDS the first slot of each tile for its own chunk (the queries of
+//      earlier tiles, then those of the same tile in earlier chunks), and
+//      each of its queries takes the next slot of its tile (LDS atomics: the
+//      order inside a tile and chunk varies from run to run, which changes
+//      only which wave computes a query, never a result).
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace msda {
 
-constexpr int kPlanSide = 64;                     // tiles per side of the unit square
-constexpr int kPlanThreads = 256;                 // count / place kernels
-constexpr int kPlanScanThreads = kPlanBins / 4;   // 4 tiles per scan thread
-static_assert(kPlanBins == kPlanSide * kPlanSide, "tile count");
+constexpr int kPlanSide = 32;  // tiles per side of the unit square
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBits = 5;   // bits of a tile coordinate
+static_assert(kPlanBins == kPlanSide * kPlanSide && kPlanBins == kPlanThreads && kPlanSide == 1 << kPlanBits,
+              "one tile per thread");
 
 __device__ inline int plan_tile(float v) {
   const float t = fminf(fmaxf(v, 0.f), 1.f) * (float)kPlanSide;  // NaN -> 0
@@ -45,32 +49,48 @@ __device__ inline int plan_bin(const float* points, int64_t at) {
   const int tx = plan_tile(p.x), ty = plan_tile(p.y);
   int code = 0;
 #pragma unroll
-  for (int bit = 0; bit < 6; ++bit) code |= (((tx >> bit) & 1) << (2 * bit)) | (((ty >> bit) & 1) << (2 * bit + 1));
+  for (int bit = 0; bit < kPlanBits; ++bit)
+    code |= (((tx >> bit) & 1) << (2 * bit)) | (((ty >> bit) & 1) << (2 * bit + 1));
   return code;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void msda_plan_clear_kernel(int32_t* __restrict__ bins, int n) {
-  const int i = blockIdx.x * kPlanThreads + threadIdx.x;
-  if (i < n) bins[i] = 0;
+// queries [lo, hi) of chunk c of a batch item
+__device__ inline void chunk_range(int Nq, int c, int* lo, int* hi) {
+  *lo = (int)((int64_t)Nq * c / kPlanChunks);
+  *hi = (int)((int64_t)Nq * (c + 1) / kPlanChunks);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void msda_plan_count_kernel(PlanArgs a) {
-  const int q = blockIdx.x * kPlanThreads + threadIdx.x, b = blockIdx.y;
-  if (q >= a.Nq) return;
-  atomicAdd(&a.bins[(int64_t)b * kPlanBins + plan_bin(a.points, b * a.batch_stride + q * a.point_stride)], 1);
+  __shared__ int hist[kPlanBins];
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  hist[t] = 0;
+  __syncthreads();
+  int lo, hi;
+  chunk_range(a.Nq, c, &lo, &hi);
+  for (int q = lo + t; q < hi; q += kPlanThreads)
+    atomicAdd(&hist[plan_bin(a.points, b * a.batch_stride + q * a.point_stride)], 1);
+  __syncthreads();
+  a.bins[((int64_t)b * kPlanChunks + c) * kPlanBins + t] = hist[t];
 }
 
-__global__ __launch_bounds__(kPlanScanThreads) void msda_plan_scan_kernel(PlanArgs a) {
-  __shared__ int wave_sums[kPlanScanThreads / kWave];
-  int32_t* bins = a.bins + (int64_t)blockIdx.x * kPlanBins;
-  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
-  int own[4], sum = 0;
+__global__ __launch_bounds__(kPlanThreads) void msda_plan_place_kernel(PlanArgs a) {
+  __shared__ int start[kPlanBins];
+  __shared__ int wave_sums[kPlanThreads / kWave];
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  // thread t owns tile t: its total over all chunks and the count of the
+  // chunks before this one
+  const int32_t* hist = a.bins + (int64_t)b * kPlanChunks * kPlanBins + t;
+  int n[kPlanChunks];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    own[u] = bins[4 * t + u];
-    sum += own[u];
+  for (int k = 0; k < kPlanChunks; ++k) n[k] = hist[(int64_t)k * kPlanBins];
+  int total = 0, before = 0;
+#pragma unroll
+  for (int k = 0; k < kPlanChunks; ++k) {
+    total += n[k];
+    before += k < c ? n[k] : 0;
   }
-  int incl = sum;
+  const int lane = t % kWave, wave = t / kWave;
+  int incl = total;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
     const int v = __shfl_up(incl, d);
@@ -78,33 +98,24 @@ __global__ __launch_bounds__(kPlanScanThreads) void msda_plan_scan_kernel(PlanAr
   }
   if (lane == kWave - 1) wave_sums[wave] = incl;
   __syncthreads();
-  int start = incl - sum;
-  for (int w = 0; w < wave; ++w) start += wave_sums[w];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    bins[4 * t + u] = start;
-    start += own[u];
+  int first = incl - total;
+  for (int w = 0; w < wave; ++w) first += wave_sums[w];
+  start[t] = first + before;
+  __syncthreads();
+  int lo, hi;
+  chunk_range(a.Nq, c, &lo, &hi);
+  int32_t* order = a.order + (int64_t)b * a.Nq;
+  for (int q = lo + t; q < hi; q += kPlanThreads) {
+    const int bin = plan_bin(a.points, b * a.batch_stride + q * a.point_stride);
+    order[atomicAdd(&start[bin], 1)] = (int32_t)((int64_t)b * a.Nq + q);
   }
 }
 
-__global__ __launch_bounds__(kPlanThreads) void msda_plan_place_kernel(PlanArgs a) {
-  const int q = blockIdx.x * kPlanThreads + threadIdx.x, b = blockIdx.y;
-  if (q >= a.Nq) return;
-  const int bin = plan_bin(a.points, b * a.batch_stride + q * a.point_stride);
-  const int slot = atomicAdd(&a.bins[(int64_t)b * kPlanBins + bin], 1);
-  a.order[(int64_t)b * a.Nq + slot] = (int32_t)((int64_t)b * a.Nq + q);
-}
-
 hipError_t launch_msda_plan(const PlanArgs& a, hipStream_t stream) {
-  const int n = a.B * kPlanBins;
-  msda_plan_clear_kernel<<<(n + kPlanThreads - 1) / kPlanThreads, kPlanThreads, 0, stream>>>(a.bins, n);
+  const dim3 grid(kPlanChunks, a.B);
+  msda_plan_count_kernel<<<grid, kPlanThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((a.Nq + kPlanThreads - 1) / kPlanThreads, a.B);
-  msda_plan_count_kernel<<<grid, kPlanThreads, 0, stream>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  msda_plan_scan_kernel<<<a.B, kPlanScanThreads, 0, stream>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   msda_plan_place_kernel<<<grid, kPlanThreads, 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -460,7 +460,7 @@ def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
 def test_msda_plan_rejects(lib):
     st = None
     n = _sz(0)
-    assert lib.msda_plan_size(2, 1000, ctypes.byref(n)) == OK and n.value == 8192 + 2 * 4096 * 4
+    assert lib.msda_plan_size(2, 1000, ctypes.byref(n)) == OK and n.value == 8192 + 2 * 16 * 1024 * 4
     assert lib.msda_plan_size(0, 10, ctypes.byref(n)) == INVALID
     assert lib.msda_plan_size(1 << 16, 1, ctypes.byref(n)) == UNSUPPORTED
     assert lib.msda_plan_size(1, 10, None) == INVALID

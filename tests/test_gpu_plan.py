@@ -23,11 +23,11 @@ def _name_the_case(request):
 
 
 def morton_bins(points):
-    """Host form of the plan's tile index: 64 x 64 tiles of the clamped unit
+    """Host form of the plan's tile index: 32 x 32 tiles of the clamped unit
     square, the bits of the row tile above those of the column tile."""
-    t = np.minimum((np.clip(points.astype(np.float32), 0, 1) * np.float32(64)).astype(np.int64), 63)
+    t = np.minimum((np.clip(points.astype(np.float32), 0, 1) * np.float32(32)).astype(np.int64), 31)
     code = np.zeros(t.shape[:-1], np.int64)
-    for bit in range(6):
+    for bit in range(5):
         code |= ((t[..., 0] >> bit) & 1) << (2 * bit) | ((t[..., 1] >> bit) & 1) << (2 * bit + 1)
     return code
 
