@@ -21,9 +21,12 @@ all of them, scatter-add and divide), "sca_train", "detr_train" and
 encoder MSDA and of the two-frame mean, the value gradient by the
 deterministic transpose gather; "_atomic" variants accumulate it with
 float32 atomics instead; the roofline then describes the backward kernel),
-"detr" (Deformable-DETR encoder MSDA), "tsa" (two stacked BEV maps, frame
-mean), "sca_frame6" (one frame of the encoder: one compaction serving six
-SCA layers, each with its own value maps, offsets and logits), "tiny".
+"detr" (Deformable-DETR encoder MSDA: each step builds the locality plan
+from the sampling locations and runs the planned gather; "detr_unplanned"
+the queries in input order), "tsa" (two stacked BEV maps, frame mean, the
+BEV-grid queries in raster order; "tsa_planned" with a plan in every step),
+"sca_frame6" (one frame of the encoder: one compaction serving six SCA
+layers, each with its own value maps, offsets and logits), "tiny".
 
 Prints one JSON line.  value = bilinear samples per second (one sample = one
 (camera, query, head, level, point) bilinear read of 4 corners x 32
@@ -738,8 +741,11 @@ def msda_workload(which):
     import workloads as W
     import scale_deformable_attention_forward_amd as m
 
-    planned = not which.endswith("_unplanned")
-    base = which.replace("_unplanned", "")
+    # the DETR encoder's queries are placed at random: its default runs the
+    # plan (inside every step); the temporal workload's BEV-grid queries
+    # come in raster order and run as given (its plan: "tsa_planned")
+    planned = which in ("detr", "tsa_planned")
+    base = which.replace("_unplanned", "").replace("_planned", "")
     if base == "detr":
         w, F = W.detr_encoder_msda(), 1
     elif base == "tiny":
@@ -800,7 +806,7 @@ def main():
     ap.add_argument("--workload", default="sca",
                     choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "sca_train", "detr",
                              "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny", "sca_frame6",
-                             "tsa_train", "tsa_train_atomic", "detr_unplanned", "tsa_unplanned", "tiny_unplanned"])
+                             "tsa_train", "tsa_train_atomic", "detr_unplanned", "tsa_planned"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-onchip-ceiling", action="store_true",
                     help="skip the L2-resident run of the main kernel behind roofline_onchip")
