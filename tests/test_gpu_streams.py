@@ -86,6 +86,35 @@ def _frames_backward(t, stream):
                                      stream=stream)
 
 
+def _msda_planned(t, stream):
+    """plan from the first sampling location of each query, then the planned
+    gather (only the result is compared: the order inside a tile varies)"""
+    B, Nq = t["loc"].shape[:2]
+    row = t["loc"][0, 0].numel()
+    plan = msda.msda_plan(t["loc"], B, Nq, Nq * row, row, stream=stream)
+    return msda.msda_gather(t["value"], t["ss"], t["starts"], t["loc"], t["logits"], plan, stream=stream)
+
+
+def _frames_planned(t, stream):
+    B, F, Nq = t["loc"].shape[:3]
+    row = t["loc"][0, 0, 0].numel()
+    plan = msda.msda_plan(t["loc"], B, Nq, F * Nq * row, row, stream=stream)
+    return msda.msda_gather(t["value"], t["ss"], t["starts"], t["loc"], t["logits"], plan, stream=stream)
+
+
+def _sca_forward_noalloc(t, stream):
+    B, Nq = t["gout"].shape[:2]
+    Ncam = t["mask"].shape[0]
+    dv = t["value"].device
+    hit = torch.full((B, Nq), -7, dtype=torch.int32, device=dv)
+    offs = torch.full((B * Ncam + 1,), -7, dtype=torch.int32, device=dv)
+    pq = torch.full((B * Ncam * Nq,), -7, dtype=torch.int32, device=dv)
+    slots = torch.empty((B, Nq, t["value"].shape[3] * 32), dtype=torch.float32, device=dv)
+    msda.sca_forward_noalloc(t["value"], t["ss"], t["starts"], t["rho"], t["mask"], t["off"], t["logits"], slots,
+                             hit_count=hit, pair_offsets=offs, pair_q=pq, stream=stream)
+    return slots, hit, offs, pq
+
+
 def _sca_forward(t, stream):
     B, Nq = t["gout"].shape[:2]
     Ncam = t["mask"].shape[0]
@@ -141,6 +170,9 @@ CASES = [
     ("msda_forward", _msda_inputs, _msda_forward),
     ("msda_backward", _msda_inputs, _msda_backward),
     ("msda_forward_frames", _frames_inputs, _frames_forward),
+    ("msda_plan_then_gather", _msda_inputs, _msda_planned),
+    ("msda_plan_then_gather_frames", _frames_inputs, _frames_planned),
+    ("sca_forward_noalloc", _sca_inputs, _sca_forward_noalloc),
     ("msda_backward_frames", _frames_inputs, _frames_backward),
     ("sca_forward", _sca_inputs, _sca_forward),
     ("sca_compact_then_gather", _sca_inputs, _sca_two_stage),
