@@ -126,6 +126,9 @@ template <bool kBF16>
 __device__ inline void gather_rows(const uint2* __restrict__ rows, int R, __amdgpu_buffer_rsrc_t img, int j,
                                    float4& acc) {
   const uint32_t lane_off = (uint32_t)j * (kBF16 ? 8u : 16u);
+  // one batch per iteration: unrolled further, the loads in flight take
+  // registers that the occupancy needs
+#pragma nounroll
   for (int r = 0; r < R; r += kBatch) {
     uint2 m[kBatch];
     uint32_t d[kBatch][kBF16 ? 2 : 4];
@@ -163,8 +166,14 @@ __device__ inline void gather_rows(const uint2* __restrict__ rows, int R, __amdg
   }
 }
 
+// v / n: a multiplication by the exact reciprocal when n is a power of two
+// (the same result, without the division's instruction sequence)
 __device__ inline float4 scaled(float4 v, int n) {
   if (n <= 1) return v;
+  if ((n & (n - 1)) == 0) {
+    const float r = 1.0f / (float)n;
+    return make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+  }
   const float f = (float)n;
   return make_float4(v.x / f, v.y / f, v.z / f, v.w / f);
 }
@@ -172,23 +181,105 @@ __device__ inline float4 scaled(float4 v, int n) {
 // ---------------------------------------------------------------------------
 // plain operator and frame mean: item = (b, q); sources = frames f
 // ---------------------------------------------------------------------------
-// Weights of one head's flat samples t = j + 8i < F*LP over F frames: frame
-// f = t / LP holds samples [f*LP, (f+1)*LP) and has its own softmax, reduced
-// over the lanes of the group that hold its samples.  fr[i] = frame of
-// sample i, or -1 for no sample.
+// The operator's work items (b, q) for one wave, in order: the queries in
+// index order, or, with a plan from msda_plan, batch item by batch item in
+// the plan's locality order.  Each die takes a contiguous eighth of a batch
+// item's items.  next() returns the next item, or -1 after the last; plan
+// entries outside [0, B*Nq) are skipped, so a foreign plan never sends a
+// read out of bounds (its queries' rows are then left unwritten).
+struct MsdaWalk {
+  const int32_t* plan;
+  int64_t n, Nq, B;
+  int64_t i, end, stride, lo, bi;
+  int waves_per_block;
+  __device__ MsdaWalk(const GatherArgs& a, int wpb)
+      : plan(a.plan), n(a.B * a.Nq), Nq(a.Nq), B(a.B), lo(0), bi(0), waves_per_block(wpb) {
+    const XcdSplit s(plan ? Nq : n, wpb);
+    i = s.begin - s.stride;
+    end = s.end;
+    stride = s.stride;
+  }
+  __device__ int64_t next() {
+    for (;;) {
+      i += stride;
+      if (i < end) {
+        if (!plan) return i;
+        const int64_t item = uniform((int64_t)plan[lo + i]);
+        if (item >= 0 && item < n) return item;
+        continue;
+      }
+      if (!plan || ++bi >= B) return -1;
+      const XcdSplit s(Nq, waves_per_block);
+      lo = bi * Nq;
+      i = s.begin - s.stride;
+      end = s.end;
+      stride = s.stride;
+    }
+  }
+};
+
+// item = b * Nq + q (a 32-bit division when both fit, as they do in practice)
+__device__ inline void split_item(int64_t item, int64_t Nq, int64_t& b, int64_t& q) {
+  if (item <= 0x7fffffff && Nq <= 0x7fffffff) {
+    const uint32_t bb = (uint32_t)item / (uint32_t)Nq;
+    b = bb;
+    q = item - (int64_t)bb * Nq;
+  } else {
+    b = item / Nq;
+    q = item - b * Nq;
+  }
+}
+
+// One unit of the all-frames-in-one-pass operator, (item, head pass hb), as
+// one lane reads it: the raw weight (or logit) and the location of its
+// samples t = j + 8i of head hb + g (zero for none).
 template <int kSPL>
-__device__ inline void frame_weights(const float* __restrict__ w0, int64_t frame_stride, bool head_ok, int LP,
-                                     int F, float inv_LP, int j, bool logits, float (&alpha)[kSPL],
-                                     int (&fr)[kSPL]) {
-  const int FLP = F * LP;
+struct FlatUnit {
+  float w[kSPL];
+  float2 s[kSPL];
+};
+
+// Frame of the lane's samples: frame f = t / LP holds samples
+// [f*LP, (f+1)*LP) of a head; -1 for no sample.
+template <int kSPL>
+__device__ inline void flat_frames(bool head_ok, int FLP, float inv_LP, int j, int (&fr)[kSPL]) {
 #pragma unroll
   for (int i = 0; i < kSPL; ++i) {
     const int t = j + 8 * i;
-    const bool valid = head_ok && t < FLP;
-    const int f = valid ? small_div(t, inv_LP) : -1;
-    fr[i] = f;
-    alpha[i] = valid ? w0[f * frame_stride + (t - f * LP)] : 0.f;
+    fr[i] = head_ok && t < FLP ? small_div(t, inv_LP) : -1;
   }
+}
+
+// Issue the loads of a unit's inputs (consumed one unit later, so that they
+// arrive while the wave gathers).
+template <int kSPL>
+__device__ inline void load_flat_unit(FlatUnit<kSPL>& u, const GatherArgs& a, int64_t b, int64_t q, int hb, int g,
+                                      int j) {
+  const int h = hb + g;
+  const bool head_ok = h < a.nH;
+  const int64_t src_row = (b * a.F * a.Nq + q) * a.nH + (head_ok ? h : 0);  // frame 0
+  const int64_t stride = a.Nq * a.nH * a.LP;                                // elements per frame
+  const float* w0 = a.weights + src_row * a.LP;
+  const float2* s0 = reinterpret_cast<const float2*>(a.loc) + src_row * a.LP;
+  int fr[kSPL];
+  flat_frames<kSPL>(head_ok, a.F * a.LP, a.inv_LP, j, fr);
+#pragma unroll
+  for (int i = 0; i < kSPL; ++i) {
+    const int f = fr[i];
+    const int64_t at = f >= 0 ? f * stride + (j + 8 * i - f * a.LP) : 0;
+    u.w[i] = f >= 0 ? w0[at] : 0.f;
+    u.s[i] = f >= 0 ? s0[at] : make_float2(0.f, 0.f);
+  }
+}
+
+// The unit's sample weights: probabilities as given, or a softmax per frame
+// over that frame's L*P logits, reduced over the lanes of the group that
+// hold its samples.
+template <int kSPL>
+__device__ inline void flat_weights(const FlatUnit<kSPL>& u, const int (&fr)[kSPL], int F, bool logits,
+                                    float (&alpha)[kSPL]) {
+#pragma unroll
+  for (int i = 0; i < kSPL; ++i) alpha[i] = u.w[i];
   if (!logits) return;
   for (int f = 0; f < F; ++f) {
     float m = -INFINITY;
@@ -210,33 +301,11 @@ __device__ inline void frame_weights(const float* __restrict__ w0, int64_t frame
   }
 }
 
-// Work items of the operator: the queries (b, q) in index order, or, with a
-// plan from msda_plan, batch item by batch item in the plan's locality
-// order.  Each die takes a contiguous eighth of a batch item's items.
-template <typename Body>
-__device__ inline void for_each_msda_item(const GatherArgs& a, int waves_per_block, Body body) {
-  const int64_t n_queries = a.B * a.Nq;
-  if (!a.plan) {
-    XcdSplit split(n_queries, waves_per_block);
-    for (int64_t item = split.begin; item < split.end; item += split.stride) body(item);
-    return;
-  }
-  for (int64_t bi = 0; bi < a.B; ++bi) {
-    const int64_t lo = bi * a.Nq;
-    XcdSplit split(a.Nq, waves_per_block);
-    for (int64_t i = lo + split.begin; i < lo + split.end; i += split.stride) {
-      // entries outside [0, B*Nq) are skipped: a foreign plan never sends a
-      // read out of bounds (its queries' rows are then left unwritten)
-      const int64_t item = uniform((int64_t)a.plan[i]);
-      if (item >= 0 && item < n_queries) body(item);
-    }
-  }
-}
-
 // kFlat: all F frames' samples of a head are staged together and gathered
 // in one pass through one buffer descriptor spanning the batch item's F
-// images (needs F*L*P <= 8*kSPL and F images under 2^31 bytes); otherwise
-// frame by frame.
+// images (needs F*L*P <= 8*kSPL and F images under 2^31 bytes); the wave
+// loads the next unit's inputs before it stages and gathers the current
+// one.  Otherwise frame by frame.
 template <bool kBF16, int kSPL, bool kFlat>
 __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(GatherArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -248,50 +317,81 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
   uint2* rows = reinterpret_cast<uint2*>(smem + sizeof(Level) * kMaxLevels) +
                 ((size_t)wave * kHeadSlots + g) * meta_stride(kFlat ? a.F * a.LP : a.LP);
   const uint32_t row_bytes = kBF16 ? 64u : 128u;
-  const int64_t frame_rows = a.Nq * a.nH;  // rows of locations / weights per frame
+  MsdaWalk walk(a, waves_per_block);
 
-  for_each_msda_item(a, waves_per_block, [&](int64_t item) {
-    const int64_t b = item / a.Nq, q = item % a.Nq;
-    for (int hb = 0; hb < a.nH; hb += kHeadSlots) {
+  if constexpr (kFlat) {
+    int64_t item = walk.next(), b = 0, q = 0;
+    int hb = 0;
+    FlatUnit<kSPL> cur;
+    if (item >= 0) {
+      split_item(item, a.Nq, b, q);
+      load_flat_unit<kSPL>(cur, a, b, q, hb, g, j);
+    }
+    while (item >= 0) {
+      // the lane's group and channel slot, re-derived in every unit so that
+      // the compiler does not hold their loop-invariant consequences in
+      // registers across the gather (which the occupancy needs)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int g = ln / 8, j = ln % 8;
+      // the next unit: its inputs are in flight while this one runs
+      int64_t n_item = item, nb = b, nq = q;
+      int n_hb = hb + kHeadSlots;
+      if (n_hb >= a.nH) {
+        n_hb = 0;
+        n_item = walk.next();
+        if (n_item >= 0) split_item(n_item, a.Nq, nb, nq);
+      }
+      FlatUnit<kSPL> nxt;
+      if (n_item >= 0) load_flat_unit<kSPL>(nxt, a, nb, nq, n_hb, g, j);
+
       const int h = hb + g;
-      const bool head_ok = h < a.nH;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (kFlat) {
-        const int64_t src_row = (b * a.F * a.Nq + q) * a.nH + (head_ok ? h : 0);  // frame 0
-        const int64_t stride = frame_rows * a.LP;                                // elements per frame
-        float alpha[kSPL];
-        int fr[kSPL];
-        frame_weights<kSPL>(a.weights + src_row * a.LP, stride, head_ok, a.LP, a.F, a.inv_LP, j,
-                            a.weight_logits != 0, alpha, fr);
-        const float2* loc = reinterpret_cast<const float2*>(a.loc) + src_row * a.LP;
-        double xs[kSPL], ys[kSPL];
-        uint32_t live = 0u;
+      int fr[kSPL];
+      flat_frames<kSPL>(h < a.nH, a.F * a.LP, a.inv_LP, j, fr);
+      float alpha[kSPL];
+      flat_weights<kSPL>(cur, fr, a.F, a.weight_logits != 0, alpha);
+      double xs[kSPL], ys[kSPL];
+      uint32_t live = 0u;
 #pragma unroll
-        for (int i = 0; i < kSPL; ++i) {
-          const int f = fr[i] < 0 ? 0 : fr[i];
-          const int k = j + 8 * i - f * a.LP;
-          const Level L = lv[fr[i] < 0 ? 0 : small_div(k, a.inv_P)];
-          const float2 s = fr[i] >= 0 ? loc[f * stride + k] : make_float2(0.f, 0.f);
-          xs[i] = (double)s.x * L.W - 0.5;
-          ys[i] = (double)s.y * L.H - 0.5;
-          if (fr[i] >= 0 && sample_live(xs[i], ys[i], L)) live |= 1u << i;
-        }
-        const int LP = a.LP;
-        const float inv_LP = a.inv_LP, inv_P = a.inv_P;
-        const uint32_t image_bytes = a.image_bytes;
-        const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv,
-                                       [&](int i) {
-                                         const int t = j + 8 * i;
-                                         const int f = small_div(t, inv_LP);
-                                         return make_int2(small_div(t - f * LP, inv_P), (int)(f * image_bytes));
-                                       },
-                                       j, h, a.nH, a.Nv, row_bytes);
-        wave_lds_sync();
-        const auto img = make_rsrc(static_cast<const char*>(a.value) + b * a.F * (int64_t)a.image_bytes,
-                                   (uint32_t)(a.F * (int64_t)a.image_bytes));
-        gather_rows<kBF16>(rows, R, img, j, acc);
-        wave_lds_sync();
-      } else {
+      for (int i = 0; i < kSPL; ++i) {
+        const int f = fr[i] < 0 ? 0 : fr[i];
+        const int k = j + 8 * i - f * a.LP;
+        const Level L = lv[fr[i] < 0 ? 0 : small_div(k, a.inv_P)];
+        xs[i] = (double)cur.s[i].x * L.W - 0.5;
+        ys[i] = (double)cur.s[i].y * L.H - 0.5;
+        if (fr[i] >= 0 && sample_live(xs[i], ys[i], L)) live |= 1u << i;
+      }
+      const int LP = a.LP;
+      const float inv_LP = a.inv_LP, inv_P = a.inv_P;
+      const uint32_t image_bytes = a.image_bytes;
+      const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv,
+                                     [&](int i) {
+                                       const int t = j + 8 * i;
+                                       const int f = small_div(t, inv_LP);
+                                       return make_int2(small_div(t - f * LP, inv_P), (int)(f * image_bytes));
+                                     },
+                                     j, h, a.nH, a.Nv, row_bytes);
+      wave_lds_sync();
+      const auto img = make_rsrc(static_cast<const char*>(a.value) + b * a.F * (int64_t)a.image_bytes,
+                                 (uint32_t)(a.F * (int64_t)a.image_bytes));
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      gather_rows<kBF16>(rows, R, img, j, acc);
+      wave_lds_sync();
+      if (h < a.nH) reinterpret_cast<float4*>(a.out + ((item * a.nH + h) * 32))[j] = scaled(acc, a.F);
+      item = n_item;
+      hb = n_hb;
+      b = nb;
+      q = nq;
+      cur = nxt;
+    }
+  } else {
+    for (int64_t item = walk.next(); item >= 0; item = walk.next()) {
+      int64_t b, q;
+      split_item(item, a.Nq, b, q);
+      for (int hb = 0; hb < a.nH; hb += kHeadSlots) {
+        const int h = hb + g;
+        const bool head_ok = h < a.nH;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int f = 0; f < a.F; ++f) {
           const int64_t img_index = b * a.F + f;
           const int64_t src_row = (img_index * a.Nq + q) * a.nH + (head_ok ? h : 0);
@@ -320,10 +420,10 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
           gather_rows<kBF16>(rows, R, img, j, acc);
           wave_lds_sync();
         }
+        if (head_ok) reinterpret_cast<float4*>(a.out + ((item * a.nH + h) * 32))[j] = scaled(acc, a.F);
       }
-      if (head_ok) reinterpret_cast<float4*>(a.out + ((item * a.nH + h) * 32))[j] = scaled(acc, a.F);
     }
-  });
+  }
 }
 
 // ---------------------------------------------------------------------------
