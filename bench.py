@@ -10,10 +10,12 @@ whole hot path: visibility, compaction and work ordering of the (camera,
 query) pairs (sca_compact) and the fused softmax / bilinear gather /
 weighted sum / camera mean (sca_gather).  Inputs are resident in HBM before
 timing starts.  Other workloads: "layer_bf16" (batch 4, bf16 value
-projection GEMM -> SCA on bf16 value -> bf16 output projection GEMM),
-"layer_full" (the same with the sampling offsets and logits projected from
-query + position embedding in one launch, and the output projection
-followed by the residual and the layer norm), "sca_bf16", "sca_rebatch"
+projection GEMM writing the head-pair layout -> SCA on that bf16 value ->
+bf16 output projection GEMM; "layer_bf16_plain" with the row-major bf16
+value layout instead), "layer_full" (the same with the sampling offsets and
+logits projected from query + position embedding in one launch, and the
+output projection followed by the residual and the layer norm), "sca_bf16"
+(the default workload on a row-major bf16 value), "sca_rebatch"
 (the default workload through the padded rebatch flow of the SCA note, an
 A/B baseline: per-camera segments padded to the longest, the operator over
 all of them, scatter-add and divide), "sca_train", "detr_train" and
@@ -367,10 +369,10 @@ def _ceiling(inb_bytes, ms, shapes):
                    f"location): every value map fits in L2, so nothing waits on memory beyond it"}
 
 
-def sca_onchip_ceiling(w, d, ws, offsets, bf16):
+def sca_onchip_ceiling(w, d, ws, offsets, bf16, pairs=False):
     """The SCA gather kernel's rate of in-map corner bytes when every corner
     row it reads sits in L2: the measured ceiling of the vector-memory path
-    for this kernel and sample mix."""
+    for this kernel and sample mix (and value layout)."""
     import numpy as np
     import torch
     import scale_deformable_attention_forward_amd as m
@@ -380,6 +382,8 @@ def sca_onchip_ceiling(w, d, ws, offsets, bf16):
     g = torch.Generator(device="cuda").manual_seed(12345)
     value = torch.randn((w["B"], w["Ncam"], Nv, w["nH"], 32), generator=g, device="cuda")
     value = value.to(torch.bfloat16) if bf16 else value
+    if pairs:
+        value = m.msda_pack_pairs_bf16(value)
     dss, dst, doff = _dev(ss), _dev(starts), _dev(off)
     slots = torch.empty((w["B"], w["Nq"], w["nH"] * 32), dtype=torch.float32, device="cuda")
     ms = _mean_launch_ms(lambda: m.sca_gather(value, dss, dst, d["reference_points_cam"], doff,
@@ -426,11 +430,15 @@ def sca_workload(kind):
     import scale_deformable_attention_forward_amd as m
 
     full = kind == "layer_full"
-    layer = kind in ("layer_bf16", "layer_full")
+    layer = kind in ("layer_bf16", "layer_full", "layer_bf16_plain")
+    # the layers write the value projection in the head-pair layout, which
+    # the gather reads with one line per x-adjacent corner pair ("_plain":
+    # the row-major bf16 layout, as A/B)
+    pairs = kind in ("layer_bf16", "layer_full")
     # one frame of the encoder: one compaction (the masks and anchors do not
     # change between layers) and the gathers of 6 layers
     layers = 6 if kind == "sca_frame6" else 1
-    bf16 = kind in ("sca_bf16", "layer_bf16", "layer_full")
+    bf16 = kind in ("sca_bf16", "layer_bf16", "layer_full", "layer_bf16_plain")
     if full:
         w = W.bevformer_layer_bf16()
     elif layer:
@@ -452,7 +460,8 @@ def sca_workload(kind):
     if layer:
         d["feat"] = _dev(w["feat"].reshape(-1, C))
         d["W_v"], d["b_v"], d["W_o"], d["b_o"] = (_dev(w[k]) for k in ("W_v", "b_v", "W_o", "b_o"))
-        d["value"] = torch.empty((B, Ncam, Nv, nH, 32), dtype=torch.bfloat16, device="cuda")
+        d["value"] = torch.empty((B, Ncam, nH, Nv, 2, 32) if pairs else (B, Ncam, Nv, nH, 32),
+                                 dtype=torch.bfloat16, device="cuda")
         d["out"] = torch.empty((B * Nq, C), dtype=torch.float32, device="cuda")
     else:
         d["value"] = _dev(w["value"])
@@ -467,7 +476,10 @@ def sca_workload(kind):
         wl.parts.append(("query_proj", lambda: m.msda_query_proj_bf16(
             d["query"], d["W_off"], d["b_off"], d["W_att"], d["b_att"], query_pos=d["query_pos"],
             offsets=d["sampling_offsets"].view(B * Nq, -1), logits=d["attention_logits"].view(B * Nq, -1))))
-    if layer:
+    if pairs:
+        wl.parts.append(("value_proj", lambda: m.msda_value_proj_pairs_bf16(d["feat"], d["W_v"], d["b_v"], Nv,
+                                                                            out=d["value"].view(-1, nH, Nv, 2, 32))))
+    elif layer:
         wl.parts.append(("value_proj", lambda: m.msda_gemm_bf16(d["feat"], d["W_v"], d["b_v"],
                                                                 out=d["value"].view(-1, C))))
     wl.parts.append(("compact", lambda: m.sca_compact(d["bev_mask"], d["reference_points_cam"], ws, hit_count=hit,
@@ -511,12 +523,14 @@ def sca_workload(kind):
         # what one gather launch must move at least once: every value map,
         # the per-query offsets and logits, the seen pairs' anchors, the
         # camera masks and work list, and the output rows
-        wl.unique_bytes = (B * Ncam * Nv * C * elem + B * Nq * nH * L * P * (8 + 4) + n_pairs * D * 8
-                           + B * Nq * (4 + 4) + B * Nq * C * 4)
-        wl.onchip = lambda: sca_onchip_ceiling(w, d, ws, off_h, bf16)
+        # (the head-pair layout holds every pixel twice)
+        wl.unique_bytes = (B * Ncam * Nv * C * elem * (2 if pairs else 1) + B * Nq * nH * L * P * (8 + 4)
+                           + n_pairs * D * 8 + B * Nq * (4 + 4) + B * Nq * C * 4)
+        wl.onchip = lambda: sca_onchip_ceiling(w, d, ws, off_h, bf16, pairs)
         if layer:
             Mv, Mo = B * Ncam * Nv, B * Nq
-            wl.extra["value_proj"] = {"flop": 2 * Mv * C * C, "bytes": Mv * C * 2 * 2 + C * C * 2}
+            wl.extra["value_proj"] = {"flop": 2 * Mv * C * C,
+                                      "bytes": Mv * C * 2 * (3 if pairs else 2) + C * C * 2}
             wl.extra["output_proj"] = {"flop": 2 * Mo * C * C, "bytes": Mo * C * 4 * 2 + C * C * 2}
         if full:
             Mq, Nqp = B * Nq, nH * L * P * 3
@@ -534,6 +548,9 @@ def sca_workload(kind):
                  "batch": B, "cameras": Ncam, "bev_queries": "200x200", "levels": "116x200/58x100/29x50/15x25",
                  "heads": nH, "head_dim": 32, "points_per_level": P, "pillar_anchors": D,
                  "value_dtype": "bf16" if bf16 else "fp32", "mask": "azimuth sectors, 1-2 cameras per query"}
+    if bf16:
+        wl.config["value_layout"] = ("head pairs [B][Ncam][nH][Nv][2][32], written by the value projection" if pairs
+                                     else "[B][Ncam][Nv][nH][32]")
     wl.dtype = "fp32 accumulate, bf16 value" if bf16 else "fp32"
     wl.kernel_key = "sca_gather_kernel_bf16" if bf16 else "sca_gather_kernel_fp32"
 
@@ -805,7 +822,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sca",
-                    choices=["sca", "layer_bf16", "layer_full", "sca_bf16", "sca_rebatch", "sca_train", "detr",
+                    choices=["sca", "layer_bf16", "layer_full", "layer_bf16_plain", "sca_bf16", "sca_rebatch",
+                             "sca_train", "detr",
                              "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny", "sca_frame6",
                              "tsa_train", "tsa_train_atomic", "detr_unplanned", "tsa_planned"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -828,7 +846,7 @@ def main():
     import scale_deformable_attention_forward_amd as m
     m.load_library()
 
-    if args.workload in ("sca", "layer_bf16", "layer_full", "sca_bf16", "sca_frame6"):
+    if args.workload in ("sca", "layer_bf16", "layer_full", "layer_bf16_plain", "sca_bf16", "sca_frame6"):
         wl = sca_workload(args.workload)
     elif args.workload == "sca_rebatch":
         wl = rebatch_workload()

@@ -80,6 +80,15 @@ extern "C" {
 /* element types */
 #define MSDA_F32 0  /* IEEE binary32 */
 #define MSDA_BF16 1 /* bfloat16 (upper half of a binary32), stored as uint16 */
+/* bfloat16 value of the SCA entry points in the head-pair layout: per value
+ * image [nH][Nv][2][Dh] with Dh == 32, element [h][p][s][d] = channel d of
+ * head h at flattened pixel p + s (s = 0, 1).  Each 128-byte line (h, p) thus
+ * holds pixel p and its right-hand neighbour p + 1, the two corners a
+ * bilinear sample reads in one row of a level, so that the gather fetches
+ * both from one cache line.  [h][Nv-1][1] is never read (msda_pack_pairs_bf16
+ * and msda_value_proj_pairs_bf16 write zeros there).  Twice the bytes of
+ * MSDA_BF16 (as many as MSDA_F32). */
+#define MSDA_BF16_PAIRS 2
 
 /* meaning of attention_weights */
 #define MSDA_WEIGHTS_PROB 0   /* already softmaxed over the L*P points of each head */
@@ -206,7 +215,8 @@ int sca_plan_workspace(int64_t B, int64_t Ncam, int64_t Nq, size_t* bytes);
  *     step 2) / max(1, hit_count[b][q]) ([8-heads] 10; [SCA-note] clamp and
  *     divide).  A query no camera sees gets zeros.
  *
- *   value                 device [B][Ncam][Nv][nH][Dh], MSDA_F32 or MSDA_BF16, 16-byte aligned
+ *   value                 device [B][Ncam][Nv][nH][Dh], MSDA_F32 or MSDA_BF16, or
+ *                         [B][Ncam][nH][Nv][2][Dh] in MSDA_BF16_PAIRS; 16-byte aligned
  *   spatial_shapes        device int64 [L][2]; level_start_index device int64 [L]
  *   reference_points_cam  device float [Ncam][B][Nq][D][2], normalised (x, y), 8-byte aligned
  *   bev_mask              device uint8 [Ncam][B][Nq][D], nonzero = anchor marked
@@ -275,6 +285,38 @@ int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes
  */
 int msda_gemm_bf16(const void* X, int x_dtype, const uint16_t* W, const float* bias, void* Y,
                    int y_dtype, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * The value projection of msda_gemm_bf16 ([8-heads] 3) with its bf16 output
+ * written in the head-pair layout (MSDA_BF16_PAIRS) for sca_forward and
+ * sca_gather: the M = n_images * Nv rows of X are the pixels of n_images
+ * value images of Nv pixels each, and the N = nH * 32 columns head h's
+ * channels h*32 .. h*32+31.  Each output row is stored twice, as the left
+ * half of its own line and the right half of its left-hand neighbour's
+ * line; [h][Nv-1][1] of every image is set to zero.  The same products,
+ * rounding and bias as msda_gemm_bf16 with y_dtype MSDA_BF16.
+ *
+ *   X      device [M][K]; MSDA_BF16 or MSDA_F32 (rounded to bf16 as read); 16-byte aligned
+ *   W      device bf16 [N][K]; bias device float [N] or NULL; W 16-byte aligned
+ *   pairs  device bf16 [n_images][nH][Nv][2][32], 16-byte aligned; must not overlap X
+ * Limits: as msda_gemm_bf16, and N % 32 == 0, M % Nv == 0, Nv * nH * 128 < 2^31.
+ */
+int msda_value_proj_pairs_bf16(const void* X, int x_dtype, const uint16_t* W, const float* bias, uint16_t* pairs,
+                               int64_t M, int64_t N, int64_t K, int64_t Nv, void* stream);
+
+/*
+ * A bf16 value in the usual layout [n_images][Nv][nH][32] rewritten in the
+ * head-pair layout [n_images][nH][Nv][2][32] (MSDA_BF16_PAIRS), for callers
+ * whose value comes from elsewhere than msda_value_proj_pairs_bf16.  A pure
+ * copy: every element keeps its bits; [h][Nv-1][1] is set to zero.
+ *
+ *   value  device bf16 [n_images][Nv][nH][32], 16-byte aligned
+ *   pairs  device bf16 [n_images][nH][Nv][2][32], 16-byte aligned; must not overlap value
+ * (both may be NULL when n_images == 0).
+ * Limits: 1 <= nH <= 64; Nv >= 1; Nv * nH * 128 < 2^31; n_images >= 0.
+ */
+int msda_pack_pairs_bf16(const uint16_t* value, uint16_t* pairs, int64_t n_images, int64_t Nv, int nH,
+                         void* stream);
 
 /*
  * Sampling offsets and attention logits from the query, in one launch on

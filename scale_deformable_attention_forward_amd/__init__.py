@@ -18,7 +18,10 @@ Functions (same names as the C entry points):
                 sca_compact, sca_gather, sca_backward, sca_backward_workspace_size
   padded flow:  sca_rebatch, sca_scatter_mean (and sca_forward_rebatch, which
                 chains them with the compaction and msda_forward)
-  projections:  msda_gemm_bf16, msda_query_proj_bf16, msda_output_proj_bf16
+  projections:  msda_gemm_bf16, msda_query_proj_bf16, msda_output_proj_bf16,
+                msda_value_proj_pairs_bf16 (the value projection written in the
+                head-pair layout that the SCA entry points also take)
+  layout:       msda_pack_pairs_bf16 (a bf16 value rewritten in that layout)
   status:       msda_status_string, msda_last_error
 """
 import ctypes
@@ -28,17 +31,18 @@ import os
 import torch
 
 __all__ = [
-    "MsdaError", "MSDA_F32", "MSDA_BF16", "MSDA_WEIGHTS_PROB", "MSDA_WEIGHTS_LOGITS",
+    "MsdaError", "MSDA_F32", "MSDA_BF16", "MSDA_BF16_PAIRS", "MSDA_WEIGHTS_PROB", "MSDA_WEIGHTS_LOGITS",
     "library_path", "load_library", "msda_forward", "msda_forward_frames", "msda_plan_size", "msda_plan",
     "msda_gather", "plan_order",
     "sca_workspace_size", "sca_plan_workspace",
-    "sca_forward", "sca_forward_noalloc", "sca_compact", "sca_gather", "msda_gemm_bf16", "msda_query_proj_bf16", "msda_output_proj_bf16",
+    "sca_forward", "sca_forward_noalloc", "sca_compact", "sca_gather", "msda_gemm_bf16", "msda_query_proj_bf16",
+    "msda_output_proj_bf16", "msda_value_proj_pairs_bf16", "msda_pack_pairs_bf16",
     "sca_rebatch", "sca_scatter_mean", "sca_forward_rebatch", "msda_backward_workspace_size",
     "sca_backward_workspace_size", "msda_backward", "msda_backward_frames", "sca_backward", "msda_status_string",
     "msda_last_error",
 ]
 
-MSDA_F32, MSDA_BF16 = 0, 1
+MSDA_F32, MSDA_BF16, MSDA_BF16_PAIRS = 0, 1, 2
 MSDA_WEIGHTS_PROB, MSDA_WEIGHTS_LOGITS = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -86,6 +90,8 @@ def load_library():
     lib.sca_gather.argtypes = [_p, _int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _int,
                                _p, _p, _sz, _p]
     lib.msda_gemm_bf16.argtypes = [_p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p]
+    lib.msda_value_proj_pairs_bf16.argtypes = [_p, _int, _p, _p, _p, _i64, _i64, _i64, _i64, _p]
+    lib.msda_pack_pairs_bf16.argtypes = [_p, _p, _i64, _i64, _int, _p]
     lib.msda_backward.argtypes = [_p, _int, _p, _p, _p, _p, _int, _p, _i64, _i64, _i64, _int, _int, _int, _int, _p,
                                   _p, _p, _p, _sz, _p]
     lib.msda_backward_frames.argtypes = [_p, _int, _p, _p, _p, _p, _int, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
@@ -102,7 +108,8 @@ def load_library():
               lib.sca_workspace_size,
               lib.sca_plan_workspace, lib.sca_forward,
               lib.sca_forward_noalloc,
-              lib.sca_compact, lib.sca_gather, lib.msda_gemm_bf16):
+              lib.sca_compact, lib.sca_gather, lib.msda_gemm_bf16, lib.msda_value_proj_pairs_bf16,
+              lib.msda_pack_pairs_bf16):
         f.restype = _int
     lib.msda_status_string.argtypes = [_int]
     lib.msda_status_string.restype = ctypes.c_char_p
@@ -162,6 +169,20 @@ def _value_dtype(value):
     if value.dtype == torch.bfloat16:
         return MSDA_BF16
     raise TypeError(f"value must be float32 or bfloat16, got {value.dtype}")
+
+
+def _sca_value(value):
+    """(B, Ncam, Nv, nH, Dh, value_dtype) of an SCA value: [B,Ncam,Nv,nH,Dh]
+    float32 or bfloat16, or bfloat16 [B,Ncam,nH,Nv,2,Dh] in the head-pair
+    layout (MSDA_BF16_PAIRS)."""
+    if value.dim() == 6:
+        if value.dtype != torch.bfloat16 or value.shape[4] != 2:
+            raise TypeError("a 6-dimensional SCA value is the bfloat16 head-pair layout [B,Ncam,nH,Nv,2,Dh]; "
+                            f"got {value.dtype} {tuple(value.shape)}")
+        B, Ncam, nH, Nv, _, Dh = value.shape
+        return B, Ncam, Nv, nH, Dh, MSDA_BF16_PAIRS
+    B, Ncam, Nv, nH, Dh = value.shape
+    return B, Ncam, Nv, nH, Dh, _value_dtype(value)
 
 
 def _given_stream(fn):
@@ -338,7 +359,9 @@ def _sca_outputs(B, Ncam, Nq, hit_count, pair_offsets, pair_q):
 def sca_forward(value, spatial_shapes, level_start_index, reference_points_cam, bev_mask, sampling_offsets,
                 attention_logits, slots=None, hit_count=None, pair_offsets=None, pair_q=None, workspace=None,
                 stream=None):
-    """value [B,Ncam,Nv,nH,Dh]; reference_points_cam float32 [Ncam,B,Nq,D,2];
+    """value [B,Ncam,Nv,nH,Dh] float32 or bfloat16, or bfloat16 [B,Ncam,nH,Nv,2,Dh] in the
+    head-pair layout (msda_pack_pairs_bf16, msda_value_proj_pairs_bf16);
+    reference_points_cam float32 [Ncam,B,Nq,D,2];
     bev_mask uint8|bool [Ncam,B,Nq,D]; sampling_offsets float32
     [B,Nq,nH,L,P,2]; attention_logits float32 [B,Nq,nH,L*P].
 
@@ -347,7 +370,7 @@ def sca_forward(value, spatial_shapes, level_start_index, reference_points_cam, 
     filled when given.  workspace: uint8 tensor of >= sca_workspace_size()
     bytes, allocated here when None."""
     lib = load_library()
-    B, Ncam, Nv, nH, Dh = value.shape
+    B, Ncam, Nv, nH, Dh, vdt = _sca_value(value)
     _, _, Nq, D, _ = reference_points_cam.shape
     _, _, _, L, P, _ = sampling_offsets.shape
     _sca_inputs(B, Ncam, Nq, D, nH, L, P, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets,
@@ -362,7 +385,7 @@ def sca_forward(value, spatial_shapes, level_start_index, reference_points_cam, 
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     i32 = (torch.int32,)
-    rc = lib.sca_forward(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
+    rc = lib.sca_forward(_ptr(value, "value"), vdt, _ptr(spatial_shapes, "spatial_shapes", _I64),
                          _ptr(level_start_index, "level_start_index", _I64),
                          _ptr(reference_points_cam, "reference_points_cam", _F32),
                          _ptr(bev_mask, "bev_mask", (torch.uint8, torch.bool)),
@@ -384,7 +407,7 @@ def sca_forward_noalloc(value, spatial_shapes, level_start_index, reference_poin
     allocates, so slots must be given.  Calls that may overlap on one device
     race on that array; order them."""
     lib = load_library()
-    B, Ncam, Nv, nH, Dh = value.shape
+    B, Ncam, Nv, nH, Dh, vdt = _sca_value(value)
     _, _, Nq, D, _ = reference_points_cam.shape
     _, _, _, L, P, _ = sampling_offsets.shape
     _sca_inputs(B, Ncam, Nq, D, nH, L, P, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets,
@@ -395,7 +418,7 @@ def sca_forward_noalloc(value, spatial_shapes, level_start_index, reference_poin
     _sca_outputs(B, Ncam, Nq, hit_count, pair_offsets, pair_q)
     _numel(bev_mask, "bev_mask", Ncam * B * Nq * D)
     i32 = (torch.int32,)
-    rc = lib.sca_forward_noalloc(_ptr(value, "value"), _value_dtype(value),
+    rc = lib.sca_forward_noalloc(_ptr(value, "value"), vdt,
                                  _ptr(spatial_shapes, "spatial_shapes", _I64),
                                  _ptr(level_start_index, "level_start_index", _I64),
                                  _ptr(reference_points_cam, "reference_points_cam", _F32),
@@ -435,7 +458,7 @@ def sca_gather(value, spatial_shapes, level_start_index, reference_points_cam, s
     """Stage 2 of sca_forward: gather, weighted sums and camera mean for the
     queries on the work list the preceding sca_compact left in `workspace`."""
     lib = load_library()
-    B, Ncam, Nv, nH, Dh = value.shape
+    B, Ncam, Nv, nH, Dh, vdt = _sca_value(value)
     _, _, Nq, D, _ = reference_points_cam.shape
     _, _, _, L, P, _ = sampling_offsets.shape
     _sca_inputs(B, Ncam, Nq, D, nH, L, P, spatial_shapes, level_start_index, reference_points_cam, sampling_offsets,
@@ -444,7 +467,7 @@ def sca_gather(value, spatial_shapes, level_start_index, reference_points_cam, s
     dev = value.device
     if slots is None:
         slots = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=dev)
-    rc = lib.sca_gather(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
+    rc = lib.sca_gather(_ptr(value, "value"), vdt, _ptr(spatial_shapes, "spatial_shapes", _I64),
                         _ptr(level_start_index, "level_start_index", _I64),
                         _ptr(reference_points_cam, "reference_points_cam", _F32),
                         _ptr(sampling_offsets, "sampling_offsets", _F32),
@@ -474,6 +497,50 @@ def msda_gemm_bf16(X, W, bias=None, y_dtype=torch.bfloat16, out=None, stream=Non
                             _ptr(bias, "bias", _F32), _ptr(out, "out", (torch.float32, torch.bfloat16)), y_dt,
                             M, N, K, _stream(stream, X.device))
     _check("msda_gemm_bf16", rc)
+    return out
+
+
+@_given_stream
+def msda_value_proj_pairs_bf16(X, W, bias, Nv, out=None, stream=None):
+    """The value projection X W^T + bias (X [M,K] float32 or bfloat16, W
+    bfloat16 [N,K], bias float32 [N] or None) written in bfloat16 in the
+    head-pair layout: returns out [M/Nv, N/32, Nv, 2, 32], the M rows being
+    M/Nv value images of Nv pixels."""
+    lib = load_library()
+    M, K = X.shape
+    N = W.shape[0]
+    _numel(W, "W", N * K)
+    _numel(bias, "bias", N)
+    n_img = M // Nv if Nv > 0 else 0
+    _numel(out, "out", n_img * (N // 32) * Nv * 64, at_least=True)
+    if out is None:
+        out = torch.empty((n_img, N // 32, Nv, 2, 32), dtype=torch.bfloat16, device=X.device)
+    x_dt = MSDA_F32 if X.dtype == torch.float32 else MSDA_BF16
+    rc = lib.msda_value_proj_pairs_bf16(_ptr(X, "X", (torch.float32, torch.bfloat16)), x_dt,
+                                        _ptr(W, "W", (torch.bfloat16,)), _ptr(bias, "bias", _F32),
+                                        _ptr(out, "out", (torch.bfloat16,)), M, N, K, Nv, _stream(stream, X.device))
+    _check("msda_value_proj_pairs_bf16", rc)
+    return out
+
+
+@_given_stream
+def msda_pack_pairs_bf16(value, out=None, stream=None):
+    """A bfloat16 value [..., Nv, nH, 32] rewritten in the head-pair layout:
+    returns out [..., nH, Nv, 2, 32] (every element keeps its bits; the
+    right half of each head's last line is zero)."""
+    lib = load_library()
+    *lead, Nv, nH, Dh = value.shape
+    if Dh != 32:
+        raise ValueError(f"value: the last dimension must be 32 channels, got {Dh}")
+    n_img = 1
+    for d in lead:
+        n_img *= d
+    _numel(out, "out", n_img * nH * Nv * 64, at_least=True)
+    if out is None:
+        out = torch.empty((*lead, nH, Nv, 2, 32), dtype=torch.bfloat16, device=value.device)
+    rc = lib.msda_pack_pairs_bf16(_ptr(value, "value", (torch.bfloat16,)), _ptr(out, "out", (torch.bfloat16,)),
+                                  n_img, Nv, nH, _stream(stream, value.device))
+    _check("msda_pack_pairs_bf16", rc)
     return out
 
 

@@ -46,13 +46,18 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 constexpr int64_t kI31 = (int64_t)1 << 31;
 
-// Checks shared by the MSDA-style entry points.  images = number of value images.
+// Checks shared by the MSDA-style entry points; pairs_ok: the entry point
+// takes MSDA_BF16_PAIRS (the SCA forward ones).
 int check_common(const void* value, int value_dtype, const int64_t* shapes, const int64_t* starts, int64_t Nv,
-                 int64_t Nq, int nH, int Dh, int L, int P, const void* out, uint32_t* image_bytes) {
+                 int64_t Nq, int nH, int Dh, int L, int P, const void* out, uint32_t* image_bytes,
+                 bool pairs_ok = false) {
   // with no queries nothing per query is read or written: those buffers may be null
   if (!value || !shapes || !starts || (!out && Nq != 0)) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
-  if (value_dtype != MSDA_F32 && value_dtype != MSDA_BF16)
-    return fail(MSDA_ERR_INVALID_ARG, "value_dtype %d is neither MSDA_F32 nor MSDA_BF16", value_dtype);
+  if (value_dtype == MSDA_BF16_PAIRS && !pairs_ok)
+    return fail(MSDA_ERR_INVALID_ARG, "MSDA_BF16_PAIRS is taken by sca_forward, sca_gather and "
+                "sca_forward_noalloc only");
+  if (value_dtype != MSDA_F32 && value_dtype != MSDA_BF16 && value_dtype != MSDA_BF16_PAIRS)
+    return fail(MSDA_ERR_INVALID_ARG, "value_dtype %d is not MSDA_F32, MSDA_BF16 or MSDA_BF16_PAIRS", value_dtype);
   if (Nv < 1 || Nq < 0 || nH < 1 || Dh < 1 || L < 1 || P < 1)
     return fail(MSDA_ERR_INVALID_ARG, "sizes must be positive (Nv=%lld Nq=%lld nH=%d Dh=%d L=%d P=%d)",
                 (long long)Nv, (long long)Nq, nH, Dh, L, P);
@@ -60,7 +65,8 @@ int check_common(const void* value, int value_dtype, const int64_t* shapes, cons
   if (nH > 64) return fail(MSDA_ERR_UNSUPPORTED, "nH=%d: at most 64 heads", nH);
   if ((int64_t)L * P > 64) return fail(MSDA_ERR_UNSUPPORTED, "L*P=%lld: at most 64 points per head", (long long)L * P);
   if (Nv >= kI31 || Nq >= kI31) return fail(MSDA_ERR_UNSUPPORTED, "Nv and Nq must be below 2^31");
-  const int64_t elem = value_dtype == MSDA_F32 ? 4 : 2;
+  // the head-pair layout stores every pixel twice
+  const int64_t elem = value_dtype == MSDA_BF16 ? 2 : 4;
   const int64_t bytes = Nv * nH * Dh * elem;
   if (bytes >= kI31) return fail(MSDA_ERR_UNSUPPORTED, "one value image is %lld bytes; the limit is 2^31", (long long)bytes);
   if (!aligned(value, 16) || (Nq != 0 && !aligned(out, 16)))
@@ -287,7 +293,7 @@ int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes
                void* workspace, size_t workspace_bytes, void* stream) {
   uint32_t image_bytes = 0;
   int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, slots,
-                        &image_bytes);
+                        &image_bytes, true);
   if (rc != MSDA_OK) return rc;
   if ((!reference_points_cam || !sampling_offsets || !attention_logits) && Nq != 0)
     return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
@@ -305,7 +311,8 @@ int sca_gather(const void* value, int value_dtype, const int64_t* spatial_shapes
   msda::GatherArgs a = {};
   a.value = value;
   a.image_bytes = image_bytes;
-  a.bf16 = value_dtype == MSDA_BF16;
+  a.bf16 = value_dtype != MSDA_F32;
+  a.pairs = value_dtype == MSDA_BF16_PAIRS;
   a.shapes = spatial_shapes;
   a.starts = level_start_index;
   a.L = L;
@@ -337,7 +344,7 @@ int sca_forward(const void* value, int value_dtype, const int64_t* spatial_shape
   // check everything both stages check before enqueuing either
   uint32_t image_bytes = 0;
   int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, slots,
-                        &image_bytes);
+                        &image_bytes, true);
   if (rc != MSDA_OK) return rc;
   if ((!reference_points_cam || !bev_mask || !sampling_offsets || !attention_logits) && Nq != 0)
     return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
@@ -373,6 +380,59 @@ int msda_gemm_bf16(const void* X, int x_dtype, const uint16_t* W, const float* b
   g.Y1 = Y;
   g.y_f32 = y_dtype == MSDA_F32;
   return hip_status(msda::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)), "gemm launch");
+}
+
+int msda_value_proj_pairs_bf16(const void* X, int x_dtype, const uint16_t* W, const float* bias, uint16_t* pairs,
+                               int64_t M, int64_t N, int64_t K, int64_t Nv, void* stream) {
+  if (!X || !W || !pairs) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (x_dtype != MSDA_F32 && x_dtype != MSDA_BF16)
+    return fail(MSDA_ERR_INVALID_ARG, "x_dtype must be MSDA_F32 or MSDA_BF16");
+  int rc = check_gemm_sizes(M, N, K);
+  if (rc != MSDA_OK) return rc;
+  if (Nv < 1) return fail(MSDA_ERR_INVALID_ARG, "Nv >= 1 required");
+  if (N % 32 != 0) return fail(MSDA_ERR_UNSUPPORTED, "N %% 32 == 0 required (heads of 32 channels), got %lld",
+                               (long long)N);
+  if (M % Nv != 0) return fail(MSDA_ERR_SHAPE, "M=%lld is not a whole number of images of Nv=%lld rows",
+                               (long long)M, (long long)Nv);
+  if (Nv * (N / 32) * 128 >= kI31)
+    return fail(MSDA_ERR_UNSUPPORTED, "one image in the head-pair layout is %lld bytes; the limit is 2^31",
+                (long long)(Nv * (N / 32) * 128));
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(pairs, 16) || (bias && !aligned(bias, 4)))
+    return fail(MSDA_ERR_INVALID_ARG, "X, W and pairs must be 16-byte aligned");
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(X), p0 = reinterpret_cast<uintptr_t>(pairs);
+  const uintptr_t xb = (uintptr_t)(M * K * (x_dtype == MSDA_F32 ? 4 : 2)), pb = (uintptr_t)(M * N * 4);
+  if (M != 0 && x0 < p0 + pb && p0 < x0 + xb) return fail(MSDA_ERR_INVALID_ARG, "pairs must not overlap X");
+  g_last_error[0] = '\0';
+  if (M == 0) return MSDA_OK;
+  msda::GemmArgs g = gemm_args(X, x_dtype == MSDA_F32, M, N, K);
+  g.W1 = W;
+  g.bias1 = bias;
+  g.Y1 = pairs;
+  g.y_f32 = 0;
+  g.pairs_Nv = Nv;
+  return hip_status(msda::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)), "value projection launch");
+}
+
+int msda_pack_pairs_bf16(const uint16_t* value, uint16_t* pairs, int64_t n_images, int64_t Nv, int nH,
+                         void* stream) {
+  // with no images nothing is read or written: the buffers may be null
+  if ((!value || !pairs) && n_images != 0) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
+  if (n_images < 0 || Nv < 1 || nH < 1)
+    return fail(MSDA_ERR_INVALID_ARG, "n_images >= 0, Nv >= 1 and nH >= 1 required");
+  if (nH > 64) return fail(MSDA_ERR_UNSUPPORTED, "nH=%d: at most 64 heads", nH);
+  if (Nv >= kI31 || Nv * nH * 128 >= kI31)
+    return fail(MSDA_ERR_UNSUPPORTED, "one image in the head-pair layout is %lld bytes; the limit is 2^31",
+                (long long)(Nv * nH * 128));
+  if (n_images > ((int64_t)1 << 40) / (Nv * nH * 128))
+    return fail(MSDA_ERR_UNSUPPORTED, "n_images=%lld too large", (long long)n_images);
+  if (!aligned(value, 16) || !aligned(pairs, 16)) return fail(MSDA_ERR_INVALID_ARG, "value and pairs must be 16-byte aligned");
+  const uintptr_t v0 = reinterpret_cast<uintptr_t>(value), p0 = reinterpret_cast<uintptr_t>(pairs);
+  const uintptr_t vb = (uintptr_t)(n_images * Nv * nH * 64), pb = 2 * vb;
+  if (vb != 0 && v0 < p0 + pb && p0 < v0 + vb) return fail(MSDA_ERR_INVALID_ARG, "pairs must not overlap value");
+  g_last_error[0] = '\0';
+  if (n_images == 0) return MSDA_OK;
+  return hip_status(msda::launch_pack_pairs(value, pairs, n_images, Nv, nH, static_cast<hipStream_t>(stream)),
+                    "pair packing launch");
 }
 
 int msda_query_proj_bf16(const float* query, const float* query_pos, const uint16_t* W_off, const float* b_off,

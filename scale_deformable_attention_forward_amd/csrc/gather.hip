@@ -42,10 +42,16 @@ namespace msda {
 constexpr int kBatch = 8;  // corner rows per load batch
 constexpr int kMaxWavesPerBlock = 4;
 
-__host__ __device__ inline int rows_padded(int LP) { return (4 * LP + kBatch - 1) / kBatch * kBatch; }
-// per-head stride of the LDS staging area, in (offset, weight) pairs; odd, so
+// staged (offset, weight) slots of one head: 4 per sample, the count
+// rounded up to whole load batches (kBatch slots; 2 * kBatch in the
+// head-pair layout, where a load takes two slots, one per corner of a pair)
+__host__ __device__ inline int rows_padded(int LP, bool pairs = false) {
+  const int q = pairs ? 2 * kBatch : kBatch;
+  return (4 * LP + q - 1) / q * q;
+}
+// per-head stride of the LDS staging area, in (offset, weight) slots; odd, so
 // that the 8 groups of a wave hit different LDS banks
-__host__ __device__ inline int meta_stride(int LP) { return rows_padded(LP) + 1; }
+__host__ __device__ inline int meta_stride(int LP, bool pairs = false) { return rows_padded(LP, pairs) + 1; }
 
 // The four corners of one sample at continuous level coordinate (x, y):
 // (row offset in bytes within the image, alpha * bilinear weight), with
@@ -76,6 +82,38 @@ __device__ inline void sample_corners(uint2 (&c)[4], double x, double y, float a
   }
 }
 
+// The same four corners for a value in the head-pair layout (per image
+// [nH][Nv][2][32] bf16: line (h, p) of 128 bytes holds pixel p of head h in
+// its left half and pixel p + 1 in its right half), as two x-adjacent pairs:
+// c[2*dy] = corner A = (x0, y0 + dy), c[2*dy + 1] = corner B = (x0 + 1,
+// y0 + dy), each (byte offset of the corner's 64 bytes, weight).  B is read
+// from the right half of A's line when A is inside the map (one line for the
+// pair), else from the left half of its own line.
+__device__ inline void sample_pairs(uint2 (&c)[4], double x, double y, float alpha, const Level& lv, bool live,
+                                    int h, int Nv) {
+  x = fmin(fmax(x, -2.0), (double)lv.W + 1.0);
+  y = fmin(fmax(y, -2.0), (double)lv.H + 1.0);
+  const double xf = floor(x), yf = floor(y);
+  const float fx = (float)(x - xf), fy = (float)(y - yf);
+  const int ix = (int)xf, iy = (int)yf;
+  const long long base = lv.start + (long long)iy * lv.W + ix;
+  const float wx[2] = {1.f - fx, fx};
+  const float wy[2] = {1.f - fy, fy};
+  const long long head = (long long)h * Nv;
+#pragma unroll
+  for (int dy = 0; dy < 2; ++dy) {
+    const int cy = iy + dy;
+    const long long pa = base + (long long)dy * lv.W, pb = pa + 1;
+    const bool row_ok = live && cy >= 0 && cy < lv.H;
+    const bool ok_a = row_ok && ix >= 0 && ix < lv.W && pa >= 0 && pa < Nv;
+    const bool ok_b = row_ok && ix + 1 >= 0 && ix + 1 < lv.W && pb >= 0 && pb < Nv;
+    const uint32_t line_a = (uint32_t)((head + pa) * 128), line_b = (uint32_t)((head + pb) * 128);
+    c[2 * dy] = ok_a ? make_uint2(line_a, __float_as_uint(alpha * wx[0] * wy[dy])) : make_uint2(kSkip, 0u);
+    c[2 * dy + 1] = ok_b ? make_uint2(ok_a ? line_a + 64u : line_b, __float_as_uint(alpha * wx[1] * wy[dy]))
+                         : make_uint2(kSkip, 0u);
+  }
+}
+
 // Write the four corner rows of the group's live samples densely into `rows`
 // (lane order, then sample order; a prefix sum over the group's 8 lanes
 // places each lane) and pad every group of the wave with skipped rows up to
@@ -83,7 +121,9 @@ __device__ inline void sample_corners(uint2 (&c)[4], double x, double y, float a
 // (the same in every lane).  Dead samples cost no row at all.  where(i)
 // gives sample i's level index and the byte offset of its image within the
 // buffer the gather reads (non-zero when one buffer holds several frames).
-template <int kSPL, typename Where>
+// With kPairs, the slots are sample_pairs' (A, B) per pair and the count
+// is rounded up to 2 * kBatch.
+template <int kSPL, typename Where, bool kPairs = false>
 __device__ inline int stage_rows(uint2* __restrict__ rows, const double (&xs)[kSPL], const double (&ys)[kSPL],
                                  const float (&alpha)[kSPL], uint32_t live, const Level* lv, Where where, int j,
                                  int h, int nH, int Nv, uint32_t row_bytes) {
@@ -99,14 +139,18 @@ __device__ inline int stage_rows(uint2* __restrict__ rows, const double (&xs)[kS
   wave_max = max(wave_max, __shfl_xor(wave_max, 8));
   wave_max = max(wave_max, __shfl_xor(wave_max, 16));
   wave_max = max(wave_max, __shfl_xor(wave_max, 32));
-  const int R = (wave_max + kBatch - 1) / kBatch * kBatch;
+  constexpr int q = kPairs ? 2 * kBatch : kBatch;
+  const int R = (wave_max + q - 1) / q * q;
   int pos = incl - n;
 #pragma unroll
   for (int i = 0; i < kSPL; ++i) {
     if ((live >> i) & 1u) {
       const int2 at = where(i);
       uint2 c[4];
-      sample_corners(c, xs[i], ys[i], alpha[i], lv[at.x], true, h, nH, Nv, row_bytes);
+      if constexpr (kPairs)
+        sample_pairs(c, xs[i], ys[i], alpha[i], lv[at.x], true, h, Nv);
+      else
+        sample_corners(c, xs[i], ys[i], alpha[i], lv[at.x], true, h, nH, Nv, row_bytes);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         // skipped corners keep their offset past every image
@@ -164,6 +208,56 @@ __device__ inline void gather_rows(const uint2* __restrict__ rows, int R, __amdg
       }
     }
   }
+}
+
+// The head-pair layout's gather: R staged slots (a multiple of 2 * kBatch)
+// hold R / 2 corner pairs (A, B).  Lanes j < 4 read corner A's channels
+// 8j..8j+7, lanes j >= 4 corner B's channels 8(7-j)..8(7-j)+7, 16 bytes
+// each, so that one wave-wide load fetches both corners of a pair for 8
+// heads, mostly from one 128-byte line per head.  Lanes j and 7 - j
+// accumulate the same 8 channels (from the two corners); pair_total() adds
+// them up.
+__device__ inline void gather_pairs(const uint2* __restrict__ rows, int R, __amdgpu_buffer_rsrc_t img, int j,
+                                    float (&acc)[8]) {
+  const bool left = j < 4;
+  const uint32_t lane_off = (uint32_t)(left ? j : 7 - j) * 16u;
+  const int half = left ? 0 : 1;
+#pragma nounroll
+  for (int r = 0; r < R; r += 2 * kBatch) {
+    uint2 m[kBatch];
+    uint32_t d[kBatch][4];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) m[u] = rows[r + 2 * u + half];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const auto raw = __builtin_amdgcn_raw_buffer_load_b128(img, m[u].x + lane_off, 0, 0);
+      d[u][0] = raw[0];
+      d[u][1] = raw[1];
+      d[u][2] = raw[2];
+      d[u][3] = raw[3];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = __uint_as_float(m[u].y);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] = fmaf(w, __uint_as_float(d[u][k] << 16), acc[2 * k]);
+        acc[2 * k + 1] = fmaf(w, __uint_as_float(d[u][k] & 0xffff0000u), acc[2 * k + 1]);
+      }
+    }
+  }
+}
+
+// Sum of lanes j and 7 - j (the two corners' shares of the same channels),
+// in both; returns this lane's 4 output channels and their float4 index in
+// the head's row: lane j < 4 channels 8j..8j+3, lane j >= 4 channels
+// 8(7-j)+4..8(7-j)+7.
+__device__ inline float4 pair_total(float (&acc)[8], int j, int& at) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] += dpp<kDppHalfMirror>(acc[k]);
+  const bool left = j < 4;
+  at = left ? 2 * j : 2 * (7 - j) + 1;
+  return left ? make_float4(acc[0], acc[1], acc[2], acc[3]) : make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 // v / n: a multiplication by the exact reciprocal when n is a power of two
@@ -436,7 +530,8 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
 // For L*P <= 32 the kernel is held to 128 VGPRs, 4 waves per SIMD (the LDS
 // allows 4): the fp32 variant then spills a few registers outside its load
 // loop and still measures about 2% faster than at 133 VGPRs and 3 waves.
-template <bool kBF16, int kSPL>
+// kPairs: bf16 value in the head-pair layout (sample_pairs, gather_pairs).
+template <bool kBF16, int kSPL, bool kPairs>
 __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void sca_gather_kernel(GatherArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Level* lv = reinterpret_cast<Level*>(smem);
@@ -445,7 +540,7 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void s
   const int lane = threadIdx.x % kWave, wave = uniform((int)(threadIdx.x / kWave));
   const int g = lane / 8, j = lane % 8;
   uint2* rows = reinterpret_cast<uint2*>(smem + sizeof(Level) * kMaxLevels) +
-                ((size_t)wave * kHeadSlots + g) * meta_stride(a.LP);
+                ((size_t)wave * kHeadSlots + g) * meta_stride(a.LP, kPairs);
   const uint32_t row_bytes = kBF16 ? 64u : 128u;
   const int64_t n_queries = a.B * a.Nq;
   const uint32_t cam_bits = a.Ncam >= 32 ? 0xffffffffu : ((1u << a.Ncam) - 1u);
@@ -479,6 +574,7 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void s
         off[i] = (head_ok && k < a.LP) ? off_row[k] : make_float2(0.f, 0.f);
       }
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // head-pair layout
       for (uint32_t rest = seen; rest != 0u; rest &= rest - 1u) {
         const int c = __builtin_ctz(rest);
         const float2* rho = reinterpret_cast<const float2*>(a.rp) + ((c * a.B + b) * a.Nq + q) * a.D;
@@ -497,16 +593,21 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void s
           if (valid && sample_live(xs[i], ys[i], L)) live |= 1u << i;
         }
         const float inv_P = a.inv_P;
-        const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv,
-                                       [&](int i) { return make_int2(small_div(j + 8 * i, inv_P), 0); }, j, h, a.nH,
-                                       a.Nv, row_bytes);
+        auto level_of = [&](int i) { return make_int2(small_div(j + 8 * i, inv_P), 0); };
+        const int R = stage_rows<kSPL, decltype(level_of), kPairs>(rows, xs, ys, alpha, live, lv, level_of, j, h,
+                                                                     a.nH, a.Nv, row_bytes);
         wave_lds_sync();
         const auto img = make_rsrc(static_cast<const char*>(a.value) + (b * a.Ncam + c) * (int64_t)a.image_bytes,
                                    a.image_bytes);
-        gather_rows<kBF16>(rows, R, img, j, acc);
+        if constexpr (kPairs)
+          gather_pairs(rows, R, img, j, acc8);
+        else
+          gather_rows<kBF16>(rows, R, img, j, acc);
         wave_lds_sync();
       }
-      if (head_ok) reinterpret_cast<float4*>(a.out + ((bq * a.nH + h) * 32))[j] = scaled(acc, __popc(seen));
+      int at = j;
+      if constexpr (kPairs) acc = pair_total(acc8, j, at);
+      if (head_ok) reinterpret_cast<float4*>(a.out + ((bq * a.nH + h) * 32))[at] = scaled(acc, __popc(seen));
     }
   }
   }
@@ -525,15 +626,15 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void s
 // launchers
 // ---------------------------------------------------------------------------
 
-static size_t smem_bytes(int LP, int waves) {
-  return sizeof(Level) * kMaxLevels + sizeof(uint2) * (size_t)waves * kHeadSlots * meta_stride(LP);
+static size_t smem_bytes(int LP, int waves, bool pairs = false) {
+  return sizeof(Level) * kMaxLevels + sizeof(uint2) * (size_t)waves * kHeadSlots * meta_stride(LP, pairs);
 }
 
 // Waves per block: as many as fit the 64 KB block LDS budget (4, or 2 for
 // L*P above 32).
-static int block_waves(int LP) {
+static int block_waves(int LP, bool pairs = false) {
   int w = kMaxWavesPerBlock;
-  while (w > 1 && smem_bytes(LP, w) > kMaxBlockLds) w /= 2;
+  while (w > 1 && smem_bytes(LP, w, pairs) > kMaxBlockLds) w /= 2;
   return w;
 }
 
@@ -609,14 +710,25 @@ hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_sca_gather(const GatherArgs& a, hipStream_t stream) {
-  const int waves = block_waves(a.LP);
-  const size_t smem = smem_bytes(a.LP, waves);
+template <int kSPL>
+static void launch_sca_spl(const GatherArgs& a, int waves, size_t smem, hipStream_t stream) {
   const int64_t n = a.B * a.Nq;
-  if (a.LP <= 32)
-    launch(a.bf16 ? sca_gather_kernel<true, 4> : sca_gather_kernel<false, 4>, n, waves, smem, true, a, stream);
+  if (a.pairs)
+    launch(sca_gather_kernel<true, kSPL, true>, n, waves, smem, true, a, stream);
+  else if (a.bf16)
+    launch(sca_gather_kernel<true, kSPL, false>, n, waves, smem, true, a, stream);
   else
-    launch(a.bf16 ? sca_gather_kernel<true, 8> : sca_gather_kernel<false, 8>, n, waves, smem, true, a, stream);
+    launch(sca_gather_kernel<false, kSPL, false>, n, waves, smem, true, a, stream);
+}
+
+hipError_t launch_sca_gather(const GatherArgs& a, hipStream_t stream) {
+  const bool pairs = a.pairs != 0;
+  const int waves = block_waves(a.LP, pairs);
+  const size_t smem = smem_bytes(a.LP, waves, pairs);
+  if (a.LP <= 32)
+    launch_sca_spl<4>(a, waves, smem, stream);
+  else
+    launch_sca_spl<8>(a, waves, smem, stream);
   return hipGetLastError();
 }
 

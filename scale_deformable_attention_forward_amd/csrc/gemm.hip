@@ -215,9 +215,41 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int kOutChunks = kBM * kRowChunks / kGemmThreads;
   constexpr int kColsPerChunk = 16 / ysz;
   __shared__ __align__(16) char ys[kBM * kYPitch];
+  // Head-pair layout (msda_value_proj_pairs_bf16): row m = pixel pix of
+  // image m / Nv, columns h*32 .. h*32+31 = head h.  Its 16-byte chunk o of
+  // head h goes to the left half of line (h, pix) and to the right half of
+  // line (h, pix - 1); the right half of the image's last line is zeroed.
+  // Lanes take consecutive rows of one head, so that a wave's two stores
+  // cover whole consecutive lines.
+  auto store_pairs = [&](int64_t m0) {
+    const int64_t Nv = a.pairs_Nv;
+    const int64_t image_bytes = Nv * (a.N / 32) * 128;
+    char* Y = static_cast<char*>(a.Y1);
+#pragma unroll
+    for (int i = 0; i < kOutChunks; ++i) {
+      const int e = threadIdx.x + i * kGemmThreads;
+      const int o = e % 4, r = (e / 4) % kBM, hb = e / (4 * kBM);  // head within the block's 8
+      const int64_t m = m0 + r;
+      const int h = blockIdx.y * (kBN / 32) + hb;
+      if (m >= a.M || h * 32 >= a.N) continue;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ys + r * kYPitch + (hb * 4 + o) * 16);
+      const uint32_t img = (uint32_t)m / (uint32_t)Nv;  // m < 2^31
+      const int64_t pix = m - (int64_t)img * Nv;
+      char* line = Y + img * image_bytes + ((int64_t)h * Nv + pix) * 128 + o * 16;
+      *reinterpret_cast<u32x4_t*>(line) = v;
+      if (pix > 0) *reinterpret_cast<u32x4_t*>(line - 64) = v;
+      if (pix == Nv - 1) *reinterpret_cast<u32x4_t*>(line + 64) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
   const bool straddles = blockIdx.y * kBN < a.N1 && (blockIdx.y + 1) * kBN > a.N1;  // uniform
   const bool all2 = blockIdx.y * kBN >= a.N1;  // uniform
   auto store_tile = [&](int64_t m0) {
+    if constexpr (!kYF32) {
+      if (a.pairs_Nv > 0) {  // uniform: the head-pair layout (single output, bf16)
+        store_pairs(m0);
+        return;
+      }
+    }
     const auto r1 = tile_rsrc(a.Y1, m0, a.M, kBM, (int64_t)a.N1 * ysz);
     const auto r2 = tile_rsrc(a.Y2, m0, a.M, kBM, (int64_t)(a.N - a.N1) * ysz);
 #pragma unroll

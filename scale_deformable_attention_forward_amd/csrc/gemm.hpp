@@ -29,6 +29,9 @@ struct GemmArgs {
   const float* gamma;
   const float* beta;
   float eps;
+  // > 0: Y1 is bf16 in the head-pair layout of images of pairs_Nv rows
+  // ([M / pairs_Nv][N / 32][pairs_Nv][2][32]); single output, no epilogue
+  int64_t pairs_Nv;
 };
 
 constexpr int kGemmNormCols = 256;  // row length the layer-norm epilogue handles

@@ -16,6 +16,7 @@ struct GatherArgs {
   const void* value;
   uint32_t image_bytes;
   int bf16;
+  int pairs;  // bf16 in the head-pair layout (SCA only): per image [nH][Nv][2][32]
   // level table (device, int64) and sizes
   const int64_t* shapes;
   const int64_t* starts;
@@ -44,6 +45,11 @@ struct GatherArgs {
 };
 
 hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream);
+
+// msda_pack_pairs_bf16 (pairs.hip): bf16 value [n_images][Nv][nH][32] to the
+// head-pair layout [n_images][nH][Nv][2][32]
+hipError_t launch_pack_pairs(const void* value, void* pairs, int64_t n_images, int64_t Nv, int nH,
+                             hipStream_t stream);
 
 // Locality plan of the operator (plan.hip): point of query (b, q) at
 // points[b*batch_stride + q*point_stride] (x, y normalised); the plan buffer

@@ -107,6 +107,7 @@ def _msda(lib, value=A, dtype=0, shapes=A, starts=A, loc=A, w=A, mode=1, B=1, Nv
     (dict(loc=A + 4), INVALID),
     (dict(Nv=1 << 31), UNSUPPORTED),
     (dict(Nv=1 << 21, nH=8), UNSUPPORTED),  # 2^21 * 8 * 32 * 4 bytes = 2 GiB per image
+    (dict(dtype=2), INVALID),  # the head-pair layout is for the SCA forward entry points only
 ])
 def test_msda_forward_rejects(lib, kw, code):
     assert _msda(lib, **kw) == code
@@ -157,7 +158,8 @@ def _sca(lib, value=A, dtype=0, B=1, Ncam=6, Nv=16, Nq=8, nH=8, Dh=32, L=1, P=8,
     (dict(ws=A + 16), WORKSPACE),
     (dict(rp=A + 4), INVALID),
     (dict(Dh=64), UNSUPPORTED),
-    (dict(dtype=2), INVALID),
+    (dict(dtype=3), INVALID),
+    (dict(dtype=2, Nv=1 << 21, nH=8), UNSUPPORTED),  # head-pair layout: 2^21 * 8 * 128 bytes = 2 GiB per image
 ])
 def test_sca_forward_rejects(lib, kw, code):
     assert _sca(lib, **kw) == code
@@ -194,6 +196,56 @@ def test_sca_stages_reject(lib):
 ])
 def test_gemm_rejects(lib, M, N, K, code):
     assert lib.msda_gemm_bf16(A, 1, A, None, B_, 1, M, N, K, None) == code
+
+
+def _vp(lib, X=A, dt=1, W=A, bias=None, Y=B_, M=64, N=256, K=256, Nv=16):
+    return lib.msda_value_proj_pairs_bf16(X, dt, W, bias, Y, M, N, K, Nv, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), INVALID),
+    (dict(W=None), INVALID),
+    (dict(Y=None), INVALID),
+    (dict(dt=2), INVALID),
+    (dict(N=48), UNSUPPORTED),  # a multiple of 16, not of 32: heads are 32 channels
+    (dict(K=48), UNSUPPORTED),
+    (dict(Nv=0), INVALID),
+    (dict(M=60), SHAPE),  # not a whole number of 16-row images
+    (dict(M=1 << 21, Nv=1 << 21), UNSUPPORTED),  # 2^21 * 8 * 128 bytes = 2 GiB per image
+    (dict(Y=MIS), INVALID),
+    (dict(Y=A + 0x4000), INVALID),  # overlaps X
+    (dict(M=0), OK),
+])
+def test_value_proj_pairs_rejects(lib, kw, code):
+    assert _vp(lib, **kw) == code
+
+
+def _pk(lib, v=A, p=B_, n=2, Nv=16, nH=8):
+    return lib.msda_pack_pairs_bf16(v, p, n, Nv, nH, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=None), INVALID),
+    (dict(p=None), INVALID),
+    (dict(n=-1), INVALID),
+    (dict(Nv=0), INVALID),
+    (dict(nH=0), INVALID),
+    (dict(nH=65), UNSUPPORTED),
+    (dict(Nv=1 << 21), UNSUPPORTED),  # 2^21 * 8 * 128 bytes = 2 GiB per image
+    (dict(v=MIS), INVALID),
+    (dict(p=A + 0x2000), INVALID),  # overlaps value
+    (dict(n=0), OK),
+    (dict(n=0, v=None, p=None), OK),  # nothing to copy: empty tensors have null data
+])
+def test_pack_pairs_rejects(lib, kw, code):
+    assert _pk(lib, **kw) == code
+
+
+def test_pairs_layout_is_for_the_sca_forward_only(lib):
+    """MSDA_BF16_PAIRS is refused by the operator and the backward passes
+    before anything is read."""
+    assert lib.msda_forward_frames(A, 2, A, A, A, A, 1, 1, 2, 16, 4, 8, 32, 1, 4, B_, None) == INVALID
+    assert _mb(lib, dtype=2) == INVALID
 
 
 def test_gemm_rejects_null_and_dtype(lib):
