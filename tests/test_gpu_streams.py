@@ -16,6 +16,7 @@ import torch
 
 import workloads as W
 from gpu_util import announce, dev, host
+from test_gpu_pairs import pairs_host
 from test_gpu_parity import _rand_msda, _rand_sca
 
 pytestmark = pytest.mark.gpu
@@ -151,6 +152,25 @@ def _sca_rebatch(t, stream):
     return slots
 
 
+def _pairs_inputs():
+    t = _sca_inputs()
+    t["value_bits"] = W.bf16_bits_trunc(t["value"])
+    t["pairs"] = pairs_host(t["value_bits"])
+    return t
+
+
+def _pack_pairs(t, stream):
+    return msda.msda_pack_pairs_bf16(t["value_bits"], stream=stream)
+
+
+def _sca_forward_pairs(t, stream):
+    return _sca_forward({**t, "value": t["pairs"]}, stream)
+
+
+def _value_proj_pairs(t, stream):
+    return msda.msda_value_proj_pairs_bf16(t["x"], t["w"], t["bias"], 100, stream=stream)  # 10 images of 100 rows
+
+
 def _gemm(t, stream):
     return (msda.msda_gemm_bf16(t["x"], t["w"], t["bias"], stream=stream),
             msda.msda_gemm_bf16(t["x"], t["w"], None, y_dtype=torch.float32, stream=stream))
@@ -179,6 +199,9 @@ CASES = [
     ("sca_backward", _sca_inputs, _sca_backward),
     ("sca_forward_rebatch", _sca_inputs, _sca_rebatch),
     ("msda_gemm_bf16", _proj_inputs, _gemm),
+    ("msda_value_proj_pairs_bf16", _proj_inputs, _value_proj_pairs),
+    ("msda_pack_pairs_bf16", _pairs_inputs, _pack_pairs),
+    ("sca_forward_head_pairs", _pairs_inputs, _sca_forward_pairs),
     ("msda_query_proj_bf16", _proj_inputs, _query_proj),
     ("msda_output_proj_bf16", _proj_inputs, _output_proj),
 ]
