@@ -115,8 +115,8 @@ __device__ inline void sample_pairs(uint2 (&c)[4], double x, double y, float alp
 }
 
 // Write the four corner rows of the group's live samples densely into `rows`
-// (lane order, then sample order; a prefix sum over the group's 8 lanes
-// places each lane) and pad every group of the wave with skipped rows up to
+// (sample order, then lane order: a ballot per sample places each lane) and
+// pad every group of the wave with skipped rows up to
 // the wave's largest count rounded up to kBatch.  Returns that row count
 // (the same in every lane).  Dead samples cost no row at all.  where(i)
 // gives sample i's level index and the byte offset of its image within the
@@ -127,23 +127,31 @@ template <int kSPL, typename Where, bool kPairs = false>
 __device__ inline int stage_rows(uint2* __restrict__ rows, const double (&xs)[kSPL], const double (&ys)[kSPL],
                                  const float (&alpha)[kSPL], uint32_t live, const Level* lv, Where where, int j,
                                  int h, int nH, int Nv, uint32_t row_bytes) {
-  const int n = 4 * __popc(live);
-  int incl = n;
+  // per sample, the group's lanes that hold it live
+  const int gbase = (int)(threadIdx.x % kWave) & ~7;  // the group's first lane
+  uint32_t group_live[kSPL];
+  int group_total = 0;
 #pragma unroll
-  for (int d = 1; d < 8; d <<= 1) {
-    const int v = __shfl_up(incl, d, 8);
-    if (j >= d) incl += v;
+  for (int i = 0; i < kSPL; ++i) {
+    group_live[i] = (uint32_t)(__ballot((live >> i) & 1u) >> gbase) & 0xffu;
+    group_total += 4 * __popc(group_live[i]);
   }
-  const int group_total = __shfl(incl, 7, 8);
   int wave_max = group_total;
   wave_max = max(wave_max, __shfl_xor(wave_max, 8));
   wave_max = max(wave_max, __shfl_xor(wave_max, 16));
   wave_max = max(wave_max, __shfl_xor(wave_max, 32));
   constexpr int q = kPairs ? 2 * kBatch : kBatch;
   const int R = (wave_max + q - 1) / q * q;
-  int pos = incl - n;
+  // rows in sample order, then lane order: all lanes' live sample 0, then
+  // sample 1, ... (for the SCA's and the DETR encoder's L*P = 32 and 16,
+  // level by level).  With the group totals from the same ballots instead
+  // of a shuffle prefix sum: 4% faster than lane order on the DETR encoder
+  // and on the batch-4 SCA with a head-pair value, the same elsewhere.
+  int base = 0;
 #pragma unroll
   for (int i = 0; i < kSPL; ++i) {
+    const int pos = base + 4 * __popc(group_live[i] & ((1u << j) - 1u));
+    base += 4 * __popc(group_live[i]);
     if ((live >> i) & 1u) {
       const int2 at = where(i);
       uint2 c[4];
@@ -157,7 +165,6 @@ __device__ inline int stage_rows(uint2* __restrict__ rows, const double (&xs)[kS
         if (c[t].x != kSkip) c[t].x += (uint32_t)at.y;
         rows[pos + t] = c[t];
       }
-      pos += 4;
     }
   }
   for (int r = group_total + j; r < R; r += 8) rows[r] = make_uint2(kSkip, 0u);
