@@ -80,14 +80,14 @@ extern "C" {
 /* element types */
 #define MSDA_F32 0  /* IEEE binary32 */
 #define MSDA_BF16 1 /* bfloat16 (upper half of a binary32), stored as uint16 */
-/* bfloat16 value of the SCA entry points in the head-pair layout: per value
- * image [nH][Nv][2][Dh] with Dh == 32, element [h][p][s][d] = channel d of
+/* bfloat16 value of the forward entry points in the head-pair layout: per
+ * value image [nH][Nv][2][Dh] with Dh == 32, element [h][p][s][d] = channel d of
  * head h at flattened pixel p + s (s = 0, 1).  Each 128-byte line (h, p) thus
  * holds pixel p and its right-hand neighbour p + 1, the two corners a
  * bilinear sample reads in one row of a level, so that the gather fetches
  * both from one cache line.  [h][Nv-1][1] is never read (msda_pack_pairs_bf16
  * and msda_value_proj_pairs_bf16 write zeros there).  Twice the bytes of
- * MSDA_BF16 (as many as MSDA_F32). */
+ * MSDA_BF16 (as many as MSDA_F32).  The backward entry points refuse it. */
 #define MSDA_BF16_PAIRS 2
 
 /* meaning of attention_weights */
@@ -100,7 +100,8 @@ extern "C" {
  * 6 bilinear sampling at x = W_l*s_x - 1/2, y = H_l*s_y - 1/2, 8 weighted sum
  * over levels and points, 9 concatenation of heads).
  *
- *   value               device [B][Nv][nH][Dh], MSDA_F32 or MSDA_BF16, 16-byte aligned
+ *   value               device [B][Nv][nH][Dh], MSDA_F32 or MSDA_BF16, or [B][nH][Nv][2][Dh]
+ *                       in MSDA_BF16_PAIRS; 16-byte aligned
  *   spatial_shapes      device int64 [L][2], (H_l, W_l)
  *   level_start_index   device int64 [L]
  *   sampling_locations  device float [B][Nq][nH][L][P][2], normalised (x, y), 8-byte aligned
@@ -124,7 +125,7 @@ int msda_forward(const void* value, int value_dtype, const int64_t* spatial_shap
  * the operator ([8-heads] 18.5); the frame mean is this library's reading of
  * the two-map workload.
  *
- *   value               device [B][F][Nv][nH][Dh]
+ *   value               device [B][F][Nv][nH][Dh] (MSDA_BF16_PAIRS: [B][F][nH][Nv][2][Dh])
  *   sampling_locations  device float [B][F][Nq][nH][L][P][2]
  *   attention_weights   device float [B][F][Nq][nH][L*P]
  *   out                 device float [B][Nq][nH*Dh] = (1/F) * sum over f of MSDA(frame f)
@@ -288,8 +289,8 @@ int msda_gemm_bf16(const void* X, int x_dtype, const uint16_t* W, const float* b
 
 /*
  * The value projection of msda_gemm_bf16 ([8-heads] 3) with its bf16 output
- * written in the head-pair layout (MSDA_BF16_PAIRS) for sca_forward and
- * sca_gather: the M = n_images * Nv rows of X are the pixels of n_images
+ * written in the head-pair layout (MSDA_BF16_PAIRS) for the forward entry
+ * points: the M = n_images * Nv rows of X are the pixels of n_images
  * value images of Nv pixels each, and the N = nH * 32 columns head h's
  * channels h*32 .. h*32+31.  Each output row is stored twice, as the left
  * half of its own line and the right half of its left-hand neighbour's

@@ -171,6 +171,25 @@ def _value_dtype(value):
     raise TypeError(f"value must be float32 or bfloat16, got {value.dtype}")
 
 
+def _op_value(value, frames):
+    """(B, F, Nv, nH, Dh, value_dtype) of the operator's value: [B,Nv,nH,Dh]
+    (frames: [B,F,Nv,nH,Dh]) float32 or bfloat16, or bfloat16 in the
+    head-pair layout [B,nH,Nv,2,Dh] ([B,F,nH,Nv,2,Dh]), MSDA_BF16_PAIRS."""
+    plain = 5 if frames else 4
+    if value.dim() == plain + 1:
+        if value.dtype != torch.bfloat16 or value.shape[-2] != 2:
+            raise TypeError(f"a {plain + 1}-dimensional value is the bfloat16 head-pair layout "
+                            f"[B,{'F,' if frames else ''}nH,Nv,2,Dh]; got {value.dtype} {tuple(value.shape)}")
+        B, F = value.shape[0], (value.shape[1] if frames else 1)
+        nH, Nv, _, Dh = value.shape[-4:]
+        return B, F, Nv, nH, Dh, MSDA_BF16_PAIRS
+    if value.dim() != plain:
+        raise ValueError(f"value: {plain} dimensions expected, got shape {tuple(value.shape)}")
+    B, F = value.shape[0], (value.shape[1] if frames else 1)
+    Nv, nH, Dh = value.shape[-3:]
+    return B, F, Nv, nH, Dh, _value_dtype(value)
+
+
 def _sca_value(value):
     """(B, Ncam, Nv, nH, Dh, value_dtype) of an SCA value: [B,Ncam,Nv,nH,Dh]
     float32 or bfloat16, or bfloat16 [B,Ncam,nH,Nv,2,Dh] in the head-pair
@@ -217,11 +236,12 @@ _F32 = (torch.float32,)
 @_given_stream
 def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
                  weight_mode=MSDA_WEIGHTS_LOGITS, out=None, stream=None):
-    """value [B,Nv,nH,Dh] (float32|bfloat16); spatial_shapes int64 [L,2] (H,W);
-    level_start_index int64 [L]; sampling_locations float32 [B,Nq,nH,L,P,2];
-    attention_weights float32 [B,Nq,nH,L*P].  Returns out float32 [B,Nq,nH*Dh]."""
+    """value [B,Nv,nH,Dh] (float32|bfloat16, or bfloat16 [B,nH,Nv,2,Dh] in the
+    head-pair layout); spatial_shapes int64 [L,2] (H,W); level_start_index
+    int64 [L]; sampling_locations float32 [B,Nq,nH,L,P,2]; attention_weights
+    float32 [B,Nq,nH,L*P].  Returns out float32 [B,Nq,nH*Dh]."""
     lib = load_library()
-    B, Nv, nH, Dh = value.shape
+    B, _, Nv, nH, Dh, vdt = _op_value(value, False)
     _, Nq, _, L, P, _ = sampling_locations.shape
     _levels(spatial_shapes, level_start_index, L)
     _numel(sampling_locations, "sampling_locations", B * Nq * nH * L * P * 2)
@@ -229,7 +249,7 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, a
     _numel(out, "out", B * Nq * nH * Dh, at_least=True)
     if out is None:
         out = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=value.device)
-    rc = lib.msda_forward(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
+    rc = lib.msda_forward(_ptr(value, "value"), vdt, _ptr(spatial_shapes, "spatial_shapes", _I64),
                           _ptr(level_start_index, "level_start_index", _I64),
                           _ptr(sampling_locations, "sampling_locations", _F32),
                           _ptr(attention_weights, "attention_weights", _F32), int(weight_mode), B, Nv, Nq, nH, Dh,
@@ -241,11 +261,11 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, a
 @_given_stream
 def msda_forward_frames(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
                         weight_mode=MSDA_WEIGHTS_LOGITS, out=None, stream=None):
-    """value [B,F,Nv,nH,Dh]; sampling_locations [B,F,Nq,nH,L,P,2];
-    attention_weights [B,F,Nq,nH,L*P].  Returns the frame mean, float32
-    [B,Nq,nH*Dh]."""
+    """value [B,F,Nv,nH,Dh] (or bfloat16 [B,F,nH,Nv,2,Dh] in the head-pair
+    layout); sampling_locations [B,F,Nq,nH,L,P,2]; attention_weights
+    [B,F,Nq,nH,L*P].  Returns the frame mean, float32 [B,Nq,nH*Dh]."""
     lib = load_library()
-    B, F, Nv, nH, Dh = value.shape
+    B, F, Nv, nH, Dh, vdt = _op_value(value, True)
     _, _, Nq, _, L, P, _ = sampling_locations.shape
     _levels(spatial_shapes, level_start_index, L)
     _numel(sampling_locations, "sampling_locations", B * F * Nq * nH * L * P * 2)
@@ -253,7 +273,7 @@ def msda_forward_frames(value, spatial_shapes, level_start_index, sampling_locat
     _numel(out, "out", B * Nq * nH * Dh, at_least=True)
     if out is None:
         out = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=value.device)
-    rc = lib.msda_forward_frames(_ptr(value, "value"), _value_dtype(value),
+    rc = lib.msda_forward_frames(_ptr(value, "value"), vdt,
                                  _ptr(spatial_shapes, "spatial_shapes", _I64),
                                  _ptr(level_start_index, "level_start_index", _I64),
                                  _ptr(sampling_locations, "sampling_locations", _F32),
@@ -298,25 +318,24 @@ def plan_order(plan, B, Nq):
 @_given_stream
 def msda_gather(value, spatial_shapes, level_start_index, sampling_locations, attention_weights, plan,
                 weight_mode=MSDA_WEIGHTS_LOGITS, out=None, stream=None):
-    """msda_forward (value [B,Nv,nH,Dh]) or msda_forward_frames (value
-    [B,F,Nv,nH,Dh], locations [B,F,Nq,..]) visiting the queries in the order
-    of the plan buffer msda_plan filled for the same B and Nq.  Same result,
-    bit for bit.  Returns out float32 [B,Nq,nH*Dh]."""
+    """msda_forward (locations [B,Nq,..]) or msda_forward_frames (locations
+    [B,F,Nq,..]), with the value as they take it, visiting the queries in the
+    order of the plan buffer msda_plan filled for the same B and Nq.  Same
+    result, bit for bit.  Returns out float32 [B,Nq,nH*Dh]."""
     lib = load_library()
-    if value.dim() == 4:
-        B, Nv, nH, Dh = value.shape
-        F = 1
-        _, Nq, _, L, P, _ = sampling_locations.shape
-    else:
-        B, F, Nv, nH, Dh = value.shape
+    frames = sampling_locations.dim() == 7
+    B, F, Nv, nH, Dh, vdt = _op_value(value, frames)
+    if frames:
         _, _, Nq, _, L, P, _ = sampling_locations.shape
+    else:
+        _, Nq, _, L, P, _ = sampling_locations.shape
     _levels(spatial_shapes, level_start_index, L)
     _numel(sampling_locations, "sampling_locations", B * F * Nq * nH * L * P * 2)
     _numel(attention_weights, "attention_weights", B * F * Nq * nH * L * P)
     _numel(out, "out", B * Nq * nH * Dh, at_least=True)
     if out is None:
         out = torch.empty((B, Nq, nH * Dh), dtype=torch.float32, device=value.device)
-    rc = lib.msda_gather(_ptr(value, "value"), _value_dtype(value), _ptr(spatial_shapes, "spatial_shapes", _I64),
+    rc = lib.msda_gather(_ptr(value, "value"), vdt, _ptr(spatial_shapes, "spatial_shapes", _I64),
                          _ptr(level_start_index, "level_start_index", _I64),
                          _ptr(sampling_locations, "sampling_locations", _F32),
                          _ptr(attention_weights, "attention_weights", _F32), int(weight_mode), B, F, Nv, Nq, nH, Dh,

@@ -47,15 +47,14 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 constexpr int64_t kI31 = (int64_t)1 << 31;
 
 // Checks shared by the MSDA-style entry points; pairs_ok: the entry point
-// takes MSDA_BF16_PAIRS (the SCA forward ones).
+// takes MSDA_BF16_PAIRS (the forward ones).
 int check_common(const void* value, int value_dtype, const int64_t* shapes, const int64_t* starts, int64_t Nv,
                  int64_t Nq, int nH, int Dh, int L, int P, const void* out, uint32_t* image_bytes,
                  bool pairs_ok = false) {
   // with no queries nothing per query is read or written: those buffers may be null
   if (!value || !shapes || !starts || (!out && Nq != 0)) return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
   if (value_dtype == MSDA_BF16_PAIRS && !pairs_ok)
-    return fail(MSDA_ERR_INVALID_ARG, "MSDA_BF16_PAIRS is taken by sca_forward, sca_gather and "
-                "sca_forward_noalloc only");
+    return fail(MSDA_ERR_INVALID_ARG, "MSDA_BF16_PAIRS is taken by the forward entry points only");
   if (value_dtype != MSDA_F32 && value_dtype != MSDA_BF16 && value_dtype != MSDA_BF16_PAIRS)
     return fail(MSDA_ERR_INVALID_ARG, "value_dtype %d is not MSDA_F32, MSDA_BF16 or MSDA_BF16_PAIRS", value_dtype);
   if (Nv < 1 || Nq < 0 || nH < 1 || Dh < 1 || L < 1 || P < 1)
@@ -120,7 +119,7 @@ static int msda_frames_impl(const void* value, int value_dtype, const int64_t* s
                             void* stream) {
   uint32_t image_bytes = 0;
   int rc = check_common(value, value_dtype, spatial_shapes, level_start_index, Nv, Nq, nH, Dh, L, P, out,
-                        &image_bytes);
+                        &image_bytes, true);
   if (rc != MSDA_OK) return rc;
   if ((!sampling_locations || !attention_weights) && Nq != 0)
     return fail(MSDA_ERR_INVALID_ARG, "null pointer argument");
@@ -136,7 +135,8 @@ static int msda_frames_impl(const void* value, int value_dtype, const int64_t* s
   msda::GatherArgs a = {};
   a.value = value;
   a.image_bytes = image_bytes;
-  a.bf16 = value_dtype == MSDA_BF16;
+  a.bf16 = value_dtype != MSDA_F32;
+  a.pairs = value_dtype == MSDA_BF16_PAIRS;
   a.shapes = spatial_shapes;
   a.starts = level_start_index;
   a.L = L;

@@ -406,8 +406,9 @@ __device__ inline void flat_weights(const FlatUnit<kSPL>& u, const int (&fr)[kSP
 // in one pass through one buffer descriptor spanning the batch item's F
 // images (needs F*L*P <= 8*kSPL and F images under 2^31 bytes); the wave
 // loads the next unit's inputs before it stages and gathers the current
-// one.  Otherwise frame by frame.
-template <bool kBF16, int kSPL, bool kFlat>
+// one.  Otherwise frame by frame.  kPairs: bf16 value in the head-pair
+// layout, as in the SCA kernel.
+template <bool kBF16, int kSPL, bool kFlat, bool kPairs>
 __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(GatherArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Level* lv = reinterpret_cast<Level*>(smem);
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
   const int lane = threadIdx.x % kWave, wave = uniform((int)(threadIdx.x / kWave));
   const int g = lane / 8, j = lane % 8;
   uint2* rows = reinterpret_cast<uint2*>(smem + sizeof(Level) * kMaxLevels) +
-                ((size_t)wave * kHeadSlots + g) * meta_stride(kFlat ? a.F * a.LP : a.LP);
+                ((size_t)wave * kHeadSlots + g) * meta_stride(kFlat ? a.F * a.LP : a.LP, kPairs);
   const uint32_t row_bytes = kBF16 ? 64u : 128u;
   MsdaWalk walk(a, waves_per_block);
 
@@ -465,20 +466,27 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
       const int LP = a.LP;
       const float inv_LP = a.inv_LP, inv_P = a.inv_P;
       const uint32_t image_bytes = a.image_bytes;
-      const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv,
-                                     [&](int i) {
-                                       const int t = j + 8 * i;
-                                       const int f = small_div(t, inv_LP);
-                                       return make_int2(small_div(t - f * LP, inv_P), (int)(f * image_bytes));
-                                     },
-                                     j, h, a.nH, a.Nv, row_bytes);
+      auto where = [&](int i) {
+        const int t = j + 8 * i;
+        const int f = small_div(t, inv_LP);
+        return make_int2(small_div(t - f * LP, inv_P), (int)(f * image_bytes));
+      };
+      const int R = stage_rows<kSPL, decltype(where), kPairs>(rows, xs, ys, alpha, live, lv, where, j, h, a.nH,
+                                                                a.Nv, row_bytes);
       wave_lds_sync();
       const auto img = make_rsrc(static_cast<const char*>(a.value) + b * a.F * (int64_t)a.image_bytes,
                                  (uint32_t)(a.F * (int64_t)a.image_bytes));
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      gather_rows<kBF16>(rows, R, img, j, acc);
+      int at = j;
+      if constexpr (kPairs) {
+        float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        gather_pairs(rows, R, img, j, acc8);
+        acc = pair_total(acc8, j, at);
+      } else {
+        gather_rows<kBF16>(rows, R, img, j, acc);
+      }
       wave_lds_sync();
-      if (h < a.nH) reinterpret_cast<float4*>(a.out + ((item * a.nH + h) * 32))[j] = scaled(acc, a.F);
+      if (h < a.nH) reinterpret_cast<float4*>(a.out + ((item * a.nH + h) * 32))[at] = scaled(acc, a.F);
       item = n_item;
       hb = n_hb;
       b = nb;
@@ -493,6 +501,7 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
         const int h = hb + g;
         const bool head_ok = h < a.nH;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // head-pair layout
         for (int f = 0; f < a.F; ++f) {
           const int64_t img_index = b * a.F + f;
           const int64_t src_row = (img_index * a.Nq + q) * a.nH + (head_ok ? h : 0);
@@ -512,16 +521,21 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
             if (valid && sample_live(xs[i], ys[i], L)) live |= 1u << i;
           }
           const float inv_P = a.inv_P;
-          const int R = stage_rows<kSPL>(rows, xs, ys, alpha, live, lv,
-                                         [&](int i) { return make_int2(small_div(j + 8 * i, inv_P), 0); }, j, h,
-                                         a.nH, a.Nv, row_bytes);
+          auto where = [&](int i) { return make_int2(small_div(j + 8 * i, inv_P), 0); };
+          const int R = stage_rows<kSPL, decltype(where), kPairs>(rows, xs, ys, alpha, live, lv, where, j, h, a.nH,
+                                                                    a.Nv, row_bytes);
           wave_lds_sync();
           const auto img = make_rsrc(static_cast<const char*>(a.value) + img_index * (int64_t)a.image_bytes,
                                      a.image_bytes);
-          gather_rows<kBF16>(rows, R, img, j, acc);
+          if constexpr (kPairs)
+            gather_pairs(rows, R, img, j, acc8);
+          else
+            gather_rows<kBF16>(rows, R, img, j, acc);
           wave_lds_sync();
         }
-        if (head_ok) reinterpret_cast<float4*>(a.out + ((item * a.nH + h) * 32))[j] = scaled(acc, a.F);
+        int at = j;
+        if constexpr (kPairs) acc = pair_total(acc8, j, at);
+        if (head_ok) reinterpret_cast<float4*>(a.out + ((item * a.nH + h) * 32))[at] = scaled(acc, a.F);
       }
     }
   }
@@ -678,8 +692,12 @@ static void launch(Kernel kernel, int64_t n_items, int waves, size_t smem, bool 
 // The operator's kernel for kSPL samples per lane (8 * kSPL per head and pass).
 template <int kSPL, bool kFlat>
 static void launch_msda_spl(const GatherArgs& a, int waves, size_t smem, bool resident, hipStream_t stream) {
-  launch(a.bf16 ? msda_gather_kernel<true, kSPL, kFlat> : msda_gather_kernel<false, kSPL, kFlat>, a.B * a.Nq,
-         waves, smem, resident, a, stream);
+  if (a.pairs)
+    launch(msda_gather_kernel<true, kSPL, kFlat, true>, a.B * a.Nq, waves, smem, resident, a, stream);
+  else if (a.bf16)
+    launch(msda_gather_kernel<true, kSPL, kFlat, false>, a.B * a.Nq, waves, smem, resident, a, stream);
+  else
+    launch(msda_gather_kernel<false, kSPL, kFlat, false>, a.B * a.Nq, waves, smem, resident, a, stream);
 }
 
 template <bool kFlat>
@@ -702,8 +720,9 @@ hipError_t launch_msda_gather(const GatherArgs& a, hipStream_t stream) {
   // their images one buffer descriptor (offset kSkip must lie beyond them)
   const bool flat = (int64_t)a.F * a.LP <= 64 && (int64_t)a.F * a.image_bytes < (int64_t)kSkip;
   const int staged = flat ? a.F * a.LP : a.LP;
-  const int waves = block_waves(staged);
-  const size_t smem = smem_bytes(staged, waves);
+  const bool pairs = a.pairs != 0;
+  const int waves = block_waves(staged, pairs);
+  const size_t smem = smem_bytes(staged, waves, pairs);
   // all waves resident, so that they sweep the (planned or given) order of
   // the queries together: measured against 8 blocks per compute unit (late
   // blocks balancing the tail), 0.0748 against 0.0782 ms on the temporal

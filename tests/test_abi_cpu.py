@@ -107,7 +107,8 @@ def _msda(lib, value=A, dtype=0, shapes=A, starts=A, loc=A, w=A, mode=1, B=1, Nv
     (dict(loc=A + 4), INVALID),
     (dict(Nv=1 << 31), UNSUPPORTED),
     (dict(Nv=1 << 21, nH=8), UNSUPPORTED),  # 2^21 * 8 * 32 * 4 bytes = 2 GiB per image
-    (dict(dtype=2), INVALID),  # the head-pair layout is for the SCA forward entry points only
+    (dict(dtype=3), INVALID),
+    (dict(dtype=2, Nv=1 << 21, nH=8), UNSUPPORTED),  # head-pair layout: 2^21 * 8 * 128 bytes = 2 GiB per image
 ])
 def test_msda_forward_rejects(lib, kw, code):
     assert _msda(lib, **kw) == code
@@ -241,11 +242,11 @@ def test_pack_pairs_rejects(lib, kw, code):
     assert _pk(lib, **kw) == code
 
 
-def test_pairs_layout_is_for_the_sca_forward_only(lib):
-    """MSDA_BF16_PAIRS is refused by the operator and the backward passes
-    before anything is read."""
-    assert lib.msda_forward_frames(A, 2, A, A, A, A, 1, 1, 2, 16, 4, 8, 32, 1, 4, B_, None) == INVALID
+def test_pairs_layout_is_refused_by_the_backward_passes(lib):
+    """MSDA_BF16_PAIRS is for the forward entry points: the backward ones
+    refuse it before anything is read."""
     assert _mb(lib, dtype=2) == INVALID
+    assert _mbf(lib, dtype=2) == INVALID
 
 
 def test_gemm_rejects_null_and_dtype(lib):

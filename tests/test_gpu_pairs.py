@@ -7,7 +7,10 @@
 - SCA on a value in pairs against the CPU oracle on the plain value: every
   row of the batch-4 bf16 layer workload, the SCA edge cases, levels so
   small that most corner pairs straddle a border, the stage path and the
-  allocation-free entry point.
+  allocation-free entry point;
+- the operator and its frame mean on a value in pairs: the DETR encoder and
+  temporal workloads on every query (planned and unplanned, bit for bit),
+  the operator's edge cases, both frame-staging paths, row ends.
 Every call goes through the C ABI (via the ctypes binding)."""
 import numpy as np
 import pytest
@@ -208,3 +211,110 @@ def test_sca_pairs_stage_path_and_noalloc():
                              dev(w["sampling_offsets"]), dev(w["attention_logits"]), out)
     assert np.array_equal(host(out).reshape(600, -1), ref), "allocation-free entry point"
     assert_fp32_close(ref, oracle_slots(w, w["value"]), "pairs, stage test inputs")
+
+
+# ---------------------------------------------------------------------------
+# the operator (and its frame mean) on a value in pairs
+# ---------------------------------------------------------------------------
+
+def _bf16_value(w):
+    """The workload with its value quantised to bf16 bits (the oracle reads
+    those bits exactly)."""
+    return {**w, "value": W.bf16_bits_trunc(w["value"])}
+
+
+def run_op_pairs(w, frames=False, plan=False):
+    args = (dev(pairs_host(w["value"])), dev(w["spatial_shapes"]), dev(w["level_start_index"]),
+            dev(w["sampling_locations"]), dev(w["attention_weights"]))
+    if plan:
+        B, Nq = w["B"], w["Nq"]
+        F = w["value"].shape[1] if frames else 1
+        loc = args[3]
+        r = loc[0, 0, 0].numel() if frames else loc[0, 0].numel()  # one query's locations
+        p = msda.msda_plan(loc, B, Nq, F * Nq * r, r)
+        out = msda.msda_gather(*args, p)
+    else:
+        out = (msda.msda_forward_frames if frames else msda.msda_forward)(*args)
+    return host(out).reshape(w["B"] * w["Nq"], -1)
+
+
+def test_detr_encoder_in_pairs():
+    """The DETR encoder workload on a bf16 value in pairs: every query
+    against the oracle, and the planned gather bit for bit against the
+    unplanned one."""
+    w = _bf16_value(W.detr_encoder_msda())
+    got = run_op_pairs(w)
+    ref = oracle_by_rows(lambda r: oracle.msda(w["value"], w["spatial_shapes"], w["level_start_index"],
+                                               w["sampling_locations"], w["attention_weights"],
+                                               weights_are_logits=True, rows=r), np.arange(w["B"] * w["Nq"]))
+    assert_fp32_close(got, ref, f"DETR encoder in pairs, all {w['Nq']} queries")
+    assert np.array_equal(run_op_pairs(w, plan=True), got), "planned != unplanned"
+
+
+def test_temporal_frames_in_pairs():
+    """Two stacked BEV maps in pairs ([B,F,nH,Nv,2,32]): the frame mean of
+    every query against the oracle, planned and unplanned."""
+    w = _bf16_value(W.temporal_frames())
+    got = run_op_pairs(w, frames=True)
+    ref = oracle_by_rows(lambda r: oracle.msda_frames(w["value"], w["spatial_shapes"], w["level_start_index"],
+                                                      w["sampling_locations"], w["attention_weights"], rows=r),
+                         np.arange(w["B"] * w["Nq"]))
+    assert_fp32_close(got, ref, "temporal frames in pairs, all queries")
+    assert np.array_equal(run_op_pairs(w, frames=True, plan=True), got), "planned != unplanned"
+
+
+OP_EDGE = [
+    # id, seed, B, Nq, shapes, nH, P
+    ("ragged_queries_nH4", 1, 2, 37, ((5, 7), (3, 2)), 4, 3),
+    ("two_head_passes_nH12_odd_LP", 2, 3, 19, ((6, 4),), 12, 5),
+    ("one_head_one_point", 3, 1, 9, ((4, 4),), 1, 1),
+    ("max_points_LP64", 4, 1, 33, ((8, 8), (4, 4), (2, 2), (1, 1)), 8, 16),
+    ("unit_levels_and_wide", 5, 2, 21, ((1, 1), (1, 40), (17, 1)), 8, 4),
+    ("many_heads_nH64", 7, 1, 5, ((3, 5),), 64, 2),
+]
+
+
+def _rand_op(seed, B, Nq, shapes, nH, P, F=None):
+    ss, starts, Nv = W.level_table(shapes)
+    L = len(ss)
+    g = np.random.default_rng(seed)
+    lead = (B,) if F is None else (B, F)
+    return {"value": W.bf16_bits_trunc(g.normal(size=lead + (Nv, nH, 32)).astype(np.float32)),
+            "spatial_shapes": ss, "level_start_index": starts,
+            "sampling_locations": g.uniform(-0.2, 1.2, lead + (Nq, nH, L, P, 2)).astype(np.float32),
+            "attention_weights": g.normal(size=lead + (Nq, nH, L * P)).astype(np.float32), "B": B, "Nq": Nq}
+
+
+@pytest.mark.parametrize("case", OP_EDGE, ids=[c[0] for c in OP_EDGE])
+def test_operator_pairs_edge_cases(case):
+    _, seed, B, Nq, shapes, nH, P = case
+    w = _rand_op(seed, B, Nq, shapes, nH, P)
+    ref = oracle.msda(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
+                      w["attention_weights"], weights_are_logits=True)
+    assert_fp32_close(run_op_pairs(w), ref, case[0])
+
+
+@pytest.mark.parametrize("F,shapes,P", [(3, ((6, 9), (3, 4)), 4), (3, ((6, 9), (3, 4)), 12)],
+                         ids=["frames_in_one_pass", "frame_by_frame_FLP72"])
+def test_frames_pairs_both_staging_paths(F, shapes, P):
+    """F * L * P <= 64 stages all frames at once; 72 goes frame by frame."""
+    w = _rand_op(40 + P, 2, 50, shapes, 8, P, F=F)
+    ref = oracle.msda_frames(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
+                             w["attention_weights"])
+    assert_fp32_close(run_op_pairs(w, frames=True), ref, f"frames in pairs, F={F}, P={P}")
+
+
+def test_operator_pairs_row_ends_never_read():
+    """As for the SCA: NaN in every row end's right half never reaches a
+    result of the operator."""
+    w = _rand_op(45, 2, 120, ((4, 5), (2, 3), (1, 1)), 8, 4)
+    pairs = pairs_host(w["value"])
+    for (H, Wd), s0 in zip(w["spatial_shapes"], w["level_start_index"]):
+        row_ends = s0 + np.arange(H) * Wd + Wd - 1
+        pairs[:, :, row_ends, 1, :] = np.uint16(0x7FC0)
+    out = host(msda.msda_forward(dev(pairs), dev(w["spatial_shapes"]), dev(w["level_start_index"]),
+                                 dev(w["sampling_locations"]), dev(w["attention_weights"]))).reshape(240, -1)
+    assert np.isfinite(out).all(), "a row end's right half was read"
+    ref = oracle.msda(w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"],
+                      w["attention_weights"], weights_are_logits=True)
+    assert_fp32_close(out, ref, "operator border pairs")
