@@ -20,7 +20,7 @@ Functions (same names as the C entry points):
                 chains them with the compaction and msda_forward)
   projections:  msda_gemm_bf16, msda_query_proj_bf16, msda_output_proj_bf16,
                 msda_value_proj_pairs_bf16 (the value projection written in the
-                head-pair layout that the SCA entry points also take)
+                head-pair layout that every forward entry point also takes)
   layout:       msda_pack_pairs_bf16 (a bf16 value rewritten in that layout)
   status:       msda_status_string, msda_last_error
 """
