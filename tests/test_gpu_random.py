@@ -1,7 +1,8 @@
 """Seeded random configurations against the oracle: head counts, level
 tables (including 1x1 and 1xN levels), points per level, anchors, cameras,
 batch sizes, query counts, value types and mask densities drawn per case,
-forward and backward (both value-gradient paths), element by element.
+forward and backward (both value-gradient paths), and the forward on the
+value's bf16 bits in the head-pair layout, element by element.
 Every call goes through the C ABI (via the ctypes binding)."""
 import numpy as np
 import pytest
@@ -10,6 +11,7 @@ import torch
 import oracle
 import workloads as W
 from gpu_util import announce, assert_fp32_close, assert_sum_close, dev, host
+from test_gpu_pairs import pairs_host
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +58,12 @@ def test_random_msda_forward_and_backward(seed):
     out = host(msda.msda_forward(*args, weight_mode=mode)).reshape(-1, c["nH"] * 32)
     ref = oracle.msda(c["value"], c["ss"], c["starts"], c["loc"], c["weights"], weights_are_logits=c["logits"])
     assert_fp32_close(out, ref, f"case {seed}: forward")
+    # the same value's bf16 bits in the head-pair layout
+    vb = c["value"] if c["value"].dtype == np.uint16 else W.bf16_bits_trunc(c["value"])
+    out_p = host(msda.msda_forward(dev(pairs_host(vb)), *args[1:], weight_mode=mode)).reshape(-1, c["nH"] * 32)
+    ref_p = ref if vb is c["value"] else oracle.msda(vb, c["ss"], c["starts"], c["loc"], c["weights"],
+                                                      weights_are_logits=c["logits"])
+    assert_fp32_close(out_p, ref_p, f"case {seed}: forward, head-pair layout")
     rv, rl, rw = oracle.msda_backward(c["value"], c["ss"], c["starts"], c["loc"], c["weights"], c["gout"],
                                       weights_are_logits=c["logits"])
     # magnitude of each value-gradient element's contributions: alpha >= 0 after a softmax, |p| otherwise
@@ -105,6 +113,11 @@ def test_random_sca_forward_and_backward(seed):
     n = int(ref["pair_offsets"][-1])
     assert np.array_equal(host(pq)[:n], ref["pair_q"]), f"case {seed}: pair lists"
     assert_fp32_close(host(slots).reshape(B * Nq, -1), ref["slots"], f"case {seed}: slots")
+    # the same value's bf16 bits in the head-pair layout
+    vb = c["value"] if c["value"].dtype == np.uint16 else W.bf16_bits_trunc(c["value"])
+    slots_p = msda.sca_forward(dev(pairs_host(vb)), d["ss"], d["starts"], d["rho"], d["mask"], d["off"], d["logits"])
+    ref_p = ref["slots"] if vb is c["value"] else oracle.sca(vb, *args[1:])["slots"]
+    assert_fp32_close(host(slots_p).reshape(B * Nq, -1), ref_p, f"case {seed}: slots, head-pair layout")
 
     ws = torch.empty(msda.sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device="cuda")
     msda.sca_compact(d["mask"], d["rho"], ws)
