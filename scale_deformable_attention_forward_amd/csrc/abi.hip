@@ -250,6 +250,7 @@ static msda::CompactArgs compact_args(const uint8_t* bev_mask, const float* refe
   c.D = D;
   c.cammask = reinterpret_cast<uint32_t*>(ws + lay.cammask);
   c.qkey = reinterpret_cast<int32_t*>(ws + lay.qkey);
+  c.qrank = reinterpret_cast<int32_t*>(ws + lay.qrank);
   c.hit_count = hit_count;
   c.tile_counts = reinterpret_cast<int32_t*>(ws + lay.tile_counts);
   c.tile_offsets = reinterpret_cast<int32_t*>(ws + lay.tile_offsets);
@@ -258,7 +259,6 @@ static msda::CompactArgs compact_args(const uint8_t* bev_mask, const float* refe
   c.bin_hist = reinterpret_cast<int32_t*>(ws + lay.bin_hist);
   c.seg_seen = reinterpret_cast<int32_t*>(ws + lay.seg_seen);
   c.seg_pairs = reinterpret_cast<int32_t*>(ws + lay.seg_pairs);
-  c.bin_offsets = reinterpret_cast<int32_t*>(ws + lay.bin_offsets);
   c.order = reinterpret_cast<int32_t*>(ws + lay.order);
   c.bin_cost = reinterpret_cast<uint64_t*>(ws + lay.bin_cost);
   c.seg_cost = reinterpret_cast<uint64_t*>(ws + lay.seg_cost);

@@ -3,28 +3,30 @@
 // queries the camera sees; and its hit count per query), plus the order in
 // which the gather kernel visits the seen queries.
 //
-// Four small stream-ordered kernels:
+// Three small stream-ordered kernels:
 //   0. clear: zero the ordering histogram and the per-segment totals;
 //   1. visibility: per (b, q) the bit set of cameras that see q (any of the D
 //      anchors marked), the hit count, per (b, c, tile of 256 queries) the
 //      number of seen queries, and for a seen query its ordering bin: the
 //      image tile (kOrderBinsX columns x kOrderBinsY rows, column-major) of
 //      the first marked anchor of its first camera, within the segment
-//      (b, first camera);
-//   2. scan: one workgroup per segment (b, c) turns the segment's tile counts
-//      and bin counts into exclusive offsets, starting from the sums of the
-//      earlier segments' totals (which the visibility kernel accumulated):
-//      pair_offsets[b*Ncam + c] is the offset of the first tile of (b, c)
-//      and pair_offsets[B*Ncam] the total; and it places the boundaries of
-//      the dies' shares of the batch item's work list where the summed cost
-//      of the bins crosses each eighth of the item's total (interpolating
-//      inside the bin), so that every die gets the same estimated work;
-//   3. compact: each query writes its index at tile offset + (seen queries
-//      before it in the tile) for every camera that sees it, so each (b, c)
-//      list comes out in ascending order (deterministic, no atomics); and a
-//      seen query takes a slot of its bin in the work order (atomic slot
-//      claims: the order inside a bin varies from run to run, which changes
-//      only which wave computes which query, never a result).
+//      (b, first camera), and its rank among the bin's queries (the count
+//      its histogram add returns: unique, in no fixed order);
+//   2. compact, two kinds of blocks in one grid:
+//      - one per (b, tile): each query writes its index at tile offset +
+//        (seen queries before it in the tile) for every camera that sees it,
+//        so each (b, c) list comes out in ascending order (deterministic, no
+//        atomics); the tile offset is the pairs of the earlier segments and
+//        of the earlier tiles of (b, c), summed from the visibility counts.
+//        A seen query takes the slot (its bin's first entry + its rank) of
+//        the work order, the bins' first entries scanned in LDS for the
+//        segments the tile's queries start in.  The rank's order varies from
+//        run to run, which changes only which wave computes which query,
+//        never a result;
+//      - one per segment (b, c): its pair offset, and the boundaries of the
+//        dies' shares of the batch item's work list where the summed cost of
+//        the bins crosses each eighth of the item's total (interpolating
+//        inside the bin), so that every die gets the same estimated work.
 // Queries that share a bin project to the same image tile of the same
 // camera, so consecutive work items read neighbouring value rows and one
 // die's L2 holds their working set.  Bins run column-major: the anchors of
@@ -37,8 +39,8 @@ namespace msda {
 
 constexpr int kTile = kQueryTile;  // queries per tile = threads per block
 constexpr int kTileWaves = kTile / kWave;
-constexpr int kScanThreads = kOrderBins;  // one bin per thread
-static_assert(kScanThreads == 1024, "the scan block holds one segment's bins");
+constexpr int kBinsPerThread = kOrderBins / kTile;
+static_assert(kBinsPerThread == 4, "a block scans one segment's bins, four (one int4) per thread");
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -55,6 +57,7 @@ CompactLayout compact_layout(int64_t B, int64_t Ncam, int64_t Nq) {
   };
   l.cammask = take(sizeof(uint32_t) * nq);
   l.qkey = take(sizeof(int32_t) * nq);
+  l.qrank = take(sizeof(int32_t) * nq);
   l.tile_counts = take(sizeof(int32_t) * segs * (size_t)l.tiles);
   l.tile_offsets = take(sizeof(int32_t) * segs * (size_t)l.tiles);
   l.pair_offsets = take(sizeof(int32_t) * (segs + 1));
@@ -68,7 +71,6 @@ CompactLayout compact_layout(int64_t B, int64_t Ncam, int64_t Nq) {
   l.seg_cost = l.bin_cost + sizeof(uint64_t) * segs * kOrderBins;
   l.clear_ints = (int)((l.seg_cost + sizeof(uint64_t) * segs - l.bin_hist) / sizeof(int32_t));
   o = align_up(l.seg_cost + sizeof(uint64_t) * segs, 256);
-  l.bin_offsets = take(sizeof(int32_t) * (segs * kOrderBins + 1));
   l.order = take(sizeof(int32_t) * nq);
   l.die_bounds = take(sizeof(int32_t) * (size_t)B * kDieBounds);
   l.total = o;
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kTile) void sca_visibility_kernel(CompactArgs a, in
       const float2 r = reinterpret_cast<const float2*>(a.rp)[(((int64_t)c0 * a.B + b) * a.Nq + q) * a.D + first_anchor];
       const int bin = tile_bin(r.x, kOrderBinsX) * kOrderBinsY + tile_bin(r.y, kOrderBinsY);
       key = (b * a.Ncam + c0) * kOrderBins + bin;
-      atomicAdd(&a.bin_hist[key], 1);
+      a.qrank[bq] = atomicAdd(&a.bin_hist[key], 1);
       atomicAdd(&a.bin_cost[key], (unsigned long long)cost);
       atomicAdd(&first_cost[c0], (unsigned long long)cost);
     }
@@ -190,152 +192,180 @@ __global__ __launch_bounds__(kTile) void sca_visibility_kernel(CompactArgs a, in
   }
 }
 
-// Exclusive scan of one value per thread over the block (kScanThreads);
-// also returns the block total.
-__device__ int block_exclusive_scan(int v, int* total) {
-  __shared__ int wave_sums[kScanThreads / kWave];
+// Sum of x[lo, hi) over the lanes of a wave (every lane gets it).
+template <typename T>
+__device__ T wave_sum(const T* __restrict__ x, int64_t lo, int64_t hi) {
+  const int lane = threadIdx.x % kWave;
+  T v = 0;
+  for (int64_t i = lo + lane; i < hi; i += kWave) v += x[i];
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
+// Exclusive scan of one value per thread over the block (kTile threads);
+// also returns the block total.  wsum: kTileWaves entries of LDS.
+template <typename T>
+__device__ T block_exclusive_scan(T v, T* total, T* wsum) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  int incl = v;
+  T incl = v;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
-    const int u = __shfl_up(incl, d);
+    const T u = __shfl_up(incl, d);
     if (lane >= d) incl += u;
   }
-  __syncthreads();  // wave_sums may still be read by a previous scan
-  if (lane == kWave - 1) wave_sums[wave] = incl;
+  __syncthreads();  // wsum may still be read by a previous scan
+  if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < kScanThreads / kWave; ++w) {
-    const int ws = wave_sums[w];
-    before += w < wave ? ws : 0;
+  T before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kTileWaves; ++w) {
+    const T ws = wsum[w];
+    before += w < wave ? ws : T(0);
     all += ws;
   }
   *total = all;
   return before + incl - v;
 }
 
-// Sum of x[0, n) over the block.
-__device__ int block_sum(const int32_t* __restrict__ x, int n) {
-  __shared__ int partial[kScanThreads / kWave];
-  int s = 0;
-  for (int i = threadIdx.x; i < n; i += kScanThreads) s += x[i];
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) s += __shfl_xor(s, d);
-  __syncthreads();
-  if (threadIdx.x % kWave == 0) partial[threadIdx.x / kWave] = s;
-  __syncthreads();
-  int all = 0;
-  for (int w = 0; w < kScanThreads / kWave; ++w) all += partial[w];
-  return all;
-}
-
-// Inclusive scan of one 64-bit value per thread over the block.
-__device__ uint64_t block_inclusive_scan64(uint64_t v) {
-  __shared__ uint64_t wave_sums64[kScanThreads / kWave];
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  uint64_t incl = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint64_t u = __shfl_up(incl, d);
-    if (lane >= d) incl += u;
-  }
-  __syncthreads();
-  if (lane == kWave - 1) wave_sums64[wave] = incl;
-  __syncthreads();
-  for (int w = 0; w < wave; ++w) incl += wave_sums64[w];
-  return incl;
-}
-
-// One block per segment s = b*Ncam + c.
-__global__ __launch_bounds__(kScanThreads) void sca_scan_kernel(CompactArgs a, int tiles) {
-  const int s = blockIdx.x, segs = a.B * a.Ncam;
+// Segment s = (b, c): its pair offset, and where its bins hold the targets
+// of the dies' shares of batch item b's work list: share x starts where the
+// summed cost, in work-list order, reaches x/8 of the item's total (inside a
+// bin, by linear interpolation over its entries).  The item's first and last
+// segments write its ends (and, with no cost at all, every boundary).
+__device__ void segment_bounds(const CompactArgs& a, int b, int c) {
+  __shared__ int wsum[kTileWaves];
+  __shared__ unsigned long long wsum64[kTileWaves];
   const int t = threadIdx.x;
-  const int b = s / a.Ncam, c = s % a.Ncam;
-  const int base_seen = block_sum(a.seg_seen, s);
-  const int base_pairs = block_sum(a.seg_pairs, s);
-  int total = 0;
-  const int64_t bin = (int64_t)s * kOrderBins + t;
-  const int count = a.bin_hist[bin];
-  const int first_item = base_seen + block_exclusive_scan(count, &total);
-  a.bin_offsets[bin] = first_item;
-
-  // Boundaries of the dies' shares of batch item b's work list: share x
-  // starts where the summed cost, in work-list order, reaches x/8 of the
-  // item's total (inside a bin, by linear interpolation over its entries).
-  // The bin holding a target writes it; the item's first and last segments
-  // write its ends (and, with no cost at all, every boundary).
-  uint64_t item_cost = 0, seg_base = 0;  // uniform: the item's total, and its cost before this segment
-  for (int k = 0; k < a.Ncam; ++k) {
-    const uint64_t v = a.seg_cost[(int64_t)b * a.Ncam + k];
-    item_cost += v;
-    seg_base += k < c ? v : 0ull;
+  const int s = b * a.Ncam + c, segs = a.B * a.Ncam;
+  const int64_t item0 = (int64_t)b * a.Ncam;
+  // uniform: seen queries and pairs of the segments before s (all items),
+  // the item's cost before s and in all
+  const int base_seen = wave_sum(a.seg_seen, 0, s);
+  const int base_pairs = wave_sum(a.seg_pairs, 0, s);
+  const uint64_t seg_base = wave_sum<unsigned long long>(
+      reinterpret_cast<const unsigned long long*>(a.seg_cost), item0, s);
+  const uint64_t item_cost = wave_sum<unsigned long long>(
+      reinterpret_cast<const unsigned long long*>(a.seg_cost), item0, item0 + a.Ncam);
+  const int64_t bin0 = (int64_t)s * kOrderBins + kBinsPerThread * t;
+  const int4 n4 = reinterpret_cast<const int4*>(a.bin_hist + bin0)[0];
+  const int count[kBinsPerThread] = {n4.x, n4.y, n4.z, n4.w};
+  unsigned long long cost[kBinsPerThread];
+  unsigned long long cost_sum = 0;
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) {
+    cost[i] = a.bin_cost[bin0 + i];
+    cost_sum += cost[i];
   }
-  const uint64_t bin_cost = a.bin_cost[bin];
-  const uint64_t bin_end = seg_base + block_inclusive_scan64(bin_cost);  // relative to the item
-  const uint64_t bin_begin = bin_end - bin_cost;
+  int seg_total = 0;
+  unsigned long long seg_cost_total = 0;
+  int first = base_seen + block_exclusive_scan(n4.x + n4.y + n4.z + n4.w, &seg_total, wsum);
+  uint64_t begin = seg_base + block_exclusive_scan(cost_sum, &seg_cost_total, wsum64);
   int32_t* bounds = a.die_bounds + (int64_t)b * kDieBounds;
-  for (int x = 1; x < kXcds; ++x) {
-    const uint64_t target = item_cost * (uint64_t)x / kXcds;
-    if (bin_cost != 0 && target >= bin_begin && target < bin_end) {
-      // entry of the bin at that fraction of its cost (double: no overflow
-      // of cost x count; the clamp keeps it inside the bin)
-      const int k = (int)((double)(target - bin_begin) / (double)bin_cost * (double)count);
-      bounds[x] = first_item + min(max(k, 0), count - 1);
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) {
+    const uint64_t end = begin + cost[i];
+    for (int x = 1; x < kXcds; ++x) {
+      const uint64_t target = item_cost * (uint64_t)x / kXcds;
+      if (cost[i] != 0 && target >= begin && target < end) {
+        // entry of the bin at that fraction of its cost (double: no overflow
+        // of cost x count; the clamp keeps it inside the bin)
+        const int k = (int)((double)(target - begin) / (double)cost[i] * (double)count[i]);
+        bounds[x] = first + min(max(k, 0), count[i] - 1);
+      }
     }
-  }
-  if (t == 0 && c == 0) {
-    bounds[0] = base_seen;
-    if (item_cost == 0)
-      for (int x = 1; x < kXcds; ++x) bounds[x] = base_seen;
-  }
-  if (t == 0 && c == a.Ncam - 1) bounds[kXcds] = base_seen + a.seg_seen[s];
-  int run = base_pairs;
-  for (int t0 = 0; t0 < tiles; t0 += kScanThreads) {
-    const int64_t i = (int64_t)s * tiles + t0 + t;
-    const int v = t0 + t < tiles ? a.tile_counts[i] : 0;
-    const int excl = block_exclusive_scan(v, &total);
-    if (t0 + t < tiles) a.tile_offsets[i] = run + excl;
-    run += total;
+    begin = end;
+    first += count[i];
   }
   if (t == 0) {
-    a.pair_offsets[s] = base_pairs;
-    if (s == segs - 1) {
-      a.pair_offsets[segs] = base_pairs + a.seg_pairs[s];
-      a.bin_offsets[(int64_t)segs * kOrderBins] = base_seen + a.seg_seen[s];
+    if (c == 0) {
+      bounds[0] = base_seen;
+      if (item_cost == 0)
+        for (int x = 1; x < kXcds; ++x) bounds[x] = base_seen;
     }
+    if (c == a.Ncam - 1) bounds[kXcds] = base_seen + seg_total;
+    a.pair_offsets[s] = base_pairs;
+    if (s == segs - 1) a.pair_offsets[segs] = base_pairs + a.seg_pairs[s];
   }
 }
 
-__global__ __launch_bounds__(kTile) void sca_compact_kernel(CompactArgs a, int tiles) {
+// Tile `tile` of batch item b: the pair lists' entries of its queries, its
+// offsets in them (tile_offsets), and its seen queries' work-order slots.
+__device__ void tile_compact(const CompactArgs& a, int b, int tile, int tiles) {
   __shared__ int wave_counts[kTileWaves][32];
   __shared__ int tile_start[32];
-  const int tile = blockIdx.x, b = blockIdx.y;
-  const int q = tile * kTile + (int)threadIdx.x;
+  __shared__ int seen_before[32];  // seen queries of the segments before (b, c), all items
+  __shared__ uint32_t wave_firsts[kTileWaves];
+  __shared__ int wsum[kTileWaves];
+  __shared__ int bin_first[kOrderBins];
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  const int q = tile * kTile + t;
   const int64_t bq = (int64_t)b * a.Nq + q;
-  if ((int)threadIdx.x < a.Ncam)  // loaded alongside the masks, used after the ballots
-    tile_start[threadIdx.x] = a.tile_offsets[((int64_t)b * a.Ncam + threadIdx.x) * tiles + tile];
   const uint32_t seen = q < a.Nq ? a.cammask[bq] : 0u;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  int key = 0, rank = 0;
+  if (seen != 0u) {
+    key = a.qkey[bq];
+    rank = a.qrank[bq];
+  }
+  // per camera (one wave each): the tile's first pair in the lists, after
+  // the pairs of the earlier segments and of the earlier tiles of (b, c)
+  for (int c = wave; c < a.Ncam; c += kTileWaves) {
+    const int s = b * a.Ncam + c;
+    const int before = wave_sum(a.seg_pairs, 0, s) + wave_sum(a.tile_counts, (int64_t)s * tiles,
+                                                              (int64_t)s * tiles + tile);
+    const int seen_b = wave_sum(a.seg_seen, 0, s);
+    if (lane == 0) {
+      tile_start[c] = before;
+      seen_before[c] = seen_b;
+      a.tile_offsets[(int64_t)s * tiles + tile] = before;
+    }
+  }
+  const int first = seen != 0u ? __builtin_ctz(seen) : -1;
+  uint32_t firsts = 0u;  // first cameras of the wave's seen queries
   for (int c = 0; c < a.Ncam; ++c) {
     const uint64_t bits = __ballot((seen >> c) & 1u);
+    if (__ballot(first == c) != 0ull) firsts |= 1u << c;
     if (lane == 0) wave_counts[wave][c] = __popcll(bits);
   }
+  if (lane == 0) wave_firsts[wave] = firsts;
   __syncthreads();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   for (int c = 0; c < a.Ncam; ++c) {
     const uint64_t bits = __ballot((seen >> c) & 1u);
     if ((seen >> c) & 1u) {
-      int rank = __popcll(bits & below);
-      for (int w = 0; w < wave; ++w) rank += wave_counts[w][c];
-      a.pair_q[tile_start[c] + rank] = q;
+      int r = __popcll(bits & below);
+      for (int w = 0; w < wave; ++w) r += wave_counts[w][c];
+      a.pair_q[tile_start[c] + r] = q;
     }
   }
-  if (seen != 0u) {
-    const int key = a.qkey[bq];
-    // count the bin down: the slot is unique, and the histogram ends at zero
-    const int slot = a.bin_offsets[key] + atomicSub(&a.bin_hist[key], 1) - 1;
-    a.order[slot] = (int32_t)bq;
+  // work-order slots, segment by segment of the tile's first cameras: the
+  // bin's first entry (seen queries before it) + the query's rank in the bin
+  uint32_t need = 0u;
+#pragma unroll
+  for (int w = 0; w < kTileWaves; ++w) need |= wave_firsts[w];
+  for (; need != 0u; need &= need - 1u) {
+    const int c = __builtin_ctz(need);
+    const int s = b * a.Ncam + c;
+    const int4 n4 = reinterpret_cast<const int4*>(a.bin_hist + (int64_t)s * kOrderBins)[t];
+    int total = 0;
+    const int at = seen_before[c] + block_exclusive_scan(n4.x + n4.y + n4.z + n4.w, &total, wsum);
+    bin_first[kBinsPerThread * t] = at;
+    bin_first[kBinsPerThread * t + 1] = at + n4.x;
+    bin_first[kBinsPerThread * t + 2] = at + n4.x + n4.y;
+    bin_first[kBinsPerThread * t + 3] = at + n4.x + n4.y + n4.z;
+    __syncthreads();
+    if (first == c) a.order[bin_first[key - s * kOrderBins] + rank] = (int32_t)bq;
+    __syncthreads();  // bin_first is rewritten for the next segment
   }
+}
+
+// Grid (tiles + Ncam, B): blocks x < tiles are tiles, the rest segments.
+__global__ __launch_bounds__(kTile) void sca_compact_kernel(CompactArgs a, int tiles) {
+  const int b = blockIdx.y;
+  if ((int)blockIdx.x < tiles)
+    tile_compact(a, b, blockIdx.x, tiles);
+  else
+    segment_bounds(a, b, (int)blockIdx.x - tiles);
 }
 
 hipError_t launch_sca_compact(const CompactArgs& a, int tiles, hipStream_t stream) {
@@ -350,10 +380,7 @@ hipError_t launch_sca_compact(const CompactArgs& a, int tiles, hipStream_t strea
     sca_visibility_kernel<false><<<grid, kTile, 0, stream>>>(a, tiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  sca_scan_kernel<<<a.B * a.Ncam, kScanThreads, 0, stream>>>(a, tiles);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  sca_compact_kernel<<<grid, kTile, 0, stream>>>(a, tiles);
+  sca_compact_kernel<<<dim3(tiles + a.Ncam, a.B), kTile, 0, stream>>>(a, tiles);
   return hipGetLastError();
 }
 

@@ -83,8 +83,8 @@ constexpr int kOrderBinsX = 64, kOrderBinsY = 16, kOrderBins = kOrderBinsX * kOr
 struct CompactLayout {
   // bin_hist, seg_seen, seg_pairs, bin_cost and seg_cost are adjacent: one
   // clear covers them
-  size_t cammask, qkey, tile_counts, tile_offsets, pair_offsets, pair_q, bin_hist, seg_seen, seg_pairs, bin_cost,
-      seg_cost, bin_offsets, order, die_bounds, total;
+  size_t cammask, qkey, qrank, tile_counts, tile_offsets, pair_offsets, pair_q, bin_hist, seg_seen, seg_pairs,
+      bin_cost, seg_cost, order, die_bounds, total;
   int tiles;  // tiles of the query axis per (b, c)
   int clear_ints;  // int32 words from bin_hist on to zero before a compaction
 };
@@ -96,6 +96,7 @@ struct CompactArgs {
   int B, Ncam, Nq, D;
   uint32_t* cammask;
   int32_t* qkey;       // [B][Nq] ordering bin of a seen query, -1 if unseen
+  int32_t* qrank;      // [B][Nq] a seen query's rank among its bin's queries
   int32_t* hit_count;  // may be null
   int32_t* tile_counts;
   int32_t* tile_offsets;
@@ -104,7 +105,6 @@ struct CompactArgs {
   int32_t* bin_hist;     // [B*Ncam*kOrderBins]
   int32_t* seg_seen;     // [B*Ncam] seen queries whose first camera is c, per (b, c)
   int32_t* seg_pairs;    // [B*Ncam] pairs per (b, c)
-  int32_t* bin_offsets;  // [B*Ncam*kOrderBins + 1]; the last entry counts the seen queries
   int32_t* order;        // [B*Nq]
   uint64_t* bin_cost;    // [B*Ncam*kOrderBins] summed cost of each ordering bin
   uint64_t* seg_cost;    // [B*Ncam] summed cost of the seen queries whose first camera is c, per (b, c)
