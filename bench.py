@@ -32,7 +32,14 @@ layers, each with its own value maps, offsets and logits), "tiny".
 
 Prints one JSON line.  value = bilinear samples per second (one sample = one
 (camera, query, head, level, point) bilinear read of 4 corners x 32
-channels) over the whole step.  Kernel figures come from HIP events
+channels) over the whole step.  The K timed steps run eagerly, one library
+call per part with HIP events between the parts; a step of more than one
+call then runs again as K replays of the step captured once in a HIP graph
+(one launch per step; the replays must reproduce the eager outputs bit for
+bit), and ms_per_step and value come from the replays' wall-clock time
+(launch.eager holds the eager figures; --eager times the eager steps only,
+and the padded rebatch flow, which reads a length back to the host, always
+runs eagerly).  Kernel figures come from the eager steps' HIP events,
 recorded on the stream the kernels run on:
   roofline         the main kernel against the 8 TB/s HBM peak, on the bytes
                    one launch must move at least once (every value map, the
@@ -54,7 +61,7 @@ inside a network); batch_items_per_s = batch items (scenes) per second;
 cpu_baseline = the CPU oracle on the same workload (or a bounded sample of
 it), on one thread and on every core this process may use.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--eager]
   python bench.py --calibrate-copy   (a plain device copy of known size, for
                                       scaling the HBM byte counters)
 """
@@ -293,6 +300,8 @@ class Workload:
         self.inbounds_corners = None  # corners inside their map, per gather launch
         self.unique_bytes = None  # bytes one launch of the main part must move at least once
         self.onchip = None  # callable: the main kernel's rate with every corner row in L2
+        self.graph = True  # the step can be captured in a HIP graph (nothing read back to the host)
+        self.outputs = []  # tensors a graph replay must reproduce bit for bit
 
 
 def count_inbounds(shapes, x, y):
@@ -504,6 +513,7 @@ def sca_workload(kind):
         wl.parts.append(("output_proj", lambda: m.msda_gemm_bf16(slots.view(-1, C), d["W_o"], d["b_o"],
                                                                  out=d["out"])))
     wl.main = "gather"
+    wl.outputs = [slots, hit, offs] + ([d["out"]] if layer else [])
 
     def finish():
         import numpy as np
@@ -608,6 +618,7 @@ def rebatch_workload():
                                                     out=views()[2])))
     wl.parts.append(("scatter_mean", lambda: m.sca_scatter_mean(views()[2], offs, pq, hit, Nq, slots=slots)))
     wl.main = "msda"
+    wl.graph = False  # the segment length is read back to the host
 
     def finish():
         n_pairs = int(offs[-1].item())
@@ -674,6 +685,7 @@ def train_workload(which):
         names += " (value gradient by float32 atomics)" if atomic else ""
         pairs = lambda: int(offs[-1].item())
         n_images = B * Ncam
+        outs = [slots, gv, go, gl]
     elif which == "tsa_train":
         w = W.temporal_frames()
         B, F, Nq, Nv, nH, L, P = w["B"], w["F"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"]
@@ -697,6 +709,7 @@ def train_workload(which):
                  + (" (value gradient by float32 atomics)" if atomic else ""))
         pairs = lambda: B * F * Nq
         n_images = B * F
+        outs = [out, gv, gloc, gw]
     else:
         w = W.detr_encoder_msda()
         B, Nq, Nv, nH, L, P = w["B"], w["Nq"], w["Nv"], w["nH"], w["L"], w["P"]
@@ -719,7 +732,10 @@ def train_workload(which):
         names += " (value gradient by float32 atomics)" if atomic else ""
         pairs = lambda: B * Nq
         n_images = B
+        outs = [out, gv, gloc, gw]
     wl.main = "backward"
+    # float32 atomics sum in no fixed order: only the forward output repeats bit for bit
+    wl.outputs = outs[:1] if atomic else outs
 
     def finish():
         n = pairs()
@@ -787,6 +803,7 @@ def msda_workload(which):
         fn = m.msda_forward if F == 1 else m.msda_forward_frames
         wl.parts.append(("gather", lambda: fn(*args, out=out)))
     wl.main = "gather"
+    wl.outputs = [out]
 
     def finish():
         wl.samples = B * F * Nq * nH * L * P
@@ -832,6 +849,9 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="steps timed after a 1 GiB write that evicts the caches (0: none)")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the eager steps only (by default the step is also captured in a HIP graph and "
+                         "the replays are timed)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -887,6 +907,46 @@ def main():
     def pct(v):
         return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
                 "p90": float(np.percentile(v, 90))}
+
+    # a step of several library calls captured once in a HIP graph and
+    # replayed K times: one launch per step instead of one call (and its
+    # host-side argument checks) per part; the replays must reproduce the
+    # eager outputs bit for bit.  A one-call step gains nothing from it (the
+    # temporal workload measured 0.0838 ms per replay against 0.0811 ms
+    # eagerly) and runs eagerly.
+    eager = {"ms_per_step": ms_per_step, "step_ms_events": pct(step_ms)}
+    graph_info = None
+    if wl.graph and len(wl.parts) > 1 and not args.eager:
+        ref = [t.clone() for t in wl.outputs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _, fn in wl.parts:
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _, fn in wl.parts:
+                fn()
+        for _ in range(args.warmup):
+            graph.replay()
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gev[0].record()
+        for k in range(K):
+            graph.replay()
+            gev[k + 1].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i, (a, b) in enumerate(zip(ref, wl.outputs)):
+            if not torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)):
+                raise RuntimeError(f"graph replay: output {i} differs from the eager step")
+        del graph
+        ms_per_step = (t1 - t0) * 1e3 / K
+        step_ms = np.array([gev[k].elapsed_time(gev[k + 1]) for k in range(K)])
+        graph_info = {"replays": K, "outputs_checked": len(ref)}
 
     # cold: a 1 GiB write before each step evicts the inputs from L2 and
     # the memory-side cache, so the step starts from HBM
@@ -948,6 +1008,10 @@ def main():
         "samples_per_step": wl.samples,
         "batch_items_per_s": wl.batch / (ms_per_step * 1e-3),
         "step_ms_events": pct(step_ms),
+        # how the timed steps were launched; the breakdown and the kernel
+        # figures always come from the eager steps' events
+        "launch": ({"mode": "hip graph, one replay per step", **graph_info, "eager": eager} if graph_info
+                   else {"mode": "eager, one library call per part"}),
         "breakdown": breakdown,
         "cold": cold,
     }
