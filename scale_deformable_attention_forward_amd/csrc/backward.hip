@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave) void msda_backward_kernel(Back
 // ---------------------------------------------------------------------------
 // SCA: item = entry of the compaction's work list; the wave runs all cameras
 // of its query, sums the offset and logit gradients over them, and writes
-// them once.  Queries no camera sees get zero gradients at the end.
+// them once.  Queries no camera sees get zero gradients first.
 // ---------------------------------------------------------------------------
 // For L*P > 32 the kernel is held to 2 waves per SIMD (256 registers).
 template <bool kBF16, int kSPL, bool kEmit>
@@ -385,6 +385,23 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave, kSPL == 8 ? 2 : 1) void sca_ba
   if (kEmit) load_corner_starts(m.lv, a.L, ext);
   const int64_t n_queries = a.B * a.Nq;
   const uint32_t cam_bits = a.Ncam >= 32 ? 0xffffffffu : ((1u << a.Ncam) - 1u);
+
+  // Queries no camera sees are on no work list: their gradients are zero.
+  // One wave-wide mask load covers 64 queries, before the wave's work.
+  {
+    const int64_t per_q = (int64_t)a.nH * a.LP;
+    const int64_t n_waves = (int64_t)gridDim.x * waves_per_block;
+    for (int64_t q0 = ((int64_t)blockIdx.x * waves_per_block + wave) * kWave; q0 < n_queries; q0 += n_waves * kWave) {
+      const bool unseen = q0 + lane < n_queries && (a.cammask[q0 + lane] & cam_bits) == 0u;
+      for (uint64_t u = __ballot(unseen); u != 0ull; u &= u - 1ull) {
+        const int64_t bq = q0 + __builtin_ctzll(u);
+        for (int64_t e = lane; e < per_q; e += kWave) {
+          reinterpret_cast<float2*>(a.grad_offsets)[bq * per_q + e] = make_float2(0.f, 0.f);
+          a.grad_logits[bq * per_q + e] = 0.f;
+        }
+      }
+    }
+  }
 
   for (int64_t bi = 0; bi < a.B; ++bi) {
     const DieShare split(a.die_bounds + bi * kDieBounds, n_queries, waves_per_block);
@@ -480,16 +497,6 @@ __global__ __launch_bounds__(kBwdMaxWaves* kWave, kSPL == 8 ? 2 : 1) void sca_ba
     }
   }
 
-  // queries no camera sees are on no work list: their gradients are zero
-  const int64_t per_q = (int64_t)a.nH * a.LP;
-  const int64_t waves = (int64_t)gridDim.x * waves_per_block;
-  for (int64_t bq = (int64_t)blockIdx.x * waves_per_block + wave; bq < n_queries; bq += waves) {
-    if ((a.cammask[bq] & cam_bits) != 0u) continue;
-    for (int64_t e = lane; e < per_q; e += kWave) {
-      reinterpret_cast<float2*>(a.grad_offsets)[bq * per_q + e] = make_float2(0.f, 0.f);
-      a.grad_logits[bq * per_q + e] = 0.f;
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------

@@ -546,7 +546,7 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
 // once, grouped by first camera and image tile); the wave runs all cameras
 // of its query and averages them in registers, so each query is written
 // once, by one wave, and no atomics are needed.  Rows of queries that no
-// camera sees are zeroed at the end.
+// camera sees are zeroed first.
 // ---------------------------------------------------------------------------
 // For L*P <= 32 the kernel is held to 128 VGPRs, 4 waves per SIMD (the LDS
 // allows 4): the fp32 and bf16 variants fit; the head-pair one spills a few
@@ -566,6 +566,22 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void s
   const uint32_t row_bytes = kBF16 ? 64u : 128u;
   const int64_t n_queries = a.B * a.Nq;
   const uint32_t cam_bits = a.Ncam >= 32 ? 0xffffffffu : ((1u << a.Ncam) - 1u);
+
+  // Queries no camera sees are on no work list: their rows are zero.  One
+  // wave-wide mask load covers 64 queries, before the wave's gathers (a loop
+  // of one query per wave after them waited for each load in turn, on the
+  // kernel's tail).
+  {
+    const int64_t row4 = (int64_t)a.nH * 8;  // float4s per output row
+    const int64_t n_waves = (int64_t)gridDim.x * waves_per_block;
+    for (int64_t q0 = ((int64_t)blockIdx.x * waves_per_block + wave) * kWave; q0 < n_queries; q0 += n_waves * kWave) {
+      const bool unseen = q0 + lane < n_queries && (a.cammask[q0 + lane] & cam_bits) == 0u;
+      for (uint64_t m = __ballot(unseen); m != 0ull; m &= m - 1ull) {
+        float4* dst = reinterpret_cast<float4*>(a.out + (q0 + __builtin_ctzll(m)) * a.nH * 32);
+        for (int64_t e = lane; e < row4; e += kWave) dst[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
 
   // Batch item by batch item, each die takes its share of the item's work
   // list (contiguous, of equal estimated cost), so the dies share one item's
@@ -634,14 +650,6 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void s
   }
   }
 
-  // queries no camera sees are on no pair list: their rows are zero
-  const int64_t row4 = (int64_t)a.nH * 8;
-  const int64_t waves = (int64_t)gridDim.x * waves_per_block;
-  for (int64_t bq = (int64_t)blockIdx.x * waves_per_block + wave; bq < a.B * a.Nq; bq += waves) {
-    if ((a.cammask[bq] & cam_bits) != 0u) continue;
-    float4* dst = reinterpret_cast<float4*>(a.out + bq * a.nH * 32);
-    for (int64_t e = lane; e < row4; e += kWave) dst[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
 }
 
 // ---------------------------------------------------------------------------
