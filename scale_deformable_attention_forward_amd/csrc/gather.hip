@@ -549,9 +549,7 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave) void msda_gather_kernel(G
 // camera sees are zeroed first.
 // ---------------------------------------------------------------------------
 // For L*P <= 32 the kernel is held to 128 VGPRs, 4 waves per SIMD (the LDS
-// allows 4): the fp32 and bf16 variants fit; the head-pair one spills a few
-// registers outside its load loop and still measures about 9% faster than
-// unbounded at 139 VGPRs and 3 waves.
+// allows 4): the fp32, bf16 and head-pair variants fit (126, 116, 128).
 // kPairs: bf16 value in the head-pair layout (sample_pairs, gather_pairs).
 template <bool kBF16, int kSPL, bool kPairs>
 __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void sca_gather_kernel(GatherArgs a) {
