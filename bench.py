@@ -26,7 +26,8 @@ float32 atomics instead; the roofline then describes the backward kernel),
 "detr" (Deformable-DETR encoder MSDA: each step builds the locality plan
 from the sampling locations and runs the planned gather; "detr_unplanned"
 the queries in input order), "tsa" (two stacked BEV maps, frame mean, the
-BEV-grid queries in raster order; "tsa_planned" with a plan in every step),
+BEV-grid queries in raster order; "tsa_planned" with a plan in every step,
+"tsa_gridplan" with one built from the BEV grid before the timed steps),
 "sca_frame6" (one frame of the encoder: one compaction serving six SCA
 layers, each with its own value maps, offsets and logits), "tiny".
 
@@ -776,9 +777,11 @@ def msda_workload(which):
 
     # the DETR encoder's queries are placed at random: its default runs the
     # plan (inside every step); the temporal workload's BEV-grid queries
-    # come in raster order and run as given (its plan: "tsa_planned")
-    planned = which in ("detr", "tsa_planned")
-    base = which.replace("_unplanned", "").replace("_planned", "")
+    # come in raster order and run as given (its plan: "tsa_planned" in every
+    # step, "tsa_gridplan" once, from the grid cells' centres, before the
+    # timed steps: the grid, and so the plan, never changes)
+    planned = which in ("detr", "tsa_planned", "tsa_gridplan")
+    base = which.replace("_unplanned", "").replace("_planned", "").replace("_gridplan", "")
     if base == "detr":
         w, F = W.detr_encoder_msda(), 1
     elif base == "tiny":
@@ -797,7 +800,15 @@ def msda_workload(which):
         # part of every step
         row = nH * L * P * 2
         plan = torch.empty(m.msda_plan_size(B, Nq), dtype=torch.uint8, device="cuda")
-        wl.parts.append(("plan", lambda: m.msda_plan(d["sampling_locations"], B, Nq, F * Nq * row, row, plan=plan)))
+        if which == "tsa_gridplan":
+            side = int(round(Nq ** 0.5))
+            c = (np.arange(side, dtype=np.float32) + 0.5) / side
+            cx, cy = np.meshgrid(c, c)  # q = row * side + col
+            cells = torch.from_numpy(np.stack([cx.ravel(), cy.ravel()], -1)).cuda().expand(B, Nq, 2).contiguous()
+            m.msda_plan(cells, B, Nq, Nq * 2, 2, plan=plan)
+        else:
+            wl.parts.append(("plan", lambda: m.msda_plan(d["sampling_locations"], B, Nq, F * Nq * row, row,
+                                                         plan=plan)))
         wl.parts.append(("gather", lambda: m.msda_gather(*args, plan, out=out)))
     else:
         fn = m.msda_forward if F == 1 else m.msda_forward_frames
@@ -822,8 +833,9 @@ def msda_workload(which):
     names = {"detr": "Deformable-DETR encoder MSDA, 4 levels 100x150/50x75/25x38/13x19, Nq=Nv=19947",
              "tiny": "tiny MSDA, 256 queries, one 32x32 level",
              "tsa": "temporal self-attention, 2 stacked 200x200 BEV maps, mean over frames"}
-    wl.config = {"workload": names[base] + (", locality plan + planned gather" if planned
-                                            else ", queries in input order (no plan)"),
+    order = {"tsa_gridplan": ", planned gather (locality plan built once from the BEV grid, outside the step)"}
+    wl.config = {"workload": names[base] + order.get(which, ", locality plan + planned gather" if planned
+                                                     else ", queries in input order (no plan)"),
                  "batch": B, "queries": Nq, "heads": nH, "head_dim": 32,
                  "levels": L, "points_per_level": P, "frames": F, "value_dtype": "fp32"}
     wl.dtype = "fp32"
@@ -842,7 +854,7 @@ def main():
                     choices=["sca", "layer_bf16", "layer_full", "layer_bf16_plain", "sca_bf16", "sca_rebatch",
                              "sca_train", "detr",
                              "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny", "sca_frame6",
-                             "tsa_train", "tsa_train_atomic", "detr_unplanned", "tsa_planned"])
+                             "tsa_train", "tsa_train_atomic", "detr_unplanned", "tsa_planned", "tsa_gridplan"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-onchip-ceiling", action="store_true",
                     help="skip the L2-resident run of the main kernel behind roofline_onchip")
