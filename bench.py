@@ -25,7 +25,9 @@ deterministic transpose gather; "_atomic" variants accumulate it with
 float32 atomics instead; the roofline then describes the backward kernel),
 "detr" (Deformable-DETR encoder MSDA: each step builds the locality plan
 from the sampling locations and runs the planned gather; "detr_unplanned"
-the queries in input order), "tsa" (two stacked BEV maps, frame mean, the
+the queries in input order; "detr_encoder6" one pass of the six-layer
+encoder: the plan built once from the shared reference points before the
+timed steps, then six layers' planned gathers), "tsa" (two stacked BEV maps, frame mean, the
 BEV-grid queries in raster order; "tsa_planned" with a plan in every step,
 "tsa_gridplan" with one built from the BEV grid before the timed steps),
 "sca_frame6" (one frame of the encoder: one compaction serving six SCA
@@ -240,8 +242,9 @@ def sca_cpu_baseline(w, kind, cores=None, sampled_queries=4000):
     return time_oracle(phases, _sca_samples(w, rows), what, cores)
 
 
-def msda_cpu_baseline(w, cores=None):
-    """The oracle's MSDA operator (or frame mean) over the whole workload."""
+def msda_cpu_baseline(w, cores=None, first_of=1):
+    """The oracle's MSDA operator (or frame mean) over the whole workload (of
+    its first layer when a step runs `first_of` layers)."""
     import oracle
     k = 4 * (cores or len(os.sched_getaffinity(0)))
     B, Nq, nH, L, P = w["B"], w["Nq"], w["nH"], w["L"], w["P"]
@@ -249,7 +252,9 @@ def msda_cpu_baseline(w, cores=None):
     args = (w["value"], w["spatial_shapes"], w["level_start_index"], w["sampling_locations"], w["attention_weights"])
     fn = oracle.msda if F == 1 else oracle.msda_frames
     tasks = [lambda r=r: fn(*args, True, rows=r) for r in _query_chunks(B * Nq, k)]
-    return time_oracle([tasks], B * F * Nq * nH * L * P, f"the whole workload: all {B * Nq} queries", cores)
+    what = f"the whole workload: all {B * Nq} queries" + (f" of the first of the {first_of} layers" if first_of > 1
+                                                              else "")
+    return time_oracle([tasks], B * F * Nq * nH * L * P, what, cores)
 
 
 def train_cpu_baseline(w, which, grad, cores=None):
@@ -780,8 +785,12 @@ def msda_workload(which):
     # come in raster order and run as given (its plan: "tsa_planned" in every
     # step, "tsa_gridplan" once, from the grid cells' centres, before the
     # timed steps: the grid, and so the plan, never changes)
-    planned = which in ("detr", "tsa_planned", "tsa_gridplan")
-    base = which.replace("_unplanned", "").replace("_planned", "").replace("_gridplan", "")
+    # "detr_encoder6": one pass of the six-layer encoder, its plan built once
+    # from the reference points (which every layer shares) before the timed
+    # steps, then the six layers' planned gathers
+    planned = which in ("detr", "tsa_planned", "tsa_gridplan", "detr_encoder6")
+    layers = 6 if which == "detr_encoder6" else 1
+    base = which.replace("_unplanned", "").replace("_planned", "").replace("_gridplan", "").replace("_encoder6", "")
     if base == "detr":
         w, F = W.detr_encoder_msda(), 1
     elif base == "tiny":
@@ -806,6 +815,8 @@ def msda_workload(which):
             cx, cy = np.meshgrid(c, c)  # q = row * side + col
             cells = torch.from_numpy(np.stack([cx.ravel(), cy.ravel()], -1)).cuda().expand(B, Nq, 2).contiguous()
             m.msda_plan(cells, B, Nq, Nq * 2, 2, plan=plan)
+        elif which == "detr_encoder6":
+            m.msda_plan(_dev(w["reference_points"]), B, Nq, Nq * 2, 2, plan=plan)
         else:
             wl.parts.append(("plan", lambda: m.msda_plan(d["sampling_locations"], B, Nq, F * Nq * row, row,
                                                          plan=plan)))
@@ -813,19 +824,31 @@ def msda_workload(which):
     else:
         fn = m.msda_forward if F == 1 else m.msda_forward_frames
         wl.parts.append(("gather", lambda: fn(*args, out=out)))
+    # layers 2..6: their own value maps, locations (the same reference
+    # points, the offsets scaled) and weights, derived from the first
+    # layer's on the device: synthetic, like it
+    ref = _dev(w["reference_points"])[:, :, None, None, None, :] if layers > 1 else None
+    for li in range(1, layers):
+        v_l = torch.roll(d["value"], shifts=997 * li, dims=1).contiguous()
+        s_l = (ref + (d["sampling_locations"] - ref) * (1.0 - 0.1 * li)).contiguous()
+        a_l = torch.roll(d["attention_weights"], shifts=li, dims=-1).contiguous()
+        o_l = torch.empty_like(out)
+        wl.parts.append((f"gather_{li + 1}", lambda v_l=v_l, s_l=s_l, a_l=a_l, o_l=o_l: m.msda_gather(
+            v_l, d["spatial_shapes"], d["level_start_index"], s_l, a_l, plan, out=o_l)))
     wl.main = "gather"
     wl.outputs = [out]
 
     def finish():
-        wl.samples = B * F * Nq * nH * L * P
+        wl.samples = B * F * Nq * nH * L * P * layers
         ss = w["spatial_shapes"]
         loc = w["sampling_locations"]
         Wd = ss[:, 1].astype(np.float64)[:, None]
         H = ss[:, 0].astype(np.float64)[:, None]
         wl.inbounds_corners = count_inbounds(ss, loc[..., 0] * Wd - 0.5, loc[..., 1] * H - 0.5)
-        wl.gathered_bytes = wl.samples * 4 * 32 * 4
-        wl.eff_bytes = wl.gathered_bytes + wl.samples * (8 + 4) + B * Nq * nH * 32 * 4
-        wl.unique_bytes = w["value"].nbytes + wl.samples * (8 + 4) + B * Nq * nH * 32 * 4
+        launch = wl.samples // layers  # one gather launch (the first layer's)
+        wl.gathered_bytes = launch * 4 * 32 * 4
+        wl.eff_bytes = wl.gathered_bytes + launch * (8 + 4) + B * Nq * nH * 32 * 4
+        wl.unique_bytes = w["value"].nbytes + launch * (8 + 4) + B * Nq * nH * 32 * 4
         if base != "tiny":  # the tiny parity workload is launch-bound: no on-chip ceiling to speak of
             wl.onchip = lambda: msda_onchip_ceiling(w, d, F, plan if planned else None)
     wl.finish = finish
@@ -833,7 +856,10 @@ def msda_workload(which):
     names = {"detr": "Deformable-DETR encoder MSDA, 4 levels 100x150/50x75/25x38/13x19, Nq=Nv=19947",
              "tiny": "tiny MSDA, 256 queries, one 32x32 level",
              "tsa": "temporal self-attention, 2 stacked 200x200 BEV maps, mean over frames"}
-    order = {"tsa_gridplan": ", planned gather (locality plan built once from the BEV grid, outside the step)"}
+    order = {"tsa_gridplan": ", planned gather (locality plan built once from the BEV grid, outside the step)",
+             "detr_encoder6": ", one encoder pass: a locality plan built once from the reference points (outside "
+                              "the step), then 6 layers' planned gathers, each with its own value map, locations "
+                              "and weights"}
     wl.config = {"workload": names[base] + order.get(which, ", locality plan + planned gather" if planned
                                                      else ", queries in input order (no plan)"),
                  "batch": B, "queries": Nq, "heads": nH, "head_dim": 32,
@@ -841,7 +867,7 @@ def msda_workload(which):
     wl.dtype = "fp32"
     wl.kernel_key = "msda_gather_kernel_fp32"
 
-    wl.cpu_baseline = lambda: msda_cpu_baseline(w)
+    wl.cpu_baseline = lambda: msda_cpu_baseline(w, first_of=layers)
     return wl
 
 
@@ -854,7 +880,8 @@ def main():
                     choices=["sca", "layer_bf16", "layer_full", "layer_bf16_plain", "sca_bf16", "sca_rebatch",
                              "sca_train", "detr",
                              "detr_train", "sca_train_atomic", "detr_train_atomic", "tsa", "tiny", "sca_frame6",
-                             "tsa_train", "tsa_train_atomic", "detr_unplanned", "tsa_planned", "tsa_gridplan"])
+                             "tsa_train", "tsa_train_atomic", "detr_unplanned", "tsa_planned", "tsa_gridplan",
+                             "detr_encoder6"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-onchip-ceiling", action="store_true",
                     help="skip the L2-resident run of the main kernel behind roofline_onchip")

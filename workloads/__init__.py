@@ -69,7 +69,8 @@ def msda_workload(cfg, B, Nq, shapes, nH=8, Dh=32, P=4, value_bf16=False, ref="u
     (ref="uniform") or the BEV cell centre of the query (ref="grid", square
     grid of sqrt(Nq) cells); each (head, level, point) location is the
     reference point plus N(0, offset_px cells of that level) scatter;
-    logits ~ N(0,1) [B,Nq,nH,L*P].
+    logits ~ N(0,1) [B,Nq,nH,L*P]; the reference points [B,Nq,2] are
+    returned too.
     """
     ss, starts, Nv = level_table(shapes)
     L = len(ss)
@@ -86,6 +87,7 @@ def msda_workload(cfg, B, Nq, shapes, nH=8, Dh=32, P=4, value_bf16=False, ref="u
     logits = _normal(g, (B, Nq, nH, L * P))
     return {"value": value, "spatial_shapes": ss, "level_start_index": starts,
             "sampling_locations": loc.astype(np.float32), "attention_weights": logits,
+            "reference_points": r.astype(np.float32),
             "B": B, "Nq": Nq, "Nv": Nv, "nH": nH, "Dh": Dh, "L": L, "P": P}
 
 
