@@ -78,11 +78,14 @@ def test_random_msda_forward_and_backward(seed):
         assert_fp32_close(gw, rw, what + ": grad weights")
 
 
-def _sca_case(seed):
-    g = np.random.default_rng(np.random.SeedSequence([901, seed]))
+def _sca_case(seed, large=False):
+    g = np.random.default_rng(np.random.SeedSequence([902 if large else 901, seed]))
     nH, L, P, shapes = _draw_shape(g)
     D = int(g.choice([d for d in (1, 2, 3, 4) if P % d == 0]))
-    B, Ncam, Nq = int(g.integers(1, 4)), int(g.integers(1, 9)), int(g.integers(1, 300))
+    if large:  # many query tiles and cameras: every tile's queries start in many segments
+        B, Ncam, Nq = int(g.integers(1, 4)), int(g.integers(4, 33)), int(g.integers(300, 3000))
+    else:
+        B, Ncam, Nq = int(g.integers(1, 4)), int(g.integers(1, 9)), int(g.integers(1, 300))
     ss, starts, Nv = W.level_table(shapes)
     value = g.normal(size=(B, Ncam, Nv, nH, 32)).astype(np.float32)
     if g.random() < 0.3:
@@ -131,3 +134,24 @@ def test_random_sca_forward_and_backward(seed):
         assert_sum_close(gv, rv, mag, what + ": grad value")
         assert_fp32_close(go, ro, what + ": grad offsets")
         assert_fp32_close(gl, rl, what + ": grad logits")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_sca_many_tiles_and_cameras(seed):
+    """Forward only, at up to 3,000 queries (a dozen query tiles) and up to
+    32 cameras: the compaction's pair lists, offsets and hit counts bit for
+    bit, the slots element by element."""
+    c = _sca_case(seed, large=True)
+    B, Ncam, Nq = c["B"], c["Ncam"], c["Nq"]
+    hit = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
+    offs = torch.empty(B * Ncam + 1, dtype=torch.int32, device="cuda")
+    pq = torch.empty(B * Ncam * Nq, dtype=torch.int32, device="cuda")
+    d = {k: dev(c[k]) for k in ("value", "ss", "starts", "rho", "mask", "off", "logits")}
+    slots = msda.sca_forward(d["value"], d["ss"], d["starts"], d["rho"], d["mask"], d["off"], d["logits"],
+                             hit_count=hit, pair_offsets=offs, pair_q=pq)
+    ref = oracle.sca(c["value"], c["ss"], c["starts"], c["rho"], c["mask"], c["off"], c["logits"])
+    assert np.array_equal(host(hit), ref["hit_count"]), f"case {seed}: hit counts"
+    assert np.array_equal(host(offs), ref["pair_offsets"]), f"case {seed}: pair offsets"
+    n = int(ref["pair_offsets"][-1])
+    assert np.array_equal(host(pq)[:n], ref["pair_q"]), f"case {seed}: pair lists"
+    assert_fp32_close(host(slots).reshape(B * Nq, -1), ref["slots"], f"case {seed}: slots")
