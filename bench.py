@@ -38,8 +38,10 @@ Prints one JSON line.  value = bilinear samples per second (one sample = one
 channels) over the whole step.  The K timed steps run eagerly, one library
 call per part with HIP events between the parts; a step of more than one
 call then runs again as K replays of the step captured once in a HIP graph
-(one launch per step; the replays must reproduce the eager outputs bit for
-bit), and ms_per_step and value come from the replays' wall-clock time
+(one launch per step; the replays, run on outputs first overwritten, must
+reproduce the eager outputs bit for bit, checked after the warm-up replays
+and again after the timed ones), and ms_per_step and value come from the
+replays' wall-clock time
 (launch.eager holds the eager figures; --eager times the eager steps only,
 and the padded rebatch flow, which reads a length back to the host, always
 runs eagerly).  Kernel figures come from the eager steps' HIP events,
@@ -968,8 +970,18 @@ def main():
         with torch.cuda.graph(graph):
             for _, fn in wl.parts:
                 fn()
-        for _ in range(args.warmup):
+        def check(when):
+            for i, (a, b) in enumerate(zip(ref, wl.outputs)):
+                if not torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)):
+                    raise RuntimeError(f"graph replay: output {i} differs from the eager step ({when})")
+
+        # the outputs overwritten first, so that the replays must write them
+        for t in wl.outputs:
+            t.fill_(float("nan") if t.is_floating_point() else -7)
+        for _ in range(max(1, args.warmup)):
             graph.replay()
+        torch.cuda.synchronize()
+        check("warm-up replays")
         gev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -979,9 +991,7 @@ def main():
             gev[k + 1].record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        for i, (a, b) in enumerate(zip(ref, wl.outputs)):
-            if not torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)):
-                raise RuntimeError(f"graph replay: output {i} differs from the eager step")
+        check("timed replays")
         del graph
         ms_per_step = (t1 - t0) * 1e3 / K
         step_ms = np.array([gev[k].elapsed_time(gev[k + 1]) for k in range(K)])
