@@ -291,6 +291,8 @@ SCA_EDGE = [
     ("thirty_two_cameras", 24, 1, 32, 40, ((4, 6),), 8, 2, 1, 0.2),
     # every tile's queries start in many cameras: the compaction scans many segments per tile
     ("thirty_two_cameras_multi_tile", 31, 2, 32, 600, ((4, 6),), 8, 2, 1, 0.04),
+    # many batch items: 240 segments, die shares per item, pair offsets across items
+    ("forty_batch_items", 32, 40, 6, 60, ((5, 7), (3, 4)), 8, 4, 2, 0.3),
     ("anchor_per_point_D1_P3", 25, 1, 4, 30, ((5, 7), (2, 3)), 8, 3, 1, 0.4),
     ("half_heads_nH4", 26, 2, 3, 45, ((6, 6),), 4, 4, 2, 0.3),
     ("two_passes_nH16", 27, 1, 3, 25, ((6, 6),), 16, 4, 4, 0.3),
