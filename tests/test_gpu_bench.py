@@ -24,13 +24,16 @@ def run_bench(*args):
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
-@pytest.mark.parametrize("workload,graph", [("detr", True), ("tsa", False)])
+@pytest.mark.parametrize("workload,graph", [("detr", True), ("tsa", False), ("detr_encoder6", True),
+                                            ("tsa_gridplan", False)])
 def test_bench_line(workload, graph):
     announce(f"bench.py --workload {workload}")
     d = run_bench("--workload", workload)
     assert d["metric"] and d["unit"] == "samples/s" and d["n_gpus"] == 1 and d["steps"] == 3
     assert d["value"] > 0 and d["ms_per_step"] > 0
     assert abs(d["value"] - d["samples_per_step"] / (d["ms_per_step"] * 1e-3)) <= 1e-6 * d["value"]
+    layers = 6 if workload == "detr_encoder6" else 1
+    assert len(d["breakdown"]) == layers + (1 if workload == "detr" else 0)
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and 0 < r["frac"] <= 1
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-12
