@@ -62,3 +62,75 @@ def test_graph_replays_match_eager(case):
             assert a.shape == b.shape and a.dtype == b.dtype, (replay, i)
             assert a.tobytes() == b.tobytes(), f"replay {replay}: output {i} differs from the eager result"
     del graph
+
+
+def test_whole_sca_layer_in_one_graph():
+    """One spatial cross-attention layer as a single graph: sampling offsets
+    and logits from the query, the value projection into the head-pair
+    layout, the compaction, the gather with its camera mean, and the output
+    projection with the residual and layer norm.  Every intermediate and the
+    layer output must equal the eager run bit for bit on every replay."""
+    import numpy as np
+
+    import workloads as W
+    from test_gpu_parity import _rand_sca
+
+    B, Ncam, Nq, nH, P, D, C = 2, 3, 400, 8, 4, 4, 256
+    w = _rand_sca(77, B, Ncam, Nq, ((12, 20), (6, 10)), nH, P, D, 0.3)
+    L, Nv = w["L"], w["Nv"]
+    g = np.random.default_rng(78)
+    bf = lambda a: W.bf16_bits_trunc(a.astype(np.float32))
+    t = {k: dev(v) for k, v in {
+        "feats": bf(g.normal(size=(B * Ncam * Nv, C))), "w_v": bf(g.normal(0, 1 / 16, (C, C))),
+        "b_v": g.normal(size=C).astype(np.float32),
+        "query": g.normal(size=(B * Nq, C)).astype(np.float32), "pos": g.normal(size=(B * Nq, C)).astype(np.float32),
+        "w_off": bf(g.normal(0, 1 / 16, (nH * L * P * 2, C))), "b_off": g.normal(size=nH * L * P * 2).astype(np.float32),
+        "w_att": bf(g.normal(0, 1 / 16, (nH * L * P, C))), "b_att": g.normal(size=nH * L * P).astype(np.float32),
+        "w_o": bf(g.normal(0, 1 / 16, (C, C))), "b_o": g.normal(size=C).astype(np.float32),
+        "gamma": g.uniform(0.5, 1.5, C).astype(np.float32), "beta": g.normal(size=C).astype(np.float32),
+        "ss": w["spatial_shapes"], "starts": w["level_start_index"], "rho": w["reference_points_cam"],
+        "mask": w["bev_mask"]}.items()}
+    dv = t["query"].device
+    o = {"off": torch.empty((B * Nq, nH * L * P * 2), dtype=torch.float32, device=dv),
+         "logits": torch.empty((B * Nq, nH * L * P), dtype=torch.float32, device=dv),
+         "value": torch.empty((B * Ncam, nH, Nv, 2, 32), dtype=torch.bfloat16, device=dv),
+         "ws": torch.empty(msda.sca_workspace_size(B, Ncam, Nq), dtype=torch.uint8, device=dv),
+         "slots": torch.empty((B, Nq, C), dtype=torch.float32, device=dv),
+         "y": torch.empty((B * Nq, C), dtype=torch.float32, device=dv)}
+
+    def layer():
+        msda.msda_query_proj_bf16(t["query"], t["w_off"], t["b_off"], t["w_att"], t["b_att"], query_pos=t["pos"],
+                                  offsets=o["off"], logits=o["logits"])
+        msda.msda_value_proj_pairs_bf16(t["feats"], t["w_v"], t["b_v"], Nv, out=o["value"])
+        msda.sca_compact(t["mask"], t["rho"], o["ws"])
+        msda.sca_gather(o["value"].view(B, Ncam, nH, Nv, 2, 32), t["ss"], t["starts"], t["rho"],
+                        o["off"].view(B, Nq, nH, L, P, 2), o["logits"].view(B, Nq, nH, L * P), o["ws"],
+                        slots=o["slots"])
+        msda.msda_output_proj_bf16(o["slots"].view(B * Nq, C), t["w_o"], t["b_o"], residual=t["query"],
+                                   gamma=t["gamma"], beta=t["beta"], out=o["y"])
+
+    checked = ("off", "logits", "value", "slots", "y")
+    layer()
+    torch.cuda.synchronize()
+    ref = {k: host(o[k]) for k in checked}
+    assert np.isfinite(ref["y"]).all() and np.abs(ref["slots"]).max() > 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    for replay in range(3):
+        for k in checked + ("ws",):
+            o[k].fill_(float("nan") if o[k].is_floating_point() else 0x5A)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in checked:
+            assert ref[k].tobytes() == host(o[k]).tobytes(), f"replay {replay}: {k} differs from the eager result"
+    del graph
