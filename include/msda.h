@@ -15,6 +15,7 @@
  *   sca_backward_workspace_size              gradients of the MSDA operator (also of its
  *                                            frame mean) and of SCA
  *   msda_status_string, msda_last_error      status reporting
+ *   msda_check_counts                        bounds-check counters (checked build)
  *
  * Sources, cited by page title and section:
  *   [8-heads]  "BEV(三) BEVFormer：Query 参数如何与 Feature 的 8 个 Head 交互"
@@ -546,6 +547,27 @@ const char* msda_status_string(int status);
 /* Message of the calling thread's last non-OK return (host; valid until the
  * thread's next call into the library). */
 const char* msda_last_error(void);
+
+/* Device-side bounds checks (host; a debugging aid for every caller, not a
+ * passage of the pages).  libmsda_checked.so is the same library built with
+ * MSDA_CHECKED: its kernels check the compaction's pair-list and work-list
+ * writes against their segments, every work-list, plan and pair-list entry
+ * they read against the range it must lie in, and every corner row a gather
+ * stages against its sample's level and head.  A failed check adds one to a
+ * counter of its kind (MSDA_CHECK_*) on the device; nothing traps and no
+ * result changes.  msda_check_counts waits for the current device
+ * (hipDeviceSynchronize, unlike every other entry point), writes the
+ * counters summed over the library to counts[0 .. MSDA_CHECK_KINDS), and
+ * zeroes them when reset != 0.  counts must hold MSDA_CHECK_KINDS entries
+ * (else MSDA_ERR_INVALID_ARG).  In the regular libmsda.so it returns
+ * MSDA_ERR_UNSUPPORTED and touches nothing.  Counters are per device and
+ * shared by every call on it. */
+#define MSDA_CHECK_KINDS 4
+#define MSDA_CHECK_GATHER_ROW 0  /* staged corner row outside its sample's level or head */
+#define MSDA_CHECK_PAIR_WRITE 1  /* pair-list entry written outside its run, or a query outside [0, Nq) */
+#define MSDA_CHECK_ORDER_WRITE 2 /* work-list slot written outside its segment's range */
+#define MSDA_CHECK_LIST_ENTRY 3  /* work-list, plan, pair-list or segment-bound entry read out of its range */
+int msda_check_counts(unsigned long long* counts, int n, int reset);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,9 @@ Functions (same names as the C entry points):
                 head-pair layout that every forward entry point also takes)
   layout:       msda_pack_pairs_bf16 (a bf16 value rewritten in that layout)
   status:       msda_status_string, msda_last_error
+  checks:       msda_check_counts (the bounds-check counters of
+                libmsda_checked.so; use_library(checked_library_path())
+                switches the binding to that build)
 """
 import ctypes
 import functools
@@ -39,11 +42,14 @@ __all__ = [
     "msda_output_proj_bf16", "msda_value_proj_pairs_bf16", "msda_pack_pairs_bf16",
     "sca_rebatch", "sca_scatter_mean", "sca_forward_rebatch", "msda_backward_workspace_size",
     "sca_backward_workspace_size", "msda_backward", "msda_backward_frames", "sca_backward", "msda_status_string",
-    "msda_last_error",
+    "msda_last_error", "MSDA_CHECK_KINDS", "checked_library_path", "use_library", "msda_check_counts",
 ]
 
 MSDA_F32, MSDA_BF16, MSDA_BF16_PAIRS = 0, 1, 2
 MSDA_WEIGHTS_PROB, MSDA_WEIGHTS_LOGITS = 0, 1
+# kinds of the checked build's bounds-check counters (msda_check_counts)
+MSDA_CHECK_KINDS = 4
+CHECK_KIND_NAMES = ("gather_row", "pair_write", "order_write", "list_entry")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -63,12 +69,30 @@ def library_path():
     return os.path.join(_HERE, "libmsda.so")
 
 
+def checked_library_path():
+    """The in-tree build with device-side bounds checks (MSDA_CHECKED)."""
+    return os.path.join(_HERE, "libmsda_checked.so")
+
+
+_path = None  # set by use_library
+
+
+def use_library(path=None):
+    """Make every later call go through the library at `path` (None: the
+    regular libmsda.so); returns the path in use before."""
+    global _lib, _path
+    before = _path or library_path()
+    _path, _lib = path, None
+    return before
+
+
 def load_library():
-    """Load the in-tree libmsda.so (raises if it has not been built)."""
+    """Load the in-tree libmsda.so, or the library use_library() chose
+    (raises if it has not been built)."""
     global _lib
     if _lib is not None:
         return _lib
-    path = library_path()
+    path = _path or library_path()
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m scale_deformable_attention_forward_amd.build`")
@@ -115,6 +139,8 @@ def load_library():
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_last_error.argtypes = []
     lib.msda_last_error.restype = ctypes.c_char_p
+    lib.msda_check_counts.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), _int, _int]
+    lib.msda_check_counts.restype = _int
     _lib = lib
     return lib
 
@@ -125,6 +151,16 @@ def msda_status_string(code):
 
 def msda_last_error():
     return load_library().msda_last_error().decode()
+
+
+def msda_check_counts(reset=False):
+    """The bounds-check counters of libmsda_checked.so, summed over the
+    library, as {kind name: count} (waits for the current device; reset
+    zeroes them).  The regular library raises MsdaError
+    (MSDA_ERR_UNSUPPORTED)."""
+    counts = (ctypes.c_ulonglong * MSDA_CHECK_KINDS)()
+    _check("msda_check_counts", load_library().msda_check_counts(counts, MSDA_CHECK_KINDS, int(bool(reset))))
+    return dict(zip(CHECK_KIND_NAMES, (int(c) for c in counts)))
 
 
 def _check(fn, code):

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
+#include <vector>
 
 #include "backward.hpp"
 #include "gemm.hpp"
@@ -23,6 +24,27 @@ int msda::device_cu_count() {
     return 256;
   }();
   return cus;
+}
+
+namespace {
+
+// the counter readers of the translation units (checked builds; see
+// common.hpp), registered by their static initialisers at load time
+std::mutex& check_mutex() {
+  static std::mutex m;
+  return m;
+}
+std::vector<msda::CheckReader>& check_readers() {
+  static std::vector<msda::CheckReader> r;
+  return r;
+}
+
+}  // namespace
+
+bool msda::register_check_reader(CheckReader reader) {
+  std::lock_guard<std::mutex> lock(check_mutex());
+  check_readers().push_back(reader);
+  return true;
 }
 
 namespace {
@@ -111,6 +133,28 @@ const char* msda_status_string(int status) {
 }
 
 const char* msda_last_error(void) { return g_last_error; }
+
+int msda_check_counts(unsigned long long* counts, int n, int reset) {
+#ifndef MSDA_CHECKED
+  (void)counts;
+  (void)n;
+  (void)reset;
+  return fail(MSDA_ERR_UNSUPPORTED, "msda_check_counts: this library is built without device-side checks "
+              "(libmsda_checked.so has them)");
+#else
+  if (!counts || n < msda::kCheckKinds)
+    return fail(MSDA_ERR_INVALID_ARG, "counts must hold MSDA_CHECK_KINDS (%d) entries", msda::kCheckKinds);
+  for (int k = 0; k < n; ++k) counts[k] = 0;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_status(e, "hipDeviceSynchronize");
+  std::lock_guard<std::mutex> lock(check_mutex());
+  for (msda::CheckReader r : check_readers()) {
+    e = r(counts, reset != 0);
+    if (e != hipSuccess) return hip_status(e, "reading the check counters");
+  }
+  return MSDA_OK;
+#endif
+}
 
 static int msda_frames_impl(const void* value, int value_dtype, const int64_t* spatial_shapes,
                             const int64_t* level_start_index, const float* sampling_locations,

@@ -48,6 +48,48 @@ __device__ inline int64_t uniform(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Checked builds (compiled with -DMSDA_CHECKED into libmsda_checked.so):
+// device-side bounds checks on the compaction's writes, on the work-list,
+// plan and pair-list entries the kernels read, and on every corner row a
+// gather stages.  A failed check adds one to a per-kind counter in device
+// memory (a vector atomic; nothing traps and no result changes), which
+// msda_check_counts reads back.  In the regular build MSDA_CHECK evaluates
+// nothing.
+constexpr int kCheckKinds = 4;
+enum CheckKind {
+  kCheckGatherRow = 0,    // a staged corner row outside its sample's level or image
+  kCheckPairWrite = 1,    // a pair-list entry written outside its tile's range, or a query index outside [0, Nq)
+  kCheckOrderWrite = 2,   // a work-list slot written outside [0, B*Nq) or its segment's range
+  kCheckListEntry = 3,    // a work-list, plan, pair-list or segment-bound entry read that had to be clamped
+};
+// Adds a translation unit's counters to counts (and zeroes them when reset);
+// the readers of every unit are registered at load time (abi.hip).
+typedef hipError_t (*CheckReader)(unsigned long long* counts, bool reset);
+bool register_check_reader(CheckReader reader);
+
+#ifdef MSDA_CHECKED
+static __device__ unsigned long long g_check_counts[kCheckKinds];
+#define MSDA_CHECK(kind, cond)                                                 \
+  do {                                                                         \
+    if (!(cond)) atomicAdd(&::msda::g_check_counts[(kind)], 1ull);             \
+  } while (0)
+static hipError_t read_check_counts(unsigned long long* counts, bool reset) {
+  unsigned long long h[kCheckKinds];
+  hipError_t e = hipMemcpyFromSymbol(h, HIP_SYMBOL(g_check_counts), sizeof h, 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  for (int k = 0; k < kCheckKinds; ++k) counts[k] += h[k];
+  if (!reset) return hipSuccess;
+  const unsigned long long zero[kCheckKinds] = {};
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_check_counts), zero, sizeof zero, 0, hipMemcpyHostToDevice);
+}
+[[maybe_unused]] static const bool g_check_reader_registered = register_check_reader(&read_check_counts);
+#else
+#define MSDA_CHECK(kind, cond) \
+  do {                         \
+    (void)sizeof(cond);        \
+  } while (0)
+#endif
+
 // Work split for a grid whose size is a multiple of kXcds.  The hardware
 // hands workgroups to the dies round-robin (block i -> die i % 8), so die x
 // owns the contiguous item range [N*x/8, N*(x+1)/8) and walks it with all of
@@ -78,6 +120,7 @@ struct DieShare {
     const int nlocal = gridDim.x / kXcds;
     const int wave = uniform(threadIdx.x / kWave);
     int64_t lo = bounds[xcd], hi = bounds[xcd + 1];
+    MSDA_CHECK(kCheckListEntry, lo >= 0 && lo <= hi && hi <= n_items);
     lo = lo < 0 ? 0 : (lo > n_items ? n_items : lo);
     hi = hi < lo ? lo : (hi > n_items ? n_items : hi);
     begin = lo + (int64_t)local * waves_per_block + wave;

@@ -335,6 +335,9 @@ __device__ void tile_compact(const CompactArgs& a, int b, int tile, int tiles) {
     if ((seen >> c) & 1u) {
       int r = __popcll(bits & below);
       for (int w = 0; w < wave; ++w) r += wave_counts[w][c];
+      // the tile's count from the visibility kernel bounds its run of (b, c)'s list
+      MSDA_CHECK(kCheckPairWrite, q < a.Nq && r < a.tile_counts[(int64_t)(b * a.Ncam + c) * tiles + tile] &&
+                                      (int64_t)tile_start[c] + r < (int64_t)a.B * a.Ncam * a.Nq);
       a.pair_q[tile_start[c] + r] = q;
     }
   }
@@ -354,7 +357,15 @@ __device__ void tile_compact(const CompactArgs& a, int b, int tile, int tiles) {
     bin_first[kBinsPerThread * t + 2] = at + n4.x + n4.y;
     bin_first[kBinsPerThread * t + 3] = at + n4.x + n4.y + n4.z;
     __syncthreads();
-    if (first == c) a.order[bin_first[key - s * kOrderBins] + rank] = (int32_t)bq;
+    if (first == c) {
+      const int bin = key - s * kOrderBins;
+      MSDA_CHECK(kCheckOrderWrite, bin >= 0 && bin < kOrderBins);
+      const int slot = bin_first[bin < 0 ? 0 : (bin < kOrderBins ? bin : kOrderBins - 1)] + rank;
+      // the segment's seen queries fill [seen_before, seen_before + total) of the list
+      MSDA_CHECK(kCheckOrderWrite, slot >= seen_before[c] && slot < seen_before[c] + total &&
+                                       (int64_t)slot < (int64_t)a.B * a.Nq);
+      a.order[slot] = (int32_t)bq;
+    }
     __syncthreads();  // bin_first is rewritten for the next segment
   }
 }

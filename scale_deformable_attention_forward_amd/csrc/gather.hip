@@ -114,6 +114,24 @@ __device__ inline void sample_pairs(uint2 (&c)[4], double x, double y, float alp
   }
 }
 
+// Checked builds: a staged corner (byte offset within its image) names a
+// pixel of its sample's level, in head h's row (or, in the head-pair layout,
+// head h's line of pixel p, whose right half holds pixel p + 1).
+template <bool kPairs>
+__device__ inline bool corner_in_level(uint32_t off, const Level& lv, int h, int nH, int Nv, uint32_t row_bytes) {
+  long long pix;
+  if constexpr (kPairs) {
+    const uint32_t part = off % 128u;
+    if (part != 0u && part != 64u) return false;
+    pix = (long long)(off / 128u) - (long long)h * Nv + (part != 0u ? 1 : 0);
+  } else {
+    const long long row = off / row_bytes;
+    if (off % row_bytes != 0u || row % nH != h) return false;
+    pix = row / nH;
+  }
+  return pix >= lv.start && pix < lv.start + (long long)lv.W * lv.H && pix < Nv;
+}
+
 // Write the four corner rows of the group's live samples densely into `rows`
 // (sample order, then lane order: a ballot per sample places each lane) and
 // pad every group of the wave with skipped rows up to
@@ -161,6 +179,7 @@ __device__ inline int stage_rows(uint2* __restrict__ rows, const double (&xs)[kS
         sample_corners(c, xs[i], ys[i], alpha[i], lv[at.x], true, h, nH, Nv, row_bytes);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
+        MSDA_CHECK(kCheckGatherRow, c[t].x == kSkip || corner_in_level<kPairs>(c[t].x, lv[at.x], h, nH, Nv, row_bytes));
         // skipped corners keep their offset past every image
         if (c[t].x != kSkip) c[t].x += (uint32_t)at.y;
         rows[pos + t] = c[t];
@@ -312,6 +331,7 @@ struct MsdaWalk {
       if (i < end) {
         if (!plan) return i;
         const int64_t item = uniform((int64_t)plan[lo + i]);
+        MSDA_CHECK(kCheckListEntry, item >= lo && item < lo + Nq);  // batch item bi's entries name its queries
         if (item >= 0 && item < n) return item;
         continue;
       }
@@ -596,6 +616,7 @@ __global__ __launch_bounds__(kMaxWavesPerBlock* kWave, kSPL == 4 ? 4 : 1) void s
   const DieShare split(a.die_bounds + bi * kDieBounds, n_queries, waves_per_block);
   for (int64_t item = split.begin; item < split.end; item += split.stride) {
     const int64_t bq = uniform((int64_t)a.order[item]);
+    MSDA_CHECK(kCheckListEntry, bq >= bi * a.Nq && bq < (bi + 1) * a.Nq);
     if (bq < 0 || bq >= n_queries) continue;
     const int64_t b = bq / a.Nq, q = bq % a.Nq;
     const uint32_t seen = uniform(a.cammask[bq] & cam_bits);

@@ -28,6 +28,7 @@ namespace msda {
 __device__ inline void segment_bounds(const int32_t* pair_offsets, int64_t bc, int64_t n_pairs, int64_t* lo,
                                       int64_t* len) {
   int64_t s = pair_offsets[bc], e = pair_offsets[bc + 1];
+  MSDA_CHECK(kCheckListEntry, s >= 0 && s <= e && e <= n_pairs);
   s = s < 0 ? 0 : (s > n_pairs ? n_pairs : s);
   e = e < s ? s : (e > n_pairs ? n_pairs : e);
   *lo = s;
@@ -47,6 +48,7 @@ __global__ __launch_bounds__(256) void sca_rebatch_kernel(RebatchArgs a) {
     int64_t lo, len;
     segment_bounds(a.pair_offsets, bc, a.B * a.Ncam * a.Nq, &lo, &len);
     int64_t q = i < len ? a.pair_q[lo + i] : -1;
+    MSDA_CHECK(kCheckListEntry, i >= len || (q >= 0 && q < a.Nq));
     const bool live = q >= 0 && q < a.Nq;  // an entry outside [0, Nq) is a padded row
     q = live ? q : 0;
     float2* loc = reinterpret_cast<float2*>(a.loc_out) + r * S;
@@ -89,6 +91,7 @@ __global__ __launch_bounds__(256) void sca_scatter_kernel(ScatterArgs a, int c) 
     segment_bounds(a.pair_offsets, bc, a.B * a.Ncam * a.Nq, &lo, &len);
     if (i >= len) continue;  // uniform over the wavefront
     const int64_t q = a.pair_q[lo + i];
+    MSDA_CHECK(kCheckListEntry, q >= 0 && q < a.Nq);
     if (q < 0 || q >= a.Nq) continue;
     const float4* src = reinterpret_cast<const float4*>(a.rows + (bc * a.max_len + i) * a.C);
     float4* dst = reinterpret_cast<float4*>(a.slots + (b * a.Nq + q) * a.C);

@@ -541,3 +541,32 @@ def test_msda_gather_rejects(lib):
     assert g(F=0) == INVALID                        # no frames
     assert g(Dh=16) == UNSUPPORTED
     assert lib.msda_gather(A, 0, A, A, None, None, 1, 1, 2, 16, 0, 8, 32, 1, 4, None, None, 0, None) == OK  # Nq = 0
+
+
+def test_check_counts_unsupported_in_the_regular_build(lib):
+    """The regular library has no device-side checks: msda_check_counts
+    returns MSDA_ERR_UNSUPPORTED and touches nothing (no device call)."""
+    counts = (ctypes.c_ulonglong * 4)(7, 7, 7, 7)
+    lib.msda_check_counts.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), _int, _int]
+    assert lib.msda_check_counts(counts, 4, 0) == UNSUPPORTED
+    assert list(counts) == [7, 7, 7, 7]
+    assert b"libmsda_checked.so" in lib.msda_last_error()
+
+
+def test_checked_build_exports_the_same_entry_points():
+    """libmsda_checked.so is the same C ABI; its msda_check_counts rejects a
+    short counts array before any device call."""
+    import scale_deformable_attention_forward_amd as m
+    path = m.checked_library_path()
+    if not os.path.exists(path):
+        from scale_deformable_attention_forward_amd import build
+        build.build(checked=True)
+    checked = ctypes.CDLL(path)
+    for name in declared_functions():
+        assert hasattr(checked, name), f"{name} missing from the checked build"
+    checked.msda_check_counts.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), _int, _int]
+    checked.msda_last_error.restype = ctypes.c_char_p
+    counts = (ctypes.c_ulonglong * 4)()
+    assert checked.msda_check_counts(counts, 3, 0) == INVALID
+    assert checked.msda_check_counts(None, 4, 0) == INVALID
+    assert b"MSDA_CHECK_KINDS" in checked.msda_last_error()
