@@ -32,7 +32,9 @@
  *    allocates or frees memory.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it asynchronously; no entry point synchronises the
- *    host.  Buffers must stay valid until the stream has finished the work.
+ *    host (the one exception is the debugging call msda_check_counts, which
+ *    waits for the device).  Buffers must stay valid until the stream has
+ *    finished the work.
  *    Every entry point enqueues kernels only (no memset or copy nodes), so
  *    it can be captured into a HIP graph and replayed.
  *  - Entry points may be called from several host threads at once.  Calls

@@ -1,6 +1,7 @@
 // C ABI of libmsda.so (declared in include/msda.h): argument checks on the
 // host, then stream-ordered launches.  Nothing here allocates device memory
-// or synchronises the host.
+// or synchronises the host, except msda_check_counts in the checked build
+// (a debugging call that waits for the device before reading its counters).
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
