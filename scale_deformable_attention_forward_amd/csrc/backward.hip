@@ -76,6 +76,11 @@ __device__ inline void sample_rows_of(SampleRec& r, double x, double y, float al
     const long long pix = base + (long long)dy * lv.W + dx;
     const bool ok = ix + dx >= 0 && ix + dx < lv.W && iy + dy >= 0 && iy + dy < lv.H && pix >= 0 && pix < Nv;
     r.row[c] = ok ? (uint32_t)(pix * nH + h) : kNoRow;
+    // checked builds: the row is pixel p's row of head h, p inside the level
+    MSDA_CHECK(kCheckGatherRow, r.row[c] == kNoRow ||
+                                    ((long long)r.row[c] % nH == h && (long long)r.row[c] / nH >= lv.start &&
+                                     (long long)r.row[c] / nH < lv.start + (long long)lv.W * lv.H &&
+                                     (long long)r.row[c] / nH < Nv));
   }
 }
 

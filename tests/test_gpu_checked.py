@@ -5,8 +5,8 @@ library.  Parity cases from the other GPU test modules are collected here a
 second time, so they run through the checked kernels and must still match
 the oracle; after each of them every check counter must read zero: no
 compaction write left its run or segment, no work-list, plan or pair-list
-entry read lay outside its range, and no gather staged a corner row outside
-its sample's level and head.  A positive control plants out-of-range plan
+entry read lay outside its range, and no gather (forward or backward)
+staged a corner row outside its sample's level and head.  A positive control plants out-of-range plan
 entries (which the operator documents as skipped) and sees them counted.
 """
 import numpy as np
@@ -16,6 +16,10 @@ import torch
 import scale_deformable_attention_forward_amd as msda
 from gpu_util import announce, dev
 
+from test_gpu_backward import (test_bevformer_sca_backward_atomic, test_bevformer_sca_backward_bf16_value,  # noqa: F401
+                               test_bevformer_sca_backward_full, test_detr_encoder_msda_backward_full,
+                               test_msda_backward_edge_cases, test_msda_backward_overlapping_levels,
+                               test_sca_backward_edge_cases, test_temporal_frames_backward_full)
 from test_gpu_pairs import (test_bevformer_sca_bf16_layer_in_pairs, test_operator_pairs_edge_cases,  # noqa: F401
                             test_sca_pairs_edge_cases, test_sca_pairs_stage_path_and_noalloc,
                             test_temporal_frames_in_pairs)
