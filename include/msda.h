@@ -556,8 +556,9 @@ const char* msda_last_error(void);
  * writes against their segments, every work-list, plan and pair-list entry
  * they read against the range it must lie in, and every corner row a gather
  * stages against its sample's level and head.  A failed check adds one to a
- * counter of its kind (MSDA_CHECK_*) on the device; nothing traps and no
- * result changes.  msda_check_counts waits for the current device
+ * counter of its kind (MSDA_CHECK_*) on the device for each lane that sees
+ * it (a count of lanes, not of distinct entries: zero is the only value
+ * with a fixed meaning); nothing traps and no result changes.  msda_check_counts waits for the current device
  * (hipDeviceSynchronize, unlike every other entry point), writes the
  * counters summed over the library to counts[0 .. MSDA_CHECK_KINDS), and
  * zeroes them when reset != 0.  counts must hold MSDA_CHECK_KINDS entries
